@@ -1,0 +1,215 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) hybrid compressed attention library
+ *          (libcsa.so): DeepSeek-V4's Compressed Sparse Attention (CSA) and
+ *          Heavily Compressed Attention (HCA).
+ *
+ * Pages this operation set is defined on:
+ *  [P1] "DeepSeek-V4 技术解析：架构革新与 Coding Agent 后训练优化" (cdjax.com),
+ *       section 1.1 "混合注意力：CSA 与 HCA 的协同": the token-level compressor
+ *       (m tokens -> one KV entry), the Lightning Indexer, the top-k selector
+ *       (Pro keeps 1024), MQA-form core attention, the extra sliding-window
+ *       branch, HCA's dense attention over all compressed entries, and the
+ *       interleaving of CSA and HCA layers.
+ *  [P2] "DeepSeek V4 详解：1M 上下文背后，真正发生了什么", sections
+ *       "第一刀：让注意力别再按原价付费" (m, m', per-query top-k, HCA dense),
+ *       "第二刀：KV cache 被当成系统在管" (compressed entries + window state),
+ *       "mHC、Muon、FP4：这些不是论文装饰" (low-precision indexer QK path).
+ *  [P3] "DeepSeek-V4 技术报告解读：百万Token上下文是怎么做到的", section
+ *       "三大架构改动" items 1-2 (sequence shrinks to 1/m; m' >> m; window).
+ *  [P5] chenxutan.com preface: CSA 4:1, HCA 128:1.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers, 16-byte aligned, dense, row-major
+ *    in the index order written next to them.  The caller owns every buffer;
+ *    the library keeps no pointer after the call returns and allocates no
+ *    device memory: scratch comes from the caller's workspace `ws` of
+ *    `ws_bytes` bytes, whose required size the matching *_ws_bytes() call
+ *    returns (0 is a valid answer; ws may then be NULL).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  On CSA_OK the work
+ *    is enqueued on that stream and the call returns without waiting.
+ *  - Every argument is validated on the host before anything is enqueued.  On
+ *    error nothing is enqueued, a csa_status_t code is returned, and
+ *    csa_last_error() (thread-local) holds a one-line explanation.  No
+ *    exception or abort crosses the ABI.
+ *  - dtypes: CSA_BF16 = bfloat16 (stored as 16-bit patterns), CSA_E4M3 = OCP
+ *    8-bit float E4M3 (e4m3fn: bias 7, max 448, 0x7f/0xff NaN).
+ *  - Results are deterministic: identical inputs give bitwise identical
+ *    outputs (no float atomics; every reduction has a fixed order).
+ *  - Inputs must be finite.
+ *
+ * Positions: raw token positions are absolute, 0-based.  A ratio-m compression
+ * of L tokens has N = ceil(L/m) entries; entry j covers raw tokens
+ * [j*m, min((j+1)*m, L)) and is visible to a query at position p iff
+ * min((j+1)*m, L) - 1 <= p (so visible entries are always a prefix).
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+    CSA_OK = 0,
+    CSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    CSA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+    CSA_ERR_DTYPE = 3,       /* unknown dtype code */
+    CSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    CSA_ERR_WORKSPACE = 5,   /* ws_bytes below the *_ws_bytes() answer */
+    CSA_ERR_UNSUPPORTED = 6, /* valid, but outside the sizes this build supports */
+    CSA_ERR_HIP = 7          /* a HIP runtime call or launch failed */
+} csa_status_t;
+
+typedef enum { CSA_BF16 = 0, CSA_E4M3 = 1 } csa_dtype_t;
+
+/* Library identity and error reporting. */
+int csa_abi_version(void);                 /* returns CSA_ABI_VERSION */
+const char* csa_status_str(int status);    /* static string for a status code */
+const char* csa_last_error(void);          /* thread-local detail of the last error ("" if none) */
+
+/* ------------------------------------------------------------------------ */
+/* A1. Token-level KV compressor ([P1] 1.1; [P2] first section; [P3] item 1) */
+/* ------------------------------------------------------------------------ */
+/* Compresses every m raw tokens into one entry.  The pages do not print the
+ * pooling weights; this library implements softmax-gated pooling within each
+ * block (block mean when w_gate = 0 and b_slot = 0):
+ *   z_t = hidden_t . w_gate + b_slot[t - j*m],   a = softmax over the block,
+ *   kv_out[j] = bf16( sum_t a_t * (hidden_t . w_kv^T) )
+ *   ik_out[j] = bf16 or e4m3( sum_t a_t * (hidden_t . w_ik^T) )   (if w_ik)
+ *   win_out[u] = bf16( hidden_{L-W+u} . w_kv^T )   for u in [0, W)  (if win_out;
+ *                rows for negative positions are zero)
+ * The tail entry j = N-1 pools the L mod m remaining tokens when m does not
+ * divide L.  Pooling is applied before the projection (equal to projecting
+ * first by linearity; the pooled hidden row is rounded to bf16 once).
+ *   hidden [B][L][Dh] bf16       w_kv [D][Dh] bf16     w_ik [dI][Dh] bf16 or NULL
+ *   w_gate [Dh] fp32             b_slot [m] fp32 or NULL (= zeros)
+ *   kv_out [B][N][D] bf16        ik_out [B][N][dI] (ik_dtype) or NULL
+ *   win_out [B][W][D] bf16 or NULL
+ * Supported: Dh % 64 == 0 and 64 <= Dh <= 16384; D, dI in {64, 128, 256, 512};
+ * 1 <= m <= 1024; 0 <= W <= 1024; 1 <= L; B >= 1. */
+size_t csa_compress_ws_bytes(int B, long long L, int Dh, int m);
+int csa_compress(const void* hidden, const void* w_kv, const void* w_ik,
+                 const float* w_gate, const float* b_slot,
+                 int B, long long L, int Dh, int D, int dI, int m, int W, int ik_dtype,
+                 void* kv_out, void* ik_out, void* win_out,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* A2 + A3. Lightning-Indexer scores and per-query top-k                     */
+/*          ([P1] 1.1; [P2] first section and "mHC、Muon、FP4")              */
+/* ------------------------------------------------------------------------ */
+/* For query t of sequence b (absolute position pos0 + t) and every visible
+ * compressed entry s, the score is the canonical fp32 value
+ *   S = fma-chain over h = 0..HI-1 of  w_idx[h] * ReLU( RN32( exact q_h . k_s ) )
+ * (each per-head dot product is the exact sum rounded once to fp32, ReLU maps
+ * <= 0 to +0, and S = fmaf(w_h, r_h, S) starting from S = +0).  The selection
+ * keeps the first min(topk, n_visible) entries under the total order
+ * (S descending, index ascending) -- bit-exact, independent of how the GPU
+ * computes its internal approximate scores.
+ *   q_idx [B][Tq][HI][dI] dtype     w_idx [B][Tq][HI] fp32
+ *   k_idx [B][Nc][dI] dtype         (Nc = ceil(L/m) entries; L raw tokens)
+ *   idx_out [B][Tq][topk] int32: selected entry indices in ascending order,
+ *           padded with -1 after cnt entries
+ *   cnt_out [B][Tq] int32 or NULL: min(topk, n_visible)
+ * Supported: dtype in {CSA_BF16, CSA_E4M3}; HI in {1,2,4,8,16}; dI in {64,128};
+ * 1 <= topk <= 4096; 1 <= Tq <= 65536; Nc <= 2^24; pos0 >= 0. */
+size_t csa_index_topk_ws_bytes(int B, int Tq, int Nc);
+int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype,
+                   int B, int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0,
+                   int topk, int32_t* idx_out, int32_t* cnt_out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* A4. CSA core attention: MQA over the selected entries plus a sliding       */
+/*     window of raw local tokens ([P1] 1.1; [P3] item 1)                    */
+/* ------------------------------------------------------------------------ */
+/* For query t of sequence b at p = pos0 + t and every head h, one softmax over
+ * the union of {kv[b][j] : j in idx[b][t][*], j >= 0} and the raw window rows
+ * {kv_raw[b][u - raw0] : u in [max(0, p-W+1), p]}; each row is both key and
+ * value (MQA, one shared KV head):
+ *   l_r = scale * (q_h . x_r),  out_h = sum_r softmax(l)_r x_r,
+ *   lse_h = log sum_r exp(l_r)   (natural log; -inf and out = 0 if no rows).
+ *   q   [B][Tq][H][D] bf16       kv [B][Nc][D] bf16
+ *   idx [B][Tq][topk] int32 (entries < 0 are skipped; must be < Nc)
+ *   kv_raw [B][Lr][D] bf16, row i = raw position raw0 + i (may be NULL if W = 0)
+ *   out [B][Tq][H][D] bf16       lse_out [B][Tq][H] fp32 or NULL
+ * Requires raw0 <= max(0, pos0 - W + 1) and pos0 + Tq - 1 < raw0 + Lr when W > 0.
+ * Supported: D in {128, 512}; H % 16 == 0, H <= 256; 0 <= topk <= 4096;
+ * 0 <= W <= 1024. */
+size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W);
+int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const void* kv_raw,
+                    int B, int Tq, int H, int D, int Nc, int topk, int Lr, long long raw0,
+                    long long pos0, int W, float scale, void* out, float* lse_out,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* A5. HCA attention: dense MQA over every visible compressed entry          */
+/*     ([P1] 1.1; [P2] first section; [P3] item 2)                           */
+/* ------------------------------------------------------------------------ */
+/* As A4 but over {kv_h[b][j] : j visible to p} (ratio mh over L raw tokens),
+ * with no selection and no window.
+ *   q [B][Tq][H][D] bf16    kv_h [B][Nh][D] bf16 (Nh = ceil(L/mh))
+ *   out [B][Tq][H][D] bf16  lse_out [B][Tq][H] fp32 or NULL
+ * Supported: D in {128, 512}; H % 16 == 0, H <= 256. */
+size_t hca_dense_attn_ws_bytes(int B, int Tq, int H, int D, int Nh);
+int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D, int Nh,
+                   long long L, int mh, long long pos0, float scale,
+                   void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* A6. Fused decode of one interleaved CSA layer followed by one HCA layer   */
+/*     ([P1] 1.1: the two attention kinds alternate across layers)           */
+/* ------------------------------------------------------------------------ */
+/* One query token per sequence at position L-1 (decode).  Runs, in stream
+ * order and without host synchronisation: csa_index_topk -> csa_sparse_attn
+ * (CSA layer), then hca_dense_attn (HCA layer).  The two layers take their own
+ * queries; a caller chaining real layers feeds one layer's output into the
+ * next layer's projections outside this call. */
+typedef struct csa_hca_decode_args {
+    int B;                 /* sequences */
+    long long L;           /* raw context length of every sequence */
+    int H, D;              /* query heads and KV dim of both layers */
+    float scale;           /* softmax scale of both layers */
+    /* CSA layer */
+    const void* csa_q;     /* [B][H][D] bf16 */
+    const void* q_idx;     /* [B][HI][dI] idx_dtype */
+    const float* w_idx;    /* [B][HI] fp32 */
+    const void* k_idx;     /* [B][Nc][dI] idx_dtype, Nc = ceil(L/m) */
+    const void* kv;        /* [B][Nc][D] bf16 */
+    const void* kv_raw;    /* [B][W][D] bf16: raw positions L-W .. L-1 */
+    int idx_dtype, HI, dI, m, topk, W;
+    void* csa_out;         /* [B][H][D] bf16 */
+    float* csa_lse;        /* [B][H] fp32 or NULL */
+    int32_t* idx_out;      /* [B][topk] int32 or NULL (then kept in the workspace) */
+    /* HCA layer */
+    const void* hca_q;     /* [B][H][D] bf16 */
+    const void* kv_h;      /* [B][Nh][D] bf16, Nh = ceil(L/mh) */
+    int mh;
+    void* hca_out;         /* [B][H][D] bf16 */
+    float* hca_lse;        /* [B][H] fp32 or NULL */
+} csa_hca_decode_args_t;
+
+size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a);
+int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing (measurement aid; not part of the method)                   */
+/* ------------------------------------------------------------------------ */
+/* While enabled, every kernel the library launches is bracketed by a pair of
+ * HIP events recorded on the stream it is launched on.  csa_prof_read() waits
+ * for the recorded events and returns the summed duration (ms) and launch
+ * count of every kernel whose name equals `kernel`.  csa_prof_reset() drops
+ * all records.  Kernel names are the ones rocprofv3 reports. */
+int csa_prof_enable(int on);
+int csa_prof_reset(void);
+int csa_prof_read(const char* kernel, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */
