@@ -1,0 +1,190 @@
+"""Thin Python binding of libcsa.so (include/csa.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+stream; every step of the method runs in the library's HIP kernels.  Each
+function has the C entry point's name and raises CsaError on a non-zero status.
+If libcsa.so is missing the import fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+BF16 = 0
+E4M3 = 1
+
+
+class CsaError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() (hipcc, gfx950) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, LL, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "csa_abi_version": ([], I),
+        "csa_status_str": ([I], ctypes.c_char_p),
+        "csa_last_error": ([], ctypes.c_char_p),
+        "csa_compress_ws_bytes": ([I, LL, I, I], Z),
+        "csa_compress": ([P, P, P, P, P, I, LL, I, I, I, I, I, I, P, P, P, P, Z, P], I),
+        "csa_index_topk_ws_bytes": ([I, I, I], Z),
+        "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, Z, P], I),
+        "csa_sparse_attn_ws_bytes": ([I, I, I, I, I, I], Z),
+        "csa_sparse_attn": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, Z, P], I),
+        "hca_dense_attn_ws_bytes": ([I, I, I, I, I], Z),
+        "hca_dense_attn": ([P, P, I, I, I, I, I, LL, I, LL, F, P, P, P, Z, P], I),
+        "csa_hca_decode_ws_bytes": ([P], Z),
+        "csa_hca_decode": ([P, P, Z, P], I),
+        "csa_debug_fp8_to_bf16": ([P, P, I, P], I),
+        "csa_prof_enable": ([I], I),
+        "csa_prof_reset": ([], I),
+        "csa_prof_read": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+EXPORTED = ("csa_abi_version", "csa_status_str", "csa_last_error", "csa_compress_ws_bytes", "csa_compress",
+            "csa_index_topk_ws_bytes", "csa_index_topk", "csa_sparse_attn_ws_bytes", "csa_sparse_attn",
+            "hca_dense_attn_ws_bytes", "hca_dense_attn", "csa_hca_decode_ws_bytes", "csa_hca_decode",
+            "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read")
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of csa_hca_decode_args_t."""
+    _fields_ = [
+        ("B", ctypes.c_int), ("L", ctypes.c_longlong), ("H", ctypes.c_int), ("D", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("csa_q", ctypes.c_void_p), ("q_idx", ctypes.c_void_p), ("w_idx", ctypes.c_void_p),
+        ("k_idx", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("kv_raw", ctypes.c_void_p),
+        ("idx_dtype", ctypes.c_int), ("HI", ctypes.c_int), ("dI", ctypes.c_int), ("m", ctypes.c_int),
+        ("topk", ctypes.c_int), ("W", ctypes.c_int),
+        ("csa_out", ctypes.c_void_p), ("csa_lse", ctypes.c_void_p), ("idx_out", ctypes.c_void_p),
+        ("hca_q", ctypes.c_void_p), ("kv_h", ctypes.c_void_p), ("mh", ctypes.c_int),
+        ("hca_out", ctypes.c_void_p), ("hca_lse", ctypes.c_void_p),
+    ]
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise CsaError(f"{lib.csa_status_str(rc).decode()}: {lib.csa_last_error().decode()}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor | None:
+    """Device workspace of at least nbytes (256-byte aligned by the caching allocator)."""
+    if nbytes == 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def csa_compress(hidden, w_kv, w_ik, w_gate, b_slot, m: int, W: int, kv_out, ik_out=None, win_out=None,
+                 ik_dtype: int = BF16, ws=None, stream=None):
+    B, L, Dh = hidden.shape
+    D = w_kv.shape[0]
+    dI = w_ik.shape[0] if w_ik is not None else 0
+    need = lib.csa_compress_ws_bytes(B, L, Dh, m)
+    if ws is None:
+        ws = workspace(need, hidden.device)
+    _check(lib.csa_compress(_p(hidden), _p(w_kv), _p(w_ik), _p(w_gate), _p(b_slot), B, L, Dh, D, dI, m, W, ik_dtype,
+                            _p(kv_out), _p(ik_out), _p(win_out), _p(ws), 0 if ws is None else ws.numel(),
+                            _stream(stream)))
+
+
+def csa_index_topk(q_idx, w_idx, k_idx, dtype: int, L: int, m: int, pos0: int, topk: int, idx_out, cnt_out=None,
+                   ws=None, stream=None):
+    B, Tq, HI, dI = q_idx.shape
+    Nc = k_idx.shape[1]
+    need = lib.csa_index_topk_ws_bytes(B, Tq, Nc)
+    if ws is None:
+        ws = workspace(need, q_idx.device)
+    _check(lib.csa_index_topk(_p(q_idx), _p(w_idx), _p(k_idx), dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,
+                              _p(idx_out), _p(cnt_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def csa_sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, out, lse_out=None, ws=None,
+                    stream=None):
+    B, Tq, H, D = q.shape
+    Nc = kv.shape[1] if kv is not None else 0
+    topk = idx.shape[-1] if idx is not None else 0
+    Lr = kv_raw.shape[1] if kv_raw is not None else 0
+    need = lib.csa_sparse_attn_ws_bytes(B, Tq, H, D, topk, W)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib.csa_sparse_attn(_p(q), _p(kv), _p(idx), _p(kv_raw), B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W,
+                               float(scale), _p(out), _p(lse_out), _p(ws), 0 if ws is None else ws.numel(),
+                               _stream(stream)))
+
+
+def hca_dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, out, lse_out=None, ws=None, stream=None):
+    B, Tq, H, D = q.shape
+    Nh = kv_h.shape[1]
+    need = lib.hca_dense_attn_ws_bytes(B, Tq, H, D, Nh)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib.hca_dense_attn(_p(q), _p(kv_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale), _p(out), _p(lse_out),
+                              _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def make_decode_args(*, L, scale, csa_q, q_idx, w_idx, k_idx, kv, kv_raw, idx_dtype, m, topk, W, csa_out,
+                     hca_q, kv_h, mh, hca_out, csa_lse=None, hca_lse=None, idx_out=None) -> DecodeArgs:
+    B, H, D = csa_q.shape[0], csa_q.shape[-2], csa_q.shape[-1]
+    HI, dI = q_idx.shape[-2], q_idx.shape[-1]
+    return DecodeArgs(B=B, L=L, H=H, D=D, scale=float(scale), csa_q=_p(csa_q), q_idx=_p(q_idx), w_idx=_p(w_idx),
+                      k_idx=_p(k_idx), kv=_p(kv), kv_raw=_p(kv_raw), idx_dtype=idx_dtype, HI=HI, dI=dI, m=m,
+                      topk=topk, W=W, csa_out=_p(csa_out), csa_lse=_p(csa_lse), idx_out=_p(idx_out),
+                      hca_q=_p(hca_q), kv_h=_p(kv_h), mh=mh, hca_out=_p(hca_out), hca_lse=_p(hca_lse))
+
+
+def csa_hca_decode_ws_bytes(args: DecodeArgs) -> int:
+    return int(lib.csa_hca_decode_ws_bytes(ctypes.byref(args)))
+
+
+def csa_hca_decode(args: DecodeArgs, ws=None, stream=None, device=None):
+    need = csa_hca_decode_ws_bytes(args)
+    if ws is None:
+        ws = workspace(need, device or torch.device("cuda"))
+    _check(lib.csa_hca_decode(ctypes.byref(args), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def csa_debug_fp8_to_bf16(inp, out, stream=None):
+    _check(lib.csa_debug_fp8_to_bf16(_p(inp), _p(out), inp.numel(), _stream(stream)))
+
+
+def prof_enable(on: bool):
+    _check(lib.csa_prof_enable(1 if on else 0))
+
+
+def prof_reset():
+    _check(lib.csa_prof_reset())
+
+
+def prof_read(kernel: str):
+    t = ctypes.c_double()
+    n = ctypes.c_int()
+    _check(lib.csa_prof_read(kernel.encode(), ctypes.byref(t), ctypes.byref(n)))
+    return t.value, n.value

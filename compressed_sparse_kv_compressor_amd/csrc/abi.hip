@@ -1,0 +1,388 @@
+// abi.hip -- the C ABI of libcsa (include/csa.h): argument validation, workspace
+// sizing and launch sequencing.  Nothing here computes; every step of the method
+// runs in the kernels of index_topk.hip, attn.hip and compress.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/csa.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace csa_host {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+// ---------------------------------------------------------------------------
+// timing registry
+// ---------------------------------------------------------------------------
+struct ProfRec {
+    std::string name;
+    hipEvent_t a, b;
+};
+static std::mutex g_prof_mu;
+static bool g_prof_on = false;
+static std::vector<ProfRec> g_prof;
+static std::vector<hipEvent_t> g_ev_pool;
+
+static hipEvent_t take_event() {
+    if (!g_ev_pool.empty()) {
+        hipEvent_t e = g_ev_pool.back();
+        g_ev_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+void* prof_begin(const char* name, hipStream_t s) {
+    if (!g_prof_on) return nullptr;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    ProfRec r;
+    r.name = name;
+    r.a = take_event();
+    r.b = take_event();
+    if (!r.a || !r.b) return nullptr;
+    (void)hipEventRecord(r.a, s);
+    g_prof.push_back(r);
+    return (void*)(uintptr_t)g_prof.size();
+}
+
+void prof_end(void* token, hipStream_t s) {
+    if (!token) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    size_t i = (size_t)(uintptr_t)token - 1;
+    if (i < g_prof.size()) (void)hipEventRecord(g_prof[i].b, s);
+}
+
+}  // namespace csa_host
+
+using csa_host::fail;
+
+// ---------------------------------------------------------------------------
+// helpers
+// ---------------------------------------------------------------------------
+namespace {
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+#define REQ_PTR(p)                                                                     \
+    do {                                                                               \
+        if (!(p)) return fail(CSA_ERR_NULL, "%s: %s is NULL", fn, #p);                 \
+        if (misaligned(p)) return fail(CSA_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+    } while (0)
+#define OPT_PTR(p)                                                                     \
+    do {                                                                               \
+        if ((p) && misaligned(p)) return fail(CSA_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+    } while (0)
+#define REQ(cond, code, ...)                                                           \
+    do {                                                                               \
+        if (!(cond)) return fail(code, __VA_ARGS__);                                   \
+    } while (0)
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+int check_ws(const char* fn, void* ws, size_t have, size_t need) {
+    if (have < need) return fail(CSA_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, have, need);
+    if (need && !ws) return fail(CSA_ERR_NULL, "%s: ws is NULL but %zu bytes are required", fn, need);
+    if (ws && misaligned(ws)) return fail(CSA_ERR_ALIGN, "%s: ws is not 16-byte aligned", fn);
+    return CSA_OK;
+}
+
+int validate_index(const char* fn, const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B,
+                   int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
+                   const int32_t* idx_out, const int32_t* cnt_out) {
+    REQ_PTR(q_idx);
+    REQ_PTR(w_idx);
+    REQ_PTR(k_idx);
+    REQ_PTR(idx_out);
+    OPT_PTR(cnt_out);
+    REQ(dtype == CSA_BF16 || dtype == CSA_E4M3, CSA_ERR_DTYPE, "%s: dtype %d unknown", fn, dtype);
+    REQ(B >= 1 && Tq >= 1 && L >= 1 && m >= 1 && pos0 >= 0, CSA_ERR_SHAPE,
+        "%s: need B, Tq, L, m >= 1 and pos0 >= 0 (B=%d Tq=%d L=%lld m=%d pos0=%lld)", fn, B, Tq, L, m, pos0);
+    REQ((long long)Nc == (L + m - 1) / m, CSA_ERR_SHAPE, "%s: Nc=%d but ceil(L/m)=%lld", fn, Nc, (L + m - 1) / m);
+    REQ(pos0 + Tq - 1 <= L - 1, CSA_ERR_SHAPE, "%s: query positions pos0..pos0+Tq-1 exceed L-1", fn);
+    REQ(topk >= 1, CSA_ERR_SHAPE, "%s: topk=%d must be >= 1", fn, topk);
+    REQ(topk <= 4096 && Tq <= 65536 && Nc <= (1 << 24), CSA_ERR_UNSUPPORTED,
+        "%s: topk <= 4096, Tq <= 65536, Nc <= 2^24 supported", fn);
+    REQ(pow2_in(HI, 1, 16), CSA_ERR_UNSUPPORTED, "%s: HI=%d (supported 1,2,4,8,16)", fn, HI);
+    REQ(dI == 64 || dI == 128, CSA_ERR_UNSUPPORTED, "%s: dI=%d (supported 64, 128)", fn, dI);
+    return CSA_OK;
+}
+
+int validate_attn_common(const char* fn, const void* q, int B, int Tq, int H, int D, float scale, const void* out,
+                         const float* lse) {
+    REQ_PTR(q);
+    REQ_PTR(out);
+    OPT_PTR(lse);
+    REQ(B >= 1 && Tq >= 1 && H >= 1, CSA_ERR_SHAPE, "%s: need B, Tq, H >= 1", fn);
+    REQ(D == 128 || D == 512, CSA_ERR_UNSUPPORTED, "%s: D=%d (supported 128, 512)", fn, D);
+    REQ(H % 16 == 0 && H <= 256, CSA_ERR_UNSUPPORTED, "%s: H=%d (supported multiples of 16 up to 256)", fn, H);
+    REQ(scale == scale && scale > -1e30f && scale < 1e30f, CSA_ERR_SHAPE, "%s: scale must be finite", fn);
+    return CSA_OK;
+}
+
+int validate_sparse(const char* fn, const void* q, const void* kv, const int32_t* idx, const void* kv_raw, int B,
+                    int Tq, int H, int D, int Nc, int topk, int Lr, long long raw0, long long pos0, int W,
+                    float scale, const void* out, const float* lse) {
+    int rc = validate_attn_common(fn, q, B, Tq, H, D, scale, out, lse);
+    if (rc) return rc;
+    REQ(topk >= 0 && W >= 0 && pos0 >= 0 && Nc >= 0, CSA_ERR_SHAPE, "%s: topk, W, pos0, Nc must be >= 0", fn);
+    REQ(topk <= 4096 && W <= 1024, CSA_ERR_UNSUPPORTED, "%s: topk <= 4096 and W <= 1024 supported", fn);
+    REQ(topk + W >= 0, CSA_ERR_SHAPE, "%s: bad sizes", fn);
+    if (topk > 0) {
+        REQ_PTR(kv);
+        REQ_PTR(idx);
+        REQ(Nc >= 1, CSA_ERR_SHAPE, "%s: Nc must be >= 1 when topk > 0", fn);
+    }
+    if (W > 0) {
+        REQ_PTR(kv_raw);
+        REQ(Lr >= 1, CSA_ERR_SHAPE, "%s: Lr must be >= 1 when W > 0", fn);
+        const long long first = pos0 - W + 1 < 0 ? 0 : pos0 - W + 1;
+        REQ(raw0 <= first, CSA_ERR_SHAPE, "%s: raw rows start at %lld, window needs %lld", fn, raw0, first);
+        REQ(pos0 + Tq - 1 < raw0 + Lr, CSA_ERR_SHAPE, "%s: raw rows end at %lld, window needs %lld", fn,
+            raw0 + Lr - 1, pos0 + Tq - 1);
+    }
+    return CSA_OK;
+}
+
+int validate_dense(const char* fn, const void* q, const void* kv_h, int B, int Tq, int H, int D, int Nh, long long L,
+                   int mh, long long pos0, float scale, const void* out, const float* lse) {
+    int rc = validate_attn_common(fn, q, B, Tq, H, D, scale, out, lse);
+    if (rc) return rc;
+    REQ_PTR(kv_h);
+    REQ(L >= 1 && mh >= 1 && pos0 >= 0, CSA_ERR_SHAPE, "%s: need L, mh >= 1 and pos0 >= 0", fn);
+    REQ((long long)Nh == (L + mh - 1) / mh, CSA_ERR_SHAPE, "%s: Nh=%d but ceil(L/mh)=%lld", fn, Nh, (L + mh - 1) / mh);
+    REQ(pos0 + Tq - 1 <= L - 1, CSA_ERR_SHAPE, "%s: query positions exceed L-1", fn);
+    return CSA_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// exported entry points
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_status_str(int s) {
+    switch (s) {
+        case CSA_OK: return "CSA_OK";
+        case CSA_ERR_NULL: return "CSA_ERR_NULL";
+        case CSA_ERR_SHAPE: return "CSA_ERR_SHAPE";
+        case CSA_ERR_DTYPE: return "CSA_ERR_DTYPE";
+        case CSA_ERR_ALIGN: return "CSA_ERR_ALIGN";
+        case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE";
+        case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED";
+        case CSA_ERR_HIP: return "CSA_ERR_HIP";
+        default: return "CSA_ERR_UNKNOWN";
+    }
+}
+
+const char* csa_last_error(void) { return csa_host::g_err; }
+
+size_t csa_compress_ws_bytes(int B, long long L, int Dh, int m) {
+    if (B < 1 || L < 1 || Dh < 1 || m < 1) return 0;
+    return csa_host::compress_ws_bytes(B, L, Dh, m);
+}
+
+int csa_compress(const void* hidden, const void* w_kv, const void* w_ik, const float* w_gate, const float* b_slot,
+                 int B, long long L, int Dh, int D, int dI, int m, int W, int ik_dtype, void* kv_out, void* ik_out,
+                 void* win_out, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa_compress";
+    csa_host::g_err[0] = 0;
+    REQ_PTR(hidden);
+    REQ_PTR(w_kv);
+    REQ_PTR(w_gate);
+    REQ_PTR(kv_out);
+    OPT_PTR(w_ik);
+    OPT_PTR(b_slot);
+    OPT_PTR(ik_out);
+    OPT_PTR(win_out);
+    REQ(B >= 1 && L >= 1 && m >= 1 && W >= 0, CSA_ERR_SHAPE, "%s: need B, L, m >= 1 and W >= 0", fn);
+    REQ(ik_dtype == CSA_BF16 || ik_dtype == CSA_E4M3, CSA_ERR_DTYPE, "%s: ik_dtype %d unknown", fn, ik_dtype);
+    REQ(Dh % 64 == 0 && Dh >= 64 && Dh <= 16384, CSA_ERR_UNSUPPORTED, "%s: Dh=%d (multiple of 64 in [64,16384])", fn, Dh);
+    REQ(D == 64 || D == 128 || D == 256 || D == 512, CSA_ERR_UNSUPPORTED, "%s: D=%d unsupported", fn, D);
+    REQ(m <= 1024 && W <= 1024, CSA_ERR_UNSUPPORTED, "%s: m <= 1024 and W <= 1024 supported", fn);
+    REQ((L + m - 1) / m <= (1LL << 24) && (long long)B * L * Dh < (1LL << 40), CSA_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+    if (w_ik || ik_out) {
+        REQ(w_ik && ik_out, CSA_ERR_NULL, "%s: w_ik and ik_out must both be given or both be NULL", fn);
+        REQ(dI == 64 || dI == 128 || dI == 256 || dI == 512, CSA_ERR_UNSUPPORTED, "%s: dI=%d unsupported", fn, dI);
+    }
+    if (W > 0) REQ(win_out != nullptr, CSA_ERR_NULL, "%s: win_out is NULL but W > 0", fn);
+    int rc = check_ws(fn, ws, ws_bytes, csa_host::compress_ws_bytes(B, L, Dh, m));
+    if (rc) return rc;
+    return csa_host::compress_launch(hidden, w_kv, w_ik, w_gate, b_slot, B, L, Dh, D, dI, m, W, ik_dtype, kv_out,
+                                     ik_out, W > 0 ? win_out : nullptr, ws, (hipStream_t)stream);
+}
+
+size_t csa_index_topk_ws_bytes(int B, int Tq, int Nc) {
+    if (B < 1 || Tq < 1 || Nc < 1) return 0;
+    return csa_host::index_topk_ws_bytes(B, Tq, Nc);
+}
+
+int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq, int HI, int dI,
+                   int Nc, long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
+                   void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa_index_topk";
+    csa_host::g_err[0] = 0;
+    int rc = validate_index(fn, q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out, cnt_out);
+    if (rc) return rc;
+    rc = check_ws(fn, ws, ws_bytes, csa_host::index_topk_ws_bytes(B, Tq, Nc));
+    if (rc) return rc;
+    return csa_host::index_topk_launch(q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out,
+                                       cnt_out, ws, (hipStream_t)stream);
+}
+
+size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W) {
+    if (B < 1 || Tq < 1 || H < 1 || topk < 0 || W < 0) return 0;
+    return csa_host::attn_ws_bytes(B, Tq, H, D, topk + W);
+}
+
+int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const void* kv_raw, int B, int Tq, int H, int D,
+                    int Nc, int topk, int Lr, long long raw0, long long pos0, int W, float scale, void* out,
+                    float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa_sparse_attn";
+    csa_host::g_err[0] = 0;
+    int rc = validate_sparse(fn, q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse_out);
+    if (rc) return rc;
+    rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, topk + W));
+    if (rc) return rc;
+    csa_host::AttnRows r{1, kv, Nc, 0, 1, idx, topk, kv_raw, Lr, raw0, W};
+    return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
+                                 "k_attn_sparse");
+}
+
+size_t hca_dense_attn_ws_bytes(int B, int Tq, int H, int D, int Nh) {
+    if (B < 1 || Tq < 1 || H < 1 || Nh < 0) return 0;
+    return csa_host::attn_ws_bytes(B, Tq, H, D, Nh);
+}
+
+int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D, int Nh, long long L, int mh,
+                   long long pos0, float scale, void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "hca_dense_attn";
+    csa_host::g_err[0] = 0;
+    int rc = validate_dense(fn, q, kv_h, B, Tq, H, D, Nh, L, mh, pos0, scale, out, lse_out);
+    if (rc) return rc;
+    rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, Nh));
+    if (rc) return rc;
+    csa_host::AttnRows r{0, kv_h, Nh, L, mh, nullptr, 0, nullptr, 0, 0, 0};
+    return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
+                                 "k_attn_dense");
+}
+
+// Fused decode: workspace = [idx (if not caller-owned)] [index_topk ws] [attention ws (max of both layers)]
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a) {
+    if (!a || a->B < 1 || a->L < 1 || a->m < 1 || a->mh < 1 || a->topk < 1) return 0;
+    const int Nc = (int)((a->L + a->m - 1) / a->m), Nh = (int)((a->L + a->mh - 1) / a->mh);
+    size_t s = a->idx_out ? 0 : align256((size_t)a->B * a->topk * 4);
+    s += align256(csa_host::index_topk_ws_bytes(a->B, 1, Nc));
+    s += std::max(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, a->topk + a->W),
+                  csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, Nh));
+    return s;
+}
+
+int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa_hca_decode";
+    csa_host::g_err[0] = 0;
+    if (!a) return fail(CSA_ERR_NULL, "%s: args is NULL", fn);
+    REQ(a->B >= 1 && a->L >= 1 && a->m >= 1 && a->mh >= 1, CSA_ERR_SHAPE, "%s: need B, L, m, mh >= 1", fn);
+    const int Nc = (int)((a->L + a->m - 1) / a->m), Nh = (int)((a->L + a->mh - 1) / a->mh);
+    const long long p = a->L - 1;
+    int rc = validate_index(fn, a->q_idx, a->w_idx, a->k_idx, a->idx_dtype, a->B, 1, a->HI, a->dI, Nc, a->L, a->m, p,
+                            a->topk, a->idx_out ? a->idx_out : (const int32_t*)16, nullptr);
+    if (rc) return rc;
+    rc = validate_sparse(fn, a->csa_q, a->kv, (const int32_t*)16, a->kv_raw, a->B, 1, a->H, a->D, Nc, a->topk, a->W,
+                         a->L - a->W, p, a->W, a->scale, a->csa_out, a->csa_lse);
+    if (rc) return rc;
+    rc = validate_dense(fn, a->hca_q, a->kv_h, a->B, 1, a->H, a->D, Nh, a->L, a->mh, p, a->scale, a->hca_out,
+                        a->hca_lse);
+    if (rc) return rc;
+    rc = check_ws(fn, ws, ws_bytes, csa_hca_decode_ws_bytes(a));
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    char* w = (char*)ws;
+    int32_t* idx = a->idx_out;
+    if (!idx) {
+        idx = (int32_t*)w;
+        w += align256((size_t)a->B * a->topk * 4);
+    }
+    const size_t iws = align256(csa_host::index_topk_ws_bytes(a->B, 1, Nc));
+    rc = csa_host::index_topk_launch(a->q_idx, a->w_idx, a->k_idx, a->idx_dtype, a->B, 1, a->HI, a->dI, Nc, a->L, a->m,
+                                     p, a->topk, idx, nullptr, w, st);
+    if (rc) return rc;
+    w += iws;
+    const size_t aws = ws_bytes - (size_t)(w - (char*)ws);
+    csa_host::AttnRows rs{1, a->kv, Nc, 0, 1, idx, a->topk, a->kv_raw, a->W, a->L - a->W, a->W};
+    rc = csa_host::attn_launch(a->csa_q, rs, a->B, 1, a->H, a->D, p, a->scale, a->csa_out, a->csa_lse, w, aws, st,
+                               "k_attn_sparse");
+    if (rc) return rc;
+    csa_host::AttnRows rd{0, a->kv_h, Nh, a->L, a->mh, nullptr, 0, nullptr, 0, 0, 0};
+    return csa_host::attn_launch(a->hca_q, rd, a->B, 1, a->H, a->D, p, a->scale, a->hca_out, a->hca_lse, w, aws, st,
+                                 "k_attn_dense");
+}
+
+// Diagnostic: fp8 (OCP e4m3) -> bf16 conversion exactly as the indexer kernel does it.
+int csa_debug_fp8_to_bf16(const void* in, void* out, int n, void* stream) {
+    const char* fn = "csa_debug_fp8_to_bf16";
+    csa_host::g_err[0] = 0;
+    REQ_PTR(in);
+    REQ_PTR(out);
+    REQ(n >= 0 && n % 4 == 0, CSA_ERR_SHAPE, "%s: n must be a non-negative multiple of 4", fn);
+    if (n == 0) return CSA_OK;
+    return csa_host::fp8_to_bf16_launch(in, out, n, (hipStream_t)stream);
+}
+
+int csa_prof_enable(int on) {
+    std::lock_guard<std::mutex> lk(csa_host::g_prof_mu);
+    csa_host::g_prof_on = on != 0;
+    return CSA_OK;
+}
+
+int csa_prof_reset(void) {
+    std::lock_guard<std::mutex> lk(csa_host::g_prof_mu);
+    for (auto& r : csa_host::g_prof) {
+        (void)hipEventSynchronize(r.b);
+        csa_host::g_ev_pool.push_back(r.a);
+        csa_host::g_ev_pool.push_back(r.b);
+    }
+    csa_host::g_prof.clear();
+    return CSA_OK;
+}
+
+int csa_prof_read(const char* kernel, double* total_ms, int* launches) {
+    const char* fn = "csa_prof_read";
+    if (!kernel || !total_ms || !launches) return fail(CSA_ERR_NULL, "%s: NULL argument", fn);
+    std::lock_guard<std::mutex> lk(csa_host::g_prof_mu);
+    double t = 0;
+    int n = 0;
+    for (auto& r : csa_host::g_prof) {
+        if (r.name != kernel) continue;
+        if (hipEventSynchronize(r.b) != hipSuccess) return fail(CSA_ERR_HIP, "%s: event sync failed", fn);
+        float ms = 0;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(CSA_ERR_HIP, "%s: elapsed time failed", fn);
+        t += ms;
+        ++n;
+    }
+    *total_ms = t;
+    *launches = n;
+    return CSA_OK;
+}
+
+}  // extern "C"

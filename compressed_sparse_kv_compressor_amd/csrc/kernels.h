@@ -1,0 +1,40 @@
+// kernels.h -- host-side launchers shared between the translation units of libcsa.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <algorithm>
+
+namespace csa_host {
+
+size_t index_topk_ws_bytes(int B, int Tq, int Nc);
+int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
+                      int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
+                      int32_t* idx_out, int32_t* cnt_out, void* ws, hipStream_t st);
+int fp8_to_bf16_launch(const void* in, void* out, int n, hipStream_t st);
+
+// Row sets of the split-KV attention: dense over a visible prefix (HCA), or
+// gathered entries followed by raw window rows (CSA).
+struct AttnRows {
+    int mode;                 // 0 = dense prefix, 1 = selected + window
+    const void* kv;           // [B][N][D]
+    int N;                    // entries per sequence in kv
+    long long L;              // raw tokens (dense visibility)
+    int ratio;                // compression ratio (dense visibility)
+    const int32_t* idx;       // [B][Tq][topk] (mode 1)
+    int topk;
+    const void* kv_raw;       // [B][Lr][D] (mode 1)
+    int Lr;
+    long long raw0;
+    int W;
+};
+size_t attn_ws_bytes(int B, int Tq, int H, int D, int max_rows);
+int attn_launch(const void* q, const AttnRows& rows, int B, int Tq, int H, int D, long long pos0, float scale,
+                void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t st, const char* tag);
+
+size_t compress_ws_bytes(int B, long long L, int Dh, int m);
+int compress_launch(const void* hidden, const void* w_kv, const void* w_ik, const float* w_gate,
+                    const float* b_slot, int B, long long L, int Dh, int D, int dI, int m, int W,
+                    int ik_dtype, void* kv_out, void* ik_out, void* win_out, void* ws, hipStream_t st);
+
+}  // namespace csa_host

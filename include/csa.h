@@ -198,6 +198,15 @@ size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a);
 int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+/* Converts n OCP-e4m3 values (n % 4 == 0) to bf16 with the exact conversion
+ * the indexer kernels apply to e4m3 keys and queries (every e4m3 value is a
+ * bf16 value, so the result must equal the code's value).  in [n] e4m3,
+ * out [n] bf16, both device pointers. */
+int csa_debug_fp8_to_bf16(const void* in, void* out, int n, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing (measurement aid; not part of the method)                   */
 /* ------------------------------------------------------------------------ */
 /* While enabled, every kernel the library launches is bracketed by a pair of

@@ -1,0 +1,122 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+function include/csa.h declares, sizes workspaces on the host, and rejects bad
+arguments with the documented status codes before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+LIB = os.path.join(ROOT, "compressed_sparse_kv_compressor_amd", "libcsa.so")
+
+CSA_OK, CSA_ERR_NULL, CSA_ERR_SHAPE, CSA_ERR_DTYPE, CSA_ERR_ALIGN, CSA_ERR_WORKSPACE, CSA_ERR_UNSUPPORTED = range(7)
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not os.path.exists(LIB):
+        from compressed_sparse_kv_compressor_amd import build
+        build.build()
+    from compressed_sparse_kv_compressor_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_][a-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("csa_", "hca_"))))
+
+
+def test_every_declared_symbol_is_exported(b):
+    names = declared_functions()
+    assert len(names) >= 15, names
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in csa.h but not exported"
+    assert set(names) == set(b.EXPORTED)
+
+
+def test_version_and_status_strings(b):
+    assert b.lib.csa_abi_version() == 1
+    assert b.lib.csa_status_str(CSA_ERR_WORKSPACE) == b"CSA_ERR_WORKSPACE"
+    assert b.lib.csa_status_str(99) == b"CSA_ERR_UNKNOWN"
+
+
+def test_workspace_sizes_are_host_arithmetic(b):
+    lib = b.lib
+    assert lib.csa_index_topk_ws_bytes(8, 1, 262144) > 8 * 262144 * 4
+    assert lib.csa_index_topk_ws_bytes(0, 1, 10) == 0
+    assert lib.csa_sparse_attn_ws_bytes(8, 1, 128, 512, 1024, 128) > 0
+    assert lib.hca_dense_attn_ws_bytes(1, 1, 16, 128, 32) == 0          # one split: no partials
+    assert lib.csa_compress_ws_bytes(4, 65536, 4096, 4) == 4 * 16384 * 4096 * 2
+
+
+A16 = ctypes.c_void_p(16 * 1000)       # aligned, never dereferenced (validation fails first)
+BAD = ctypes.c_void_p(16 * 1000 + 2)   # misaligned
+
+
+def test_index_topk_validation_codes(b):
+    lib = b.lib
+    f = lib.csa_index_topk
+    good = dict(q=A16, w=A16, k=A16, dt=0, B=1, Tq=1, HI=8, dI=128, Nc=1024, L=4096, m=4, pos0=4095, topk=64,
+                idx=A16, cnt=None, ws=A16, wsb=10 ** 9)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return f(a["q"], a["w"], a["k"], a["dt"], a["B"], a["Tq"], a["HI"], a["dI"], a["Nc"], a["L"], a["m"],
+                 a["pos0"], a["topk"], a["idx"], a["cnt"], a["ws"], a["wsb"], None)
+
+    assert call(q=None) == CSA_ERR_NULL
+    assert call(k=BAD) == CSA_ERR_ALIGN
+    assert call(dt=7) == CSA_ERR_DTYPE
+    assert call(Nc=1000) == CSA_ERR_SHAPE                 # not ceil(L/m)
+    assert call(pos0=4096) == CSA_ERR_SHAPE               # query beyond the context
+    assert call(topk=0) == CSA_ERR_SHAPE
+    assert call(HI=3) == CSA_ERR_UNSUPPORTED
+    assert call(dI=96) == CSA_ERR_UNSUPPORTED
+    assert call(topk=5000) == CSA_ERR_UNSUPPORTED
+    assert call(wsb=10) == CSA_ERR_WORKSPACE
+    assert b"workspace" in lib.csa_last_error()
+    assert call(ws=None) == CSA_ERR_NULL
+
+
+def test_attention_validation_codes(b):
+    lib = b.lib
+    sp = lib.csa_sparse_attn
+    # q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse, ws, wsb, stream
+    assert sp(A16, A16, A16, A16, 1, 1, 16, 96, 10, 4, 8, 0, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_UNSUPPORTED
+    assert sp(A16, A16, A16, A16, 1, 1, 24, 128, 10, 4, 8, 0, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_UNSUPPORTED
+    assert sp(A16, A16, A16, None, 1, 1, 16, 128, 10, 4, 8, 0, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_NULL
+    # window needs raw rows starting at 4 but they start at 5
+    assert sp(A16, A16, A16, A16, 1, 1, 16, 128, 10, 4, 8, 5, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
+    # window needs position 7 but rows end at 6
+    assert sp(A16, A16, A16, A16, 1, 1, 16, 128, 10, 4, 7, 0, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
+    assert sp(A16, A16, A16, A16, 1, 1, 16, 128, 10, 4, 8, 0, 7, 4, float("nan"), A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
+    de = lib.hca_dense_attn
+    # q, kv_h, B, Tq, H, D, Nh, L, mh, pos0, scale, out, lse, ws, wsb, stream
+    assert de(A16, A16, 1, 1, 16, 128, 31, 4096, 128, 4095, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
+    assert de(A16, None, 1, 1, 16, 128, 32, 4096, 128, 4095, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_NULL
+    assert de(A16, A16, 1, 1, 16, 128, 32, 4096, 128, 4095, 0.1, BAD, None, A16, 10 ** 9, None) == CSA_ERR_ALIGN
+
+
+def test_compress_and_decode_validation_codes(b):
+    lib = b.lib
+    c = lib.csa_compress
+    # hidden, w_kv, w_ik, w_gate, b_slot, B, L, Dh, D, dI, m, W, ik_dtype, kv, ik, win, ws, wsb, stream
+    assert c(A16, A16, None, A16, None, 1, 100, 100, 128, 0, 4, 0, 0, A16, None, None, A16, 10 ** 9, None) == CSA_ERR_UNSUPPORTED
+    assert c(A16, A16, A16, A16, None, 1, 100, 128, 128, 64, 4, 0, 0, A16, None, None, A16, 10 ** 9, None) == CSA_ERR_NULL
+    assert c(A16, A16, None, A16, None, 1, 100, 128, 128, 0, 4, 8, 0, A16, None, None, A16, 10 ** 9, None) == CSA_ERR_NULL
+    assert c(A16, A16, None, A16, None, 1, 100, 128, 128, 0, 4, 0, 5, A16, None, None, A16, 10 ** 9, None) == CSA_ERR_DTYPE
+    assert c(A16, A16, None, A16, None, 1, 100, 128, 128, 0, 4, 0, 0, A16, None, None, A16, 10, None) == CSA_ERR_WORKSPACE
+    args = b.DecodeArgs(B=1, L=4096, H=16, D=128, scale=0.1, csa_q=A16, q_idx=A16, w_idx=A16, k_idx=A16, kv=A16,
+                        kv_raw=A16, idx_dtype=0, HI=4, dI=64, m=4, topk=64, W=128, csa_out=A16, csa_lse=None,
+                        idx_out=None, hca_q=A16, kv_h=None, mh=128, hca_out=A16, hca_lse=None)
+    assert lib.csa_hca_decode(ctypes.byref(args), A16, 10 ** 9, None) == CSA_ERR_NULL
+    assert lib.csa_hca_decode(None, A16, 10 ** 9, None) == CSA_ERR_NULL
+    args.kv_h = A16
+    assert lib.csa_hca_decode(ctypes.byref(args), A16, 16, None) == CSA_ERR_WORKSPACE
+    assert lib.csa_hca_decode_ws_bytes(ctypes.byref(args)) > 16
