@@ -1,0 +1,224 @@
+"""Benchmark: one interleaved CSA + HCA decode pair at 1M context on one MI355X.
+
+Workload (decode_b8_1m): 8 sequences x 1,048,576 raw tokens, one query token
+each.  CSA layer: m = 4 -> 262,144 compressed entries per sequence, OCP-e4m3
+indexer keys (8 heads x 128), top-k = 1024, 128-token raw window, MQA with
+128 query heads x 512.  HCA layer: m' = 128 -> 8,192 entries, dense MQA.
+A step is one csa_hca_decode call (indexer scores -> top-k -> sparse attention
+-> dense attention) over one batch; inputs are resident in HBM.  Three copies
+of every input rotate across steps so that the 256 MB Infinity Cache cannot
+serve a step from the previous one.
+
+Prints one JSON line: queries/s (value), the indexer-score kernel's achieved
+HBM bandwidth against the 8 TB/s peak (roofline), and the CPU oracle timed on
+a bounded sample of the same workload (cpu_baseline), plus a sampled parity
+check of that sample against the GPU result.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA+HCA decode queries/s & HBM GB/s at 1M ctx; indexer prefill TFLOP/s"
+HBM_PEAK_GBPS = 8000.0
+DOMINANT = "k_score"
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("index_topk.hip", "common.h", "exact_dot.h"):
+        with open(os.path.join(ROOT, "compressed_sparse_kv_compressor_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(per_launch_alg_bytes):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "k_score_decode_b8_1m_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_src_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from compressed_sparse_kv_compressor_amd import binding as b
+    from compressed_sparse_kv_compressor_amd import synth
+    from compressed_sparse_kv_compressor_amd.configs import DECODE_B8_1M as cfg
+
+    dev = torch.device("cuda:0")
+    B, H, D, L, HI, dI = cfg.B, cfg.H, cfg.D, cfg.L, cfg.HI, cfg.dI
+    Nc, Nh, W, topk = cfg.Nc, cfg.Nh, cfg.W, cfg.topk
+    es = 1 if cfg.idx_dtype == 1 else 2
+    t0 = time.time()
+    g = synth.parallel_bits_to_device
+    base = dict(
+        q_idx=g(0, "q_idx", (B, 1, HI, dI), dI ** -0.5, cfg.idx_dtype, dev),
+        k_idx=g(0, "k_idx", (B, Nc, dI), dI ** -0.5, cfg.idx_dtype, dev),
+        csa_q=g(0, "csa_q", (B, H, D), D ** -0.5, 0, dev),
+        kv=g(0, "kv", (B, Nc, D), D ** -0.5, 0, dev),
+        raw=g(0, "raw", (B, W, D), D ** -0.5, 0, dev),
+        hca_q=g(0, "hca_q", (B, H, D), D ** -0.5, 0, dev),
+        kv_h=g(0, "kv_h", (B, Nh, D), D ** -0.5, 0, dev),
+    )
+    base["w_idx"] = torch.from_numpy(synth.half_normal_f32(0, "w_idx", (B, 1, HI), HI ** -0.5)).to(dev)
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.copies - 1)]
+    gen_s = time.time() - t0
+
+    outs = []
+    dargs = []
+    for c in copies:
+        csa_out = torch.empty((B, H, D), dtype=torch.int16, device=dev)
+        hca_out = torch.empty((B, H, D), dtype=torch.int16, device=dev)
+        idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+        outs.append((csa_out, hca_out, idx))
+        dargs.append(b.make_decode_args(L=L, scale=cfg.scale, csa_q=c["csa_q"], q_idx=c["q_idx"], w_idx=c["w_idx"],
+                                        k_idx=c["k_idx"], kv=c["kv"], kv_raw=c["raw"], idx_dtype=cfg.idx_dtype,
+                                        m=cfg.m, topk=topk, W=W, csa_out=csa_out, hca_q=c["hca_q"], kv_h=c["kv_h"],
+                                        mh=cfg.mh, hca_out=hca_out, idx_out=idx))
+    ws = b.workspace(b.csa_hca_decode_ws_bytes(dargs[0]), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        b.csa_hca_decode(dargs[i % len(dargs)], ws=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    b.prof_reset()
+    b.prof_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    b.prof_enable(False)
+    kern = {}
+    for name in ("k_fill", "k_score", "k_refine1", "k_refine2", "k_classify", "k_finalize", "k_attn_sparse",
+                 "k_attn_dense", "k_combine"):
+        ms, n = b.prof_read(name)
+        if n:
+            kern[name] = round(ms / n * 1000.0, 2)      # average microseconds per launch
+    ms_step = elapsed / args.steps * 1e3
+    value = B * args.steps / elapsed
+
+    # algorithmic bytes (every input read once, outputs written once)
+    score_bytes = B * Nc * dI * es + B * HI * dI * es + B * HI * 4
+    step_bytes = (score_bytes + B * (topk + W) * D * 2 + 2 * B * H * D * 2 + B * Nh * D * 2 + 2 * B * H * D * 2)
+    score_us = kern.get(DOMINANT)
+    achieved = score_bytes / (score_us * 1e-6) / 1e9 if score_us else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "L": L, "H": H, "D": D, "m": cfg.m, "mh": cfg.mh, "topk": topk,
+                   "W": W, "HI": HI, "dI": dI, "idx_dtype": "e4m3" if cfg.idx_dtype else "bf16",
+                   "parallelism": "single-gpu", "input_copies": args.copies},
+        "step_algorithmic_bytes": step_bytes,
+        "step_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "kernel_us": kern,
+        "roofline": {"bound": "hbm", "kernel": DOMINANT,
+                     "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
+                     "traffic": load_traffic(score_bytes), "algorithmic_bytes_per_launch": score_bytes},
+        "input_gen_s": round(gen_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        out.update(cpu_leg(cfg, base, outs[0], dev))
+    print(json.dumps(out), flush=True)
+
+
+def cpu_leg(cfg, x, gpu_out, dev):
+    """The oracle on one sequence of the same workload (bounded CPU sample) and
+    a parity check of the GPU's result for that sequence."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    B, H, D, L, W, topk = cfg.B, cfg.H, cfg.D, cfg.L, cfg.W, cfg.topk
+    bsel = 0
+    u16 = lambda t: t.cpu().numpy().view(np.uint16)
+    dt = cfg.idx_dtype
+    kbits = (lambda t: t.cpu().numpy()) if dt == 1 else u16
+    q_idx = kbits(x["q_idx"][bsel:bsel + 1])
+    w_idx = x["w_idx"][bsel:bsel + 1].cpu().numpy()
+    k_idx = kbits(x["k_idx"][bsel:bsel + 1])
+    csa_q = u16(x["csa_q"][bsel:bsel + 1]).reshape(1, 1, H, D)
+    raw = u16(x["raw"][bsel:bsel + 1])
+    hca_q = u16(x["hca_q"][bsel:bsel + 1]).reshape(1, 1, H, D)
+    kv_h = u16(x["kv_h"][bsel:bsel + 1])
+    p = L - 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    idx, cnt, _, _ = oracle.index_topk(q_idx, w_idx, k_idx, L, cfg.m, p, topk, dt)
+    t_index = time.perf_counter() - t0
+    rows = torch.from_numpy(idx[0, 0].astype(np.int64)).to(dev)
+    kv_sel = u16(x["kv"][bsel].index_select(0, rows)).reshape(1, topk, D)
+    local = np.arange(topk, dtype=np.int32).reshape(1, 1, topk)
+    t1 = time.perf_counter()
+    o_csa, _ = oracle.sparse_attn(csa_q, kv_sel, local, raw, L - W, p, W, cfg.scale)
+    o_hca, _ = oracle.dense_attn(hca_q, kv_h, L, cfg.mh, p, cfg.scale)
+    t_attn = time.perf_counter() - t1
+    total = t_index + t_attn
+
+    csa_out, hca_out, gidx = gpu_out
+    g_idx = gidx[bsel].cpu().numpy()
+
+    def rel(got, want):
+        g = (got.cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        g = g.reshape(-1, D)
+        o = want.reshape(-1, D)
+        return float((np.abs(g - o).max(1) / np.abs(o).max(1)).max())
+
+    return {
+        "cpu_baseline": {"value": round(1.0 / total, 4), "unit": "queries/s", "cores": threads, "kind": "oracle",
+                         "sample": f"sequence 0 of {cfg.name}: indexer over all {cfg.Nc} entries + top-{topk} + "
+                                   f"CSA attention ({topk}+{W} rows) + HCA attention ({cfg.Nh} rows), 1 query",
+                         "seconds": round(total, 2), "index_s": round(t_index, 2), "attn_s": round(t_attn, 2)},
+        "parity_sample": {"topk_bit_exact": bool(np.array_equal(g_idx, idx[0, 0])),
+                          "csa_max_row_rel_err": rel(csa_out[bsel], o_csa), "hca_max_row_rel_err": rel(hca_out[bsel], o_hca),
+                          "tolerance": 2e-2},
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -152,3 +152,30 @@ def normal_bits_to_device(seed, name, shape, scale, dtype, device, heavy=False):
         t = t.to(torch.bfloat16).view(torch.int16) if dtype == 0 else t.to(torch.float8_e4m3fn).view(torch.uint8)
         out[s:e].copy_(t)
     return out.view(*shape)
+
+
+def parallel_bits_to_device(seed, name, shape, scale, dtype, device, workers=8):
+    """Like normal_bits_to_device but each 2^24-element chunk has its own
+    substream (seed, crc32(name), chunk), generated by a thread pool: the large
+    caches of the 1M-context workloads fill in seconds.  Values differ from the
+    single-stream generators; use the same function on both sides."""
+    import concurrent.futures as cf
+    n = int(np.prod(shape))
+    tdt = torch.int16 if dtype == 0 else torch.uint8
+    out = torch.empty(n, dtype=tdt, device=device)
+    starts = list(range(0, n, _CHUNK))
+
+    def gen(ci):
+        s = starts[ci]
+        e = min(n, s + _CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), zlib.crc32(name.encode()), ci])))
+        x = g.standard_normal(e - s, dtype=np.float32)
+        x *= np.float32(scale)
+        t = torch.from_numpy(x)
+        return t.to(torch.bfloat16).view(torch.int16) if dtype == 0 else t.to(torch.float8_e4m3fn).view(torch.uint8)
+
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        for ci, t in enumerate(ex.map(gen, range(len(starts)))):
+            s = starts[ci]
+            out[s:s + t.numel()].copy_(t)
+    return out.view(*shape)
