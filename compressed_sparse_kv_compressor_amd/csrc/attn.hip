@@ -216,6 +216,314 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
     }
 }
 
+// ---------------------------------------------------------------------------
+// k_attn32 (D = 512, H % 32 == 0): a wave owns 32 heads (v_mfma_f32_32x32x16_bf16),
+// so every K / V byte read from LDS feeds 32 heads, the balance point of the
+// LDS-read and MFMA rates of a CU.  Waves work in pairs over the two halves of
+// D: each computes the partial scores of its 256 dims, the pair exchanges them
+// through LDS (summed in a fixed order, so both hold identical S), and each
+// accumulates O only for its own half -- 128 accumulators and 64 Q registers
+// per lane, two workgroups per CU.  The two pairs of a workgroup take the two
+// halves of the split's rows and merge (m, l, O) in LDS at the end.  Tiles are
+// unpadded and XOR-swizzled per 16-byte chunk (conflict-free row reads and
+// transposed reads).  1D grid, XCD-aware: the H/32 head-group workgroups that
+// read the same rows land on the same XCD (workgroup i runs on XCD i mod 8).
+// ---------------------------------------------------------------------------
+constexpr int HD = 256;   // d-half handled by one wave
+
+// 16-byte chunk c of row r is stored at chunk c ^ f(r & 15), f(x) = 4 (x & 3) + (x >> 2): any 16
+// consecutive rows at one chunk, and any 4 aligned rows x 4 aligned chunks (the footprint of a
+// transposed read), fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_chunk(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int r, int c) {   // element offset of (row, col) in a [32][256] tile
+    return r * HD + (((c >> 3) ^ swz_chunk(r)) << 3) + (c & 7);
+}
+
+#ifndef CSA_ATTN32_WAVES_PER_EU
+#define CSA_ATTN32_WAVES_PER_EU 1
+#endif
+// MODE 0: dense prefix (row r = entry r); MODE 1: selected entries then window rows.
+template <int MODE>
+__global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
+    const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
+    int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
+    float* __restrict__ lse)
+{
+    constexpr int D = 512;
+    constexpr int KS = HD / 16;               // 32x32x16 k-steps over a d-half
+    constexpr int DT = HD / 32;               // 32-wide d tiles of a d-half
+    __shared__ __attribute__((aligned(16))) uint16_t bufA[4 * TILE * HD];     // 64 KiB: tile buffer 0 of each wave
+    __shared__ __attribute__((aligned(16))) uint16_t bufB[4 * TILE * HD];     // 64 KiB: tile buffer 1 of each wave
+    __shared__ __attribute__((aligned(16))) float sx[4][16][64];              // 16 KiB
+
+    const int HG = H / 32;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int hg = slot % HG, unit = (slot / HG) * 8 + xcd;
+    if (unit >= nunits) return;                // padding workgroups (uniform exit)
+    const int bt = unit / nsplit, split = unit % nsplit;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    const int pr = w & 1, dh = w >> 1;         // row half, d half
+    const int hl = lane & 31, g = lane >> 5;
+    const int h = hg * 32 + hl;
+    uint16_t* const ta = bufA + w * (TILE * HD);
+    uint16_t* const tb = bufB + w * (TILE * HD);
+
+    const int b = bt / Tq;
+    const long long p = pos0 + bt % Tq;
+    int nrows;
+    long long w0 = 0;
+    if (MODE == 0) {
+        nrows = dense_visible(p, R.L, R.ratio, R.N);
+    } else {
+        w0 = p - R.W + 1 < 0 ? 0 : p - R.W + 1;
+        nrows = R.topk + (R.W > 0 ? (int)(p - w0 + 1) : 0);
+    }
+    const int s_begin = split * rps;
+    const int s_end = min(nrows, s_begin + rps);
+    const int per_pair = rps / 2;              // multiple of TILE
+    const int r_begin = s_begin + pr * per_pair;
+    const int r_end = min(s_end, r_begin + per_pair);
+    const int ntiles = per_pair / TILE;        // same count for every wave (barriers inside)
+
+    const uint16_t* kvb = R.kv ? R.kv + (size_t)b * R.N * D : nullptr;
+    const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
+    const uint16_t* fallback = kvb ? kvb : rawb;          // a valid row for masked slots
+
+    // Row code of row r: >= 0 entry index in kv, <= -2 raw row (-code-2), -1 masked.
+    auto row_code = [&](int r) -> int {
+        if (r >= r_end) return -1;
+        if constexpr (MODE == 0) {
+            return r;
+        } else {
+            if (r < R.topk) return R.idx[(size_t)bt * R.topk + r];    // (< 0 -> masked)
+            return -2 - (int)(w0 + (r - R.topk) - R.raw0);
+        }
+    };
+    auto row_ptr = [&](int c) -> const uint16_t* {
+        if (c >= 0) return kvb + (size_t)c * D;
+        if constexpr (MODE == 0) {
+            return nullptr;
+        } else {
+            if (c == -1) return nullptr;
+            return rawb + (size_t)(-c - 2) * D;
+        }
+    };
+
+    bf16x8_t qreg[KS];
+    {
+        const uint16_t* qp = q + ((size_t)bt * H + h) * D + dh * HD + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qreg[s] = as_bf16x8(*(const u32x4_t*)(qp + 16 * s));
+    }
+    f32x16_t acc[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int b16 = lane >> 4, j16 = lane & 15;
+    const int tr_row = 4 * (b16 >> 1) + (j16 >> 2);
+    const int tr_col = 16 * (b16 & 1) + 4 * (j16 & 3);
+    const int rsub = lane >> 5, pch = lane & 31;
+
+    // codes of the lane's 16 rows (2 i + rsub) of tile it
+    int code[TILE / 2];
+    auto fetch_codes = [&](int it) {
+        if constexpr (MODE == 0) {
+            code[0] = r_begin + it * TILE;                            // dense: the tile's first row
+        } else {
+#pragma unroll
+            for (int i = 0; i < TILE / 2; ++i) code[i] = row_code(r_begin + it * TILE + 2 * i + rsub);
+        }
+    };
+    // Direct global->LDS loads (16 B per lane; lane l lands at base + 16 l): one
+    // instruction moves rows (2i, 2i+1) of this d-half; the XOR swizzle goes on
+    // the source address.  Masked rows read a valid row and are excluded by the
+    // returned validity mask.  Issues no other memory operation.
+    auto issue_tile = [&](uint16_t* buf) -> uint32_t {
+        if constexpr (MODE == 0) {
+            // dense rows are consecutive entries starting at code[0] (wave-uniform)
+            const int first = code[0];
+            const int nval = max(0, min(TILE, r_end - first));
+            const uint16_t* base = kvb + (size_t)(nval > 0 ? first : 0) * D + dh * HD;
+#pragma unroll
+            for (int i = 0; i < TILE / 2; ++i) {
+                const int row = 2 * i + rsub;
+                const int rr = row < nval ? row : 0;                  // past the end: reread row 0 (masked)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(base + (size_t)rr * D + ((pch ^ swz_chunk(row)) << 3)),
+                    (CSA_LDS void*)(buf + i * 2 * HD), 16, 0, 0);
+            }
+            return nval >= 32 ? 0xffffffffu : ((1u << nval) - 1u);
+        }
+        uint32_t vm = 0;
+#pragma unroll
+        for (int i = 0; i < TILE / 2; ++i) {
+            const int row = 2 * i + rsub;
+            const uint16_t* src = row_ptr(code[i]);
+            const unsigned long long bal = __ballot(src != nullptr);
+            vm |= (uint32_t)(bal & 1ull) << (2 * i);
+            vm |= (uint32_t)((bal >> 32) & 1ull) << (2 * i + 1);
+            const uint16_t* s8 = (src ? src : fallback) + dh * HD + ((pch ^ swz_chunk(row)) << 3);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)s8,
+                                             (CSA_LDS void*)(buf + i * 2 * HD), 16, 0, 0);
+        }
+        return vm;
+    };
+
+    // Compute on one tile; the loads of the next tile (into the other LDS object) stay in flight.
+    auto compute_tile = [&](const uint16_t* tile, uint32_t vmask) {
+        const CSA_LDS uint16_t* tl = (const CSA_LDS uint16_t*)tile;
+        // ---- partial S^T[32 rows][32 heads] over this d-half ----
+        f32x16_t sacc, sacc1;                    // two chains: even / odd k-steps
+#pragma unroll
+        for (int j = 0; j < 16; ++j) { sacc[j] = 0.f; sacc1[j] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < KS; s += 2) {
+            const bf16x8_t a0 = as_bf16x8(*(const u32x4_t*)(tile + swz(hl, 16 * s + 8 * g)));
+            const bf16x8_t a1 = as_bf16x8(*(const u32x4_t*)(tile + swz(hl, 16 * (s + 1) + 8 * g)));
+            sacc = mfma32_bf16(a0, qreg[s], sacc);
+            sacc1 = mfma32_bf16(a1, qreg[s + 1], sacc1);
+        }
+        sacc += sacc1;
+        // ---- exchange with the other d-half of the pair; S = S_dh0 + S_dh1 in both ----
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sx[w][j][lane] = sacc[j];
+        __syncthreads();
+        float x[16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float o = sx[w ^ 2][j][lane];
+            const float sv = dh == 0 ? sacc[j] + o : o + sacc[j];
+            const int row = 8 * (j >> 2) + 4 * g + (j & 3);
+            x[j] = ((vmask >> row) & 1u) ? sv * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, x[j]);
+        }
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        // rescale only when the running max grows by more than 2^8 (exact: the
+        // reference point of the exponentials is free; p stays <= 256)
+        if (mx > m_run + 8.0f) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mx);   // 0 on the first tile
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < DT; ++d) acc[d] *= alpha;
+            m_run = mx;
+        }
+        float pv[16], ps = 0.f;
+        if (m_run == -INFINITY) {                // nothing valid yet: all probabilities are 0
+#pragma unroll
+            for (int j = 0; j < 16; ++j) pv[j] = 0.f;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                pv[j] = __builtin_amdgcn_exp2f(x[j] - m_run);   // argument <= 8; -inf -> 0
+                ps += pv[j];
+            }
+        }
+        ps += shfl_xor_f(ps, 32);
+        l_run += ps;
+        u32x4_t pw0, pw1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pw0[j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+            pw1[j] = pack_bf16x2(pv[8 + 2 * j], pv[8 + 2 * j + 1]);
+        }
+        const bf16x8_t pb0 = as_bf16x8(pw0), pb1 = as_bf16x8(pw1);
+        // ---- O^T[d-half][h] += V^T P^T (rows in two k-steps of 16) ----
+        typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) {
+            const int c0 = d * 32 + tr_col;
+            const u32x2_t w0r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4_t*)(tl + swz(tr_row, c0))));
+            const u32x2_t w1r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4_t*)(tl + swz(8 + tr_row, c0))));
+            const u32x2_t w2r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4_t*)(tl + swz(16 + tr_row, c0))));
+            const u32x2_t w3r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4_t*)(tl + swz(24 + tr_row, c0))));
+            acc[d] = mfma32_bf16(as_bf16x8(u32x4_t{w0r[0], w0r[1], w1r[0], w1r[1]}), pb0, acc[d]);
+            acc[d] = mfma32_bf16(as_bf16x8(u32x4_t{w2r[0], w2r[1], w3r[0], w3r[1]}), pb1, acc[d]);
+        }
+    };
+
+    uint32_t vm_a = 0, vm_b = 0;
+    if (ntiles > 0) {
+        fetch_codes(0);
+        vm_a = issue_tile(ta);
+        if (ntiles > 1) fetch_codes(1);
+    }
+    for (int it = 0; it < ntiles; it += 2) {
+        __builtin_amdgcn_s_waitcnt(0);           // tile it (buffer A) and the codes of tile it+1 have landed
+        __builtin_amdgcn_wave_barrier();
+        if (it + 1 < ntiles) {
+            vm_b = issue_tile(tb);
+            if (it + 2 < ntiles) fetch_codes(it + 2);
+        }
+        compute_tile(ta, vm_a);
+        __syncthreads();                         // sx reuse; buffer A is reloaded next
+        if (it + 1 < ntiles) {                   // workgroup-uniform
+            __builtin_amdgcn_s_waitcnt(0);       // tile it+1 (buffer B) and the codes of tile it+2
+            __builtin_amdgcn_wave_barrier();
+            if (it + 2 < ntiles) {
+                vm_a = issue_tile(ta);
+                if (it + 3 < ntiles) fetch_codes(it + 3);
+            }
+            compute_tile(tb, vm_b);
+            __syncthreads();
+        }
+    }
+
+    // ---- merge the two row halves: wave (pr=0, dh) += wave (pr=1, dh) ----
+    float* ob = (float*)bufA;                  // [2][DT*16][64] floats = 64 KiB
+    if (pr == 1) {
+        float* dst = ob + (size_t)dh * DT * 16 * 64;
+#pragma unroll
+        for (int d = 0; d < DT; ++d)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) dst[(d * 16 + j) * 64 + lane] = acc[d][j];
+        if (g == 0) { sx[dh][0][hl] = m_run; sx[dh][1][hl] = l_run; }
+    }
+    __syncthreads();
+    if (pr == 1) return;
+    {
+        const float* src = ob + (size_t)dh * DT * 16 * 64;
+        const float mo = sx[dh][0][hl], lo = sx[dh][1][hl];
+        const float M = fmaxf(m_run, mo);
+        const float fa = M == -INFINITY ? 0.f : exp2f(m_run - M);
+        const float fb = M == -INFINITY ? 0.f : exp2f(mo - M);
+#pragma unroll
+        for (int d = 0; d < DT; ++d)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[d][j] = acc[d][j] * fa + src[(d * 16 + j) * 64 + lane] * fb;
+        l_run = l_run * fa + lo * fb;
+        m_run = M;
+    }
+    // lane holds O^T[dh*256 + d*32 + 8 (j/4) + 4 g + j%4][h]
+    if (nsplit == 1) {
+        const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+        uint16_t* op = out + ((size_t)bt * H + h) * D + dh * HD + 4 * g;
+#pragma unroll
+        for (int d = 0; d < DT; ++d)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                uint2 v;
+                v.x = pack_bf16x2(acc[d][4 * q4] * inv, acc[d][4 * q4 + 1] * inv);
+                v.y = pack_bf16x2(acc[d][4 * q4 + 2] * inv, acc[d][4 * q4 + 3] * inv);
+                *(uint2*)(op + d * 32 + 8 * q4) = v;
+            }
+        if (lse && g == 0 && dh == 0) lse[(size_t)bt * H + h] = l_run > 0.f ? (m_run + log2f(l_run)) * LN2 : -INFINITY;
+    } else {
+        const size_t sl = ((size_t)bt * nsplit + split) * H + h;
+        float* op = part_o + sl * D + dh * HD + 4 * g;
+#pragma unroll
+        for (int d = 0; d < DT; ++d)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *(f32x4_t*)(op + d * 32 + 8 * q4) = f32x4_t{acc[d][4 * q4], acc[d][4 * q4 + 1], acc[d][4 * q4 + 2],
+                                                            acc[d][4 * q4 + 3]};
+        if (g == 0 && dh == 0) part_ml[sl] = make_float2(m_run, l_run);
+    }
+}
+
 // Merge split partials in split order: out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.
 template <int D>
 __global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
@@ -249,9 +557,23 @@ namespace csa_host {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Split count: enough workgroups to cover the chip twice, splits of >= 64 rows.
-static void choose_split(int BT, int HG, int max_rows, int* nsplit, int* rps) {
-    if (max_rows <= 0) { *nsplit = 1; *rps = 32; return; }
+// Split counts.  k_attn (16 heads per wave): enough workgroups to cover the
+// chip twice, splits of >= 64 rows.  k_attn32 (32 heads per wave, one
+// workgroups per CU): about one workgroup per CU, whole 32-row tiles per wave pair.
+static bool use32(int D, int H) { return D == 512 && H % 32 == 0; }
+
+static void choose_split(int BT, int H, int D, int max_rows, int* nsplit, int* rps) {
+    if (max_rows <= 0) { *nsplit = 1; *rps = 128; return; }
+    if (use32(D, H)) {
+        const int HG = H / 32;
+        int ns = std::max(1, 256 / (BT * HG));
+        int r = (max_rows + ns - 1) / ns;
+        r = (r + 2 * TILE - 1) / (2 * TILE) * (2 * TILE);
+        *rps = r;
+        *nsplit = (max_rows + r - 1) / r;
+        return;
+    }
+    const int HG = (H + 63) / 64;
     const int target = 512;
     int ns = (target + BT * HG - 1) / (BT * HG);
     const int cap = std::max(1, (max_rows + 63) / 64);
@@ -263,9 +585,9 @@ static void choose_split(int BT, int HG, int max_rows, int* nsplit, int* rps) {
 }
 
 size_t attn_ws_bytes(int B, int Tq, int H, int D, int max_rows) {
-    const int BT = B * Tq, HG = (H + 63) / 64;
+    const int BT = B * Tq;
     int ns, rps;
-    choose_split(BT, HG, max_rows, &ns, &rps);
+    choose_split(BT, H, D, max_rows, &ns, &rps);
     if (ns == 1) return 0;
     return align256((size_t)BT * ns * H * D * 4) + align256((size_t)BT * ns * H * 8);
 }
@@ -284,10 +606,10 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     R.Lr = a.Lr;
     R.raw0 = a.raw0;
     R.W = a.W;
-    const int BT = B * Tq, HG = (H + 63) / 64;
+    const int BT = B * Tq;
     const int max_rows = a.mode == 0 ? a.N : a.topk + a.W;
     int ns, rps;
-    choose_split(BT, HG, max_rows, &ns, &rps);
+    choose_split(BT, H, D, max_rows, &ns, &rps);
     float* part_o = nullptr;
     float2* part_ml = nullptr;
     if (ns > 1) {
@@ -295,7 +617,21 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         part_ml = (float2*)((char*)ws + align256((size_t)BT * ns * H * D * 4));
     }
     const float sl2 = scale * LOG2E;
-    dim3 grid(ns, HG, BT);
+    if (use32(D, H)) {
+        const int nunits = BT * ns, HG = H / 32;
+        const int nblk = (nunits + 7) / 8 * 8 * HG;
+        if (a.mode == 0)
+            CSA_LAUNCH(tag, k_attn32<0>, dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2,
+                       nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
+        else
+            CSA_LAUNCH(tag, k_attn32<1>, dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2,
+                       nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
+        if (ns > 1)
+            CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
+                       (uint16_t*)out, lse);
+        return 0;
+    }
+    dim3 grid(ns, (H + 63) / 64, BT);
     if (D == 512) {
         CSA_LAUNCH(tag, k_attn<512>, grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns, rps,
                    part_o, part_ml, (uint16_t*)out, lse);

@@ -50,6 +50,13 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float f) {
     return (uint8_t)(s | code);
 }
 
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // Order-preserving map of an fp32 to uint32 (larger float -> larger key); -0 maps like +0.
 __host__ __device__ __forceinline__ uint32_t f32_key(float f) {
     uint32_t u;

@@ -4,26 +4,28 @@
 // a light Lightning Indexer scores every compressed KV entry against the query
 // and a top-k selector keeps the most relevant entries (Pro keeps 1024);
 // "DeepSeek V4 详解" section "第一刀": every query looks only at its own top-k.
-// The score of entry s for query row r (library definition, the pages print
+// The score of entry s for query row r (library definition; the pages print
 // none): S = fma-chain_h w_h * ReLU(RN32(exact q_h . k_s)).
 //
 // GPU pipeline (all on the caller's stream, no host synchronisation):
-//   k_fill      zero the per-row histograms and error maxima
-//   k_score     MFMA (bf16 16x16x32) approximate scores S~ plus a per-entry
-//               rigorous error bound; writes S~, a 2048-bin histogram of the
-//               top 11 key bits, and the row's largest bound Dmax
-//   k_refine<1> histogram of key bits 20..10 inside the threshold bin
-//   k_refine<2> histogram of key bits 9..0 inside the threshold bin
-//   k_classify  tau = exact k-th largest S~; entries with S~ > tau + 2 Dmax are
-//               certainly selected, entries with S~ < tau - 2 Dmax certainly
-//               not; the rest (the band) are rescored exactly (wave-cooperative
-//               fixed-point dot products) in place; bitmaps "in" and "band"
-//   k_finalize  per row: radix-select the remaining slots among the band by
-//               (exact S desc, index asc), then compact the selected bitmap
-//               into ascending indices.
-// The selected set therefore equals the one defined on exact scores, whatever
-// rounding the MFMA accumulation uses, provided its error stays inside the
-// bound (checked on hardware by the parity tests).
+//   k_fill     zero the per-row histogram, error maximum and candidate count
+//   k_score    the HBM-bound pass: v_mfma_f32_16x16x32_bf16 approximate scores
+//              S~ (e4m3 keys are widened to bf16 exactly in registers), a
+//              rigorous per-entry error bound from a second MFMA on |q|, |k|,
+//              a 4096-bin histogram of the top 12 bits of S~ and the row's
+//              largest bound Dmax
+//   k_collect  every entry that can still reach the top-k (S~ >= lower edge of
+//              the bin holding the k-th largest, minus 2 Dmax) -> a per-row
+//              candidate list
+//   k_select   one workgroup per row: exact k-th largest S~ (tau) over the
+//              candidates; S~ > tau + 2 Dmax is certainly selected, S~ <
+//              tau - 2 Dmax certainly not; the band in between is rescored
+//              exactly (wave-cooperative fixed-point dot products) and its
+//              remaining slots go by (exact S desc, index asc); the k indices
+//              are sorted ascending (bitonic, LDS).
+// The selected set equals the one defined on exact scores whatever order the
+// MFMA accumulates in, provided its error stays inside the bound (the parity
+// tests check both the sets and, on hardware, the bound's margin).
 #include "common.h"
 #include "exact_dot.h"
 #include "kernels.h"
@@ -32,8 +34,9 @@ namespace {
 
 using namespace csa;
 
-constexpr int BINS1 = 2048, BINS2 = 2048, BINS3 = 1024;
-constexpr int HIST_WORDS = BINS1 + BINS2 + BINS3 + 1;   // + Dmax word
+constexpr int BINS1 = 4096;                  // histogram of key bits 31..20
+constexpr int HW_DMAX = BINS1, HW_CNT = BINS1 + 1;
+constexpr int HIST_WORDS = BINS1 + 4;        // hist, Dmax, candidate count, pad
 constexpr int TPB = 256;
 
 __device__ __forceinline__ int n_visible(long long p, long long L, int m, int Nc) {
@@ -42,31 +45,27 @@ __device__ __forceinline__ int n_visible(long long p, long long L, int m, int Nc
     return v < Nc ? (int)v : Nc;
 }
 
-// ---------------------------------------------------------------------------
-// block-wide helpers
-// ---------------------------------------------------------------------------
 // Given a histogram in LDS (nb bins, nb % TPB == 0) find the bin b holding the
 // need-th largest element: sum(h[b+1..]) < need <= sum(h[b..]).  Results in
-// out[0] = b, out[1] = sum(h[b+1..]).  All threads must call.
+// out[0] = b, out[1] = sum(h[b+1..]).  All threads of a TPB-wide block call.
 __device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* out, uint32_t* scratch) {
-    const int tid = threadIdx.x, per = nb / TPB;
+    const int tid = threadIdx.x, per = nb / TPB, lane = tid & 63, wave = tid >> 6;
     uint32_t s = 0;
     for (int i = 0; i < per; ++i) s += h[tid * per + i];
-    scratch[tid] = s;
-    __syncthreads();
-    // suffix sums over threads (TPB = 256): simple log-step scan in LDS
-    for (int off = 1; off < TPB; off <<= 1) {
-        uint32_t v = (tid + off < TPB) ? scratch[tid + off] : 0;
-        __syncthreads();
-        scratch[tid] += v;
-        __syncthreads();
+    uint32_t incl = s;                                  // suffix sum within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_down(incl, o, 64);
+        if (lane + o < 64) incl += v;
     }
-    uint32_t incl = scratch[tid];            // sum of threads tid..TPB-1
-    uint32_t above = incl - s;
+    if (lane == 0) scratch[wave] = incl;
+    __syncthreads();
+    for (int w = wave + 1; w < TPB / 64; ++w) incl += scratch[w];
+    const uint32_t above = incl - s;
     if (above < need && need <= incl) {
         uint32_t acc = above;
         for (int i = per - 1; i >= 0; --i) {
-            uint32_t c = h[tid * per + i];
+            const uint32_t c = h[tid * per + i];
             if (acc + c >= need) { out[0] = tid * per + i; out[1] = acc; break; }
             acc += c;
         }
@@ -74,17 +73,11 @@ __device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* out
     __syncthreads();
 }
 
-// ---------------------------------------------------------------------------
-// k_fill
-// ---------------------------------------------------------------------------
 __global__ void k_fill(uint32_t* p, size_t n) {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
-// ---------------------------------------------------------------------------
-// k_score
-// ---------------------------------------------------------------------------
 // fp8 (OCP e4m3) pair -> bf16 pair, exact (gfx950 hardware conversion, scale 1).
 template <bool HI_WORD>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t v) {
@@ -93,28 +86,47 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t v) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// Error model of the MFMA path (see DESIGN notes in the host file):
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
+    return u32x4_t{e4m3x2_to_bf16x2<false>(x0), e4m3x2_to_bf16x2<true>(x0),
+                   e4m3x2_to_bf16x2<false>(x1), e4m3x2_to_bf16x2<true>(x1)};
+}
+
+// Error model of the MFMA path:
 //   |d~_h - d_h| <= E_h = C_DOT * A_h,  A_h = MFMA(|q_h|, |k|) ~ sum_i |q_hi k_i|
-//   |S~ - S| <= sum_h |w_h| ( C_SUM (|d~_h| + E_h) + E_h ) (1 + 2^-10) + 2^-126
+//   |S~ - S| <= sum_h |w_h| ( C_SUM (|d~_h| + E_h) + E_h ) (1 + 2^-10) + 2^-24 |S~| + 2^-126
 // C_DOT = 2^-18 is 64 unit roundoffs (the bf16 MFMA measures <= 2 u sum|p| on
 // gfx950); C_SUM = 2^-19 covers the fp32 rounding of the head reduction on both
-// sides and of the final RN32 of each dot.
+// sides and the final RN32 of each exact dot.
 #define C_DOT 3.814697265625e-06f   // 2^-18
 #define C_SUM 1.9073486328125e-06f  // 2^-19
 
+// ---------------------------------------------------------------------------
+// k_score
+// ---------------------------------------------------------------------------
+// MFMA roles: A = 16 query columns (row t, head h; heads padded to HP = max(HI, 4)),
+// B = 16 keys, both loaded as 1/4 of a row per lane (the same k-slot order),
+// so D[column][key] leaves every lane with HP/4... 4 heads of one key: the
+// head reduction is mostly lane-local (one xor-16 shuffle for HP = 8).
 template <int DT, int DI, int HI>
 __global__ __launch_bounds__(TPB) void k_score(
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int keys_per_wg, int topk,
     float* __restrict__ S, uint32_t* __restrict__ hist)
 {
-    constexpr int STEPS = DI / 32;            // 16x16x32 MFMAs per 16-key tile
-    constexpr int EPL = DI / 4;               // elements per lane per key row
+    constexpr int STEPS = DI / 32;            // bf16 16x16x32 MFMAs per 16-key tile
+    constexpr int EPL = DI / 4;               // key elements per lane
     constexpr int KB = DT == 0 ? EPL * 2 : EPL;   // key bytes per lane
-    constexpr int G = 16 / HI;                // query rows per column group
+    constexpr int NV = KB / 16;               // 16-byte loads per lane per tile
+#ifndef CSA_SCORE_BATCH_BYTES
+#define CSA_SCORE_BATCH_BYTES 128
+#endif
+    constexpr int U = CSA_SCORE_BATCH_BYTES / KB;   // tiles per load batch (bytes per lane in flight)
+    constexpr int HP = HI < 4 ? 4 : HI;       // padded heads per query row
+    constexpr int G = 16 / HP;                // query rows per column group
+    constexpr int LPR = HP / 4;               // lanes (of one key) holding one row's heads
     constexpr int ES = DT == 0 ? 2 : 1;
 
-    __shared__ uint32_t lh[2][BINS1];         // histogram for up to 2 rows of a group
+    __shared__ uint32_t lh[2][BINS1];         // histograms of up to 2 rows of a group
     __shared__ uint32_t ldmax[2];
 
     const int b = blockIdx.y;
@@ -122,188 +134,212 @@ __global__ __launch_bounds__(TPB) void k_score(
     const int col = lane & 15, grp = lane >> 4;
     const int key0 = blockIdx.x * keys_per_wg;
     const int NG = (Tq + G - 1) / G;
+    const int tiles = keys_per_wg / 64;       // 16-key tiles per wave
 
     for (int g = 0; g < NG; ++g) {
-        // rows of this column group that need a selection at all
-        const int t = g * G + col / HI, h = col % HI;
-        const bool colv = t < Tq;
         const int nrow = min(G, Tq - g * G);
         const int nlds = min(nrow, 2);
-        for (int i = threadIdx.x; i < 2 * BINS1; i += TPB) (&lh[0][0])[i] = 0;
+        for (int i = threadIdx.x; i < nlds * BINS1; i += TPB) (&lh[0][0])[i] = 0;
         if (threadIdx.x < 2) ldmax[threadIdx.x] = 0;
         __syncthreads();
 
-        // B operands: q and |q| for (t, h), permuted like the key loads
+        // A operand: query column `col` = (row ta, head ha)
+        const int ta = g * G + col / HP, ha = col % HP;
+        const bool av = ta < Tq && ha < HI;
         bf16x8_t qb[STEPS], qa[STEPS];
-        float w = 0.f;
-        int nv = 0;
-        if (colv) {
-            const size_t r = (size_t)b * Tq + t;
-            w = w_idx[r * HI + h];
-            nv = n_visible(pos0 + t, L, m, Nc);
-            const char* qp = (const char*)q_idx + (r * HI + h) * DI * ES + (size_t)grp * EPL * ES;
+        u32x4_t qf8a[2];                      // |q| as raw e4m3 bytes (DT == 1)
+        if (av) {
+            const size_t r = (size_t)b * Tq + ta;
+            const char* qp = (const char*)q_idx + (r * HI + ha) * DI * ES + (size_t)grp * EPL * ES;
 #pragma unroll
             for (int s = 0; s < STEPS; ++s) {
                 u32x4_t v;
-                if (DT == 0) {
-                    v = *(const u32x4_t*)(qp + s * 16);
-                } else {
-                    uint32_t x0 = *(const uint32_t*)(qp + s * 8), x1 = *(const uint32_t*)(qp + s * 8 + 4);
-                    v = u32x4_t{e4m3x2_to_bf16x2<false>(x0), e4m3x2_to_bf16x2<true>(x0),
-                                e4m3x2_to_bf16x2<false>(x1), e4m3x2_to_bf16x2<true>(x1)};
-                }
+                if (DT == 0) v = *(const u32x4_t*)(qp + s * 16);
+                else v = e4m3x8_to_bf16x8(*(const uint32_t*)(qp + s * 8), *(const uint32_t*)(qp + s * 8 + 4));
                 qb[s] = as_bf16x8(v);
                 qa[s] = as_bf16x8(v & 0x7fff7fffu);
+            }
+            if (DT == 1) {
+                qf8a[0] = (*(const u32x4_t*)qp) & 0x7f7f7f7fu;
+                qf8a[1] = DI == 128 ? (*(const u32x4_t*)(qp + 16)) & 0x7f7f7f7fu : u32x4_t{0, 0, 0, 0};
             }
         } else {
 #pragma unroll
             for (int s = 0; s < STEPS; ++s) { qb[s] = as_bf16x8(u32x4_t{0, 0, 0, 0}); qa[s] = qb[s]; }
+            qf8a[0] = qf8a[1] = u32x4_t{0, 0, 0, 0};
         }
-        const float aw = fabsf(w);
-        // Rows whose whole visible prefix is selected need no scores.
-        int nvmax = 0;
+        // output side: this lane's 4 columns 4*grp + j all belong to row tr
+        const int tr = g * G + (4 * grp) / HP;
+        const bool rv = tr < Tq;
+        const size_t r = (size_t)b * Tq + (rv ? tr : 0);
+        float w4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int hh = (4 * grp + j) % HP;
+            w4[j] = (rv && hh < HI) ? w_idx[r * HI + hh] : 0.f;
+        }
+        const int nv = rv ? n_visible(pos0 + tr, L, m, Nc) : 0;
+        const bool need_sel = rv && nv > topk;
+        const bool writer = need_sel && (grp % LPR) == 0;
+        int nvmax;                            // keys any row of the group needs scored
         {
-            int v = (colv && nv > topk) ? nv : 0;
-            for (int o = 1; o < 16; o <<= 1) v = max(v, __shfl_xor(v, o, 64));
+            int v = need_sel ? nv : 0;
+            v = max(v, __shfl_xor(v, 16, 64));
+            v = max(v, __shfl_xor(v, 32, 64));
             nvmax = v;
         }
         float dmax_loc = 0.f;
+        const int lrow = tr - g * G;
 
-        const int tiles = keys_per_wg / 64;   // 16-key tiles per wave
-        for (int tt = 0; tt < tiles; ++tt) {
-            const int kbase = key0 + (tt * 4 + wave) * 16;   // waves interleave 16-key tiles
-            if (kbase >= nvmax) break;
-            const int krow = kbase + col;
-            // A operands: key row krow, bytes [grp*KB, grp*KB + KB)
-            u32x4_t kr[KB / 16 > 0 ? KB / 16 : 1];
-            if (krow < Nc) {
+        // key loads are software-pipelined: batch i+1 is in flight while batch i computes
+        auto load_batch = [&](int tt0, u32x4_t (&dst)[U][NV]) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int krow = key0 + ((tt0 + u) * 4 + wave) * 16 + col;
                 const char* kp = (const char*)k_idx + ((size_t)b * Nc + krow) * DI * ES + (size_t)grp * KB;
 #pragma unroll
-                for (int i = 0; i < (KB >= 16 ? KB / 16 : 1); ++i) {
-                    if (KB >= 16) kr[i] = *(const u32x4_t*)(kp + i * 16);
-                    else { uint2 x = *(const uint2*)kp; kr[i] = u32x4_t{x.x, x.y, 0, 0}; }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < (KB >= 16 ? KB / 16 : 1); ++i) kr[i] = u32x4_t{0, 0, 0, 0};
+                for (int i = 0; i < NV; ++i)
+                    dst[u][i] = krow < Nc ? *(const u32x4_t*)(kp + i * 16) : u32x4_t{0, 0, 0, 0};
             }
-            f32x4_t acc = {0, 0, 0, 0}, aacc = {0, 0, 0, 0};
+        };
+        auto compute_batch = [&](int tt0, const u32x4_t (&cur)[U][NV]) {
 #pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                u32x4_t v;
-                if (DT == 0) {
-                    v = kr[s];
-                } else {
-                    // 8 fp8 bytes per step: dwords (2s, 2s+1) of the lane's bytes
-                    const uint32_t x0 = kr[s / 2][(s & 1) * 2], x1 = kr[s / 2][(s & 1) * 2 + 1];
-                    v = u32x4_t{e4m3x2_to_bf16x2<false>(x0), e4m3x2_to_bf16x2<true>(x0),
-                                e4m3x2_to_bf16x2<false>(x1), e4m3x2_to_bf16x2<true>(x1)};
-                }
-                acc = mfma16_bf16(as_bf16x8(v), qb[s], acc);
-                aacc = mfma16_bf16(as_bf16x8(v & 0x7fff7fffu), qa[s], aacc);
-            }
-            // lane holds d~ for keys kbase + 4*grp + j (j = 0..3) and column (t, h)
-            float x[4], e[4];
+            for (int u = 0; u < U; ++u) {
+                    const int kbase = key0 + ((tt0 + u) * 4 + wave) * 16;
+                    if (kbase >= nvmax) break;
+                    f32x4_t acc = {0, 0, 0, 0}, aacc = {0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float d = acc[j];
-                const float E = C_DOT * aacc[j];
-                x[j] = w * fmaxf(d, 0.0f);
-                e[j] = aw * (C_SUM * (fabsf(d) + E) + E);
-            }
-            // reduce over the HI lanes of one query row (adjacent columns)
+                    for (int s = 0; s < STEPS; ++s) {
+                        u32x4_t v;
+                        if (DT == 0) v = cur[u][s];
+                        else v = e4m3x8_to_bf16x8(cur[u][s / 2][(s & 1) * 2], cur[u][s / 2][(s & 1) * 2 + 1]);
+                        acc = mfma16_bf16(qb[s], as_bf16x8(v), acc);
+                        if (DT == 0) aacc = mfma16_bf16(qa[s], as_bf16x8(v & 0x7fff7fffu), aacc);
+                    }
+                    if (DT == 1) {
+                        // |q|.|k| bound: one e4m3 MFMA (K = 128) on the raw bytes with the sign bits cleared
+                        typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+                        const u32x4_t k0 = cur[u][0] & 0x7f7f7f7fu;
+                        const u32x4_t k1 = NV > 1 ? cur[u][NV > 1 ? 1 : 0] & 0x7f7f7f7fu : u32x4_t{0, 0, 0, 0};
+                        const i32x8_t A8 = {(int)qf8a[0][0], (int)qf8a[0][1], (int)qf8a[0][2], (int)qf8a[0][3],
+                                            (int)qf8a[1][0], (int)qf8a[1][1], (int)qf8a[1][2], (int)qf8a[1][3]};
+                        const i32x8_t B8 = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                                            (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+                        aacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A8, B8, aacc, 0, 0, 0, 127, 0, 127);
+                    }
+                    // lane: key kbase + col, columns 4*grp + j of row tr
+                    float x = 0.f, e = 0.f;
 #pragma unroll
-            for (int o = 1; o < HI; o <<= 1) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { x[j] += shfl_xor_f(x[j], o); e[j] += shfl_xor_f(e[j], o); }
-            }
-            if (colv && h == 0 && nv > topk) {
-                const size_t r = (size_t)b * Tq + t;
-                const int lrow = t - g * G;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s = kbase + 4 * grp + j;
-                    if (s < nv) {
-                        const float sc = x[j] + 0.0f;            // canonical +0 for exact zero
+                    for (int j = 0; j < 4; ++j) {
+                        const float d = acc[j];
+                        // all-positive e4m3 MFMA sums are inflated by 2^-8 for its reduced-precision accumulation
+                        const float E = C_DOT * (DT == 1 ? aacc[j] * 1.00390625f : aacc[j]);
+                        x = fmaf(w4[j], fmaxf(d, 0.0f), x);
+                        e = fmaf(fabsf(w4[j]), C_SUM * (fabsf(d) + E) + E, e);
+                    }
+                    if (LPR >= 2) { x += shfl_xor_f(x, 16); e += shfl_xor_f(e, 16); }
+                    if (LPR >= 4) { x += shfl_xor_f(x, 32); e += shfl_xor_f(e, 32); }
+                    const int s = kbase + col;
+                    if (writer && s < nv) {
+                        const float sc = x + 0.0f;                        // canonical +0
                         S[r * NcP + s] = sc;
                         const uint32_t key = f32_key(sc);
-                        if (lrow < nlds) atomicAdd(&lh[lrow][key >> 21], 1u);
-                        else atomicAdd(&hist[r * HIST_WORDS + (key >> 21)], 1u);
-                        const float ej = e[j] * 1.0009765625f + 1.1754943508222875e-38f;
+                        if (lrow < nlds) atomicAdd(&lh[lrow][key >> 20], 1u);
+                        else atomicAdd(&hist[r * HIST_WORDS + (key >> 20)], 1u);
+                        const float ej = e * 1.0009765625f + 1.1754943508222875e-38f;
                         dmax_loc = fmaxf(dmax_loc, ej + fabsf(sc) * 5.9604644775390625e-08f);
                     }
                 }
-            }
+        };
+        u32x4_t ka[U][NV], kb[U][NV];
+        if (key0 + wave * 16 < nvmax) load_batch(0, ka);
+        for (int tt0 = 0; tt0 < tiles; tt0 += 2 * U) {
+            if (key0 + (tt0 * 4 + wave) * 16 >= nvmax) break;
+            const bool more1 = tt0 + U < tiles && key0 + ((tt0 + U) * 4 + wave) * 16 < nvmax;
+            if (more1) load_batch(tt0 + U, kb);
+            compute_batch(tt0, ka);
+            if (!more1) break;
+            const bool more2 = tt0 + 2 * U < tiles && key0 + ((tt0 + 2 * U) * 4 + wave) * 16 < nvmax;
+            if (more2) load_batch(tt0 + 2 * U, ka);
+            compute_batch(tt0 + U, kb);
         }
-        // row maxima of the error bound
-        if (colv && h == 0 && nv > topk) {
-            const int lrow = t - g * G;
-            const size_t r = (size_t)b * Tq + t;
+        if (writer) {
             if (lrow < nlds) atomicMax(&ldmax[lrow], __float_as_uint(dmax_loc));
-            else atomicMax(&hist[r * HIST_WORDS + BINS1 + BINS2 + BINS3], __float_as_uint(dmax_loc));
+            else atomicMax(&hist[r * HIST_WORDS + HW_DMAX], __float_as_uint(dmax_loc));
         }
         __syncthreads();
         for (int lr = 0; lr < nlds; ++lr) {
-            const size_t r = (size_t)b * Tq + g * G + lr;
+            const size_t rr = (size_t)b * Tq + g * G + lr;
             for (int i = threadIdx.x; i < BINS1; i += TPB)
-                if (lh[lr][i]) atomicAdd(&hist[r * HIST_WORDS + i], lh[lr][i]);
-            if (threadIdx.x == 0 && ldmax[lr]) atomicMax(&hist[r * HIST_WORDS + BINS1 + BINS2 + BINS3], ldmax[lr]);
+                if (lh[lr][i]) atomicAdd(&hist[rr * HIST_WORDS + i], lh[lr][i]);
+            if (threadIdx.x == 0 && ldmax[lr]) atomicMax(&hist[rr * HIST_WORDS + HW_DMAX], ldmax[lr]);
         }
         __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
-// k_refine: second and third radix levels of the threshold search
+// k_collect: per-row candidate list
 // ---------------------------------------------------------------------------
-template <int LEVEL>
-__global__ __launch_bounds__(TPB) void k_refine(const float* __restrict__ S, uint32_t* __restrict__ hist,
-                                                int Tq, int Nc, int NcP, long long L, int m, long long pos0,
-                                                int topk, int chunk)
+constexpr int CCHUNK = 4096;     // entries per workgroup (4 waves x 16 groups of 64)
+
+__global__ __launch_bounds__(TPB) void k_collect(const float* __restrict__ S, uint32_t* __restrict__ hist,
+                                                 uint2* __restrict__ list, int Tq, int Nc, int NcP, long long L,
+                                                 int m, long long pos0, int topk)
 {
-    __shared__ uint32_t lh[BINS2];
+    __shared__ uint32_t lh[BINS1];
     __shared__ uint32_t scratch[TPB];
     __shared__ uint32_t res[4];
-    const int r = blockIdx.y;
-    const int t = r % Tq;
+    __shared__ uint32_t wcount[TPB / 64], wbase[TPB / 64];
+    const int r = blockIdx.y, t = r % Tq;
     const int nv = n_visible(pos0 + t, L, m, Nc);
     if (nv <= topk) return;
     uint32_t* H = hist + (size_t)r * HIST_WORDS;
     for (int i = threadIdx.x; i < BINS1; i += TPB) lh[i] = H[i];
     __syncthreads();
     find_bin(lh, BINS1, (uint32_t)topk, res, scratch);
-    const uint32_t b1 = res[0], above1 = res[1];
-    uint32_t prefix, shift, mask, nb;
-    if (LEVEL == 1) {
-        prefix = b1; shift = 21; mask = BINS2 - 1; nb = BINS2;
-    } else {
-        __syncthreads();
-        for (int i = threadIdx.x; i < BINS2; i += TPB) lh[i] = H[BINS1 + i];
-        __syncthreads();
-        find_bin(lh, BINS2, (uint32_t)topk - above1, res, scratch);
-        prefix = (b1 << 11) | res[0]; shift = 10; mask = BINS3 - 1; nb = BINS3;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < (int)nb; i += TPB) lh[i] = 0;
-    __syncthreads();
-    const int s0 = blockIdx.x * chunk, s1 = min(nv, s0 + chunk);
+    const double thr = (double)key_f32(res[0] << 20) - 2.0 * (double)__uint_as_float(H[HW_DMAX]);
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int s_w = blockIdx.x * CCHUNK + wave * (CCHUNK / 4);
     const float* Sr = S + (size_t)r * NcP;
-    for (int s = s0 + threadIdx.x; s < s1; s += TPB) {
-        const uint32_t key = f32_key(Sr[s]);
-        if ((key >> shift) == prefix) {
-            const uint32_t bin = LEVEL == 1 ? (key >> 10) & mask : key & mask;
-            atomicAdd(&lh[bin], 1u);
-        }
+    unsigned long long mask[CCHUNK / 4 / 64];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int gi = 0; gi < CCHUNK / 4 / 64; ++gi) {
+        const int s = s_w + gi * 64 + lane;
+        const bool c = s < nv && (double)Sr[s] >= thr;
+        mask[gi] = __ballot(c);
+        cnt += __popcll(mask[gi]);
+    }
+    if (lane == 0) wcount[wave] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t tot = 0;
+        for (int w = 0; w < TPB / 64; ++w) tot += wcount[w];
+        uint32_t base = tot ? atomicAdd(&H[HW_CNT], tot) : 0;
+        for (int w = 0; w < TPB / 64; ++w) { wbase[w] = base; base += wcount[w]; }
     }
     __syncthreads();
-    uint32_t* dst = H + (LEVEL == 1 ? BINS1 : BINS1 + BINS2);
-    for (int i = threadIdx.x; i < (int)nb; i += TPB)
-        if (lh[i]) atomicAdd(&dst[i], lh[i]);
+    uint32_t pos = wbase[wave];
+    uint2* Lr = list + (size_t)r * NcP;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int gi = 0; gi < CCHUNK / 4 / 64; ++gi) {
+        const int sidx = s_w + gi * 64 + lane;
+        if ((mask[gi] >> lane) & 1ull)
+            Lr[pos + __popcll(mask[gi] & below)] = make_uint2((uint32_t)sidx, __float_as_uint(Sr[sidx]));
+        pos += __popcll(mask[gi]);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// k_classify: in / band bitmaps; exact rescoring of band entries
+// k_select: one workgroup per query row
 // ---------------------------------------------------------------------------
+constexpr int STPB = 1024;
+constexpr int MAXK = 4096;
+constexpr int BAND_LDS = 1024;
+constexpr int CAND_LDS = 4096;
+
 // Wave-cooperative exact score of entry s: HI head groups of LPH lanes, each
 // lane EPL elements; per head, fixed-point window accumulation (as in
 // exact_dot.h) reduced across the group, then the fma chain in head order.
@@ -365,199 +401,176 @@ __device__ float wave_exact_score(const void* qrow, const float* wrow, const voi
     return Sx;
 }
 
+
+// wave 0: find the bin (of 256, counting from the top) that holds the need-th
+// largest element given the count already above; writes out[0] = bin,
+// out[1] = count above that bin.
+__device__ void wave_find_bin256(const uint32_t* h, uint32_t need, uint32_t above, uint32_t* out) {
+    const int lane = lane_id();
+    // lane L covers bins 255-4L .. 252-4L (descending)
+    uint32_t c[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { c[i] = h[255 - 4 * lane - i]; s += c[i]; }
+    uint32_t incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    uint32_t acc = above + incl - s;
+    if (acc < need && need <= acc + s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (acc + c[i] >= need) { out[0] = 255 - 4 * lane - i; out[1] = acc; break; }
+            acc += c[i];
+        }
+    }
+}
+
 template <int DT, int DI, int HI>
-__global__ __launch_bounds__(TPB) void k_classify(
-    float* __restrict__ S, const uint32_t* __restrict__ hist, uint32_t* __restrict__ inb, uint32_t* __restrict__ bandb,
+__global__ __launch_bounds__(STPB) void k_select(
+    const uint32_t* __restrict__ hist, const uint2* __restrict__ list,
+    uint32_t* __restrict__ band_g, unsigned long long* __restrict__ bkey_g,
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
-    int Tq, int Nc, int NcP, long long L, int m, long long pos0, int topk, int chunk)
+    int Tq, int Nc, int NcP, long long L, int m, long long pos0, int topk,
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
 {
     constexpr int ES = DT == 0 ? 2 : 1;
-    __shared__ uint32_t lh[BINS2];
-    __shared__ uint32_t scratch[TPB];
+    __shared__ int32_t sel[MAXK];
+    __shared__ uint32_t hst[256];
     __shared__ uint32_t res[4];
-    const int r = blockIdx.y;
-    const int b = r / Tq, t = r % Tq;
-    const int nv = n_visible(pos0 + t, L, m, Nc);
-    if (nv <= topk) return;
-    const uint32_t* H = hist + (size_t)r * HIST_WORDS;
-    for (int i = threadIdx.x; i < BINS1; i += TPB) lh[i] = H[i];
-    __syncthreads();
-    find_bin(lh, BINS1, (uint32_t)topk, res, scratch);
-    const uint32_t b1 = res[0], a1 = res[1];
-    __syncthreads();
-    for (int i = threadIdx.x; i < BINS2; i += TPB) lh[i] = H[BINS1 + i];
-    __syncthreads();
-    find_bin(lh, BINS2, (uint32_t)topk - a1, res, scratch);
-    const uint32_t b2 = res[0], a2 = res[1];
-    __syncthreads();
-    for (int i = threadIdx.x; i < BINS3; i += TPB) lh[i] = H[BINS1 + BINS2 + i];
-    __syncthreads();
-    find_bin(lh, BINS3, (uint32_t)topk - a1 - a2, res, scratch);
-    const uint32_t b3 = res[0];
-    const float tau = key_f32((b1 << 21) | (b2 << 10) | b3);
-    const float dmax = __uint_as_float(H[BINS1 + BINS2 + BINS3]);
-    const double lo = (double)tau - 2.0 * (double)dmax, hi = (double)tau + 2.0 * (double)dmax;
-
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    const int s0 = blockIdx.x * chunk, s1 = min(NcP, s0 + chunk);     // chunk % 64 == 0
-    float* Sr = S + (size_t)r * NcP;
-    const char* qrow = (const char*)q_idx + (size_t)r * HI * DI * ES;
-    const float* wrow = w_idx + (size_t)r * HI;
-    for (int base = s0 + wave * 64; base < s1; base += TPB) {
-        const int s = base + lane;
-        bool isin = false, isband = false;
-        if (s < nv) {
-            const double v = (double)Sr[s];
-            isin = v > hi;
-            isband = !isin && v >= lo;
-        }
-        const unsigned long long bin = __ballot(isin), bband = __ballot(isband);
-        if (lane == 0) {
-            inb[(size_t)r * (NcP / 32) + base / 32] = (uint32_t)bin;
-            inb[(size_t)r * (NcP / 32) + base / 32 + 1] = (uint32_t)(bin >> 32);
-            bandb[(size_t)r * (NcP / 32) + base / 32] = (uint32_t)bband;
-            bandb[(size_t)r * (NcP / 32) + base / 32 + 1] = (uint32_t)(bband >> 32);
-        }
-        unsigned long long todo = bband;
-        while (todo) {
-            const int j = __ffsll((long long)todo) - 1;
-            todo &= todo - 1;
-            const int e = base + j;
-            const float sx = wave_exact_score<DT, DI, HI>(qrow, wrow, (const char*)k_idx + ((size_t)b * Nc + e) * DI * ES);
-            if (lane == 0) Sr[e] = sx;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// k_finalize: one workgroup per query row
-// ---------------------------------------------------------------------------
-constexpr int FTPB = 512;
-
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
-    // sh: FTPB words
-    const int tid = threadIdx.x;
-    sh[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < FTPB; off <<= 1) {
-        uint32_t x = tid >= off ? sh[tid - off] : 0;
-        __syncthreads();
-        sh[tid] += x;
-        __syncthreads();
-    }
-    const uint32_t incl = sh[tid];
-    *total = sh[FTPB - 1];
-    __syncthreads();
-    return incl - v;
-}
-
-__global__ __launch_bounds__(FTPB) void k_finalize(const float* __restrict__ S, const uint32_t* __restrict__ inb,
-                                                   const uint32_t* __restrict__ bandb, int Tq, int Nc, int NcP,
-                                                   long long L, int m, long long pos0, int topk,
-                                                   int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
-{
-    __shared__ uint32_t sh[FTPB];
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t res[4];
-    const int r = blockIdx.x, t = r % Tq, tid = threadIdx.x;
+    __shared__ uint32_t nsel, nband;
+    __shared__ unsigned long long bkey[BAND_LDS];
+    __shared__ uint32_t bidx[BAND_LDS];
+    __shared__ uint2 cand[CAND_LDS];
+    const int r = blockIdx.x, b = r / Tq, t = r % Tq, tid = threadIdx.x;
+    const int lane = lane_id(), wave = tid >> 6;
     const int nv = n_visible(pos0 + t, L, m, Nc);
     int32_t* out = idx_out + (size_t)r * topk;
     if (nv <= topk) {
-        for (int i = tid; i < topk; i += FTPB) out[i] = i < nv ? i : -1;
+        for (int i = tid; i < topk; i += STPB) out[i] = i < nv ? i : -1;
         if (cnt_out && tid == 0) cnt_out[r] = nv;
         return;
     }
-    const int NW = NcP / 32;
-    const int per = (NW + FTPB - 1) / FTPB;
-    const int w0 = min(NW, tid * per), w1 = min(NW, w0 + per);
-    const uint32_t* IB = inb + (size_t)r * NW;
-    const uint32_t* BB = bandb + (size_t)r * NW;
-    const float* Sr = S + (size_t)r * NcP;
-    uint32_t total;
-    uint32_t nin = 0, nband = 0;
-    for (int w = w0; w < w1; ++w) { nin += __popc(IB[w]); nband += __popc(BB[w]); }
-    block_excl_scan(nin, sh, &total);
-    const uint32_t n_in = total;
-    block_excl_scan(nband, sh, &total);
-    const uint32_t n_band = total;
-    const uint32_t need = (uint32_t)topk - n_in;            // 0 <= need <= n_band by construction
-    // exact threshold among band entries: need-th largest key (radix, 8 bits per pass)
+    const uint32_t* H = hist + (size_t)r * HIST_WORDS;
+    const uint32_t n = H[HW_CNT];
+    const float dmax = __uint_as_float(H[HW_DMAX]);
+    const uint2* Lg = list + (size_t)r * NcP;
+    // candidates (index, score bits) live in LDS when they fit, else are read from the global list
+    const bool in_lds = n <= (uint32_t)CAND_LDS;
+    if (in_lds)
+        for (uint32_t i = tid; i < n; i += STPB) cand[i] = Lg[i];
+    __syncthreads();
+    const uint2* Lr = in_lds ? cand : Lg;
+
+    // 1. tau = exact k-th largest S~ among the candidates (radix, 8 bits per pass)
     uint32_t prefix = 0, above = 0;
-    bool all_band = need == n_band;
-    if (need > 0 && !all_band) {
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            for (int i = tid; i < 256; i += FTPB) hist[i] = 0;
-            __syncthreads();
-            for (int w = w0; w < w1; ++w) {
-                uint32_t bits = BB[w];
-                while (bits) {
-                    const int j = __ffs((int)bits) - 1;
-                    bits &= bits - 1;
-                    const uint32_t key = f32_key(Sr[w * 32 + j]);
-                    const bool match = pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8));
-                    if (match) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-                }
-            }
-            __syncthreads();
-            if (tid == 0) {
-                uint32_t acc = above;
-                for (int bin = 255; bin >= 0; --bin) {
-                    if (acc + hist[bin] >= need) { res[0] = bin; res[1] = acc; break; }
-                    acc += hist[bin];
-                }
-            }
-            __syncthreads();
-            prefix |= res[0] << shift;
-            above = res[1];
-            __syncthreads();
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int i = tid; i < 256; i += STPB) hst[i] = 0;
+        __syncthreads();
+        for (uint32_t i = tid; i < n; i += STPB) {
+            const uint32_t key = f32_key(__uint_as_float(Lr[i].y));
+            if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))) atomicAdd(&hst[(key >> shift) & 255u], 1u);
         }
+        __syncthreads();
+        if (wave == 0) wave_find_bin256(hst, (uint32_t)topk, above, res);
+        __syncthreads();
+        prefix |= res[0] << shift;
+        above = res[1];
+        __syncthreads();
     }
-    const uint32_t need_eq = need - above;   // ties at the threshold key, taken by ascending index
-    // count ties in my range, scan, then build the selected words and compact
-    uint32_t nties = 0;
-    if (need > 0 && !all_band) {
-        for (int w = w0; w < w1; ++w) {
-            uint32_t bits = BB[w];
-            while (bits) {
-                const int j = __ffs((int)bits) - 1;
-                bits &= bits - 1;
-                nties += f32_key(Sr[w * 32 + j]) == prefix;
-            }
-        }
+    const float tau = key_f32(prefix);
+    const double lo = (double)tau - 2.0 * (double)dmax, hi = (double)tau + 2.0 * (double)dmax;
+
+    // 2. classify: certainly in -> sel[]; band -> band list
+    if (tid == 0) { nsel = 0; nband = 0; }
+    __syncthreads();
+    uint32_t* Bg = band_g + (size_t)r * NcP;
+    for (uint32_t i = tid; i < n; i += STPB) {
+        const uint2 c = Lr[i];
+        const double v = (double)__uint_as_float(c.y);
+        if (v > hi) sel[atomicAdd(&nsel, 1u)] = (int32_t)c.x;
+        else if (v >= lo) Bg[atomicAdd(&nband, 1u)] = c.x;
     }
-    uint32_t tie_rank = block_excl_scan(nties, sh, &total);
-    uint32_t nsel = 0;
-    // first pass: count selected in my range
-    for (int pass = 0; pass < 2; ++pass) {
-        uint32_t tr = tie_rank;
-        uint32_t pos = 0;
-        if (pass == 1) pos = block_excl_scan(nsel, sh, &total);
-        for (int w = w0; w < w1; ++w) {
-            uint32_t sel = IB[w];
-            uint32_t bits = BB[w];
-            if (need > 0) {
-                if (all_band) sel |= bits;
-                else {
-                    while (bits) {
-                        const int j = __ffs((int)bits) - 1;
-                        bits &= bits - 1;
-                        const uint32_t key = f32_key(Sr[w * 32 + j]);
-                        if (key > prefix) sel |= 1u << j;
-                        else if (key == prefix) { if (tr < need_eq) sel |= 1u << j; ++tr; }
-                    }
-                }
-            }
-            if (pass == 0) nsel += __popc(sel);
-            else {
-                while (sel) {
-                    const int j = __ffs((int)sel) - 1;
-                    sel &= sel - 1;
-                    out[pos++] = w * 32 + j;
-                }
+    __syncthreads();
+    const uint32_t n_in = nsel, nb = nband;
+    const uint32_t need = (uint32_t)topk - n_in;       // 0 <= need <= nb by construction
+
+    // 3. exact rescoring of the band (one wave per entry), composite keys
+    //    (exact score key, inverted index): larger composite = earlier in the order
+    unsigned long long* Kg = bkey_g + (size_t)r * NcP;
+    const char* qrow = (const char*)q_idx + (size_t)r * HI * DI * ES;
+    const float* wrow = w_idx + (size_t)r * HI;
+    if (need > 0 && need < nb) {
+        for (uint32_t i = wave; i < nb; i += STPB / 64) {
+            const uint32_t s = Bg[i];
+            const float sx = wave_exact_score<DT, DI, HI>(qrow, wrow, (const char*)k_idx + ((size_t)b * Nc + s) * DI * ES);
+            if (lane == 0) {
+                const unsigned long long ck = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - s);
+                Kg[i] = ck;
+                if (i < BAND_LDS) { bkey[i] = ck; bidx[i] = s; }
             }
         }
     }
+    __syncthreads();
+
+    // 4. the `need` largest composite keys among the band
+    if (need > 0 && need == nb) {
+        for (uint32_t i = tid; i < nb; i += STPB) sel[n_in + i] = (int32_t)Bg[i];
+    } else if (need > 0 && nb <= BAND_LDS) {
+        // rank by counting (composite keys are distinct)
+        for (uint32_t i = tid; i < nb; i += STPB) {
+            const unsigned long long ki = bkey[i];
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < nb; ++j) rank += bkey[j] > ki;
+            if (rank < need) sel[n_in + rank] = (int32_t)bidx[i];
+        }
+    } else if (need > 0) {
+        // large band: radix select on the 64-bit composite keys, 8 bits per pass
+        unsigned long long pfx = 0;
+        uint32_t ab = 0;
+        for (int pass = 0; pass < 8; ++pass) {
+            const int shift = 56 - 8 * pass;
+            for (int i = tid; i < 256; i += STPB) hst[i] = 0;
+            __syncthreads();
+            for (uint32_t i = tid; i < nb; i += STPB) {
+                const unsigned long long key = Kg[i];
+                if (pass == 0 || (key >> (shift + 8)) == (pfx >> (shift + 8))) atomicAdd(&hst[(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (wave == 0) wave_find_bin256(hst, need, ab, res);
+            __syncthreads();
+            pfx |= (unsigned long long)res[0] << shift;
+            ab = res[1];
+            __syncthreads();
+        }
+        if (tid == 0) nsel = n_in;
+        __syncthreads();
+        for (uint32_t i = tid; i < nb; i += STPB)
+            if (Kg[i] >= pfx) sel[atomicAdd(&nsel, 1u)] = (int32_t)(0xffffffffu - (uint32_t)(Kg[i] & 0xffffffffu));
+    }
+    __syncthreads();
+
+    // 5. ascending order: bitonic sort of sel[0..P), padded with INT_MAX
+    int P = 1;
+    while (P < topk) P <<= 1;
+    for (int i = topk + tid; i < P; i += STPB) sel[i] = 0x7fffffff;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < P; i += STPB) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const int a = sel[i], c = sel[ixj];
+                    const bool up = (i & k) == 0;
+                    if ((a > c) == up) { sel[i] = c; sel[ixj] = a; }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = tid; i < topk; i += STPB) out[i] = sel[i];
     if (cnt_out && tid == 0) cnt_out[r] = topk;
 }
 
@@ -570,10 +583,12 @@ namespace csa_host {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// S~ [R][NcP] f32 | hist [R][HIST_WORDS] | list [R][NcP] (u32,u32) | band [R][NcP] u32 | band keys [R][NcP] u64
 size_t index_topk_ws_bytes(int B, int Tq, int Nc) {
     const size_t R = (size_t)B * Tq;
-    const size_t NcP = ((size_t)Nc + 63) / 64 * 64;
-    return align256(R * NcP * 4) + align256(R * HIST_WORDS * 4) + 2 * align256(R * (NcP / 32) * 4);
+    const size_t NcP = ((size_t)Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
+    return align256(R * NcP * 4) + align256(R * HIST_WORDS * 4) + align256(R * NcP * 8) + align256(R * NcP * 4) +
+           align256(R * NcP * 8);
 }
 
 template <int DT, int DI, int HI>
@@ -581,30 +596,32 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
                         void* ws, hipStream_t st) {
     const size_t R = (size_t)B * Tq;
-    const int NcP = (Nc + 63) / 64 * 64;
+    const int NcP = (Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
     char* p = (char*)ws;
-    float* S = (float*)p;            p += align256(R * (size_t)NcP * 4);
-    uint32_t* hist = (uint32_t*)p;   p += align256(R * HIST_WORDS * 4);
-    uint32_t* inb = (uint32_t*)p;    p += align256(R * (size_t)(NcP / 32) * 4);
-    uint32_t* bandb = (uint32_t*)p;
+    float* S = (float*)p;                       p += align256(R * (size_t)NcP * 4);
+    uint32_t* hist = (uint32_t*)p;              p += align256(R * HIST_WORDS * 4);
+    uint2* list = (uint2*)p;                    p += align256(R * (size_t)NcP * 8);
+    uint32_t* band = (uint32_t*)p;              p += align256(R * (size_t)NcP * 4);
+    unsigned long long* bkey = (unsigned long long*)p;
     {
         const size_t n = R * HIST_WORDS;
-        int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+        const int blocks = (int)std::min<size_t>((n + 255) / 256, 2048);
         CSA_LAUNCH("k_fill", k_fill, dim3(blocks), dim3(256), 0, st, hist, n);
     }
-    // scoring: 1024 keys per workgroup (4 waves x 16 tiles of 16)
-    const int kpw = 1024;
-    dim3 g1((Nc + kpw - 1) / kpw, B);
-    CSA_LAUNCH("k_score", (k_score<DT, DI, HI>), g1, dim3(TPB), 0, st,
+    // keys per scoring workgroup (4 waves x tiles of 16): the largest of 4096/2048/1024 that still
+    // gives >= 512 workgroups (two per CU), so the grid runs in one round without a tail
+#ifndef CSA_SCORE_KPW
+    int kpw = 4096;
+    while (kpw > 1024 && (size_t)((Nc + kpw - 1) / kpw) * B < 512) kpw >>= 1;
+#else
+    const int kpw = CSA_SCORE_KPW;
+#endif
+    CSA_LAUNCH("k_score", (k_score<DT, DI, HI>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
                q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist);
-    const int chunk = 4096;
-    dim3 g2((NcP + chunk - 1) / chunk, (unsigned)R);
-    CSA_LAUNCH("k_refine1", k_refine<1>, g2, dim3(TPB), 0, st, S, hist, Tq, Nc, NcP, L, m, pos0, topk, chunk);
-    CSA_LAUNCH("k_refine2", k_refine<2>, g2, dim3(TPB), 0, st, S, hist, Tq, Nc, NcP, L, m, pos0, topk, chunk);
-    CSA_LAUNCH("k_classify", (k_classify<DT, DI, HI>), g2, dim3(TPB), 0, st, S, hist, inb, bandb,
-               q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, chunk);
-    CSA_LAUNCH("k_finalize", k_finalize, dim3((unsigned)R), dim3(FTPB), 0, st, S, inb, bandb, Tq, Nc, NcP,
-               L, m, pos0, topk, idx_out, cnt_out);
+    CSA_LAUNCH("k_collect", k_collect, dim3(NcP / CCHUNK, (unsigned)R), dim3(TPB), 0, st, S, hist, list, Tq, Nc, NcP,
+               L, m, pos0, topk);
+    CSA_LAUNCH("k_select", (k_select<DT, DI, HI>), dim3((unsigned)R), dim3(STPB), 0, st, hist, list, band, bkey,
+               q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out);
     return 0;
 }
 
