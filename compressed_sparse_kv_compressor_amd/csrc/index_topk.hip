@@ -23,9 +23,18 @@
 //              exactly (wave-cooperative fixed-point dot products) and its
 //              remaining slots go by (exact S desc, index asc); the k indices
 //              are sorted ascending (bitonic, LDS).
-// The selected set equals the one defined on exact scores whatever order the
-// MFMA accumulates in, provided its error stays inside the bound (the parity
-// tests check both the sets and, on hardware, the bound's margin).
+// Why the classification is safe.  Let every entry satisfy |S~_s - S_s| <= D
+// (D = Dmax of the row) and let tau be the k-th largest S~ (so fewer than k
+// entries have S~ > tau and at least k have S~ >= tau).
+//  * S~_s < tau - 2D: at least k entries t have S_t >= S~_t - D >= tau - D >
+//    S~_s + D >= S_s, i.e. k entries beat s strictly, so s is not selected.
+//  * S~_s > tau + 2D: any t with S_t >= S_s has S~_t >= S_t - D >= S_s - D >=
+//    S~_s - 2D > tau; fewer than k entries (s included) have S~ > tau, so at most
+//    k-1 entries can precede s in the order, so s is selected.
+//  * entries in between (the band) get their exact score, and the slots left
+//    after the certain ones go to the band by (exact S desc, index asc).
+// The selected set therefore equals the one defined on exact scores whatever
+// order the MFMA accumulates in, provided its error stays inside the bound.
 #include "common.h"
 #include "exact_dot.h"
 #include "kernels.h"
