@@ -122,7 +122,7 @@ def main():
     b.prof_enable(False)
     kern = {}
     for name in ("k_fill", "k_score", "k_refine1", "k_refine2", "k_classify", "k_finalize", "k_attn_sparse",
-                 "k_attn_dense", "k_combine", "k_collect", "k_select"):
+                 "k_attn_dense", "k_combine", "k_collect", "k_select", "k_collect_select"):
         ms, n = b.prof_read(name)
         if n:
             kern[name] = round(ms / n * 1000.0, 2)      # average microseconds per launch

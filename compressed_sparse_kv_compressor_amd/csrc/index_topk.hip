@@ -16,13 +16,14 @@
 //              largest bound Dmax
 //   k_collect  every entry that can still reach the top-k (S~ >= lower edge of
 //              the bin holding the k-th largest, minus 2 Dmax) -> a per-row
-//              candidate list
-//   k_select   one workgroup per row: exact k-th largest S~ (tau) over the
-//              candidates; S~ > tau + 2 Dmax is certainly selected, S~ <
-//              tau - 2 Dmax certainly not; the band in between is rescored
-//              exactly (wave-cooperative fixed-point dot products) and its
-//              remaining slots go by (exact S desc, index asc); the k indices
-//              are sorted ascending (bitonic, LDS).
+//              candidate list of (index, S~)
+//   k_select   one workgroup per row: exact k-th largest S~ (tau) by a bitonic
+//              sort of the candidates in LDS;
+//              S~ > tau + 2 Dmax is certainly selected, S~ < tau - 2 Dmax
+//              certainly not; the band in between is rescored exactly
+//              (wave-cooperative fixed-point dot products) and its remaining
+//              slots go by (exact S desc, index asc); the k indices are sorted
+//              ascending (bitonic, LDS).
 // Why the classification is safe.  Let every entry satisfy |S~_s - S_s| <= D
 // (D = Dmax of the row) and let tau be the k-th largest S~ (so fewer than k
 // entries have S~ > tau and at least k have S~ >= tau).
@@ -44,8 +45,9 @@ namespace {
 using namespace csa;
 
 constexpr int BINS1 = 4096;                  // histogram of key bits 31..20
-constexpr int HW_DMAX = BINS1, HW_CNT = BINS1 + 1;
-constexpr int HIST_WORDS = BINS1 + 4;        // hist, Dmax, candidate count, pad
+constexpr int BINS2 = 4096;                  // histogram of key bits 19..8 inside the threshold bin
+constexpr int HW_DMAX = BINS1 + BINS2, HW_CNT = BINS1 + BINS2 + 1;   // row max error bound; candidate count
+constexpr int HIST_WORDS = BINS1 + BINS2 + 8;
 constexpr int TPB = 256;
 
 __device__ __forceinline__ int n_visible(long long p, long long L, int m, int Nc) {
@@ -70,6 +72,33 @@ __device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* out
     if (lane == 0) scratch[wave] = incl;
     __syncthreads();
     for (int w = wave + 1; w < TPB / 64; ++w) incl += scratch[w];
+    const uint32_t above = incl - s;
+    if (above < need && need <= incl) {
+        uint32_t acc = above;
+        for (int i = per - 1; i >= 0; --i) {
+            const uint32_t c = h[tid * per + i];
+            if (acc + c >= need) { out[0] = tid * per + i; out[1] = acc; break; }
+            acc += c;
+        }
+    }
+    __syncthreads();
+}
+
+// find_bin for a 1024-thread block over BINS1 = 4096 bins (4 per thread).
+__device__ void find_bin_wide(const uint32_t* h, uint32_t need, uint32_t* out, uint32_t* scratch) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int per = BINS1 / blockDim.x;
+    uint32_t s = 0;
+    for (int i = 0; i < per; ++i) s += h[tid * per + i];
+    uint32_t incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_down(incl, o, 64);
+        if (lane + o < 64) incl += v;
+    }
+    if (lane == 0) scratch[wave] = incl;
+    __syncthreads();
+    for (int w = wave + 1; w < nw; ++w) incl += scratch[w];
     const uint32_t above = incl - s;
     if (above < need && need <= incl) {
         uint32_t acc = above;
@@ -283,71 +312,20 @@ __global__ __launch_bounds__(TPB) void k_score(
                 if (lh[lr][i]) atomicAdd(&hist[rr * HIST_WORDS + i], lh[lr][i]);
             if (threadIdx.x == 0 && ldmax[lr]) atomicMax(&hist[rr * HIST_WORDS + HW_DMAX], ldmax[lr]);
         }
-        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
-// k_collect: per-row candidate list
+// candidate lists, then the per-row selection
 // ---------------------------------------------------------------------------
-constexpr int CCHUNK = 4096;     // entries per workgroup (4 waves x 16 groups of 64)
-
-__global__ __launch_bounds__(TPB) void k_collect(const float* __restrict__ S, uint32_t* __restrict__ hist,
-                                                 uint2* __restrict__ list, int Tq, int Nc, int NcP, long long L,
-                                                 int m, long long pos0, int topk)
-{
-    __shared__ uint32_t lh[BINS1];
-    __shared__ uint32_t scratch[TPB];
-    __shared__ uint32_t res[4];
-    __shared__ uint32_t wcount[TPB / 64], wbase[TPB / 64];
-    const int r = blockIdx.y, t = r % Tq;
-    const int nv = n_visible(pos0 + t, L, m, Nc);
-    if (nv <= topk) return;
-    uint32_t* H = hist + (size_t)r * HIST_WORDS;
-    for (int i = threadIdx.x; i < BINS1; i += TPB) lh[i] = H[i];
-    __syncthreads();
-    find_bin(lh, BINS1, (uint32_t)topk, res, scratch);
-    const double thr = (double)key_f32(res[0] << 20) - 2.0 * (double)__uint_as_float(H[HW_DMAX]);
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    const int s_w = blockIdx.x * CCHUNK + wave * (CCHUNK / 4);
-    const float* Sr = S + (size_t)r * NcP;
-    unsigned long long mask[CCHUNK / 4 / 64];
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int gi = 0; gi < CCHUNK / 4 / 64; ++gi) {
-        const int s = s_w + gi * 64 + lane;
-        const bool c = s < nv && (double)Sr[s] >= thr;
-        mask[gi] = __ballot(c);
-        cnt += __popcll(mask[gi]);
-    }
-    if (lane == 0) wcount[wave] = cnt;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t tot = 0;
-        for (int w = 0; w < TPB / 64; ++w) tot += wcount[w];
-        uint32_t base = tot ? atomicAdd(&H[HW_CNT], tot) : 0;
-        for (int w = 0; w < TPB / 64; ++w) { wbase[w] = base; base += wcount[w]; }
-    }
-    __syncthreads();
-    uint32_t pos = wbase[wave];
-    uint2* Lr = list + (size_t)r * NcP;
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int gi = 0; gi < CCHUNK / 4 / 64; ++gi) {
-        const int sidx = s_w + gi * 64 + lane;
-        if ((mask[gi] >> lane) & 1ull)
-            Lr[pos + __popcll(mask[gi] & below)] = make_uint2((uint32_t)sidx, __float_as_uint(Sr[sidx]));
-        pos += __popcll(mask[gi]);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// k_select: one workgroup per query row
-// ---------------------------------------------------------------------------
+// Each k_collect workgroup filters CCHUNK entries of one row against the row's
+// threshold (lower edge of the bin holding the k-th largest S~, minus 2 Dmax),
+// appends (index, S~) pairs to the row's candidate list and builds the second
+// radix level; k_select then selects each row with one workgroup and emits the
+// chosen indices in ascending order without sorting.
 constexpr int STPB = 1024;
-constexpr int MAXK = 4096;
-constexpr int BAND_LDS = 1024;
-constexpr int CAND_LDS = 4096;
+constexpr int CCHUNK = STPB * 16;    // entries per workgroup (16 waves x 16 groups of 64)
+constexpr int BAND_LDS = 1024;       // band entries ranked in LDS (larger bands: 64-bit radix in HBM)
 
 // Wave-cooperative exact score of entry s: HI head groups of LPH lanes, each
 // lane EPL elements; per head, fixed-point window accumulation (as in
@@ -436,150 +414,244 @@ __device__ void wave_find_bin256(const uint32_t* h, uint32_t need, uint32_t abov
     }
 }
 
+// Block-wide exclusive scan (1024 threads); returns the exclusive prefix, *total the sum.
+__device__ uint32_t block_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += x;
+    }
+    if (lane == 63) scratch[wave] = incl;
+    __syncthreads();
+    uint32_t wprefix = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        const uint32_t c = scratch[w];
+        if (w < wave) wprefix += c;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return wprefix + incl - v;
+}
+
+// k_collect: each workgroup filters CCHUNK entries of one row against the row's threshold (lower edge of
+// the bin b1 holding the k-th largest S~, minus 2 Dmax), appends (index, S~) pairs to the row's candidate
+// list in ascending index order (one contiguous run per workgroup, recorded in the chunk table), and
+// histograms key bits 19..8 of the entries inside bin b1 (second radix level).
+__global__ __launch_bounds__(STPB) void k_collect(const float* __restrict__ S, uint32_t* __restrict__ hist,
+                                                  uint2* __restrict__ list, uint2* __restrict__ ctab, int Tq, int Nc,
+                                                  int NcP, long long L, int m, long long pos0, int topk)
+{
+    constexpr int GPW = CCHUNK / (STPB / 64) / 64;   // groups of 64 entries per wave
+    __shared__ uint32_t lh[BINS1];
+    __shared__ uint32_t scratch[STPB / 64], res[4], wcount[STPB / 64], wbase[STPB / 64];
+    const int r = blockIdx.y, t = r % Tq;
+    const int nv = n_visible(pos0 + t, L, m, Nc);
+    if (nv <= topk) return;
+    uint32_t* H = hist + (size_t)r * HIST_WORDS;
+    for (int i = threadIdx.x; i < BINS1; i += STPB) lh[i] = H[i];
+    __syncthreads();
+    find_bin_wide(lh, (uint32_t)topk, res, scratch);
+    const uint32_t b1 = res[0];
+    const double thr = (double)key_f32(b1 << 20) - 2.0 * (double)__uint_as_float(H[HW_DMAX]);
+    for (int i = threadIdx.x; i < BINS2; i += STPB) lh[i] = 0;
+    __syncthreads();
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int s_w = blockIdx.x * CCHUNK + wave * (GPW * 64);
+    const float* Sr = S + (size_t)r * NcP;
+    unsigned long long mask[GPW];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+        const int sidx = s_w + gi * 64 + lane;
+        const float v = sidx < nv ? Sr[sidx] : -INFINITY;
+        const bool c = sidx < nv && (double)v >= thr;
+        if (c) {
+            const uint32_t key = f32_key(v);
+            if ((key >> 20) == b1) atomicAdd(&lh[(key >> 8) & (BINS2 - 1)], 1u);
+        }
+        mask[gi] = __ballot(c);
+        cnt += __popcll(mask[gi]);
+    }
+    if (lane == 0) wcount[wave] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t tot = 0;
+        for (int w = 0; w < STPB / 64; ++w) tot += wcount[w];
+        uint32_t base = tot ? atomicAdd(&H[HW_CNT], tot) : 0;
+        ctab[(size_t)r * (NcP / CCHUNK) + blockIdx.x] = make_uint2(base, tot);
+        for (int w = 0; w < STPB / 64; ++w) { wbase[w] = base; base += wcount[w]; }
+    }
+    __syncthreads();
+    uint32_t pos = wbase[wave];
+    uint2* Lr = list + (size_t)r * NcP;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+        const int sidx = s_w + gi * 64 + lane;
+        if ((mask[gi] >> lane) & 1ull)
+            Lr[pos + __popcll(mask[gi] & below)] = make_uint2((uint32_t)sidx, __float_as_uint(Sr[sidx]));
+        pos += __popcll(mask[gi]);
+    }
+    for (int i = threadIdx.x; i < BINS2; i += STPB)
+        if (lh[i]) atomicAdd(&H[BINS1 + i], lh[i]);
+}
+
+// k_select: one 1024-thread workgroup per row (see the header for the argument).  Candidates are addressed
+// in ascending index order through the chunk table ("sorted position" e).
 template <int DT, int DI, int HI>
 __global__ __launch_bounds__(STPB) void k_select(
-    const uint32_t* __restrict__ hist, const uint2* __restrict__ list,
-    uint32_t* __restrict__ band_g, unsigned long long* __restrict__ bkey_g,
+    const uint32_t* __restrict__ hist, const uint2* __restrict__ list, const uint2* __restrict__ ctab,
+    uint2* __restrict__ band_g, unsigned long long* __restrict__ bkey_g, uint8_t* __restrict__ flag_g,
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int topk,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
 {
     constexpr int ES = DT == 0 ? 2 : 1;
-    __shared__ int32_t sel[MAXK];
-    __shared__ uint32_t hst[256];
-    __shared__ uint32_t res[4];
-    __shared__ uint32_t nsel, nband;
+    __shared__ uint32_t lh[BINS1];
+    __shared__ uint32_t scratch[STPB / 64], res[4], nband;
+    __shared__ uint32_t cpre[STPB + 1], cbase[STPB];
     __shared__ unsigned long long bkey[BAND_LDS];
-    __shared__ uint32_t bidx[BAND_LDS];
-    __shared__ uint2 cand[CAND_LDS];
+    __shared__ uint32_t bpos[BAND_LDS];
     const int r = blockIdx.x, b = r / Tq, t = r % Tq, tid = threadIdx.x;
     const int lane = lane_id(), wave = tid >> 6;
     const int nv = n_visible(pos0 + t, L, m, Nc);
     int32_t* out = idx_out + (size_t)r * topk;
-    if (nv <= topk) {
+    if (nv <= topk) {                                 // every visible entry is selected
         for (int i = tid; i < topk; i += STPB) out[i] = i < nv ? i : -1;
         if (cnt_out && tid == 0) cnt_out[r] = nv;
         return;
     }
     const uint32_t* H = hist + (size_t)r * HIST_WORDS;
-    const uint32_t n = H[HW_CNT];
     const float dmax = __uint_as_float(H[HW_DMAX]);
-    const uint2* Lg = list + (size_t)r * NcP;
-    // candidates (index, score bits) live in LDS when they fit, else are read from the global list
-    const bool in_lds = n <= (uint32_t)CAND_LDS;
-    if (in_lds)
-        for (uint32_t i = tid; i < n; i += STPB) cand[i] = Lg[i];
-    __syncthreads();
-    const uint2* Lr = in_lds ? cand : Lg;
-
-    // 1. tau = exact k-th largest S~ among the candidates (radix, 8 bits per pass)
-    uint32_t prefix = 0, above = 0;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        for (int i = tid; i < 256; i += STPB) hst[i] = 0;
-        __syncthreads();
-        for (uint32_t i = tid; i < n; i += STPB) {
-            const uint32_t key = f32_key(__uint_as_float(Lr[i].y));
-            if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))) atomicAdd(&hst[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) wave_find_bin256(hst, (uint32_t)topk, above, res);
-        __syncthreads();
-        prefix |= res[0] << shift;
-        above = res[1];
+    const uint2* Lr = list + (size_t)r * NcP;
+    uint8_t* F = flag_g + (size_t)r * NcP;
+    // chunk table -> prefix of counts in chunk (= index) order
+    const int NCH = NcP / CCHUNK;                     // <= 1024
+    uint32_t total;
+    {
+        const uint2 c = tid < NCH ? ctab[(size_t)r * NCH + tid] : make_uint2(0u, 0u);
+        const uint32_t pre = block_scan(c.y, scratch, &total);
+        if (tid < NCH) { cpre[tid] = pre; cbase[tid] = c.x; }
+        if (tid == 0) cpre[NCH] = total;
         __syncthreads();
     }
-    const float tau = key_f32(prefix);
+    const uint32_t n = total;
+    auto cand = [&](uint32_t e) -> uint2 {            // e-th candidate in index order
+        int lo_c = 0, hi_c = NCH - 1;                 // largest c with cpre[c] <= e: a non-empty chunk holding e
+        while (lo_c < hi_c) {
+            const int mid = (lo_c + hi_c + 1) >> 1;
+            if (cpre[mid] <= e) lo_c = mid; else hi_c = mid - 1;
+        }
+        return Lr[cbase[lo_c] + (e - cpre[lo_c])];
+    };
+
+    // 1. tau: the bin b1 (level 1), then b2 (level 2, built by k_collect), then the last 8 bits
+    for (int i = tid; i < BINS1; i += STPB) lh[i] = H[i];
+    __syncthreads();
+    find_bin_wide(lh, (uint32_t)topk, res, scratch);
+    const uint32_t b1 = res[0], a1 = res[1];
+    __syncthreads();
+    for (int i = tid; i < BINS2; i += STPB) lh[i] = H[BINS1 + i];
+    __syncthreads();
+    find_bin_wide(lh, (uint32_t)topk - a1, res, scratch);
+    const uint32_t b2 = res[0], a2 = res[1];
+    __syncthreads();
+    const uint32_t pfx = (b1 << 12) | b2;
+    for (int i = tid; i < 256; i += STPB) lh[i] = 0;
+    __syncthreads();
+    for (uint32_t e = tid; e < n; e += STPB) {
+        const uint32_t key = f32_key(__uint_as_float(cand(e).y));
+        if ((key >> 8) == pfx) atomicAdd(&lh[key & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) wave_find_bin256(lh, (uint32_t)topk - a1 - a2, 0u, res);
+    __syncthreads();
+    const float tau = key_f32((pfx << 8) | res[0]);
     const double lo = (double)tau - 2.0 * (double)dmax, hi = (double)tau + 2.0 * (double)dmax;
 
-    // 2. classify: certainly in -> sel[]; band -> band list
-    if (tid == 0) { nsel = 0; nband = 0; }
+    // 2. classify: flag 1 = certainly in, 2 = band (listed with its position), 0 = out
+    if (tid == 0) nband = 0;
     __syncthreads();
-    uint32_t* Bg = band_g + (size_t)r * NcP;
-    for (uint32_t i = tid; i < n; i += STPB) {
-        const uint2 c = Lr[i];
+    uint2* Bg = band_g + (size_t)r * NcP;
+    uint32_t my_in = 0;
+    for (uint32_t e = tid; e < n; e += STPB) {
+        const uint2 c = cand(e);
         const double v = (double)__uint_as_float(c.y);
-        if (v > hi) sel[atomicAdd(&nsel, 1u)] = (int32_t)c.x;
-        else if (v >= lo) Bg[atomicAdd(&nband, 1u)] = c.x;
+        uint8_t f = 0;
+        if (v > hi) { f = 1; ++my_in; }
+        else if (v >= lo) { f = 2; Bg[atomicAdd(&nband, 1u)] = make_uint2(c.x, e); }
+        F[e] = f;
     }
+    uint32_t n_in;
+    block_scan(my_in, scratch, &n_in);
     __syncthreads();
-    const uint32_t n_in = nsel, nb = nband;
+    const uint32_t nb = nband;
     const uint32_t need = (uint32_t)topk - n_in;       // 0 <= need <= nb by construction
 
-    // 3. exact rescoring of the band (one wave per entry), composite keys
-    //    (exact score key, inverted index): larger composite = earlier in the order
+    // 3. exact rescoring of the band (one wave per entry); composite keys (exact score key,
+    //    inverted index): larger composite = earlier in the order
     unsigned long long* Kg = bkey_g + (size_t)r * NcP;
     const char* qrow = (const char*)q_idx + (size_t)r * HI * DI * ES;
     const float* wrow = w_idx + (size_t)r * HI;
     if (need > 0 && need < nb) {
         for (uint32_t i = wave; i < nb; i += STPB / 64) {
-            const uint32_t s = Bg[i];
-            const float sx = wave_exact_score<DT, DI, HI>(qrow, wrow, (const char*)k_idx + ((size_t)b * Nc + s) * DI * ES);
+            const uint2 be = Bg[i];
+            const float sx = wave_exact_score<DT, DI, HI>(qrow, wrow, (const char*)k_idx + ((size_t)b * Nc + be.x) * DI * ES);
             if (lane == 0) {
-                const unsigned long long ck = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - s);
+                const unsigned long long ck = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - be.x);
                 Kg[i] = ck;
-                if (i < BAND_LDS) { bkey[i] = ck; bidx[i] = s; }
+                if (i < BAND_LDS) { bkey[i] = ck; bpos[i] = be.y; }
             }
         }
     }
     __syncthreads();
 
-    // 4. the `need` largest composite keys among the band
+    // 4. the `need` largest composite keys among the band get flag 1
     if (need > 0 && need == nb) {
-        for (uint32_t i = tid; i < nb; i += STPB) sel[n_in + i] = (int32_t)Bg[i];
+        for (uint32_t i = tid; i < nb; i += STPB) F[Bg[i].y] = 1;
     } else if (need > 0 && nb <= BAND_LDS) {
-        // rank by counting (composite keys are distinct)
-        for (uint32_t i = tid; i < nb; i += STPB) {
+        for (uint32_t i = tid; i < nb; i += STPB) {          // rank by counting (keys are distinct)
             const unsigned long long ki = bkey[i];
             uint32_t rank = 0;
             for (uint32_t j = 0; j < nb; ++j) rank += bkey[j] > ki;
-            if (rank < need) sel[n_in + rank] = (int32_t)bidx[i];
+            if (rank < need) F[bpos[i]] = 1;
         }
     } else if (need > 0) {
-        // large band: radix select on the 64-bit composite keys, 8 bits per pass
-        unsigned long long pfx = 0;
+        unsigned long long kp = 0;
         uint32_t ab = 0;
         for (int pass = 0; pass < 8; ++pass) {
             const int shift = 56 - 8 * pass;
-            for (int i = tid; i < 256; i += STPB) hst[i] = 0;
+            for (int i = tid; i < 256; i += STPB) lh[i] = 0;
             __syncthreads();
             for (uint32_t i = tid; i < nb; i += STPB) {
                 const unsigned long long key = Kg[i];
-                if (pass == 0 || (key >> (shift + 8)) == (pfx >> (shift + 8))) atomicAdd(&hst[(key >> shift) & 255u], 1u);
+                if (pass == 0 || (key >> (shift + 8)) == (kp >> (shift + 8))) atomicAdd(&lh[(key >> shift) & 255u], 1u);
             }
             __syncthreads();
-            if (wave == 0) wave_find_bin256(hst, need, ab, res);
+            if (wave == 0) wave_find_bin256(lh, need, ab, res);
             __syncthreads();
-            pfx |= (unsigned long long)res[0] << shift;
+            kp |= (unsigned long long)res[0] << shift;
             ab = res[1];
             __syncthreads();
         }
-        if (tid == 0) nsel = n_in;
-        __syncthreads();
         for (uint32_t i = tid; i < nb; i += STPB)
-            if (Kg[i] >= pfx) sel[atomicAdd(&nsel, 1u)] = (int32_t)(0xffffffffu - (uint32_t)(Kg[i] & 0xffffffffu));
+            if (Kg[i] >= kp) F[Bg[i].y] = 1;
     }
+    __threadfence_block();
     __syncthreads();
 
-    // 5. ascending order: bitonic sort of sel[0..P), padded with INT_MAX
-    int P = 1;
-    while (P < topk) P <<= 1;
-    for (int i = topk + tid; i < P; i += STPB) sel[i] = 0x7fffffff;
-    __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < P; i += STPB) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const int a = sel[i], c = sel[ixj];
-                    const bool up = (i & k) == 0;
-                    if ((a > c) == up) { sel[i] = c; sel[ixj] = a; }
-                }
-            }
-            __syncthreads();
-        }
-    }
-    for (int i = tid; i < topk; i += STPB) out[i] = sel[i];
+    // 5. compaction in index order: thread tid owns positions [tid*per, (tid+1)*per)
+    const uint32_t per = (n + STPB - 1) / STPB;
+    const uint32_t e0 = min(n, tid * per), e1 = min(n, e0 + per);
+    uint32_t mine = 0;
+    for (uint32_t e = e0; e < e1; ++e) mine += F[e] == 1;
+    uint32_t tot2;
+    uint32_t o = block_scan(mine, scratch, &tot2);
+    for (uint32_t e = e0; e < e1; ++e)
+        if (F[e] == 1 && o < (uint32_t)topk) out[o++] = (int32_t)cand(e).x;
     if (cnt_out && tid == 0) cnt_out[r] = topk;
 }
 
@@ -592,12 +664,13 @@ namespace csa_host {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// S~ [R][NcP] f32 | hist [R][HIST_WORDS] | list [R][NcP] (u32,u32) | band [R][NcP] u32 | band keys [R][NcP] u64
+// S~ [R][NcP] f32 | hist [R][HIST_WORDS] | list [R][NcP] (index, S~) | chunk table [R][NcP/CCHUNK] |
+// band [R][NcP] (index, position) | band keys [R][NcP] u64 | flags [R][NcP] u8
 size_t index_topk_ws_bytes(int B, int Tq, int Nc) {
     const size_t R = (size_t)B * Tq;
     const size_t NcP = ((size_t)Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
-    return align256(R * NcP * 4) + align256(R * HIST_WORDS * 4) + align256(R * NcP * 8) + align256(R * NcP * 4) +
-           align256(R * NcP * 8);
+    return align256(R * NcP * 4) + align256(R * HIST_WORDS * 4) + align256(R * NcP * 8) +
+           align256(R * (NcP / CCHUNK) * 8) + align256(R * NcP * 8) + align256(R * NcP * 8) + align256(R * NcP);
 }
 
 template <int DT, int DI, int HI>
@@ -610,8 +683,10 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
     float* S = (float*)p;                       p += align256(R * (size_t)NcP * 4);
     uint32_t* hist = (uint32_t*)p;              p += align256(R * HIST_WORDS * 4);
     uint2* list = (uint2*)p;                    p += align256(R * (size_t)NcP * 8);
-    uint32_t* band = (uint32_t*)p;              p += align256(R * (size_t)NcP * 4);
-    unsigned long long* bkey = (unsigned long long*)p;
+    uint2* ctab = (uint2*)p;                    p += align256(R * (size_t)(NcP / CCHUNK) * 8);
+    uint2* band = (uint2*)p;                    p += align256(R * (size_t)NcP * 8);
+    unsigned long long* bkey = (unsigned long long*)p; p += align256(R * (size_t)NcP * 8);
+    uint8_t* flags = (uint8_t*)p;
     {
         const size_t n = R * HIST_WORDS;
         const int blocks = (int)std::min<size_t>((n + 255) / 256, 2048);
@@ -627,10 +702,10 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
 #endif
     CSA_LAUNCH("k_score", (k_score<DT, DI, HI>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
                q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist);
-    CSA_LAUNCH("k_collect", k_collect, dim3(NcP / CCHUNK, (unsigned)R), dim3(TPB), 0, st, S, hist, list, Tq, Nc, NcP,
-               L, m, pos0, topk);
-    CSA_LAUNCH("k_select", (k_select<DT, DI, HI>), dim3((unsigned)R), dim3(STPB), 0, st, hist, list, band, bkey,
-               q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out);
+    CSA_LAUNCH("k_collect", k_collect, dim3(NcP / CCHUNK, (unsigned)R), dim3(STPB), 0, st, S, hist, list, ctab, Tq,
+               Nc, NcP, L, m, pos0, topk);
+    CSA_LAUNCH("k_select", (k_select<DT, DI, HI>), dim3((unsigned)R), dim3(STPB), 0, st, hist, list, ctab, band,
+               bkey, flags, q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out);
     return 0;
 }
 
