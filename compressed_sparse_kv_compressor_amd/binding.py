@@ -45,6 +45,7 @@ def _load():
         "csa_debug_fp8_to_bf16": ([P, P, I, P], I),
         "csa_prof_enable": ([I], I),
         "csa_prof_reset": ([], I),
+        "csa_prof_only": ([ctypes.c_char_p], I),
         "csa_prof_read": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)], I),
     }
     for name, (args, res) in sig.items():
@@ -59,7 +60,8 @@ lib = _load()
 EXPORTED = ("csa_abi_version", "csa_status_str", "csa_last_error", "csa_compress_ws_bytes", "csa_compress",
             "csa_index_topk_ws_bytes", "csa_index_topk", "csa_sparse_attn_ws_bytes", "csa_sparse_attn",
             "hca_dense_attn_ws_bytes", "hca_dense_attn", "csa_hca_decode_ws_bytes", "csa_hca_decode",
-            "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read")
+            "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read",
+            "csa_prof_only")
 
 
 class DecodeArgs(ctypes.Structure):
@@ -177,6 +179,11 @@ def csa_debug_fp8_to_bf16(inp, out, stream=None):
 
 def prof_enable(on: bool):
     _check(lib.csa_prof_enable(1 if on else 0))
+
+
+def prof_only(kernel):
+    """Record only launches of `kernel` (None: all)."""
+    _check(lib.csa_prof_only(kernel.encode() if kernel else None))
 
 
 def prof_reset():

@@ -34,6 +34,7 @@ struct ProfRec {
 };
 static std::mutex g_prof_mu;
 static bool g_prof_on = false;
+static std::string g_prof_only;          // non-empty: record only launches of this kernel
 static std::vector<ProfRec> g_prof;
 static std::vector<hipEvent_t> g_ev_pool;
 
@@ -51,6 +52,7 @@ static hipEvent_t take_event() {
 void* prof_begin(const char* name, hipStream_t s) {
     if (!g_prof_on) return nullptr;
     std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_only.empty() && g_prof_only != name) return nullptr;
     ProfRec r;
     r.name = name;
     r.a = take_event();
@@ -250,7 +252,7 @@ int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int
 
 size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W) {
     if (B < 1 || Tq < 1 || H < 1 || topk < 0 || W < 0) return 0;
-    return csa_host::attn_ws_bytes(B, Tq, H, D, topk + W);
+    return csa_host::attn_ws_bytes(B, Tq, H, D, 1, topk, W);
 }
 
 int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const void* kv_raw, int B, int Tq, int H, int D,
@@ -260,7 +262,7 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
     csa_host::g_err[0] = 0;
     int rc = validate_sparse(fn, q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse_out);
     if (rc) return rc;
-    rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, topk + W));
+    rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, 1, topk, W));
     if (rc) return rc;
     csa_host::AttnRows r{1, kv, Nc, 0, 1, idx, topk, kv_raw, Lr, raw0, W};
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
@@ -269,7 +271,7 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
 
 size_t hca_dense_attn_ws_bytes(int B, int Tq, int H, int D, int Nh) {
     if (B < 1 || Tq < 1 || H < 1 || Nh < 0) return 0;
-    return csa_host::attn_ws_bytes(B, Tq, H, D, Nh);
+    return csa_host::attn_ws_bytes(B, Tq, H, D, 0, Nh, 0);
 }
 
 int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D, int Nh, long long L, int mh,
@@ -278,7 +280,7 @@ int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D,
     csa_host::g_err[0] = 0;
     int rc = validate_dense(fn, q, kv_h, B, Tq, H, D, Nh, L, mh, pos0, scale, out, lse_out);
     if (rc) return rc;
-    rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, Nh));
+    rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, 0, Nh, 0));
     if (rc) return rc;
     csa_host::AttnRows r{0, kv_h, Nh, L, mh, nullptr, 0, nullptr, 0, 0, 0};
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
@@ -293,8 +295,8 @@ size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a) {
     const int Nc = (int)((a->L + a->m - 1) / a->m), Nh = (int)((a->L + a->mh - 1) / a->mh);
     size_t s = a->idx_out ? 0 : align256((size_t)a->B * a->topk * 4);
     s += align256(csa_host::index_topk_ws_bytes(a->B, 1, Nc));
-    s += std::max(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, a->topk + a->W),
-                  csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, Nh));
+    s += std::max(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 1, a->topk, a->W),
+                  csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 0, Nh, 0));
     return s;
 }
 
@@ -352,6 +354,12 @@ int csa_debug_fp8_to_bf16(const void* in, void* out, int n, void* stream) {
 int csa_prof_enable(int on) {
     std::lock_guard<std::mutex> lk(csa_host::g_prof_mu);
     csa_host::g_prof_on = on != 0;
+    return CSA_OK;
+}
+
+int csa_prof_only(const char* kernel) {
+    std::lock_guard<std::mutex> lk(csa_host::g_prof_mu);
+    csa_host::g_prof_only = kernel ? kernel : "";
     return CSA_OK;
 }
 

@@ -20,6 +20,8 @@
 //   * with one split the kernel normalises and writes bf16 output + LSE;
 //     otherwise it writes unnormalised fp32 partials that k_combine merges in a
 //     fixed split order (deterministic).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -239,11 +241,31 @@ __device__ __forceinline__ int swz(int r, int c) {   // element offset of (row, 
     return r * HD + (((c >> 3) ^ swz_chunk(r)) << 3) + (c & 7);
 }
 
+// Raw buffer resource (stride 0, byte offsets) over [base, base + bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+#ifndef CSA_ATTN32_QK_AHEAD
+#define CSA_ATTN32_QK_AHEAD 4      // K-operand LDS reads in flight ahead of the QK MFMAs
+#endif
+#ifndef CSA_ATTN32_PV_AHEAD
+#define CSA_ATTN32_PV_AHEAD 2      // d-tiles of V reads in flight ahead of the PV MFMAs
+#endif
 #ifndef CSA_ATTN32_WAVES_PER_EU
 #define CSA_ATTN32_WAVES_PER_EU 1
 #endif
-// MODE 0: dense prefix (row r = entry r); MODE 1: selected entries then window rows.
-template <int MODE>
+// Masked rows get -2^100 added to their scores by one extra MFMA k-step (A: a 1 in column 0 of each
+// masked row; B: -2^100 in row 0, d-half 0 only), which sends their probabilities to exactly 0
+// without any per-element select on the common path.  A tile or split with no valid row at all ends
+// with a running max below EMPTY_M, which the merge treats as empty.
+constexpr uint32_t BF16_ONE = 0x3f80u, BF16_NEG_2P100 = 0xf180u;
+constexpr float EMPTY_M = -1.0e25f;
+
+// MODE 0: dense prefix (row r = entry r); MODE 1: selected entries then window rows.  BIG: some
+// array is beyond the reach of 32-bit byte offsets, so tiles are loaded with 64-bit addresses (the
+// other variant uses buffer loads only, which keeps the LDS wait counting exact in the main loop).
+template <int MODE, bool BIG>
 __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
     const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
     int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
@@ -252,62 +274,44 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
     constexpr int D = 512;
     constexpr int KS = HD / 16;               // 32x32x16 k-steps over a d-half
     constexpr int DT = HD / 32;               // 32-wide d tiles of a d-half
-    __shared__ __attribute__((aligned(16))) uint16_t bufA[4 * TILE * HD];     // 64 KiB: tile buffer 0 of each wave
-    __shared__ __attribute__((aligned(16))) uint16_t bufB[4 * TILE * HD];     // 64 KiB: tile buffer 1 of each wave
-    __shared__ __attribute__((aligned(16))) float sx[4][16][64];              // 16 KiB
+    __shared__ __attribute__((aligned(1024))) uint16_t bufA[4 * TILE * HD];   // 64 KiB: tile buffer 0 of each wave
+    __shared__ __attribute__((aligned(1024))) uint16_t bufB[4 * TILE * HD];   // 64 KiB: tile buffer 1 of each wave
+    __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];         // 32 KiB: [tile parity][wave][j/4][lane][j%4]
 
     const int HG = H / 32;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int hg = slot % HG, unit = (slot / HG) * 8 + xcd;
     if (unit >= nunits) return;                // padding workgroups (uniform exit)
     const int bt = unit / nsplit, split = unit % nsplit;
-    const int lane = lane_id(), w = threadIdx.x >> 6;
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // w: wave-uniform
     const int pr = w & 1, dh = w >> 1;         // row half, d half
     const int hl = lane & 31, g = lane >> 5;
     const int h = hg * 32 + hl;
-    uint16_t* const ta = bufA + w * (TILE * HD);
-    uint16_t* const tb = bufB + w * (TILE * HD);
 
     const int b = bt / Tq;
     const long long p = pos0 + bt % Tq;
+    // MODE 1 row space: [0, topk) selected entries, [topk, topk32) masked padding (so that no tile
+    // mixes the two sources), [topk32, topk32 + window) raw window rows.
+    const int topk32 = MODE == 1 ? (R.topk + TILE - 1) / TILE * TILE : 0;
     int nrows;
     long long w0 = 0;
     if (MODE == 0) {
         nrows = dense_visible(p, R.L, R.ratio, R.N);
     } else {
         w0 = p - R.W + 1 < 0 ? 0 : p - R.W + 1;
-        nrows = R.topk + (R.W > 0 ? (int)(p - w0 + 1) : 0);
+        nrows = topk32 + (R.W > 0 ? (int)(p - w0 + 1) : 0);
     }
     const int s_begin = split * rps;
     const int s_end = min(nrows, s_begin + rps);
-    const int per_pair = rps / 2;              // multiple of TILE
+    const int per_pair = rps / 2;              // multiple of 2 TILE
     const int r_begin = s_begin + pr * per_pair;
     const int r_end = min(s_end, r_begin + per_pair);
-    const int ntiles = per_pair / TILE;        // same count for every wave (barriers inside)
+    // even tile count, the same for every wave (barriers inside); an empty split runs no tile
+    const int ntiles = s_begin < nrows ? per_pair / TILE : 0;
 
     const uint16_t* kvb = R.kv ? R.kv + (size_t)b * R.N * D : nullptr;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
-    const uint16_t* fallback = kvb ? kvb : rawb;          // a valid row for masked slots
-
-    // Row code of row r: >= 0 entry index in kv, <= -2 raw row (-code-2), -1 masked.
-    auto row_code = [&](int r) -> int {
-        if (r >= r_end) return -1;
-        if constexpr (MODE == 0) {
-            return r;
-        } else {
-            if (r < R.topk) return R.idx[(size_t)bt * R.topk + r];    // (< 0 -> masked)
-            return -2 - (int)(w0 + (r - R.topk) - R.raw0);
-        }
-    };
-    auto row_ptr = [&](int c) -> const uint16_t* {
-        if (c >= 0) return kvb + (size_t)c * D;
-        if constexpr (MODE == 0) {
-            return nullptr;
-        } else {
-            if (c == -1) return nullptr;
-            return rawb + (size_t)(-c - 2) * D;
-        }
-    };
+    constexpr bool kv32 = !BIG, raw32 = !BIG;  // 32-bit byte offsets reach every row (buffer loads)
 
     bf16x8_t qreg[KS];
     {
@@ -315,6 +319,7 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
 #pragma unroll
         for (int s = 0; s < KS; ++s) qreg[s] = as_bf16x8(*(const u32x4_t*)(qp + 16 * s));
     }
+    const bf16x8_t qmask = as_bf16x8(u32x4_t{g == 0 && dh == 0 ? BF16_NEG_2P100 : 0u, 0u, 0u, 0u});
     f32x16_t acc[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i)
@@ -324,106 +329,203 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
 
     const int b16 = lane >> 4, j16 = lane & 15;
     const int tr_row = 4 * (b16 >> 1) + (j16 >> 2);
-    const int tr_col = 16 * (b16 & 1) + 4 * (j16 & 3);
     const int rsub = lane >> 5, pch = lane & 31;
 
-    // codes of the lane's 16 rows (2 i + rsub) of tile it
+    // Loads of one tile.  Instruction i moves row slots 2i (lanes 0-31) and 2i+1 (lanes 32-63) of this
+    // d-half, 16 B per lane, landing at (tile + 1024 i + 16 lane); the XOR swizzle goes on the source:
+    // the lane fetches logical chunk pch ^ swz_chunk(2i + rsub) = (pch ^ 4 rsub) ^ kappa(i) with
+    // kappa(i) = 8 (i & 1) | ((i >> 1) & 3).  Masked slots load a valid row (their data is never weighted).
+    auto kappa = [](int i) -> uint32_t { return (uint32_t)(8 * (i & 1) | ((i >> 1) & 3)); };
+    const uint32_t lane_chunk = 16u * (uint32_t)(pch ^ (4 * rsub));
+    const uint32_t lane_row = (uint32_t)rsub * (D * 2);
+
+    // MODE 1: entry indices of the lane's 16 row slots of a tile, loaded one tile ahead and only
+    // used after the next full wait (a use right after the load would also wait for the tile loads).
     int code[TILE / 2];
     auto fetch_codes = [&](int it) {
-        if constexpr (MODE == 0) {
-            code[0] = r_begin + it * TILE;                            // dense: the tile's first row
-        } else {
-#pragma unroll
-            for (int i = 0; i < TILE / 2; ++i) code[i] = row_code(r_begin + it * TILE + 2 * i + rsub);
-        }
-    };
-    // Direct global->LDS loads (16 B per lane; lane l lands at base + 16 l): one
-    // instruction moves rows (2i, 2i+1) of this d-half; the XOR swizzle goes on
-    // the source address.  Masked rows read a valid row and are excluded by the
-    // returned validity mask.  Issues no other memory operation.
-    auto issue_tile = [&](uint16_t* buf) -> uint32_t {
-        if constexpr (MODE == 0) {
-            // dense rows are consecutive entries starting at code[0] (wave-uniform)
-            const int first = code[0];
-            const int nval = max(0, min(TILE, r_end - first));
-            const uint16_t* base = kvb + (size_t)(nval > 0 ? first : 0) * D + dh * HD;
+        if constexpr (MODE == 1) {
+            const int r0 = r_begin + it * TILE;
 #pragma unroll
             for (int i = 0; i < TILE / 2; ++i) {
-                const int row = 2 * i + rsub;
-                const int rr = row < nval ? row : 0;                  // past the end: reread row 0 (masked)
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void*)(base + (size_t)rr * D + ((pch ^ swz_chunk(row)) << 3)),
-                    (CSA_LDS void*)(buf + i * 2 * HD), 16, 0, 0);
+                const int r = r0 + 2 * i + rsub;
+                code[i] = (r < r_end && r < R.topk) ? R.idx[(size_t)bt * R.topk + r] : -1;
+            }
+        }
+    };
+    // Buffer resources over this d-half of the batch's rows (raw buffer, byte offsets).  An absent
+    // array gets an empty resource: nothing is ever loaded through it.
+    const bool has_kv = kvb && kv32, has_raw = MODE == 1 && rawb && raw32;
+    const __amdgpu_buffer_rsrc_t rs_kv =
+        make_rsrc(has_kv ? kvb + dh * HD : nullptr, has_kv ? (uint32_t)((size_t)R.N * D * 2 - dh * HD * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rs_raw =
+        make_rsrc(has_raw ? rawb + dh * HD : nullptr, has_raw ? (uint32_t)((size_t)R.Lr * D * 2 - dh * HD * 2) : 0u);
+    const int raw_first = MODE == 1 ? (int)(w0 - R.raw0) : 0;         // raw row of the first window row
+    auto issue_tile = [&](bool second, int it) -> uint32_t {
+        CSA_LDS char* lb = (second ? (CSA_LDS char*)bufB : (CSA_LDS char*)bufA) + w * (TILE * HD * 2);
+        const int r0 = r_begin + it * TILE;
+        // one instruction: 16 B per lane from (resource + soffset + voffset) to (lb + 1024 i + 16 lane)
+        auto bdma = [&](__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, int i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (CSA_LDS void*)(lb + 1024 * i), 16, (int)voff, (int)soff, 0, 0);
+        };
+        auto gdma = [&](const void* src, int i) {
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                             (CSA_LDS void*)(lb + 1024 * i), 16, 0, 0);
+        };
+        const int nval = max(0, min(TILE, r_end - r0));
+        if constexpr (MODE == 0) {
+            if constexpr (kv32) {
+                if (r0 + TILE <= R.N) {                 // all 32 row slots lie inside the array
+#pragma unroll
+                    for (int i = 0; i < TILE / 2; ++i)
+                        bdma(rs_kv, (lane_row + lane_chunk) ^ (16u * kappa(i)), (uint32_t)r0 * (D * 2) + 2048u * i, i);
+                } else {                                // tail: slots past the array reread row 0
+#pragma unroll
+                    for (int i = 0; i < TILE / 2; ++i) {
+                        const int r = r0 + 2 * i + rsub;
+                        bdma(rs_kv, (uint32_t)(r < R.N ? r : 0) * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < TILE / 2; ++i) {
+                    const int r = r0 + 2 * i + rsub;
+                    gdma((const char*)(kvb + (size_t)(r < R.N ? r : 0) * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
+                }
             }
             return nval >= 32 ? 0xffffffffu : ((1u << nval) - 1u);
-        }
-        uint32_t vm = 0;
+        } else {
+            uint32_t vm = 0;
+            if (r0 < topk32) {                          // selected entries (masked slots read row 0)
+                uint32_t roff[TILE / 2];
 #pragma unroll
-        for (int i = 0; i < TILE / 2; ++i) {
-            const int row = 2 * i + rsub;
-            const uint16_t* src = row_ptr(code[i]);
-            const unsigned long long bal = __ballot(src != nullptr);
-            vm |= (uint32_t)(bal & 1ull) << (2 * i);
-            vm |= (uint32_t)((bal >> 32) & 1ull) << (2 * i + 1);
-            const uint16_t* s8 = (src ? src : fallback) + dh * HD + ((pch ^ swz_chunk(row)) << 3);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)s8,
-                                             (CSA_LDS void*)(buf + i * 2 * HD), 16, 0, 0);
+                for (int i = 0; i < TILE / 2; ++i) {
+                    const bool ok = code[i] >= 0;
+                    const unsigned long long bal = __ballot(ok);
+                    vm |= (uint32_t)(bal & 1ull) << (2 * i);
+                    vm |= (uint32_t)((bal >> 32) & 1ull) << (2 * i + 1);
+                    roff[i] = ok ? (uint32_t)code[i] : 0u;
+                }
+                if constexpr (kv32) {
+#pragma unroll
+                    for (int i = 0; i < TILE / 2; ++i) bdma(rs_kv, roff[i] * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < TILE / 2; ++i)
+                        gdma((const char*)(kvb + (size_t)roff[i] * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
+                }
+            } else {                                    // raw window rows (masked slots read the first one)
+                const int u0 = raw_first + (r0 - topk32);                   // raw row of slot 0
+                vm = nval >= 32 ? 0xffffffffu : ((1u << nval) - 1u);
+                if constexpr (raw32) {
+                    if (nval == TILE) {
+#pragma unroll
+                        for (int i = 0; i < TILE / 2; ++i)
+                            bdma(rs_raw, (lane_row + lane_chunk) ^ (16u * kappa(i)), (uint32_t)u0 * (D * 2) + 2048u * i, i);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < TILE / 2; ++i) {
+                            const int slot = 2 * i + rsub;
+                            const int u = slot < nval ? u0 + slot : raw_first;
+                            bdma(rs_raw, (uint32_t)u * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < TILE / 2; ++i) {
+                        const int slot = 2 * i + rsub;
+                        const int u = slot < nval ? u0 + slot : raw_first;
+                        gdma((const char*)(rawb + (size_t)u * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
+                    }
+                }
+            }
+            return vm;
         }
-        return vm;
+    };
+
+    // Byte offsets of this lane's reads inside a wave's tile.  With the tile 512-byte aligned the swizzled
+    // address of k-step s is (base + qk_off) ^ 32 s, and that of the transposed read of rows 8k.. and d-tile d
+    // is ((base + tr_off) ^ (64 d + 32 (k & 1))) + 4096 k (the XOR touches bits 5..8 only).
+    // (Offsets include the wave's tile, w * 16 KiB, which the XOR leaves alone.)
+    const uint32_t qk_off = w * (TILE * HD * 2) + hl * 512 + 16 * (g ^ swz_chunk(hl));
+    const uint32_t tr_off = w * (TILE * HD * 2) + tr_row * 512 +
+                            16 * ((2 * (b16 & 1) + ((j16 >> 1) & 1)) ^ swz_chunk(tr_row)) + 8 * (j16 & 1);
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+    // max / sum over the two lane halves (the two 16-row groups of a head's column)
+    auto xhalf_max = [](float v) -> float {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    };
+    auto xhalf_sum = [](float v) -> float {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
     };
 
     // Compute on one tile; the loads of the next tile (into the other LDS object) stay in flight.
-    auto compute_tile = [&](const uint16_t* tile, uint32_t vmask) {
-        const CSA_LDS uint16_t* tl = (const CSA_LDS uint16_t*)tile;
-        // ---- partial S^T[32 rows][32 heads] over this d-half ----
-        f32x16_t sacc, sacc1;                    // two chains: even / odd k-steps
+    // Addresses are formed from the buffer object itself so that the compiler can tell them apart
+    // from the in-flight loads into the other buffer.
+    auto compute_tile = [&](bool second, uint32_t vmask, int par) {
+        const CSA_LDS char* gb = second ? (const CSA_LDS char*)bufB : (const CSA_LDS char*)bufA;
+        uint32_t qb = qk_off, trb = tr_off;
+        asm volatile("" : "+v"(qb), "+v"(trb));   // keep the per-read XORs in the loop (no hoisted address table)
+        // ---- partial S^T[32 rows][32 heads] over this d-half (+ the row mask) ----
+        // K reads run QK_AHEAD k-steps ahead of the MFMAs; scheduling barriers keep this order
+        constexpr int QK_AHEAD = CSA_ATTN32_QK_AHEAD;
+        bf16x8_t ka[KS];
+        f32x16_t sacc;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) { sacc[j] = 0.f; sacc1[j] = 0.f; }
+        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
 #pragma unroll
-        for (int s = 0; s < KS; s += 2) {
-            const bf16x8_t a0 = as_bf16x8(*(const u32x4_t*)(tile + swz(hl, 16 * s + 8 * g)));
-            const bf16x8_t a1 = as_bf16x8(*(const u32x4_t*)(tile + swz(hl, 16 * (s + 1) + 8 * g)));
-            sacc = mfma32_bf16(a0, qreg[s], sacc);
-            sacc1 = mfma32_bf16(a1, qreg[s + 1], sacc1);
+        for (int s = 0; s < QK_AHEAD; ++s) ka[s] = as_bf16x8(*(const CSA_LDS u32x4_t*)(gb + (qb ^ (32u * s))));
+        {
+            const uint32_t masked = g == 0 && !((vmask >> hl) & 1u) ? BF16_ONE : 0u;
+            sacc = mfma32_bf16(as_bf16x8(u32x4_t{masked, 0u, 0u, 0u}), qmask, sacc);
         }
-        sacc += sacc1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sacc = mfma32_bf16(ka[s], qreg[s], sacc);
+            if (s + QK_AHEAD < KS)
+                ka[s + QK_AHEAD] = as_bf16x8(*(const CSA_LDS u32x4_t*)(gb + (qb ^ (32u * (s + QK_AHEAD)))));
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // ---- exchange with the other d-half of the pair; S = S_dh0 + S_dh1 in both ----
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sx[w][j][lane] = sacc[j];
-        __syncthreads();
+        for (int q4 = 0; q4 < 4; ++q4)
+            *(f32x4_t*)&sx[par][w][q4][lane][0] = f32x4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
+        // LDS writes complete, then a plain barrier: the next tile's loads stay in flight
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         float x[16];
-        float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float o = sx[w ^ 2][j][lane];
-            const float sv = dh == 0 ? sacc[j] + o : o + sacc[j];
-            const int row = 8 * (j >> 2) + 4 * g + (j & 3);
-            x[j] = ((vmask >> row) & 1u) ? sv * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, x[j]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4_t o = *(const f32x4_t*)&sx[par][w ^ 2][q4][lane][0];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sv = dh == 0 ? sacc[4 * q4 + i] + o[i] : o[i] + sacc[4 * q4 + i];
+                x[4 * q4 + i] = sv * scale_log2;
+            }
         }
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        float mx = x[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, x[j]);
+        mx = xhalf_max(mx);
         // rescale only when the running max grows by more than 2^8 (exact: the
         // reference point of the exponentials is free; p stays <= 256)
-        if (mx > m_run + 8.0f) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mx);   // 0 on the first tile
+        const bool grow = mx > m_run + 8.0f;
+        if (__builtin_expect(__builtin_amdgcn_readfirstlane((uint32_t)__ballot(grow) | (uint32_t)(__ballot(grow) >> 32)) != 0u, 0)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;   // 0 on the first tile
             l_run *= alpha;
 #pragma unroll
             for (int d = 0; d < DT; ++d) acc[d] *= alpha;
-            m_run = mx;
+            m_run = grow ? mx : m_run;
         }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;     // all -inf so far: every p is 0
         float pv[16], ps = 0.f;
-        if (m_run == -INFINITY) {                // nothing valid yet: all probabilities are 0
 #pragma unroll
-            for (int j = 0; j < 16; ++j) pv[j] = 0.f;
-        } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                pv[j] = __builtin_amdgcn_exp2f(x[j] - m_run);   // argument <= 8; -inf -> 0
-                ps += pv[j];
-            }
+        for (int j = 0; j < 16; ++j) {
+            pv[j] = __builtin_amdgcn_exp2f(x[j] - m_use);   // argument <= 8; masked rows -> 0
+            ps += pv[j];
         }
-        ps += shfl_xor_f(ps, 32);
-        l_run += ps;
+        l_run += xhalf_sum(ps);
         u32x4_t pw0, pw1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -432,69 +534,82 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
         }
         const bf16x8_t pb0 = as_bf16x8(pw0), pb1 = as_bf16x8(pw1);
         // ---- O^T[d-half][h] += V^T P^T (rows in two k-steps of 16) ----
-        typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+        auto trd = [&](uint32_t off) -> u32x2_t {
+            return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (CSA_LDS i16x4_t*)const_cast<CSA_LDS char*>(gb + off)));
+        };
+        // V reads run PV_AHEAD d-tiles ahead of the MFMAs (same pinned order)
+        constexpr int PV_AHEAD = CSA_ATTN32_PV_AHEAD;
+        u32x2_t vr[DT][4];
+        auto load_d = [&](int d) {
+            const uint32_t e = trb ^ (64u * d), o = trb ^ (64u * d + 32u);
+            vr[d][0] = trd(e); vr[d][1] = trd(o + 4096u); vr[d][2] = trd(e + 8192u); vr[d][3] = trd(o + 12288u);
+        };
+#pragma unroll
+        for (int d = 0; d < PV_AHEAD; ++d) load_d(d);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
-            const int c0 = d * 32 + tr_col;
-            const u32x2_t w0r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4_t*)(tl + swz(tr_row, c0))));
-            const u32x2_t w1r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4_t*)(tl + swz(8 + tr_row, c0))));
-            const u32x2_t w2r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4_t*)(tl + swz(16 + tr_row, c0))));
-            const u32x2_t w3r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4_t*)(tl + swz(24 + tr_row, c0))));
-            acc[d] = mfma32_bf16(as_bf16x8(u32x4_t{w0r[0], w0r[1], w1r[0], w1r[1]}), pb0, acc[d]);
-            acc[d] = mfma32_bf16(as_bf16x8(u32x4_t{w2r[0], w2r[1], w3r[0], w3r[1]}), pb1, acc[d]);
+            const u32x2_t* v = vr[d];
+            acc[d] = mfma32_bf16(as_bf16x8(u32x4_t{v[0][0], v[0][1], v[1][0], v[1][1]}), pb0, acc[d]);
+            acc[d] = mfma32_bf16(as_bf16x8(u32x4_t{v[2][0], v[2][1], v[3][0], v[3][1]}), pb1, acc[d]);
+            if (d + PV_AHEAD < DT) load_d(d + PV_AHEAD);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     uint32_t vm_a = 0, vm_b = 0;
     if (ntiles > 0) {
         fetch_codes(0);
-        vm_a = issue_tile(ta);
-        if (ntiles > 1) fetch_codes(1);
+        __builtin_amdgcn_s_waitcnt(0);
+        vm_a = issue_tile(false, 0);
+        fetch_codes(1);
     }
+    // Buffers are per wave, so only the S exchange synchronises the workgroup (once per tile; the
+    // exchange area alternates with the tile parity).
     for (int it = 0; it < ntiles; it += 2) {
         __builtin_amdgcn_s_waitcnt(0);           // tile it (buffer A) and the codes of tile it+1 have landed
         __builtin_amdgcn_wave_barrier();
-        if (it + 1 < ntiles) {
-            vm_b = issue_tile(tb);
-            if (it + 2 < ntiles) fetch_codes(it + 2);
+        vm_b = issue_tile(true, it + 1);
+        if (it + 2 < ntiles) fetch_codes(it + 2);
+        compute_tile(false, vm_a, 0);
+        __builtin_amdgcn_s_waitcnt(0);           // tile it+1 (buffer B) and the codes of tile it+2
+        __builtin_amdgcn_wave_barrier();
+        if (it + 2 < ntiles) {
+            vm_a = issue_tile(false, it + 2);
+            fetch_codes(it + 3);
         }
-        compute_tile(ta, vm_a);
-        __syncthreads();                         // sx reuse; buffer A is reloaded next
-        if (it + 1 < ntiles) {                   // workgroup-uniform
-            __builtin_amdgcn_s_waitcnt(0);       // tile it+1 (buffer B) and the codes of tile it+2
-            __builtin_amdgcn_wave_barrier();
-            if (it + 2 < ntiles) {
-                vm_a = issue_tile(ta);
-                if (it + 3 < ntiles) fetch_codes(it + 3);
-            }
-            compute_tile(tb, vm_b);
-            __syncthreads();
-        }
+        compute_tile(true, vm_b, 1);
     }
+    __syncthreads();
+    // a wave that saw no valid row holds garbage-weighted sums under a hugely negative max
+    const bool empty = !(m_run > EMPTY_M);
 
     // ---- merge the two row halves: wave (pr=0, dh) += wave (pr=1, dh) ----
     float* ob = (float*)bufA;                  // [2][DT*16][64] floats = 64 KiB
+    float* mlx = &sx[0][0][0][0][0];           // [2 d-halves][m, l][32 heads]
     if (pr == 1) {
         float* dst = ob + (size_t)dh * DT * 16 * 64;
 #pragma unroll
         for (int d = 0; d < DT; ++d)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) dst[(d * 16 + j) * 64 + lane] = acc[d][j];
-        if (g == 0) { sx[dh][0][hl] = m_run; sx[dh][1][hl] = l_run; }
+            for (int j = 0; j < 16; ++j) dst[(d * 16 + j) * 64 + lane] = empty ? 0.f : acc[d][j];
+        if (g == 0) { mlx[dh * 64 + hl] = empty ? -INFINITY : m_run; mlx[dh * 64 + 32 + hl] = empty ? 0.f : l_run; }
     }
     __syncthreads();
     if (pr == 1) return;
     {
         const float* src = ob + (size_t)dh * DT * 16 * 64;
-        const float mo = sx[dh][0][hl], lo = sx[dh][1][hl];
-        const float M = fmaxf(m_run, mo);
-        const float fa = M == -INFINITY ? 0.f : exp2f(m_run - M);
-        const float fb = M == -INFINITY ? 0.f : exp2f(mo - M);
+        const float mo = mlx[dh * 64 + hl], lo = mlx[dh * 64 + 32 + hl];
+        const float ma = empty ? -INFINITY : m_run;
+        const float M = fmaxf(ma, mo);
+        const float fa = ma == -INFINITY ? 0.f : exp2f(ma - M);
+        const float fb = mo == -INFINITY ? 0.f : exp2f(mo - M);
 #pragma unroll
         for (int d = 0; d < DT; ++d)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[d][j] = acc[d][j] * fa + src[(d * 16 + j) * 64 + lane] * fb;
-        l_run = l_run * fa + lo * fb;
+            for (int j = 0; j < 16; ++j) acc[d][j] = (fa == 0.f ? 0.f : acc[d][j] * fa) + src[(d * 16 + j) * 64 + lane] * fb;
+        l_run = (fa == 0.f ? 0.f : l_run * fa) + lo * fb;
         m_run = M;
     }
     // lane holds O^T[dh*256 + d*32 + 8 (j/4) + 4 g + j%4][h]
@@ -568,7 +683,7 @@ static void choose_split(int BT, int H, int D, int max_rows, int* nsplit, int* r
         const int HG = H / 32;
         int ns = std::max(1, 256 / (BT * HG));
         int r = (max_rows + ns - 1) / ns;
-        r = (r + 2 * TILE - 1) / (2 * TILE) * (2 * TILE);
+        r = (r + 4 * TILE - 1) / (4 * TILE) * (4 * TILE);      // each wave pair: an even number of tiles
         *rps = r;
         *nsplit = (max_rows + r - 1) / r;
         return;
@@ -584,8 +699,15 @@ static void choose_split(int BT, int H, int D, int max_rows, int* nsplit, int* r
     *nsplit = (max_rows + r - 1) / r;
 }
 
-size_t attn_ws_bytes(int B, int Tq, int H, int D, int max_rows) {
+// Row-space size of one query: dense N; sparse topk (padded to whole tiles for k_attn32) + window.
+static int attn_rows(int mode, int H, int D, int n, int W) {
+    if (mode == 0) return n;
+    return (use32(D, H) ? (n + TILE - 1) / TILE * TILE : n) + W;
+}
+
+size_t attn_ws_bytes(int B, int Tq, int H, int D, int mode, int n, int W) {
     const int BT = B * Tq;
+    const int max_rows = attn_rows(mode, H, D, n, W);
     int ns, rps;
     choose_split(BT, H, D, max_rows, &ns, &rps);
     if (ns == 1) return 0;
@@ -607,7 +729,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     R.raw0 = a.raw0;
     R.W = a.W;
     const int BT = B * Tq;
-    const int max_rows = a.mode == 0 ? a.N : a.topk + a.W;
+    const int max_rows = a.mode == 0 ? a.N : attn_rows(1, H, D, a.topk, a.W);
     int ns, rps;
     choose_split(BT, H, D, max_rows, &ns, &rps);
     float* part_o = nullptr;
@@ -620,12 +742,17 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     if (use32(D, H)) {
         const int nunits = BT * ns, HG = H / 32;
         const int nblk = (nunits + 7) / 8 * 8 * HG;
-        if (a.mode == 0)
-            CSA_LAUNCH(tag, k_attn32<0>, dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2,
-                       nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
-        else
-            CSA_LAUNCH(tag, k_attn32<1>, dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2,
-                       nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
+        // byte offsets of whole arrays must fit 32 bits for the buffer-load variant
+        const bool big = (size_t)a.N * D * 2 > 0xffffffffull || (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
+#define CSA_ATTN32(M, BIG_)                                                                                  \
+    CSA_LAUNCH(tag, (k_attn32<M, BIG_>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, \
+               nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse)
+        if (a.mode == 0) {
+            if (big) CSA_ATTN32(0, true); else CSA_ATTN32(0, false);
+        } else {
+            if (big) CSA_ATTN32(1, true); else CSA_ATTN32(1, false);
+        }
+#undef CSA_ATTN32
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse);

@@ -28,7 +28,8 @@ struct AttnRows {
     long long raw0;
     int W;
 };
-size_t attn_ws_bytes(int B, int Tq, int H, int D, int max_rows);
+// mode 0: dense over n rows; mode 1: n selected entries + W window rows
+size_t attn_ws_bytes(int B, int Tq, int H, int D, int mode, int n, int W);
 int attn_launch(const void* q, const AttnRows& rows, int B, int Tq, int H, int D, long long pos0, float scale,
                 void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t st, const char* tag);
 

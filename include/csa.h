@@ -215,6 +215,9 @@ int csa_debug_fp8_to_bf16(const void* in, void* out, int n, void* stream);
  * count of every kernel whose name equals `kernel`.  csa_prof_reset() drops
  * all records.  Kernel names are the ones rocprofv3 reports. */
 int csa_prof_enable(int on);
+/* Restrict recording to launches of one kernel (NULL or "" records all), so
+ * that timing one kernel adds only its own two events to the stream. */
+int csa_prof_only(const char* kernel);
 int csa_prof_reset(void);
 int csa_prof_read(const char* kernel, double* total_ms, int* launches);
 
