@@ -219,17 +219,21 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// k_attn32 (D = 512, H % 32 == 0): a wave owns 32 heads (v_mfma_f32_32x32x16_bf16),
-// so every K / V byte read from LDS feeds 32 heads, the balance point of the
-// LDS-read and MFMA rates of a CU.  Waves work in pairs over the two halves of
-// D: each computes the partial scores of its 256 dims, the pair exchanges them
-// through LDS (summed in a fixed order, so both hold identical S), and each
-// accumulates O only for its own half -- 128 accumulators and 64 Q registers
-// per lane, two workgroups per CU.  The two pairs of a workgroup take the two
-// halves of the split's rows and merge (m, l, O) in LDS at the end.  Tiles are
-// unpadded and XOR-swizzled per 16-byte chunk (conflict-free row reads and
-// transposed reads).  1D grid, XCD-aware: the H/32 head-group workgroups that
-// read the same rows land on the same XCD (workgroup i runs on XCD i mod 8).
+// k_attn64 (D = 512, H % 32 == 0): one workgroup = 4 waves = 64 heads (two head
+// groups of 32) x the two halves of D.  A wave owns 32 heads of one d-half
+// (v_mfma_f32_32x32x16_bf16: every K / V byte read from LDS feeds 32 heads);
+// the two head groups share each K tile in LDS, so a tile is fetched once per
+// 64 heads.  The two d-half waves of a head group compute partial scores over
+// their 256 dims and exchange them through LDS (summed in a fixed order, so
+// both hold identical S); each accumulates O only for its own d-half (128
+// accumulators and 64 Q registers per lane).  The split's rows stream through
+// three tile buffers filled by direct global->LDS loads, so a tile's loads have
+// a whole tile of compute to land.  Per tile the waves run one software-
+// pipelined step: the softmax of tile t overlaps the QK MFMAs of tile t+1,
+// then the PV MFMAs of tile t, then the score exchange (the one barrier).
+// Tiles are unpadded and XOR-swizzled per 16-byte chunk (conflict-free row
+// reads and transposed reads).  1D grid, XCD-aware: the head-pair workgroups
+// that read the same rows land on the same XCD (workgroup i runs on XCD i mod 8).
 // ---------------------------------------------------------------------------
 constexpr int HD = 256;   // d-half handled by one wave
 
@@ -237,36 +241,31 @@ constexpr int HD = 256;   // d-half handled by one wave
 // consecutive rows at one chunk, and any 4 aligned rows x 4 aligned chunks (the footprint of a
 // transposed read), fall on 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz_chunk(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int swz(int r, int c) {   // element offset of (row, col) in a [32][256] tile
-    return r * HD + (((c >> 3) ^ swz_chunk(r)) << 3) + (c & 7);
-}
 
 // Raw buffer resource (stride 0, byte offsets) over [base, base + bytes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-#ifndef CSA_ATTN32_QK_AHEAD
-#define CSA_ATTN32_QK_AHEAD 4      // K-operand LDS reads in flight ahead of the QK MFMAs
+#ifndef CSA_ATTN64_QK_AHEAD
+#define CSA_ATTN64_QK_AHEAD 4      // K-operand LDS reads in flight ahead of the QK MFMAs
 #endif
-#ifndef CSA_ATTN32_PV_AHEAD
-#define CSA_ATTN32_PV_AHEAD 2      // d-tiles of V reads in flight ahead of the PV MFMAs
-#endif
-#ifndef CSA_ATTN32_WAVES_PER_EU
-#define CSA_ATTN32_WAVES_PER_EU 1
+#ifndef CSA_ATTN64_PV_AHEAD
+#define CSA_ATTN64_PV_AHEAD 2      // d-tiles of V reads in flight ahead of the PV MFMAs
 #endif
 // Masked rows get -2^100 added to their scores by one extra MFMA k-step (A: a 1 in column 0 of each
 // masked row; B: -2^100 in row 0, d-half 0 only), which sends their probabilities to exactly 0
-// without any per-element select on the common path.  A tile or split with no valid row at all ends
-// with a running max below EMPTY_M, which the merge treats as empty.
+// without any per-element select on the common path.  A split with no valid row at all ends with a
+// running max below EMPTY_M, which the output step treats as empty.
 constexpr uint32_t BF16_ONE = 0x3f80u, BF16_NEG_2P100 = 0xf180u;
 constexpr float EMPTY_M = -1.0e25f;
+constexpr int ATT_TILES = 3;      // tile buffers; a split's tile count is a multiple of this
 
 // MODE 0: dense prefix (row r = entry r); MODE 1: selected entries then window rows.  BIG: some
 // array is beyond the reach of 32-bit byte offsets, so tiles are loaded with 64-bit addresses (the
 // other variant uses buffer loads only, which keeps the LDS wait counting exact in the main loop).
 template <int MODE, bool BIG>
-__global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
+__global__ __launch_bounds__(TPB, 1) void k_attn64(
     const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
     int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse)
@@ -274,19 +273,25 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
     constexpr int D = 512;
     constexpr int KS = HD / 16;               // 32x32x16 k-steps over a d-half
     constexpr int DT = HD / 32;               // 32-wide d tiles of a d-half
-    __shared__ __attribute__((aligned(1024))) uint16_t bufA[4 * TILE * HD];   // 64 KiB: tile buffer 0 of each wave
-    __shared__ __attribute__((aligned(1024))) uint16_t bufB[4 * TILE * HD];   // 64 KiB: tile buffer 1 of each wave
-    __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];         // 32 KiB: [tile parity][wave][j/4][lane][j%4]
+    constexpr int HALF_B = TILE * HD * 2;     // bytes of one d-half of a tile (16 KiB)
+    // three tile buffers [d-half][32 rows][256] bf16 (distinct objects: the compiler tells a read of
+    // one from the loads in flight into another) and the score exchange [parity][wave][j/4][lane][j%4]
+    __shared__ __attribute__((aligned(1024))) uint16_t bufA[2 * TILE * HD];
+    __shared__ __attribute__((aligned(1024))) uint16_t bufB[2 * TILE * HD];
+    __shared__ __attribute__((aligned(1024))) uint16_t bufC[2 * TILE * HD];
+    __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];
 
-    const int HG = H / 32;
+    const int HP = (H + 63) / 64;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int hg = slot % HG, unit = (slot / HG) * 8 + xcd;
+    const int hp = slot % HP, unit = (slot / HP) * 8 + xcd;
     if (unit >= nunits) return;                // padding workgroups (uniform exit)
     const int bt = unit / nsplit, split = unit % nsplit;
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // w: wave-uniform
-    const int pr = w & 1, dh = w >> 1;         // row half, d half
+    const int hgl = w & 1, dh = w >> 1;        // head group within the pair, d half
     const int hl = lane & 31, g = lane >> 5;
-    const int h = hg * 32 + hl;
+    const int hbase = hp * 64 + hgl * 32;      // first head of this wave
+    const bool hv = hbase < H;                 // the wave's heads exist (H % 64 == 32: the last pair is half)
+    const int h = hbase + hl;
 
     const int b = bt / Tq;
     const long long p = pos0 + bt % Tq;
@@ -303,11 +308,8 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
     }
     const int s_begin = split * rps;
     const int s_end = min(nrows, s_begin + rps);
-    const int per_pair = rps / 2;              // multiple of 2 TILE
-    const int r_begin = s_begin + pr * per_pair;
-    const int r_end = min(s_end, r_begin + per_pair);
-    // even tile count, the same for every wave (barriers inside); an empty split runs no tile
-    const int ntiles = s_begin < nrows ? per_pair / TILE : 0;
+    // a multiple of ATT_TILES tiles, the same for every wave (barriers inside); an empty split runs none
+    const int ntiles = s_begin < nrows ? rps / TILE : 0;
 
     const uint16_t* kvb = R.kv ? R.kv + (size_t)b * R.N * D : nullptr;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
@@ -315,9 +317,9 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
 
     bf16x8_t qreg[KS];
     {
-        const uint16_t* qp = q + ((size_t)bt * H + h) * D + dh * HD + 8 * g;
+        const uint16_t* qp = q + ((size_t)bt * H + (hv ? h : 0)) * D + dh * HD + 8 * g;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qreg[s] = as_bf16x8(*(const u32x4_t*)(qp + 16 * s));
+        for (int s = 0; s < KS; ++s) qreg[s] = hv ? as_bf16x8(*(const u32x4_t*)(qp + 16 * s)) : as_bf16x8(u32x4_t{0, 0, 0, 0});
     }
     const bf16x8_t qmask = as_bf16x8(u32x4_t{g == 0 && dh == 0 ? BF16_NEG_2P100 : 0u, 0u, 0u, 0u});
     f32x16_t acc[DT];
@@ -331,24 +333,27 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
     const int tr_row = 4 * (b16 >> 1) + (j16 >> 2);
     const int rsub = lane >> 5, pch = lane & 31;
 
-    // Loads of one tile.  Instruction i moves row slots 2i (lanes 0-31) and 2i+1 (lanes 32-63) of this
-    // d-half, 16 B per lane, landing at (tile + 1024 i + 16 lane); the XOR swizzle goes on the source:
-    // the lane fetches logical chunk pch ^ swz_chunk(2i + rsub) = (pch ^ 4 rsub) ^ kappa(i) with
-    // kappa(i) = 8 (i & 1) | ((i >> 1) & 3).  Masked slots load a valid row (their data is never weighted).
+    // ---- tile loads ----
+    // Instruction i (0..15) moves row slots 2i (lanes 0-31) and 2i+1 (lanes 32-63) of one d-half, 16 B
+    // per lane, landing at (half + 1024 i + 16 lane); the XOR swizzle goes on the source: the lane
+    // fetches logical chunk pch ^ swz_chunk(2i + rsub) = (pch ^ 4 rsub) ^ kappa(i), kappa(i) =
+    // 8 (i & 1) | ((i >> 1) & 3).  The two waves of a d-half split the 16 instructions; masked slots
+    // load a valid row (their data is never weighted).
     auto kappa = [](int i) -> uint32_t { return (uint32_t)(8 * (i & 1) | ((i >> 1) & 3)); };
     const uint32_t lane_chunk = 16u * (uint32_t)(pch ^ (4 * rsub));
     const uint32_t lane_row = (uint32_t)rsub * (D * 2);
+    const int i0 = 8 * hgl;                    // this wave's instructions: i0 .. i0 + 7
 
-    // MODE 1: entry indices of the lane's 16 row slots of a tile, loaded one tile ahead and only
-    // used after the next full wait (a use right after the load would also wait for the tile loads).
+    // MODE 1: entry indices of the lane's 16 row slots of a tile, loaded one tile ahead and only used
+    // after the next full wait (a use right after the load would also wait for the tile loads).
     int code[TILE / 2];
-    auto fetch_codes = [&](int it) {
+    auto fetch_codes = [&](int t) {
         if constexpr (MODE == 1) {
-            const int r0 = r_begin + it * TILE;
+            const int r0 = s_begin + t * TILE;
 #pragma unroll
             for (int i = 0; i < TILE / 2; ++i) {
                 const int r = r0 + 2 * i + rsub;
-                code[i] = (r < r_end && r < R.topk) ? R.idx[(size_t)bt * R.topk + r] : -1;
+                code[i] = (r < s_end && r < R.topk) ? R.idx[(size_t)bt * R.topk + r] : -1;
             }
         }
     };
@@ -360,10 +365,10 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
     const __amdgpu_buffer_rsrc_t rs_raw =
         make_rsrc(has_raw ? rawb + dh * HD : nullptr, has_raw ? (uint32_t)((size_t)R.Lr * D * 2 - dh * HD * 2) : 0u);
     const int raw_first = MODE == 1 ? (int)(w0 - R.raw0) : 0;         // raw row of the first window row
-    auto issue_tile = [&](bool second, int it) -> uint32_t {
-        CSA_LDS char* lb = (second ? (CSA_LDS char*)bufB : (CSA_LDS char*)bufA) + w * (TILE * HD * 2);
-        const int r0 = r_begin + it * TILE;
-        // one instruction: 16 B per lane from (resource + soffset + voffset) to (lb + 1024 i + 16 lane)
+    // Issue this wave's part of tile t into `buf`; returns the tile's validity mask (bit = row slot).
+    auto issue_tile = [&](uint16_t* buf, int t) -> uint32_t {
+        CSA_LDS char* lb = (CSA_LDS char*)buf + dh * HALF_B;
+        const int r0 = s_begin + t * TILE;
         auto bdma = [&](__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, int i) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (CSA_LDS void*)(lb + 1024 * i), 16, (int)voff, (int)soff, 0, 0);
         };
@@ -371,24 +376,26 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                              (CSA_LDS void*)(lb + 1024 * i), 16, 0, 0);
         };
-        const int nval = max(0, min(TILE, r_end - r0));
+        const int nval = max(0, min(TILE, s_end - r0));
         if constexpr (MODE == 0) {
             if constexpr (kv32) {
                 if (r0 + TILE <= R.N) {                 // all 32 row slots lie inside the array
 #pragma unroll
-                    for (int i = 0; i < TILE / 2; ++i)
+                    for (int k = 0; k < 8; ++k) {
+                        const int i = i0 + k;
                         bdma(rs_kv, (lane_row + lane_chunk) ^ (16u * kappa(i)), (uint32_t)r0 * (D * 2) + 2048u * i, i);
+                    }
                 } else {                                // tail: slots past the array reread row 0
 #pragma unroll
-                    for (int i = 0; i < TILE / 2; ++i) {
-                        const int r = r0 + 2 * i + rsub;
+                    for (int k = 0; k < 8; ++k) {
+                        const int i = i0 + k, r = r0 + 2 * i + rsub;
                         bdma(rs_kv, (uint32_t)(r < R.N ? r : 0) * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
                     }
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < TILE / 2; ++i) {
-                    const int r = r0 + 2 * i + rsub;
+                for (int k = 0; k < 8; ++k) {
+                    const int i = i0 + k, r = r0 + 2 * i + rsub;
                     gdma((const char*)(kvb + (size_t)(r < R.N ? r : 0) * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
                 }
             }
@@ -405,13 +412,11 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
                     vm |= (uint32_t)((bal >> 32) & 1ull) << (2 * i + 1);
                     roff[i] = ok ? (uint32_t)code[i] : 0u;
                 }
-                if constexpr (kv32) {
 #pragma unroll
-                    for (int i = 0; i < TILE / 2; ++i) bdma(rs_kv, roff[i] * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < TILE / 2; ++i)
-                        gdma((const char*)(kvb + (size_t)roff[i] * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
+                for (int k = 0; k < 8; ++k) {
+                    const int i = i0 + k;
+                    if constexpr (kv32) bdma(rs_kv, roff[i] * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
+                    else gdma((const char*)(kvb + (size_t)roff[i] * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
                 }
             } else {                                    // raw window rows (masked slots read the first one)
                 const int u0 = raw_first + (r0 - topk32);                   // raw row of slot 0
@@ -419,21 +424,23 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
                 if constexpr (raw32) {
                     if (nval == TILE) {
 #pragma unroll
-                        for (int i = 0; i < TILE / 2; ++i)
+                        for (int k = 0; k < 8; ++k) {
+                            const int i = i0 + k;
                             bdma(rs_raw, (lane_row + lane_chunk) ^ (16u * kappa(i)), (uint32_t)u0 * (D * 2) + 2048u * i, i);
+                        }
                     } else {
 #pragma unroll
-                        for (int i = 0; i < TILE / 2; ++i) {
-                            const int slot = 2 * i + rsub;
-                            const int u = slot < nval ? u0 + slot : raw_first;
+                        for (int k = 0; k < 8; ++k) {
+                            const int i = i0 + k, slot_ = 2 * i + rsub;
+                            const int u = slot_ < nval ? u0 + slot_ : raw_first;
                             bdma(rs_raw, (uint32_t)u * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
                         }
                     }
                 } else {
 #pragma unroll
-                    for (int i = 0; i < TILE / 2; ++i) {
-                        const int slot = 2 * i + rsub;
-                        const int u = slot < nval ? u0 + slot : raw_first;
+                    for (int k = 0; k < 8; ++k) {
+                        const int i = i0 + k, slot_ = 2 * i + rsub;
+                        const int u = slot_ < nval ? u0 + slot_ : raw_first;
                         gdma((const char*)(rawb + (size_t)u * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
                     }
                 }
@@ -442,12 +449,12 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
         }
     };
 
-    // Byte offsets of this lane's reads inside a wave's tile.  With the tile 512-byte aligned the swizzled
-    // address of k-step s is (base + qk_off) ^ 32 s, and that of the transposed read of rows 8k.. and d-tile d
-    // is ((base + tr_off) ^ (64 d + 32 (k & 1))) + 4096 k (the XOR touches bits 5..8 only).
-    // (Offsets include the wave's tile, w * 16 KiB, which the XOR leaves alone.)
-    const uint32_t qk_off = w * (TILE * HD * 2) + hl * 512 + 16 * (g ^ swz_chunk(hl));
-    const uint32_t tr_off = w * (TILE * HD * 2) + tr_row * 512 +
+    // ---- LDS reads ----
+    // Byte offsets of this lane's reads inside a tile buffer.  With the half 512-byte aligned the
+    // swizzled address of k-step s is (qk_off ^ 32 s), and that of the transposed read of rows 8k.. and
+    // d-tile d is ((tr_off ^ (64 d + 32 (k & 1))) + 4096 k) (the XOR touches bits 5..8 only).
+    const uint32_t qk_off = dh * HALF_B + hl * 512 + 16 * (g ^ swz_chunk(hl));
+    const uint32_t tr_off = dh * HALF_B + tr_row * 512 +
                             16 * ((2 * (b16 & 1) + ((j16 >> 1) & 1)) ^ swz_chunk(tr_row)) + 8 * (j16 & 1);
     typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
     // max / sum over the two lane halves (the two 16-row groups of a head's column)
@@ -460,41 +467,14 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
         return __uint_as_float(r[0]) + __uint_as_float(r[1]);
     };
 
-    // Compute on one tile; the loads of the next tile (into the other LDS object) stay in flight.
-    // Addresses are formed from the buffer object itself so that the compiler can tell them apart
-    // from the in-flight loads into the other buffer.
-    auto compute_tile = [&](bool second, uint32_t vmask, int par) {
-        const CSA_LDS char* gb = second ? (const CSA_LDS char*)bufB : (const CSA_LDS char*)bufA;
-        uint32_t qb = qk_off, trb = tr_off;
-        asm volatile("" : "+v"(qb), "+v"(trb));   // keep the per-read XORs in the loop (no hoisted address table)
-        // ---- partial S^T[32 rows][32 heads] over this d-half (+ the row mask) ----
-        // K reads run QK_AHEAD k-steps ahead of the MFMAs; scheduling barriers keep this order
-        constexpr int QK_AHEAD = CSA_ATTN32_QK_AHEAD;
-        bf16x8_t ka[KS];
-        f32x16_t sacc;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
-#pragma unroll
-        for (int s = 0; s < QK_AHEAD; ++s) ka[s] = as_bf16x8(*(const CSA_LDS u32x4_t*)(gb + (qb ^ (32u * s))));
-        {
-            const uint32_t masked = g == 0 && !((vmask >> hl) & 1u) ? BF16_ONE : 0u;
-            sacc = mfma32_bf16(as_bf16x8(u32x4_t{masked, 0u, 0u, 0u}), qmask, sacc);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            sacc = mfma32_bf16(ka[s], qreg[s], sacc);
-            if (s + QK_AHEAD < KS)
-                ka[s + QK_AHEAD] = as_bf16x8(*(const CSA_LDS u32x4_t*)(gb + (qb ^ (32u * (s + QK_AHEAD)))));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // ---- exchange with the other d-half of the pair; S = S_dh0 + S_dh1 in both ----
+    // QK of one tile: partial S^T[32 rows][32 heads] over this d-half plus the row mask.
+    float x[16];                               // scaled scores of the tile being finished
+    auto write_scores = [&](const f32x16_t& sacc, int par) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
             *(f32x4_t*)&sx[par][w][q4][lane][0] = f32x4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
-        // LDS writes complete, then a plain barrier: the next tile's loads stay in flight
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        float x[16];
+    };
+    auto read_scores = [&](const f32x16_t& sacc, int par) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const f32x4_t o = *(const f32x4_t*)&sx[par][w ^ 2][q4][lane][0];
@@ -504,42 +484,75 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
                 x[4 * q4 + i] = sv * scale_log2;
             }
         }
-        float mx = x[0];
+    };
+    // LDS writes complete, then a plain barrier (the tile loads in flight are not waited for here)
+    auto exchange_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+    // One pipelined step: softmax of tile t (x) interleaved with QK of tile t+1 (from Qb, mask vmn),
+    // then PV of tile t (from Pb); returns the partial scores of tile t+1.  Reads are formed from the
+    // buffer objects themselves so that the compiler tells them from the loads in flight.
+    auto step = [&](const uint16_t* Pbuf, const uint16_t* Qbuf, uint32_t vmn) -> f32x16_t {
+        const CSA_LDS char* Pb = (const CSA_LDS char*)Pbuf;
+        const CSA_LDS char* Qb = (const CSA_LDS char*)Qbuf;
+        uint32_t qb = qk_off, trb = tr_off;
+        asm volatile("" : "+v"(qb), "+v"(trb));   // keep the per-read XORs in the loop (no hoisted address table)
+        constexpr int QK_AHEAD = CSA_ATTN64_QK_AHEAD;
+        bf16x8_t ka[KS];
+        f32x16_t sacc;
 #pragma unroll
-        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, x[j]);
-        mx = xhalf_max(mx);
-        // rescale only when the running max grows by more than 2^8 (exact: the
-        // reference point of the exponentials is free; p stays <= 256)
-        const bool grow = mx > m_run + 8.0f;
-        if (__builtin_expect(__builtin_amdgcn_readfirstlane((uint32_t)__ballot(grow) | (uint32_t)(__ballot(grow) >> 32)) != 0u, 0)) {
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;   // 0 on the first tile
-            l_run *= alpha;
+        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
 #pragma unroll
-            for (int d = 0; d < DT; ++d) acc[d] *= alpha;
-            m_run = grow ? mx : m_run;
+        for (int s = 0; s < QK_AHEAD; ++s) ka[s] = as_bf16x8(*(const CSA_LDS u32x4_t*)(Qb + (qb ^ (32u * s))));
+        {
+            const uint32_t masked = g == 0 && !((vmn >> hl) & 1u) ? BF16_ONE : 0u;
+            sacc = mfma32_bf16(as_bf16x8(u32x4_t{masked, 0u, 0u, 0u}), qmask, sacc);
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;     // all -inf so far: every p is 0
-        float pv[16], ps = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            pv[j] = __builtin_amdgcn_exp2f(x[j] - m_use);   // argument <= 8; masked rows -> 0
-            ps += pv[j];
-        }
-        l_run += xhalf_sum(ps);
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])), fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]))));
+        __builtin_amdgcn_sched_barrier(0);
+        // the softmax of tile t is spread over the 16 k-steps of tile t+1
+        float alpha = 1.f, m_use = 0.f, ps = 0.f;
         u32x4_t pw0, pw1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pw0[j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
-            pw1[j] = pack_bf16x2(pv[8 + 2 * j], pv[8 + 2 * j + 1]);
+        for (int s = 0; s < KS; ++s) {
+            sacc = mfma32_bf16(ka[s], qreg[s], sacc);
+            if (s + QK_AHEAD < KS)
+                ka[s + QK_AHEAD] = as_bf16x8(*(const CSA_LDS u32x4_t*)(Qb + (qb ^ (32u * (s + QK_AHEAD)))));
+            if (s == 0) {
+                // rescale only when the running max grows by more than 2^8 (exact: the reference
+                // point of the exponentials is free; p stays <= 256)
+                mx = xhalf_max(mx);
+                const bool grow = mx > m_run + 8.0f;
+                alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;     // 0 on the first valid tile
+                m_run = grow ? mx : m_run;
+                m_use = m_run == -INFINITY ? 0.f : m_run;                      // all -inf so far: every p is 0
+            } else if (s <= 8) {
+                const int j = 2 * (s - 1);
+                x[j] = __builtin_amdgcn_exp2f(x[j] - m_use);                   // masked rows -> 0
+                x[j + 1] = __builtin_amdgcn_exp2f(x[j + 1] - m_use);
+                ps += x[j] + x[j + 1];
+            } else if (s <= 12) {
+                const int j = s - 9;
+                pw0[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+                pw1[j] = pack_bf16x2(x[8 + 2 * j], x[8 + 2 * j + 1]);
+            } else if (s == 13) {
+                l_run = l_run * alpha + xhalf_sum(ps);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // (rare) the running max grew: rescale the accumulators before this tile's PV
+        if (__builtin_expect(__builtin_amdgcn_readfirstlane((uint32_t)__ballot(alpha != 1.0f) |
+                                                            (uint32_t)(__ballot(alpha != 1.0f) >> 32)) != 0u, 0)) {
+#pragma unroll
+            for (int d = 0; d < DT; ++d) acc[d] *= alpha;
         }
         const bf16x8_t pb0 = as_bf16x8(pw0), pb1 = as_bf16x8(pw1);
-        // ---- O^T[d-half][h] += V^T P^T (rows in two k-steps of 16) ----
+        // ---- O^T[d-half][h] += V^T P^T (rows in two k-steps of 16); V reads run PV_AHEAD d-tiles ahead ----
         auto trd = [&](uint32_t off) -> u32x2_t {
             return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                   (CSA_LDS i16x4_t*)const_cast<CSA_LDS char*>(gb + off)));
+                                                   (CSA_LDS i16x4_t*)const_cast<CSA_LDS char*>(Pb + off)));
         };
-        // V reads run PV_AHEAD d-tiles ahead of the MFMAs (same pinned order)
-        constexpr int PV_AHEAD = CSA_ATTN32_PV_AHEAD;
+        constexpr int PV_AHEAD = CSA_ATTN64_PV_AHEAD;
         u32x2_t vr[DT][4];
         auto load_d = [&](int d) {
             const uint32_t e = trb ^ (64u * d), o = trb ^ (64u * d + 32u);
@@ -556,61 +569,74 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
             if (d + PV_AHEAD < DT) load_d(d + PV_AHEAD);
             __builtin_amdgcn_sched_barrier(0);
         }
+        return sacc;
+    };
+    // QK alone (the first tile): partial scores of the tile in Qbuf.
+    auto qk_only = [&](const uint16_t* Qbuf, uint32_t vm) -> f32x16_t {
+        const CSA_LDS char* Qb = (const CSA_LDS char*)Qbuf;
+        f32x16_t sacc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+        const uint32_t masked = g == 0 && !((vm >> hl) & 1u) ? BF16_ONE : 0u;
+        sacc = mfma32_bf16(as_bf16x8(u32x4_t{masked, 0u, 0u, 0u}), qmask, sacc);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            sacc = mfma32_bf16(as_bf16x8(*(const CSA_LDS u32x4_t*)(Qb + (qk_off ^ (32u * s)))), qreg[s], sacc);
+        return sacc;
     };
 
-    uint32_t vm_a = 0, vm_b = 0;
+    // ---- the tile pipeline ----
+    // Tile t lives in buffer t % 3.  Step t: softmax(t) + QK(t+1), PV(t), exchange of S(t+1) with one
+    // barrier; before the barrier each wave waits for its own loads of tile t+2, so after it tile t+2
+    // is complete for all waves and buffer t % 3 (PV of tile t done everywhere) takes the loads of
+    // tile t+3.  Steps past the last tile compute on stale buffers and their results are dropped.
+    uint32_t vm0 = 0, vm1 = 0, vm2 = 0;
     if (ntiles > 0) {
         fetch_codes(0);
         __builtin_amdgcn_s_waitcnt(0);
-        vm_a = issue_tile(false, 0);
+        vm0 = issue_tile(bufA, 0);
         fetch_codes(1);
+        __builtin_amdgcn_s_waitcnt(0);         // own loads of tile 0, codes of tile 1
+        vm1 = issue_tile(bufB, 1);
+        fetch_codes(2);
+        __syncthreads();                       // tile 0 complete for all waves
+        const f32x16_t s0 = qk_only(bufA, vm0);
+        write_scores(s0, 0);
+        __builtin_amdgcn_s_waitcnt(0);         // own loads of tile 1, codes of tile 2
+        exchange_barrier();
+        vm2 = issue_tile(bufC, 2);
+        fetch_codes(3);
+        read_scores(s0, 0);
     }
-    // Buffers are per wave, so only the S exchange synchronises the workgroup (once per tile; the
-    // exchange area alternates with the tile parity).
-    for (int it = 0; it < ntiles; it += 2) {
-        __builtin_amdgcn_s_waitcnt(0);           // tile it (buffer A) and the codes of tile it+1 have landed
-        __builtin_amdgcn_wave_barrier();
-        vm_b = issue_tile(true, it + 1);
-        if (it + 2 < ntiles) fetch_codes(it + 2);
-        compute_tile(false, vm_a, 0);
-        __builtin_amdgcn_s_waitcnt(0);           // tile it+1 (buffer B) and the codes of tile it+2
-        __builtin_amdgcn_wave_barrier();
-        if (it + 2 < ntiles) {
-            vm_a = issue_tile(false, it + 2);
-            fetch_codes(it + 3);
+    for (int t = 0; t < ntiles; t += ATT_TILES) {
+        // step t (P = A, QK = B), step t+1 (P = B, QK = C), step t+2 (P = C, QK = A)
+#define CSA_ATT_STEP(PB, QB, VMN, DMA_BUF, VM_OUT, K)                                             \
+        {                                                                                         \
+            const int par = (t + K + 1) & 1;   /* exchange parity of tile t+K+1 */                  \
+            const f32x16_t sn = step(PB, QB, VMN);                                                \
+            write_scores(sn, par);                                                                \
+            __builtin_amdgcn_s_waitcnt(0);     /* own loads of tile t+K+2, codes of tile t+K+3 */  \
+            exchange_barrier();                                                                   \
+            if (t + K + 3 < ntiles) {                                                             \
+                VM_OUT = issue_tile(DMA_BUF, t + K + 3);                                          \
+                fetch_codes(t + K + 4);                                                           \
+            } else {                                                                              \
+                VM_OUT = 0u;                                                                      \
+            }                                                                                     \
+            read_scores(sn, par);                                                                 \
         }
-        compute_tile(true, vm_b, 1);
+        CSA_ATT_STEP(bufA, bufB, vm1, bufA, vm0, 0)
+        CSA_ATT_STEP(bufB, bufC, vm2, bufB, vm1, 1)
+        CSA_ATT_STEP(bufC, bufA, vm0, bufC, vm2, 2)
+#undef CSA_ATT_STEP
     }
-    __syncthreads();
-    // a wave that saw no valid row holds garbage-weighted sums under a hugely negative max
-    const bool empty = !(m_run > EMPTY_M);
 
-    // ---- merge the two row halves: wave (pr=0, dh) += wave (pr=1, dh) ----
-    float* ob = (float*)bufA;                  // [2][DT*16][64] floats = 64 KiB
-    float* mlx = &sx[0][0][0][0][0];           // [2 d-halves][m, l][32 heads]
-    if (pr == 1) {
-        float* dst = ob + (size_t)dh * DT * 16 * 64;
-#pragma unroll
-        for (int d = 0; d < DT; ++d)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) dst[(d * 16 + j) * 64 + lane] = empty ? 0.f : acc[d][j];
-        if (g == 0) { mlx[dh * 64 + hl] = empty ? -INFINITY : m_run; mlx[dh * 64 + 32 + hl] = empty ? 0.f : l_run; }
-    }
-    __syncthreads();
-    if (pr == 1) return;
-    {
-        const float* src = ob + (size_t)dh * DT * 16 * 64;
-        const float mo = mlx[dh * 64 + hl], lo = mlx[dh * 64 + 32 + hl];
-        const float ma = empty ? -INFINITY : m_run;
-        const float M = fmaxf(ma, mo);
-        const float fa = ma == -INFINITY ? 0.f : exp2f(ma - M);
-        const float fb = mo == -INFINITY ? 0.f : exp2f(mo - M);
-#pragma unroll
-        for (int d = 0; d < DT; ++d)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[d][j] = (fa == 0.f ? 0.f : acc[d][j] * fa) + src[(d * 16 + j) * 64 + lane] * fb;
-        l_run = (fa == 0.f ? 0.f : l_run * fa) + lo * fb;
-        m_run = M;
+    // ---- output: both d-half waves of a head group hold the same (m, l) ----
+    if (!hv) return;
+    const bool empty = !(m_run > EMPTY_M);     // no valid row: garbage-weighted sums under a tiny max
+    if (empty) {
+        m_run = -INFINITY;
+        l_run = 0.f;
     }
     // lane holds O^T[dh*256 + d*32 + 8 (j/4) + 4 g + j%4][h]
     if (nsplit == 1) {
@@ -633,8 +659,9 @@ __global__ __launch_bounds__(TPB, CSA_ATTN32_WAVES_PER_EU) void k_attn32(
         for (int d = 0; d < DT; ++d)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4)
-                *(f32x4_t*)(op + d * 32 + 8 * q4) = f32x4_t{acc[d][4 * q4], acc[d][4 * q4 + 1], acc[d][4 * q4 + 2],
-                                                            acc[d][4 * q4 + 3]};
+                *(f32x4_t*)(op + d * 32 + 8 * q4) =
+                    empty ? f32x4_t{0.f, 0.f, 0.f, 0.f}
+                          : f32x4_t{acc[d][4 * q4], acc[d][4 * q4 + 1], acc[d][4 * q4 + 2], acc[d][4 * q4 + 3]};
         if (g == 0 && dh == 0) part_ml[sl] = make_float2(m_run, l_run);
     }
 }
@@ -673,17 +700,27 @@ namespace csa_host {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Split counts.  k_attn (16 heads per wave): enough workgroups to cover the
-// chip twice, splits of >= 64 rows.  k_attn32 (32 heads per wave, one
-// workgroups per CU): about one workgroup per CU, whole 32-row tiles per wave pair.
-static bool use32(int D, int H) { return D == 512 && H % 32 == 0; }
+// chip twice, splits of >= 64 rows.  k_attn64 (64 heads per workgroup, one
+// workgroup per CU): about one workgroup per CU, but at least ATT_MIN_TILES
+// tiles per split (each split writes 64 heads x 512 fp32 partials, so thin
+// splits cost more in partials than they save), tile counts a multiple of 3.
+#ifndef CSA_ATT_MIN_TILES
+#define CSA_ATT_MIN_TILES 6
+#endif
+#ifndef CSA_ATT_TARGET_WG
+#define CSA_ATT_TARGET_WG 256
+#endif
+static bool use64(int D, int H) { return D == 512 && H % 32 == 0; }
 
 static void choose_split(int BT, int H, int D, int max_rows, int* nsplit, int* rps) {
     if (max_rows <= 0) { *nsplit = 1; *rps = 128; return; }
-    if (use32(D, H)) {
-        const int HG = H / 32;
-        int ns = std::max(1, 256 / (BT * HG));
+    if (use64(D, H)) {
+        const int HP = (H + 63) / 64;
+        const int ns = std::max(1, CSA_ATT_TARGET_WG / (BT * HP));
+        const int unit = ATT_TILES * TILE;
         int r = (max_rows + ns - 1) / ns;
-        r = (r + 4 * TILE - 1) / (4 * TILE) * (4 * TILE);      // each wave pair: an even number of tiles
+        r = std::max(r, CSA_ATT_MIN_TILES * TILE);
+        r = (r + unit - 1) / unit * unit;
         *rps = r;
         *nsplit = (max_rows + r - 1) / r;
         return;
@@ -699,10 +736,10 @@ static void choose_split(int BT, int H, int D, int max_rows, int* nsplit, int* r
     *nsplit = (max_rows + r - 1) / r;
 }
 
-// Row-space size of one query: dense N; sparse topk (padded to whole tiles for k_attn32) + window.
+// Row-space size of one query: dense N; sparse topk (padded to whole tiles for k_attn64) + window.
 static int attn_rows(int mode, int H, int D, int n, int W) {
     if (mode == 0) return n;
-    return (use32(D, H) ? (n + TILE - 1) / TILE * TILE : n) + W;
+    return (use64(D, H) ? (n + TILE - 1) / TILE * TILE : n) + W;
 }
 
 size_t attn_ws_bytes(int B, int Tq, int H, int D, int mode, int n, int W) {
@@ -739,20 +776,20 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         part_ml = (float2*)((char*)ws + align256((size_t)BT * ns * H * D * 4));
     }
     const float sl2 = scale * LOG2E;
-    if (use32(D, H)) {
-        const int nunits = BT * ns, HG = H / 32;
-        const int nblk = (nunits + 7) / 8 * 8 * HG;
+    if (use64(D, H)) {
+        const int nunits = BT * ns, HP = (H + 63) / 64;
+        const int nblk = (nunits + 7) / 8 * 8 * HP;
         // byte offsets of whole arrays must fit 32 bits for the buffer-load variant
         const bool big = (size_t)a.N * D * 2 > 0xffffffffull || (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
-#define CSA_ATTN32(M, BIG_)                                                                                  \
-    CSA_LAUNCH(tag, (k_attn32<M, BIG_>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, \
+#define CSA_ATTN64(M, BIG_)                                                                                  \
+    CSA_LAUNCH(tag, (k_attn64<M, BIG_>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, \
                nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse)
         if (a.mode == 0) {
-            if (big) CSA_ATTN32(0, true); else CSA_ATTN32(0, false);
+            if (big) CSA_ATTN64(0, true); else CSA_ATTN64(0, false);
         } else {
-            if (big) CSA_ATTN32(1, true); else CSA_ATTN32(1, false);
+            if (big) CSA_ATTN64(1, true); else CSA_ATTN64(1, false);
         }
-#undef CSA_ATTN32
+#undef CSA_ATTN64
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse);

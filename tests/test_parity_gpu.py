@@ -164,6 +164,9 @@ SPARSE_CASES = [
     (1, 3, 32, 128, 300, 37, 5, 4.0),          # ragged, several queries
     (1, 1, 16, 512, 100, 0, 17, 1.0),          # window only
     (1, 1, 16, 128, 100, 20, 0, 1.0),          # no window
+    (1, 2, 32, 512, 700, 100, 20, 2.0),        # one head group (half a head pair), ragged top-k
+    (1, 1, 96, 512, 2000, 300, 128, 1.0),      # 96 heads: the last head pair is half
+    (3, 1, 128, 512, 9000, 2048, 128, 1.0),    # long top-k: several tiles per split
 ]
 
 
@@ -203,6 +206,9 @@ DENSE_CASES = [
     (1, 1, 64, 512, 128 * 333, 128, 16.0),
     (1, 5, 16, 128, 4 * 33, 4, 4.0),           # causal visibility per query
     (1, 1, 16, 128, 40, 1, 1.0),               # ratio 1: textbook MQA
+    (1, 3, 96, 512, 128 * 50 + 7, 128, 4.0),   # several queries, 96 heads, ragged tail tile
+    (2, 1, 32, 512, 4 * 700, 4, 1.0),          # one head group
+    (1, 1, 64, 512, 128 * 20000, 128, 1.0),    # long prefix: many splits and tiles
 ]
 
 
