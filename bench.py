@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA+HCA decode queries/s & HBM GB/s at 1M ctx; indexer prefill TFLOP/s"
 HBM_PEAK_GBPS = 8000.0
 DOMINANT = "k_score"
-KERNELS = ("k_fill", "k_score", "k_collect", "k_select", "k_attn_sparse", "k_attn_dense", "k_combine")
+KERNELS = ("k_fill", "k_score", "k_collect", "k_select", "k_attn_pair", "k_attn_sparse", "k_attn_dense", "k_combine")
 
 
 def kernel_source_sha() -> str:

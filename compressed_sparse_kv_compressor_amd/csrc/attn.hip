@@ -264,25 +264,22 @@ constexpr int ATT_TILES = 3;      // tile buffers; a split's tile count is a mul
 // MODE 0: dense prefix (row r = entry r); MODE 1: selected entries then window rows.  BIG: some
 // array is beyond the reach of 32-bit byte offsets, so tiles are loaded with 64-bit addresses (the
 // other variant uses buffer loads only, which keeps the LDS wait counting exact in the main loop).
+typedef float SxArr[4][4][64][4];         // score exchange [wave][j/4][lane][j%4] (one parity)
+
 template <int MODE, bool BIG>
-__global__ __launch_bounds__(TPB, 1) void k_attn64(
-    const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
-    int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
+__device__ __forceinline__ void attn64_body(
+    int bid, uint16_t* bufA, uint16_t* bufB, uint16_t* bufC, SxArr* sx,
+    const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
+    int nsplit, int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse)
 {
     constexpr int D = 512;
     constexpr int KS = HD / 16;               // 32x32x16 k-steps over a d-half
     constexpr int DT = HD / 32;               // 32-wide d tiles of a d-half
     constexpr int HALF_B = TILE * HD * 2;     // bytes of one d-half of a tile (16 KiB)
-    // three tile buffers [d-half][32 rows][256] bf16 (distinct objects: the compiler tells a read of
-    // one from the loads in flight into another) and the score exchange [parity][wave][j/4][lane][j%4]
-    __shared__ __attribute__((aligned(1024))) uint16_t bufA[2 * TILE * HD];
-    __shared__ __attribute__((aligned(1024))) uint16_t bufB[2 * TILE * HD];
-    __shared__ __attribute__((aligned(1024))) uint16_t bufC[2 * TILE * HD];
-    __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];
 
     const int HP = (H + 63) / 64;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int xcd = bid & 7, slot = bid >> 3;
     const int hp = slot % HP, unit = (slot / HP) * 8 + xcd;
     if (unit >= nunits) return;                // padding workgroups (uniform exit)
     const int bt = unit / nsplit, split = unit % nsplit;
@@ -666,21 +663,90 @@ __global__ __launch_bounds__(TPB, 1) void k_attn64(
     }
 }
 
-// Merge split partials in split order: out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.
-template <int D>
-__global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
-                                                   int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse)
+// Tile buffers [d-half][32 rows][256] bf16 (distinct objects: the compiler tells a read of one from the
+// loads in flight into another) and the score exchange [parity][wave][j/4][lane][j%4].
+#define CSA_ATT64_LDS                                                         \
+    __shared__ __attribute__((aligned(1024))) uint16_t bufA[2 * TILE * HD];   \
+    __shared__ __attribute__((aligned(1024))) uint16_t bufB[2 * TILE * HD];   \
+    __shared__ __attribute__((aligned(1024))) uint16_t bufC[2 * TILE * HD];   \
+    __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];
+
+template <int MODE, bool BIG>
+__global__ __launch_bounds__(TPB, 1) void k_attn64(
+    const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
+    int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
+    float* __restrict__ lse)
 {
-    const int h = blockIdx.x, bt = blockIdx.y, d = threadIdx.x * 4;
+    CSA_ATT64_LDS
+    attn64_body<MODE, BIG>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
+                           part_o, part_ml, out, lse);
+}
+
+// One attention problem of a fused launch.
+struct AttnJob {
+    const uint16_t* q;
+    Rows R;
+    int Tq, H;
+    long long pos0;
+    float scale_log2;
+    int nunits, nsplit, rps;
+    float* part_o;
+    float2* part_ml;
+    uint16_t* out;
+    float* lse;
+};
+
+// CSA sparse (workgroups [0, nblk_s)) and HCA dense attention in one launch: the short, latency-bound
+// sparse workgroups run beside the dense ones instead of before them.
+template <bool BIG>
+__global__ __launch_bounds__(TPB, 1) void k_attn64_pair(AttnJob js, AttnJob jd, int nblk_s)
+{
+    CSA_ATT64_LDS
+    if ((int)blockIdx.x < nblk_s)
+        attn64_body<1, BIG>(blockIdx.x, bufA, bufB, bufC, sx, js.q, js.R, js.Tq, js.H, js.pos0, js.scale_log2,
+                            js.nunits, js.nsplit, js.rps, js.part_o, js.part_ml, js.out, js.lse);
+    else
+        attn64_body<0, BIG>(blockIdx.x - nblk_s, bufA, bufB, bufC, sx, jd.q, jd.R, jd.Tq, jd.H, jd.pos0,
+                            jd.scale_log2, jd.nunits, jd.nsplit, jd.rps, jd.part_o, jd.part_ml, jd.out, jd.lse);
+}
+#undef CSA_ATT64_LDS
+
+// Merge split partials in split order: out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.  Thread tid
+// owns d = 4 tid .. 4 tid + 3 of head h; the split loop is unrolled so that several partial loads are
+// in flight (the order of the sums is fixed, so the result is deterministic).
+template <int D>
+__device__ __forceinline__ void combine_body(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
+                                             int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
+                                             int h, int bt)
+{
+    const int d = threadIdx.x * 4;
+    const size_t s0 = (size_t)bt * nsplit * H + h;     // slot of split 0; split s at s0 + s H
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((size_t)bt * nsplit + s) * H + h].x);
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[s0 + (size_t)s * H].x);
     float l = 0.f;
     f32x4_t o = {0, 0, 0, 0};
     if (M != -INFINITY) {
-        for (int s = 0; s < nsplit; ++s) {
-            const size_t slot = ((size_t)bt * nsplit + s) * H + h;
+        int s = 0;
+        for (; s + 4 <= nsplit; s += 4) {
+            float2 ml[4];
+            f32x4_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const size_t slot = s0 + (size_t)(s + u) * H;
+                ml[u] = part_ml[slot];
+                v[u] = *(const f32x4_t*)(part_o + slot * D + d);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float f = exp2f(ml[u].x - M);      // 0 for empty splits (m = -inf)
+                l += f * ml[u].y;
+                o += f * v[u];
+            }
+        }
+        for (; s < nsplit; ++s) {
+            const size_t slot = s0 + (size_t)s * H;
             const float2 ml = part_ml[slot];
-            const float f = exp2f(ml.x - M);      // 0 for empty splits (m = -inf)
+            const float f = exp2f(ml.x - M);
             l += f * ml.y;
             o += f * *(const f32x4_t*)(part_o + slot * D + d);
         }
@@ -691,6 +757,22 @@ __global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ par
     v.y = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
     *(uint2*)(out + ((size_t)bt * H + h) * D + d) = v;
     if (lse && threadIdx.x == 0) lse[(size_t)bt * H + h] = l > 0.f ? (M + log2f(l)) * LN2 : -INFINITY;
+}
+
+template <int D>
+__global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
+                                                   int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse)
+{
+    combine_body<D>(part_o, part_ml, H, nsplit, out, lse, blockIdx.x, blockIdx.y);
+}
+
+// The combines of a fused launch: rows y < nbt_s of the grid merge job s, the rest job d.
+__global__ __launch_bounds__(128) void k_combine_pair(AttnJob js, AttnJob jd, int nbt_s)
+{
+    if ((int)blockIdx.y < nbt_s)
+        combine_body<512>(js.part_o, js.part_ml, js.H, js.nsplit, js.out, js.lse, blockIdx.x, blockIdx.y);
+    else
+        combine_body<512>(jd.part_o, jd.part_ml, jd.H, jd.nsplit, jd.out, jd.lse, blockIdx.x, blockIdx.y - nbt_s);
 }
 
 }  // namespace
@@ -810,6 +892,61 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
                        (uint16_t*)out, lse);
     } else {
         return fail(6, "attention: D = %d unsupported", D);
+    }
+    return 0;
+}
+
+
+// CSA sparse + HCA dense attention of one decode step in a single launch (and a single combine), when
+// both take k_attn64 with 32-bit offsets; returns -1 when it does not apply (the caller launches them
+// apart), else 0 or a status code.
+// Workspace: the sparse partials, then the dense partials.
+size_t attn_pair_ws_bytes(int B, int H, int D, int topk, int W, int Nh) {
+    return align256(attn_ws_bytes(B, 1, H, D, 1, topk, W)) + attn_ws_bytes(B, 1, H, D, 0, Nh, 0);
+}
+
+int attn_pair_launch(const void* q_s, const AttnRows& as, void* out_s, float* lse_s, const void* q_d,
+                     const AttnRows& ad, void* out_d, float* lse_d, int B, int H, int D, long long pos0, float scale,
+                     void* ws, hipStream_t st) {
+    if (!use64(D, H)) return -1;
+    const bool big = (size_t)as.N * D * 2 > 0xffffffffull || (size_t)as.Lr * D * 2 > 0xffffffffull ||
+                     (size_t)ad.N * D * 2 > 0xffffffffull;
+    if (big) return -1;
+    auto rows_of = [](const AttnRows& a) {
+        Rows R;
+        R.mode = a.mode; R.kv = (const uint16_t*)a.kv; R.N = a.N; R.L = a.L; R.ratio = a.ratio; R.idx = a.idx;
+        R.topk = a.topk; R.kv_raw = (const uint16_t*)a.kv_raw; R.Lr = a.Lr; R.raw0 = a.raw0; R.W = a.W;
+        return R;
+    };
+    const int HP = (H + 63) / 64;
+    const float sl2 = scale * LOG2E;
+    AttnJob js{}, jd{};
+    char* wsp = (char*)ws;
+    int nblk[2], nbt[2];
+    for (int k = 0; k < 2; ++k) {
+        const AttnRows& a = k == 0 ? as : ad;
+        AttnJob& j = k == 0 ? js : jd;
+        const int max_rows = a.mode == 0 ? a.N : attn_rows(1, H, D, a.topk, a.W);
+        int ns, rps;
+        choose_split(B, H, D, max_rows, &ns, &rps);
+        j.q = (const uint16_t*)(k == 0 ? q_s : q_d);
+        j.R = rows_of(a);
+        j.Tq = 1; j.H = H; j.pos0 = pos0; j.scale_log2 = sl2;
+        j.nunits = B * ns; j.nsplit = ns; j.rps = rps;
+        j.out = (uint16_t*)(k == 0 ? out_s : out_d);
+        j.lse = k == 0 ? lse_s : lse_d;
+        if (ns > 1) {
+            j.part_o = (float*)wsp;
+            j.part_ml = (float2*)(wsp + align256((size_t)B * ns * H * D * 4));
+        }
+        wsp += align256(attn_ws_bytes(B, 1, H, D, a.mode, a.mode == 0 ? a.N : a.topk, a.W));
+        nblk[k] = (j.nunits + 7) / 8 * 8 * HP;
+        nbt[k] = ns > 1 ? B : 0;
+    }
+    CSA_LAUNCH("k_attn_pair", k_attn64_pair<false>, dim3(nblk[0] + nblk[1]), dim3(TPB), 0, st, js, jd, nblk[0]);
+    if (nbt[0] + nbt[1] > 0) {
+        AttnJob j0 = nbt[0] ? js : jd, j1 = jd;
+        CSA_LAUNCH("k_combine", k_combine_pair, dim3(H, nbt[0] + nbt[1]), dim3(128), 0, st, j0, j1, nbt[0]);
     }
     return 0;
 }
