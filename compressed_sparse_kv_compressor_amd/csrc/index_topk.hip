@@ -47,6 +47,7 @@ using namespace csa;
 constexpr int BINS1 = 4096;                  // histogram of key bits 31..20
 constexpr int BINS2 = 4096;                  // histogram of key bits 19..8 inside the threshold bin
 constexpr int HW_DMAX = BINS1 + BINS2, HW_CNT = BINS1 + BINS2 + 1;   // row max error bound; candidate count
+constexpr int HW_B1 = BINS1 + BINS2 + 2, HW_A1 = BINS1 + BINS2 + 3;    // level-1 bin of tau; count above it
 constexpr int HIST_WORDS = BINS1 + BINS2 + 8;
 constexpr int TPB = 256;
 
@@ -326,6 +327,7 @@ __global__ __launch_bounds__(TPB) void k_score(
 constexpr int STPB = 1024;
 constexpr int CCHUNK = STPB * 16;    // entries per workgroup (16 waves x 16 groups of 64)
 constexpr int BAND_LDS = 1024;       // band entries ranked in LDS (larger bands: 64-bit radix in HBM)
+constexpr int CAND_LDS = 8192;       // candidates kept in LDS by k_select (more: read from HBM each pass)
 
 // Wave-cooperative exact score of entry s: HI head groups of LPH lanes, each
 // lane EPL elements; per head, fixed-point window accumulation (as in
@@ -450,26 +452,33 @@ __global__ __launch_bounds__(STPB) void k_collect(const float* __restrict__ S, u
     const int r = blockIdx.y, t = r % Tq;
     const int nv = n_visible(pos0 + t, L, m, Nc);
     if (nv <= topk) return;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int s_w = blockIdx.x * CCHUNK + wave * (GPW * 64);
+    const float* Sr = S + (size_t)r * NcP;
+    // the chunk's scores first: their loads overlap the histogram scan below
+    float v[GPW];
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+        const int sidx = s_w + gi * 64 + lane;
+        v[gi] = sidx < nv ? Sr[sidx] : -INFINITY;
+    }
     uint32_t* H = hist + (size_t)r * HIST_WORDS;
     for (int i = threadIdx.x; i < BINS1; i += STPB) lh[i] = H[i];
     __syncthreads();
     find_bin_wide(lh, (uint32_t)topk, res, scratch);
     const uint32_t b1 = res[0];
+    if (blockIdx.x == 0 && threadIdx.x == 0) { H[HW_B1] = b1; H[HW_A1] = res[1]; }   // for k_select
     const double thr = (double)key_f32(b1 << 20) - 2.0 * (double)__uint_as_float(H[HW_DMAX]);
     for (int i = threadIdx.x; i < BINS2; i += STPB) lh[i] = 0;
     __syncthreads();
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    const int s_w = blockIdx.x * CCHUNK + wave * (GPW * 64);
-    const float* Sr = S + (size_t)r * NcP;
     unsigned long long mask[GPW];
     uint32_t cnt = 0;
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
         const int sidx = s_w + gi * 64 + lane;
-        const float v = sidx < nv ? Sr[sidx] : -INFINITY;
-        const bool c = sidx < nv && (double)v >= thr;
+        const bool c = sidx < nv && (double)v[gi] >= thr;
         if (c) {
-            const uint32_t key = f32_key(v);
+            const uint32_t key = f32_key(v[gi]);
             if ((key >> 20) == b1) atomicAdd(&lh[(key >> 8) & (BINS2 - 1)], 1u);
         }
         mask[gi] = __ballot(c);
@@ -492,7 +501,7 @@ __global__ __launch_bounds__(STPB) void k_collect(const float* __restrict__ S, u
     for (int gi = 0; gi < GPW; ++gi) {
         const int sidx = s_w + gi * 64 + lane;
         if ((mask[gi] >> lane) & 1ull)
-            Lr[pos + __popcll(mask[gi] & below)] = make_uint2((uint32_t)sidx, __float_as_uint(Sr[sidx]));
+            Lr[pos + __popcll(mask[gi] & below)] = make_uint2((uint32_t)sidx, __float_as_uint(v[gi]));
         pos += __popcll(mask[gi]);
     }
     for (int i = threadIdx.x; i < BINS2; i += STPB)
@@ -510,11 +519,14 @@ __global__ __launch_bounds__(STPB) void k_select(
     int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
 {
     constexpr int ES = DT == 0 ? 2 : 1;
-    __shared__ uint32_t lh[BINS1];
+    __shared__ uint32_t lh[BINS2];
     __shared__ uint32_t scratch[STPB / 64], res[4], nband;
     __shared__ uint32_t cpre[STPB + 1], cbase[STPB];
     __shared__ unsigned long long bkey[BAND_LDS];
     __shared__ uint32_t bpos[BAND_LDS];
+    __shared__ uint2 bl[BAND_LDS];                    // band entries (index, position); more go to HBM
+    __shared__ uint2 cl[CAND_LDS];                    // candidates in index order (when they fit)
+    __shared__ uint8_t fl[CAND_LDS];                  // their flags
     const int r = blockIdx.x, b = r / Tq, t = r % Tq, tid = threadIdx.x;
     const int lane = lane_id(), wave = tid >> 6;
     const int nv = n_visible(pos0 + t, L, m, Nc);
@@ -539,7 +551,7 @@ __global__ __launch_bounds__(STPB) void k_select(
         __syncthreads();
     }
     const uint32_t n = total;
-    auto cand = [&](uint32_t e) -> uint2 {            // e-th candidate in index order
+    auto cand_g = [&](uint32_t e) -> uint2 {          // e-th candidate in index order, from HBM
         int lo_c = 0, hi_c = NCH - 1;                 // largest c with cpre[c] <= e: a non-empty chunk holding e
         while (lo_c < hi_c) {
             const int mid = (lo_c + hi_c + 1) >> 1;
@@ -547,14 +559,17 @@ __global__ __launch_bounds__(STPB) void k_select(
         }
         return Lr[cbase[lo_c] + (e - cpre[lo_c])];
     };
+    const bool inl = n <= (uint32_t)CAND_LDS;        // candidates and flags live in LDS (uniform)
+    auto cand = [&](uint32_t e) -> uint2 { return inl ? cl[e] : cand_g(e); };
+    auto fget = [&](uint32_t e) -> uint8_t { return inl ? fl[e] : F[e]; };
+    auto fset = [&](uint32_t e, uint8_t f) { if (inl) fl[e] = f; else F[e] = f; };
 
-    // 1. tau: the bin b1 (level 1), then b2 (level 2, built by k_collect), then the last 8 bits
-    for (int i = tid; i < BINS1; i += STPB) lh[i] = H[i];
-    __syncthreads();
-    find_bin_wide(lh, (uint32_t)topk, res, scratch);
-    const uint32_t b1 = res[0], a1 = res[1];
-    __syncthreads();
+    // 1. tau: the bin b1 (level 1, found by k_collect), then b2 (level 2, built by k_collect), then the
+    //    last 8 bits.  The candidates are read once into LDS in the same pass as the level-2 histogram.
+    const uint32_t b1 = H[HW_B1], a1 = H[HW_A1];
     for (int i = tid; i < BINS2; i += STPB) lh[i] = H[BINS1 + i];
+    if (inl)
+        for (uint32_t e = tid; e < n; e += STPB) cl[e] = cand_g(e);
     __syncthreads();
     find_bin_wide(lh, (uint32_t)topk - a1, res, scratch);
     const uint32_t b2 = res[0], a2 = res[1];
@@ -582,14 +597,20 @@ __global__ __launch_bounds__(STPB) void k_select(
         const double v = (double)__uint_as_float(c.y);
         uint8_t f = 0;
         if (v > hi) { f = 1; ++my_in; }
-        else if (v >= lo) { f = 2; Bg[atomicAdd(&nband, 1u)] = make_uint2(c.x, e); }
-        F[e] = f;
+        else if (v >= lo) {
+            f = 2;
+            const uint32_t slot = atomicAdd(&nband, 1u);
+            if (slot < (uint32_t)BAND_LDS) bl[slot] = make_uint2(c.x, e);
+            else Bg[slot] = make_uint2(c.x, e);
+        }
+        fset(e, f);
     }
     uint32_t n_in;
     block_scan(my_in, scratch, &n_in);
     __syncthreads();
     const uint32_t nb = nband;
     const uint32_t need = (uint32_t)topk - n_in;       // 0 <= need <= nb by construction
+    auto band = [&](uint32_t i) -> uint2 { return i < (uint32_t)BAND_LDS ? bl[i] : Bg[i]; };
 
     // 3. exact rescoring of the band (one wave per entry); composite keys (exact score key,
     //    inverted index): larger composite = earlier in the order
@@ -598,11 +619,11 @@ __global__ __launch_bounds__(STPB) void k_select(
     const float* wrow = w_idx + (size_t)r * HI;
     if (need > 0 && need < nb) {
         for (uint32_t i = wave; i < nb; i += STPB / 64) {
-            const uint2 be = Bg[i];
+            const uint2 be = band(i);
             const float sx = wave_exact_score<DT, DI, HI>(qrow, wrow, (const char*)k_idx + ((size_t)b * Nc + be.x) * DI * ES);
             if (lane == 0) {
                 const unsigned long long ck = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - be.x);
-                Kg[i] = ck;
+                if (nb > (uint32_t)BAND_LDS) Kg[i] = ck;       // the radix path reads every key from HBM
                 if (i < BAND_LDS) { bkey[i] = ck; bpos[i] = be.y; }
             }
         }
@@ -611,13 +632,13 @@ __global__ __launch_bounds__(STPB) void k_select(
 
     // 4. the `need` largest composite keys among the band get flag 1
     if (need > 0 && need == nb) {
-        for (uint32_t i = tid; i < nb; i += STPB) F[Bg[i].y] = 1;
+        for (uint32_t i = tid; i < nb; i += STPB) fset(band(i).y, 1);
     } else if (need > 0 && nb <= BAND_LDS) {
         for (uint32_t i = tid; i < nb; i += STPB) {          // rank by counting (keys are distinct)
             const unsigned long long ki = bkey[i];
             uint32_t rank = 0;
             for (uint32_t j = 0; j < nb; ++j) rank += bkey[j] > ki;
-            if (rank < need) F[bpos[i]] = 1;
+            if (rank < need) fset(bpos[i], 1);
         }
     } else if (need > 0) {
         unsigned long long kp = 0;
@@ -638,7 +659,7 @@ __global__ __launch_bounds__(STPB) void k_select(
             __syncthreads();
         }
         for (uint32_t i = tid; i < nb; i += STPB)
-            if (Kg[i] >= kp) F[Bg[i].y] = 1;
+            if (Kg[i] >= kp) fset(band(i).y, 1);
     }
     __threadfence_block();
     __syncthreads();
@@ -647,11 +668,11 @@ __global__ __launch_bounds__(STPB) void k_select(
     const uint32_t per = (n + STPB - 1) / STPB;
     const uint32_t e0 = min(n, tid * per), e1 = min(n, e0 + per);
     uint32_t mine = 0;
-    for (uint32_t e = e0; e < e1; ++e) mine += F[e] == 1;
+    for (uint32_t e = e0; e < e1; ++e) mine += fget(e) == 1;
     uint32_t tot2;
     uint32_t o = block_scan(mine, scratch, &tot2);
     for (uint32_t e = e0; e < e1; ++e)
-        if (F[e] == 1 && o < (uint32_t)topk) out[o++] = (int32_t)cand(e).x;
+        if (fget(e) == 1 && o < (uint32_t)topk) out[o++] = (int32_t)cand(e).x;
     if (cnt_out && tid == 0) cnt_out[r] = topk;
 }
 

@@ -145,6 +145,32 @@ def test_index_topk_all_equal_scores(b):
     assert list(got_idx[0, 0]) == list(range(topk))
 
 
+@pytest.mark.parametrize("dt", [0, 1])
+def test_index_topk_all_equal_scores_large(b, dt):
+    # more candidates than the select kernel keeps in LDS, and a band wider than its LDS ranking:
+    # the HBM fallbacks (candidate reads, 64-bit radix over the band) must give the same answer
+    B, HI, dI, m, topk = 1, 8, 128, 4, 300
+    Nc = 20000
+    q, w, k, _ = synth.indexer_inputs(14, B, 1, HI, dI, Nc, dt)
+    k = np.repeat(k[:, :1], Nc, axis=1)
+    got_idx, _ = run_index(b, q, w, k, Nc * m, m, Nc * m - 1, topk, dt)
+    assert list(got_idx[0, 0]) == list(range(topk))
+
+
+def test_index_topk_wide_band_ties(b):
+    # 3000 exact copies of one key among random keys: the k-th score falls inside the tied block
+    B, HI, dI, m, topk = 1, 8, 128, 4, 2000
+    Nc = 12000
+    q, w, k, _ = synth.indexer_inputs(15, B, 1, HI, dI, Nc, 0)
+    S, _ = oracle.index_scores(q, w, k, Nc * m, m, Nc * m - 1)
+    src = int(np.argsort(-S[0, 0], kind="stable")[1500])       # a key ranked 1500th
+    k = k.copy()
+    k[:, 5000:8000] = k[:, src:src + 1]
+    want_idx, want_cnt, _, _ = oracle.index_topk(q, w, k, Nc * m, m, Nc * m - 1, topk)
+    got_idx, _ = run_index(b, q, w, k, Nc * m, m, Nc * m - 1, topk, 0)
+    assert np.array_equal(got_idx, want_idx)
+
+
 def test_index_topk_deterministic(b):
     q, w, k, _ = synth.indexer_inputs(13, 2, 1, 8, 128, 20000, 1)
     a1, _ = run_index(b, q, w, k, 80000, 4, 79999, 512, 1)
