@@ -60,6 +60,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed region, run two plain device copies of MIB MiB (a kernel of known "
+                         "traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE by)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -174,6 +177,14 @@ def main():
                      "traffic": load_traffic(score_bytes), "algorithmic_bytes_per_launch": score_bytes},
         "input_gen_s": round(gen_s, 1),
     }
+
+    if args.copy_calibration > 0:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = args.copy_calibration << 20
 
     if not args.no_cpu_baseline:
         out.update(cpu_leg(cfg, base, outs[0], dev))

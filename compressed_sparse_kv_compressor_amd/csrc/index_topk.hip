@@ -187,20 +187,26 @@ __global__ __launch_bounds__(TPB) void k_score(
         const bool av = ta < Tq && ha < HI;
         bf16x8_t qb[STEPS], qa[STEPS];
         u32x4_t qf8a[2];                      // |q| as raw e4m3 bytes (DT == 1)
+        // Element order of the contraction (shared by Q and K): lane group grp takes the 16-byte chunks
+        // at bytes 64 i + 16 grp of a row, so that one load instruction reads 64 contiguous bytes of
+        // each of its 16 key rows.  bf16: k-step s = chunk s; e4m3: k-step s = half (s & 1) of chunk s / 2.
         if (av) {
             const size_t r = (size_t)b * Tq + ta;
-            const char* qp = (const char*)q_idx + (r * HI + ha) * DI * ES + (size_t)grp * EPL * ES;
+            const char* qp = (const char*)q_idx + (r * HI + ha) * DI * ES + (size_t)grp * 16;
 #pragma unroll
             for (int s = 0; s < STEPS; ++s) {
                 u32x4_t v;
-                if (DT == 0) v = *(const u32x4_t*)(qp + s * 16);
-                else v = e4m3x8_to_bf16x8(*(const uint32_t*)(qp + s * 8), *(const uint32_t*)(qp + s * 8 + 4));
+                if (DT == 0) v = *(const u32x4_t*)(qp + s * 64);
+                else {
+                    const char* c = qp + (s >> 1) * 64 + (s & 1) * 8;
+                    v = e4m3x8_to_bf16x8(*(const uint32_t*)c, *(const uint32_t*)(c + 4));
+                }
                 qb[s] = as_bf16x8(v);
                 qa[s] = as_bf16x8(v & 0x7fff7fffu);
             }
             if (DT == 1) {
                 qf8a[0] = (*(const u32x4_t*)qp) & 0x7f7f7f7fu;
-                qf8a[1] = DI == 128 ? (*(const u32x4_t*)(qp + 16)) & 0x7f7f7f7fu : u32x4_t{0, 0, 0, 0};
+                qf8a[1] = DI == 128 ? (*(const u32x4_t*)(qp + 64)) & 0x7f7f7f7fu : u32x4_t{0, 0, 0, 0};
             }
         } else {
 #pragma unroll
@@ -231,21 +237,23 @@ __global__ __launch_bounds__(TPB) void k_score(
         const int lrow = tr - g * G;
 
         // key loads are software-pipelined: batch i+1 is in flight while batch i computes
+        // (rows past the end reread the last row: branch-free loads keep the wait counts exact, so the
+        //  next batch stays in flight; those keys are never written)
         auto load_batch = [&](int tt0, u32x4_t (&dst)[U][NV]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int krow = key0 + ((tt0 + u) * 4 + wave) * 16 + col;
-                const char* kp = (const char*)k_idx + ((size_t)b * Nc + krow) * DI * ES + (size_t)grp * KB;
+                const int krow = min(key0 + ((tt0 + u) * 4 + wave) * 16 + col, Nc - 1);
+                const char* kp = (const char*)k_idx + ((size_t)b * Nc + krow) * DI * ES + (size_t)grp * 16;
 #pragma unroll
-                for (int i = 0; i < NV; ++i)
-                    dst[u][i] = krow < Nc ? *(const u32x4_t*)(kp + i * 16) : u32x4_t{0, 0, 0, 0};
+                for (int i = 0; i < NV; ++i) dst[u][i] = *(const u32x4_t*)(kp + i * 64);
             }
         };
         auto compute_batch = [&](int tt0, const u32x4_t (&cur)[U][NV]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
+                    // (tiles past the visible keys are computed and dropped: no branch between the
+                    //  loads and their uses)
                     const int kbase = key0 + ((tt0 + u) * 4 + wave) * 16;
-                    if (kbase >= nvmax) break;
                     f32x4_t acc = {0, 0, 0, 0}, aacc = {0, 0, 0, 0};
 #pragma unroll
                     for (int s = 0; s < STEPS; ++s) {
@@ -290,17 +298,23 @@ __global__ __launch_bounds__(TPB) void k_score(
                     }
                 }
         };
+        // The loads of the next batch are issued unconditionally (past the end they reread the current
+        // batch, an L2 hit), so that no branch separates loads from their uses and the compiler's wait
+        // counts stay exact: the next batch stays in flight while this one computes.
+        __builtin_amdgcn_s_waitcnt(0);        // the per-row loads above have landed
         u32x4_t ka[U][NV], kb[U][NV];
-        if (key0 + wave * 16 < nvmax) load_batch(0, ka);
-        for (int tt0 = 0; tt0 < tiles; tt0 += 2 * U) {
-            if (key0 + (tt0 * 4 + wave) * 16 >= nvmax) break;
-            const bool more1 = tt0 + U < tiles && key0 + ((tt0 + U) * 4 + wave) * 16 < nvmax;
-            if (more1) load_batch(tt0 + U, kb);
-            compute_batch(tt0, ka);
-            if (!more1) break;
-            const bool more2 = tt0 + 2 * U < tiles && key0 + ((tt0 + 2 * U) * 4 + wave) * 16 < nvmax;
-            if (more2) load_batch(tt0 + 2 * U, ka);
-            compute_batch(tt0 + U, kb);
+        if (key0 + wave * 16 < nvmax) {
+            load_batch(0, ka);
+            for (int tt0 = 0; tt0 < tiles; tt0 += 2 * U) {
+                const bool more1 = tt0 + U < tiles && key0 + ((tt0 + U) * 4 + wave) * 16 < nvmax;
+                load_batch(more1 ? tt0 + U : tt0, kb);
+                compute_batch(tt0, ka);
+                if (!more1) break;
+                const bool more2 = tt0 + 2 * U < tiles && key0 + ((tt0 + 2 * U) * 4 + wave) * 16 < nvmax;
+                load_batch(more2 ? tt0 + 2 * U : tt0 + U, ka);
+                compute_batch(tt0 + U, kb);
+                if (!more2) break;
+            }
         }
         if (writer) {
             if (lrow < nlds) atomicMax(&ldmax[lrow], __float_as_uint(dmax_loc));
