@@ -34,7 +34,7 @@ def _load():
         "csa_last_error": ([], ctypes.c_char_p),
         "csa_compress_ws_bytes": ([I, LL, I, I], Z),
         "csa_compress": ([P, P, P, P, P, I, LL, I, I, I, I, I, I, P, P, P, P, Z, P], I),
-        "csa_index_topk_ws_bytes": ([I, I, I], Z),
+        "csa_index_topk_ws_bytes": ([I, I, I, I, I, I, I], Z),
         "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, Z, P], I),
         "csa_sparse_attn_ws_bytes": ([I, I, I, I, I, I], Z),
         "csa_sparse_attn": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, Z, P], I),
@@ -121,7 +121,7 @@ def csa_index_topk(q_idx, w_idx, k_idx, dtype: int, L: int, m: int, pos0: int, t
                    ws=None, stream=None):
     B, Tq, HI, dI = q_idx.shape
     Nc = k_idx.shape[1]
-    need = lib.csa_index_topk_ws_bytes(B, Tq, Nc)
+    need = lib.csa_index_topk_ws_bytes(B, Tq, HI, dI, Nc, topk, dtype)
     if ws is None:
         ws = workspace(need, q_idx.device)
     _check(lib.csa_index_topk(_p(q_idx), _p(w_idx), _p(k_idx), dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,

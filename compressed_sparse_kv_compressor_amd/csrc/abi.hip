@@ -232,9 +232,9 @@ int csa_compress(const void* hidden, const void* w_kv, const void* w_ik, const f
                                      ik_out, W > 0 ? win_out : nullptr, ws, (hipStream_t)stream);
 }
 
-size_t csa_index_topk_ws_bytes(int B, int Tq, int Nc) {
-    if (B < 1 || Tq < 1 || Nc < 1) return 0;
-    return csa_host::index_topk_ws_bytes(B, Tq, Nc);
+size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype) {
+    if (B < 1 || Tq < 1 || Nc < 1 || HI < 1 || dI < 1 || topk < 1) return 0;
+    return csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk);
 }
 
 int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq, int HI, int dI,
@@ -244,7 +244,7 @@ int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int
     csa_host::g_err[0] = 0;
     int rc = validate_index(fn, q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out, cnt_out);
     if (rc) return rc;
-    rc = check_ws(fn, ws, ws_bytes, csa_host::index_topk_ws_bytes(B, Tq, Nc));
+    rc = check_ws(fn, ws, ws_bytes, csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk));
     if (rc) return rc;
     return csa_host::index_topk_launch(q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out,
                                        cnt_out, ws, (hipStream_t)stream);
@@ -294,7 +294,7 @@ size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a) {
     if (!a || a->B < 1 || a->L < 1 || a->m < 1 || a->mh < 1 || a->topk < 1) return 0;
     const int Nc = (int)((a->L + a->m - 1) / a->m), Nh = (int)((a->L + a->mh - 1) / a->mh);
     size_t s = a->idx_out ? 0 : align256((size_t)a->B * a->topk * 4);
-    s += align256(csa_host::index_topk_ws_bytes(a->B, 1, Nc));
+    s += align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk));
     s += csa_host::attn_pair_ws_bytes(a->B, a->H, a->D, a->topk, a->W, Nh);
     return s;
 }
@@ -324,7 +324,7 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
         idx = (int32_t*)w;
         w += align256((size_t)a->B * a->topk * 4);
     }
-    const size_t iws = align256(csa_host::index_topk_ws_bytes(a->B, 1, Nc));
+    const size_t iws = align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk));
     rc = csa_host::index_topk_launch(a->q_idx, a->w_idx, a->k_idx, a->idx_dtype, a->B, 1, a->HI, a->dI, Nc, a->L, a->m,
                                      p, a->topk, idx, nullptr, w, st);
     if (rc) return rc;

@@ -38,6 +38,7 @@
 // order the MFMA accumulates in, provided its error stays inside the bound.
 #include "common.h"
 #include "exact_dot.h"
+#include "index_common.h"
 #include "kernels.h"
 
 namespace {
@@ -51,11 +52,6 @@ constexpr int HW_B1 = BINS1 + BINS2 + 2, HW_A1 = BINS1 + BINS2 + 3;    // level-
 constexpr int HIST_WORDS = BINS1 + BINS2 + 8;
 constexpr int TPB = 256;
 
-__device__ __forceinline__ int n_visible(long long p, long long L, int m, int Nc) {
-    if (p >= L - 1) return Nc;
-    long long v = (p + 1) / m;
-    return v < Nc ? (int)v : Nc;
-}
 
 // Given a histogram in LDS (nb bins, nb % TPB == 0) find the bin b holding the
 // need-th largest element: sum(h[b+1..]) < need <= sum(h[b..]).  Results in
@@ -130,14 +126,6 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
                    e4m3x2_to_bf16x2<false>(x1), e4m3x2_to_bf16x2<true>(x1)};
 }
 
-// Error model of the MFMA path:
-//   |d~_h - d_h| <= E_h = C_DOT * A_h,  A_h = MFMA(|q_h|, |k|) ~ sum_i |q_hi k_i|
-//   |S~ - S| <= sum_h |w_h| ( C_SUM (|d~_h| + E_h) + E_h ) (1 + 2^-10) + 2^-24 |S~| + 2^-126
-// C_DOT = 2^-18 is 64 unit roundoffs (the bf16 MFMA measures <= 2 u sum|p| on
-// gfx950); C_SUM = 2^-19 covers the fp32 rounding of the head reduction on both
-// sides and the final RN32 of each exact dot.
-#define C_DOT 3.814697265625e-06f   // 2^-18
-#define C_SUM 1.9073486328125e-06f  // 2^-19
 
 // ---------------------------------------------------------------------------
 // k_score
@@ -343,114 +331,9 @@ constexpr int CCHUNK = STPB * 16;    // entries per workgroup (16 waves x 16 gro
 constexpr int BAND_LDS = 1024;       // band entries ranked in LDS (larger bands: 64-bit radix in HBM)
 constexpr int CAND_LDS = 8192;       // candidates kept in LDS by k_select (more: read from HBM each pass)
 
-// Wave-cooperative exact score of entry s: HI head groups of LPH lanes, each
-// lane EPL elements; per head, fixed-point window accumulation (as in
-// exact_dot.h) reduced across the group, then the fma chain in head order.
-template <int DT, int DI, int HI>
-__device__ float wave_exact_score(const void* qrow, const float* wrow, const void* krow) {
-    using namespace csa_exact;
-    constexpr int LPH = 64 / HI, EPL = DI / LPH, ES = DT == 0 ? 2 : 1;
-    const int lane = lane_id(), h = lane / LPH, sub = lane % LPH;
-    const char* qp = (const char*)qrow + ((size_t)h * DI + sub * EPL) * ES;
-    const char* kp = (const char*)krow + (size_t)sub * EPL * ES;
-    uint32_t P[EPL];
-    int ex[EPL];
-    uint32_t ng[EPL];
-    int top = -100000;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        xv x = DT == 0 ? decode_bf16(((const uint16_t*)qp)[i]) : decode_e4m3(((const uint8_t*)qp)[i]);
-        xv y = DT == 0 ? decode_bf16(((const uint16_t*)kp)[i]) : decode_e4m3(((const uint8_t*)kp)[i]);
-        P[i] = x.M * y.M;
-        ex[i] = x.e + y.e;
-        ng[i] = x.neg ^ y.neg;
-        if (P[i]) top = max(top, ex[i] + 31 - (int)__clz((int)P[i]));
-    }
-#pragma unroll
-    for (int o = 1; o < LPH; o <<= 1) top = max(top, __shfl_xor(top, o, 64));
-    const int base = top - 100;
-    u128 pos = 0, neg = 0;
-    int wide = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        if (!P[i]) continue;
-        const int sh = ex[i] - base;
-        if (sh < 0) { wide = 1; continue; }
-        const u128 v = ((u128)P[i]) << (unsigned)sh;
-        if (ng[i]) neg += v; else pos += v;
-    }
-#pragma unroll
-    for (int o = 1; o < LPH; o <<= 1) {
-        wide |= __shfl_xor(wide, o, 64);
-        uint32_t p0 = (uint32_t)pos, p1 = (uint32_t)(pos >> 32), p2 = (uint32_t)(pos >> 64), p3 = (uint32_t)(pos >> 96);
-        uint32_t n0 = (uint32_t)neg, n1 = (uint32_t)(neg >> 32), n2 = (uint32_t)(neg >> 64), n3 = (uint32_t)(neg >> 96);
-        p0 = __shfl_xor(p0, o, 64); p1 = __shfl_xor(p1, o, 64); p2 = __shfl_xor(p2, o, 64); p3 = __shfl_xor(p3, o, 64);
-        n0 = __shfl_xor(n0, o, 64); n1 = __shfl_xor(n1, o, 64); n2 = __shfl_xor(n2, o, 64); n3 = __shfl_xor(n3, o, 64);
-        pos += ((u128)p3 << 96) | ((u128)p2 << 64) | ((u128)p1 << 32) | p0;
-        neg += ((u128)n3 << 96) | ((u128)n2 << 64) | ((u128)n1 << 32) | n0;
-    }
-    float d;
-    if (wide) {
-        d = exact_dot<DT>((const char*)qrow + (size_t)h * DI * ES, krow, DI);   // rare: long accumulator
-    } else {
-        d = pos >= neg ? round_to_f32(pos - neg, base, false) : round_to_f32(neg - pos, base, true);
-    }
-    const float rr = d > 0.0f ? d : 0.0f;
-    float Sx = 0.0f;
-    for (int hh = 0; hh < HI; ++hh) {
-        const float rh = __shfl(rr, hh * LPH, 64);
-        Sx = __builtin_fmaf(wrow[hh], rh, Sx);
-    }
-    return Sx;
-}
 
 
-// wave 0: find the bin (of 256, counting from the top) that holds the need-th
-// largest element given the count already above; writes out[0] = bin,
-// out[1] = count above that bin.
-__device__ void wave_find_bin256(const uint32_t* h, uint32_t need, uint32_t above, uint32_t* out) {
-    const int lane = lane_id();
-    // lane L covers bins 255-4L .. 252-4L (descending)
-    uint32_t c[4], s = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { c[i] = h[255 - 4 * lane - i]; s += c[i]; }
-    uint32_t incl = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-    }
-    uint32_t acc = above + incl - s;
-    if (acc < need && need <= acc + s) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (acc + c[i] >= need) { out[0] = 255 - 4 * lane - i; out[1] = acc; break; }
-            acc += c[i];
-        }
-    }
-}
 
-// Block-wide exclusive scan (1024 threads); returns the exclusive prefix, *total the sum.
-__device__ uint32_t block_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-    uint32_t incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t x = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += x;
-    }
-    if (lane == 63) scratch[wave] = incl;
-    __syncthreads();
-    uint32_t wprefix = 0, tot = 0;
-    for (int w = 0; w < nw; ++w) {
-        const uint32_t c = scratch[w];
-        if (w < wave) wprefix += c;
-        tot += c;
-    }
-    __syncthreads();
-    *total = tot;
-    return wprefix + incl - v;
-}
 
 // k_collect: each workgroup filters CCHUNK entries of one row against the row's threshold (lower edge of
 // the bin b1 holding the k-th largest S~, minus 2 Dmax), appends (index, S~) pairs to the row's candidate
@@ -701,7 +584,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // S~ [R][NcP] f32 | hist [R][HIST_WORDS] | list [R][NcP] (index, S~) | chunk table [R][NcP/CCHUNK] |
 // band [R][NcP] (index, position) | band keys [R][NcP] u64 | flags [R][NcP] u8
-size_t index_topk_ws_bytes(int B, int Tq, int Nc) {
+static size_t decode_index_ws_bytes(int B, int Tq, int Nc) {
     const size_t R = (size_t)B * Tq;
     const size_t NcP = ((size_t)Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
     return align256(R * NcP * 4) + align256(R * HIST_WORDS * 4) + align256(R * NcP * 8) +
@@ -744,9 +627,16 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
     return 0;
 }
 
+size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk) {
+    if (prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk)) return prefill_index_ws_bytes(B, Tq, Nc);
+    return decode_index_ws_bytes(B, Tq, Nc);
+}
+
 int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
                       int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
                       int32_t* idx_out, int32_t* cnt_out, void* ws, hipStream_t st) {
+    if (prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk))
+        return prefill_index_launch(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk, idx_out, cnt_out, ws, st);
 #define CSA_IDX_CASE(DT, DI, HI_)                                                              \
     if (dtype == DT && dI == DI && HI == HI_)                                                  \
         return launch_index<DT, DI, HI_>(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk,     \

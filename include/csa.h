@@ -117,8 +117,12 @@ int csa_compress(const void* hidden, const void* w_kv, const void* w_ik,
  *           padded with -1 after cnt entries
  *   cnt_out [B][Tq] int32 or NULL: min(topk, n_visible)
  * Supported: dtype in {CSA_BF16, CSA_E4M3}; HI in {1,2,4,8,16}; dI in {64,128};
- * 1 <= topk <= 4096; 1 <= Tq <= 65536; Nc <= 2^24; pos0 >= 0. */
-size_t csa_index_topk_ws_bytes(int B, int Tq, int Nc);
+ * 1 <= topk <= 4096; 1 <= Tq <= 65536; Nc <= 2^24; pos0 >= 0.
+ * Workspace: csa_index_topk_ws_bytes with the call's sizes (the many-query path
+ * used for Tq >= 64 with bf16, HI = 8, dI = 128, topk <= 1024 keeps no score
+ * matrix; the per-query path holds Tq x Nc fp32 scores and lists).  Returns 0 on
+ * invalid sizes. */
+size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype);
 int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype,
                    int B, int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0,
                    int topk, int32_t* idx_out, int32_t* cnt_out,

@@ -47,8 +47,12 @@ def test_version_and_status_strings(b):
 
 def test_workspace_sizes_are_host_arithmetic(b):
     lib = b.lib
-    assert lib.csa_index_topk_ws_bytes(8, 1, 262144) > 8 * 262144 * 4
-    assert lib.csa_index_topk_ws_bytes(0, 1, 10) == 0
+    assert lib.csa_index_topk_ws_bytes(8, 1, 8, 128, 262144, 1024, 1) > 8 * 262144 * 4
+    assert lib.csa_index_topk_ws_bytes(0, 1, 8, 128, 10, 4, 0) == 0
+    # chunked prefill, 8192 queries x 65536 entries: the many-query path keeps no score matrix
+    assert lib.csa_index_topk_ws_bytes(1, 8192, 8, 128, 65536, 1024, 0) < 8192 * 65536 * 4 // 2
+    # the same queries in e4m3 take the per-query path, which holds the scores
+    assert lib.csa_index_topk_ws_bytes(1, 8192, 8, 128, 65536, 1024, 1) > 8192 * 65536 * 4
     assert lib.csa_sparse_attn_ws_bytes(8, 1, 128, 512, 1024, 128) > 0
     assert lib.hca_dense_attn_ws_bytes(1, 1, 16, 128, 32) == 0          # one split: no partials
     assert lib.csa_compress_ws_bytes(4, 65536, 4096, 4) == 4 * 16384 * 4096 * 2

@@ -179,6 +179,97 @@ def test_index_topk_deterministic(b):
 
 
 # ---------------------------------------------------------------------------
+# A7: the many-query (chunked prefill) indexer path: bf16, HI = 8, dI = 128,
+# Tq >= 64, topk <= 1024 (sampled threshold, MFMA contraction with candidate
+# lists, per-row select, exact fallback)
+# ---------------------------------------------------------------------------
+
+PREFILL_INDEX_CASES = [
+    # (B, Tq, L, pos0 or None (= L - Tq), topk)
+    (1, 200, 4 * 3000 + 1, None, 64),      # ragged query block and entry tail
+    (2, 64, 4 * 2500, None, 100),          # two sequences, one query block each
+    (1, 130, 4 * 9000, None, 1024),        # the largest k the path takes; several key splits
+    (1, 300, 4 * 3000, 4 * 400, 64),       # causal: visible counts 400..475 (few samples per row)
+    (1, 256, 4 * 3000, 100, 64),           # causal: the first rows see fewer than k entries
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_INDEX_CASES)
+def test_index_topk_many_queries_bit_exact(b, case):
+    B, Tq, L, pos0, topk = case
+    m, HI, dI = 4, 8, 128
+    Nc = -(-L // m)
+    pos0 = L - Tq if pos0 is None else pos0
+    q, w, k, _ = synth.indexer_inputs(300 + Tq, B, Tq, HI, dI, Nc, 0)
+    want_idx, want_cnt, _, _ = oracle.index_topk(q, w, k, L, m, pos0, topk)
+    got_idx, got_cnt = run_index(b, q, w, k, L, m, pos0, topk, 0)
+    assert np.array_equal(got_cnt, want_cnt)
+    bad = np.nonzero((got_idx != want_idx).any(axis=-1))
+    assert len(bad[0]) == 0, f"{len(bad[0])} rows differ, first {bad[0][:5]} {bad[1][:5]}"
+
+
+def test_index_topk_many_queries_planted(b):
+    B, Tq, HI, dI, m, topk = 1, 96, 8, 128, 4, 256
+    Nc = 6000
+    q, w, k, pl = synth.indexer_inputs(21, B, Tq, HI, dI, Nc, 0, planted=16)
+    want_idx, _, _, _ = oracle.index_topk(q, w, k, Nc * m, m, Nc * m - Tq, topk)
+    got_idx, _ = run_index(b, q, w, k, Nc * m, m, Nc * m - Tq, topk, 0)
+    assert np.array_equal(got_idx, want_idx)
+    assert set(pl[0]) <= set(got_idx[0, 0].tolist())
+
+
+def test_index_topk_many_queries_exact_ties(b):
+    # copies of a block of keys: exact ties around every row's k-th score (band ranking by index)
+    B, Tq, HI, dI, m, topk = 1, 64, 8, 128, 4, 64
+    Nc = 3000
+    q, w, k, _ = synth.indexer_inputs(22, B, Tq, HI, dI, Nc, 0)
+    k = k.copy()
+    k[:, 1000:1600] = k[:, 400:1000]
+    k[:, 2000:2600] = k[:, 400:1000]
+    want_idx, _, _, _ = oracle.index_topk(q, w, k, Nc * m, m, Nc * m - Tq, topk)
+    got_idx, _ = run_index(b, q, w, k, Nc * m, m, Nc * m - Tq, topk, 0)
+    assert np.array_equal(got_idx, want_idx)
+
+
+@pytest.mark.parametrize("Nc", [3000, 5000])
+def test_index_topk_many_queries_all_equal_scores(b, Nc):
+    # every score identical: the band holds every entry (3000) or the list overflows its capacity
+    # (5000); both rows go to the exact fallback, which keeps the lowest indices
+    B, Tq, HI, dI, m, topk = 1, 64, 8, 128, 4, 50
+    q, w, k, _ = synth.indexer_inputs(23, B, Tq, HI, dI, Nc, 0)
+    k = np.repeat(k[:, :1], Nc, axis=1)
+    got_idx, got_cnt = run_index(b, q, w, k, Nc * m, m, Nc * m - Tq, topk, 0)
+    assert (got_cnt == topk).all()
+    assert (got_idx == np.arange(topk)[None, None, :]).all()
+
+
+def test_index_topk_many_queries_prefill_size_sampled(b):
+    # the chunked-prefill workload: 8192 new queries at the end of a 262144-token context
+    # (65536 entries, k = 1024); sampled rows against the oracle, every row for its invariants
+    B, Tq, HI, dI, m, topk = 1, 8192, 8, 128, 4, 1024
+    L = 262144
+    Nc, pos0 = L // m, L - Tq
+    q, w, k, _ = synth.indexer_inputs(0, B, Tq, HI, dI, Nc, 0)
+    got_idx, got_cnt = run_index(b, q, w, k, L, m, pos0, topk, 0)
+    assert (got_cnt == topk).all()
+    assert (np.diff(got_idx[0], axis=-1) > 0).all()
+    nv = (pos0 + np.arange(Tq) + 1) // m
+    assert (got_idx[0].max(axis=-1) < nv).all()
+    rows = sorted(set([0, 1, 2, 31, 32, 4095, 4096, 8190, 8191] +
+                      list(np.random.default_rng(5).integers(0, Tq, 7))))
+    for t in rows:
+        want_idx, _, _, _ = oracle.index_topk(q[:, t:t + 1], w[:, t:t + 1], k, L, m, pos0 + t, topk)
+        assert np.array_equal(got_idx[:, t], want_idx[:, 0]), f"row {t}"
+
+
+def test_index_topk_many_queries_deterministic(b):
+    q, w, k, _ = synth.indexer_inputs(24, 1, 128, 8, 128, 8000, 0)
+    a1, _ = run_index(b, q, w, k, 32000, 4, 32000 - 128, 256, 0)
+    a2, _ = run_index(b, q, w, k, 32000, 4, 32000 - 128, 256, 0)
+    assert np.array_equal(a1, a2)
+
+
+# ---------------------------------------------------------------------------
 # A4: CSA sparse attention
 # ---------------------------------------------------------------------------
 
