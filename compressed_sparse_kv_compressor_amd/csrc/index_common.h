@@ -26,13 +26,68 @@ __device__ __forceinline__ int n_visible(long long p, long long L, int m, int Nc
 // Wave-cooperative exact score of entry s: HI head groups of LPH lanes, each
 // lane EPL elements; per head, fixed-point window accumulation (as in
 // exact_dot.h) reduced across the group, then the fma chain in head order.
+// Fast path: every product of two bf16 (e4m3) values has at most 16 (8) significant bits and is
+// exact in fp32 unless it underflows.  If the leading-bit exponents of a head's nonzero products
+// span at most 45 - MB bits (MB = 15 or 7 bits below the leading bit), every partial sum of at
+// most 2^7 of them is a multiple of the smallest product's last bit below 2^53 of it, so the fp64
+// sum in any order is exact and one conversion gives RN32 of the exact dot product.  Otherwise
+// (wide exponent span, or an fp32 product that underflows) the fixed-point window path below runs.
+template <int DT>
+__device__ __forceinline__ float raw_to_f32(const char* p, int i) {
+    if (DT == 0) return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+    const csa_exact::xv x = csa_exact::decode_e4m3(((const uint8_t*)p)[i]);
+    const float v = ldexpf((float)x.M, x.e);
+    return x.neg ? -v : v;
+}
+
 template <int DT, int DI, int HI>
 __device__ float wave_exact_score(const void* qrow, const float* wrow, const void* krow) {
     using namespace csa_exact;
     constexpr int LPH = 64 / HI, EPL = DI / LPH, ES = DT == 0 ? 2 : 1;
+    constexpr int MB = DT == 0 ? 15 : 7;
+    static_assert(DI <= 128, "fast-path sum bound assumes at most 2^7 products per head");
     const int lane = lane_id(), h = lane / LPH, sub = lane % LPH;
     const char* qp = (const char*)qrow + ((size_t)h * DI + sub * EPL) * ES;
     const char* kp = (const char*)krow + (size_t)sub * EPL * ES;
+    {
+        double s = 0.0;
+        int emin = 1000, emax = -1000, bad = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const float x = raw_to_f32<DT>(qp, i), y = raw_to_f32<DT>(kp, i);
+            const float pr = x * y;
+            const int e = (int)((__float_as_uint(pr) >> 23) & 0xffu);
+            if (x != 0.0f && y != 0.0f) {
+                bad |= e == 0 || e == 255;            // zero/subnormal product (maybe inexact) or overflow
+                emin = min(emin, e);
+                emax = max(emax, e);
+            }
+            s += (double)pr;
+        }
+#pragma unroll
+        for (int o = 1; o < LPH; o <<= 1) {
+            emin = min(emin, __shfl_xor(emin, o, 64));
+            emax = max(emax, __shfl_xor(emax, o, 64));
+            bad |= __shfl_xor(bad, o, 64);
+        }
+        const bool fast = !bad && emax - emin <= 45 - MB;     // uniform within a head's lanes
+        if (__builtin_amdgcn_ballot_w64(!fast) == 0ull) {      // every head fast (the common case)
+#pragma unroll
+            for (int o = 1; o < LPH; o <<= 1) {
+                const unsigned long long u = __double_as_longlong(s);
+                const int lo = __shfl_xor((int)(uint32_t)u, o, 64), hi = __shfl_xor((int)(uint32_t)(u >> 32), o, 64);
+                s += __longlong_as_double(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+            }
+            const float d = (float)s;
+            const float rr = d > 0.0f ? d : 0.0f;
+            float Sx = 0.0f;
+            for (int hh = 0; hh < HI; ++hh) {
+                const float rh = __shfl(rr, hh * LPH, 64);
+                Sx = __builtin_fmaf(wrow[hh], rh, Sx);
+            }
+            return Sx;
+        }
+    }
     uint32_t P[EPL];
     int ex[EPL];
     uint32_t ng[EPL];

@@ -14,7 +14,7 @@
 //   k_pscore<0> approximate scores S~ of every 16th entry only (MFMA, 1/16 of the work),
 //               stored as the top 16 bits of their order key
 //   k_pthresh   per row: thr = lower edge of the key bin of the j-th largest sampled
-//               S~ (j = k/8 + 16), i.e. about 2k + O(sqrt k) entries lie above it
+//               S~ (j = 3k/32 + 16), i.e. about 1.5k + 256 +- 16 sqrt(j) entries lie above it
 //   k_pscore<1> the dense contraction [queries x heads] x [entries] on MFMA with the
 //               ReLU-weighted head reduction fused; entries with S~ >= thr are
 //               appended to per-(row, key split) lists in ascending index order
@@ -38,6 +38,8 @@
 #include "index_common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace {
 
 using namespace csa;
@@ -45,20 +47,29 @@ using namespace csa;
 constexpr int P_HI = 8, P_DI = 128;           // indexer heads and dim served by this path
 constexpr int P_ROW_B = P_DI * 2;             // bytes per key row (bf16)
 constexpr int P_TK = 64;                      // entries per LDS tile
-constexpr int P_NA = 4;                       // 16-row MFMA blocks per wave (2 queries x 8 heads each)
-constexpr int P_QPW = 2 * P_NA;               // queries per wave
-constexpr int P_NW = 4;                       // waves per workgroup
+constexpr int P_NA = 2;                       // 32-row MFMA blocks per wave (4 queries x 8 heads each)
+constexpr int P_QPW = 4 * P_NA;               // queries per wave
+#ifndef CSA_PF_NW
+#define CSA_PF_NW 4
+#endif
+#ifndef CSA_PF_UNITS
+#define CSA_PF_UNITS 1024
+#endif
+#ifndef CSA_PF_NBUF
+#define CSA_PF_NBUF 4
+#endif
+constexpr int P_NBUF = CSA_PF_NBUF;           // LDS tile buffers (loads run P_NBUF - 1 tiles ahead)
+static_assert(P_NBUF >= 3 && P_NBUF <= 8, "tile buffers");
+constexpr int P_NW = CSA_PF_NW;               // waves per workgroup
 constexpr int P_QPG = P_QPW * P_NW;           // queries per workgroup
 constexpr int P_TPB = 64 * P_NW;
 constexpr int P_DMA = 16 / P_NW;              // 1 KiB tile loads per wave per tile
 constexpr int SAMPLE = 16;                    // the sampling pass scores entries 0, 16, 32, ...
 constexpr int MAX_SPLIT = 8;                  // key splits per query block
-constexpr int CAND_P = 4096;                  // list entries per row the select holds (in registers)
-constexpr int BAND_P = 256;                   // band entries ranked in LDS
-constexpr int SEL_TPB = 256, SEL_CPT = CAND_P / SEL_TPB;
+constexpr int CAND_P = 4096;                  // list capacity scale (per-split capacities derive from it)
 constexpr int FB_TPB = 1024, FB_SLOTS = 64;
 
-__device__ __forceinline__ int sample_rank(int topk) { return topk / 8 + 16; }
+__device__ __forceinline__ int sample_rank(int topk) { return topk * 3 / 32 + 16; }
 
 // Raw buffer resource (stride 0, byte offsets) over [base, base + bytes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -76,61 +87,97 @@ __device__ __forceinline__ float round_up_f32(double x) {
 }
 
 // ---------------------------------------------------------------------------
-// k_pnorm: Kmax per sequence (atomic max of non-negative float bits) and Wq per row
+// k_pnorm: Kmax per sequence (atomic max of non-negative float bits) and Wq per row.
+// Key blocks: 16 lanes per key (16 bytes each), four keys per wave at a time.  Row
+// blocks: one wave per row, 8 lanes per head.  Squares and sums in fp64 (each square
+// of a bf16 is exact); the results are rounded up to fp32.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ double sumsq8(u32x4_t x) {
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const double lo = (double)__uint_as_float(x[j] << 16), hi = (double)__uint_as_float(x[j] & 0xffff0000u);
+        s = fma(lo, lo, s);
+        s = fma(hi, hi, s);
+    }
+    return s;
+}
+__device__ __forceinline__ double shfl_xor_d(double v, int o) {
+    const unsigned long long u = __double_as_longlong(v);
+    const int lo = __shfl_xor((int)(uint32_t)u, o, 64), hi = __shfl_xor((int)(uint32_t)(u >> 32), o, 64);
+    return __longlong_as_double(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+constexpr int NORM_KEYS_PER_BLOCK = 64;     // 4 waves x 4 keys x 4 rounds
+
 __global__ __launch_bounds__(256) void k_pnorm(const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
                                                 const uint16_t* __restrict__ k_idx, int B, int Nc, int R,
                                                 float* __restrict__ wq, uint32_t* __restrict__ kmax)
 {
-    const long long nk = (long long)B * Nc, kblocks = (nk + 255) / 256;
-    const long long i = (long long)blockIdx.x < kblocks ? (long long)blockIdx.x * 256 + threadIdx.x
-                                                         : nk + ((long long)blockIdx.x - kblocks) * 256 + threadIdx.x;
-    auto norm = [](const uint16_t* v) -> double {   // ||v||_2 of P_DI bf16, rounded up a little
-        double s = 0.0;
-        for (int e = 0; e < P_DI; e += 8) {
-            const u32x4_t x = *(const u32x4_t*)(v + e);
+    const long long nk = (long long)B * Nc;
+    const long long kblocks = (nk + NORM_KEYS_PER_BLOCK - 1) / NORM_KEYS_PER_BLOCK;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    if ((long long)blockIdx.x < kblocks) {
+        __shared__ uint32_t wmax[4];
+        const long long k0 = (long long)blockIdx.x * NORM_KEYS_PER_BLOCK;
+        const long long k1 = min(nk, k0 + NORM_KEYS_PER_BLOCK) - 1;
+        const bool one_seq = k0 / Nc == k1 / Nc;        // uniform: the block's keys share a sequence
+        uint32_t mx = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const double lo = (double)__uint_as_float(x[j] << 16), hi = (double)__uint_as_float(x[j] & 0xffff0000u);
-                s = fma(lo, lo, s);
-                s = fma(hi, hi, s);
+        for (int rd = 0; rd < 4; ++rd) {
+            const long long key = k0 + rd * 16 + wave * 4 + (lane >> 4);
+            double ss = 0.0;
+            if (key < nk) ss = sumsq8(*(const u32x4_t*)(k_idx + (size_t)key * P_DI + 8 * (lane & 15)));
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) ss += shfl_xor_d(ss, o);
+            if (key < nk) {
+                const uint32_t f = __float_as_uint(round_up_f32(sqrt(ss) * (1.0 + 1.0e-12)));
+                if (one_seq) mx = max(mx, f);
+                else if ((lane & 15) == 0) atomicMax(&kmax[(int)(key / Nc)], f);
             }
         }
-        return sqrt(s) * (1.0 + 1.0e-12);
-    };
-    if (i < nk) {
-        const uint32_t f = __float_as_uint(round_up_f32(norm(k_idx + (size_t)i * P_DI)));
-        const int bi = (int)(i / Nc);
-        if (__all(bi == __shfl(bi, 0, 64))) {          // one sequence in this wave: one atomic
-            uint32_t u = f;
+        if (one_seq) {                                  // one atomic per block
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) u = max(u, (uint32_t)__shfl_xor((int)u, o, 64));
-            if ((threadIdx.x & 63) == 0) atomicMax(&kmax[bi], u);
-        } else {
-            atomicMax(&kmax[bi], f);
+            for (int o = 16; o < 64; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+            if (lane == 0) wmax[wave] = mx;
+            __syncthreads();
+            if (threadIdx.x == 0)
+                atomicMax(&kmax[(int)(k0 / Nc)], max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
         }
-    } else if (i >= nk && i < nk + R) {
-        const size_t r = (size_t)(i - nk);
-        double s = 0.0;
-        for (int h = 0; h < P_HI; ++h) s += fabs((double)w_idx[r * P_HI + h]) * norm(q_idx + (r * P_HI + h) * P_DI);
-        wq[r] = round_up_f32(s * (1.0 + 1.0e-12));
+    } else {
+        const long long r = ((long long)blockIdx.x - kblocks) * 4 + wave;
+        if (r >= R) return;
+        const int h = lane >> 3, part = lane & 7;     // 8 lanes per head, 16 elements each
+        const uint16_t* qp = q_idx + ((size_t)r * P_HI + h) * P_DI + 16 * part;
+        double ss = sumsq8(*(const u32x4_t*)qp) + sumsq8(*(const u32x4_t*)(qp + 8));
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) ss += shfl_xor_d(ss, o);
+        double t = fabs((double)w_idx[(size_t)r * P_HI + h]) * (sqrt(ss) * (1.0 + 1.0e-12));
+#pragma unroll
+        for (int o = 8; o < 64; o <<= 1) t += shfl_xor_d(t, o);
+        if (lane == 0) wq[r] = round_up_f32(t * (1.0 + 1.0e-12));
     }
 }
 
 // ---------------------------------------------------------------------------
 // k_pscore: the contraction.  A workgroup owns P_QPG queries and one key split;
-// wave w owns queries q0 + 8w .. +7 as P_NA A blocks (16 rows = 2 queries x 8 heads,
-// row = 8 query + head) held in registers for the whole sweep.  Key tiles of 64
-// entries stream through four LDS buffers by buffer-load DMA (issued three tiles
-// ahead); per 16-entry sub-tile and block: 4 v_mfma_f32_16x16x32_bf16.
-// Element order of the contraction: k-step s, lane group g takes the 16-byte
-// chunk 4s + g of a row (the same for Q and K).  LDS rows are 256 B with chunk c
-// of row r stored at chunk c ^ (r & 15): the 16 rows one read instruction touches
-// at one chunk fall on 16 distinct 16-byte bank groups.
-// Epilogue per pair of blocks: D lane (g, c) holds rows 4g..4g+3 = heads 4(g&1)..+3
-// of query 2a + g/2 at key c; the 4-term w-weighted ReLU sums of two blocks are
-// combined by one v_permlane16_swap, after which lane row g holds the full S~ of
-// query 4p + 2(g & 1) + (g >> 1) at key c.
+// wave w owns queries qw = q0 + 8w .. +7 as P_NA A blocks of 32 rows (4 queries x
+// 8 heads, row = 8 query + head) held in registers for the whole sweep.  Key tiles
+// of 64 entries stream through four LDS buffers by buffer-load DMA (issued three
+// tiles ahead); per 32-entry sub-tile and block: 8 v_mfma_f32_32x32x16_bf16.
+// The 32x32x16 shape leaves the most VALU issue room beside the matrix pipe
+// (about six VALU instructions per MFMA at no cost), which the fused epilogue needs.
+// Element order of the contraction: k-step s, lane half g2 takes the 16-byte chunk
+// 2s + g2 of a row (the same for Q and K).  LDS rows are 256 B with chunk c of row r
+// stored at chunk c ^ (r & 15): the rows one read instruction touches at one chunk
+// fall on distinct 16-byte bank groups.
+// Epilogue: D lane (g2, c) register r holds row 8 (r/4) + 4 g2 + r%4, i.e. head
+// 4 g2 + r%4 of query r/4 at key c.  Four-term w-weighted ReLU sums per query, then
+// one v_permlane32_swap per query pair adds the two head halves: lane half g2 holds
+// S~ of query 2 g2 (first register) and 2 g2 + 1 (second).  After the two sub-tiles
+// of a tile one more permlane32 swap per register pair leaves one register per
+// query with its 64 keys in lane order, so that the threshold, the count and the
+// list offset of every store are wave-uniform.
 // MODE 0: sample indices (key 16 i) and the top 16 key bits of S~ stored per row.
 // MODE 1: entries; S~ >= thr (and visible) appended to the row's list of this split.
 // ---------------------------------------------------------------------------
@@ -152,13 +199,12 @@ struct PScoreArgs {
 };
 
 template <int MODE>
-__device__ __forceinline__ void pscore_body(uint16_t* bufA, uint16_t* bufB, uint16_t* bufC, uint16_t* bufD,
-                                            const PScoreArgs& A)
+__device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], const PScoreArgs& A)
 {
     const int bid = blockIdx.x;
     const int qb = bid % A.nqb, rest = bid / A.nqb, split = rest % A.nsplit, b = rest / A.nsplit;
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = lane >> 4, c = lane & 15;
+    const int r32 = lane & 31, g2 = lane >> 5;
     const int Tq = A.Tq, Nc = A.Nc;
     const int q0 = qb * P_QPG, qw = q0 + w * P_QPW;
     const int NKS = MODE == 0 ? (Nc + SAMPLE - 1) / SAMPLE : Nc;     // key space of this mode
@@ -170,43 +216,55 @@ __device__ __forceinline__ void pscore_body(uint16_t* bufA, uint16_t* bufB, uint
     int ntiles = ke > kb ? (ke - kb + P_TK - 1) / P_TK : 0;
     if (MODE == 1 && nvl <= A.topk) ntiles = 0;                       // no row of the block selects
 
-    // ---- A operands and head weights ----
-    bf16x8_t qa[P_NA][4];
-    float wv[P_NA][4];
+    // ---- A operands (rows 8 j + h of block a = head h of query qw + 4a + j) and head weights ----
+    bf16x8_t qa[P_NA][8];
+    float wv[P_NA][16];                       // register r of block a: query qw + 4a + r/4, head 4 g2 + r%4
 #pragma unroll
     for (int a = 0; a < P_NA; ++a) {
-        const int t = qw + 2 * a + (c >> 3), h = c & 7;
+        const int t = qw + 4 * a + (r32 >> 3), h = r32 & 7;
         const bool v = t < Tq;
-        const uint16_t* qp = A.q_idx + (((size_t)b * Tq + (v ? t : 0)) * P_HI + h) * P_DI + 8 * g;
+        const uint16_t* qp = A.q_idx + (((size_t)b * Tq + (v ? t : 0)) * P_HI + h) * P_DI + 8 * g2;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            qa[a][s] = as_bf16x8(v ? *(const u32x4_t*)(qp + 32 * s) : u32x4_t{0u, 0u, 0u, 0u});
-        const int tw = qw + 2 * a + (g >> 1);
+        for (int s = 0; s < 8; ++s)
+            qa[a][s] = as_bf16x8(v ? *(const u32x4_t*)(qp + 16 * s) : u32x4_t{0u, 0u, 0u, 0u});
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            wv[a][r] = tw < Tq ? A.w_idx[((size_t)b * Tq + tw) * P_HI + 4 * (g & 1) + r] : 0.f;
-    }
-    // ---- per-lane output rows: pair p holds query qw + 4p + 2(g & 1) + (g >> 1) ----
-    int rowt[2];
-    float thr_l[2];
-    int nv_l[2];
-    uint32_t cn[2] = {0u, 0u};
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int t = qw + 4 * p + 2 * (g & 1) + (g >> 1);
-        rowt[p] = t;
-        thr_l[p] = INFINITY;
-        nv_l[p] = 0;
-        if (MODE == 1 && t < Tq) {
-            thr_l[p] = A.thr[(size_t)b * Tq + t];
-            nv_l[p] = n_visible(A.pos0 + t, A.L, A.m, Nc);
+        for (int r = 0; r < 16; ++r) {
+            const int tw = qw + 4 * a + r / 4;
+            wv[a][r] = tw < Tq ? A.w_idx[((size_t)b * Tq + tw) * P_HI + 4 * g2 + r % 4] : 0.f;
         }
     }
-    const uint32_t below = (1u << c) - 1u;
-    uint2* crow[2];                           // this split's list of the lane's rows (MODE 1)
+    // ---- per-query state (wave-uniform): local query lq = 0..7 is query qw + lq ----
+    float thr_q[P_QPW];
+    int nv_q[P_QPW];
+    uint32_t C[P_QPW];                        // list entries so far (MODE 1)
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-        crow[p] = A.cand + (((size_t)b * Tq + min(rowt[p], Tq - 1)) * A.nsplit + split) * A.caps;
+    for (int lq = 0; lq < P_QPW; ++lq) {
+        const int t = qw + lq;
+        thr_q[lq] = INFINITY;
+        nv_q[lq] = 0;
+        C[lq] = 0u;
+        if (MODE == 1 && t < Tq) {
+            thr_q[lq] = A.thr[(size_t)b * Tq + t];
+            nv_q[lq] = n_visible(A.pos0 + t, A.L, A.m, Nc);
+        }
+    }
+    // list stores go through a buffer resource over this workgroup's rows of this split; a
+    // non-candidate lane stores at an offset past its end, which the hardware drops (no branch).
+    // (the pieces go through readfirstlane so that the resource is built in scalar registers)
+    const int nrow_wg = max(0, min(P_QPG, Tq - q0));
+    const uint32_t seg_bytes = (uint32_t)A.caps * 8u;
+    const uint64_t cbase = MODE == 1 ? (uint64_t)(A.cand + (((size_t)b * Tq + q0) * A.nsplit + split) * A.caps) : 0u;
+    const uint32_t cb_lo = __builtin_amdgcn_readfirstlane((uint32_t)cbase);
+    const uint32_t cb_hi = __builtin_amdgcn_readfirstlane((uint32_t)(cbase >> 32));
+    const uint32_t cb_n = __builtin_amdgcn_readfirstlane(MODE == 1 ? (uint32_t)nrow_wg * (uint32_t)A.nsplit * seg_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const void*)(((uint64_t)cb_hi << 32) | cb_lo), cb_n);
+    const uint32_t drop = __builtin_amdgcn_readfirstlane(0x80000000u | cb_n);   // an offset past the resource
+    // MODE 0: the sample rows of this workgroup, same scheme
+    const uint64_t sbase64 = MODE == 0 ? (uint64_t)(A.samp + ((size_t)b * Tq + q0) * A.NSP) : 0u;
+    const uint32_t sb_lo = __builtin_amdgcn_readfirstlane((uint32_t)sbase64);
+    const uint32_t sb_hi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase64 >> 32));
+    const uint32_t sb_n = __builtin_amdgcn_readfirstlane(MODE == 0 ? (uint32_t)nrow_wg * (uint32_t)A.NSP * 2u : 0u);
+    const __amdgpu_buffer_rsrc_t rsmp = make_rsrc((const void*)(((uint64_t)sb_hi << 32) | sb_lo), sb_n);
 
     // ---- tile loads: instruction i of wave w covers tile rows 4 (w + P_NW i) .. +3 ----
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(A.k_idx + (size_t)b * Nc * P_DI, (uint32_t)((size_t)Nc * P_ROW_B));
@@ -225,114 +283,188 @@ __device__ __forceinline__ void pscore_body(uint16_t* bufA, uint16_t* bufB, uint
                                                      (int)voff, 0, 0, 0);
         }
     };
-    // this lane's B read at k-step s of sub-tile j: (boff ^ 64 s) + 4096 j
-    const uint32_t boff = (uint32_t)c * P_ROW_B + 64u * (uint32_t)(c >> 2) + 16u * (uint32_t)(g ^ (c & 3));
+    // this lane's B read at k-step s of sub-tile j: (boff ^ 32 s) + 8192 j (key 32 j + r32, chunk 2 s + g2)
+    const uint32_t boff = (uint32_t)r32 * P_ROW_B + 32u * (uint32_t)((r32 & 15) >> 1) + 16u * (uint32_t)(g2 ^ (r32 & 1));
 
-    auto epilogue = [&](const f32x4_t (&acc)[P_NA], int kk) {
+    // ReLU as a signed-integer max on the bit pattern (negative floats, -0 included, are negative
+    // integers): one VALU op, with no NaN canonicalisation
+    auto relu = [](float x) { return __int_as_float(max(__float_as_int(x), 0)); };
+    // S~ of one block: va = query 4a (lanes 0-31) / 4a + 2 (lanes 32-63), vb = 4a + 1 / 4a + 3, at key r32
+    auto block_scores = [&](const f32x16_t& acc, const float (&wb)[16], float& va, float& vb) {
+        float p[4];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            // ReLU as a signed-integer max on the bit pattern (negative floats, -0 included, are negative
-            // integers): one VALU op, with no NaN canonicalisation
-            auto relu = [](float x) { return __int_as_float(max(__float_as_int(x), 0)); };
-            float x0 = 0.f, x1 = 0.f;
+        for (int j = 0; j < 4; ++j) {
+            float x = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                x0 = fmaf(wv[2 * p][r], relu(acc[2 * p][r]), x0);
-                x1 = fmaf(wv[2 * p + 1][r], relu(acc[2 * p + 1][r]), x1);
-            }
-            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
-            const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if constexpr (MODE == 0) {
-                if (rowt[p] < Tq)
-                    A.samp[((size_t)b * Tq + rowt[p]) * A.NSP + kk] = (uint16_t)(f32_key(v) >> 16);
-            } else {
-                const bool cd = kk < nv_l[p] && v >= thr_l[p];
-                const unsigned long long mask = __builtin_amdgcn_ballot_w64(cd);
-                const uint32_t seg = (uint32_t)(mask >> (16 * g)) & 0xffffu;
-                // past the capacity the last slot is overwritten: the count then exceeds it and the
-                // select hands the row to the exact path
-                const uint32_t pos = min(cn[p] + __popc(seg & below), (uint32_t)A.caps - 1u);
-                if (cd) crow[p][pos] = make_uint2((uint32_t)kk, __float_as_uint(v));
-                cn[p] += __popc(seg);
-            }
+            for (int i = 0; i < 4; ++i) x = fmaf(wb[4 * j + i], relu(acc[4 * j + i]), x);
+            p[j] = x;
+        }
+        const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+        va = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+        vb = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+    };
+    // one query's 64 keys (lane = key - kbase): sample store or list append
+    auto emit = [&](float v, int lq, int kk, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;     // every key of the tile visible to every query
+        if constexpr (MODE == 0) {
+            // every lane stores (a missing row's offset lies past the resource): the number of memory
+            // operations per tile is fixed, which the tile wait below counts on
+            const uint32_t off = qw + lq < Tq ? ((uint32_t)(w * P_QPW + lq) * (uint32_t)A.NSP + (uint32_t)kk) * 2u
+                                              : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(f32_key(v) >> 16), rsmp, (int)off, 0, 0);
+        } else {
+            const bool cd = FULL ? v >= thr_q[lq] : (kk < nv_q[lq] && v >= thr_q[lq]);
+            const unsigned long long mask = __builtin_amdgcn_ballot_w64(cd);
+            // slot base of this query's stores (scalar); once fewer than 64 slots remain the stores
+            // go to the last 64 (the count then exceeds caps - 64 and the select hands the row to the
+            // exact path)
+            const uint32_t sbase = (uint32_t)((w * P_QPW + lq) * A.nsplit) * seg_bytes +
+                                   8u * min(C[lq], (uint32_t)A.caps - 64u);
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+            // (the select is written as one v_cndmask on the ballot so that the compiler does not turn it
+            // into an exec-masked branch, which would blur its count of memory operations per step)
+            uint32_t off;
+            asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(off) : "v"(drop), "v"(sbase + 8u * rank), "s"(mask));
+            typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{(uint32_t)kk, __float_as_uint(v)}, rc, (int)off, 0, 0);
+            C[lq] += (uint32_t)__popcll(mask);
+        }
+    };
+    auto tile_out = [&](const float (&VA)[P_NA][2], const float (&VB)[P_NA][2], int tile, auto full_tag) {
+        const int kk = kb + tile * P_TK + lane;
+#pragma unroll
+        for (int a = 0; a < P_NA; ++a) {
+            const auto tA = __builtin_amdgcn_permlane32_swap(__float_as_uint(VA[a][0]), __float_as_uint(VA[a][1]), false, false);
+            const auto tB = __builtin_amdgcn_permlane32_swap(__float_as_uint(VB[a][0]), __float_as_uint(VB[a][1]), false, false);
+            emit(__uint_as_float(tA[0]), 4 * a + 0, kk, full_tag);
+            emit(__uint_as_float(tB[0]), 4 * a + 1, kk, full_tag);
+            emit(__uint_as_float(tA[1]), 4 * a + 2, kk, full_tag);
+            emit(__uint_as_float(tB[1]), 4 * a + 3, kk, full_tag);
         }
     };
     auto compute = [&](const uint16_t* buf, int tile) {
         const CSA_LDS char* lb = (const CSA_LDS char*)buf;
-        const int k0 = kb + tile * P_TK + c;
+        float VA[P_NA][2], VB[P_NA][2];
+        // all B fragments of the tile are read up front (16 reads in flight): the MFMAs of the first
+        // sub-tile wait for the first eight only, and LDS latency is paid once per tile
+        u32x4_t bt[P_TK / 32][8];
 #pragma unroll
-        for (int j = 0; j < P_TK / 16; ++j) {
-            u32x4_t bv[4];
+        for (int j = 0; j < P_TK / 32; ++j)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) bv[s] = *(const CSA_LDS u32x4_t*)(lb + ((boff ^ (64u * s)) + 4096u * j));
-            f32x4_t acc[P_NA];
+            for (int s = 0; s < 8; ++s) bt[j][s] = *(const CSA_LDS u32x4_t*)(lb + ((boff ^ (32u * s)) + 8192u * j));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int a = 0; a < P_NA; ++a) acc[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < P_TK / 32; ++j) {
+            const u32x4_t (&bv)[8] = bt[j];
+            f32x16_t acc[P_NA];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int a = 0; a < P_NA; ++a)
 #pragma unroll
-                for (int a = 0; a < P_NA; ++a) acc[a] = mfma16_bf16(qa[a][s], as_bf16x8(bv[s]), acc[a]);
-            epilogue(acc, k0 + 16 * j);
+                for (int r = 0; r < 16; ++r) acc[a][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int a = 0; a < P_NA; ++a) acc[a] = mfma32_bf16(qa[a][s], as_bf16x8(bv[s]), acc[a]);
+#pragma unroll
+            for (int a = 0; a < P_NA; ++a) block_scores(acc[a], wv[a], VA[a][j], VB[a][j]);
         }
+        // (one code path: a branch between variants would leave the compiler unsure of the number of
+        // stores per step, and it would then add waits of its own before the tile reads)
+        tile_out(VA, VB, tile, std::false_type{});
     };
 
-    // ---- the tile pipeline: tile t in buffer t % 4, loads issued three tiles ahead ----
-    // Before the barrier of tile t each wave waits for its own loads of tile t; at least the
-    // loads of tiles t+1 and t+2 were issued after them (candidate stores in between only make
-    // the wait longer), hence vmcnt(2 P_DMA).  After the barrier buffer (t+3) % 4 = (t-1) % 4 is
-    // free everywhere; it takes tile t+3 once tile t is done.  Loads past the last tile reread
-    // clamped rows, so every step issues the same number of loads.
+    // ---- the tile pipeline: tile t in buffer t % NB, loads issued NB - 1 tiles ahead ----
+    // Vector memory operations complete in issue order as far as vmcnt is concerned.  Step t
+    // waits, passes the barrier, issues exactly P_DMA loads (tile t+NB-1, into buffer (t-1) % NB,
+    // which every wave has finished reading once it is past this barrier) and then exactly P_QPW
+    // stores (tile t's scores), with no branch around them.  Before the barrier of tile t each wave
+    // waits for its own loads of tile t: issued after them are the loads of tiles t+1 .. t+NB-2 and
+    // the stores of the min(t, NB-1) steps before, hence vmcnt((NB-2) P_DMA + min(t, NB-1) P_QPW).
+    // Loads past the last tile reread clamped rows.
+    constexpr int NB = P_NBUF;
+    static_assert((NB - 2) * P_DMA + (NB - 1) * P_QPW < 64, "vmcnt field");
+    auto wait_tile = [&](int t) {
+        switch (min(t, NB - 1)) {
+#define CSA_PWAIT(I) case I: if constexpr (I < NB) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 2) * P_DMA + I * P_QPW)); break;
+            CSA_PWAIT(0) CSA_PWAIT(1) CSA_PWAIT(2) CSA_PWAIT(3) CSA_PWAIT(4) CSA_PWAIT(5) CSA_PWAIT(6) CSA_PWAIT(7)
+#undef CSA_PWAIT
+        }
+    };
+    auto step = [&](auto kc, int t) {
+        constexpr int K = decltype(kc)::value;
+        wait_tile(t + K);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(bufs[(K + NB - 1) % NB], t + K + NB - 1);
+        compute(bufs[K], t + K);
+    };
     if (ntiles > 0) {
-        issue(bufA, 0);
-        issue(bufB, 1);
-        issue(bufC, 2);
-        for (int t = 0; t < ntiles; t += 4) {
-#define CSA_PSTEP(CUR, K, NXT)                                         \
-            {                                                          \
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * P_DMA));      \
-                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
-                compute(CUR, t + K);                                   \
-                issue(NXT, t + K + 3);                                 \
-            }
-            CSA_PSTEP(bufA, 0, bufD)
-            if (t + 1 >= ntiles) break;
-            CSA_PSTEP(bufB, 1, bufA)
-            if (t + 2 >= ntiles) break;
-            CSA_PSTEP(bufC, 2, bufB)
-            if (t + 3 >= ntiles) break;
-            CSA_PSTEP(bufD, 3, bufC)
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i) issue(bufs[i], i);
+        for (int t = 0; t < ntiles; t += NB) {
+#define CSA_PSTEP(K) if constexpr (K < NB) { if (t + K >= ntiles) break; step(std::integral_constant<int, K>{}, t); }
+            CSA_PSTEP(0) CSA_PSTEP(1) CSA_PSTEP(2) CSA_PSTEP(3) CSA_PSTEP(4) CSA_PSTEP(5) CSA_PSTEP(6) CSA_PSTEP(7)
 #undef CSA_PSTEP
         }
         __builtin_amdgcn_s_waitcnt(0);        // no tile load may still target this workgroup's LDS
     }
     if constexpr (MODE == 1) {
-        if (c == 0) {
+        if (lane < P_QPW) {
+            uint32_t cv = 0;
 #pragma unroll
-            for (int p = 0; p < 2; ++p)
-                if (rowt[p] < Tq) A.cnt[((size_t)b * Tq + rowt[p]) * A.nsplit + split] = cn[p];
+            for (int lq = 0; lq < P_QPW; ++lq) cv = lane == lq ? C[lq] : cv;
+            if (qw + lane < Tq) A.cnt[((size_t)b * Tq + qw + lane) * A.nsplit + split] = cv;
         }
     }
 }
 
-// Four tile buffers (distinct objects: the compiler tells a read of one from the loads in
+// P_NBUF tile buffers (distinct objects: the compiler tells a read of one from the loads in
 // flight into another).
 template <int MODE>
-__global__ __launch_bounds__(P_TPB, 2) void k_pscore(PScoreArgs A)
+__global__ __launch_bounds__(P_TPB, 8 / P_NW) void k_pscore(PScoreArgs A)
 {
-    __shared__ __attribute__((aligned(1024))) uint16_t bufA[P_TK * P_DI];
-    __shared__ __attribute__((aligned(1024))) uint16_t bufB[P_TK * P_DI];
-    __shared__ __attribute__((aligned(1024))) uint16_t bufC[P_TK * P_DI];
-    __shared__ __attribute__((aligned(1024))) uint16_t bufD[P_TK * P_DI];
-    pscore_body<MODE>(bufA, bufB, bufC, bufD, A);
+#define CSA_PBUF(I) __shared__ __attribute__((aligned(1024))) uint16_t buf##I[I < P_NBUF ? P_TK * P_DI : 1];
+    CSA_PBUF(0) CSA_PBUF(1) CSA_PBUF(2) CSA_PBUF(3) CSA_PBUF(4) CSA_PBUF(5) CSA_PBUF(6) CSA_PBUF(7)
+#undef CSA_PBUF
+    uint16_t* const all[8] = {buf0, buf1, buf2, buf3, buf4, buf5, buf6, buf7};
+    uint16_t* bufs[P_NBUF];
+#pragma unroll
+    for (int i = 0; i < P_NBUF; ++i) bufs[i] = all[i];
+    pscore_body<MODE>(bufs, A);
 }
 
 // ---------------------------------------------------------------------------
-// k_pthresh: one wave per row; 16-bit radix select of the j-th largest sample key
+// k_pthresh: one wave per row.  The j-th largest sample key (16 bits) by a radix
+// select over bins of the key range present in the row (min .. max), so that the
+// few values most samples share do not pile their LDS atomics onto one bin.
 // ---------------------------------------------------------------------------
+// wave: the bin (of 1024, counted from the top) holding the need-th largest; out = {bin, count above}
+__device__ void wave_find_bin1024(const uint32_t* h, uint32_t need, uint32_t* out) {
+    const int lane = lane_id();
+    uint32_t s = 0;                                    // lane L covers bins 1023 - 16 L down to 1008 - 16 L
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += h[1023 - 16 * lane - i];
+    uint32_t incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    uint32_t acc = incl - s;
+    if (acc < need && need <= incl) {
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t c = h[1023 - 16 * lane - i];
+            if (acc + c >= need) { out[0] = 1023 - 16 * lane - i; out[1] = acc; break; }
+            acc += c;
+        }
+    }
+}
+
 __global__ __launch_bounds__(64) void k_pthresh(const uint16_t* __restrict__ samp, int NSP, int Tq, int Nc, long long L,
                                                  int m, long long pos0, int topk, float* __restrict__ thr)
 {
-    __shared__ uint32_t h[256];
+    __shared__ uint32_t h[1024];
     __shared__ uint32_t res[2];
     const int r = blockIdx.x, t = r % Tq, lane = lane_id();
     const int nv = n_visible(pos0 + t, L, m, Nc);
@@ -345,166 +477,259 @@ __global__ __launch_bounds__(64) void k_pthresh(const uint16_t* __restrict__ sam
         if (lane == 0) thr[r] = -INFINITY;
         return;
     }
-    const uint16_t* sp = samp + (size_t)r * NSP;
-    for (int i = lane; i < 256; i += 64) h[i] = 0;
-    __syncthreads();
-    for (int i = lane; i < ns; i += 64) atomicAdd(&h[sp[i] >> 8], 1u);
-    __syncthreads();
-    wave_find_bin256(h, (uint32_t)j, 0u, res);
-    __syncthreads();
-    const uint32_t b1 = res[0], a1 = res[1];
-    __syncthreads();
-    for (int i = lane; i < 256; i += 64) h[i] = 0;
-    __syncthreads();
-    for (int i = lane; i < ns; i += 64) {
-        const uint32_t v = sp[i];
-        if ((v >> 8) == b1) atomicAdd(&h[v & 255u], 1u);
+    const uint16_t* sp = samp + (size_t)r * NSP;      // rows are 128-byte aligned (NSP % 64 == 0)
+    const int nvec = (ns + 7) / 8;
+    // visit every sample (8 per 16-byte load), f(x)
+    // (chunks of 8 loads per lane, all issued before any is used)
+    auto for_samples = [&](auto f) {
+        for (int c0 = 0; c0 < nvec; c0 += 512) {
+            u32x4_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {             // unconditional (clamped) loads: all in flight at once
+                const int i = c0 + 64 * u + lane;
+                v[u] = *(const u32x4_t*)(sp + 8 * min(i, nvec - 1));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = c0 + 64 * u + lane;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (8 * i + e < ns) f((v[u][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            }
+        }
+    };
+    uint32_t mn = 0xffffu, mx = 0u;
+    for_samples([&](uint32_t x) { mn = min(mn, x); mx = max(mx, x); });
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
     }
-    __syncthreads();
-    wave_find_bin256(h, (uint32_t)j - a1, 0u, res);
-    __syncthreads();
-    if (lane == 0) thr[r] = key_f32(((b1 << 8) | res[0]) << 16);
+    uint32_t base = mn, need = (uint32_t)j;
+    int shift = max(0, 32 - (int)__clz((int)(mx - mn)) - 10), pshift = 32;
+    for (;;) {
+        for (int i = lane; i < 1024; i += 64) h[i] = 0;
+        __syncthreads();
+        for_samples([&](uint32_t x) {
+            const uint32_t d = x - base;               // wraps for x < base: outside the range
+            if (pshift >= 32 || d < (1u << pshift)) atomicAdd(&h[d >> shift], 1u);
+        });
+        __syncthreads();
+        wave_find_bin1024(h, need, res);
+        __syncthreads();
+        base += res[0] << shift;
+        need -= res[1];
+        if (shift == 0) break;
+        pshift = shift;
+        shift = max(0, shift - 10);
+        __syncthreads();
+    }
+    if (lane == 0) thr[r] = key_f32(base << 16);
 }
 
 // ---------------------------------------------------------------------------
-// k_pselect: one 256-thread workgroup per row; thread i holds list positions
-// 16 i .. 16 i + 15 (the list is in ascending index order across the splits)
+// k_pselect: one wave per row (SW_ROWS rows per workgroup, no workgroup barrier).
+// The row's list segments are read in 64-entry slots: slot k of the wave holds, in
+// lane L, entry 64 (k - first slot of its segment) + L of that segment, so that slot
+// order and lane order follow the ascending index order (a segment's last slot is
+// partly empty).  Keys and indices stay in registers; every step is wave-level.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(SEL_TPB) void k_pselect(
+constexpr int SW_SLOTS = 48;                  // 64-entry slots per row (3072 list entries minus padding)
+constexpr int SW_BAND = 128;                  // band entries per row ranked in LDS
+constexpr int SW_ROWS = 4;                    // rows (waves) per workgroup
+
+// order-preserving LDS code motion fence within a wave (the LDS executes a wave's operations in order)
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     const uint2* __restrict__ cand, const uint32_t* __restrict__ cnt, const float* __restrict__ thr,
     const float* __restrict__ wq, const uint32_t* __restrict__ kmax, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, int Tq, int Nc, long long L, int m,
-    long long pos0, int topk, int nsplit, int caps, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
+    long long pos0, int topk, int nsplit, int caps, int R, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
     uint32_t* __restrict__ fail)
 {
-    __shared__ uint32_t spre[MAX_SPLIT + 1];
-    __shared__ uint32_t hist[256], res[4], scratch[SEL_TPB / 64], nband, bad;
-    __shared__ unsigned long long bkey[BAND_P];
-    __shared__ uint32_t bpos[BAND_P], bidx[BAND_P];
-    __shared__ uint32_t chosen[CAND_P / 32];
-    const int r = blockIdx.x, b = r / Tq, t = r % Tq, tid = threadIdx.x;
-    const int lane = lane_id(), wave = tid >> 6;
+    __shared__ uint32_t hist_all[SW_ROWS][1024];
+    __shared__ uint32_t res_all[SW_ROWS][2];
+    __shared__ unsigned long long bkey_all[SW_ROWS][SW_BAND];
+    __shared__ uint32_t bpos_all[SW_ROWS][SW_BAND], bidx_all[SW_ROWS][SW_BAND];
+    __shared__ unsigned long long chosen_all[SW_ROWS][SW_SLOTS];
+    const int wv = threadIdx.x >> 6, lane = lane_id();
+    const int r = blockIdx.x * SW_ROWS + wv;
+    if (r >= R) return;                               // wave-uniform; nothing below synchronises waves
+    uint32_t* h = hist_all[wv];
+    uint32_t* res = res_all[wv];
+    unsigned long long* bkey = bkey_all[wv];
+    uint32_t* bpos = bpos_all[wv];
+    uint32_t* bidx = bidx_all[wv];
+    unsigned long long* chosen = chosen_all[wv];
+    const int b = r / Tq, t = r % Tq;
     const int nv = n_visible(pos0 + t, L, m, Nc);
     int32_t* out = idx_out + (size_t)r * topk;
-    if (nv <= topk) {
-        for (int i = tid; i < topk; i += SEL_TPB) out[i] = i < nv ? i : -1;
-        if (cnt_out && tid == 0) cnt_out[r] = nv;
+    if (nv <= topk) {                                 // every visible entry is selected
+        for (int i = lane; i < topk; i += 64) out[i] = i < nv ? i : -1;
+        if (cnt_out && lane == 0) cnt_out[r] = nv;
         return;
     }
-    auto give_up = [&]() {                              // uniform: the exact fallback takes the row
-        if (tid == 0) fail[1 + atomicAdd(&fail[0], 1u)] = (uint32_t)r;
+    auto give_up = [&]() {                            // the exact fallback takes the row
+        if (lane == 0) fail[1 + atomicAdd(&fail[0], 1u)] = (uint32_t)r;
     };
-    if (tid == 0) {
-        uint32_t s = 0, over = 0;
-        for (int i = 0; i < nsplit; ++i) {
-            const uint32_t ci = cnt[(size_t)r * nsplit + i];
-            spre[i] = s;
-            over |= ci > (uint32_t)caps;
-            s += ci;
-        }
-        spre[nsplit] = s;
-        bad = over || s < (uint32_t)topk || s > (uint32_t)CAND_P;
-        nband = 0;
+    // segment counts (lane s holds segment s), slots per segment and their prefix
+    const uint32_t mc = lane < nsplit ? cnt[(size_t)r * nsplit + lane] : 0u;
+    const uint32_t msl = (mc + 63u) / 64u;
+    uint32_t send = msl;                              // inclusive prefix of slot counts
+#pragma unroll
+    for (int o = 1; o < MAX_SPLIT; o <<= 1) {
+        const uint32_t x = __shfl_up(send, o, 64);
+        if (lane >= o) send += x;
     }
-    for (int i = tid; i < CAND_P / 32; i += SEL_TPB) chosen[i] = 0;
-    __syncthreads();
-    if (bad) { give_up(); return; }
-    const uint32_t n = spre[nsplit];
-    const uint32_t e0 = (uint32_t)tid * SEL_CPT;
-    uint32_t key[SEL_CPT], cid[SEL_CPT];
+    uint32_t n = mc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) n += __shfl_xor(n, o, 64);
+    const uint32_t nslots = __shfl(send, nsplit - 1, 64);
+    const bool over = __builtin_amdgcn_ballot_w64(lane < nsplit && mc > (uint32_t)caps - 64u) != 0;
+    if (over || n < (uint32_t)topk || nslots > (uint32_t)SW_SLOTS) { give_up(); return; }
+
+    // ---- load: slot k belongs to segment seg(k) = #{s : send[s] <= k} ----
+    // lane k works out slot k's first storage entry (seg caps + 64 (k - first slot of seg)) and its
+    // number of entries; each slot then fetches both with a lane permute (kept in vector registers:
+    // one scalar copy per slot would exhaust the scalar file)
+    uint32_t soff = 0u, sval = 0u;
     {
-        int seg = 0;
-        while (seg + 1 < nsplit && e0 >= spre[seg + 1]) ++seg;
+        uint32_t seg = 0u;
 #pragma unroll
-        for (int i = 0; i < SEL_CPT; ++i) {
-            const uint32_t e = e0 + i;
-            key[i] = 0u;
-            cid[i] = 0u;
-            if (e < n) {
-                while (e >= spre[seg + 1]) ++seg;
-                const uint2 cv = cand[((size_t)r * nsplit + seg) * caps + (e - spre[seg])];
-                key[i] = f32_key(__uint_as_float(cv.y));
-                cid[i] = cv.x;
-            }
+        for (int s2 = 0; s2 < MAX_SPLIT; ++s2) {
+            const uint32_t e = (uint32_t)__shfl((int)send, s2, 64);
+            if (s2 < nsplit && e <= (uint32_t)lane) seg = (uint32_t)s2 + 1u;
+        }
+        const uint32_t sg = min(seg, (uint32_t)MAX_SPLIT - 1u);
+        const uint32_t sbeg = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * sg), (int)(send - msl));
+        const uint32_t scnt = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * sg), (int)mc);
+        if ((uint32_t)lane < nslots && seg < (uint32_t)nsplit) {
+            const uint32_t first = 64u * ((uint32_t)lane - sbeg);
+            soff = seg * (uint32_t)caps + first;
+            sval = min(64u, scnt - first);
         }
     }
-    // 1. tau = k-th largest S~ of the list (four 8-bit radix passes)
-    uint32_t pref = 0, need = (uint32_t)topk;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
+    // every slot loads unconditionally (empty lanes reread the row's first entry), so that all the
+    // loads are in flight before the first result is used; empty lanes are masked afterwards
+    const uint2* crow = cand + (size_t)r * nsplit * caps;
+    uint32_t key[SW_SLOTS], cid[SW_SLOTS];
+    uint64_t valid = 0ull;                            // bit k: this lane's entry of slot k exists
 #pragma unroll
-        for (int i = 0; i < SEL_CPT; ++i)
-            if (e0 + i < n && (pass == 0 || (key[i] >> (shift + 8)) == (pref >> (shift + 8))))
-                atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
-        __syncthreads();
-        if (wave == 0) wave_find_bin256(hist, need, 0u, res);
-        __syncthreads();
-        pref |= res[0] << shift;
-        need -= res[1];
-        __syncthreads();
+    for (int k = 0; k < SW_SLOTS; ++k) {
+        const uint32_t so = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * k, (int)soff);
+        const uint32_t sv = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * k, (int)sval);
+        const bool ok = (uint32_t)k < nslots && (uint32_t)lane < sv;
+        valid |= (uint64_t)(ok ? 1u : 0u) << k;
+        const uint2 e = crow[ok ? so + (uint32_t)lane : 0u];
+        key[k] = e.y;
+        cid[k] = e.x;
     }
-    const float tau = key_f32(pref);
+#pragma unroll
+    for (int k = 0; k < SW_SLOTS; ++k)                // 0 = empty (no finite score has order key 0)
+        key[k] = ((valid >> k) & 1ull) ? f32_key(__uint_as_float(key[k])) : 0u;
+    // ---- tau: radix select over 1024 bins of the key range present, then inside the chosen bin ----
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+#pragma unroll
+    for (int k = 0; k < SW_SLOTS; ++k)
+        if (key[k]) { kmn = min(kmn, key[k]); kmx = max(kmx, key[k]); }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, 64));
+        kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, 64));
+    }
+    uint32_t base = kmn, need = (uint32_t)topk;
+    {
+        int shift = max(0, 32 - (int)__clz((int)(kmx - kmn)) - 10), pshift = 32;
+        for (;;) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *(u32x4_t*)(h + 4 * (lane + 64 * i)) = u32x4_t{0u, 0u, 0u, 0u};
+            wave_lds_fence();
+#pragma unroll
+            for (int k = 0; k < SW_SLOTS; ++k) {
+                const uint32_t d = key[k] - base;     // wraps below base: outside the range
+                if (key[k] && (pshift >= 32 || d < (1u << pshift))) atomicAdd(&h[d >> shift], 1u);
+            }
+            wave_lds_fence();
+            wave_find_bin1024(h, need, res);
+            wave_lds_fence();
+            base += res[0] << shift;
+            need -= res[1];
+            if (shift == 0) break;
+            pshift = shift;
+            shift = max(0, shift - 10);
+        }
+    }
+    const float tau = key_f32(base);
     const double D = (double)wq[r] * (double)__uint_as_float(kmax[b]) * 7.62939453125e-06 * (1.0 + 1.0 / 512) +
                      1.1754943508222875e-38;
     const double lo = (double)tau - 2.0 * D, hi = (double)tau + 2.0 * D;
     if (!((double)thr[r] <= lo)) { give_up(); return; }       // the list might miss band entries
 
-    // 2. classify: in (above hi), band (listed), out
-    uint32_t in_m = 0, band_m = 0, my_in = 0;
+    // ---- classify: in (above hi) / band (listed in LDS with its slot position) / out ----
+    // In the key domain with the bounds rounded outward to fp32: an entry just above hi may be
+    // ranked with the band and one just below lo may join it, which changes nothing (the band
+    // is ranked exactly, and the certain classes stay certain).
+    uint32_t khi = f32_key((float)hi), klo = f32_key((float)lo);
+    if ((double)key_f32(khi) < hi) khi += 1u;         // key of the smallest float >= hi
+    if ((double)key_f32(klo) > lo) klo -= 1u;         // key of the largest float <= lo
+    unsigned long long inm = 0ull, bandm = 0ull;
+    uint32_t n_in = 0, nb = 0;
 #pragma unroll
-    for (int i = 0; i < SEL_CPT; ++i) {
-        if (e0 + i >= n) continue;
-        const double v = (double)key_f32(key[i]);
-        if (v > hi) { in_m |= 1u << i; ++my_in; }
-        else if (v >= lo) {
-            band_m |= 1u << i;
-            const uint32_t slot = atomicAdd(&nband, 1u);
-            if (slot < (uint32_t)BAND_P) { bidx[slot] = cid[i]; bpos[slot] = e0 + i; }
+    for (int k = 0; k < SW_SLOTS; ++k) {
+        const uint32_t f_in = (key[k] != 0u && key[k] > khi) ? 1u : 0u;
+        const uint32_t f_band = (key[k] != 0u && key[k] <= khi && key[k] >= klo) ? 1u : 0u;
+        inm |= (unsigned long long)f_in << k;
+        bandm |= (unsigned long long)f_band << k;
+        const unsigned long long mi = __builtin_amdgcn_ballot_w64(f_in != 0u), mb = __builtin_amdgcn_ballot_w64(f_band != 0u);
+        if (mb) {                                     // uniform
+            const uint32_t slot = nb + __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u));
+            if (f_band && slot < (uint32_t)SW_BAND) { bidx[slot] = cid[k]; bpos[slot] = 64u * k + lane; }
         }
+        n_in += (uint32_t)__popcll(mi);
+        nb += (uint32_t)__popcll(mb);
     }
-    uint32_t n_in;
-    block_scan(my_in, scratch, &n_in);
-    __syncthreads();
-    const uint32_t nb = nband;
-    if (nb > (uint32_t)BAND_P || n_in > (uint32_t)topk || (uint32_t)topk - n_in > nb) { give_up(); return; }
+    if (nb > (uint32_t)SW_BAND || n_in > (uint32_t)topk || (uint32_t)topk - n_in > nb) { give_up(); return; }
     const uint32_t needb = (uint32_t)topk - n_in;
+    if (lane < SW_SLOTS) chosen[lane] = 0ull;
+    wave_lds_fence();
 
-    // 3. exact scores of the band, composite keys (score key, inverted index), rank, choose
+    // ---- exact scores of the band, composite keys (score key, inverted index), rank, choose ----
     if (needb > 0 && needb < nb) {
         const uint16_t* qrow = q_idx + (size_t)r * P_HI * P_DI;
         const float* wrow = w_idx + (size_t)r * P_HI;
-        for (uint32_t i = wave; i < nb; i += SEL_TPB / 64) {
+        for (uint32_t i = 0; i < nb; ++i) {
             const float sx = wave_exact_score<0, P_DI, P_HI>(qrow, wrow, k_idx + ((size_t)b * Nc + bidx[i]) * P_DI);
             if (lane == 0) bkey[i] = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - bidx[i]);
         }
-        __syncthreads();
-        for (uint32_t i = tid; i < nb; i += SEL_TPB) {
+        wave_lds_fence();
+        for (uint32_t i = lane; i < nb; i += 64) {
             const unsigned long long ki = bkey[i];
             uint32_t rank = 0;
             for (uint32_t j = 0; j < nb; ++j) rank += bkey[j] > ki;
-            if (rank < needb) atomicOr(&chosen[bpos[i] >> 5], 1u << (bpos[i] & 31));
+            if (rank < needb) atomicOr(&chosen[bpos[i] >> 6], 1ull << (bpos[i] & 63));
         }
     } else if (needb == nb) {
-        for (uint32_t i = tid; i < nb; i += SEL_TPB) atomicOr(&chosen[bpos[i] >> 5], 1u << (bpos[i] & 31));
+        for (uint32_t i = lane; i < nb; i += 64) atomicOr(&chosen[bpos[i] >> 6], 1ull << (bpos[i] & 63));
     }
-    __syncthreads();
+    wave_lds_fence();
 
-    // 4. the chosen indices in ascending order
-    uint32_t sel = in_m;
+    // ---- the chosen indices in ascending order: a ballot scan over the slots ----
+    uint32_t o = 0;
 #pragma unroll
-    for (int i = 0; i < SEL_CPT; ++i) {
-        const uint32_t e = e0 + i;
-        if (((band_m >> i) & 1u) && ((chosen[e >> 5] >> (e & 31)) & 1u)) sel |= 1u << i;
+    for (int k = 0; k < SW_SLOTS; ++k) {
+        if ((uint32_t)k < nslots) {
+            const bool sel = ((inm >> k) & 1ull) || (((bandm >> k) & 1ull) && ((chosen[k] >> lane) & 1ull));
+            const unsigned long long ms = __builtin_amdgcn_ballot_w64(sel);
+            const uint32_t pos = o + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
+            if (sel && pos < (uint32_t)topk) out[pos] = (int32_t)cid[k];
+            o += (uint32_t)__popcll(ms);
+        }
     }
-    uint32_t tot;
-    uint32_t o = block_scan(__popc(sel), scratch, &tot);
-    if (tot != (uint32_t)topk) { give_up(); return; }          // inconsistent: leave it to the exact path
-#pragma unroll
-    for (int i = 0; i < SEL_CPT; ++i)
-        if ((sel >> i) & 1u) out[o++] = (int32_t)cid[i];
-    if (cnt_out && tid == 0) cnt_out[r] = topk;
+    if (cnt_out && lane == 0) cnt_out[r] = topk;
 }
 
 // ---------------------------------------------------------------------------
@@ -588,7 +813,7 @@ static PrefillPlan prefill_plan(int B, int Tq, int Nc) {
     P.nqb = (Tq + P_QPG - 1) / P_QPG;
     auto splits = [&](int nks, int& nsplit, int& span) {
         const int units = B * P.nqb;
-        int ns = (1024 + units - 1) / units;
+        int ns = (CSA_PF_UNITS + units - 1) / units;
         ns = std::max(1, std::min(ns, MAX_SPLIT));
         ns = std::min(ns, std::max(1, (nks + 1023) / 1024));
         span = ((nks + ns - 1) / ns + P_TK - 1) / P_TK * P_TK;
@@ -639,7 +864,7 @@ int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_id
     CSA_LAUNCH("k_pzero", k_pzero, dim3((B + 255) / 256), dim3(256), 0, st, kmax, B);
     CSA_LAUNCH("k_pzero", k_pzero, dim3(1), dim3(64), 0, st, fail, 1);
     {
-        const long long nb = ((long long)B * Nc + 255) / 256 + ((long long)P.R + 255) / 256;
+        const long long nb = ((long long)B * Nc + NORM_KEYS_PER_BLOCK - 1) / NORM_KEYS_PER_BLOCK + ((long long)P.R + 3) / 4;
         CSA_LAUNCH("k_pnorm", k_pnorm, dim3((unsigned)nb), dim3(256), 0, st, q, w_idx, k, B, Nc,
                    (int)P.R, wq, kmax);
     }
@@ -653,8 +878,9 @@ int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_id
                thr);
     A.nsplit = P.nsplit1; A.span = P.span1;
     CSA_LAUNCH("k_pscore", k_pscore<1>, dim3((unsigned)(B * P.nqb * P.nsplit1)), dim3(P_TPB), 0, st, A);
-    CSA_LAUNCH("k_pselect", k_pselect, dim3((unsigned)P.R), dim3(SEL_TPB), 0, st, cand, cnt, thr, wq, kmax, q, w_idx,
-               k, Tq, Nc, L, m, pos0, topk, P.nsplit1, P.caps, idx_out, cnt_out, fail);
+    CSA_LAUNCH("k_pselect", k_pselect, dim3((unsigned)((P.R + SW_ROWS - 1) / SW_ROWS)), dim3(64 * SW_ROWS), 0, st, cand,
+               cnt, thr, wq, kmax, q, w_idx, k, Tq, Nc, L, m, pos0, topk, P.nsplit1, P.caps, (int)P.R, idx_out, cnt_out,
+               fail);
     CSA_LAUNCH("k_pfallback", k_pfallback, dim3(FB_SLOTS), dim3(FB_TPB), 0, st, fail, q, w_idx, k, Tq, Nc, L, m,
                pos0, topk, fbk, P.NcP, idx_out, cnt_out);
     return 0;
