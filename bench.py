@@ -13,6 +13,13 @@ Prints one JSON line: queries/s (value), the indexer-score kernel's achieved
 HBM bandwidth against the 8 TB/s peak (roofline), and the CPU oracle timed on
 a bounded sample of the same workload (cpu_baseline), plus a sampled parity
 check of that sample against the GPU result.
+
+The metric's second part, indexer prefill TFLOP/s, is measured in the same run
+and reported under "indexer_prefill" (workload prefill_8k_on_256k: 8192 new
+query tokens at the end of a 262,144-token context, 65,536 bf16 indexer keys,
+8 heads x 128, causal at block granularity, top-k = 1024).  A call there is one
+csa_index_topk over all 8192 queries; FLOPs are 2 HI dI per (query, visible
+entry); its roofline is the contraction kernel against the bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -28,13 +35,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CSA+HCA decode queries/s & HBM GB/s at 1M ctx; indexer prefill TFLOP/s"
 HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 DOMINANT = "k_score"
+PREFILL_DOMINANT = "k_pscore"
+PREFILL_KERNELS = ("k_pzero", "k_pnorm", "k_pscore_sample", "k_pthresh", "k_pscore", "k_pselect", "k_pfallback")
 KERNELS = ("k_fill", "k_score", "k_collect", "k_select", "k_attn_pair", "k_attn_sparse", "k_attn_dense", "k_combine")
 
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("index_topk.hip", "common.h", "exact_dot.h"):
+    for f in ("index_topk.hip", "index_common.h", "common.h", "exact_dot.h"):
         with open(os.path.join(ROOT, "compressed_sparse_kv_compressor_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -60,6 +70,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=20, help="timed calls of the prefill indexer leg (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run two plain device copies of MIB MiB (a kernel of known "
                          "traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE by)")
@@ -188,7 +199,111 @@ def main():
 
     if not args.no_cpu_baseline:
         out.update(cpu_leg(cfg, base, outs[0], dev))
+    del copies, base, dargs, outs, ws
+    torch.cuda.empty_cache()
+    if args.prefill_steps > 0:
+        out["indexer_prefill"] = prefill_leg(args, dev, cpu=not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)
+
+
+def prefill_leg(args, dev, cpu=True):
+    """csa_index_topk over 8192 queries of the chunked-prefill workload."""
+    import numpy as np
+    import torch
+
+    from compressed_sparse_kv_compressor_amd import binding as b
+    from compressed_sparse_kv_compressor_amd import synth
+    from compressed_sparse_kv_compressor_amd.configs import PREFILL_8K_256K as pc
+
+    Tq, L, m, HI, dI, topk, Nc, pos0 = pc.Tq, pc.L, pc.m, pc.HI, pc.dI, pc.topk, pc.Nc, pc.pos0
+    g = synth.parallel_bits_to_device
+    q_idx = g(0, "prefill_q_idx", (1, Tq, HI, dI), dI ** -0.5, 0, dev)
+    k_idx = g(0, "prefill_k_idx", (1, Nc, dI), dI ** -0.5, 0, dev)
+    w_idx = torch.from_numpy(synth.half_normal_f32(0, "prefill_w_idx", (1, Tq, HI), HI ** -0.5)).to(dev)
+    idx = torch.empty((1, Tq, topk), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, Tq), dtype=torch.int32, device=dev)
+    ws = b.workspace(b.lib.csa_index_topk_ws_bytes(1, Tq, HI, dI, Nc, topk, 0), dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        b.csa_index_topk(q_idx, w_idx, k_idx, 0, L, m, pos0, topk, idx, cnt, ws=ws, stream=stream)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    b.prof_reset()
+    b.prof_only(PREFILL_DOMINANT)
+    b.prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.prefill_steps):
+        call()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    b.prof_enable(False)
+    kms, kn = b.prof_read(PREFILL_DOMINANT)
+    b.prof_reset()
+    b.prof_only(None)
+    b.prof_enable(True)
+    for _ in range(min(args.prefill_steps, 10)):
+        call()
+    torch.cuda.synchronize()
+    b.prof_enable(False)
+    kern = {}
+    for name in PREFILL_KERNELS:
+        t, n = b.prof_read(name)
+        if n:
+            kern[name] = round(t / n * 1000.0, 2)
+    b.prof_reset()
+
+    nv = np.minimum((pos0 + np.arange(Tq) + 1) // m, Nc)
+    flops = 2.0 * HI * dI * float(nv.sum())            # visible (query, entry) pairs
+    ms_call = el / args.prefill_steps * 1e3
+    k_us = kms / kn * 1000.0 if kn else None
+    res = {
+        "workload": pc.name, "Tq": Tq, "L": L, "Nc": Nc, "HI": HI, "dI": dI, "topk": topk, "dtype": "bf16",
+        "calls": args.prefill_steps, "ms_per_call": round(ms_call, 4),
+        "value": round(flops / (ms_call * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+        "algorithmic_flops_per_call": flops,
+        "frac_of_bf16_peak": round(flops / (ms_call * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "kernel_us_breakdown": kern,
+        "roofline": {"bound": "mfma", "kernel": PREFILL_DOMINANT,
+                     "achieved": round(flops / (k_us * 1e-6) / 1e12, 1) if k_us else None,
+                     "kernel_us": round(k_us, 2) if k_us else None, "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / (k_us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+                     if k_us else None, "traffic": None},
+    }
+    if cpu:
+        res.update(prefill_cpu_leg(pc, q_idx, w_idx, k_idx, idx))
+    return res
+
+
+def prefill_cpu_leg(pc, q_idx, w_idx, k_idx, gidx, rows=(0, 4095, 8191)):
+    """The oracle on a few query rows of the prefill workload (bounded CPU sample),
+    and a bit-exact check of the GPU's selection for those rows."""
+    import numpy as np
+
+    import oracle
+
+    q = q_idx.cpu().numpy().view(np.uint16)
+    w = w_idx.cpu().numpy()
+    k = k_idx.cpu().numpy().view(np.uint16)
+    g = gidx.cpu().numpy()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    ok = True
+    flops = 0.0
+    for t in rows:
+        want, _, _, nv = oracle.index_topk(q[:, t:t + 1], w[:, t:t + 1], k, pc.L, pc.m, pc.pos0 + t, pc.topk)
+        flops += 2.0 * pc.HI * pc.dI * float(nv[0, 0])
+        ok = ok and bool(np.array_equal(want[0, 0], g[0, t]))
+    el = time.perf_counter() - t0
+    return {
+        "cpu_baseline": {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                         "sample": f"query rows {list(rows)} of {pc.name}: exact indexer scores over all visible "
+                                   f"entries + top-{pc.topk}", "seconds": round(el, 2)},
+        "parity_sample": {"rows": list(rows), "topk_bit_exact": ok},
+    }
 
 
 def cpu_leg(cfg, x, gpu_out, dev):
