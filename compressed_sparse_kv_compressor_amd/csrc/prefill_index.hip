@@ -55,11 +55,18 @@ constexpr int P_QPW = 4 * P_NA;               // queries per wave
 #ifndef CSA_PF_UNITS
 #define CSA_PF_UNITS 1024
 #endif
+#ifndef CSA_PF_VPM1
+#define CSA_PF_VPM1 8                 // VALU instructions scheduled after each MFMA of a tile's first half
+#endif
+#ifndef CSA_PF_VPM2
+#define CSA_PF_VPM2 5                 // ... and of its second half
+#endif
 #ifndef CSA_PF_NBUF
-#define CSA_PF_NBUF 4
+#define CSA_PF_NBUF 5
 #endif
 constexpr int P_NBUF = CSA_PF_NBUF;           // LDS tile buffers (loads run P_NBUF - 1 tiles ahead)
 static_assert(P_NBUF >= 3 && P_NBUF <= 8, "tile buffers");
+static_assert(P_TK == 64, "the tile pipeline handles two 32-entry sub-tiles per tile");
 constexpr int P_NW = CSA_PF_NW;               // waves per workgroup
 constexpr int P_QPG = P_QPW * P_NW;           // queries per workgroup
 constexpr int P_TPB = 64 * P_NW;
@@ -305,16 +312,17 @@ __device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], con
         vb = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
     };
     // one query's 64 keys (lane = key - kbase): sample store or list append
-    auto emit = [&](float v, int lq, int kk, auto full_tag) {
+    auto emit = [&](float v, int lq, int kk, bool live, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;     // every key of the tile visible to every query
         if constexpr (MODE == 0) {
             // every lane stores (a missing row's offset lies past the resource): the number of memory
             // operations per tile is fixed, which the tile wait below counts on
-            const uint32_t off = qw + lq < Tq ? ((uint32_t)(w * P_QPW + lq) * (uint32_t)A.NSP + (uint32_t)kk) * 2u
-                                              : 0x80000000u;
+            const uint32_t off = live && qw + lq < Tq
+                                     ? ((uint32_t)(w * P_QPW + lq) * (uint32_t)A.NSP + (uint32_t)kk) * 2u
+                                     : 0x80000000u;
             __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(f32_key(v) >> 16), rsmp, (int)off, 0, 0);
         } else {
-            const bool cd = FULL ? v >= thr_q[lq] : (kk < nv_q[lq] && v >= thr_q[lq]);
+            const bool cd = live && (FULL ? v >= thr_q[lq] : (kk < nv_q[lq] && v >= thr_q[lq]));
             const unsigned long long mask = __builtin_amdgcn_ballot_w64(cd);
             // slot base of this query's stores (scalar); once fewer than 64 slots remain the stores
             // go to the last 64 (the count then exceeds caps - 64 and the select hands the row to the
@@ -332,21 +340,46 @@ __device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], con
             C[lq] += (uint32_t)__popcll(mask);
         }
     };
-    auto tile_out = [&](const float (&VA)[P_NA][2], const float (&VB)[P_NA][2], int tile, auto full_tag) {
+    auto tile_out = [&](const float (&VA)[P_NA][2], const float (&VB)[P_NA][2], int tile, bool live, auto full_tag) {
         const int kk = kb + tile * P_TK + lane;
 #pragma unroll
         for (int a = 0; a < P_NA; ++a) {
             const auto tA = __builtin_amdgcn_permlane32_swap(__float_as_uint(VA[a][0]), __float_as_uint(VA[a][1]), false, false);
             const auto tB = __builtin_amdgcn_permlane32_swap(__float_as_uint(VB[a][0]), __float_as_uint(VB[a][1]), false, false);
-            emit(__uint_as_float(tA[0]), 4 * a + 0, kk, full_tag);
-            emit(__uint_as_float(tB[0]), 4 * a + 1, kk, full_tag);
-            emit(__uint_as_float(tA[1]), 4 * a + 2, kk, full_tag);
-            emit(__uint_as_float(tB[1]), 4 * a + 3, kk, full_tag);
+            emit(__uint_as_float(tA[0]), 4 * a + 0, kk, live, full_tag);
+            emit(__uint_as_float(tB[0]), 4 * a + 1, kk, live, full_tag);
+            emit(__uint_as_float(tA[1]), 4 * a + 2, kk, live, full_tag);
+            emit(__uint_as_float(tB[1]), 4 * a + 3, kk, live, full_tag);
         }
+    };
+    // Software pipeline across tiles: the MFMAs of a tile's first sub-tile run beside the epilogue of
+    // the previous tile's second sub-tile and that tile's list stores, and the MFMAs of the second
+    // sub-tile beside the epilogue of the first, so that the VALU work always has MFMAs to hide
+    // behind.  Carried from one tile to the next: the accumulators of the second sub-tile and the
+    // scores of the first.  (At the first tile the carried state is empty and its stores are dropped,
+    // which keeps the number of stores per step fixed.)
+    f32x16_t pacc[P_NA];
+    float pVA[P_NA], pVB[P_NA];
+#pragma unroll
+    for (int a = 0; a < P_NA; ++a) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pacc[a][r] = 0.f;
+        pVA[a] = pVB[a] = 0.f;
+    }
+    auto finish_prev = [&](int tile, bool live) {             // epilogue + stores of tile `tile`
+        float qVA[P_NA][2], qVB[P_NA][2];
+#pragma unroll
+        for (int a = 0; a < P_NA; ++a) {
+            qVA[a][0] = pVA[a];
+            qVB[a][0] = pVB[a];
+            block_scores(pacc[a], wv[a], qVA[a][1], qVB[a][1]);
+        }
+        // (one code path: a branch between variants would leave the compiler unsure of the number of
+        // stores per step, and it would then add waits of its own before the tile reads)
+        tile_out(qVA, qVB, tile, live, std::false_type{});
     };
     auto compute = [&](const uint16_t* buf, int tile) {
         const CSA_LDS char* lb = (const CSA_LDS char*)buf;
-        float VA[P_NA][2], VB[P_NA][2];
         // all B fragments of the tile are read up front (16 reads in flight): the MFMAs of the first
         // sub-tile wait for the first eight only, and LDS latency is paid once per tile
         u32x4_t bt[P_TK / 32][8];
@@ -355,24 +388,42 @@ __device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], con
 #pragma unroll
             for (int s = 0; s < 8; ++s) bt[j][s] = *(const CSA_LDS u32x4_t*)(lb + ((boff ^ (32u * s)) + 8192u * j));
         __builtin_amdgcn_sched_barrier(0);
+        f32x16_t acc0[P_NA], acc1[P_NA];
 #pragma unroll
-        for (int j = 0; j < P_TK / 32; ++j) {
-            const u32x4_t (&bv)[8] = bt[j];
-            f32x16_t acc[P_NA];
+        for (int a = 0; a < P_NA; ++a)
 #pragma unroll
-            for (int a = 0; a < P_NA; ++a)
+            for (int r = 0; r < 16; ++r) { acc0[a][r] = 0.f; acc1[a][r] = 0.f; }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[a][r] = 0.f;
+        for (int s = 0; s < 8; ++s)
 #pragma unroll
-            for (int s = 0; s < 8; ++s)
+            for (int a = 0; a < P_NA; ++a) acc0[a] = mfma32_bf16(qa[a][s], as_bf16x8(bt[0][s]), acc0[a]);
+        finish_prev(tile - 1, tile > 0);
+#ifndef CSA_PF_NO_INTERLEAVE
+        // one MFMA, then a share of the VALU work (the 32x32x16 MFMA leaves room for about six VALU
+        // instructions beside it)
 #pragma unroll
-                for (int a = 0; a < P_NA; ++a) acc[a] = mfma32_bf16(qa[a][s], as_bf16x8(bv[s]), acc[a]);
-#pragma unroll
-            for (int a = 0; a < P_NA; ++a) block_scores(acc[a], wv[a], VA[a][j], VB[a][j]);
+        for (int i = 0; i < 8 * P_NA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, CSA_PF_VPM1, 0);
         }
-        // (one code path: a branch between variants would leave the compiler unsure of the number of
-        // stores per step, and it would then add waits of its own before the tile reads)
-        tile_out(VA, VB, tile, std::false_type{});
+#endif
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int a = 0; a < P_NA; ++a) acc1[a] = mfma32_bf16(qa[a][s], as_bf16x8(bt[1][s]), acc1[a]);
+#pragma unroll
+        for (int a = 0; a < P_NA; ++a) {
+            block_scores(acc0[a], wv[a], pVA[a], pVB[a]);
+            pacc[a] = acc1[a];
+        }
+#ifndef CSA_PF_NO_INTERLEAVE
+#pragma unroll
+        for (int i = 0; i < 8 * P_NA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, CSA_PF_VPM2, 1);
+        }
+#endif
     };
 
     // ---- the tile pipeline: tile t in buffer t % NB, loads issued NB - 1 tiles ahead ----
@@ -407,6 +458,7 @@ __device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], con
             CSA_PSTEP(0) CSA_PSTEP(1) CSA_PSTEP(2) CSA_PSTEP(3) CSA_PSTEP(4) CSA_PSTEP(5) CSA_PSTEP(6) CSA_PSTEP(7)
 #undef CSA_PSTEP
         }
+        finish_prev(ntiles - 1, true);         // the last tile's second sub-tile and stores
         __builtin_amdgcn_s_waitcnt(0);        // no tile load may still target this workgroup's LDS
     }
     if constexpr (MODE == 1) {
