@@ -275,7 +275,46 @@ def prefill_leg(args, dev, cpu=True):
     }
     if cpu:
         res.update(prefill_cpu_leg(pc, q_idx, w_idx, k_idx, idx))
+    del q_idx, k_idx, w_idx, ws
+    torch.cuda.empty_cache()
+    res["sparse_attn"] = prefill_attn_leg(args, dev, pc, idx)
     return res
+
+
+def prefill_attn_leg(args, dev, pc, idx):
+    """csa_sparse_attn over the same 8192 queries: 64 heads x 512, the selected 1024 entries plus the
+    128-token window of each query (FLOPs 4 H D (k + W) per query)."""
+    import torch
+
+    from compressed_sparse_kv_compressor_amd import binding as b
+    from compressed_sparse_kv_compressor_amd import synth
+
+    Tq, H, D, W, topk, Nc, pos0 = pc.Tq, pc.H, pc.D, pc.W, pc.topk, pc.Nc, pc.pos0
+    g = synth.parallel_bits_to_device
+    q = g(0, "prefill_q", (1, Tq, H, D), D ** -0.5, 0, dev)
+    kv = g(0, "prefill_kv", (1, Nc, D), D ** -0.5, 0, dev)
+    Lr, raw0 = Tq + W - 1, pos0 - (W - 1)
+    raw = g(0, "prefill_raw", (1, Lr, D), D ** -0.5, 0, dev)
+    out = torch.empty((1, Tq, H, D), dtype=torch.int16, device=dev)
+    ws = b.workspace(b.lib.csa_sparse_attn_ws_bytes(1, Tq, H, D, topk, W), dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        b.csa_sparse_attn(q, kv, idx, raw, raw0, pos0, W, pc.D ** -0.5, out, ws=ws, stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    n = max(1, min(args.prefill_steps, 10))
+    t0 = time.perf_counter()
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / n * 1e3
+    flops = 4.0 * H * D * (topk + W) * Tq
+    return {"H": H, "D": D, "W": W, "calls": n, "ms_per_call": round(ms, 4),
+            "value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_call": flops, "index_source": "the indexer leg's selection"}
 
 
 def prefill_cpu_leg(pc, q_idx, w_idx, k_idx, gidx, rows=(0, 4095, 8191)):

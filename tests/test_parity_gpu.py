@@ -284,6 +284,7 @@ SPARSE_CASES = [
     (1, 2, 32, 512, 700, 100, 20, 2.0),        # one head group (half a head pair), ragged top-k
     (1, 1, 96, 512, 2000, 300, 128, 1.0),      # 96 heads: the last head pair is half
     (3, 1, 128, 512, 9000, 2048, 128, 1.0),    # long top-k: several tiles per split
+    (1, 96, 64, 512, 3000, 256, 128, 1.0),     # prefill-shaped: many queries, each with its own window
 ]
 
 
