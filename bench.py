@@ -43,10 +43,16 @@ KERNELS = ("k_fill", "k_score", "k_collect", "k_select", "k_attn_pair", "k_attn_
 
 
 def kernel_source_sha() -> str:
+    """Hash of the sources the indexer-score kernel is built from, comments and blank space removed (a
+    comment edit does not invalidate counters taken on the same code)."""
+    import re
     h = hashlib.sha256()
     for f in ("index_topk.hip", "index_common.h", "common.h", "exact_dot.h"):
-        with open(os.path.join(ROOT, "compressed_sparse_kv_compressor_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "compressed_sparse_kv_compressor_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -17,13 +17,13 @@
 //   k_collect  every entry that can still reach the top-k (S~ >= lower edge of
 //              the bin holding the k-th largest, minus 2 Dmax) -> a per-row
 //              candidate list of (index, S~)
-//   k_select   one workgroup per row: exact k-th largest S~ (tau) by a bitonic
-//              sort of the candidates in LDS;
+//   k_select   one workgroup per row: exact k-th largest S~ (tau) from the two
+//              histogram levels plus an 8-bit third level over the candidates;
 //              S~ > tau + 2 Dmax is certainly selected, S~ < tau - 2 Dmax
 //              certainly not; the band in between is rescored exactly
-//              (wave-cooperative fixed-point dot products) and its remaining
-//              slots go by (exact S desc, index asc); the k indices are sorted
-//              ascending (bitonic, LDS).
+//              (wave-cooperative exact dot products) and its remaining slots go
+//              by (exact S desc, index asc); the candidates are kept in index
+//              order, so one prefix scan writes the k indices ascending.
 // Why the classification is safe.  Let every entry satisfy |S~_s - S_s| <= D
 // (D = Dmax of the row) and let tau be the k-th largest S~ (so fewer than k
 // entries have S~ > tau and at least k have S~ >= tau).
