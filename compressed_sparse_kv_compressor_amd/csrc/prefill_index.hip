@@ -491,33 +491,44 @@ __global__ __launch_bounds__(P_TPB, 8 / P_NW) void k_pscore(PScoreArgs A)
 // select over bins of the key range present in the row (min .. max), so that the
 // few values most samples share do not pile their LDS atomics onto one bin.
 // ---------------------------------------------------------------------------
-// wave: the bin (of 1024, counted from the top) holding the need-th largest; out = {bin, count above}
-__device__ void wave_find_bin1024(const uint32_t* h, uint32_t need, uint32_t* out) {
+// wave: the bin (of 1024, counted from the top) holding the need-th largest; returns {bin, count above it}.
+// Lane L reads bins 1008 - 16 L .. 1023 - 16 L once (four 16-byte reads) and locates from registers.
+__device__ __forceinline__ uint2 wave_find_bin1024(const uint32_t* h, uint32_t need) {
     const int lane = lane_id();
-    uint32_t s = 0;                                    // lane L covers bins 1023 - 16 L down to 1008 - 16 L
+    const u32x4_t* hp = (const u32x4_t*)(h + 1008 - 16 * lane);
+    uint32_t c[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += h[1023 - 16 * lane - i];
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x4_t v = hp[q4];
+        c[4 * q4] = v[0]; c[4 * q4 + 1] = v[1]; c[4 * q4 + 2] = v[2]; c[4 * q4 + 3] = v[3];
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += c[i];
     uint32_t incl = s;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const uint32_t v = __shfl_up(incl, o, 64);
         if (lane >= o) incl += v;
     }
-    uint32_t acc = incl - s;
-    if (acc < need && need <= incl) {
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t c = h[1023 - 16 * lane - i];
-            if (acc + c >= need) { out[0] = 1023 - 16 * lane - i; out[1] = acc; break; }
-            acc += c;
-        }
+    const uint32_t acc0 = incl - s;
+    const bool found = acc0 < need && need <= incl;
+    uint32_t bin = 0, above = 0, a = acc0;
+    bool done = !found;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {                    // descending bins
+        if (!done && a + c[i] >= need) { bin = 1008u - 16u * lane + i; above = a; done = true; }
+        if (!done) a += c[i];
     }
+    const unsigned long long fm = __builtin_amdgcn_ballot_w64(found);
+    const int fl = fm ? (int)__builtin_ctzll(fm) : 0;
+    return make_uint2((uint32_t)__builtin_amdgcn_readlane((int)bin, fl), (uint32_t)__builtin_amdgcn_readlane((int)above, fl));
 }
 
 __global__ __launch_bounds__(64) void k_pthresh(const uint16_t* __restrict__ samp, int NSP, int Tq, int Nc, long long L,
                                                  int m, long long pos0, int topk, float* __restrict__ thr)
 {
-    __shared__ uint32_t h[1024];
-    __shared__ uint32_t res[2];
+    __shared__ __attribute__((aligned(16))) uint32_t h[1024];
     const int r = blockIdx.x, t = r % Tq, lane = lane_id();
     const int nv = n_visible(pos0 + t, L, m, Nc);
     if (nv <= topk) {                                  // every visible entry is selected
@@ -567,10 +578,10 @@ __global__ __launch_bounds__(64) void k_pthresh(const uint16_t* __restrict__ sam
             if (pshift >= 32 || d < (1u << pshift)) atomicAdd(&h[d >> shift], 1u);
         });
         __syncthreads();
-        wave_find_bin1024(h, need, res);
+        const uint2 fb = wave_find_bin1024(h, need);
         __syncthreads();
-        base += res[0] << shift;
-        need -= res[1];
+        base += fb.x << shift;
+        need -= fb.y;
         if (shift == 0) break;
         pshift = shift;
         shift = max(0, shift - 10);
@@ -596,6 +607,104 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// Reductions over aligned groups of 8 lanes with DPP moves: swap neighbours, swap pairs, then
+// mirror the two halves of the group (every lane ends with the group's result).
+template <int CTRL> __device__ __forceinline__ int dpp8(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141;
+__device__ __forceinline__ int g8_min(int v) {
+    v = min(v, dpp8<DPP_XOR1>(v)); v = min(v, dpp8<DPP_XOR2>(v)); return min(v, dpp8<DPP_HALF_MIRROR>(v));
+}
+__device__ __forceinline__ int g8_max(int v) {
+    v = max(v, dpp8<DPP_XOR1>(v)); v = max(v, dpp8<DPP_XOR2>(v)); return max(v, dpp8<DPP_HALF_MIRROR>(v));
+}
+template <int CTRL> __device__ __forceinline__ double dpp8_d(double v) {
+    const unsigned long long u = __double_as_longlong(v);
+    const int lo = dpp8<CTRL>((int)(uint32_t)u), hi = dpp8<CTRL>((int)(uint32_t)(u >> 32));
+    return __longlong_as_double(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double g8_sum(double v) {     // exact here: every partial sum is representable
+    v += dpp8_d<DPP_XOR1>(v); v += dpp8_d<DPP_XOR2>(v); return v + dpp8_d<DPP_HALF_MIRROR>(v);
+}
+
+// The bf16 pair c of a fragment word as two fp32 values.
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// The exact score of one key row whose fragments sit in registers (lane L: head L / 8, elements
+// 16 (L % 8) .. + 15 of q and k, bf16 pairs).  A bf16 product is an fp32 value with a 16-bit
+// significand; when a head's products are normal and their exponents span at most 30, their fp64
+// sum is exact (30 + 16 + 7 < 53 bits for 128 terms), and rounding it once to fp32 gives the
+// correctly rounded head dot.  A span of up to 61 is split at 30 below the top exponent into two
+// such exact sums, added with an error-free transformation and rounded once (a tie of the rounded
+// sum is broken by the sign of the error).  Returns false (uniformly) outside these cases.
+__device__ __forceinline__ bool band_score_frag(const u32x4_t (&qf)[2], const u32x4_t (&kf)[2], const float (&w)[P_HI],
+                                                float& score) {
+    double s = 0.0;
+    int emin = 1000, emax = -1000, bad = 0;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const float x = hf ? bf_hi(qf[v][c]) : bf_lo(qf[v][c]);
+                const float y = hf ? bf_hi(kf[v][c]) : bf_lo(kf[v][c]);
+                const float pr = x * y;
+                const int e = (int)((__float_as_uint(pr) >> 23) & 0xffu);
+                if (x != 0.0f && y != 0.0f) {
+                    bad |= e == 0 || e == 255;
+                    emin = min(emin, e);
+                    emax = max(emax, e);
+                }
+                s += (double)pr;
+            }
+    emin = g8_min(emin);
+    emax = g8_max(emax);
+    bad = g8_max(bad);
+    float d;
+    if (__builtin_amdgcn_ballot_w64(bad || emax - emin > 30) == 0ull) {
+        d = (float)g8_sum(s);
+    } else {
+        if (__builtin_amdgcn_ballot_w64(bad || emax - emin > 61) != 0ull) return false;
+        const int T = emax - emin > 30 ? emax - 30 : -1000;   // products below T form the low sum
+        double hi = 0.0, lo = 0.0;
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const float pr = (hf ? bf_hi(qf[v][c]) : bf_lo(qf[v][c])) * (hf ? bf_hi(kf[v][c]) : bf_lo(kf[v][c]));
+                    const int e = (int)((__float_as_uint(pr) >> 23) & 0xffu);
+                    if (e >= T) hi += (double)pr; else lo += (double)pr;
+                }
+        hi = g8_sum(hi);
+        lo = g8_sum(lo);
+        const double sm = hi + lo, bv = sm - hi;
+        const double er = (hi - (sm - bv)) + (lo - bv);           // hi + lo = sm + er exactly
+        d = (float)sm;
+        if (er != 0.0 && sm > 0.0) {                               // only positive dots survive the relu
+            if (sm < 0x1p-125 || sm > 0x1p+127) return false;      // (uniform: rare, outside the fp32 normal range)
+            const unsigned long long bits = __double_as_longlong(sm);
+            if ((bits & 0x1fffffffull) == 0x10000000ull) {        // sm is halfway between two floats
+                if (er > 0.0 && (double)d < sm) d = __uint_as_float(__float_as_uint(d) + 1u);
+                if (er < 0.0 && (double)d > sm) d = __uint_as_float(__float_as_uint(d) - 1u);
+            }
+        }
+    }
+    const float rr = d > 0.0f ? d : 0.0f;
+    float sx = 0.0f;
+#pragma unroll
+    for (int hh = 0; hh < P_HI; ++hh)
+        sx = __builtin_fmaf(w[hh], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rr), 8 * hh)), sx);
+    score = sx;
+    return true;
+}
+
+constexpr int SW_BG = 4;                      // band rows fetched together
+
 __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     const uint2* __restrict__ cand, const uint32_t* __restrict__ cnt, const float* __restrict__ thr,
     const float* __restrict__ wq, const uint32_t* __restrict__ kmax, const uint16_t* __restrict__ q_idx,
@@ -604,15 +713,13 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     uint32_t* __restrict__ fail)
 {
     __shared__ uint32_t hist_all[SW_ROWS][1024];
-    __shared__ uint32_t res_all[SW_ROWS][2];
     __shared__ unsigned long long bkey_all[SW_ROWS][SW_BAND];
     __shared__ uint32_t bpos_all[SW_ROWS][SW_BAND], bidx_all[SW_ROWS][SW_BAND];
     __shared__ unsigned long long chosen_all[SW_ROWS][SW_SLOTS];
-    const int wv = threadIdx.x >> 6, lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
     const int r = blockIdx.x * SW_ROWS + wv;
     if (r >= R) return;                               // wave-uniform; nothing below synchronises waves
     uint32_t* h = hist_all[wv];
-    uint32_t* res = res_all[wv];
     unsigned long long* bkey = bkey_all[wv];
     uint32_t* bpos = bpos_all[wv];
     uint32_t* bidx = bidx_all[wv];
@@ -640,7 +747,8 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     uint32_t n = mc;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) n += __shfl_xor(n, o, 64);
-    const uint32_t nslots = __shfl(send, nsplit - 1, 64);
+    n = (uint32_t)__builtin_amdgcn_readfirstlane((int)n);                 // uniform: kept in scalar registers
+    const uint32_t nslots = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl((int)send, nsplit - 1, 64));
     const bool over = __builtin_amdgcn_ballot_w64(lane < nsplit && mc > (uint32_t)caps - 64u) != 0;
     if (over || n < (uint32_t)topk || nslots > (uint32_t)SW_SLOTS) { give_up(); return; }
 
@@ -667,51 +775,90 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     }
     // every slot loads unconditionally (empty lanes reread the row's first entry), so that all the
     // loads are in flight before the first result is used; empty lanes are masked afterwards
-    const uint2* crow = cand + (size_t)r * nsplit * caps;
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(cand + (size_t)r * nsplit * caps, (uint32_t)(nsplit * caps * 8));
     uint32_t key[SW_SLOTS], cid[SW_SLOTS];
-    uint64_t valid = 0ull;                            // bit k: this lane's entry of slot k exists
 #pragma unroll
     for (int k = 0; k < SW_SLOTS; ++k) {
-        const uint32_t so = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * k, (int)soff);
-        const uint32_t sv = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * k, (int)sval);
-        const bool ok = (uint32_t)k < nslots && (uint32_t)lane < sv;
-        valid |= (uint64_t)(ok ? 1u : 0u) << k;
-        const uint2 e = crow[ok ? so + (uint32_t)lane : 0u];
-        key[k] = e.y;
-        cid[k] = e.x;
+        const uint32_t so = (uint32_t)__builtin_amdgcn_readlane((int)soff, k);
+        const uint32_t sv = (uint32_t)__builtin_amdgcn_readlane((int)sval, k);
+        const bool ok = (uint32_t)lane < sv;        // sval is 0 in lanes >= nslots
+        const auto e = __builtin_amdgcn_raw_buffer_load_b64(crs, ok ? 8u * (so + (uint32_t)lane) : 0u, 0, 0);
+        key[k] = e[1];
+        cid[k] = e[0];
     }
+    // the per-slot validity is derived again from an opaque copy of the slot sizes, so that the
+    // compiler does not hold 48 lane masks in scalar registers across the loads
+    uint32_t sval2 = sval;
+    asm volatile("" : "+v"(sval2));
 #pragma unroll
-    for (int k = 0; k < SW_SLOTS; ++k)                // 0 = empty (no finite score has order key 0)
-        key[k] = ((valid >> k) & 1ull) ? f32_key(__uint_as_float(key[k])) : 0u;
+    for (int k = 0; k < SW_SLOTS; ++k) {              // 0 = empty (no finite score has order key 0)
+        const uint32_t sv = (uint32_t)__builtin_amdgcn_readlane((int)sval2, k);
+        key[k] = (uint32_t)lane < sv ? f32_key(__uint_as_float(key[k])) : 0u;
+        asm volatile("" : "+v"(key[k]));
+    }
     // ---- tau: radix select over 1024 bins of the key range present, then inside the chosen bin ----
+    // (empty keys are 0: below every key, so they are excluded by "key >= base" tests below, and
+    // kmn is the minimum of key - 1 + 1, where an empty key wraps to the top)
     uint32_t kmn = 0xffffffffu, kmx = 0u;
 #pragma unroll
-    for (int k = 0; k < SW_SLOTS; ++k)
-        if (key[k]) { kmn = min(kmn, key[k]); kmx = max(kmx, key[k]); }
+    for (int k = 0; k < SW_SLOTS; ++k) { kmn = min(kmn, key[k] - 1u); kmx = max(kmx, key[k]); }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, 64));
         kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, 64));
     }
+    kmn += 1u;
     uint32_t base = kmn, need = (uint32_t)topk;
     {
-        int shift = max(0, 32 - (int)__clz((int)(kmx - kmn)) - 10), pshift = 32;
+        int shift = max(0, 32 - (int)__clz((int)(kmx - kmn)) - 10);
+        uint32_t lim = 0xffffffffu;                   // the current bin spans keys base .. base + lim
         for (;;) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) *(u32x4_t*)(h + 4 * (lane + 64 * i)) = u32x4_t{0u, 0u, 0u, 0u};
             wave_lds_fence();
 #pragma unroll
             for (int k = 0; k < SW_SLOTS; ++k) {
-                const uint32_t d = key[k] - base;     // wraps below base: outside the range
-                if (key[k] && (pshift >= 32 || d < (1u << pshift))) atomicAdd(&h[d >> shift], 1u);
+                const uint32_t d = key[k] - base;
+                if (key[k] >= base && d <= lim) atomicAdd(&h[d >> shift], 1u);
             }
             wave_lds_fence();
-            wave_find_bin1024(h, need, res);
+            const uint2 fb = wave_find_bin1024(h, need);
+            const uint32_t nbin = h[fb.x];
             wave_lds_fence();
-            base += res[0] << shift;
-            need -= res[1];
+            base += fb.x << shift;
+            need -= fb.y;
             if (shift == 0) break;
-            pshift = shift;
+            if (nbin <= 64u) {
+                // few keys left in the bin: gather them into one register (lane j holds the j-th key met,
+                // through the histogram's LDS, which is no longer needed) and take the need-th largest by
+                // counting, instead of more histogram levels
+                const uint32_t width = 1u << shift;
+                uint32_t got = 0u;
+#pragma unroll
+                for (int k = 0; k < SW_SLOTS; ++k) {
+                    const bool inb = key[k] >= base && key[k] - base < width;
+                    const unsigned long long mb = __builtin_amdgcn_ballot_w64(inb);
+                    if (mb) {                          // uniform
+                        const uint32_t pos = got + __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u));
+                        if (inb) h[pos] = key[k];
+                        got += (uint32_t)__popcll(mb);
+                    }
+                }
+                wave_lds_fence();
+                const uint32_t mine = (uint32_t)lane < got ? h[lane] : 0u;
+                uint32_t gt = 0u, ge = 0u;
+                for (uint32_t i = 0; i < got; ++i) {
+                    const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)mine, (int)i);
+                    gt += y > mine;
+                    ge += y >= mine;
+                }
+                const bool ok = (uint32_t)lane < got && gt < need && need <= ge;
+                const unsigned long long om = __builtin_amdgcn_ballot_w64(ok);
+                base = (uint32_t)__builtin_amdgcn_readlane((int)mine, om ? (int)__builtin_ctzll(om) : 0);
+                break;
+            }
+            lim = (1u << shift) - 1u;
             shift = max(0, shift - 10);
         }
     }
@@ -728,19 +875,20 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     uint32_t khi = f32_key((float)hi), klo = f32_key((float)lo);
     if ((double)key_f32(khi) < hi) khi += 1u;         // key of the smallest float >= hi
     if ((double)key_f32(klo) > lo) klo -= 1u;         // key of the largest float <= lo
-    unsigned long long inm = 0ull, bandm = 0ull;
+    klo = max(klo, 1u);                               // empty keys (0) belong to no class
+    // the class is kept in the two top bits of the entry's index (bit 31: in, bit 30: band)
     uint32_t n_in = 0, nb = 0;
 #pragma unroll
     for (int k = 0; k < SW_SLOTS; ++k) {
-        const uint32_t f_in = (key[k] != 0u && key[k] > khi) ? 1u : 0u;
-        const uint32_t f_band = (key[k] != 0u && key[k] <= khi && key[k] >= klo) ? 1u : 0u;
-        inm |= (unsigned long long)f_in << k;
-        bandm |= (unsigned long long)f_band << k;
-        const unsigned long long mi = __builtin_amdgcn_ballot_w64(f_in != 0u), mb = __builtin_amdgcn_ballot_w64(f_band != 0u);
+        const bool f_in = key[k] > khi;
+        const bool f_band = key[k] <= khi && key[k] >= klo;
+        const unsigned long long mi = __builtin_amdgcn_ballot_w64(f_in), mb = __builtin_amdgcn_ballot_w64(f_band);
         if (mb) {                                     // uniform
             const uint32_t slot = nb + __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u));
             if (f_band && slot < (uint32_t)SW_BAND) { bidx[slot] = cid[k]; bpos[slot] = 64u * k + lane; }
         }
+        cid[k] |= (f_in ? 0x80000000u : 0u) | (f_band ? 0x40000000u : 0u);
+        asm volatile("" : "+v"(cid[k]));              // tag now: no lane masks carried to the output scan
         n_in += (uint32_t)__popcll(mi);
         nb += (uint32_t)__popcll(mb);
     }
@@ -753,9 +901,34 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     if (needb > 0 && needb < nb) {
         const uint16_t* qrow = q_idx + (size_t)r * P_HI * P_DI;
         const float* wrow = w_idx + (size_t)r * P_HI;
-        for (uint32_t i = 0; i < nb; ++i) {
-            const float sx = wave_exact_score<0, P_DI, P_HI>(qrow, wrow, k_idx + ((size_t)b * Nc + bidx[i]) * P_DI);
-            if (lane == 0) bkey[i] = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - bidx[i]);
+        const int sub = lane & 7;
+        u32x4_t qf[2];
+        qf[0] = *(const u32x4_t*)(qrow + (lane >> 3) * P_DI + 16 * sub);
+        qf[1] = *(const u32x4_t*)(qrow + (lane >> 3) * P_DI + 16 * sub + 8);
+        float w[P_HI];
+#pragma unroll
+        for (int hh = 0; hh < P_HI; ++hh) w[hh] = wrow[hh];
+        const uint16_t* kseq = k_idx + (size_t)b * Nc * P_DI + 16 * sub;
+        for (uint32_t i0 = 0; i0 < nb; i0 += SW_BG) {
+            // the group's key rows are fetched together (a short group rereads its last row)
+            u32x4_t kf[SW_BG][2];
+            uint32_t gi[SW_BG];
+#pragma unroll
+            for (int g = 0; g < SW_BG; ++g) {
+                gi[g] = bidx[min(i0 + (uint32_t)g, nb - 1u)];
+                const uint16_t* kp = kseq + (size_t)gi[g] * P_DI;
+                kf[g][0] = *(const u32x4_t*)kp;
+                kf[g][1] = *(const u32x4_t*)(kp + 8);
+            }
+#pragma unroll
+            for (int g = 0; g < SW_BG; ++g) {
+                if (i0 + (uint32_t)g < nb) {
+                    float sx;
+                    // outside the fp64 case (rare) the exact fallback takes the row
+                    if (!band_score_frag(qf, kf[g], w, sx)) { give_up(); return; }
+                    if (lane == 0) bkey[i0 + g] = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - gi[g]);
+                }
+            }
         }
         wave_lds_fence();
         for (uint32_t i = lane; i < nb; i += 64) {
@@ -770,14 +943,20 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     wave_lds_fence();
 
     // ---- the chosen indices in ascending order: a ballot scan over the slots ----
+    // lane k holds the chosen-band mask of slot k; each slot reads it with lane reads
+    const unsigned long long cm = lane < SW_SLOTS ? chosen[lane] : 0ull;
+    const uint32_t cm_lo = (uint32_t)cm, cm_hi = (uint32_t)(cm >> 32);
     uint32_t o = 0;
 #pragma unroll
     for (int k = 0; k < SW_SLOTS; ++k) {
         if ((uint32_t)k < nslots) {
-            const bool sel = ((inm >> k) & 1ull) || (((bandm >> k) & 1ull) && ((chosen[k] >> lane) & 1ull));
+            const uint32_t clo = (uint32_t)__builtin_amdgcn_readlane((int)cm_lo, k);
+            const uint32_t chi = (uint32_t)__builtin_amdgcn_readlane((int)cm_hi, k);
+            const uint32_t cw = lane < 32 ? clo : chi;
+            const bool sel = (cid[k] >> 31) || (((cid[k] >> 30) & 1u) && ((cw >> (lane & 31)) & 1u));
             const unsigned long long ms = __builtin_amdgcn_ballot_w64(sel);
             const uint32_t pos = o + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
-            if (sel && pos < (uint32_t)topk) out[pos] = (int32_t)cid[k];
+            if (sel && pos < (uint32_t)topk) out[pos] = (int32_t)(cid[k] & 0x3fffffffu);
             o += (uint32_t)__popcll(ms);
         }
     }
@@ -785,64 +964,186 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
 }
 
 // ---------------------------------------------------------------------------
-// k_pfallback: exact scores of every visible entry of each failed row, then a
-// 64-bit radix select on (score key, inverted index); FB_SLOTS rows at a time
+// Exact fallback for the rows the certified path gave up on.  The first FB_SLOTS
+// failed rows: k_pfb_score spreads the exact scores of their visible entries over
+// the whole grid (a score key per entry), then k_pfb_select selects each row's
+// top-k from its stored keys with one workgroup.  Rows beyond FB_SLOTS (only when
+// more than FB_SLOTS rows fail) go to k_pfallback, which scores its row itself.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(FB_TPB) void k_pfallback(
-    const uint32_t* __restrict__ fail, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-    const uint16_t* __restrict__ k_idx, int Tq, int Nc, long long L, int m, long long pos0, int topk,
-    unsigned long long* __restrict__ keys, size_t NcP, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
-{
-    __shared__ uint32_t hist[256], res[4], scratch[FB_TPB / 64];
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const uint32_t nf = fail[0];
-    unsigned long long* K = keys + (size_t)blockIdx.x * NcP;
-    for (uint32_t fi = blockIdx.x; fi < nf; fi += gridDim.x) {
-        const int r = (int)fail[1 + fi], b = r / Tq, t = r % Tq;
-        const int nv = n_visible(pos0 + t, L, m, Nc);
-        const uint16_t* qrow = q_idx + (size_t)r * P_HI * P_DI;
-        const float* wrow = w_idx + (size_t)r * P_HI;
-        for (int s = wave; s < nv; s += FB_TPB / 64) {
-            const float sx = wave_exact_score<0, P_DI, P_HI>(qrow, wrow, k_idx + ((size_t)b * Nc + s) * P_DI);
-            if (lane == 0) K[s] = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - (uint32_t)s);
+constexpr int FB_CH = 512;                    // workgroups of k_pfb_score (4 waves each)
+constexpr int FB_G = 8;                       // key rows fetched together per wave
+
+// exact score keys K[s] of entries s = s0, s0 + step, .. < nv of row r (one wave)
+__device__ __forceinline__ void fb_score_entries(int r, int b, int nv, int s0, int step,
+                                                 const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+                                                 const uint16_t* __restrict__ k_idx, int Nc, uint32_t* K) {
+    const int lane = lane_id(), sub = lane & 7;
+    const uint16_t* qrow = q_idx + (size_t)r * P_HI * P_DI;
+    const float* wrow = w_idx + (size_t)r * P_HI;
+    u32x4_t qf[2];
+    qf[0] = *(const u32x4_t*)(qrow + (lane >> 3) * P_DI + 16 * sub);
+    qf[1] = *(const u32x4_t*)(qrow + (lane >> 3) * P_DI + 16 * sub + 8);
+    float w[P_HI];
+#pragma unroll
+    for (int hh = 0; hh < P_HI; ++hh) w[hh] = wrow[hh];
+    const uint16_t* kseq = k_idx + (size_t)b * Nc * P_DI;
+    for (int s = s0; s < nv; s += FB_G * step) {
+        u32x4_t kf[FB_G][2];
+#pragma unroll
+        for (int g = 0; g < FB_G; ++g) {
+            const uint16_t* kp = kseq + (size_t)min(s + g * step, nv - 1) * P_DI + 16 * sub;
+            kf[g][0] = *(const u32x4_t*)kp;
+            kf[g][1] = *(const u32x4_t*)(kp + 8);
         }
-        __threadfence_block();
-        __syncthreads();
-        unsigned long long kp = 0;
-        uint32_t above = 0;
-        for (int pass = 0; pass < 8; ++pass) {
-            const int shift = 56 - 8 * pass;
-            if (tid < 256) hist[tid] = 0;
-            __syncthreads();
-            for (int s = tid; s < nv; s += FB_TPB) {
-                const unsigned long long k = K[s];
-                if (pass == 0 || (k >> (shift + 8)) == (kp >> (shift + 8))) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+#pragma unroll
+        for (int g = 0; g < FB_G; ++g) {
+            const int e = s + g * step;
+            if (e < nv) {
+                float sx;
+                if (!band_score_frag(qf, kf[g], w, sx))
+                    sx = wave_exact_score<0, P_DI, P_HI>(qrow, wrow, kseq + (size_t)e * P_DI);
+                if (lane == 0) K[e] = f32_key(sx);
             }
-            __syncthreads();
-            if (wave == 0) wave_find_bin256(hist, (uint32_t)topk, above, res);
-            __syncthreads();
-            kp |= (unsigned long long)res[0] << shift;
-            above = res[1];
-            __syncthreads();
         }
-        // keys are distinct: exactly topk of them are >= kp
-        const int per = (nv + FB_TPB - 1) / FB_TPB;
-        const int s0 = min(nv, tid * per), s1 = min(nv, s0 + per);
-        uint32_t mine = 0;
-        for (int s = s0; s < s1; ++s) mine += K[s] >= kp;
-        uint32_t tot;
-        uint32_t o = block_scan(mine, scratch, &tot);
-        int32_t* out = idx_out + (size_t)r * topk;
-        for (int s = s0; s < s1; ++s)
-            if (K[s] >= kp && o < (uint32_t)topk) out[o++] = s;
-        if (cnt_out && tid == 0) cnt_out[r] = topk;
-        __syncthreads();                               // K and hist are reused by the next row
     }
 }
 
-__global__ void k_pzero(uint32_t* p, int n) {
+// top-k of one row from its exact score keys K[0, nv) (a 1024-thread workgroup): the
+// topk-th largest key tau by radix levels over 1024 bins of the key range present,
+// then every entry above tau and the lowest-indexed entries equal to tau, ascending.
+// Thread t owns the contiguous entries [t per, (t + 1) per), per a multiple of 64, read
+// 64 at a time with 16-byte loads (K holds a multiple of 64 keys).
+__device__ __forceinline__ void fb_select_row(const uint32_t* K, int nv, int topk, int32_t* out, uint32_t* h, uint32_t* red) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int per = ((nv + FB_TPB - 1) / FB_TPB + 63) & ~63;
+    const int s0 = min(nv, tid * per), s1 = min(nv, s0 + per);
+    auto for_any = [&](auto&& f) {                    // every key once, in any order (coalesced)
+        for (int c = 4 * tid; c < nv; c += 32 * FB_TPB) {
+            u32x4_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = *(const u32x4_t*)(K + min(c + 4 * FB_TPB * j, (nv - 1) & ~3));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c + 4 * FB_TPB * j + e < nv) f(v[j][e]);
+        }
+    };
+    auto for_keys = [&](auto&& f) {                   // this thread's keys in ascending order
+        for (int c = s0; c < s1; c += 64) {
+            u32x4_t v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = *(const u32x4_t*)(K + c + 4 * j);
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c + 4 * j + e < s1) f(c + 4 * j + e, v[j][e]);
+        }
+    };
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    for_any([&](uint32_t x) { mn = min(mn, x); mx = max(mx, x); });
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    }
+    if (lane == 0) { red[2 * wave] = mn; red[2 * wave + 1] = mx; }
+    __syncthreads();
+    mn = 0xffffffffu; mx = 0u;
+    for (int w2 = 0; w2 < FB_TPB / 64; ++w2) { mn = min(mn, red[2 * w2]); mx = max(mx, red[2 * w2 + 1]); }
+    __syncthreads();
+    uint32_t base = mn, need = (uint32_t)topk, lim = 0xffffffffu;
+    int shift = max(0, 32 - (int)__clz((int)(mx - mn)) - 10);
+    for (;;) {
+        for (int i = tid; i < 1024; i += FB_TPB) h[i] = 0;
+        __syncthreads();
+        for_any([&](uint32_t x) {
+            const uint32_t d = x - base;
+            if (x >= base && d <= lim) atomicAdd(&h[d >> shift], 1u);
+        });
+        __syncthreads();
+        if (wave == 0) {
+            const uint2 fb = wave_find_bin1024(h, need);
+            if (lane == 0) { red[0] = fb.x; red[1] = fb.y; }
+        }
+        __syncthreads();
+        base += red[0] << shift;
+        need -= red[1];
+        __syncthreads();
+        if (shift == 0) break;
+        lim = (1u << shift) - 1u;
+        shift = max(0, shift - 10);
+    }
+    // tau = base; need entries equal to tau are taken, the lowest indices first
+    uint32_t gt = 0, eq = 0;
+    for_keys([&](int, uint32_t x) { gt += x > base; eq += x == base; });
+    uint32_t tot;
+    const uint32_t eq0 = block_scan(eq, red, &tot);
+    const uint32_t mine = gt + min(eq, need > eq0 ? need - eq0 : 0u);
+    uint32_t o = block_scan(mine, red, &tot);
+    uint32_t e = eq0;
+    for_keys([&](int s, uint32_t x) {
+        const bool sel = x > base || (x == base && (e++) < need);
+        if (sel && o < (uint32_t)topk) out[o++] = s;
+    });
+}
+
+__global__ __launch_bounds__(256) void k_pfb_score(
+    const uint32_t* __restrict__ fail, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint16_t* __restrict__ k_idx, int Tq, int Nc, long long L, int m, long long pos0, uint32_t* __restrict__ keys,
+    size_t NcP)
+{
+    const uint32_t nf = min(fail[0], (uint32_t)FB_SLOTS);
+    const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = gridDim.x * 4;
+    for (uint32_t fi = 0; fi < nf; ++fi) {
+        const int r = (int)fail[1 + fi], b = r / Tq, t = r % Tq;
+        const int nv = n_visible(pos0 + t, L, m, Nc);
+        fb_score_entries(r, b, nv, gw, nw, q_idx, w_idx, k_idx, Nc, keys + (size_t)fi * NcP);
+    }
+}
+
+__global__ __launch_bounds__(FB_TPB) void k_pfb_select(
+    const uint32_t* __restrict__ fail, int Tq, int Nc, long long L, int m, long long pos0, int topk,
+    const uint32_t* __restrict__ keys, size_t NcP, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
+{
+    __shared__ __align__(16) uint32_t h[1024];
+    __shared__ uint32_t red[2 * (FB_TPB / 64)];
+    const uint32_t fi = blockIdx.x;
+    if (fi >= min(fail[0], (uint32_t)FB_SLOTS)) return;
+    const int r = (int)fail[1 + fi], t = r % Tq;
+    const int nv = n_visible(pos0 + t, L, m, Nc);
+    fb_select_row(keys + (size_t)fi * NcP, nv, topk, idx_out + (size_t)r * topk, h, red);
+    if (cnt_out && threadIdx.x == 0) cnt_out[r] = topk;
+}
+
+__global__ __launch_bounds__(FB_TPB) void k_pfallback(
+    const uint32_t* __restrict__ fail, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint16_t* __restrict__ k_idx, int Tq, int Nc, long long L, int m, long long pos0, int topk,
+    uint32_t* __restrict__ keys, size_t NcP, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
+{
+    __shared__ __align__(16) uint32_t h[1024];
+    __shared__ uint32_t red[2 * (FB_TPB / 64)];
+    const uint32_t nf = fail[0];
+    uint32_t* K = keys + (size_t)blockIdx.x * NcP;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (uint32_t fi = FB_SLOTS + blockIdx.x; fi < nf; fi += gridDim.x) {
+        const int r = (int)fail[1 + fi], b = r / Tq, t = r % Tq;
+        const int nv = n_visible(pos0 + t, L, m, Nc);
+        fb_score_entries(r, b, nv, wave, FB_TPB / 64, q_idx, w_idx, k_idx, Nc, K);
+        __threadfence_block();
+        __syncthreads();
+        fb_select_row(K, nv, topk, idx_out + (size_t)r * topk, h, red);
+        if (cnt_out && threadIdx.x == 0) cnt_out[r] = topk;
+        __syncthreads();                               // K is reused by the next row
+    }
+}
+
+// clears the Kmax accumulators [n] and the fallback row count
+__global__ void k_pzero(uint32_t* p, int n, uint32_t* fail) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0;
+    if (i == 0) fail[0] = 0;
 }
 
 }  // namespace
@@ -889,12 +1190,12 @@ bool prefill_index_applicable(int dtype, int HI, int dI, int B, int Tq, int Nc, 
 }
 
 // kmax [B] | fail [1 + R] | wq [R] | thr [R] | samp [R][NSP] u16 | cnt [R][nsplit1] | cand [R][nsplit1][caps]
-// | fallback keys [FB_SLOTS][NcP] u64
+// | fallback score keys [FB_SLOTS][NcP] u32
 size_t prefill_index_ws_bytes(int B, int Tq, int Nc) {
     const PrefillPlan P = prefill_plan(B, Tq, Nc);
     return align256((size_t)B * 4) + align256((P.R + 1) * 4) + align256(P.R * 4) + align256(P.R * 4) +
            align256(P.R * P.NSP * 2) + align256(P.R * P.nsplit1 * 4) + align256(P.R * P.nsplit1 * P.caps * 8) +
-           align256((size_t)FB_SLOTS * P.NcP * 8);
+           align256((size_t)FB_SLOTS * P.NcP * 4);
 }
 
 int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_idx, int B, int Tq, int Nc,
@@ -909,12 +1210,11 @@ int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_id
     uint16_t* samp = (uint16_t*)p;          p += align256(P.R * P.NSP * 2);
     uint32_t* cnt = (uint32_t*)p;           p += align256(P.R * P.nsplit1 * 4);
     uint2* cand = (uint2*)p;                p += align256(P.R * P.nsplit1 * P.caps * 8);
-    unsigned long long* fbk = (unsigned long long*)p;
+    uint32_t* fbk = (uint32_t*)p;
     const uint16_t* q = (const uint16_t*)q_idx;
     const uint16_t* k = (const uint16_t*)k_idx;
 
-    CSA_LAUNCH("k_pzero", k_pzero, dim3((B + 255) / 256), dim3(256), 0, st, kmax, B);
-    CSA_LAUNCH("k_pzero", k_pzero, dim3(1), dim3(64), 0, st, fail, 1);
+    CSA_LAUNCH("k_pzero", k_pzero, dim3((B + 255) / 256), dim3(256), 0, st, kmax, B, fail);
     {
         const long long nb = ((long long)B * Nc + NORM_KEYS_PER_BLOCK - 1) / NORM_KEYS_PER_BLOCK + ((long long)P.R + 3) / 4;
         CSA_LAUNCH("k_pnorm", k_pnorm, dim3((unsigned)nb), dim3(256), 0, st, q, w_idx, k, B, Nc,
@@ -933,6 +1233,10 @@ int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_id
     CSA_LAUNCH("k_pselect", k_pselect, dim3((unsigned)((P.R + SW_ROWS - 1) / SW_ROWS)), dim3(64 * SW_ROWS), 0, st, cand,
                cnt, thr, wq, kmax, q, w_idx, k, Tq, Nc, L, m, pos0, topk, P.nsplit1, P.caps, (int)P.R, idx_out, cnt_out,
                fail);
+    CSA_LAUNCH("k_pfb_score", k_pfb_score, dim3(FB_CH), dim3(256), 0, st, fail, q, w_idx, k, Tq, Nc, L, m, pos0, fbk,
+               P.NcP);
+    CSA_LAUNCH("k_pfb_select", k_pfb_select, dim3(FB_SLOTS), dim3(FB_TPB), 0, st, fail, Tq, Nc, L, m, pos0, topk, fbk,
+               P.NcP, idx_out, cnt_out);
     CSA_LAUNCH("k_pfallback", k_pfallback, dim3(FB_SLOTS), dim3(FB_TPB), 0, st, fail, q, w_idx, k, Tq, Nc, L, m,
                pos0, topk, fbk, P.NcP, idx_out, cnt_out);
     return 0;

@@ -231,16 +231,64 @@ def test_index_topk_many_queries_exact_ties(b):
     assert np.array_equal(got_idx, want_idx)
 
 
-@pytest.mark.parametrize("Nc", [3000, 5000])
-def test_index_topk_many_queries_all_equal_scores(b, Nc):
+@pytest.mark.parametrize("Nc,Tq", [(3000, 64), (5000, 128)])
+def test_index_topk_many_queries_all_equal_scores(b, Nc, Tq):
     # every score identical: the band holds every entry (3000) or the list overflows its capacity
-    # (5000); both rows go to the exact fallback, which keeps the lowest indices
-    B, Tq, HI, dI, m, topk = 1, 64, 8, 128, 4, 50
+    # (5000); every row goes to the exact fallback, which keeps the lowest indices (with 128 rows,
+    # the rows past the fallback's 64 slots take its overflow kernel)
+    B, HI, dI, m, topk = 1, 8, 128, 4, 50
     q, w, k, _ = synth.indexer_inputs(23, B, Tq, HI, dI, Nc, 0)
     k = np.repeat(k[:, :1], Nc, axis=1)
     got_idx, got_cnt = run_index(b, q, w, k, Nc * m, m, Nc * m - Tq, topk, 0)
     assert (got_cnt == topk).all()
     assert (got_idx == np.arange(topk)[None, None, :]).all()
+
+
+def test_index_topk_many_queries_fallback_distinct(b):
+    # one key row scaled by 2^16 inflates every row's bound on the contraction error, so that the
+    # certified path hands (nearly) every row, with distinct scores, to the exact fallback; 96 rows
+    # cover both its slots and its overflow kernel
+    B, Tq, HI, dI, m, topk = 1, 96, 8, 128, 4, 64
+    Nc = 3000
+    q, w, k, _ = synth.indexer_inputs(25, B, Tq, HI, dI, Nc, 0)
+    k = k.copy()
+    row = k[0, 1234].astype(np.uint32)
+    expo = (row >> 7) & 0xFF
+    k[0, 1234] = np.where((expo > 0) & (expo < 200), row + (16 << 7), row).astype(np.uint16)
+    want_idx, _, _, _ = oracle.index_topk(q, w, k, Nc * m, m, Nc * m - Tq, topk)
+    got_idx, _ = run_index(b, q, w, k, Nc * m, m, Nc * m - Tq, topk, 0)
+    bad = np.nonzero((got_idx != want_idx).any(axis=-1))
+    assert len(bad[0]) == 0, f"{len(bad[0])} rows differ, first {bad[1][:5]}"
+
+
+@pytest.mark.parametrize("fallback", [False, True])
+def test_index_topk_many_queries_rounding_tie(b, fallback):
+    # head dots whose products span 60 binades: 1 + 2^-24 + 2^-60 must round up to 1 + 2^-23 (a
+    # plain fp64 sum lands on the halfway point and rounds to even, 1.0); it then ties with an entry
+    # at 1 + 2^-23 exactly and wins by its lower index, while 1 + 2^-24 - 2^-60 rounds down.  With
+    # fallback=True a key scaled to 2^16 widens every row's error bound so far that the rows go to
+    # the exact fallback, which scores the same entries.
+    B, Tq, HI, dI, m, Nc = 1, 64, 8, 128, 4, 256
+    qf = np.zeros((B, Tq, HI, dI), np.float32)
+    qf[:, :, 0, :4] = [1.0, 2.0 ** -12, 2.0 ** -30, 1.0]
+    w = np.zeros((B, Tq, HI), np.float32)
+    w[:, :, 0] = 1.0
+    g = np.random.default_rng(3)
+    kf = np.zeros((B, Nc, dI), np.float32)
+    kf[:, :, :4] = g.standard_normal((B, Nc, 4)).astype(np.float32) * np.float32(2.0 ** -10)
+    kf[0, 100, :4] = [1.0, 0.0, 0.0, 2.0 ** -23]
+    kf[0, 50, :4] = [1.0, 2.0 ** -12, 2.0 ** -30, 0.0]
+    kf[0, 30, :4] = [1.0, 2.0 ** -12, -(2.0 ** -30), 0.0]
+    topk = 2
+    if fallback:
+        kf[0, 200, :4] = [2.0 ** 16, 0.0, 0.0, 0.0]
+        topk = 3
+    q, k = synth.to_bf16_bits(qf), synth.to_bf16_bits(kf)
+    L = Nc * m
+    want_idx, _, _, _ = oracle.index_topk(q, w, k, L, m, L - Tq, topk)
+    assert (want_idx[0] == ([50, 100, 200] if fallback else [50, 100])).all()
+    got_idx, _ = run_index(b, q, w, k, L, m, L - Tq, topk, 0)
+    assert np.array_equal(got_idx, want_idx)
 
 
 def test_index_topk_many_queries_prefill_size_sampled(b):
