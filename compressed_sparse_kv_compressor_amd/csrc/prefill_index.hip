@@ -223,12 +223,16 @@ __device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], con
     int ntiles = ke > kb ? (ke - kb + P_TK - 1) / P_TK : 0;
     if (MODE == 1 && nvl <= A.topk) ntiles = 0;                       // no row of the block selects
 
-    // ---- A operands (rows 8 j + h of block a = head h of query qw + 4a + j) and head weights ----
+    // ---- A operands and head weights ----
+    // Row 8 j + 4 g + i of block a (j, i = 0..3, g = 0, 1) is head 4 (j % 2) + i of query qw + 4a + 2g + j/2,
+    // so that accumulator register r = 4 j + i of a lane in half g (which holds row 8 j + 4 g + i) covers
+    // all eight heads of queries 4a + 2g (registers 0-7) and 4a + 2g + 1 (registers 8-15): the head sum
+    // stays within the lane.
     bf16x8_t qa[P_NA][8];
-    float wv[P_NA][16];                       // register r of block a: query qw + 4a + r/4, head 4 g2 + r%4
+    float wv[P_NA][16];                       // register r of block a: query qw + 4a + 2 g2 + r/8, head 4 (r/4 % 2) + r%4
 #pragma unroll
     for (int a = 0; a < P_NA; ++a) {
-        const int t = qw + 4 * a + (r32 >> 3), h = r32 & 7;
+        const int t = qw + 4 * a + 2 * ((r32 >> 2) & 1) + (r32 >> 4), h = 4 * ((r32 >> 3) & 1) + (r32 & 3);
         const bool v = t < Tq;
         const uint16_t* qp = A.q_idx + (((size_t)b * Tq + (v ? t : 0)) * P_HI + h) * P_DI + 8 * g2;
 #pragma unroll
@@ -236,8 +240,8 @@ __device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], con
             qa[a][s] = as_bf16x8(v ? *(const u32x4_t*)(qp + 16 * s) : u32x4_t{0u, 0u, 0u, 0u});
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int tw = qw + 4 * a + r / 4;
-            wv[a][r] = tw < Tq ? A.w_idx[((size_t)b * Tq + tw) * P_HI + 4 * g2 + r % 4] : 0.f;
+            const int tw = qw + 4 * a + 2 * g2 + r / 8;
+            wv[a][r] = tw < Tq ? A.w_idx[((size_t)b * Tq + tw) * P_HI + 4 * ((r / 4) % 2) + r % 4] : 0.f;
         }
     }
     // ---- per-query state (wave-uniform): local query lq = 0..7 is query qw + lq ----
@@ -298,18 +302,14 @@ __device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], con
     auto relu = [](float x) { return __int_as_float(max(__float_as_int(x), 0)); };
     // S~ of one block: va = query 4a (lanes 0-31) / 4a + 2 (lanes 32-63), vb = 4a + 1 / 4a + 3, at key r32
     auto block_scores = [&](const f32x16_t& acc, const float (&wb)[16], float& va, float& vb) {
-        float p[4];
+        float x = 0.f, y = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float x = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x = fmaf(wb[4 * j + i], relu(acc[4 * j + i]), x);
-            p[j] = x;
+        for (int r = 0; r < 8; ++r) {
+            x = fmaf(wb[r], relu(acc[r]), x);
+            y = fmaf(wb[8 + r], relu(acc[8 + r]), y);
         }
-        const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
-        const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
-        va = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
-        vb = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+        va = x;
+        vb = y;
     };
     // one query's 64 keys (lane = key - kbase): sample store or list append
     auto emit = [&](float v, int lq, int kk, bool live, auto full_tag) {
