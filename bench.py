@@ -78,6 +78,8 @@ def main():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20, help="timed calls of the prefill indexer leg (0: skip)")
+    ap.add_argument("--compress-steps", type=int, default=10,
+                    help="timed calls of the compression + decode-stack leg (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run two plain device copies of MIB MiB (a kernel of known "
                          "traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE by)")
@@ -210,6 +212,8 @@ def main():
     torch.cuda.empty_cache()
     if args.prefill_steps > 0:
         out["indexer_prefill"] = prefill_leg(args, dev, cpu=not args.no_cpu_baseline)
+    if args.compress_steps > 0:
+        out["compress_stack"] = compress_leg(args, dev, cpu=not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)
 
 
@@ -286,6 +290,179 @@ def prefill_leg(args, dev, cpu=True):
     torch.cuda.empty_cache()
     res["sparse_attn"] = prefill_attn_leg(args, dev, pc, idx)
     return res
+
+
+COMPRESS_KERNELS = ("k_pool2", "k_pool", "k_gemm2", "k_g2reduce", "k_gemm", "k_fill", "k_score", "k_collect", "k_select", "k_attn_pair", "k_attn_sparse",
+                    "k_attn_dense", "k_combine")
+
+
+def compress_leg(args, dev, cpu=True):
+    """Compression of 4 x 64K tokens of hidden 4096 into the CSA (m = 4, indexer keys, window) and HCA
+    (m' = 128) caches, then a CSA, HCA, CSA, HCA stack of one-token decodes against them."""
+    import numpy as np
+    import torch
+
+    from compressed_sparse_kv_compressor_amd import binding as b
+    from compressed_sparse_kv_compressor_amd import synth
+    from compressed_sparse_kv_compressor_amd.configs import COMPRESS_B4_64K as cc
+
+    B, L, Dh, D, dI, HI, m, mh, W, H, topk = cc.B, cc.L, cc.Dh, cc.D, cc.dI, cc.HI, cc.m, cc.mh, cc.W, cc.H, cc.topk
+    Nc, Nh = -(-L // m), -(-L // mh)
+    t0 = time.time()
+    X = synth.parallel_bits_to_device(0, "c5_hidden", (B, L, Dh), 1.0, 0, dev, heavy=True)
+    tod = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    wkv, wik, gate, bslot = (tod(a) for a in synth.compress_weights(0, Dh, D, dI, m, prefix="c5_csa_"))
+    hw = synth.compress_weights(0, Dh, D, 0, mh, prefix="c5_hca_")
+    wkv_h, gate_h, bslot_h = tod(hw[0]), tod(hw[2]), tod(hw[3])
+    gen_s = time.time() - t0
+    kv = torch.empty((B, Nc, D), dtype=torch.int16, device=dev)
+    ik = torch.empty((B, Nc, dI), dtype=torch.int16, device=dev)
+    win = torch.empty((B, W, D), dtype=torch.int16, device=dev)
+    kv_h = torch.empty((B, Nh, D), dtype=torch.int16, device=dev)
+    ws = b.workspace(b.lib.csa_hca_compress_ws_bytes(B, L, Dh, D, dI, m, W, mh), dev)
+    stream = torch.cuda.current_stream()
+
+    def compress():
+        b.csa_hca_compress(X, wkv, wik, gate, bslot, m, W, kv, ik, win, wkv_h, gate_h, bslot_h, mh, kv_h,
+                           ik_dtype=0, ws=ws, stream=stream)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def breakdown(fn, n):
+        b.prof_reset()
+        b.prof_only(None)
+        b.prof_enable(True)
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        b.prof_enable(False)
+        kern = {}
+        for name in COMPRESS_KERNELS:
+            t, k = b.prof_read(name)
+            if k:
+                kern[name] = {"us_per_call": round(t / n * 1000.0, 2), "launches_per_call": k // n}
+        b.prof_reset()
+        return kern
+
+    ms_c = timed(compress, args.compress_steps)
+    kern_c = breakdown(compress, min(args.compress_steps, 5))
+    x_bytes = B * L * Dh * 2
+    w_bytes = (2 * D + dI) * Dh * 2 + 2 * Dh * 4
+    o_bytes = (B * Nc * (D + dI) + B * W * D + B * Nh * D) * 2
+    c_bytes = x_bytes + w_bytes + o_bytes                      # hidden read once for both caches
+    c_flops = 2.0 * 2 * Dh * B * L + 2.0 * Dh * (B * Nc * (D + dI) + B * Nh * D + B * W * D)
+    pool = kern_c.get("k_pool2")
+    pooled_bytes = (B * Nc + B * Nh) * Dh * 2
+    res = {
+        "workload": cc.name, "B": B, "L": L, "Dh": Dh, "D": D, "dI": dI, "m": m, "mh": mh, "W": W,
+        "hidden": "N(0,1) with 1% Student-t(3), bf16", "input_gen_s": round(gen_s, 1),
+        "compress": {
+            "calls": args.compress_steps, "ms_per_call": round(ms_c, 4),
+            "algorithmic_bytes": c_bytes, "algorithmic_flops": c_flops,
+            "GBps": round(c_bytes / (ms_c * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(c_bytes / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "kernel_us_breakdown": kern_c,
+            "roofline": {"bound": "hbm", "kernel": "k_pool2",
+                         "achieved": round((x_bytes + pooled_bytes) / (pool["us_per_call"] * 1e-6) / 1e9, 1)
+                         if pool else None,
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "algorithmic_bytes_per_launch": x_bytes + pooled_bytes,
+                         "note": "one pass over the hidden rows pools both caches; bytes = hidden read once + "
+                                 "pooled rows written once"},
+        },
+    }
+    if cpu:
+        res["compress"]["parity_sample"] = compress_parity(cc, X, (wkv, wik, gate, bslot), (wkv_h, gate_h, bslot_h),
+                                                           kv, ik, win, kv_h)
+
+    # the decode stack: CSA, HCA, CSA, HCA (two fused pairs), one query per sequence, against the caches
+    g = synth.parallel_bits_to_device
+    pairs = []
+    for layer in range(cc.layers // 2):
+        pf = f"c5_l{layer}_"
+        pq = dict(
+            q_idx=g(0, pf + "q_idx", (B, 1, HI, dI), dI ** -0.5, 0, dev, heavy=True),
+            csa_q=g(0, pf + "csa_q", (B, H, D), D ** -0.5, 0, dev, heavy=True),
+            hca_q=g(0, pf + "hca_q", (B, H, D), D ** -0.5, 0, dev, heavy=True),
+            w_idx=torch.from_numpy(synth.half_normal_f32(0, pf + "w_idx", (B, 1, HI), HI ** -0.5)).to(dev),
+            csa_out=torch.empty((B, H, D), dtype=torch.int16, device=dev),
+            hca_out=torch.empty((B, H, D), dtype=torch.int16, device=dev),
+            idx=torch.empty((B, topk), dtype=torch.int32, device=dev))
+        pq["args"] = b.make_decode_args(L=L, scale=D ** -0.5, csa_q=pq["csa_q"], q_idx=pq["q_idx"], w_idx=pq["w_idx"],
+                                        k_idx=ik, kv=kv, kv_raw=win, idx_dtype=0, m=m, topk=topk, W=W,
+                                        csa_out=pq["csa_out"], hca_q=pq["hca_q"], kv_h=kv_h, mh=mh,
+                                        hca_out=pq["hca_out"], idx_out=pq["idx"])
+        pairs.append(pq)
+    dws = b.workspace(max(b.csa_hca_decode_ws_bytes(p["args"]) for p in pairs), dev)
+
+    def stack():
+        for p in pairs:
+            b.csa_hca_decode(p["args"], ws=dws, stream=stream)
+
+    steps = max(10, 10 * args.compress_steps)
+    ms_s = timed(stack, steps)
+    kern_s = breakdown(stack, min(steps, 20))
+    s_bytes = 0
+    for _ in pairs:
+        s_bytes += B * Nc * dI * 2 + B * HI * (dI * 2 + 4) + B * (topk + W) * D * 2 + B * Nh * D * 2 + 4 * B * H * D * 2
+    res["decode_stack"] = {
+        "layers": cc.layers, "H": H, "topk": topk, "idx_dtype": "bf16", "calls": steps,
+        "us_per_stack": round(ms_s * 1e3, 2), "queries_per_s": round(B / (ms_s * 1e-3), 1),
+        "algorithmic_bytes": s_bytes, "GBps": round(s_bytes / (ms_s * 1e-3) / 1e9, 1),
+        "kernel_us_breakdown": kern_s,
+    }
+    del X, kv, ik, win, kv_h, ws, dws, pairs
+    torch.cuda.empty_cache()
+    return res
+
+
+def compress_parity(cc, X, wc, wh, kv, ik, win, kv_h):
+    """Oracle check of a few compressed rows of sequence 0 (CSA entries 0-1 and the last, the first HCA
+    entry, the window rows): max row-relative error against the 2e-2 bar."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    host = lambda t: t.cpu().numpy().view(np.uint16) if t.dtype == torch.int16 else t.cpu().numpy()
+    m, mh, W, L = cc.m, cc.mh, cc.W, cc.L
+    Nc = -(-L // m)
+    wkv, wik, gate, bslot = (host(t) for t in wc)
+    wkv_h, gate_h, bslot_h = (host(t) for t in wh)
+
+    def bf(t):
+        return (t.cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    def rel(got, want):
+        got = got.reshape(-1, want.shape[-1])
+        want = want.reshape(-1, want.shape[-1])
+        return float((np.abs(got - want).max(1) / np.abs(want).max(1)).max())
+
+    err = {}
+    t0 = time.perf_counter()
+    for j in (0, 1, Nc - 1):
+        xs = host(X[0:1, j * m:(j + 1) * m])
+        okv, oik, _ = oracle.compress(xs, wkv, wik, gate, bslot, m)
+        err[f"csa_kv_{j}"] = rel(bf(kv[0, j]), okv)
+        err[f"csa_ik_{j}"] = rel(bf(ik[0, j]), oik)
+    xs = host(X[0:1, 0:mh])
+    okh, _, _ = oracle.compress(xs, wkv_h, None, gate_h, bslot_h, mh)
+    err["hca_kv_0"] = rel(bf(kv_h[0, 0]), okh)
+    xs = host(X[0:1, L - W:L])
+    _, _, ow = oracle.compress(xs, wkv, None, gate, bslot, m, W=W)
+    err["window"] = rel(bf(win[0]), ow)
+    return {"max_row_rel_err": err, "tolerance": 2e-2, "ok": bool(max(err.values()) <= 2e-2),
+            "oracle_s": round(time.perf_counter() - t0, 2)}
 
 
 def prefill_attn_leg(args, dev, pc, idx):

@@ -32,8 +32,10 @@ def _load():
         "csa_abi_version": ([], I),
         "csa_status_str": ([I], ctypes.c_char_p),
         "csa_last_error": ([], ctypes.c_char_p),
-        "csa_compress_ws_bytes": ([I, LL, I, I], Z),
+        "csa_compress_ws_bytes": ([I, LL, I, I, I, I, I], Z),
         "csa_compress": ([P, P, P, P, P, I, LL, I, I, I, I, I, I, P, P, P, P, Z, P], I),
+        "csa_hca_compress_ws_bytes": ([I, LL, I, I, I, I, I, I], Z),
+        "csa_hca_compress": ([P, I, LL, I, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, I, P, P, Z, P], I),
         "csa_index_topk_ws_bytes": ([I, I, I, I, I, I, I], Z),
         "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, Z, P], I),
         "csa_sparse_attn_ws_bytes": ([I, I, I, I, I, I], Z),
@@ -58,6 +60,7 @@ def _load():
 lib = _load()
 
 EXPORTED = ("csa_abi_version", "csa_status_str", "csa_last_error", "csa_compress_ws_bytes", "csa_compress",
+            "csa_hca_compress_ws_bytes", "csa_hca_compress",
             "csa_index_topk_ws_bytes", "csa_index_topk", "csa_sparse_attn_ws_bytes", "csa_sparse_attn",
             "hca_dense_attn_ws_bytes", "hca_dense_attn", "csa_hca_decode_ws_bytes", "csa_hca_decode",
             "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read",
@@ -109,12 +112,26 @@ def csa_compress(hidden, w_kv, w_ik, w_gate, b_slot, m: int, W: int, kv_out, ik_
     B, L, Dh = hidden.shape
     D = w_kv.shape[0]
     dI = w_ik.shape[0] if w_ik is not None else 0
-    need = lib.csa_compress_ws_bytes(B, L, Dh, m)
+    need = lib.csa_compress_ws_bytes(B, L, Dh, D, dI if ik_out is not None else 0, m, W if win_out is not None else 0)
     if ws is None:
         ws = workspace(need, hidden.device)
     _check(lib.csa_compress(_p(hidden), _p(w_kv), _p(w_ik), _p(w_gate), _p(b_slot), B, L, Dh, D, dI, m, W, ik_dtype,
                             _p(kv_out), _p(ik_out), _p(win_out), _p(ws), 0 if ws is None else ws.numel(),
                             _stream(stream)))
+
+
+def csa_hca_compress(hidden, w_kv, w_ik, w_gate, b_slot, m: int, W: int, kv_out, ik_out, win_out, w_kv_h, w_gate_h,
+                     b_slot_h, mh: int, kv_h_out, ik_dtype: int = BF16, ws=None, stream=None):
+    B, L, Dh = hidden.shape
+    D = w_kv.shape[0]
+    dI = w_ik.shape[0] if w_ik is not None else 0
+    need = lib.csa_hca_compress_ws_bytes(B, L, Dh, D, dI if ik_out is not None else 0, m,
+                                         W if win_out is not None else 0, mh)
+    if ws is None:
+        ws = workspace(need, hidden.device)
+    _check(lib.csa_hca_compress(_p(hidden), B, L, Dh, _p(w_kv), _p(w_ik), _p(w_gate), _p(b_slot), D, dI, m, W,
+                                ik_dtype, _p(kv_out), _p(ik_out), _p(win_out), _p(w_kv_h), _p(w_gate_h), _p(b_slot_h),
+                                mh, _p(kv_h_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def csa_index_topk(q_idx, w_idx, k_idx, dtype: int, L: int, m: int, pos0: int, topk: int, idx_out, cnt_out=None,

@@ -197,9 +197,9 @@ const char* csa_status_str(int s) {
 
 const char* csa_last_error(void) { return csa_host::g_err; }
 
-size_t csa_compress_ws_bytes(int B, long long L, int Dh, int m) {
-    if (B < 1 || L < 1 || Dh < 1 || m < 1) return 0;
-    return csa_host::compress_ws_bytes(B, L, Dh, m);
+size_t csa_compress_ws_bytes(int B, long long L, int Dh, int D, int dI, int m, int W) {
+    if (B < 1 || L < 1 || Dh < 1 || D < 1 || dI < 0 || m < 1 || W < 0) return 0;
+    return csa_host::compress_ws_bytes(B, L, Dh, D, dI, m, W);
 }
 
 int csa_compress(const void* hidden, const void* w_kv, const void* w_ik, const float* w_gate, const float* b_slot,
@@ -226,10 +226,53 @@ int csa_compress(const void* hidden, const void* w_kv, const void* w_ik, const f
         REQ(dI == 64 || dI == 128 || dI == 256 || dI == 512, CSA_ERR_UNSUPPORTED, "%s: dI=%d unsupported", fn, dI);
     }
     if (W > 0) REQ(win_out != nullptr, CSA_ERR_NULL, "%s: win_out is NULL but W > 0", fn);
-    int rc = check_ws(fn, ws, ws_bytes, csa_host::compress_ws_bytes(B, L, Dh, m));
+    int rc = check_ws(fn, ws, ws_bytes, csa_host::compress_ws_bytes(B, L, Dh, D, (w_ik && ik_out) ? dI : 0, m,
+                                                                 win_out ? W : 0));
     if (rc) return rc;
     return csa_host::compress_launch(hidden, w_kv, w_ik, w_gate, b_slot, B, L, Dh, D, dI, m, W, ik_dtype, kv_out,
                                      ik_out, W > 0 ? win_out : nullptr, ws, (hipStream_t)stream);
+}
+
+size_t csa_hca_compress_ws_bytes(int B, long long L, int Dh, int D, int dI, int m, int W, int mh) {
+    if (B < 1 || L < 1 || Dh < 1 || D < 1 || dI < 0 || m < 1 || W < 0 || mh < 1) return 0;
+    return csa_host::hca_compress_ws_bytes(B, L, Dh, D, dI, m, W, mh);
+}
+
+int csa_hca_compress(const void* hidden, int B, long long L, int Dh, const void* w_kv, const void* w_ik,
+                     const float* w_gate, const float* b_slot, int D, int dI, int m, int W, int ik_dtype, void* kv_out,
+                     void* ik_out, void* win_out, const void* w_kv_h, const float* w_gate_h, const float* b_slot_h,
+                     int mh, void* kv_h_out, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa_hca_compress";
+    csa_host::g_err[0] = 0;
+    REQ_PTR(hidden);
+    REQ_PTR(w_kv);
+    REQ_PTR(w_gate);
+    REQ_PTR(kv_out);
+    REQ_PTR(w_kv_h);
+    REQ_PTR(w_gate_h);
+    REQ_PTR(kv_h_out);
+    OPT_PTR(w_ik);
+    OPT_PTR(b_slot);
+    OPT_PTR(ik_out);
+    OPT_PTR(win_out);
+    OPT_PTR(b_slot_h);
+    REQ(B >= 1 && L >= 1 && m >= 1 && mh >= 1 && W >= 0, CSA_ERR_SHAPE, "%s: need B, L, m, mh >= 1 and W >= 0", fn);
+    REQ(ik_dtype == CSA_BF16 || ik_dtype == CSA_E4M3, CSA_ERR_DTYPE, "%s: ik_dtype %d unknown", fn, ik_dtype);
+    REQ(Dh % 64 == 0 && Dh >= 64 && Dh <= 16384, CSA_ERR_UNSUPPORTED, "%s: Dh=%d (multiple of 64 in [64,16384])", fn, Dh);
+    REQ(D == 64 || D == 128 || D == 256 || D == 512, CSA_ERR_UNSUPPORTED, "%s: D=%d unsupported", fn, D);
+    REQ(m <= 1024 && mh <= 1024 && W <= 1024, CSA_ERR_UNSUPPORTED, "%s: m, mh <= 1024 and W <= 1024 supported", fn);
+    REQ((L + m - 1) / m <= (1LL << 24) && (long long)B * L * Dh < (1LL << 40), CSA_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+    if (w_ik || ik_out) {
+        REQ(w_ik && ik_out, CSA_ERR_NULL, "%s: w_ik and ik_out must both be given or both be NULL", fn);
+        REQ(dI == 64 || dI == 128 || dI == 256 || dI == 512, CSA_ERR_UNSUPPORTED, "%s: dI=%d unsupported", fn, dI);
+    }
+    if (W > 0) REQ(win_out != nullptr, CSA_ERR_NULL, "%s: win_out is NULL but W > 0", fn);
+    int rc = check_ws(fn, ws, ws_bytes, csa_host::hca_compress_ws_bytes(B, L, Dh, D, (w_ik && ik_out) ? dI : 0, m,
+                                                                     win_out ? W : 0, mh));
+    if (rc) return rc;
+    return csa_host::hca_compress_launch(hidden, w_kv, w_ik, w_gate, b_slot, B, L, Dh, D, dI, m, W, ik_dtype, kv_out,
+                                         ik_out, W > 0 ? win_out : nullptr, w_kv_h, w_gate_h, b_slot_h, mh, kv_h_out,
+                                         ws, (hipStream_t)stream);
 }
 
 size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype) {

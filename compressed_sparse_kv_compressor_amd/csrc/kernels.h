@@ -45,7 +45,12 @@ int attn_pair_launch(const void* q_s, const AttnRows& as, void* out_s, float* ls
                      const AttnRows& ad, void* out_d, float* lse_d, int B, int H, int D, long long pos0, float scale,
                      void* ws, hipStream_t st);
 
-size_t compress_ws_bytes(int B, long long L, int Dh, int m);
+size_t compress_ws_bytes(int B, long long L, int Dh, int D, int dI, int m, int W);
+size_t hca_compress_ws_bytes(int B, long long L, int Dh, int D, int dI, int m, int W, int mh);
+int hca_compress_launch(const void* hidden, const void* w_kv, const void* w_ik, const float* w_gate,
+                        const float* b_slot, int B, long long L, int Dh, int D, int dI, int m, int W, int ik_dtype,
+                        void* kv_out, void* ik_out, void* win_out, const void* w_kv_h, const float* w_gate_h,
+                        const float* b_slot_h, int mh, void* kv_h_out, void* ws, hipStream_t st);
 int compress_launch(const void* hidden, const void* w_kv, const void* w_ik, const float* w_gate,
                     const float* b_slot, int B, long long L, int Dh, int D, int dI, int m, int W,
                     int ik_dtype, void* kv_out, void* ik_out, void* win_out, void* ws, hipStream_t st);

@@ -114,6 +114,14 @@ def attn_inputs(seed, B, Tq, H, D, Nrows, prefix, heavy=False):
     return q, rows
 
 
+def compress_weights(seed, Dh, D, dI, m, gate_scale=1.0, prefix=""):
+    """The weights of compress_inputs alone (same streams): w_kv, w_ik (or None), w_gate, b_slot."""
+    wkv = to_bf16_bits(normal_f32(seed, prefix + "w_kv", (D, Dh), 1.0 / np.sqrt(Dh)))
+    wik = to_bf16_bits(normal_f32(seed, prefix + "w_ik", (dI, Dh), 1.0 / np.sqrt(Dh))) if dI else None
+    gate = normal_f32(seed, prefix + "w_gate", (Dh,), gate_scale / np.sqrt(Dh))
+    return wkv, wik, gate, np.zeros(m, np.float32)
+
+
 def compress_inputs(seed, B, L, Dh, D, dI, m, heavy=False, gate_scale=1.0, prefix=""):
     """hidden[B][L][Dh] bf16, w_kv[D][Dh] bf16, w_ik[dI][Dh] bf16 (or None),
     w_gate[Dh] fp32 ~ N(0,1)/sqrt(Dh) * gate_scale, b_slot[m] fp32 zeros."""
@@ -154,11 +162,12 @@ def normal_bits_to_device(seed, name, shape, scale, dtype, device, heavy=False):
     return out.view(*shape)
 
 
-def parallel_bits_to_device(seed, name, shape, scale, dtype, device, workers=8):
+def parallel_bits_to_device(seed, name, shape, scale, dtype, device, workers=8, heavy=False):
     """Like normal_bits_to_device but each 2^24-element chunk has its own
     substream (seed, crc32(name), chunk), generated by a thread pool: the large
     caches of the 1M-context workloads fill in seconds.  Values differ from the
-    single-stream generators; use the same function on both sides."""
+    single-stream generators; use the same function on both sides.  heavy: the
+    N(0,1) / Student-t(3) mixture of heavy_tail_f32 (1% t draws per chunk)."""
     import concurrent.futures as cf
     n = int(np.prod(shape))
     tdt = torch.int16 if dtype == 0 else torch.uint8
@@ -170,6 +179,11 @@ def parallel_bits_to_device(seed, name, shape, scale, dtype, device, workers=8):
         e = min(n, s + _CHUNK)
         g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), zlib.crc32(name.encode()), ci])))
         x = g.standard_normal(e - s, dtype=np.float32)
+        if heavy:
+            pick = g.random(e - s) < 0.01
+            k = int(pick.sum())
+            if k:
+                x[pick] = g.standard_t(3.0, size=k).astype(np.float32)
         x *= np.float32(scale)
         t = torch.from_numpy(x)
         return t.to(torch.bfloat16).view(torch.int16) if dtype == 0 else t.to(torch.float8_e4m3fn).view(torch.uint8)

@@ -92,12 +92,31 @@ const char* csa_last_error(void);          /* thread-local detail of the last er
  *   win_out [B][W][D] bf16 or NULL
  * Supported: Dh % 64 == 0 and 64 <= Dh <= 16384; D, dI in {64, 128, 256, 512};
  * 1 <= m <= 1024; 0 <= W <= 1024; 1 <= L; B >= 1. */
-size_t csa_compress_ws_bytes(int B, long long L, int Dh, int m);
+/* Workspace of csa_compress: pooled rows [B][N][Dh] bf16, plus fp32 split-K partial sums when a
+ * projection has too few output tiles to fill the GPU.  Pass dI = 0 when no indexer keys are
+ * requested and W = 0 when no window rows are. */
+size_t csa_compress_ws_bytes(int B, long long L, int Dh, int D, int dI, int m, int W);
 int csa_compress(const void* hidden, const void* w_kv, const void* w_ik,
                  const float* w_gate, const float* b_slot,
                  int B, long long L, int Dh, int D, int dI, int m, int W, int ik_dtype,
                  void* kv_out, void* ik_out, void* win_out,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* Both compressed caches of the same tokens in one call ([P1] 1.1: CSA and HCA side by side;
+ * [P3] item 1): the result equals csa_compress with the CSA arguments (m, indexer keys, window)
+ * followed by csa_compress(hidden, w_kv_h, NULL, w_gate_h, b_slot_h, ..., m = mh, W = 0,
+ * kv_h_out).  Where the shape allows (Dh in {1024, 2048, 4096}, m = 4, mh a multiple of 16) the
+ * hidden rows are read once for both caches; otherwise the two poolings run one after the other.
+ *   w_kv_h [D][Dh] bf16    w_gate_h [Dh] fp32    b_slot_h [mh] fp32 or NULL
+ *   kv_h_out [B][ceil(L/mh)][D] bf16
+ * Supported: as csa_compress, and 1 <= mh <= 1024.  Errors and ownership as csa_compress. */
+size_t csa_hca_compress_ws_bytes(int B, long long L, int Dh, int D, int dI, int m, int W, int mh);
+int csa_hca_compress(const void* hidden, int B, long long L, int Dh,
+                     const void* w_kv, const void* w_ik, const float* w_gate, const float* b_slot,
+                     int D, int dI, int m, int W, int ik_dtype,
+                     void* kv_out, void* ik_out, void* win_out,
+                     const void* w_kv_h, const float* w_gate_h, const float* b_slot_h, int mh, void* kv_h_out,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* A2 + A3. Lightning-Indexer scores and per-query top-k                     */

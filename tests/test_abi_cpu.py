@@ -55,7 +55,13 @@ def test_workspace_sizes_are_host_arithmetic(b):
     assert lib.csa_index_topk_ws_bytes(1, 8192, 8, 128, 65536, 1024, 1) > 8192 * 65536 * 4
     assert lib.csa_sparse_attn_ws_bytes(8, 1, 128, 512, 1024, 128) > 0
     assert lib.hca_dense_attn_ws_bytes(1, 1, 16, 128, 32) == 0          # one split: no partials
-    assert lib.csa_compress_ws_bytes(4, 65536, 4096, 4) == 4 * 16384 * 4096 * 2
+    # compression of 4 x 65536 tokens of hidden 4096: the pooled rows, plus split-K partials only for
+    # the projections with few output tiles (the window rows, the HCA entries)
+    pooled = 4 * 16384 * 4096 * 2
+    assert lib.csa_compress_ws_bytes(4, 65536, 4096, 512, 128, 4, 0) == pooled
+    assert pooled < lib.csa_compress_ws_bytes(4, 65536, 4096, 512, 128, 4, 128) <= pooled + (64 << 20)
+    assert lib.csa_compress_ws_bytes(4, 65536, 4096, 512, 0, 128, 0) > 4 * 512 * 4096 * 2
+    assert lib.csa_compress_ws_bytes(4, 65536, 4096, 512, 0, 0, 0) == 0
 
 
 A16 = ctypes.c_void_p(16 * 1000)       # aligned, never dereferenced (validation fails first)

@@ -429,6 +429,9 @@ COMPRESS_CASES = [
     (2, 1000, 512, 512, 128, 4, 100, 1, 4.0, True),       # ragged tail, e4m3 keys, heavy tails
     (1, 300, 256, 256, 64, 7, 300, 0, 8.0, False),        # odd ratio; window = whole sequence
     (1, 50, 128, 64, 0, 1, 64, 0, 1.0, False),            # ratio 1, L < W
+    (1, 1003, 4096, 512, 128, 4, 128, 0, 1.0, True),      # hidden 4096 (streaming pool), ragged tail
+    (2, 777, 2048, 256, 64, 2, 32, 0, 2.0, False),        # ratio 2, hidden 2048
+    (1, 2000, 4096, 512, 0, 64, 0, 0, 1.0, True),         # coarse ratio 64 (streaming pool), ragged tail
 ]
 
 
@@ -459,6 +462,53 @@ def test_compress_parity(b, case):
             # e4m3 keeps 3 mantissa bits: allow its half-step on top of the 2e-2 row bar
             bound = 0.0625 * np.abs(o) + TOL * np.abs(o).max(axis=1, keepdims=True) + 2.0 ** -10
             assert np.all(np.abs(g - o) <= bound)
+
+
+HCA_COMPRESS_CASES = [
+    # (B, L, Dh, D, dI, m, W, mh, heavy)
+    (2, 1001, 1024, 128, 64, 4, 16, 128, True),      # one read for both caches, ragged tails
+    (1, 4096, 4096, 512, 128, 4, 128, 128, True),    # the 4 x 64K workload's shapes, one sequence of 4K
+    (1, 700, 512, 128, 64, 4, 32, 128, False),       # hidden 512: the two poolings run separately
+    (1, 640, 1024, 64, 0, 2, 0, 64, False),          # ratio 2 with 64: separate poolings
+]
+
+
+@pytest.mark.parametrize("case", HCA_COMPRESS_CASES)
+def test_hca_compress_parity(b, case):
+    B, L, Dh, D, dI, m, W, mh, heavy = case
+    X, wkv, wik, gate, _ = synth.compress_inputs(43, B, L, Dh, D, dI, m, heavy=heavy)
+    bslot = synth.normal_f32(43, "b_slot", (m,), 0.5)
+    wkv_h, _, gate_h, _ = synth.compress_weights(43, Dh, D, 0, mh, gate_scale=2.0, prefix="hca_")
+    bslot_h = synth.normal_f32(43, "b_slot_h", (mh,), 0.5)
+    Nc, Nh = -(-L // m), -(-L // mh)
+    kv_w, ik_w, win_w = oracle.compress(X, wkv, wik, gate, bslot, m, W=W)
+    kvh_w, _, _ = oracle.compress(X, wkv_h, None, gate_h, bslot_h, mh)
+    kv = torch.empty((B, Nc, D), dtype=torch.int16, device=DEV)
+    ik = torch.empty((B, Nc, dI), dtype=torch.int16, device=DEV) if dI else None
+    win = torch.empty((B, W, D), dtype=torch.int16, device=DEV) if W else None
+    kvh = torch.empty((B, Nh, D), dtype=torch.int16, device=DEV)
+    Xd = dev(X)
+    b.csa_hca_compress(Xd, dev(wkv), dev(wik) if dI else None, dev(gate), dev(bslot), m, W, kv, ik, win,
+                       dev(wkv_h), dev(gate_h), dev(bslot_h), mh, kvh)
+    torch.cuda.synchronize()
+    assert_rows_close(host_bf16(kv), kv_w, what="kv")
+    assert_rows_close(host_bf16(kvh), kvh_w, what="kv_h")
+    if dI:
+        assert_rows_close(host_bf16(ik), ik_w, what="ik")
+    if W:
+        assert_rows_close(host_bf16(win), win_w, what="window")
+    # the same as the two separate compressions, bit for bit
+    kv2, kvh2 = torch.empty_like(kv), torch.empty_like(kvh)
+    ik2 = torch.empty_like(ik) if dI else None
+    win2 = torch.empty_like(win) if W else None
+    b.csa_compress(Xd, dev(wkv), dev(wik) if dI else None, dev(gate), dev(bslot), m, W, kv2, ik2, win2)
+    b.csa_compress(Xd, dev(wkv_h), None, dev(gate_h), dev(bslot_h), mh, 0, kvh2)
+    torch.cuda.synchronize()
+    assert torch.equal(kv, kv2) and torch.equal(kvh, kvh2)
+    if dI:
+        assert torch.equal(ik, ik2)
+    if W:
+        assert torch.equal(win, win2)
 
 
 # ---------------------------------------------------------------------------
