@@ -134,10 +134,20 @@ __global__ __launch_bounds__(PTPB) void k_pool(const uint16_t* __restrict__ X, c
 // ---------------------------------------------------------------------------
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Sum over the wave, the same value in every lane: DPP within rows of 16 (swap neighbours, swap
+// pairs, mirror the halves of 8, mirror the row), then the row swaps of permlane16 / permlane32.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
 template <int CPL, int G, int MODE>   // MODE bit 0: fine blocks, bit 1: coarse blocks
@@ -207,45 +217,27 @@ __global__ __launch_bounds__(256, 2) void k_pool2(const uint16_t* __restrict__ X
             if (fine) zf[u] = wave_sum(zf[u]);
             if (coarse) zc[u] = wave_sum(zc[u]);
         }
-        // the packed rows are re-expanded for each use below (keeping the expanded values alive
-        // across the phases would take G CPL 8 more registers)
+        // the packed rows are expanded again below (the expanded values of the gate phase are not
+        // kept: that would take 8 G CPL more registers)
 #pragma unroll
         for (int u = 0; u < G; ++u)
 #pragma unroll
             for (int c = 0; c < CPL; ++c) asm volatile("" : "+v"(x[u][c]));
+        // weights of the group's tokens: fine softmax over the block; coarse online softmax, whose
+        // running maximum (and the rescale of the accumulators) moves only when the group's
+        // maximum exceeds it (a uniform branch)
+        float pf[G], pcw[G], inv = 0.f;
         if (fine) {
-            // fine block (tg - 0) / m: the group is one block, its valid tokens are tg .. min(tg + m, L) - 1
-            float mx = -INFINITY;
+            float mx = -INFINITY, l = 0.f;
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 zf[u] += bslot_f ? bslot_f[u] : 0.f;
                 if (tg + u < L) mx = fmaxf(mx, zf[u]);
             }
-            float p[G], l = 0.f;
 #pragma unroll
-            for (int u = 0; u < G; ++u) { p[u] = tg + u < L ? exp2f((zf[u] - mx) * LOG2E) : 0.f; l += p[u]; }
-            const float inv = 1.0f / l;
-            uint16_t* dst = out_f + ((size_t)b * Nf + (size_t)(tg / m)) * Dh;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                u32x4_t o;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float lo = 0.f, hi = 0.f;
-#pragma unroll
-                    for (int u = 0; u < G; ++u) {
-                        lo = fmaf(p[u], __uint_as_float(x[u][c][q] << 16), lo);
-                        hi = fmaf(p[u], __uint_as_float(x[u][c][q] & 0xffff0000u), hi);
-                    }
-                    o[q] = (uint32_t)f32_to_bf16(lo * inv) | ((uint32_t)f32_to_bf16(hi * inv) << 16);
-                }
-                *(u32x4_t*)(dst + 8 * (64 * c + lane)) = o;
-            }
+            for (int u = 0; u < G; ++u) { pf[u] = tg + u < L ? exp2f((zf[u] - mx) * LOG2E) : 0.f; l += pf[u]; }
+            inv = 1.0f / l;
         }
-#pragma unroll
-        for (int u = 0; u < G; ++u)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) asm volatile("" : "+v"(x[u][c]));
         if (coarse) {
             const long long jb = (long long)blockIdx.x * S;    // the coarse block's first token (S = mc)
             float gm = -INFINITY;
@@ -254,26 +246,37 @@ __global__ __launch_bounds__(256, 2) void k_pool2(const uint16_t* __restrict__ X
                 zc[u] += bslot_c ? bslot_c[(int)(tg + u - jb)] : 0.f;
                 if (tg + u < L) gm = fmaxf(gm, zc[u]);
             }
-            const float mnew = fmaxf(mrun, gm);
-            const float alpha = exp2f((mrun - mnew) * LOG2E);
-            float p[G], ps = 0.f;
+            if (gm > mrun) {
+                const float alpha = exp2f((mrun - gm) * LOG2E);
 #pragma unroll
-            for (int u = 0; u < G; ++u) { p[u] = tg + u < L ? exp2f((zc[u] - mnew) * LOG2E) : 0.f; ps += p[u]; }
-            lrun = lrun * alpha + ps;
-            mrun = mnew;
+                for (int c = 0; c < CPL; ++c)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c)
+                    for (int e = 0; e < 8; ++e) acc[c][e] *= alpha;
+                lrun *= alpha;
+                mrun = gm;
+            }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float lo = acc[c][2 * q] * alpha, hi = acc[c][2 * q + 1] * alpha;
+            for (int u = 0; u < G; ++u) { pcw[u] = tg + u < L ? exp2f((zc[u] - mrun) * LOG2E) : 0.f; lrun += pcw[u]; }
+        }
+        // one expansion of each packed element feeds both poolings
+        uint16_t* dst = fine ? out_f + ((size_t)b * Nf + (size_t)(tg / (fine ? m : 1))) * Dh : nullptr;
 #pragma unroll
-                    for (int u = 0; u < G; ++u) {
-                        lo = fmaf(p[u], __uint_as_float(x[u][c][q] << 16), lo);
-                        hi = fmaf(p[u], __uint_as_float(x[u][c][q] & 0xffff0000u), hi);
-                    }
-                    acc[c][2 * q] = lo;
-                    acc[c][2 * q + 1] = hi;
+        for (int c = 0; c < CPL; ++c) {
+            u32x4_t o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float flo = 0.f, fhi = 0.f;
+                float clo = coarse ? acc[c][2 * q] : 0.f, chi = coarse ? acc[c][2 * q + 1] : 0.f;
+#pragma unroll
+                for (int u = 0; u < G; ++u) {
+                    const float lo = __uint_as_float(x[u][c][q] << 16), hi = __uint_as_float(x[u][c][q] & 0xffff0000u);
+                    if (fine) { flo = fmaf(pf[u], lo, flo); fhi = fmaf(pf[u], hi, fhi); }
+                    if (coarse) { clo = fmaf(pcw[u], lo, clo); chi = fmaf(pcw[u], hi, chi); }
                 }
+                if (fine) o[q] = pack_bf16x2(flo * inv, fhi * inv);
+                if (coarse) { acc[c][2 * q] = clo; acc[c][2 * q + 1] = chi; }
+            }
+            if (fine) *(u32x4_t*)(dst + 8 * (64 * c + lane)) = o;
         }
     }
     if (!coarse) return;
@@ -307,8 +310,8 @@ __global__ __launch_bounds__(256, 2) void k_pool2(const uint16_t* __restrict__ X
             const int c = i / 128, hf = (i / 64) & 1, l = i & 63;
             const int e0 = 8 * (64 * (hp * (CPL / 2) + c) + l) + 4 * hf;
             uint2 o;
-            o.x = (uint32_t)f32_to_bf16(a[0] * inv) | ((uint32_t)f32_to_bf16(a[1] * inv) << 16);
-            o.y = (uint32_t)f32_to_bf16(a[2] * inv) | ((uint32_t)f32_to_bf16(a[3] * inv) << 16);
+            o.x = pack_bf16x2(a[0] * inv, a[1] * inv);
+            o.y = pack_bf16x2(a[2] * inv, a[3] * inv);
             *(uint2*)(dst + e0) = o;
         }
         __syncthreads();
