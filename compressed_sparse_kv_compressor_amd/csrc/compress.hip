@@ -155,12 +155,12 @@ __global__ __launch_bounds__(256, 2) void k_pool2(const uint16_t* __restrict__ X
                                                int m, const float* __restrict__ gate_f, const float* __restrict__ bslot_f,
                                                int Nf, uint16_t* __restrict__ out_f,
                                                int mc, const float* __restrict__ gate_c, const float* __restrict__ bslot_c,
-                                               int Ncc, uint16_t* __restrict__ out_c)
+                                               int Ncc, uint16_t* __restrict__ out_c, int b0)
 {
     __shared__ f32x4_t gl[2][CPL * 2 * 64];                    // gates: [fine, coarse][chunk][half][lane]
     __shared__ f32x4_t mrg[4][CPL / 2 * 2 * 64];               // coarse merge: half of the chunks at a time
     __shared__ float ml[4][2];
-    const int b = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = b0 + (int)blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const long long t0 = (long long)blockIdx.x * S;
     constexpr bool fine = MODE & 1, coarse = MODE & 2;
     for (int i = tid; i < CPL * 2 * 64; i += 256) {
@@ -635,10 +635,13 @@ size_t hca_compress_ws_bytes(int B, long long L, int Dh, int D, int dI, int m, i
 }
 
 // one k_gemm2 launch (+ its reduction when the K range is split)
+// (P holds pcap floats: the split count is lowered until its partial sums fit)
 static int gemm2_launch(const uint16_t* A, long long a_bstride, int batch, int M, int K, const uint16_t* B0, int N0,
-                        const uint16_t* B1, int N1, int c1_e4m3, uint16_t* C0, void* C1, float* P, hipStream_t st) {
+                        const uint16_t* B1, int N1, int c1_e4m3, uint16_t* C0, void* C1, float* P, size_t pcap,
+                        hipStream_t st) {
     const int N = N0 + N1;
-    const int S = g2_splits(batch, M, N, K);
+    int S = g2_splits(batch, M, N, K);
+    while (S > 1 && (size_t)S * batch * M * N > pcap) S >>= 1;
     const int units = ((M + G2_T - 1) / G2_T) * ((N + G2_T - 1) / G2_T) * S;
     const dim3 grid((unsigned)((units + 7) / 8 * 8), (unsigned)batch);
     if (c1_e4m3)
@@ -667,7 +670,8 @@ static bool pool2_dh_ok(int Dh) { return Dh == 1024 || Dh == 2048 || Dh == 4096;
 // the streaming kernel does not cover the shape
 static int pool2_launch(const uint16_t* X, int B, long long L, int Dh, int m, const float* gate_f, const float* bslot_f,
                         uint16_t* out_f, int mc, const float* gate_c, const float* bslot_c, uint16_t* out_c,
-                        hipStream_t st) {
+                        hipStream_t st, int b0 = 0, int nb = -1) {
+    if (nb < 0) nb = B - b0;
     if (!pool2_dh_ok(Dh)) return -1;
     if (m > 0 && !pool2_fine_ok(Dh, m)) return -1;
     if (mc > 0 && (mc % 16 != 0 || (m > 0 && (m != 4 || mc % (4 * m) != 0)))) return -1;
@@ -676,13 +680,13 @@ static int pool2_launch(const uint16_t* X, int B, long long L, int Dh, int m, co
     const int G = m > 0 ? m : 4;
     const int Nf = m > 0 ? (int)((L + m - 1) / m) : 0;
     const int Ncc = mc > 0 ? (int)((L + mc - 1) / mc) : 0;
-    const dim3 grid((unsigned)((L + S - 1) / S), (unsigned)B);
+    const dim3 grid((unsigned)((L + S - 1) / S), (unsigned)nb);
     const int cpl = Dh / 512;
     const int mode = (m > 0 ? 1 : 0) | (mc > 0 ? 2 : 0);
 #define CSA_POOL2(C, GG, MD)                                                                                    \
     if (cpl == C && G == GG && mode == MD) {                                                                    \
         CSA_LAUNCH("k_pool2", (k_pool2<C, GG, MD>), grid, dim3(256), 0, st, X, L, Dh, S, m, gate_f, bslot_f, Nf,  \
-                   out_f, mc, gate_c, bslot_c, Ncc, out_c);                                                     \
+                   out_f, mc, gate_c, bslot_c, Ncc, out_c, b0);                                                 \
         return 0;                                                                                               \
     }
     CSA_POOL2(2, 1, 1) CSA_POOL2(2, 2, 1) CSA_POOL2(2, 4, 1) CSA_POOL2(4, 1, 1) CSA_POOL2(4, 2, 1) CSA_POOL2(4, 4, 1)
@@ -721,16 +725,16 @@ static int pool_launch(const void* hidden, const float* w_gate, const float* b_s
 // projections of the pooled rows (KV and indexer keys in one launch) and of the window rows
 static int project_launch(const void* hidden, const uint16_t* pooled, const void* w_kv, const void* w_ik, int B,
                           long long L, int Dh, int D, int dI, int Nc, int W, int ik_dtype, void* kv_out, void* ik_out,
-                          void* win_out, float* partial, hipStream_t st) {
+                          void* win_out, float* partial, size_t pcap, hipStream_t st) {
     const int N1 = (w_ik && ik_out) ? dI : 0;
     int rc = gemm2_launch(pooled, 0, 1, B * Nc, Dh, (const uint16_t*)w_kv, D, (const uint16_t*)w_ik, N1,
-                          N1 && ik_dtype == 1, (uint16_t*)kv_out, ik_out, partial, st);
+                          N1 && ik_dtype == 1, (uint16_t*)kv_out, ik_out, partial, pcap, st);
     if (rc) return rc;
     if (win_out && W > 0) {
         if (L >= W) {
             // each sequence's last W hidden rows are contiguous: one batch of the GEMM per sequence
             rc = gemm2_launch((const uint16_t*)hidden + (size_t)(L - W) * Dh, L * Dh, B, W, Dh, (const uint16_t*)w_kv,
-                              D, nullptr, 0, 0, (uint16_t*)win_out, nullptr, partial, st);
+                              D, nullptr, 0, 0, (uint16_t*)win_out, nullptr, partial, pcap, st);
             if (rc) return rc;
         } else {
             ARows wa{1, (const uint16_t*)hidden, L, W};
@@ -748,10 +752,11 @@ int compress_launch(const void* hidden, const void* w_kv, const void* w_ik, cons
     const int Nc = (int)((L + m - 1) / m);
     uint16_t* pooled = (uint16_t*)ws;
     float* partial = (float*)((char*)ws + align256((size_t)B * Nc * Dh * 2));
+    const size_t pcap = partial_floats(B, L, Dh, D, (w_ik && ik_out) ? dI : 0, m, win_out ? W : 0, 0);
     int rc = pool_launch(hidden, w_gate, b_slot, B, L, Dh, m, pooled, st);
     if (rc) return rc;
     return project_launch(hidden, pooled, w_kv, w_ik, B, L, Dh, D, dI, Nc, W, ik_dtype, kv_out, ik_out, win_out,
-                          partial, st);
+                          partial, pcap, st);
 }
 
 int hca_compress_launch(const void* hidden, const void* w_kv, const void* w_ik, const float* w_gate,
@@ -762,6 +767,8 @@ int hca_compress_launch(const void* hidden, const void* w_kv, const void* w_ik, 
     uint16_t* pooled = (uint16_t*)ws;
     uint16_t* pooled_h = (uint16_t*)((char*)ws + align256((size_t)B * Nc * Dh * 2));
     float* partial = (float*)((char*)pooled_h + align256((size_t)B * Nh * Dh * 2));
+    const int N1 = (w_ik && ik_out) ? dI : 0;
+    const size_t pcap = partial_floats(B, L, Dh, D, N1, m, win_out ? W : 0, Nh);
     // both pooled sets from one read of the hidden rows where the streaming kernel covers the shape
     int rc = pool2_launch((const uint16_t*)hidden, B, L, Dh, m, w_gate, b_slot, pooled, mh, w_gate_h, b_slot_h,
                           pooled_h, st);
@@ -772,10 +779,10 @@ int hca_compress_launch(const void* hidden, const void* w_kv, const void* w_ik, 
     }
     if (rc) return rc;
     rc = project_launch(hidden, pooled, w_kv, w_ik, B, L, Dh, D, dI, Nc, W, ik_dtype, kv_out, ik_out, win_out, partial,
-                        st);
+                        pcap, st);
     if (rc) return rc;
     return gemm2_launch(pooled_h, 0, 1, B * Nh, Dh, (const uint16_t*)w_kv_h, D, nullptr, 0, 0, (uint16_t*)kv_h_out,
-                        nullptr, partial, st);
+                        nullptr, partial, pcap, st);
 }
 
 }  // namespace csa_host
