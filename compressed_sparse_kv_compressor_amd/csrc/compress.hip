@@ -129,9 +129,14 @@ __global__ __launch_bounds__(PTPB) void k_pool(const uint16_t* __restrict__ X, c
 // products are lane partials plus one wave reduction, and no workgroup barrier is needed until the
 // coarse merge at the end.  Fine: softmax over the group's valid tokens, pooled row written at
 // once.  Coarse: an online softmax per wave, then the four waves' (max, sum, accumulator) merged
-// through LDS.  Gates are staged in LDS as [chunk][half][lane] float4 so that each read is one
-// contiguous 16-byte access per lane.
+// through LDS.  Each fp32 gate weight is staged in LDS as two bf16 terms (hi + lo, within 2^-17
+// of it), as [chunk][hi, lo][lane] 16-byte vectors, so that the gate products run as bf16 pair dot
+// instructions straight on the packed rows (fp32 accumulation) and each read is one contiguous
+// 16-byte access per lane.
 // ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+// (by value: a bit_cast applied directly to a vector-element expression was compiled as element 0)
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
 constexpr float LOG2E = 1.4426950408889634f;
 
 // Sum over the wave, the same value in every lane: DPP within rows of 16 (swap neighbours, swap
@@ -157,17 +162,27 @@ __global__ __launch_bounds__(256, 2) void k_pool2(const uint16_t* __restrict__ X
                                                int mc, const float* __restrict__ gate_c, const float* __restrict__ bslot_c,
                                                int Ncc, uint16_t* __restrict__ out_c, int b0)
 {
-    __shared__ f32x4_t gl[2][CPL * 2 * 64];                    // gates: [fine, coarse][chunk][half][lane]
+    __shared__ u32x4_t gl[2][CPL * 2 * 64];                    // gates: [fine, coarse][chunk][hi, lo][lane]
     __shared__ f32x4_t mrg[4][CPL / 2 * 2 * 64];               // coarse merge: half of the chunks at a time
     __shared__ float ml[4][2];
     const int b = b0 + (int)blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const long long t0 = (long long)blockIdx.x * S;
     constexpr bool fine = MODE & 1, coarse = MODE & 2;
-    for (int i = tid; i < CPL * 2 * 64; i += 256) {
-        const int c = i / 128, hf = (i / 64) & 1, l = i & 63;
-        const int e0 = 8 * (64 * c + l) + 4 * hf;
-        if (fine) gl[0][i] = *(const f32x4_t*)(gate_f + e0);
-        if (coarse) gl[1][i] = *(const f32x4_t*)(gate_c + e0);
+    // each fp32 gate weight as the sum of two bf16 values (hi = RNE(g), lo = RNE(g - hi): within
+    // 2^-17 of g), so that the dot products run as bf16 pair dots on the packed rows
+    auto split_gate = [&](const float* g, int c, int l, u32x4_t& hi, u32x4_t& lo) {
+        const f32x4_t a = *(const f32x4_t*)(g + 8 * (64 * c + l)), b2 = *(const f32x4_t*)(g + 8 * (64 * c + l) + 4);
+        const float v[8] = {a[0], a[1], a[2], a[3], b2[0], b2[1], b2[2], b2[3]};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            hi[p] = pack_bf16x2(v[2 * p], v[2 * p + 1]);
+            lo[p] = pack_bf16x2(v[2 * p] - __uint_as_float(hi[p] << 16), v[2 * p + 1] - __uint_as_float(hi[p] & 0xffff0000u));
+        }
+    };
+    for (int i = tid; i < CPL * 64; i += 256) {
+        const int c = i / 64, l = i & 63;
+        if (fine) split_gate(gate_f, c, l, gl[0][(2 * c) * 64 + l], gl[0][(2 * c + 1) * 64 + l]);
+        if (coarse) split_gate(gate_c, c, l, gl[1][(2 * c) * 64 + l], gl[1][(2 * c + 1) * 64 + l]);
     }
     __syncthreads();
     const int span = S / 4;
@@ -196,20 +211,19 @@ __global__ __launch_bounds__(256, 2) void k_pool2(const uint16_t* __restrict__ X
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const f32x4_t gf = fine ? gl[0][(2 * c + hf) * 64 + lane] : f32x4_t{0, 0, 0, 0};
-                const f32x4_t gc = coarse ? gl[1][(2 * c + hf) * 64 + lane] : f32x4_t{0, 0, 0, 0};
+            for (int hf = 0; hf < 2; ++hf) {                   // hi parts, then lo parts of the gates
+                const u32x4_t gf = fine ? gl[0][(2 * c + hf) * 64 + lane] : u32x4_t{0, 0, 0, 0};
+                const u32x4_t gc = coarse ? gl[1][(2 * c + hf) * 64 + lane] : u32x4_t{0, 0, 0, 0};
 #pragma unroll
                 for (int u = 0; u < G; ++u)
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const uint32_t wd = x[u][c][2 * hf + e];
-                        const float lo = __uint_as_float(wd << 16), hi = __uint_as_float(wd & 0xffff0000u);
-                        zf[u] = fmaf(hi, gf[2 * e + 1], fmaf(lo, gf[2 * e], zf[u]));
-                        zc[u] = fmaf(hi, gc[2 * e + 1], fmaf(lo, gc[2 * e], zc[u]));
+                    for (int p = 0; p < 4; ++p) {
+                        const bf16x2_t xv = as_bf16x2(x[u][c][p]);
+                        if (fine) zf[u] = __builtin_amdgcn_fdot2_f32_bf16(xv, as_bf16x2(gf[p]), zf[u], false);
+                        if (coarse) zc[u] = __builtin_amdgcn_fdot2_f32_bf16(xv, as_bf16x2(gc[p]), zc[u], false);
                     }
                 // (keeps the gate reads of later chunks from being hoisted here: they would hold
-                // 16 CPL more registers)
+                // 8 CPL more registers)
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
