@@ -421,8 +421,9 @@ __global__ __launch_bounds__(GTPB) void k_gemm(ARows a, const uint16_t* __restri
 // pooled rows are one launch.  gridDim.y batches of rows: batch y reads A + y a_bstride and writes
 // rows y M ..  With S > 1 the K range is split S ways and each split writes fp32 partial sums to
 // P [y][S][M][N0 + N1], which k_g2reduce adds in split order (deterministic) and rounds.
-// A workgroup owns a 256 x 256 tile: four waves, each 128 x 128 as 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).  K advances 32 at a time through
+// A workgroup owns a 256 x 256 tile: eight waves (two per SIMD, so that one computes while the other
+// waits on a barrier or LDS), each 128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32
+// accumulators per lane; four waves of 128 x 128 with the accumulators in AGPRs ran ~6% slower).  K advances 32 at a time through
 // four LDS buffers (64-byte rows, 16-byte chunk c of row r stored at c ^ ((r >> 2) & 3): the 16
 // lanes a 16-byte read serves per cycle then cover all 64 banks), filled by buffer-load DMA issued
 // two steps ahead; every step issues the same number of loads (steps past the end reread the last
@@ -431,7 +432,13 @@ __global__ __launch_bounds__(GTPB) void k_gemm(ARows a, const uint16_t* __restri
 // ---------------------------------------------------------------------------
 constexpr int G2_T = 256, G2_KS = 32, G2_NB = 4, G2_ROWB = G2_KS * 2;     // tile, K step, buffers, row bytes
 constexpr int G2_BUF = 2 * G2_T * G2_ROWB;                                 // A rows then B rows: 32 KiB
-constexpr int G2_DMA = G2_T * G2_ROWB / 1024 / 4;                          // 1 KiB loads per wave per operand (4)
+#ifndef CSA_G2_NW
+#define CSA_G2_NW 8
+#endif
+constexpr int G2_NW = CSA_G2_NW;                                           // waves per workgroup (4 or 8)
+constexpr int G2_WNB = 16 / G2_NW;                                         // 32-column blocks per wave (4 or 2)
+constexpr int G2_WNW = G2_T / (32 * G2_WNB);                               // waves across N (2 or 4)
+constexpr int G2_DMA = G2_T * G2_ROWB / 1024 / G2_NW;                      // 1 KiB loads per wave per operand
 
 // s_waitcnt immediate: vmcnt(n) with expcnt and lgkmcnt left free
 __device__ __forceinline__ constexpr int vmcnt_imm2(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -441,7 +448,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t g2_rsrc(const void* base, uint
 }
 
 template <int C1_E4M3>
-__global__ __launch_bounds__(256) void k_gemm2(const uint16_t* __restrict__ A, long long a_bstride, int M, int K,
+__global__ __launch_bounds__(64 * G2_NW) void k_gemm2(const uint16_t* __restrict__ A, long long a_bstride, int M, int K,
                                                const uint16_t* __restrict__ B0, int N0, const uint16_t* __restrict__ B1,
                                                int N1, uint16_t* __restrict__ C0, void* __restrict__ C1, int S,
                                                float* __restrict__ P)
@@ -455,7 +462,7 @@ __global__ __launch_bounds__(256) void k_gemm2(const uint16_t* __restrict__ A, l
     const int tile = unit / S, ks = unit % S;
     const int m0 = (tile / ntn) * G2_T, n0 = (tile % ntn) * G2_T;
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+    const int wm = (w / G2_WNW) * 128, wn = (w % G2_WNW) * (32 * G2_WNB);
     const int nk = K / S / G2_KS, kbeg = ks * (K / S);
     const int y = blockIdx.y;
     A += (size_t)y * a_bstride;
@@ -473,14 +480,14 @@ __global__ __launch_bounds__(256) void k_gemm2(const uint16_t* __restrict__ A, l
         CSA_LDS char* lb = (CSA_LDS char*)g2_lds + buf * G2_BUF;
 #pragma unroll
         for (int i = 0; i < G2_DMA; ++i) {                 // A rows 16 I .. 16 I + 15
-            const int I = w + 4 * i, row = 16 * I + drow;
+            const int I = w + G2_NW * i, row = 16 * I + drow;
             const int r = min(row, mrows - 1);
             const uint32_t voff = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)(k0 + 8 * (dpos ^ ((row >> 2) & 3))) * 2u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (CSA_LDS void*)(lb + 1024 * I), 16, (int)voff, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < G2_DMA; ++i) {                 // B rows 16 I .. 16 I + 15 of the tile
-            const int I = w + 4 * i, row = 16 * I + drow;
+            const int I = w + G2_NW * i, row = 16 * I + drow;
             const int nbase = n0 + 16 * I;
             const bool second = nbase >= N0 && nbase < N;           // uniform per load
             const int br = second ? min(n0 + row - N0, N1 - 1) : min(n0 + row, N0 - 1);
@@ -489,11 +496,11 @@ __global__ __launch_bounds__(256) void k_gemm2(const uint16_t* __restrict__ A, l
                                                      16, (int)voff, 0, 0, 0);
         }
     };
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][G2_WNB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < G2_WNB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     // this lane's fragment offset within a buffer for row `row`, k sub-step s (logical chunk 2 s + lane/32)
@@ -501,21 +508,23 @@ __global__ __launch_bounds__(256) void k_gemm2(const uint16_t* __restrict__ A, l
         return (uint32_t)row * G2_ROWB + 16u * (uint32_t)((2 * s + (lane >> 5)) ^ ((row >> 2) & 3));
     };
     const int r32 = lane & 31;
-    auto read_frags = [&](int step, u32x4_t (&fa)[4][2], u32x4_t (&fb)[4][2]) {
+    auto read_frags = [&](int step, u32x4_t (&fa)[4][2], u32x4_t (&fb)[G2_WNB][2]) {
         const CSA_LDS char* lb = (const CSA_LDS char*)g2_lds + (step % G2_NB) * G2_BUF;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                fa[i][s2] = *(const CSA_LDS u32x4_t*)(lb + frag(wm + 32 * i + r32, s2));
-                fb[i][s2] = *(const CSA_LDS u32x4_t*)(lb + G2_T * G2_ROWB + frag(wn + 32 * i + r32, s2));
-            }
+            for (int i = 0; i < 4; ++i) fa[i][s2] = *(const CSA_LDS u32x4_t*)(lb + frag(wm + 32 * i + r32, s2));
+#pragma unroll
+            for (int j = 0; j < G2_WNB; ++j)
+                fb[j][s2] = *(const CSA_LDS u32x4_t*)(lb + G2_T * G2_ROWB + frag(wn + 32 * j + r32, s2));
+        }
     };
-    auto mfmas = [&](const u32x4_t (&fa)[4][2], const u32x4_t (&fb)[4][2], int s2) {
+    auto mfmas = [&](const u32x4_t (&fa)[4][2], const u32x4_t (&fb)[G2_WNB][2], int s2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_bf16(as_bf16x8(fa[i][s2]), as_bf16x8(fb[j][s2]), acc[i][j]);
+            for (int j = 0; j < G2_WNB; ++j)
+                acc[i][j] = mfma32_bf16(as_bf16x8(fa[i][s2]), as_bf16x8(fb[j][s2]), acc[i][j]);
     };
     // Step t's fragments are read from LDS during step t - 1, between its two halves of MFMAs, so
     // that the LDS latency hides behind MFMAs.  The barrier in step t certifies step t + 1's tile
@@ -525,11 +534,11 @@ __global__ __launch_bounds__(256) void k_gemm2(const uint16_t* __restrict__ A, l
     for (int b = 0; b < G2_NB - 1; ++b) issue(b, b);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm2((G2_NB - 2) * 2 * G2_DMA));
     __syncthreads();
-    u32x4_t ca[4][2], cb[4][2];
+    u32x4_t ca[4][2], cb[G2_WNB][2];
     read_frags(0, ca, cb);
     for (int t = 0; t < nk; ++t) {
         mfmas(ca, cb, 0);
-        u32x4_t na[4][2], nb[4][2];
+        u32x4_t na[4][2], nb[G2_WNB][2];
         if (t + 1 < nk) {                                  // uniform
             __builtin_amdgcn_s_waitcnt(vmcnt_imm2((G2_NB - 3) * 2 * G2_DMA));
             __syncthreads();
@@ -539,9 +548,12 @@ __global__ __launch_bounds__(256) void k_gemm2(const uint16_t* __restrict__ A, l
         mfmas(ca, cb, 1);
         if (t + 1 < nk) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) { ca[i][s2] = na[i][s2]; cb[i][s2] = nb[i][s2]; }
+                for (int i = 0; i < 4; ++i) ca[i][s2] = na[i][s2];
+#pragma unroll
+                for (int j = 0; j < G2_WNB; ++j) cb[j][s2] = nb[j][s2];
+            }
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm2(0));             // the reread loads past the end land before exit
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(256) void k_gemm2(const uint16_t* __restrict__ A, l
     if (S > 1) {
         float* Pk = P + ((size_t)y * S + ks) * M * N;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < G2_WNB; ++j) {
             const int gj = n0 + wn + 32 * j + r32;
             if (n0 + wn + 32 * j >= N) continue;             // uniform: N0 and N1 are multiples of 32
 #pragma unroll
@@ -563,7 +575,7 @@ __global__ __launch_bounds__(256) void k_gemm2(const uint16_t* __restrict__ A, l
         return;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < G2_WNB; ++j) {
         const int gj = n0 + wn + 32 * j + r32;
         if (n0 + wn + 32 * j >= N) continue;                 // uniform: N0 and N1 are multiples of 32
         const bool second = n0 + wn + 32 * j >= N0;
@@ -659,9 +671,9 @@ static int gemm2_launch(const uint16_t* A, long long a_bstride, int batch, int M
     const int units = ((M + G2_T - 1) / G2_T) * ((N + G2_T - 1) / G2_T) * S;
     const dim3 grid((unsigned)((units + 7) / 8 * 8), (unsigned)batch);
     if (c1_e4m3)
-        CSA_LAUNCH("k_gemm2", k_gemm2<1>, grid, dim3(256), 0, st, A, a_bstride, M, K, B0, N0, B1, N1, C0, C1, S, P);
+        CSA_LAUNCH("k_gemm2", k_gemm2<1>, grid, dim3(64 * G2_NW), 0, st, A, a_bstride, M, K, B0, N0, B1, N1, C0, C1, S, P);
     else
-        CSA_LAUNCH("k_gemm2", k_gemm2<0>, grid, dim3(256), 0, st, A, a_bstride, M, K, B0, N0, B1, N1, C0, C1, S, P);
+        CSA_LAUNCH("k_gemm2", k_gemm2<0>, grid, dim3(64 * G2_NW), 0, st, A, a_bstride, M, K, B0, N0, B1, N1, C0, C1, S, P);
     if (S > 1) {
         const dim3 rg((unsigned)(((long long)M * N / 4 + 255) / 256), (unsigned)batch);
         if (c1_e4m3)
