@@ -11,14 +11,15 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libcsa.so")
 OBJ = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["abi.hip", "index_topk.hip", "prefill_index.hip", "attn.hip", "compress.hip"]
+SOURCES = ["abi.hip", "index_topk.hip", "prefill_index.hip", "attn.hip", "attn128.hip", "compress.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # keep the compiler from emitting packed-fp32 VALU ops
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(HERE, "..", "include")]
-# per-source extras: the attention kernels keep MFMA accumulators in ordinary VGPRs (their
-# occasional rescale is VALU work on the accumulators)
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source extras: the attention kernels start with MFMA accumulators in ordinary VGPRs (their
+# occasional rescale is VALU work on the accumulators); in attn128.hip the compiler then moves what does
+# not fit into the AGPRs
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "attn128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -24,36 +24,14 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "attn_common.h"
 
 namespace {
 
 using namespace csa;
+using namespace csa_attn;
 
 constexpr int TPB = 256;
-constexpr int TILE = 32;
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
-
-struct Rows {
-    int mode;
-    const uint16_t* kv;
-    int N;
-    long long L;
-    int ratio;
-    const int32_t* idx;
-    int topk;
-    const uint16_t* kv_raw;
-    int Lr;
-    long long raw0;
-    int W;
-};
-
-__device__ __forceinline__ int dense_visible(long long p, long long L, int m, int N) {
-    if (p >= L - 1) return N;
-    long long v = (p + 1) / m;
-    return v < N ? (int)v : N;
-}
-
 // Number of rows of query (b, t) and pointer to row r (nullptr = masked row).
 struct RowSet {
     int n;
@@ -237,28 +215,12 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
 // ---------------------------------------------------------------------------
 constexpr int HD = 256;   // d-half handled by one wave
 
-// 16-byte chunk c of row r is stored at chunk c ^ f(r & 15), f(x) = 4 (x & 3) + (x >> 2): any 16
-// consecutive rows at one chunk, and any 4 aligned rows x 4 aligned chunks (the footprint of a
-// transposed read), fall on 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz_chunk(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-// Raw buffer resource (stride 0, byte offsets) over [base, base + bytes).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 #ifndef CSA_ATTN64_QK_AHEAD
 #define CSA_ATTN64_QK_AHEAD 4      // K-operand LDS reads in flight ahead of the QK MFMAs
 #endif
 #ifndef CSA_ATTN64_PV_AHEAD
 #define CSA_ATTN64_PV_AHEAD 2      // d-tiles of V reads in flight ahead of the PV MFMAs
 #endif
-// Masked rows get -2^100 added to their scores by one extra MFMA k-step (A: a 1 in column 0 of each
-// masked row; B: -2^100 in row 0, d-half 0 only), which sends their probabilities to exactly 0
-// without any per-element select on the common path.  A split with no valid row at all ends with a
-// running max below EMPTY_M, which the output step treats as empty.
-constexpr uint32_t BF16_ONE = 0x3f80u, BF16_NEG_2P100 = 0xf180u;
-constexpr float EMPTY_M = -1.0e25f;
 constexpr int ATT_TILES = 3;      // tile buffers; a split's tile count is a multiple of this
 
 // MODE 0: dense prefix (row r = entry r); MODE 1: selected entries then window rows.  BIG: some
@@ -682,20 +644,6 @@ __global__ __launch_bounds__(TPB, 1) void k_attn64(
                            part_o, part_ml, out, lse);
 }
 
-// One attention problem of a fused launch.
-struct AttnJob {
-    const uint16_t* q;
-    Rows R;
-    int Tq, H;
-    long long pos0;
-    float scale_log2;
-    int nunits, nsplit, rps;
-    float* part_o;
-    float2* part_ml;
-    uint16_t* out;
-    float* lse;
-};
-
 // CSA sparse (workgroups [0, nblk_s)) and HCA dense attention in one launch: the short, latency-bound
 // sparse workgroups run beside the dense ones instead of before them.
 template <bool BIG>
@@ -824,13 +772,46 @@ static int attn_rows(int mode, int H, int D, int n, int W) {
     return (use64(D, H) ? (n + TILE - 1) / TILE * TILE : n) + W;
 }
 
+// k_attn128 (128 heads per workgroup, one workgroup per CU): the rows per split are the same for every
+// workgroup of a launch (a multiple of 4 tiles), chosen so that the launch's tiles spread over about
+// CSA_A128_TARGET_WG workgroups, and at least CSA_A128_MIN_TILES tiles per split.
+#ifndef CSA_ATT128
+#define CSA_ATT128 1
+#endif
+#ifndef CSA_A128_TARGET_WG
+#define CSA_A128_TARGET_WG 256
+#endif
+#ifndef CSA_A128_MIN_TILES
+#define CSA_A128_MIN_TILES 4
+#endif
+static bool use128(int D, int H) { return CSA_ATT128 && D == 512 && H % 128 == 0; }
+static int a128_tiles(int rows) { return (rows + TILE - 1) / TILE; }
+static int a128_rps(long long total_tiles) {
+    long long tpw = (total_tiles + CSA_A128_TARGET_WG - 1) / CSA_A128_TARGET_WG;
+    tpw = std::max<long long>(tpw, CSA_A128_MIN_TILES);
+    long long r = (tpw * TILE + ATT128_UNIT - 1) / ATT128_UNIT * ATT128_UNIT;
+    return (int)std::min<long long>(r, ATT128_MAX_RPS);
+}
+static int a128_nsplit(int max_rows, int rps) { return max_rows <= 0 ? 1 : (max_rows + rps - 1) / rps; }
+// row space of k_attn128 (topk padded to whole tiles, then the window)
+static int a128_rows(int mode, int n, int W) { return mode == 0 ? n : a128_tiles(n) * TILE + W; }
+static size_t part_bytes(int BT, int ns, int H, int D) {
+    if (ns <= 1) return 0;
+    return align256((size_t)BT * ns * H * D * 4) + align256((size_t)BT * ns * H * 8);
+}
+
 size_t attn_ws_bytes(int B, int Tq, int H, int D, int mode, int n, int W) {
     const int BT = B * Tq;
     const int max_rows = attn_rows(mode, H, D, n, W);
     int ns, rps;
     choose_split(BT, H, D, max_rows, &ns, &rps);
-    if (ns == 1) return 0;
-    return align256((size_t)BT * ns * H * D * 4) + align256((size_t)BT * ns * H * 8);
+    size_t s = part_bytes(BT, ns, H, D);
+    if (use128(D, H)) {      // either kernel may run (k_attn64 when an array is beyond 32-bit offsets)
+        const int r128 = a128_rows(mode, n, W);
+        const int rp = a128_rps((long long)BT * (H / 128) * a128_tiles(r128));
+        s = std::max(s, part_bytes(BT, a128_nsplit(r128, rp), H, D));
+    }
+    return s;
 }
 
 int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, long long pos0, float scale,
@@ -858,6 +839,21 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         part_ml = (float2*)((char*)ws + align256((size_t)BT * ns * H * D * 4));
     }
     const float sl2 = scale * LOG2E;
+    const bool big32 = (size_t)a.N * D * 2 > 0xffffffffull || (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
+    if (use128(D, H) && !big32) {
+        const int r128 = a.mode == 0 ? a.N : a128_rows(1, a.topk, a.W);
+        AttnJob j{};
+        j.q = (const uint16_t*)q; j.R = R; j.Tq = Tq; j.H = H; j.pos0 = pos0; j.scale_log2 = sl2;
+        j.rps = a128_rps((long long)BT * (H / 128) * a128_tiles(r128));
+        j.nsplit = a128_nsplit(r128, j.rps);
+        j.nunits = BT * j.nsplit;
+        j.out = (uint16_t*)out; j.lse = lse;
+        if (j.nsplit > 1) {
+            j.part_o = (float*)ws;
+            j.part_ml = (float2*)((char*)ws + align256((size_t)BT * j.nsplit * H * D * 4));
+        }
+        return attn128_launch(j, st, tag);
+    }
     if (use64(D, H)) {
         const int nunits = BT * ns, HP = (H + 63) / 64;
         const int nblk = (nunits + 7) / 8 * 8 * HP;
@@ -901,8 +897,22 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
 // both take k_attn64 with 32-bit offsets; returns -1 when it does not apply (the caller launches them
 // apart), else 0 or a status code.
 // Workspace: the sparse partials, then the dense partials.
+// k_attn128 pair: one rows-per-split for both jobs, from their tiles together.
+static void a128_pair_split(int B, int H, int topk, int W, int Nh, int* rps, int* ns_s, int* ns_d) {
+    const int rs = a128_rows(1, topk, W), rd = Nh;
+    *rps = a128_rps((long long)B * (H / 128) * (a128_tiles(rs) + a128_tiles(rd)));
+    *ns_s = a128_nsplit(rs, *rps);
+    *ns_d = a128_nsplit(rd, *rps);
+}
+
 size_t attn_pair_ws_bytes(int B, int H, int D, int topk, int W, int Nh) {
-    return align256(attn_ws_bytes(B, 1, H, D, 1, topk, W)) + attn_ws_bytes(B, 1, H, D, 0, Nh, 0);
+    size_t s = align256(attn_ws_bytes(B, 1, H, D, 1, topk, W)) + attn_ws_bytes(B, 1, H, D, 0, Nh, 0);
+    if (use128(D, H)) {
+        int rps, ns_s, ns_d;
+        a128_pair_split(B, H, topk, W, Nh, &rps, &ns_s, &ns_d);
+        s = std::max(s, align256(part_bytes(B, ns_s, H, D)) + part_bytes(B, ns_d, H, D));
+    }
+    return s;
 }
 
 int attn_pair_launch(const void* q_s, const AttnRows& as, void* out_s, float* lse_s, const void* q_d,
@@ -918,6 +928,29 @@ int attn_pair_launch(const void* q_s, const AttnRows& as, void* out_s, float* ls
         R.topk = a.topk; R.kv_raw = (const uint16_t*)a.kv_raw; R.Lr = a.Lr; R.raw0 = a.raw0; R.W = a.W;
         return R;
     };
+    const float sl2_ = scale * LOG2E;
+    if (use128(D, H)) {
+        int rps, ns[2];
+        a128_pair_split(B, H, as.topk, as.W, ad.N, &rps, &ns[0], &ns[1]);
+        AttnJob j2[2] = {};
+        char* wp = (char*)ws;
+        for (int k = 0; k < 2; ++k) {
+            const AttnRows& a = k == 0 ? as : ad;
+            AttnJob& j = j2[k];
+            j.q = (const uint16_t*)(k == 0 ? q_s : q_d);
+            j.R = rows_of(a);
+            j.Tq = 1; j.H = H; j.pos0 = pos0; j.scale_log2 = sl2_;
+            j.nsplit = ns[k]; j.rps = rps; j.nunits = B * ns[k];
+            j.out = (uint16_t*)(k == 0 ? out_s : out_d);
+            j.lse = k == 0 ? lse_s : lse_d;
+            if (ns[k] > 1) {
+                j.part_o = (float*)wp;
+                j.part_ml = (float2*)(wp + align256((size_t)B * ns[k] * H * D * 4));
+            }
+            wp += align256(part_bytes(B, ns[k], H, D));
+        }
+        return attn128_pair_launch(j2[0], j2[1], st, "k_attn_pair");
+    }
     const int HP = (H + 63) / 64;
     const float sl2 = scale * LOG2E;
     AttnJob js{}, jd{};

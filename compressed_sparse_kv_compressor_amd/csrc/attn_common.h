@@ -1,0 +1,79 @@
+// attn_common.h -- row sets, job records and tile constants shared by the MQA attention kernels.
+//
+// Method: "DeepSeek-V4 技术解析：架构革新与 Coding Agent 后训练优化", section 1.1 (CSA attends to the
+// selected compressed entries plus a window of raw tokens; HCA attends to every compressed entry).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace csa_attn {
+
+constexpr int TILE = 32;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+struct Rows {
+    int mode;
+    const uint16_t* kv;
+    int N;
+    long long L;
+    int ratio;
+    const int32_t* idx;
+    int topk;
+    const uint16_t* kv_raw;
+    int Lr;
+    long long raw0;
+    int W;
+};
+
+__device__ __forceinline__ int dense_visible(long long p, long long L, int m, int N) {
+    if (p >= L - 1) return N;
+    long long v = (p + 1) / m;
+    return v < N ? (int)v : N;
+}
+
+// 16-byte chunk c of row r is stored at chunk c ^ f(r & 15), f(x) = 4 (x & 3) + (x >> 2): any 16
+// consecutive rows at one chunk, and any 4 aligned rows x 4 aligned chunks (the footprint of a
+// transposed read), fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_chunk(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Raw buffer resource (stride 0, byte offsets) over [base, base + bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Masked rows get -2^100 added to their scores by one extra MFMA k-step (A: a 1 in column 0 of each
+// masked row; B: -2^100 in row 0 of one k-step of the contraction), which sends their probabilities to exactly 0
+// without any per-element select on the common path.  A split with no valid row at all ends with a
+// running max below EMPTY_M, which the output step treats as empty.
+constexpr uint32_t BF16_ONE = 0x3f80u, BF16_NEG_2P100 = 0xf180u;
+constexpr float EMPTY_M = -1.0e25f;
+
+// One attention problem of a fused launch.
+struct AttnJob {
+    const uint16_t* q;
+    Rows R;
+    int Tq, H;
+    long long pos0;
+    float scale_log2;
+    int nunits, nsplit, rps;
+    float* part_o;
+    float2* part_ml;
+    uint16_t* out;
+    float* lse;
+};
+
+}  // namespace csa_attn
+
+namespace csa_host {
+// k_attn128 (attn128.hip): D = 512, H % 128 == 0, every array within reach of 32-bit byte offsets.
+// Rows per split must be a multiple of ATT128_UNIT and at most ATT128_MAX_RPS.
+constexpr int ATT128_UNIT = 128, ATT128_MAX_RPS = 2048;
+// Each launches the attention and, for jobs with more than one split, the merge of the split partials
+// (part_o then holds fp16 partials, half the bytes of the fp32 ones of k_attn64; part_ml as there).
+int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag);
+// both jobs (same H, Tq = 1 each) in one attention launch and one merge launch
+int attn128_pair_launch(const csa_attn::AttnJob& js, const csa_attn::AttnJob& jd, hipStream_t st, const char* tag);
+}  // namespace csa_host

@@ -333,6 +333,11 @@ SPARSE_CASES = [
     (1, 1, 96, 512, 2000, 300, 128, 1.0),      # 96 heads: the last head pair is half
     (3, 1, 128, 512, 9000, 2048, 128, 1.0),    # long top-k: several tiles per split
     (1, 96, 64, 512, 3000, 256, 128, 1.0),     # prefill-shaped: many queries, each with its own window
+    # 128-head workgroups (k_attn128)
+    (1, 3, 128, 512, 800, 100, 20, 2.0),       # several queries, ragged top-k, short window
+    (1, 1, 128, 512, 100, 0, 17, 1.0),         # window only
+    (2, 1, 256, 512, 3000, 300, 0, 1.0),       # two head quads, no window
+    (1, 1, 128, 512, 70000, 2048, 128, 1.0),   # one query: many splits of the selected rows
 ]
 
 
@@ -375,6 +380,10 @@ DENSE_CASES = [
     (1, 3, 96, 512, 128 * 50 + 7, 128, 4.0),   # several queries, 96 heads, ragged tail tile
     (2, 1, 32, 512, 4 * 700, 4, 1.0),          # one head group
     (1, 1, 64, 512, 128 * 20000, 128, 1.0),    # long prefix: many splits and tiles
+    # 128-head workgroups (k_attn128)
+    (1, 5, 128, 512, 4 * 33, 4, 4.0),          # causal visibility per query (mostly masked tiles)
+    (1, 1, 128, 512, 128 * 20000 + 9, 128, 1.0),   # long prefix: many splits, ragged last one
+    (3, 2, 256, 512, 4 * 500, 4, 1.0),         # two head quads, two queries
 ]
 
 
@@ -394,10 +403,11 @@ def test_dense_attn_parity(b, case):
     assert np.allclose(lse.cpu().numpy(), wlse, atol=2e-2, rtol=0)
 
 
-def test_dense_attn_no_visible_entry(b):
-    q, kv = synth.attn_inputs(32, 1, 1, 16, 128, 4, "nv_")
-    out = torch.full((1, 1, 16, 128), 7, dtype=torch.int16, device=DEV)
-    lse = torch.empty((1, 1, 16), dtype=torch.float32, device=DEV)
+@pytest.mark.parametrize("H,D", [(16, 128), (128, 512)])
+def test_dense_attn_no_visible_entry(b, H, D):
+    q, kv = synth.attn_inputs(32, 1, 1, H, D, 4, "nv_")
+    out = torch.full((1, 1, H, D), 7, dtype=torch.int16, device=DEV)
+    lse = torch.empty((1, 1, H), dtype=torch.float32, device=DEV)
     b.hca_dense_attn(dev(q), dev(kv), 16, 4, 2, 0.1, out, lse)   # p = 2: no block complete
     torch.cuda.synchronize()
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
@@ -550,10 +560,20 @@ def test_fused_decode_matches_oracle_and_separate_calls(b, L, B, H, D, HI, dI, t
     assert np.array_equal(idx.cpu().numpy(), want_idx[:, 0])
     assert_rows_close(host_bf16(csa_out), want_csa, what="csa layer")
     assert_rows_close(host_bf16(hca_out), want_hca, what="hca layer")
-    # the fused call equals the separate entry points bitwise
+    # the separate entry points agree with the fused call (their splits of the rows may differ, so to
+    # rounding), and a repeated fused call is bitwise identical
     o1 = torch.empty((B, 1, H, D), dtype=torch.int16, device=DEV)
     o2 = torch.empty_like(o1)
     b.csa_sparse_attn(t["csa_q"], t["kv"], idx.view(B, 1, topk), t["raw"], L - cfg.W, p, cfg.W, cfg.scale, o1)
     b.hca_dense_attn(t["hca_q"], t["kv_h"], L, 128, p, cfg.scale, o2)
     torch.cuda.synchronize()
-    assert torch.equal(o1.view(B, H, D), csa_out) and torch.equal(o2.view(B, H, D), hca_out)
+    assert_rows_close(host_bf16(o1.view(B, H, D)), bf16_f64(host_bf16(csa_out)), what="csa separate")
+    assert_rows_close(host_bf16(o2.view(B, H, D)), bf16_f64(host_bf16(hca_out)), what="hca separate")
+    c2, h2 = torch.empty_like(csa_out), torch.empty_like(hca_out)
+    args2 = b.make_decode_args(L=L, scale=cfg.scale, csa_q=t["csa_q"].view(B, H, D), q_idx=t["q_idx"],
+                               w_idx=t["w_idx"], k_idx=t["k_idx"], kv=t["kv"], kv_raw=t["raw"], idx_dtype=dt, m=4,
+                               topk=topk, W=cfg.W, csa_out=c2, hca_q=t["hca_q"].view(B, H, D), kv_h=t["kv_h"],
+                               mh=128, hca_out=h2, idx_out=idx)
+    b.csa_hca_decode(args2)
+    torch.cuda.synchronize()
+    assert torch.equal(c2, csa_out) and torch.equal(h2, hca_out)
