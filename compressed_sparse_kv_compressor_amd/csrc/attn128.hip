@@ -79,21 +79,27 @@ __device__ __forceinline__ void attn128_body(
     const int s_end = min(nrows, s_begin + rps);
     const int ntiles = s_begin < nrows ? rps / TILE : 0;   // same for every non-empty split
 
-    // MODE 1: the split's entry indices (selected region only), staged once in LDS
-    if (MODE == 1) {
-        const int nc = max(0, min(s_end, topk32) - s_begin);
-        for (int i = threadIdx.x; i < nc; i += A_TPB) {
-            const int r = s_begin + i;
-            rcode[i] = r < R.topk ? R.idx[(size_t)bt * R.topk + r] : -1;
+    const int raw_first = MODE == 1 ? (int)(w0 - R.raw0) : 0;      // raw row of the first window row
+    // The row of every slot the split will load, staged once in LDS: the entry (dense rows, selected
+    // entries) or the raw row (window); -1 for masked slots (unselected padding, rows past the visible
+    // ones, and the tiles loaded past the end), which load row 0 and get no weight.
+    const int nstage = ntiles * TILE + NBUF * TILE;
+    for (int i = threadIdx.x; i < nstage; i += A_TPB) {
+        const int r = s_begin + i;
+        int v = -1;
+        if (r < s_end) {
+            if (MODE == 0) v = r;
+            else if (r < R.topk) v = R.idx[(size_t)bt * R.topk + r];
+            else if (r >= topk32) v = raw_first + (r - topk32);
         }
-        __syncthreads();
+        rcode[i] = v;
     }
+    __syncthreads();
 
     const uint16_t* kvb = R.kv ? R.kv + (size_t)b * R.N * D : nullptr;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
     const __amdgpu_buffer_rsrc_t rs_kv = make_rsrc(kvb, kvb ? (uint32_t)((size_t)R.N * ROWB) : 0u);
     const __amdgpu_buffer_rsrc_t rs_raw = make_rsrc(rawb, rawb ? (uint32_t)((size_t)R.Lr * ROWB) : 0u);
-    const int raw_first = MODE == 1 ? (int)(w0 - R.raw0) : 0;      // raw row of the first window row
 
     bf16x8_t qreg[KS];
     {
@@ -112,50 +118,29 @@ __device__ __forceinline__ void attn128_body(
     // ---- tile loads ----
     // Wave w moves row slots 8w .. 8w+7 of a tile, one 1 KiB row per instruction (16 B per lane, landing
     // at slot * 1 KiB + 16 lane); the XOR swizzle goes on the source: lane l fetches logical chunk
-    // l ^ f(slot).  The row is wave-uniform (scalar offset); slots past the rows of the split, and whole
-    // tiles past the end, load a valid row whose data is never weighted.
+    // l ^ f(slot).  The rows come from the staged list (wave-uniform scalar offsets); a tile of window
+    // rows reads the raw array.  One group of 8 loads serves every kind of tile, so the compiler's
+    // tracking of loads into LDS stays exact (a read waits only for the loads of its own buffer).
     const uint32_t lane16 = 16u * (uint32_t)lane;
     auto issue = [&](uint16_t* bufp, int t) {
         CSA_LDS char* lb = (CSA_LDS char*)bufp + w * 8 * ROWB;
-        const int r0 = s_begin + t * TILE;
-        auto bdma = [&](__amdgpu_buffer_rsrc_t rs, int k, uint32_t row) {
-            const uint32_t voff = lane16 ^ (16u * (uint32_t)swz_chunk(8 * w + k));   // w, k uniform
+        const bool from_raw = MODE == 1 && s_begin + t * TILE >= topk32 && R.W > 0;
+        const __amdgpu_buffer_rsrc_t rs = from_raw ? rs_raw : rs_kv;
+        const CSA_LDS int* cp = (const CSA_LDS int*)rcode + t * TILE + 8 * w;
+        const u32x4_t c0 = *(const CSA_LDS u32x4_t*)cp, c1 = *(const CSA_LDS u32x4_t*)(cp + 4);
+        uint32_t l16 = lane16;
+        asm volatile("" : "+v"(l16));             // per-issue lane offsets (nothing held across the loop)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = (int)__builtin_amdgcn_readfirstlane(k < 4 ? c0[k] : c1[k - 4]);
+            const uint32_t row = (uint32_t)(c >= 0 ? c : 0);
+            const uint32_t voff = l16 ^ (16u * (uint32_t)swz_chunk(8 * w + k));   // w, k uniform
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (CSA_LDS void*)(lb + ROWB * k), 16, (int)voff,
                                                      (int)(row * ROWB), 0, 0);
-        };
-        const bool from_raw = MODE == 1 && r0 >= topk32 && R.W > 0;
-        if (!from_raw) {
-            if (MODE == 1 && r0 < s_end) {             // selected entries (-1 slots read entry 0)
-                const CSA_LDS int* cp = (const CSA_LDS int*)rcode + (r0 - s_begin) + 8 * w;
-                const u32x4_t c0 = *(const CSA_LDS u32x4_t*)cp, c1 = *(const CSA_LDS u32x4_t*)(cp + 4);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int c = (int)__builtin_amdgcn_readfirstlane(k < 4 ? c0[k] : c1[k - 4]);
-                    bdma(rs_kv, k, (uint32_t)(c >= 0 ? c : 0));
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int r = r0 + 8 * w + k;
-                    bdma(rs_kv, k, (uint32_t)(MODE == 0 && r < s_end ? r : 0));
-                }
-            }
-        } else {                                       // raw window rows
-            const int u0 = raw_first + (r0 - topk32);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int r = r0 + 8 * w + k;
-                bdma(rs_raw, k, (uint32_t)(r < s_end ? u0 + 8 * w + k : raw_first));
-            }
         }
     };
     // the lane's row (slot hl) of tile t is a valid row
-    auto row_ok = [&](int t) -> bool {
-        const int r0 = s_begin + t * TILE;
-        if (r0 >= s_end) return false;
-        if (MODE == 1 && r0 < topk32) return rcode[(r0 - s_begin) + hl] >= 0;
-        return r0 + hl < s_end;
-    };
+    auto row_ok = [&](int t) -> bool { return rcode[t * TILE + hl] >= 0; };
 
     // ---- LDS reads ----
     // QK: k-step s of row hl is logical chunk 2s + g, stored at (2s + g) ^ f(hl): offset qk_off ^ 32 s.
@@ -420,20 +405,11 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
     __shared__ __attribute__((aligned(1024))) uint16_t buf1[TILE * 512];    \
     __shared__ __attribute__((aligned(1024))) uint16_t buf2[TILE * 512];    \
     __shared__ __attribute__((aligned(1024))) uint16_t buf3[TILE * 512];    \
-    __shared__ __attribute__((aligned(16))) int rcode[csa_host::ATT128_MAX_RPS];
+    __shared__ __attribute__((aligned(16))) int rcode[csa_host::ATT128_MAX_RPS + NBUF * TILE];
 
-__global__ __launch_bounds__(A_TPB, 1) void k_attn128(
-    const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
-    int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
-    float* __restrict__ lse)
-{
-    CSA_A128_LDS
-    attn128_body(blockIdx.x, buf0, buf1, buf2, buf3, rcode, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
-                 part_o, part_ml, out, lse);
-}
-
-// Two jobs in one launch (the CSA sparse and the HCA dense attention of a decode step): workgroups
-// [0, nblk_s) take job s, the rest job d.
+// One or two jobs in one launch (the CSA sparse and the HCA dense attention of a decode step):
+// workgroups [0, nblk_s) take job s, the rest job d.  A single job is launched with every workgroup
+// below nblk_s (one kernel, so one register allocation serves both uses).
 __global__ __launch_bounds__(A_TPB, 1) void k_attn128_pair(AttnJob js, AttnJob jd, int nblk_s)
 {
     CSA_A128_LDS
@@ -444,16 +420,8 @@ __global__ __launch_bounds__(A_TPB, 1) void k_attn128_pair(AttnJob js, AttnJob j
 }
 #undef CSA_A128_LDS
 
-// grid (32, HQ, BT): 256 threads x 32 = the 8192 chunk positions of one query and head quad
-__global__ __launch_bounds__(256) void k_combine128(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
-                                                    int H, int nsplit, uint16_t* __restrict__ out,
-                                                    float* __restrict__ lse)
-{
-    combine128_body((const uint16_t*)part_o, part_ml, H, nsplit, out, lse, blockIdx.z, blockIdx.y,
-                    blockIdx.x * 256 + threadIdx.x);
-}
-
-// The merges of a fused launch: grid (32, HQ, nbt_s + nbt_d); z < nbt_s merges job s, the rest job d.
+// The merges of one or two jobs: grid (32, HQ, nbt_s + nbt_d); z < nbt_s merges job s, the rest job d;
+// 256 threads x 32 cover the 8192 chunk positions of one query and head quad.
 __global__ __launch_bounds__(256) void k_combine128_pair(AttnJob js, AttnJob jd, int nbt_s)
 {
     const bool first = (int)blockIdx.z < nbt_s;
@@ -468,11 +436,10 @@ namespace csa_host {
 
 int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag) {
     const int HQ = j.H / 128, BT = j.nunits / j.nsplit;
-    CSA_LAUNCH(tag, k_attn128, dim3(j.nunits * HQ), dim3(A_TPB), 0, st, j.q, j.R, j.Tq, j.H, j.pos0, j.scale_log2,
-               j.nunits, j.nsplit, j.rps, j.part_o, j.part_ml, j.out, j.lse);
+    const int nblk = j.nunits * HQ;
+    CSA_LAUNCH(tag, k_attn128_pair, dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
     if (j.nsplit > 1)
-        CSA_LAUNCH("k_combine", k_combine128, dim3(32, HQ, BT), dim3(256), 0, st, j.part_o, j.part_ml, j.H, j.nsplit,
-                   j.out, j.lse);
+        CSA_LAUNCH("k_combine", k_combine128_pair, dim3(32, HQ, BT), dim3(256), 0, st, j, j, BT);
     return 0;
 }
 
