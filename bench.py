@@ -40,7 +40,7 @@ DOMINANT = "k_score"
 PREFILL_DOMINANT = "k_pscore"
 PREFILL_KERNELS = ("k_pzero", "k_pnorm", "k_pscore_sample", "k_pthresh", "k_pscore", "k_pselect", "k_pfb_score",
                    "k_pfb_select", "k_pfallback")
-KERNELS = ("k_fill", "k_score", "k_collect", "k_select", "k_attn_pair", "k_attn_sparse", "k_attn_dense", "k_combine")
+KERNELS = ("k_fill", "k_score", "k_collect", "k_select", "k_attn_sparse", "k_attn_dense", "k_combine")
 
 
 def kernel_source_sha() -> str:
@@ -292,7 +292,7 @@ def prefill_leg(args, dev, cpu=True):
     return res
 
 
-COMPRESS_KERNELS = ("k_pool2", "k_pool", "k_gemm2", "k_g2reduce", "k_gemm", "k_fill", "k_score", "k_collect", "k_select", "k_attn_pair", "k_attn_sparse",
+COMPRESS_KERNELS = ("k_pool2", "k_pool", "k_gemm2", "k_g2reduce", "k_gemm", "k_fill", "k_score", "k_collect", "k_select", "k_attn_sparse",
                     "k_attn_dense", "k_combine")
 
 
@@ -385,7 +385,7 @@ def compress_leg(args, dev, cpu=True):
         res["compress"]["parity_sample"] = compress_parity(cc, X, (wkv, wik, gate, bslot), (wkv_h, gate_h, bslot_h),
                                                            kv, ik, win, kv_h)
 
-    # the decode stack: CSA, HCA, CSA, HCA (two fused pairs), one query per sequence, against the caches
+    # the decode stack: CSA, HCA, CSA, HCA (two csa_hca_decode calls), one query per sequence, against the caches
     g = synth.parallel_bits_to_device
     pairs = []
     for layer in range(cc.layers // 2):

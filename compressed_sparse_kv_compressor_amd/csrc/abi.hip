@@ -338,7 +338,8 @@ size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a) {
     const int Nc = (int)((a->L + a->m - 1) / a->m), Nh = (int)((a->L + a->mh - 1) / a->mh);
     size_t s = a->idx_out ? 0 : align256((size_t)a->B * a->topk * 4);
     s += align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk));
-    s += csa_host::attn_pair_ws_bytes(a->B, a->H, a->D, a->topk, a->W, Nh);
+    s += align256(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 1, a->topk, a->W));
+    s += csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 0, Nh, 0);
     return s;
 }
 
@@ -375,10 +376,8 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     const size_t aws = ws_bytes - (size_t)(w - (char*)ws);
     csa_host::AttnRows rs{1, a->kv, Nc, 0, 1, idx, a->topk, a->kv_raw, a->W, a->L - a->W, a->W};
     csa_host::AttnRows rd{0, a->kv_h, Nh, a->L, a->mh, nullptr, 0, nullptr, 0, 0, 0};
-    // both attentions in one launch when the kernel allows it, else one after the other
-    rc = csa_host::attn_pair_launch(a->csa_q, rs, a->csa_out, a->csa_lse, a->hca_q, rd, a->hca_out, a->hca_lse,
-                                    a->B, a->H, a->D, p, a->scale, w, st);
-    if (rc >= 0) return rc;
+    // the CSA layer's attention, then the HCA layer's (layer order: a real next layer's query depends on the
+    // previous layer's output, so the two are never overlapped)
     const size_t sws = align256(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 1, a->topk, a->W));
     rc = csa_host::attn_launch(a->csa_q, rs, a->B, 1, a->H, a->D, p, a->scale, a->csa_out, a->csa_lse, w, sws, st,
                                "k_attn_sparse");

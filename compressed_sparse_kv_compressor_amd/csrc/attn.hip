@@ -644,19 +644,6 @@ __global__ __launch_bounds__(TPB, 1) void k_attn64(
                            part_o, part_ml, out, lse);
 }
 
-// CSA sparse (workgroups [0, nblk_s)) and HCA dense attention in one launch: the short, latency-bound
-// sparse workgroups run beside the dense ones instead of before them.
-template <bool BIG>
-__global__ __launch_bounds__(TPB, 1) void k_attn64_pair(AttnJob js, AttnJob jd, int nblk_s)
-{
-    CSA_ATT64_LDS
-    if ((int)blockIdx.x < nblk_s)
-        attn64_body<1, BIG>(blockIdx.x, bufA, bufB, bufC, sx, js.q, js.R, js.Tq, js.H, js.pos0, js.scale_log2,
-                            js.nunits, js.nsplit, js.rps, js.part_o, js.part_ml, js.out, js.lse);
-    else
-        attn64_body<0, BIG>(blockIdx.x - nblk_s, bufA, bufB, bufC, sx, jd.q, jd.R, jd.Tq, jd.H, jd.pos0,
-                            jd.scale_log2, jd.nunits, jd.nsplit, jd.rps, jd.part_o, jd.part_ml, jd.out, jd.lse);
-}
 #undef CSA_ATT64_LDS
 
 // Merge split partials in split order: out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.  Thread tid
@@ -712,15 +699,6 @@ __global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ par
                                                    int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse)
 {
     combine_body<D>(part_o, part_ml, H, nsplit, out, lse, blockIdx.x, blockIdx.y);
-}
-
-// The combines of a fused launch: rows y < nbt_s of the grid merge job s, the rest job d.
-__global__ __launch_bounds__(128) void k_combine_pair(AttnJob js, AttnJob jd, int nbt_s)
-{
-    if ((int)blockIdx.y < nbt_s)
-        combine_body<512>(js.part_o, js.part_ml, js.H, js.nsplit, js.out, js.lse, blockIdx.x, blockIdx.y);
-    else
-        combine_body<512>(jd.part_o, jd.part_ml, jd.H, jd.nsplit, jd.out, jd.lse, blockIdx.x, blockIdx.y - nbt_s);
 }
 
 }  // namespace
@@ -888,98 +866,6 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
                        (uint16_t*)out, lse);
     } else {
         return fail(6, "attention: D = %d unsupported", D);
-    }
-    return 0;
-}
-
-
-// CSA sparse + HCA dense attention of one decode step in a single launch (and a single combine), when
-// both take k_attn64 with 32-bit offsets; returns -1 when it does not apply (the caller launches them
-// apart), else 0 or a status code.
-// Workspace: the sparse partials, then the dense partials.
-// k_attn128 pair: one rows-per-split for both jobs, from their tiles together.
-static void a128_pair_split(int B, int H, int topk, int W, int Nh, int* rps, int* ns_s, int* ns_d) {
-    const int rs = a128_rows(1, topk, W), rd = Nh;
-    *rps = a128_rps((long long)B * (H / 128) * (a128_tiles(rs) + a128_tiles(rd)));
-    *ns_s = a128_nsplit(rs, *rps);
-    *ns_d = a128_nsplit(rd, *rps);
-}
-
-size_t attn_pair_ws_bytes(int B, int H, int D, int topk, int W, int Nh) {
-    size_t s = align256(attn_ws_bytes(B, 1, H, D, 1, topk, W)) + attn_ws_bytes(B, 1, H, D, 0, Nh, 0);
-    if (use128(D, H)) {
-        int rps, ns_s, ns_d;
-        a128_pair_split(B, H, topk, W, Nh, &rps, &ns_s, &ns_d);
-        s = std::max(s, align256(part_bytes(B, ns_s, H, D)) + part_bytes(B, ns_d, H, D));
-    }
-    return s;
-}
-
-int attn_pair_launch(const void* q_s, const AttnRows& as, void* out_s, float* lse_s, const void* q_d,
-                     const AttnRows& ad, void* out_d, float* lse_d, int B, int H, int D, long long pos0, float scale,
-                     void* ws, hipStream_t st) {
-    if (!use64(D, H)) return -1;
-    const bool big = (size_t)as.N * D * 2 > 0xffffffffull || (size_t)as.Lr * D * 2 > 0xffffffffull ||
-                     (size_t)ad.N * D * 2 > 0xffffffffull;
-    if (big) return -1;
-    auto rows_of = [](const AttnRows& a) {
-        Rows R;
-        R.mode = a.mode; R.kv = (const uint16_t*)a.kv; R.N = a.N; R.L = a.L; R.ratio = a.ratio; R.idx = a.idx;
-        R.topk = a.topk; R.kv_raw = (const uint16_t*)a.kv_raw; R.Lr = a.Lr; R.raw0 = a.raw0; R.W = a.W;
-        return R;
-    };
-    const float sl2_ = scale * LOG2E;
-    if (use128(D, H)) {
-        int rps, ns[2];
-        a128_pair_split(B, H, as.topk, as.W, ad.N, &rps, &ns[0], &ns[1]);
-        AttnJob j2[2] = {};
-        char* wp = (char*)ws;
-        for (int k = 0; k < 2; ++k) {
-            const AttnRows& a = k == 0 ? as : ad;
-            AttnJob& j = j2[k];
-            j.q = (const uint16_t*)(k == 0 ? q_s : q_d);
-            j.R = rows_of(a);
-            j.Tq = 1; j.H = H; j.pos0 = pos0; j.scale_log2 = sl2_;
-            j.nsplit = ns[k]; j.rps = rps; j.nunits = B * ns[k];
-            j.out = (uint16_t*)(k == 0 ? out_s : out_d);
-            j.lse = k == 0 ? lse_s : lse_d;
-            if (ns[k] > 1) {
-                j.part_o = (float*)wp;
-                j.part_ml = (float2*)(wp + align256((size_t)B * ns[k] * H * D * 4));
-            }
-            wp += align256(part_bytes(B, ns[k], H, D));
-        }
-        return attn128_pair_launch(j2[0], j2[1], st, "k_attn_pair");
-    }
-    const int HP = (H + 63) / 64;
-    const float sl2 = scale * LOG2E;
-    AttnJob js{}, jd{};
-    char* wsp = (char*)ws;
-    int nblk[2], nbt[2];
-    for (int k = 0; k < 2; ++k) {
-        const AttnRows& a = k == 0 ? as : ad;
-        AttnJob& j = k == 0 ? js : jd;
-        const int max_rows = a.mode == 0 ? a.N : attn_rows(1, H, D, a.topk, a.W);
-        int ns, rps;
-        choose_split(B, H, D, max_rows, &ns, &rps);
-        j.q = (const uint16_t*)(k == 0 ? q_s : q_d);
-        j.R = rows_of(a);
-        j.Tq = 1; j.H = H; j.pos0 = pos0; j.scale_log2 = sl2;
-        j.nunits = B * ns; j.nsplit = ns; j.rps = rps;
-        j.out = (uint16_t*)(k == 0 ? out_s : out_d);
-        j.lse = k == 0 ? lse_s : lse_d;
-        if (ns > 1) {
-            j.part_o = (float*)wsp;
-            j.part_ml = (float2*)(wsp + align256((size_t)B * ns * H * D * 4));
-        }
-        wsp += align256(attn_ws_bytes(B, 1, H, D, a.mode, a.mode == 0 ? a.N : a.topk, a.W));
-        nblk[k] = (j.nunits + 7) / 8 * 8 * HP;
-        nbt[k] = ns > 1 ? B : 0;
-    }
-    CSA_LAUNCH("k_attn_pair", k_attn64_pair<false>, dim3(nblk[0] + nblk[1]), dim3(TPB), 0, st, js, jd, nblk[0]);
-    if (nbt[0] + nbt[1] > 0) {
-        AttnJob j0 = nbt[0] ? js : jd, j1 = jd;
-        CSA_LAUNCH("k_combine", k_combine_pair, dim3(H, nbt[0] + nbt[1]), dim3(128), 0, st, j0, j1, nbt[0]);
     }
     return 0;
 }

@@ -407,10 +407,10 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
     __shared__ __attribute__((aligned(1024))) uint16_t buf3[TILE * 512];    \
     __shared__ __attribute__((aligned(16))) int rcode[csa_host::ATT128_MAX_RPS + NBUF * TILE];
 
-// One or two jobs in one launch (the CSA sparse and the HCA dense attention of a decode step):
-// workgroups [0, nblk_s) take job s, the rest job d.  A single job is launched with every workgroup
-// below nblk_s (one kernel, so one register allocation serves both uses).
-__global__ __launch_bounds__(A_TPB, 1) void k_attn128_pair(AttnJob js, AttnJob jd, int nblk_s)
+// Two job slots: workgroups [0, nblk_s) run job s, the rest job d; one job is launched with every workgroup
+// below nblk_s.  (With the parameters selected per workgroup like this the compiler allocates the body's
+// registers without spills; with the job's fields passed straight in it spilled ~100 VGPRs.)
+__global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, int nblk_s)
 {
     CSA_A128_LDS
     const bool first = (int)blockIdx.x < nblk_s;
@@ -420,14 +420,11 @@ __global__ __launch_bounds__(A_TPB, 1) void k_attn128_pair(AttnJob js, AttnJob j
 }
 #undef CSA_A128_LDS
 
-// The merges of one or two jobs: grid (32, HQ, nbt_s + nbt_d); z < nbt_s merges job s, the rest job d;
-// 256 threads x 32 cover the 8192 chunk positions of one query and head quad.
-__global__ __launch_bounds__(256) void k_combine128_pair(AttnJob js, AttnJob jd, int nbt_s)
+// grid (32, HQ, BT): 256 threads x 32 cover the 8192 chunk positions of one query and head quad
+__global__ __launch_bounds__(256) void k_combine128(AttnJob j)
 {
-    const bool first = (int)blockIdx.z < nbt_s;
-    const AttnJob& j = first ? js : jd;
-    combine128_body((const uint16_t*)j.part_o, j.part_ml, j.H, j.nsplit, j.out, j.lse,
-                    first ? blockIdx.z : blockIdx.z - nbt_s, blockIdx.y, blockIdx.x * 256 + threadIdx.x);
+    combine128_body((const uint16_t*)j.part_o, j.part_ml, j.H, j.nsplit, j.out, j.lse, blockIdx.z, blockIdx.y,
+                    blockIdx.x * 256 + threadIdx.x);
 }
 
 }  // namespace
@@ -437,19 +434,8 @@ namespace csa_host {
 int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag) {
     const int HQ = j.H / 128, BT = j.nunits / j.nsplit;
     const int nblk = j.nunits * HQ;
-    CSA_LAUNCH(tag, k_attn128_pair, dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
-    if (j.nsplit > 1)
-        CSA_LAUNCH("k_combine", k_combine128_pair, dim3(32, HQ, BT), dim3(256), 0, st, j, j, BT);
-    return 0;
-}
-
-int attn128_pair_launch(const csa_attn::AttnJob& js, const csa_attn::AttnJob& jd, hipStream_t st, const char* tag) {
-    const int HQ = js.H / 128;
-    CSA_LAUNCH(tag, k_attn128_pair, dim3((js.nunits + jd.nunits) * HQ), dim3(A_TPB), 0, st, js, jd, js.nunits * HQ);
-    const int nbt0 = js.nsplit > 1 ? js.nunits / js.nsplit : 0, nbt1 = jd.nsplit > 1 ? jd.nunits / jd.nsplit : 0;
-    if (nbt0 + nbt1 > 0)
-        CSA_LAUNCH("k_combine", k_combine128_pair, dim3(32, HQ, nbt0 + nbt1), dim3(256), 0, st, nbt0 ? js : jd, jd,
-                   nbt0);
+    CSA_LAUNCH(tag, k_attn128, dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
+    if (j.nsplit > 1) CSA_LAUNCH("k_combine", k_combine128, dim3(32, HQ, BT), dim3(256), 0, st, j);
     return 0;
 }
 

@@ -51,7 +51,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 constexpr uint32_t BF16_ONE = 0x3f80u, BF16_NEG_2P100 = 0xf180u;
 constexpr float EMPTY_M = -1.0e25f;
 
-// One attention problem of a fused launch.
+// One attention problem (the parameters of one launch).
 struct AttnJob {
     const uint16_t* q;
     Rows R;
@@ -71,9 +71,7 @@ namespace csa_host {
 // k_attn128 (attn128.hip): D = 512, H % 128 == 0, every array within reach of 32-bit byte offsets.
 // Rows per split must be a multiple of ATT128_UNIT and at most ATT128_MAX_RPS.
 constexpr int ATT128_UNIT = 128, ATT128_MAX_RPS = 2048;
-// Each launches the attention and, for jobs with more than one split, the merge of the split partials
+// Launches the attention and, for a job with more than one split, the merge of the split partials
 // (part_o then holds fp16 partials, half the bytes of the fp32 ones of k_attn64; part_ml as there).
 int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag);
-// both jobs (same H, Tq = 1 each) in one attention launch and one merge launch
-int attn128_pair_launch(const csa_attn::AttnJob& js, const csa_attn::AttnJob& jd, hipStream_t st, const char* tag);
 }  // namespace csa_host

@@ -39,12 +39,6 @@ struct AttnRows {
 size_t attn_ws_bytes(int B, int Tq, int H, int D, int mode, int n, int W);
 int attn_launch(const void* q, const AttnRows& rows, int B, int Tq, int H, int D, long long pos0, float scale,
                 void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t st, const char* tag);
-// sparse (as) + dense (ad) attention of one decode step (Tq = 1) in one launch; returns -1 if not applicable
-size_t attn_pair_ws_bytes(int B, int H, int D, int topk, int W, int Nh);
-int attn_pair_launch(const void* q_s, const AttnRows& as, void* out_s, float* lse_s, const void* q_d,
-                     const AttnRows& ad, void* out_d, float* lse_d, int B, int H, int D, long long pos0, float scale,
-                     void* ws, hipStream_t st);
-
 size_t compress_ws_bytes(int B, long long L, int Dh, int D, int dI, int m, int W);
 size_t hca_compress_ws_bytes(int B, long long L, int Dh, int D, int dI, int m, int W, int mh);
 int hca_compress_launch(const void* hidden, const void* w_kv, const void* w_ik, const float* w_gate,
