@@ -357,14 +357,14 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
     const float2* mlp = part_ml + (slot0 * 4 + w) * 32 + hl;       // split s at mlp[s HQ 128]
     const uint16_t* pp = part + (((slot0 * 4 + w) * 32 + c) * 64 + lane) * 8;   // split s at pp[s HQ 2^19]
     const size_t ml_step = (size_t)HQ * 128, p_step = (size_t)HQ * 4 * 32 * 64 * 8;
-    constexpr int U = 8;                                           // splits in flight
+    constexpr int UM = 32, U = 16;                                 // splits in flight (maxima, partials)
     float M = -INFINITY;
-    for (int s0 = 0; s0 < nsplit; s0 += U) {
-        float mv[U];
+    for (int s0 = 0; s0 < nsplit; s0 += UM) {
+        float mv[UM];
 #pragma unroll
-        for (int u = 0; u < U; ++u) mv[u] = s0 + u < nsplit ? mlp[(size_t)(s0 + u) * ml_step].x : -INFINITY;
+        for (int u = 0; u < UM; ++u) mv[u] = s0 + u < nsplit ? mlp[(size_t)(s0 + u) * ml_step].x : -INFINITY;
 #pragma unroll
-        for (int u = 0; u < U; ++u) M = fmaxf(M, mv[u]);
+        for (int u = 0; u < UM; ++u) M = fmaxf(M, mv[u]);
     }
     float l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
