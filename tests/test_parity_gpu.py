@@ -413,6 +413,38 @@ def test_dense_attn_no_visible_entry(b, H, D):
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
 
 
+def test_dense_attn_some_splits_empty(b):
+    # early query positions over a long prefix (m' = 1): the rows are split for the longest prefix, so the
+    # later splits of these queries hold no visible row and must merge as empty partials
+    B, Tq, H, D, L, mh, pos0 = 1, 3, 128, 512, 4000, 1, 100
+    q, kv = synth.attn_inputs(34, B, Tq, H, D, L, "es_")
+    scale = 1.0 / np.sqrt(D)
+    want, wlse = oracle.dense_attn(q, kv, L, mh, pos0, scale)
+    out = torch.empty((B, Tq, H, D), dtype=torch.int16, device=DEV)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+    b.hca_dense_attn(dev(q), dev(kv), L, mh, pos0, scale, out, lse)
+    torch.cuda.synchronize()
+    assert_rows_close(host_bf16(out), want, what="dense out")
+    assert np.allclose(lse.cpu().numpy(), wlse, atol=2e-2, rtol=0)
+
+
+def test_sparse_attn_short_window_empty_split(b):
+    # position 10 with W = 128: 11 window rows, so the last split of the (topk32 + W)-row space is empty
+    B, Tq, H, D, Nc, topk, W, pos0 = 2, 1, 128, 512, 3000, 300, 128, 10
+    rng = np.random.default_rng(35)
+    q, kv = synth.attn_inputs(35, B, Tq, H, D, Nc, "sw_")
+    _, raw = synth.attn_inputs(36, B, Tq, H, D, pos0 + 1, "swr_")
+    idx = np.stack([np.sort(rng.choice(Nc, size=topk, replace=False)).astype(np.int32)[None] for _ in range(B)])
+    scale = 1.0 / np.sqrt(D)
+    want, wlse = oracle.sparse_attn(q, kv, idx, raw, 0, pos0, W, scale)
+    out = torch.empty((B, Tq, H, D), dtype=torch.int16, device=DEV)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+    b.csa_sparse_attn(dev(q), dev(kv), dev(idx), dev(raw), 0, pos0, W, scale, out, lse)
+    torch.cuda.synchronize()
+    assert_rows_close(host_bf16(out), want, what="sparse out")
+    assert np.allclose(lse.cpu().numpy(), wlse, atol=2e-2, rtol=0)
+
+
 def test_sparse_full_selection_equals_dense(b):
     B, H, D, Nc, m = 1, 64, 512, 700, 4
     q, kv = synth.attn_inputs(33, B, 1, H, D, Nc, "fd_")
