@@ -79,9 +79,9 @@ def _load():
         lib.ora_index_scores.restype = None
         lib.ora_topk.argtypes = [I, I, I, P, P, P, P]
         lib.ora_topk.restype = None
-        lib.ora_sparse_attn.argtypes = [I, I, I, I, I, I, I, LL, LL, I, D, P, P, P, P, P, P]
+        lib.ora_sparse_attn.argtypes = [I, I, I, I, I, I, I, LL, LL, I, D, P, P, P, P, P, P, P]
         lib.ora_sparse_attn.restype = I
-        lib.ora_dense_attn.argtypes = [I, I, I, I, I, LL, I, LL, D, P, P, P, P]
+        lib.ora_dense_attn.argtypes = [I, I, I, I, I, LL, I, LL, D, P, P, P, P, P]
         lib.ora_dense_attn.restype = None
         _lib = lib
     return _lib
@@ -193,8 +193,18 @@ def index_topk(q_idx, w_idx, k_idx, L: int, m: int, pos0: int, k: int, dtype=BF1
 
 # --- A4 / A5 ---------------------------------------------------------------
 
-def sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float):
-    """CSA attention over selected entries + raw window; returns (out, lse) fp64."""
+def _sink(sink, H):
+    if sink is None:
+        return None
+    s = np.ascontiguousarray(sink, dtype=np.float64)
+    if s.shape != (H,):
+        raise ValueError("sink: one logit per head")
+    return s
+
+
+def sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, sink=None):
+    """CSA attention over selected entries + raw window; returns (out, lse) fp64.  sink: optional
+    per-head attention-sink logits [H] (an extra denominator term with no value row)."""
     lib = _load()
     q, pq = _c(q, np.uint16)
     kv, pk = _c(kv, np.uint16)
@@ -208,15 +218,16 @@ def sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float):
     Lr = kr.shape[1]
     out = np.empty((B, Tq, H, D), np.float64)
     lse = np.empty((B, Tq, H), np.float64)
+    sk = _sink(sink, H)
     rc = lib.ora_sparse_attn(B, Tq, H, D, Nc, topk_, Lr, raw0, pos0, W, float(scale),
-                             pq, pk, pi, pr, _ptr(out), _ptr(lse))
+                             pq, pk, pi, pr, _ptr(sk), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle sparse_attn: index or window outside the given rows")
     return out, lse
 
 
-def dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float):
-    """HCA attention over all visible compressed entries; returns (out, lse) fp64."""
+def dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, sink=None):
+    """HCA attention over all visible compressed entries; returns (out, lse) fp64 (sink as above)."""
     lib = _load()
     q, pq = _c(q, np.uint16)
     kv, pk = _c(kv_h, np.uint16)
@@ -224,7 +235,8 @@ def dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float):
     Nh = kv.shape[1]
     out = np.empty((B, Tq, H, D), np.float64)
     lse = np.empty((B, Tq, H), np.float64)
-    lib.ora_dense_attn(B, Tq, H, D, Nh, L, mh, pos0, float(scale), pq, pk, _ptr(out), _ptr(lse))
+    sk = _sink(sink, H)
+    lib.ora_dense_attn(B, Tq, H, D, Nh, L, mh, pos0, float(scale), pq, pk, _ptr(sk), _ptr(out), _ptr(lse))
     return out, lse
 
 

@@ -423,13 +423,17 @@ void ora_topk(int rows, int Nc, int k, const float* S, const int* n_vis, int* id
  * share one KV head).  Reading taken: one vector per entry is both key and
  * value.  For head h: l_r = scale * (q_h . x_r), o_h = sum_r softmax(l)_r x_r,
  * lse_h = log sum_r exp(l_r).  An empty key set gives o = 0, lse = -inf. */
+/* One softmax per head over the rows' logits l_r = scale (q_h . x_r) and, when sink is given, the head's
+ * attention-sink logit sink[h] (a term of the denominator with no value row): [P1 section 1.1] gives
+ * every query head a learnable sink logit that lets it send its total attention towards 0.
+ * out_h = sum_r e^{l_r} x_r / (e^{sink_h} + sum_r e^{l_r}),  lse_h = log(e^{sink_h} + sum_r e^{l_r}). */
 static void ora_attend(const uint16_t* q, int H, int D, const uint16_t** rows, int nr,
-                       double scale, double* out, double* lse)
+                       double scale, const double* sink, double* out, double* lse)
 {
     int h, r, d;
     double* l = (double*)malloc(sizeof(double) * (nr > 0 ? nr : 1));
     for (h = 0; h < H; ++h) {
-        double mx = -INFINITY, s = 0.0;
+        double mx = sink ? sink[h] : -INFINITY, s = 0.0;
         for (r = 0; r < nr; ++r) {
             double dot = 0.0;
             for (d = 0; d < D; ++d)
@@ -438,8 +442,9 @@ static void ora_attend(const uint16_t* q, int H, int D, const uint16_t** rows, i
             if (l[r] > mx) mx = l[r];
         }
         for (d = 0; d < D; ++d) out[(size_t)h * D + d] = 0.0;
-        if (nr == 0) { lse[h] = -INFINITY; continue; }
+        if (mx == -INFINITY) { lse[h] = -INFINITY; continue; }     /* no row and no sink */
         for (r = 0; r < nr; ++r) { l[r] = exp(l[r] - mx); s += l[r]; }
+        if (sink) s += exp(sink[h] - mx);
         for (r = 0; r < nr; ++r)
             for (d = 0; d < D; ++d)
                 out[(size_t)h * D + d] += l[r] * ora_bf16_value(rows[r][d]);
@@ -461,7 +466,7 @@ static void ora_attend(const uint16_t* q, int H, int D, const uint16_t** rows, i
 int ora_sparse_attn(int B, int Tq, int H, int D, int Nc, int topk, int Lr, long long raw0,
                     long long pos0, int W, double scale,
                     const uint16_t* q, const uint16_t* kv, const int* idx, const uint16_t* kv_raw,
-                    double* out, double* lse)
+                    const double* sink, double* out, double* lse)
 {
     int bt, bad = 0;
     #pragma omp parallel for schedule(dynamic) reduction(|:bad)
@@ -479,7 +484,7 @@ int ora_sparse_attn(int B, int Tq, int H, int D, int Nc, int topk, int Lr, long 
             if (u < raw0 || u >= raw0 + Lr) { bad = 1; continue; }
             rows[nr++] = kv_raw + ((size_t)b * Lr + (size_t)(u - raw0)) * D;
         }
-        ora_attend(q + (size_t)bt * H * D, H, D, rows, nr, scale,
+        ora_attend(q + (size_t)bt * H * D, H, D, rows, nr, scale, sink,
                    out + (size_t)bt * H * D, lse + (size_t)bt * H);
         free(rows);
     }
@@ -491,7 +496,8 @@ int ora_sparse_attn(int B, int Tq, int H, int D, int Nc, int topk, int Lr, long 
  * selection.  Reading taken: no sliding window in HCA.  Entries visible to the
  * query at p as defined above.  q[B][Tq][H][D], kv_h[B][Nh][D]. */
 void ora_dense_attn(int B, int Tq, int H, int D, int Nh, long long L, int mh, long long pos0,
-                    double scale, const uint16_t* q, const uint16_t* kv_h, double* out, double* lse)
+                    double scale, const uint16_t* q, const uint16_t* kv_h, const double* sink,
+                    double* out, double* lse)
 {
     int bt;
     #pragma omp parallel for schedule(dynamic)
@@ -501,7 +507,7 @@ void ora_dense_attn(int B, int Tq, int H, int D, int Nh, long long L, int mh, lo
         const uint16_t** rows = (const uint16_t**)malloc(sizeof(void*) * (nv > 0 ? nv : 1));
         if (nv > Nh) nv = Nh;
         for (j = 0; j < nv; ++j) rows[j] = kv_h + ((size_t)b * Nh + j) * D;
-        ora_attend(q + (size_t)bt * H * D, H, D, rows, nv, scale,
+        ora_attend(q + (size_t)bt * H * D, H, D, rows, nv, scale, sink,
                    out + (size_t)bt * H * D, lse + (size_t)bt * H);
         free(rows);
     }

@@ -488,3 +488,40 @@ def test_empty_key_set():
     q, rows = synth.attn_inputs(36, 1, 1, 16, 32, 4, "e_")
     out, lse = oracle.dense_attn(q, rows, L=8, mh=4, pos0=2, scale=1.0)   # no entry complete yet
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# attention sink: a per-head logit in the softmax denominator with no value row (P1 section 1.1)
+
+def test_sink_zero_equals_an_extra_all_zero_row():
+    # a row of zeros has logit scale * (q . 0) = 0 and contributes no value: exactly a sink of 0
+    B, Tq, H, D, Nc = 1, 2, 16, 64, 30
+    q, rows = synth.attn_inputs(37, B, Tq, H, D, Nc, "sk_")
+    _, raw = synth.attn_inputs(38, B, Tq, H, D, 6, "skr_")
+    kvz = np.concatenate([rows, np.zeros((B, 1, D), np.uint16)], axis=1)
+    idx = np.array([[[2, 7, 11, 25, -1], [0, 5, 6, 29, 13]]], np.int32)
+    idx_z = np.concatenate([idx, np.full((B, Tq, 1), Nc, np.int32)], axis=-1)
+    out_s, lse_s = oracle.sparse_attn(q, rows, idx, raw, raw0=0, pos0=4, W=3, scale=0.7, sink=np.zeros(H))
+    out_z, lse_z = oracle.sparse_attn(q, kvz, idx_z, raw, raw0=0, pos0=4, W=3, scale=0.7)
+    np.testing.assert_allclose(out_s, out_z, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse_s, lse_z, rtol=1e-13)
+
+
+def test_sink_limits_and_textbook_softmax():
+    B, Tq, H, D, L = 1, 1, 16, 32, 12
+    q, rows = synth.attn_inputs(39, B, Tq, H, D, L, "sl_")
+    out0, lse0 = oracle.dense_attn(q, rows, L=L, mh=1, pos0=L - 1, scale=0.4)
+    out_m, lse_m = oracle.dense_attn(q, rows, L=L, mh=1, pos0=L - 1, scale=0.4, sink=np.full(H, -np.inf))
+    assert np.array_equal(out_m, out0) and np.array_equal(lse_m, lse0)          # -inf: no sink
+    big = np.full(H, 1.0e4)
+    out_b, lse_b = oracle.dense_attn(q, rows, L=L, mh=1, pos0=L - 1, scale=0.4, sink=big)
+    assert np.all(out_b == 0) and np.array_equal(lse_b[0, 0], big)               # all attention on the sink
+    out_e, lse_e = oracle.dense_attn(q, rows, L=L, mh=4, pos0=2, scale=0.4, sink=np.arange(H) * 0.5)
+    assert np.all(out_e == 0) and np.array_equal(lse_e[0, 0], np.arange(H) * 0.5)   # no row: lse = sink
+    # per-head sinks against a library softmax over the logits and the sink
+    sk = np.linspace(-3.0, 3.0, H)
+    out_s, lse_s = oracle.dense_attn(q, rows, L=L, mh=1, pos0=L - 1, scale=0.4, sink=sk)
+    qf, Kf = _bf16_f64(q[0, 0]), _bf16_f64(rows[0])
+    logits = np.concatenate([0.4 * qf @ Kf.T, sk[:, None]], axis=1)
+    p = scipy.special.softmax(logits, axis=1)
+    np.testing.assert_allclose(out_s[0, 0], p[:, :-1] @ Kf, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(lse_s[0, 0], scipy.special.logsumexp(logits, axis=1), rtol=1e-13)
