@@ -39,9 +39,9 @@ def _load():
         "csa_index_topk_ws_bytes": ([I, I, I, I, I, I, I], Z),
         "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, Z, P], I),
         "csa_sparse_attn_ws_bytes": ([I, I, I, I, I, I], Z),
-        "csa_sparse_attn": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, Z, P], I),
+        "csa_sparse_attn": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P, Z, P], I),
         "hca_dense_attn_ws_bytes": ([I, I, I, I, I], Z),
-        "hca_dense_attn": ([P, P, I, I, I, I, I, LL, I, LL, F, P, P, P, Z, P], I),
+        "hca_dense_attn": ([P, P, I, I, I, I, I, LL, I, LL, F, P, P, P, P, Z, P], I),
         "csa_hca_decode_ws_bytes": ([P], Z),
         "csa_hca_decode": ([P, P, Z, P], I),
         "csa_debug_fp8_to_bf16": ([P, P, I, P], I),
@@ -77,8 +77,9 @@ class DecodeArgs(ctypes.Structure):
         ("idx_dtype", ctypes.c_int), ("HI", ctypes.c_int), ("dI", ctypes.c_int), ("m", ctypes.c_int),
         ("topk", ctypes.c_int), ("W", ctypes.c_int),
         ("csa_out", ctypes.c_void_p), ("csa_lse", ctypes.c_void_p), ("idx_out", ctypes.c_void_p),
+        ("csa_sink", ctypes.c_void_p),
         ("hca_q", ctypes.c_void_p), ("kv_h", ctypes.c_void_p), ("mh", ctypes.c_int),
-        ("hca_out", ctypes.c_void_p), ("hca_lse", ctypes.c_void_p),
+        ("hca_out", ctypes.c_void_p), ("hca_lse", ctypes.c_void_p), ("hca_sink", ctypes.c_void_p),
     ]
 
 
@@ -145,8 +146,15 @@ def csa_index_topk(q_idx, w_idx, k_idx, dtype: int, L: int, m: int, pos0: int, t
                               _p(idx_out), _p(cnt_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
+def _sink(sink, H: int):
+    """The per-head attention-sink logits: None, or H float32 values on the device."""
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != H or not sink.is_contiguous()):
+        raise ValueError(f"sink must be {H} contiguous float32 values, got {sink.dtype} x {sink.numel()}")
+    return _p(sink)
+
+
 def csa_sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, out, lse_out=None, ws=None,
-                    stream=None):
+                    stream=None, sink=None):
     B, Tq, H, D = q.shape
     Nc = kv.shape[1] if kv is not None else 0
     topk = idx.shape[-1] if idx is not None else 0
@@ -155,28 +163,35 @@ def csa_sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: flo
     if ws is None:
         ws = workspace(need, q.device)
     _check(lib.csa_sparse_attn(_p(q), _p(kv), _p(idx), _p(kv_raw), B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W,
-                               float(scale), _p(out), _p(lse_out), _p(ws), 0 if ws is None else ws.numel(),
-                               _stream(stream)))
+                               float(scale), _sink(sink, H), _p(out), _p(lse_out), _p(ws),
+                               0 if ws is None else ws.numel(), _stream(stream)))
 
 
-def hca_dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, out, lse_out=None, ws=None, stream=None):
+def hca_dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, out, lse_out=None, ws=None, stream=None,
+                   sink=None):
     B, Tq, H, D = q.shape
     Nh = kv_h.shape[1]
     need = lib.hca_dense_attn_ws_bytes(B, Tq, H, D, Nh)
     if ws is None:
         ws = workspace(need, q.device)
-    _check(lib.hca_dense_attn(_p(q), _p(kv_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale), _p(out), _p(lse_out),
-                              _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    _check(lib.hca_dense_attn(_p(q), _p(kv_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale), _sink(sink, H), _p(out),
+                              _p(lse_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def make_decode_args(*, L, scale, csa_q, q_idx, w_idx, k_idx, kv, kv_raw, idx_dtype, m, topk, W, csa_out,
-                     hca_q, kv_h, mh, hca_out, csa_lse=None, hca_lse=None, idx_out=None) -> DecodeArgs:
+                     hca_q, kv_h, mh, hca_out, csa_lse=None, hca_lse=None, idx_out=None, csa_sink=None,
+                     hca_sink=None) -> DecodeArgs:
     B, H, D = csa_q.shape[0], csa_q.shape[-2], csa_q.shape[-1]
     HI, dI = q_idx.shape[-2], q_idx.shape[-1]
-    return DecodeArgs(B=B, L=L, H=H, D=D, scale=float(scale), csa_q=_p(csa_q), q_idx=_p(q_idx), w_idx=_p(w_idx),
+    args = DecodeArgs(B=B, L=L, H=H, D=D, scale=float(scale), csa_q=_p(csa_q), q_idx=_p(q_idx), w_idx=_p(w_idx),
                       k_idx=_p(k_idx), kv=_p(kv), kv_raw=_p(kv_raw), idx_dtype=idx_dtype, HI=HI, dI=dI, m=m,
                       topk=topk, W=W, csa_out=_p(csa_out), csa_lse=_p(csa_lse), idx_out=_p(idx_out),
-                      hca_q=_p(hca_q), kv_h=_p(kv_h), mh=mh, hca_out=_p(hca_out), hca_lse=_p(hca_lse))
+                      csa_sink=_sink(csa_sink, H), hca_q=_p(hca_q), kv_h=_p(kv_h), mh=mh, hca_out=_p(hca_out),
+                      hca_lse=_p(hca_lse), hca_sink=_sink(hca_sink, hca_q.shape[-2]))
+    # the struct holds bare device addresses: keep every tensor they point into alive as long as the struct
+    args._keep = (csa_q, q_idx, w_idx, k_idx, kv, kv_raw, csa_out, csa_lse, idx_out, csa_sink, hca_q, kv_h, hca_out,
+                  hca_lse, hca_sink)
+    return args
 
 
 def csa_hca_decode_ws_bytes(args: DecodeArgs) -> int:

@@ -299,15 +299,15 @@ size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W) {
 }
 
 int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const void* kv_raw, int B, int Tq, int H, int D,
-                    int Nc, int topk, int Lr, long long raw0, long long pos0, int W, float scale, void* out,
-                    float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+                    int Nc, int topk, int Lr, long long raw0, long long pos0, int W, float scale, const float* sink,
+                    void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
     const char* fn = "csa_sparse_attn";
     csa_host::g_err[0] = 0;
     int rc = validate_sparse(fn, q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse_out);
     if (rc) return rc;
     rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, 1, topk, W));
     if (rc) return rc;
-    csa_host::AttnRows r{1, kv, Nc, 0, 1, idx, topk, kv_raw, Lr, raw0, W};
+    csa_host::AttnRows r{1, kv, Nc, 0, 1, idx, topk, kv_raw, Lr, raw0, W, sink};
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
                                  "k_attn_sparse");
 }
@@ -318,14 +318,15 @@ size_t hca_dense_attn_ws_bytes(int B, int Tq, int H, int D, int Nh) {
 }
 
 int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D, int Nh, long long L, int mh,
-                   long long pos0, float scale, void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+                   long long pos0, float scale, const float* sink, void* out, float* lse_out, void* ws,
+                   size_t ws_bytes, void* stream) {
     const char* fn = "hca_dense_attn";
     csa_host::g_err[0] = 0;
     int rc = validate_dense(fn, q, kv_h, B, Tq, H, D, Nh, L, mh, pos0, scale, out, lse_out);
     if (rc) return rc;
     rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, 0, Nh, 0));
     if (rc) return rc;
-    csa_host::AttnRows r{0, kv_h, Nh, L, mh, nullptr, 0, nullptr, 0, 0, 0};
+    csa_host::AttnRows r{0, kv_h, Nh, L, mh, nullptr, 0, nullptr, 0, 0, 0, sink};
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
                                  "k_attn_dense");
 }
@@ -374,8 +375,8 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     if (rc) return rc;
     w += iws;
     const size_t aws = ws_bytes - (size_t)(w - (char*)ws);
-    csa_host::AttnRows rs{1, a->kv, Nc, 0, 1, idx, a->topk, a->kv_raw, a->W, a->L - a->W, a->W};
-    csa_host::AttnRows rd{0, a->kv_h, Nh, a->L, a->mh, nullptr, 0, nullptr, 0, 0, 0};
+    csa_host::AttnRows rs{1, a->kv, Nc, 0, 1, idx, a->topk, a->kv_raw, a->W, a->L - a->W, a->W, a->csa_sink};
+    csa_host::AttnRows rd{0, a->kv_h, Nh, a->L, a->mh, nullptr, 0, nullptr, 0, 0, 0, a->hca_sink};
     // the CSA layer's attention, then the HCA layer's (layer order: a real next layer's query depends on the
     // previous layer's output, so the two are never overlapped)
     const size_t sws = align256(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 1, a->topk, a->W));

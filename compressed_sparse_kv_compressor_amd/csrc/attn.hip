@@ -177,7 +177,8 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
     if (!wave_active) return;
     // lane holds O^T[d*16 + 4*grp + j][h]
     if (nsplit == 1) {
-        const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+        float lse_v;
+        const float inv = sink_norm(m_run, l_run, sink_log2(R.sink, h), lse_v);
         uint16_t* op = out + ((size_t)bt * H + h) * D + 4 * grp;
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
             v.y = (uint32_t)f32_to_bf16(acc[d][2] * inv) | ((uint32_t)f32_to_bf16(acc[d][3] * inv) << 16);
             *(uint2*)(op + d * 16) = v;
         }
-        if (lse && grp == 0) lse[(size_t)bt * H + h] = l_run > 0.f ? (m_run + log2f(l_run)) * LN2 : -INFINITY;
+        if (lse && grp == 0) lse[(size_t)bt * H + h] = lse_v;
     } else {
         const size_t slot = ((size_t)bt * nsplit + split) * H + h;
         float* op = part_o + slot * D + 4 * grp;
@@ -599,7 +600,8 @@ __device__ __forceinline__ void attn64_body(
     }
     // lane holds O^T[dh*256 + d*32 + 8 (j/4) + 4 g + j%4][h]
     if (nsplit == 1) {
-        const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+        float lse_v;
+        const float inv = sink_norm(m_run, l_run, sink_log2(R.sink, h), lse_v);
         uint16_t* op = out + ((size_t)bt * H + h) * D + dh * HD + 4 * g;
 #pragma unroll
         for (int d = 0; d < DT; ++d)
@@ -610,7 +612,7 @@ __device__ __forceinline__ void attn64_body(
                 v.y = pack_bf16x2(acc[d][4 * q4 + 2] * inv, acc[d][4 * q4 + 3] * inv);
                 *(uint2*)(op + d * 32 + 8 * q4) = v;
             }
-        if (lse && g == 0 && dh == 0) lse[(size_t)bt * H + h] = l_run > 0.f ? (m_run + log2f(l_run)) * LN2 : -INFINITY;
+        if (lse && g == 0 && dh == 0) lse[(size_t)bt * H + h] = lse_v;
     } else {
         const size_t sl = ((size_t)bt * nsplit + split) * H + h;
         float* op = part_o + sl * D + dh * HD + 4 * g;
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(TPB, 1) void k_attn64(
 template <int D>
 __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
                                              int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
-                                             int h, int bt)
+                                             const float* __restrict__ sink, int h, int bt)
 {
     const int d = threadIdx.x * 4;
     const size_t s0 = (size_t)bt * nsplit * H + h;     // slot of split 0; split s at s0 + s H
@@ -686,19 +688,21 @@ __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, c
             o += f * *(const f32x4_t*)(part_o + slot * D + d);
         }
     }
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    float lse_v;
+    const float inv = sink_norm(M, l, sink_log2(sink, h), lse_v);
     uint2 v;
     v.x = (uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16);
     v.y = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
     *(uint2*)(out + ((size_t)bt * H + h) * D + d) = v;
-    if (lse && threadIdx.x == 0) lse[(size_t)bt * H + h] = l > 0.f ? (M + log2f(l)) * LN2 : -INFINITY;
+    if (lse && threadIdx.x == 0) lse[(size_t)bt * H + h] = lse_v;
 }
 
 template <int D>
 __global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
-                                                   int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse)
+                                                   int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                   const float* __restrict__ sink)
 {
-    combine_body<D>(part_o, part_ml, H, nsplit, out, lse, blockIdx.x, blockIdx.y);
+    combine_body<D>(part_o, part_ml, H, nsplit, out, lse, sink, blockIdx.x, blockIdx.y);
 }
 
 }  // namespace
@@ -806,6 +810,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     R.Lr = a.Lr;
     R.raw0 = a.raw0;
     R.W = a.W;
+    R.sink = a.sink;
     const int BT = B * Tq;
     const int max_rows = a.mode == 0 ? a.N : attn_rows(1, H, D, a.topk, a.W);
     int ns, rps;
@@ -826,11 +831,14 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         j.nsplit = a128_nsplit(r128, j.rps);
         j.nunits = BT * j.nsplit;
         j.out = (uint16_t*)out; j.lse = lse;
-        if (j.nsplit > 1) {
-            j.part_o = (float*)ws;
-            j.part_ml = (float2*)((char*)ws + align256((size_t)BT * j.nsplit * H * D * 4));
+        // k_attn128 applies an attention sink in its merge only: a sink with a single split runs k_attn64
+        if (!(R.sink && j.nsplit == 1)) {
+            if (j.nsplit > 1) {
+                j.part_o = (float*)ws;
+                j.part_ml = (float2*)((char*)ws + align256((size_t)BT * j.nsplit * H * D * 4));
+            }
+            return attn128_launch(j, st, tag);
         }
-        return attn128_launch(j, st, tag);
     }
     if (use64(D, H)) {
         const int nunits = BT * ns, HP = (H + 63) / 64;
@@ -848,7 +856,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
 #undef CSA_ATTN64
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
-                       (uint16_t*)out, lse);
+                       (uint16_t*)out, lse, R.sink);
         return 0;
     }
     dim3 grid(ns, (H + 63) / 64, BT);
@@ -857,13 +865,13 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
                    part_o, part_ml, (uint16_t*)out, lse);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
-                       (uint16_t*)out, lse);
+                       (uint16_t*)out, lse, R.sink);
     } else if (D == 128) {
         CSA_LAUNCH(tag, k_attn<128>, grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns, rps,
                    part_o, part_ml, (uint16_t*)out, lse);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<128>, dim3(H, BT), dim3(32), 0, st, part_o, part_ml, H, ns,
-                       (uint16_t*)out, lse);
+                       (uint16_t*)out, lse, R.sink);
     } else {
         return fail(6, "attention: D = %d unsupported", D);
     }

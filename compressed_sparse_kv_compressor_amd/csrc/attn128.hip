@@ -293,6 +293,8 @@ __device__ __forceinline__ void attn128_body(
     }
     // lane holds O^T[d*32 + 8 (j/4) + 4 g + j%4][h]
     if (nsplit == 1) {
+        // (a launch with an attention sink and a single split runs k_attn64 instead; the sink of a split
+        // launch is applied by the merge)
         const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
         uint16_t* op = out + ((size_t)bt * H + h) * D + 4 * g;
 #pragma unroll
@@ -347,7 +349,8 @@ __device__ __forceinline__ __attribute__((ext_vector_type(2))) _Float16 as_f16x2
 // (wave w, chunk c, lane) of every split.
 __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ part, const float2* __restrict__ part_ml,
                                                 int H, int nsplit, uint16_t* __restrict__ out,
-                                                float* __restrict__ lse, int bt, int hq, int tid)
+                                                float* __restrict__ lse, const float* __restrict__ sink, int bt,
+                                                int hq, int tid)
 {
     const int HQ = H >> 7;
     const int w = tid >> 11, c = (tid >> 6) & 31, lane = tid & 63;
@@ -390,12 +393,13 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
             }
         }
     }
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    float lse_v;
+    const float inv = sink_norm(M, l, sink_log2(sink, h), lse_v);
     // o[jj] is O^T[d][h] at d = 32 (c / 2) + 8 ((8 (c % 2) + jj) / 4) + 4 g + jj % 4: two runs of 4
     uint16_t* op = out + ((size_t)bt * H + h) * 512 + 32 * (c >> 1) + 16 * (c & 1) + 4 * g;
     *(uint2*)op = make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
     *(uint2*)(op + 8) = make_uint2(pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv));
-    if (lse && c == 0 && g == 0) lse[(size_t)bt * H + h] = l > 0.f ? (M + log2f(l)) * LN2 : -INFINITY;
+    if (lse && c == 0 && g == 0) lse[(size_t)bt * H + h] = lse_v;
 }
 
 // Tile buffers [32 rows][512] bf16 (distinct objects: the compiler tells a read of one from the loads in
@@ -423,8 +427,8 @@ __global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, in
 // grid (32, HQ, BT): 256 threads x 32 cover the 8192 chunk positions of one query and head quad
 __global__ __launch_bounds__(256) void k_combine128(AttnJob j)
 {
-    combine128_body((const uint16_t*)j.part_o, j.part_ml, j.H, j.nsplit, j.out, j.lse, blockIdx.z, blockIdx.y,
-                    blockIdx.x * 256 + threadIdx.x);
+    combine128_body((const uint16_t*)j.part_o, j.part_ml, j.H, j.nsplit, j.out, j.lse, j.R.sink, blockIdx.z,
+                    blockIdx.y, blockIdx.x * 256 + threadIdx.x);
 }
 
 }  // namespace

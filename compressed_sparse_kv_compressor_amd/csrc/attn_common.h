@@ -26,12 +26,32 @@ struct Rows {
     int Lr;
     long long raw0;
     int W;
+    const float* sink;        // [H] attention-sink logits (natural log) or null
 };
 
 __device__ __forceinline__ int dense_visible(long long p, long long L, int m, int N) {
     if (p >= L - 1) return N;
     long long v = (p + 1) / m;
     return v < N ? (int)v : N;
+}
+
+// Final normalization of one head.  The rows give (m, l) in the log2 domain (m = -inf, l = 0: no row) and
+// value sums O relative to 2^m; s2 is the head's attention-sink logit in log2 units (-inf: none), one more
+// denominator term with no value row.  Returns f with out = O f and sets the natural-log lse; without a
+// sink this is f = 1 / l, lse = (m + log2 l) ln 2 exactly.
+__device__ __forceinline__ float sink_norm(float m, float l, float s2, float& lse_out) {
+    const float M = fmaxf(m, s2);
+    if (!(M > -INFINITY)) {
+        lse_out = -INFINITY;
+        return 0.f;
+    }
+    const float a = m > -INFINITY ? exp2f(m - M) : 0.f;
+    const float lt = l * a + exp2f(s2 - M);
+    lse_out = (M + log2f(lt)) * LN2;
+    return lt > 0.f ? a / lt : 0.f;
+}
+__device__ __forceinline__ float sink_log2(const float* sink, int h) {
+    return sink ? sink[h] * LOG2E : -INFINITY;
 }
 
 // 16-byte chunk c of row r is stored at chunk c ^ f(r & 15), f(x) = 4 (x & 3) + (x >> 2): any 16

@@ -34,6 +34,7 @@ struct AttnRows {
     int Lr;
     long long raw0;
     int W;
+    const float* sink;        // [H] per-head attention-sink logits (natural log), or null
 };
 // mode 0: dense over n rows; mode 1: n selected entries + W window rows
 size_t attn_ws_bytes(int B, int Tq, int H, int D, int mode, int n, int W);

@@ -114,6 +114,11 @@ def attn_inputs(seed, B, Tq, H, D, Nrows, prefix, heavy=False):
     return q, rows
 
 
+def sink_logits(seed, H, prefix, scale=2.0):
+    """Per-head attention-sink logits (natural log units) as float32, N(0, scale^2)."""
+    return normal_f32(seed, prefix + "sink", (H,), scale)
+
+
 def compress_weights(seed, Dh, D, dI, m, gate_scale=1.0, prefix=""):
     """The weights of compress_inputs alone (same streams): w_kv, w_ik (or None), w_gate, b_slot."""
     wkv = to_bf16_bits(normal_f32(seed, prefix + "w_kv", (D, Dh), 1.0 / np.sqrt(Dh)))

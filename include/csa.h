@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum {
     CSA_OK = 0,
@@ -157,6 +157,10 @@ int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int
  * value (MQA, one shared KV head):
  *   l_r = scale * (q_h . x_r),  out_h = sum_r softmax(l)_r x_r,
  *   lse_h = log sum_r exp(l_r)   (natural log; -inf and out = 0 if no rows).
+ * With sink (device, [H] fp32 natural-log logits, or NULL) every head's softmax has one more denominator
+ * term exp(sink[h]) with no value row ([P1] 1.1: a learnable attention-sink logit lets a head send its
+ * total attention towards 0): out_h = sum_r exp(l_r) x_r / (exp(sink_h) + sum_r exp(l_r)),
+ * lse_h = log(exp(sink_h) + sum_r exp(l_r)) (= sink_h when there are no rows).
  *   q   [B][Tq][H][D] bf16       kv [B][Nc][D] bf16
  *   idx [B][Tq][topk] int32 (entries < 0 are skipped; must be < Nc)
  *   kv_raw [B][Lr][D] bf16, row i = raw position raw0 + i (may be NULL if W = 0)
@@ -167,21 +171,21 @@ int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int
 size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W);
 int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const void* kv_raw,
                     int B, int Tq, int H, int D, int Nc, int topk, int Lr, long long raw0,
-                    long long pos0, int W, float scale, void* out, float* lse_out,
+                    long long pos0, int W, float scale, const float* sink, void* out, float* lse_out,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* A5. HCA attention: dense MQA over every visible compressed entry          */
 /*     ([P1] 1.1; [P2] first section; [P3] item 2)                           */
 /* ------------------------------------------------------------------------ */
-/* As A4 but over {kv_h[b][j] : j visible to p} (ratio mh over L raw tokens),
- * with no selection and no window.
+/* As A4 (sink included) but over {kv_h[b][j] : j visible to p} (ratio mh over L
+ * raw tokens), with no selection and no window.
  *   q [B][Tq][H][D] bf16    kv_h [B][Nh][D] bf16 (Nh = ceil(L/mh))
  *   out [B][Tq][H][D] bf16  lse_out [B][Tq][H] fp32 or NULL
  * Supported: D in {128, 512}; H % 16 == 0, H <= 256. */
 size_t hca_dense_attn_ws_bytes(int B, int Tq, int H, int D, int Nh);
 int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D, int Nh,
-                   long long L, int mh, long long pos0, float scale,
+                   long long L, int mh, long long pos0, float scale, const float* sink,
                    void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
@@ -209,12 +213,14 @@ typedef struct csa_hca_decode_args {
     void* csa_out;         /* [B][H][D] bf16 */
     float* csa_lse;        /* [B][H] fp32 or NULL */
     int32_t* idx_out;      /* [B][topk] int32 or NULL (then kept in the workspace) */
+    const float* csa_sink; /* [H] fp32 attention-sink logits of the CSA layer or NULL (see A4) */
     /* HCA layer */
     const void* hca_q;     /* [B][H][D] bf16 */
     const void* kv_h;      /* [B][Nh][D] bf16, Nh = ceil(L/mh) */
     int mh;
     void* hca_out;         /* [B][H][D] bf16 */
     float* hca_lse;        /* [B][H] fp32 or NULL */
+    const float* hca_sink; /* [H] fp32 attention-sink logits of the HCA layer or NULL */
 } csa_hca_decode_args_t;
 
 size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a);

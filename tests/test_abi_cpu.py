@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(b):
 
 
 def test_version_and_status_strings(b):
-    assert b.lib.csa_abi_version() == 1
+    assert b.lib.csa_abi_version() == 2
     assert b.lib.csa_status_str(CSA_ERR_WORKSPACE) == b"CSA_ERR_WORKSPACE"
     assert b.lib.csa_status_str(99) == b"CSA_ERR_UNKNOWN"
 
@@ -97,20 +97,20 @@ def test_index_topk_validation_codes(b):
 def test_attention_validation_codes(b):
     lib = b.lib
     sp = lib.csa_sparse_attn
-    # q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse, ws, wsb, stream
-    assert sp(A16, A16, A16, A16, 1, 1, 16, 96, 10, 4, 8, 0, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_UNSUPPORTED
-    assert sp(A16, A16, A16, A16, 1, 1, 24, 128, 10, 4, 8, 0, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_UNSUPPORTED
-    assert sp(A16, A16, A16, None, 1, 1, 16, 128, 10, 4, 8, 0, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_NULL
+    # q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, sink, out, lse, ws, wsb, stream
+    assert sp(A16, A16, A16, A16, 1, 1, 16, 96, 10, 4, 8, 0, 7, 4, 0.1, None, A16, None, A16, 10 ** 9, None) == CSA_ERR_UNSUPPORTED
+    assert sp(A16, A16, A16, A16, 1, 1, 24, 128, 10, 4, 8, 0, 7, 4, 0.1, None, A16, None, A16, 10 ** 9, None) == CSA_ERR_UNSUPPORTED
+    assert sp(A16, A16, A16, None, 1, 1, 16, 128, 10, 4, 8, 0, 7, 4, 0.1, None, A16, None, A16, 10 ** 9, None) == CSA_ERR_NULL
     # window needs raw rows starting at 4 but they start at 5
-    assert sp(A16, A16, A16, A16, 1, 1, 16, 128, 10, 4, 8, 5, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
+    assert sp(A16, A16, A16, A16, 1, 1, 16, 128, 10, 4, 8, 5, 7, 4, 0.1, None, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
     # window needs position 7 but rows end at 6
-    assert sp(A16, A16, A16, A16, 1, 1, 16, 128, 10, 4, 7, 0, 7, 4, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
-    assert sp(A16, A16, A16, A16, 1, 1, 16, 128, 10, 4, 8, 0, 7, 4, float("nan"), A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
+    assert sp(A16, A16, A16, A16, 1, 1, 16, 128, 10, 4, 7, 0, 7, 4, 0.1, None, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
+    assert sp(A16, A16, A16, A16, 1, 1, 16, 128, 10, 4, 8, 0, 7, 4, float("nan"), None, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
     de = lib.hca_dense_attn
-    # q, kv_h, B, Tq, H, D, Nh, L, mh, pos0, scale, out, lse, ws, wsb, stream
-    assert de(A16, A16, 1, 1, 16, 128, 31, 4096, 128, 4095, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
-    assert de(A16, None, 1, 1, 16, 128, 32, 4096, 128, 4095, 0.1, A16, None, A16, 10 ** 9, None) == CSA_ERR_NULL
-    assert de(A16, A16, 1, 1, 16, 128, 32, 4096, 128, 4095, 0.1, BAD, None, A16, 10 ** 9, None) == CSA_ERR_ALIGN
+    # q, kv_h, B, Tq, H, D, Nh, L, mh, pos0, scale, sink, out, lse, ws, wsb, stream
+    assert de(A16, A16, 1, 1, 16, 128, 31, 4096, 128, 4095, 0.1, None, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE
+    assert de(A16, None, 1, 1, 16, 128, 32, 4096, 128, 4095, 0.1, None, A16, None, A16, 10 ** 9, None) == CSA_ERR_NULL
+    assert de(A16, A16, 1, 1, 16, 128, 32, 4096, 128, 4095, 0.1, None, BAD, None, A16, 10 ** 9, None) == CSA_ERR_ALIGN
 
 
 def test_compress_and_decode_validation_codes(b):
@@ -130,3 +130,20 @@ def test_compress_and_decode_validation_codes(b):
     args.kv_h = A16
     assert lib.csa_hca_decode(ctypes.byref(args), A16, 16, None) == CSA_ERR_WORKSPACE
     assert lib.csa_hca_decode_ws_bytes(ctypes.byref(args)) > 16
+
+
+def test_decode_args_keep_their_tensors_alive(b):
+    """The decode args hold bare addresses; the struct must own references to what they point into."""
+    import gc
+    import weakref
+
+    import torch
+    t = torch.zeros(16, dtype=torch.float32)
+    ref = weakref.ref(t)
+    z = torch.zeros(4, dtype=torch.int16)
+    args = b.make_decode_args(L=8, scale=0.1, csa_q=torch.zeros(1, 16, 128, dtype=torch.int16), q_idx=z.view(1, 1, 4),
+                              w_idx=z, k_idx=z, kv=z, kv_raw=z, idx_dtype=0, m=4, topk=1, W=0, csa_out=z,
+                              hca_q=torch.zeros(1, 16, 128, dtype=torch.int16), kv_h=z, mh=4, hca_out=z, csa_sink=t)
+    del t
+    gc.collect()
+    assert ref() is not None and args.csa_sink == ref().data_ptr()

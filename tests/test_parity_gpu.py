@@ -445,6 +445,85 @@ def test_sparse_attn_short_window_empty_split(b):
     assert np.allclose(lse.cpu().numpy(), wlse, atol=2e-2, rtol=0)
 
 
+# attention sink: one extra per-head logit in the softmax denominator, with no value row
+SINK_SPARSE_CASES = [
+    # (B, Tq, H, D, Nc, topk, W, scale_mul, sink_shift)
+    (1, 3, 32, 128, 300, 37, 5, 4.0, 0.0),          # generic kernel
+    (2, 1, 64, 512, 3000, 512, 128, 1.0, 0.0),      # 64-head workgroups, split and merged
+    (1, 1, 96, 512, 2000, 300, 128, 1.0, 3.0),      # half last head pair, sink often dominant
+    (1, 3, 128, 512, 800, 100, 20, 2.0, 0.0),       # 128 heads, one split: the 64-head kernel runs
+    (1, 1, 128, 512, 70000, 2048, 128, 1.0, 0.0),   # 128 heads, many splits: sink in the merge
+    (1, 1, 128, 512, 100, 0, 0, 1.0, 0.0),          # nothing visible: out 0, lse = sink
+]
+
+
+@pytest.mark.parametrize("case", SINK_SPARSE_CASES)
+def test_sparse_attn_sink_parity(b, case):
+    B, Tq, H, D, Nc, topk, W, sm, shift = case
+    rng = np.random.default_rng(Nc + topk + 1)
+    q, kv = synth.attn_inputs(23, B, Tq, H, D, Nc, "sps_")
+    sink = synth.sink_logits(23, H, "sps_") + np.float32(shift)
+    L = Nc * 4
+    pos0 = L - Tq
+    Lr = W + Tq + 3
+    raw0 = pos0 + Tq - Lr
+    _, raw = synth.attn_inputs(24, B, Tq, H, D, Lr, "raws_")
+    idx = np.full((B, Tq, max(topk, 1)), -1, np.int32)
+    for bb in range(B):
+        for t in range(Tq):
+            c = rng.integers(max(0, topk - 5), topk + 1) if topk else 0
+            idx[bb, t, :c] = np.sort(rng.choice(Nc, size=c, replace=False))
+    scale = sm / np.sqrt(D)
+    want, wlse = oracle.sparse_attn(q, kv, idx, raw, raw0, pos0, W, scale, sink=sink.astype(np.float64))
+    out = torch.empty((B, Tq, H, D), dtype=torch.int16, device=DEV)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+    b.csa_sparse_attn(dev(q), dev(kv), dev(idx), dev(raw), raw0, pos0, W, scale, out, lse, sink=dev(sink))
+    torch.cuda.synchronize()
+    if topk == 0 and W == 0:
+        assert not bf16_f64(host_bf16(out)).any()     # zero as a value (the sign of a zero is free)
+    else:
+        assert_rows_close(host_bf16(out), want, what="sparse out with sink")
+    assert np.allclose(lse.cpu().numpy(), wlse, atol=2e-2, rtol=0)
+
+
+SINK_DENSE_CASES = [
+    # (B, Tq, H, D, L, mh, scale_mul)
+    (1, 5, 16, 128, 4 * 33, 4, 4.0),               # generic kernel, causal visibility per query
+    (1, 1, 64, 512, 128 * 20000, 128, 1.0),        # 64-head workgroups, many splits
+    (1, 5, 128, 512, 4 * 33, 4, 4.0),              # 128 heads, one split: the 64-head kernel runs
+    (1, 1, 128, 512, 128 * 20000 + 9, 128, 1.0),   # 128 heads, many splits: sink in the merge
+]
+
+
+@pytest.mark.parametrize("case", SINK_DENSE_CASES)
+def test_dense_attn_sink_parity(b, case):
+    B, Tq, H, D, L, mh, sm = case
+    Nh = -(-L // mh)
+    q, kv = synth.attn_inputs(33, B, Tq, H, D, Nh, "des_")
+    sink = synth.sink_logits(33, H, "des_")
+    pos0 = L - Tq
+    scale = sm / np.sqrt(D)
+    want, wlse = oracle.dense_attn(q, kv, L, mh, pos0, scale, sink=sink.astype(np.float64))
+    out = torch.empty((B, Tq, H, D), dtype=torch.int16, device=DEV)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+    b.hca_dense_attn(dev(q), dev(kv), L, mh, pos0, scale, out, lse, sink=dev(sink))
+    torch.cuda.synchronize()
+    assert_rows_close(host_bf16(out), want, what="dense out with sink")
+    assert np.allclose(lse.cpu().numpy(), wlse, atol=2e-2, rtol=0)
+
+
+@pytest.mark.parametrize("H,D", [(16, 128), (128, 512)])
+def test_dense_attn_sink_no_visible_entry(b, H, D):
+    q, kv = synth.attn_inputs(34, 1, 1, H, D, 4, "den_")
+    sink = synth.sink_logits(34, H, "den_")
+    out = torch.full((1, 1, H, D), 7, dtype=torch.int16, device=DEV)
+    lse = torch.empty((1, 1, H), dtype=torch.float32, device=DEV)
+    b.hca_dense_attn(dev(q), dev(kv), 16, 4, 2, 0.1, out, lse, sink=dev(sink))   # p = 2: no block complete
+    torch.cuda.synchronize()
+    assert not bf16_f64(host_bf16(out)).any()
+    assert np.allclose(lse.cpu().numpy().reshape(H), sink, atol=1e-5, rtol=0)
+
+
 def test_sparse_full_selection_equals_dense(b):
     B, H, D, Nc, m = 1, 64, 512, 700, 4
     q, kv = synth.attn_inputs(33, B, 1, H, D, Nc, "fd_")
@@ -608,3 +687,36 @@ def test_fused_decode_matches_oracle_and_separate_calls(b, L, B, H, D, HI, dI, t
     b.csa_hca_decode(args2)
     torch.cuda.synchronize()
     assert torch.equal(c2, csa_out) and torch.equal(h2, hca_out)
+
+
+@pytest.mark.parametrize("L,B,H,D,HI,dI,topk,dt", [(4096, 1, 16, 128, 4, 64, 64, 0),
+                                                   (4 * 6000, 2, 128, 512, 8, 128, 1024, 1)])
+def test_fused_decode_with_sinks_matches_oracle(b, L, B, H, D, HI, dI, topk, dt):
+    from compressed_sparse_kv_compressor_amd.configs import DecodeCfg
+    cfg = DecodeCfg("t", B=B, L=L, H=H, D=D, HI=HI, dI=dI, m=4, mh=128, topk=topk, W=128, idx_dtype=dt)
+    x = decode_case(cfg, seed=6)
+    cs = synth.sink_logits(6, H, "csa_")
+    hs = synth.sink_logits(6, H, "hca_")
+    p = L - 1
+    want_idx, _, _, _ = oracle.index_topk(x["q_idx"], x["w_idx"], x["k_idx"], L, 4, p, topk, dt)
+    want_csa, wl_csa = oracle.sparse_attn(x["csa_q"], x["kv"], want_idx, x["raw"], L - cfg.W, p, cfg.W, cfg.scale,
+                                          sink=cs.astype(np.float64))
+    want_hca, wl_hca = oracle.dense_attn(x["hca_q"], x["kv_h"], L, 128, p, cfg.scale, sink=hs.astype(np.float64))
+    t = {k: dev(v) for k, v in x.items()}
+    csa_out = torch.empty((B, H, D), dtype=torch.int16, device=DEV)
+    hca_out = torch.empty_like(csa_out)
+    csa_lse = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    hca_lse = torch.empty_like(csa_lse)
+    idx = torch.empty((B, topk), dtype=torch.int32, device=DEV)
+    args = b.make_decode_args(L=L, scale=cfg.scale, csa_q=t["csa_q"].view(B, H, D), q_idx=t["q_idx"],
+                              w_idx=t["w_idx"], k_idx=t["k_idx"], kv=t["kv"], kv_raw=t["raw"], idx_dtype=dt, m=4,
+                              topk=topk, W=cfg.W, csa_out=csa_out, hca_q=t["hca_q"].view(B, H, D), kv_h=t["kv_h"],
+                              mh=128, hca_out=hca_out, csa_lse=csa_lse, hca_lse=hca_lse, idx_out=idx,
+                              csa_sink=dev(cs), hca_sink=dev(hs))     # the args keep the sink tensors alive
+    b.csa_hca_decode(args)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), want_idx[:, 0])
+    assert_rows_close(host_bf16(csa_out), want_csa, what="csa layer with sink")
+    assert_rows_close(host_bf16(hca_out), want_hca, what="hca layer with sink")
+    assert np.allclose(csa_lse.cpu().numpy(), wl_csa.reshape(B, H), atol=2e-2, rtol=0)
+    assert np.allclose(hca_lse.cpu().numpy(), wl_hca.reshape(B, H), atol=2e-2, rtol=0)
