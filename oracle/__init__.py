@@ -83,6 +83,8 @@ def _load():
         lib.ora_sparse_attn.restype = I
         lib.ora_dense_attn.argtypes = [I, I, I, I, I, LL, I, LL, D, P, P, P, P, P]
         lib.ora_dense_attn.restype = None
+        lib.ora_rope.argtypes = [I, I, I, I, D, I, P, P, P]
+        lib.ora_rope.restype = None
         _lib = lib
     return _lib
 
@@ -238,6 +240,22 @@ def dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, sink=None):
     sk = _sink(sink, H)
     lib.ora_dense_attn(B, Tq, H, D, Nh, L, mh, pos0, float(scale), pq, pk, _ptr(sk), _ptr(out), _ptr(lse))
     return out, lse
+
+
+def rope(x, pos, rd: int = 64, theta: float = 10000.0, inverse: bool = False, group: int = 1):
+    """Partial rotary position embedding of bf16 rows x[..., D] (C11): the last rd dimensions are rotated in
+    adjacent pairs, pair j by pos * theta^(-2j/rd) (negated when inverse); row r takes pos[r // group].
+    Returns fp64 rows of x's shape."""
+    lib = _load()
+    x, px = _c(x, np.uint16)
+    D = x.shape[-1]
+    n = x.size // D
+    pos = np.ascontiguousarray(pos, dtype=np.int64).reshape(-1)
+    if rd % 2 or not 0 < rd <= D or n % group or pos.size != n // group:
+        raise ValueError("rope: rd even in (0, D], one position per group of rows")
+    y = np.empty(x.shape, np.float64)
+    lib.ora_rope(n, D, rd, group, float(theta), 1 if inverse else 0, px, _ptr(pos), _ptr(y))
+    return y
 
 
 # --- A1 ---------------------------------------------------------------------

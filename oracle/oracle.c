@@ -512,3 +512,30 @@ void ora_dense_attn(int B, int Tq, int H, int D, int Nh, long long L, int mh, lo
         free(rows);
     }
 }
+
+/* ---- C11: partial rotary position embedding ----------------------------------------------------------
+ * [P1 section 1.1]: the rotary position embedding acts only on the last 64 dimensions of a query / KV
+ * vector, and the core attention output receives the inverse rotation at the query's position, which
+ * restores the relative-position structure.  The pages print no formula; the rotation is the standard
+ * rotary embedding with adjacent-pair (interleaved) pairing over the last rd dimensions:
+ *   pair j = (D-rd+2j, D-rd+2j+1), frequency f_j = theta^(-2j/rd), angle a = pos * f_j,
+ *   (u, v) -> (u cos a - v sin a, u sin a + v cos a); the inverse uses -a.
+ * Row r of x (bf16 [n][D]) takes position pos[r / group]; the first D-rd dimensions pass unchanged.
+ * y is fp64 [n][D]. */
+void ora_rope(int n, int D, int rd, int group, double theta, int inverse, const uint16_t* x,
+              const long long* pos, double* y)
+{
+    for (int r = 0; r < n; ++r) {
+        const double p = (double)pos[r / group];
+        const uint16_t* xr = x + (size_t)r * D;
+        double* yr = y + (size_t)r * D;
+        for (int d = 0; d < D - rd; ++d) yr[d] = ora_bf16_value(xr[d]);
+        for (int j = 0; j < rd / 2; ++j) {
+            const double f = pow(theta, -2.0 * j / rd);
+            const double a = (inverse ? -p : p) * f;
+            const double u = ora_bf16_value(xr[D - rd + 2 * j]), v = ora_bf16_value(xr[D - rd + 2 * j + 1]);
+            yr[D - rd + 2 * j] = u * cos(a) - v * sin(a);
+            yr[D - rd + 2 * j + 1] = u * sin(a) + v * cos(a);
+        }
+    }
+}

@@ -525,3 +525,67 @@ def test_sink_limits_and_textbook_softmax():
     p = scipy.special.softmax(logits, axis=1)
     np.testing.assert_allclose(out_s[0, 0], p[:, :-1] @ Kf, rtol=1e-11, atol=1e-14)
     np.testing.assert_allclose(lse_s[0, 0], scipy.special.logsumexp(logits, axis=1), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# C11: partial rotary position embedding
+# ---------------------------------------------------------------------------
+
+def _rope_rows(seed, n, D):
+    return synth.to_bf16_bits(synth.normal_f32(seed, "rope_x", (n, D)))
+
+
+def test_rope_matches_library_interleaved_rotation():
+    """The rotated part equals transformers' DeepSeek-V3 interleaved rotary routine (which returns the pair
+    halves de-interleaved) with cos/sin from its Llama rotary-embedding module, theta = 10000, rd = 64."""
+    from transformers import LlamaConfig
+    from transformers.models.deepseek_v3.modeling_deepseek_v3 import apply_rotary_pos_emb_interleave
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding
+    D, rd, n = 128, 64, 40
+    x = _rope_rows(1, n, D)
+    pos = np.arange(n, dtype=np.int64) * 7 + 3                      # positions 3 .. 276
+    got = oracle.rope(x, pos, rd=rd, theta=10000.0)
+    cfg = LlamaConfig(hidden_size=rd, num_attention_heads=1, head_dim=rd, rope_theta=10000.0)
+    emb = LlamaRotaryEmbedding(config=cfg)
+    xt = torch.from_numpy(oracle.bf16_value(x)[:, D - rd:]).view(1, 1, n, rd)   # (batch, heads, seq, dim)
+    cos, sin = emb(xt.float(), torch.from_numpy(pos).view(1, n))
+    ref, _ = apply_rotary_pos_emb_interleave(xt, xt, cos.double(), sin.double())
+    ref = ref.view(n, rd).numpy()
+    mine = np.concatenate([got[:, D - rd::2], got[:, D - rd + 1::2]], axis=1)
+    assert np.abs(mine - ref).max() < 1e-4                          # the library's cos/sin are fp32
+    assert np.array_equal(got[:, :D - rd], oracle.bf16_value(x)[:, :D - rd])
+
+
+def test_rope_rotation_invariants():
+    D, rd = 512, 64
+    x = _rope_rows(2, 6, D)
+    xv = oracle.bf16_value(x)
+    assert np.array_equal(oracle.rope(x, np.zeros(6, np.int64)), xv)              # position 0: identity
+    p = np.array([0, 1, 1000, 65_537, 262_143, 1_048_575], np.int64)
+    y = oracle.rope(x, p, rd=rd)
+    yi = oracle.rope(x, p, rd=rd, inverse=True)
+    assert np.array_equal(y[:, :D - rd], xv[:, :D - rd])
+    # each pair keeps its length
+    pr = lambda a: a[:, D - rd:].reshape(6, rd // 2, 2)
+    assert np.allclose(np.hypot(*np.moveaxis(pr(y), -1, 0)), np.hypot(*np.moveaxis(pr(xv), -1, 0)), atol=1e-12)
+    # the inverse is the rotation by the opposite angle: rope(x, p)_j . rope_inv(x, p)_j = |x_j|^2 cos(2 a_j) and
+    # the forward rotation of a vector by p then by -p is the vector (checked as a relative-position identity)
+    q, k = xv[0], xv[1]
+    qb, kb = x[0:1], x[1:2]
+    for i, j in [(5, 2), (1000, 999), (262_143, 100)]:
+        lhs = oracle.rope(qb, [i])[0, D - rd:] @ oracle.rope(kb, [j])[0, D - rd:]
+        rhs = oracle.rope(qb, [i - j])[0, D - rd:] @ k[D - rd:]
+        assert abs(lhs - rhs) < 1e-9 * (1 + abs(rhs))
+        inv = oracle.rope(qb, [i], inverse=True)[0, D - rd:] @ oracle.rope(kb, [j], inverse=True)[0, D - rd:]
+        assert abs(inv - oracle.rope(qb, [j - i])[0, D - rd:] @ k[D - rd:]) < 1e-9 * (1 + abs(rhs))
+    assert np.allclose(yi[1:2], oracle.rope(x[1:2], [-1]), atol=0)                 # inverse at p == forward at -p
+
+
+def test_rope_group_maps_rows_to_positions():
+    x = _rope_rows(3, 12, 128)
+    pos = np.array([4, 9000, 77], np.int64)
+    a = oracle.rope(x, pos, group=4)
+    b = oracle.rope(x, np.repeat(pos, 4))
+    assert np.array_equal(a, b)
+    with pytest.raises(ValueError):
+        oracle.rope(x, pos, group=5)
