@@ -495,7 +495,23 @@ def prefill_attn_leg(args, dev, pc, idx):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / n * 1e3
     flops = 4.0 * H * D * (topk + W) * Tq
-    return {"H": H, "D": D, "W": W, "calls": n, "ms_per_call": round(ms, 4),
+    # partial rotary embedding of the same queries (rd = 64, one position per query): one read and one write
+    # of every query row, out of place
+    qo = torch.empty_like(q)
+    qpos = torch.arange(pos0, pos0 + Tq, dtype=torch.int64, device=dev)
+    b.csa_rope(q, qpos, qo, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        b.csa_rope(q, qpos, qo, stream=stream)
+    torch.cuda.synchronize()
+    rms = (time.perf_counter() - t0) / n * 1e3
+    rbytes = 2.0 * q.numel() * 2 + qpos.numel() * 8
+    rope = {"workload": f"rope_{Tq}q_{H}h_{D}", "rd": 64, "calls": n, "ms_per_call": round(rms, 4),
+            "value": round(rbytes / (rms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_call": rbytes}
+    del qo
+    return {"H": H, "D": D, "W": W, "calls": n, "ms_per_call": round(ms, 4), "rope": rope,
             "value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
             "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
             "algorithmic_flops_per_call": flops, "index_source": "the indexer leg's selection"}

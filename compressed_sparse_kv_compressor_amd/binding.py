@@ -44,6 +44,7 @@ def _load():
         "hca_dense_attn": ([P, P, I, I, I, I, I, LL, I, LL, F, P, P, P, P, Z, P], I),
         "csa_hca_decode_ws_bytes": ([P], Z),
         "csa_hca_decode": ([P, P, Z, P], I),
+        "csa_rope": ([P, P, P, LL, I, I, I, ctypes.c_double, I, P], I),
         "csa_debug_fp8_to_bf16": ([P, P, I, P], I),
         "csa_prof_enable": ([I], I),
         "csa_prof_reset": ([], I),
@@ -63,7 +64,7 @@ EXPORTED = ("csa_abi_version", "csa_status_str", "csa_last_error", "csa_compress
             "csa_hca_compress_ws_bytes", "csa_hca_compress",
             "csa_index_topk_ws_bytes", "csa_index_topk", "csa_sparse_attn_ws_bytes", "csa_sparse_attn",
             "hca_dense_attn_ws_bytes", "hca_dense_attn", "csa_hca_decode_ws_bytes", "csa_hca_decode",
-            "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read",
+            "csa_rope", "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read",
             "csa_prof_only")
 
 
@@ -203,6 +204,19 @@ def csa_hca_decode(args: DecodeArgs, ws=None, stream=None, device=None):
     if ws is None:
         ws = workspace(need, device or torch.device("cuda"))
     _check(lib.csa_hca_decode(ctypes.byref(args), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def csa_rope(x, pos, out=None, rd: int = 64, theta: float = 10000.0, inverse: bool = False, stream=None):
+    """Partial rotary embedding of bf16 rows x[..., D] (int16 bit tensor) into out (x itself when None);
+    pos: int64 device tensor with one position per group of rows, group = rows / pos.numel()."""
+    D = x.shape[-1]
+    n = x.numel() // D
+    if pos.dtype != torch.int64 or pos.numel() == 0 or n % pos.numel():
+        raise ValueError("pos must be a non-empty int64 tensor whose size divides the row count")
+    out = x if out is None else out
+    _check(lib.csa_rope(_p(x), _p(out), _p(pos), n, D, rd, n // pos.numel(), float(theta), 1 if inverse else 0,
+                        _stream(stream)))
+    return out
 
 
 def csa_debug_fp8_to_bf16(inp, out, stream=None):

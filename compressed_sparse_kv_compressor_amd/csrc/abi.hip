@@ -1,6 +1,7 @@
 // abi.hip -- the C ABI of libcsa (include/csa.h): argument validation, workspace
 // sizing and launch sequencing.  Nothing here computes; every step of the method
 // runs in the kernels of index_topk.hip, attn.hip and compress.hip.
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -385,6 +386,24 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     if (rc) return rc;
     return csa_host::attn_launch(a->hca_q, rd, a->B, 1, a->H, a->D, p, a->scale, a->hca_out, a->hca_lse, w + sws,
                                  aws - sws, st, "k_attn_dense");
+}
+
+// Partial rotary position embedding of bf16 rows (see include/csa.h).
+int csa_rope(const void* x, void* y, const long long* pos, long long n, int D, int rd, int group, double theta,
+             int inverse, void* stream) {
+    const char* fn = "csa_rope";
+    csa_host::g_err[0] = 0;
+    REQ(n >= 0 && D >= 8 && D % 8 == 0, CSA_ERR_SHAPE, "%s: need n >= 0 and D a positive multiple of 8", fn);
+    REQ(rd > 0 && rd % 8 == 0 && rd <= D, CSA_ERR_SHAPE, "%s: rd must be a multiple of 8 in (0, D]", fn);
+    REQ(group >= 1 && n % group == 0, CSA_ERR_SHAPE, "%s: group must be >= 1 and divide n", fn);
+    REQ(std::isfinite(theta) && theta > 1.0, CSA_ERR_SHAPE, "%s: theta must be finite and > 1", fn);
+    REQ(inverse == 0 || inverse == 1, CSA_ERR_SHAPE, "%s: inverse must be 0 or 1", fn);
+    if (n == 0) return CSA_OK;
+    REQ_PTR(x);
+    REQ_PTR(y);
+    REQ(pos != nullptr, CSA_ERR_NULL, "%s: pos is NULL", fn);
+    REQ(((uintptr_t)pos & 7u) == 0, CSA_ERR_ALIGN, "%s: pos is not 8-byte aligned", fn);
+    return csa_host::rope_launch(x, y, pos, n, D, rd, group, theta, inverse, (hipStream_t)stream);
 }
 
 // Diagnostic: fp8 (OCP e4m3) -> bf16 conversion exactly as the indexer kernel does it.

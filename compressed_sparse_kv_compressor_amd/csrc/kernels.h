@@ -19,6 +19,8 @@ int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_id
                          long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out, void* ws,
                          hipStream_t st);
 int fp8_to_bf16_launch(const void* in, void* out, int n, hipStream_t st);
+int rope_launch(const void* x, void* y, const long long* pos, long long n, int D, int rd, int group, double theta,
+                int inverse, hipStream_t st);
 
 // Row sets of the split-KV attention: dense over a visible prefix (HCA), or
 // gathered entries followed by raw window rows (CSA).

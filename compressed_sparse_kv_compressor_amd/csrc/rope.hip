@@ -1,0 +1,66 @@
+// Partial rotary position embedding (V4 technical summary, section 1.1 "hybrid attention"): the rotation
+// acts on the last rd dimensions of a query / KV row only, and the attention output takes the inverse
+// rotation at its query position.  Pair j = (D-rd+2j, D-rd+2j+1) turns by pos * theta^(-2j/rd) (the
+// opposite angle for the inverse); the first D-rd dimensions pass through.
+//
+// HBM-bound elementwise work: one lane per 16-byte chunk (8 bf16) of a row, grid-stride over all chunks,
+// so every wave reads and writes whole contiguous 1 KiB spans.  Angles are formed and reduced in fp64
+// (positions reach 2^20 and more: an fp32 product pos * f would already be off by ~0.1 rad there); the
+// rotation itself is fp32 and each output is rounded once to bf16.  In place (y == x) is allowed: a lane
+// reads its chunk before it writes it and no lane touches another's.
+#include "common.h"
+#include "kernels.h"
+
+using namespace csa;
+
+namespace {
+
+constexpr int RT = 256;
+
+__global__ __launch_bounds__(RT) void k_rope(const uint16_t* x, uint16_t* y, const long long* __restrict__ pos,
+                                            long long n, int D, int rd, int group, double log2_theta,
+                                            int inverse)
+{
+    const int cpr = D / 8;
+    const long long total = n * cpr;
+    const int first = (D - rd) / 8;          // first rotated chunk of a row
+    for (long long i = (long long)blockIdx.x * RT + threadIdx.x; i < total; i += (long long)gridDim.x * RT) {
+        const long long r = i / cpr;
+        const int c = (int)(i - r * cpr);
+        uint4 v = *(const uint4*)(x + r * D + 8 * c);
+        if (c >= first) {
+            const double p = (double)pos[r / group];
+            const double sp = inverse ? -p : p;
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = 4 * (c - first) + k;
+                const double a = sp * exp2(-2.0 * j / rd * log2_theta);
+                double s, co;
+                sincos(a, &s, &co);
+                const float cf = (float)co, sf = (float)s;
+                const float u = bf16_to_f32((uint16_t)(w[k] & 0xffffu)), t = bf16_to_f32((uint16_t)(w[k] >> 16));
+                w[k] = (uint32_t)f32_to_bf16(u * cf - t * sf) | ((uint32_t)f32_to_bf16(u * sf + t * cf) << 16);
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        *(uint4*)(y + r * D + 8 * c) = v;
+    }
+}
+
+}  // namespace
+
+namespace csa_host {
+
+int rope_launch(const void* x, void* y, const long long* pos, long long n, int D, int rd, int group, double theta,
+                int inverse, hipStream_t st) {
+    if (n == 0) return 0;
+    const long long chunks = n * (D / 8);
+    const long long blocks = (chunks + RT - 1) / RT;
+    const int grid = (int)(blocks < 2048 ? blocks : 2048);
+    CSA_LAUNCH("k_rope", k_rope, dim3(grid), dim3(RT), 0, st, (const uint16_t*)x, (uint16_t*)y, pos, n, D, rd,
+               group, log2(theta), inverse);
+    return 0;
+}
+
+}  // namespace csa_host

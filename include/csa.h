@@ -226,6 +226,23 @@ typedef struct csa_hca_decode_args {
 size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a);
 int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
+/* C11: partial rotary position embedding [P1 section 1.1]: the rotation acts
+ * on the last rd dimensions of a query / KV row only (rd = 64 on the pages),
+ * and the core attention output takes the inverse rotation at its query
+ * position.  Pair j = (D-rd+2j, D-rd+2j+1) turns by a = pos * theta^(-2j/rd):
+ * (u, v) -> (u cos a - v sin a, u sin a + v cos a); inverse = 1 uses -a.  The
+ * first D-rd dimensions are copied unchanged.
+ *   x, y : device [n][D] bf16, 16-byte aligned; y == x (in place) is allowed,
+ *          other overlaps are not.  Caller-owned.
+ *   pos  : device [n / group] int64, 8-byte aligned; row r takes pos[r / group]
+ *          (group = H for a [rows][H][D] query or output tensor, 1 for KV rows).
+ *   D % 8 == 0, rd % 8 == 0, 0 < rd <= D, group >= 1 divides n, theta > 1
+ *   (10000 is the usual base), inverse 0 or 1.  n = 0 is a no-op.
+ * Angles are formed in fp64, the rotation in fp32, outputs rounded once (RNE).
+ * Errors: CSA_ERR_SHAPE, CSA_ERR_NULL, CSA_ERR_ALIGN (nothing launched). */
+int csa_rope(const void* x, void* y, const long long* pos, long long n, int D, int rd, int group, double theta,
+             int inverse, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */
 /* ------------------------------------------------------------------------ */

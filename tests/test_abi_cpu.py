@@ -147,3 +147,20 @@ def test_decode_args_keep_their_tensors_alive(b):
     del t
     gc.collect()
     assert ref() is not None and args.csa_sink == ref().data_ptr()
+
+
+def test_rope_validation_codes(b):
+    """Argument checks of csa_rope (no launch: every call fails before one, or has no rows)."""
+    lib = b.lib
+    r = lib.csa_rope
+    # x, y, pos, n, D, rd, group, theta, inverse, stream
+    assert r(None, None, None, 0, 512, 64, 1, 10000.0, 0, None) == 0                    # no rows: no-op
+    assert r(A16, A16, A16, 4, 500, 64, 1, 10000.0, 0, None) == CSA_ERR_SHAPE            # D % 8
+    assert r(A16, A16, A16, 4, 512, 60, 1, 10000.0, 0, None) == CSA_ERR_SHAPE            # rd % 8
+    assert r(A16, A16, A16, 4, 128, 256, 1, 10000.0, 0, None) == CSA_ERR_SHAPE           # rd > D
+    assert r(A16, A16, A16, 4, 512, 64, 3, 10000.0, 0, None) == CSA_ERR_SHAPE            # group does not divide n
+    assert r(A16, A16, A16, 4, 512, 64, 1, 1.0, 0, None) == CSA_ERR_SHAPE                # theta <= 1
+    assert r(A16, A16, A16, 4, 512, 64, 1, float("inf"), 0, None) == CSA_ERR_SHAPE
+    assert r(A16, A16, A16, 4, 512, 64, 1, 10000.0, 2, None) == CSA_ERR_SHAPE            # inverse not 0/1
+    assert r(A16, A16, None, 4, 512, 64, 1, 10000.0, 0, None) == CSA_ERR_NULL
+    assert r(BAD, A16, A16, 4, 512, 64, 1, 10000.0, 0, None) == CSA_ERR_ALIGN

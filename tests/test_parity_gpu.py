@@ -720,3 +720,72 @@ def test_fused_decode_with_sinks_matches_oracle(b, L, B, H, D, HI, dI, topk, dt)
     assert_rows_close(host_bf16(hca_out), want_hca, what="hca layer with sink")
     assert np.allclose(csa_lse.cpu().numpy(), wl_csa.reshape(B, H), atol=2e-2, rtol=0)
     assert np.allclose(hca_lse.cpu().numpy(), wl_hca.reshape(B, H), atol=2e-2, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# C11: partial rotary position embedding
+# ---------------------------------------------------------------------------
+
+def assert_rope_close(got_bits, want, x_bits, rd):
+    """Elementwise: within one bf16 rounding of the fp64 rotation (plus fp32 rotation error on the row's scale);
+    the first D - rd dimensions bit-identical to the input; and the per-row bar of the attention outputs."""
+    D = want.shape[-1]
+    g = bf16_f64(got_bits).reshape(-1, D)
+    o = want.reshape(-1, D)
+    row = np.abs(bf16_f64(x_bits).reshape(-1, D)).max(axis=1, keepdims=True)
+    assert (np.abs(g - o) <= 2.0 ** -8 * np.abs(o) + 2.0 ** -20 * row).all()
+    assert np.array_equal(got_bits.reshape(-1, D)[:, :D - rd], x_bits.reshape(-1, D)[:, :D - rd])
+    assert_rows_close(got_bits, want, what="rope")
+
+
+ROPE_CASES = [
+    # (rows shape, rd, group, inverse, max position)
+    ((2, 3, 16, 128), 64, 16, False, 5000),             # queries [B][Tq][H][D]: one position per (b, t)
+    ((8, 128, 512), 64, 128, True, 1_048_575),          # decode output at the 1M position, inverse
+    ((8, 128, 512), 64, 128, False, 1_048_575),
+    ((1000, 512), 64, 1, False, 1 << 22),               # KV rows, one position each, ragged grid tail
+    ((37, 128), 128, 1, False, 70_000),                 # whole row rotated
+    ((5, 512), 8, 1, True, 300),                        # one chunk rotated
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES)
+def test_rope_parity(b, case):
+    shape, rd, group, inverse, pmax = case
+    x = synth.to_bf16_bits(synth.normal_f32(41, "rope", shape))
+    n = int(np.prod(shape[:-1]))
+    pos = np.random.default_rng(n + rd).integers(0, pmax + 1, size=n // group).astype(np.int64)
+    pos[0] = pmax
+    want = oracle.rope(x, pos, rd=rd, inverse=inverse, group=group)
+    out = torch.empty(shape, dtype=torch.int16, device=DEV)
+    b.csa_rope(dev(x), dev(pos), out, rd=rd, inverse=inverse)
+    xin = dev(x)
+    b.csa_rope(xin, dev(pos), rd=rd, inverse=inverse)                  # in place
+    torch.cuda.synchronize()
+    assert_rope_close(host_bf16(out), want, x, rd)
+    assert torch.equal(xin, out)
+
+
+def test_rope_inverse_undoes_forward(b):
+    x = synth.to_bf16_bits(synth.normal_f32(42, "rope_rt", (4, 64, 512)))
+    pos = dev(np.array([0, 1, 262_143, 1_048_575], np.int64))
+    t = dev(x)
+    b.csa_rope(t, pos)
+    b.csa_rope(t, pos, inverse=True)
+    torch.cuda.synchronize()
+    assert_rows_close(host_bf16(t), bf16_f64(x), what="rope round trip")
+
+
+def test_rope_prefill_size_sampled(b):
+    """The prefill query tensor (8192 queries x 64 heads x 512) in one call; sampled rows vs the oracle."""
+    Tq, H, D = 8192, 64, 512
+    g = torch.Generator(device=DEV).manual_seed(43)
+    x = (torch.randn((Tq, H, D), generator=g, device=DEV, dtype=torch.float32)).to(torch.bfloat16).view(torch.int16)
+    pos = torch.arange(262_144 - Tq, 262_144, dtype=torch.int64, device=DEV)
+    out = torch.empty_like(x)
+    b.csa_rope(x, pos, out)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(43).choice(Tq * H, size=512, replace=False)
+    xs = host_bf16(x).reshape(-1, D)[rows]
+    want = oracle.rope(xs, pos.cpu().numpy()[rows // H])
+    assert_rope_close(host_bf16(out).reshape(-1, D)[rows], want, xs, 64)
