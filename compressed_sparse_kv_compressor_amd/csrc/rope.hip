@@ -5,8 +5,10 @@
 //
 // HBM-bound elementwise work: one lane per 16-byte chunk (8 bf16) of a row, grid-stride over all chunks,
 // so every wave reads and writes whole contiguous 1 KiB spans.  Angles are formed and reduced in fp64
-// (positions reach 2^20 and more: an fp32 product pos * f would already be off by ~0.1 rad there); the
-// rotation itself is fp32 and each output is rounded once to bf16.  In place (y == x) is allowed: a lane
+// (positions reach 2^20 and more: an fp32 product pos * f would already be off by ~0.1 rad there): a lane's
+// four frequencies are one fp64 exp2 and three steps of the ratio theta^(-2/rd), each angle is reduced
+// modulo 2 pi with a two-term (Cody-Waite) constant, and only the reduced angle, in [-pi, pi], goes to an
+// fp32 sincos; the rotation is fp32 and each output is rounded once to bf16.  In place (y == x) is allowed: a lane
 // reads its chunk before it writes it and no lane touches another's.
 #include "common.h"
 #include "kernels.h"
@@ -16,10 +18,13 @@ using namespace csa;
 namespace {
 
 constexpr int RT = 256;
+constexpr double TWO_PI_HI = 6.283185307179586;            // 2 pi rounded to double
+constexpr double TWO_PI_LO = 2.4492935982947064e-16;       // 2 pi - TWO_PI_HI
+constexpr double INV_TWO_PI = 0.15915494309189535;
 
 __global__ __launch_bounds__(RT) void k_rope(const uint16_t* x, uint16_t* y, const long long* __restrict__ pos,
                                             long long n, int D, int rd, int group, double log2_theta,
-                                            int inverse)
+                                            double ratio, int inverse)
 {
     const int cpr = D / 8;
     const long long total = n * cpr;
@@ -32,13 +37,15 @@ __global__ __launch_bounds__(RT) void k_rope(const uint16_t* x, uint16_t* y, con
             const double p = (double)pos[r / group];
             const double sp = inverse ? -p : p;
             uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            double f = exp2(-2.0 * (4 * (c - first)) / rd * log2_theta);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int j = 4 * (c - first) + k;
-                const double a = sp * exp2(-2.0 * j / rd * log2_theta);
-                double s, co;
-                sincos(a, &s, &co);
-                const float cf = (float)co, sf = (float)s;
+                const double a = sp * f;
+                const double q = rint(a * INV_TWO_PI);
+                const float r = (float)fma(-q, TWO_PI_LO, fma(-q, TWO_PI_HI, a));
+                f *= ratio;
+                float sf, cf;
+                sincosf(r, &sf, &cf);
                 const float u = bf16_to_f32((uint16_t)(w[k] & 0xffffu)), t = bf16_to_f32((uint16_t)(w[k] >> 16));
                 w[k] = (uint32_t)f32_to_bf16(u * cf - t * sf) | ((uint32_t)f32_to_bf16(u * sf + t * cf) << 16);
             }
@@ -59,7 +66,7 @@ int rope_launch(const void* x, void* y, const long long* pos, long long n, int D
     const long long blocks = (chunks + RT - 1) / RT;
     const int grid = (int)(blocks < 2048 ? blocks : 2048);
     CSA_LAUNCH("k_rope", k_rope, dim3(grid), dim3(RT), 0, st, (const uint16_t*)x, (uint16_t*)y, pos, n, D, rd,
-               group, log2(theta), inverse);
+               group, log2(theta), pow(theta, -2.0 / rd), inverse);
     return 0;
 }
 
