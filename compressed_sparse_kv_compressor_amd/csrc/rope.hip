@@ -55,6 +55,44 @@ __global__ __launch_bounds__(RT) void k_rope(const uint16_t* x, uint16_t* y, con
     }
 }
 
+// D = 512, rd <= 128: a row is 64 chunks, so every wave of the grid-stride loop holds exactly one row (256 and
+// the grid stride are multiples of 64, and the chunk count is too, so whole waves enter and leave the loop
+// together).  Lane j forms pair j's angle once and the rotated lanes fetch their four (cos, sin) by shuffle:
+// the angle work is spread over the wave instead of running on its last rd / 8 lanes only.
+__global__ __launch_bounds__(RT) void k_rope512(const uint16_t* x, uint16_t* y, const long long* __restrict__ pos,
+                                               long long n, int rd, int group, double log2_theta, int inverse)
+{
+    const int lane = threadIdx.x & 63;
+    const int first = (512 - rd) / 8;
+    const long long total = n * 64;
+    for (long long i = (long long)blockIdx.x * RT + threadIdx.x; i < total; i += (long long)gridDim.x * RT) {
+        const long long r = i >> 6;
+        uint4 v = *(const uint4*)(x + r * 512 + 8 * lane);
+        const double p = (double)pos[r / group];
+        const double a = (inverse ? -p : p) * exp2(-2.0 * (lane < rd / 2 ? lane : 0) / rd * log2_theta);
+        const double q = rint(a * INV_TWO_PI);
+        float sn, cs;
+        sincosf((float)fma(-q, TWO_PI_LO, fma(-q, TWO_PI_HI, a)), &sn, &cs);
+        const int src = lane >= first ? 4 * (lane - first) : 0;
+        float sk[4], ck[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            sk[k] = __shfl(sn, src + k);
+            ck[k] = __shfl(cs, src + k);
+        }
+        if (lane >= first) {
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float u = bf16_to_f32((uint16_t)(w[k] & 0xffffu)), t = bf16_to_f32((uint16_t)(w[k] >> 16));
+                w[k] = (uint32_t)f32_to_bf16(u * ck[k] - t * sk[k]) | ((uint32_t)f32_to_bf16(u * sk[k] + t * ck[k]) << 16);
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        *(uint4*)(y + r * 512 + 8 * lane) = v;
+    }
+}
+
 }  // namespace
 
 namespace csa_host {
@@ -65,6 +103,11 @@ int rope_launch(const void* x, void* y, const long long* pos, long long n, int D
     const long long chunks = n * (D / 8);
     const long long blocks = (chunks + RT - 1) / RT;
     const int grid = (int)(blocks < 2048 ? blocks : 2048);
+    if (D == 512 && rd <= 128) {
+        CSA_LAUNCH("k_rope", k_rope512, dim3(grid), dim3(RT), 0, st, (const uint16_t*)x, (uint16_t*)y, pos, n, rd,
+                   group, log2(theta), inverse);
+        return 0;
+    }
     CSA_LAUNCH("k_rope", k_rope, dim3(grid), dim3(RT), 0, st, (const uint16_t*)x, (uint16_t*)y, pos, n, D, rd,
                group, log2(theta), pow(theta, -2.0 / rd), inverse);
     return 0;
