@@ -37,7 +37,7 @@ def _load():
         "csa_hca_compress_ws_bytes": ([I, LL, I, I, I, I, I, I], Z),
         "csa_hca_compress": ([P, I, LL, I, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, I, P, P, Z, P], I),
         "csa_index_topk_ws_bytes": ([I, I, I, I, I, I, I], Z),
-        "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, Z, P], I),
+        "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, Z, P], I),
         "csa_sparse_attn_ws_bytes": ([I, I, I, I, I, I], Z),
         "csa_sparse_attn": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P, Z, P], I),
         "hca_dense_attn_ws_bytes": ([I, I, I, I, I], Z),
@@ -137,14 +137,15 @@ def csa_hca_compress(hidden, w_kv, w_ik, w_gate, b_slot, m: int, W: int, kv_out,
 
 
 def csa_index_topk(q_idx, w_idx, k_idx, dtype: int, L: int, m: int, pos0: int, topk: int, idx_out, cnt_out=None,
-                   ws=None, stream=None):
+                   ws=None, stream=None, score_out=None):
     B, Tq, HI, dI = q_idx.shape
     Nc = k_idx.shape[1]
     need = lib.csa_index_topk_ws_bytes(B, Tq, HI, dI, Nc, topk, dtype)
     if ws is None:
         ws = workspace(need, q_idx.device)
     _check(lib.csa_index_topk(_p(q_idx), _p(w_idx), _p(k_idx), dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,
-                              _p(idx_out), _p(cnt_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+                              _p(idx_out), _p(cnt_out), _p(score_out), _p(ws), 0 if ws is None else ws.numel(),
+                              _stream(stream)))
 
 
 def _sink(sink, H: int):

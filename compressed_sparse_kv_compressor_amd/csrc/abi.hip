@@ -283,15 +283,16 @@ size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, 
 
 int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq, int HI, int dI,
                    int Nc, long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
-                   void* ws, size_t ws_bytes, void* stream) {
+                   float* score_out, void* ws, size_t ws_bytes, void* stream) {
     const char* fn = "csa_index_topk";
     csa_host::g_err[0] = 0;
     int rc = validate_index(fn, q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out, cnt_out);
     if (rc) return rc;
+    OPT_PTR(score_out);
     rc = check_ws(fn, ws, ws_bytes, csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk));
     if (rc) return rc;
     return csa_host::index_topk_launch(q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out,
-                                       cnt_out, ws, (hipStream_t)stream);
+                                       cnt_out, score_out, ws, (hipStream_t)stream);
 }
 
 size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W) {
@@ -372,7 +373,7 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     }
     const size_t iws = align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk));
     rc = csa_host::index_topk_launch(a->q_idx, a->w_idx, a->k_idx, a->idx_dtype, a->B, 1, a->HI, a->dI, Nc, a->L, a->m,
-                                     p, a->topk, idx, nullptr, w, st);
+                                     p, a->topk, idx, nullptr, nullptr, w, st);
     if (rc) return rc;
     w += iws;
     const size_t aws = ws_bytes - (size_t)(w - (char*)ws);

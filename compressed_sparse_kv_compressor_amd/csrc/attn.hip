@@ -216,20 +216,16 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
 // ---------------------------------------------------------------------------
 constexpr int HD = 256;   // d-half handled by one wave
 
-#ifndef CSA_ATTN64_QK_AHEAD
-#define CSA_ATTN64_QK_AHEAD 4      // K-operand LDS reads in flight ahead of the QK MFMAs
-#endif
-#ifndef CSA_ATTN64_PV_AHEAD
-#define CSA_ATTN64_PV_AHEAD 2      // d-tiles of V reads in flight ahead of the PV MFMAs
-#endif
+constexpr int ATT64_QK_AHEAD = 4;  // K-operand LDS reads in flight ahead of the QK MFMAs
+constexpr int ATT64_PV_AHEAD = 2;  // d-tiles of V reads in flight ahead of the PV MFMAs
 constexpr int ATT_TILES = 3;      // tile buffers; a split's tile count is a multiple of this
 
-// MODE 0: dense prefix (row r = entry r); MODE 1: selected entries then window rows.  BIG: some
-// array is beyond the reach of 32-bit byte offsets, so tiles are loaded with 64-bit addresses (the
-// other variant uses buffer loads only, which keeps the LDS wait counting exact in the main loop).
+// MODE 0: dense prefix (row r = entry r); MODE 1: selected entries then window rows.  Every array must
+// be within reach of 32-bit byte offsets: tiles are moved by buffer loads only, which keeps the LDS wait
+// counting exact in the main loop (larger arrays run the generic kernel).
 typedef float SxArr[4][4][64][4];         // score exchange [wave][j/4][lane][j%4] (one parity)
 
-template <int MODE, bool BIG>
+template <int MODE>
 __device__ __forceinline__ void attn64_body(
     int bid, uint16_t* bufA, uint16_t* bufB, uint16_t* bufC, SxArr* sx,
     const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
@@ -273,7 +269,6 @@ __device__ __forceinline__ void attn64_body(
 
     const uint16_t* kvb = R.kv ? R.kv + (size_t)b * R.N * D : nullptr;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
-    constexpr bool kv32 = !BIG, raw32 = !BIG;  // 32-bit byte offsets reach every row (buffer loads)
 
     bf16x8_t qreg[KS];
     {
@@ -319,7 +314,7 @@ __device__ __forceinline__ void attn64_body(
     };
     // Buffer resources over this d-half of the batch's rows (raw buffer, byte offsets).  An absent
     // array gets an empty resource: nothing is ever loaded through it.
-    const bool has_kv = kvb && kv32, has_raw = MODE == 1 && rawb && raw32;
+    const bool has_kv = kvb != nullptr, has_raw = MODE == 1 && rawb != nullptr;
     const __amdgpu_buffer_rsrc_t rs_kv =
         make_rsrc(has_kv ? kvb + dh * HD : nullptr, has_kv ? (uint32_t)((size_t)R.N * D * 2 - dh * HD * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rs_raw =
@@ -332,31 +327,19 @@ __device__ __forceinline__ void attn64_body(
         auto bdma = [&](__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, int i) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (CSA_LDS void*)(lb + 1024 * i), 16, (int)voff, (int)soff, 0, 0);
         };
-        auto gdma = [&](const void* src, int i) {
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                             (CSA_LDS void*)(lb + 1024 * i), 16, 0, 0);
-        };
         const int nval = max(0, min(TILE, s_end - r0));
         if constexpr (MODE == 0) {
-            if constexpr (kv32) {
-                if (r0 + TILE <= R.N) {                 // all 32 row slots lie inside the array
+            if (r0 + TILE <= R.N) {                     // all 32 row slots lie inside the array
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const int i = i0 + k;
-                        bdma(rs_kv, (lane_row + lane_chunk) ^ (16u * kappa(i)), (uint32_t)r0 * (D * 2) + 2048u * i, i);
-                    }
-                } else {                                // tail: slots past the array reread row 0
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const int i = i0 + k, r = r0 + 2 * i + rsub;
-                        bdma(rs_kv, (uint32_t)(r < R.N ? r : 0) * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
-                    }
+                for (int k = 0; k < 8; ++k) {
+                    const int i = i0 + k;
+                    bdma(rs_kv, (lane_row + lane_chunk) ^ (16u * kappa(i)), (uint32_t)r0 * (D * 2) + 2048u * i, i);
                 }
-            } else {
+            } else {                                    // tail: slots past the array reread row 0
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int i = i0 + k, r = r0 + 2 * i + rsub;
-                    gdma((const char*)(kvb + (size_t)(r < R.N ? r : 0) * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
+                    bdma(rs_kv, (uint32_t)(r < R.N ? r : 0) * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
                 }
             }
             return nval >= 32 ? 0xffffffffu : ((1u << nval) - 1u);
@@ -375,33 +358,23 @@ __device__ __forceinline__ void attn64_body(
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int i = i0 + k;
-                    if constexpr (kv32) bdma(rs_kv, roff[i] * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
-                    else gdma((const char*)(kvb + (size_t)roff[i] * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
+                    bdma(rs_kv, roff[i] * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
                 }
             } else {                                    // raw window rows (masked slots read the first one)
                 const int u0 = raw_first + (r0 - topk32);                   // raw row of slot 0
                 vm = nval >= 32 ? 0xffffffffu : ((1u << nval) - 1u);
-                if constexpr (raw32) {
-                    if (nval == TILE) {
+                if (nval == TILE) {
 #pragma unroll
-                        for (int k = 0; k < 8; ++k) {
-                            const int i = i0 + k;
-                            bdma(rs_raw, (lane_row + lane_chunk) ^ (16u * kappa(i)), (uint32_t)u0 * (D * 2) + 2048u * i, i);
-                        }
-                    } else {
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) {
-                            const int i = i0 + k, slot_ = 2 * i + rsub;
-                            const int u = slot_ < nval ? u0 + slot_ : raw_first;
-                            bdma(rs_raw, (uint32_t)u * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
-                        }
+                    for (int k = 0; k < 8; ++k) {
+                        const int i = i0 + k;
+                        bdma(rs_raw, (lane_row + lane_chunk) ^ (16u * kappa(i)), (uint32_t)u0 * (D * 2) + 2048u * i, i);
                     }
                 } else {
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
                         const int i = i0 + k, slot_ = 2 * i + rsub;
                         const int u = slot_ < nval ? u0 + slot_ : raw_first;
-                        gdma((const char*)(rawb + (size_t)u * D + dh * HD) + (lane_chunk ^ (16u * kappa(i))), i);
+                        bdma(rs_raw, (uint32_t)u * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
                     }
                 }
             }
@@ -456,7 +429,7 @@ __device__ __forceinline__ void attn64_body(
         const CSA_LDS char* Qb = (const CSA_LDS char*)Qbuf;
         uint32_t qb = qk_off, trb = tr_off;
         asm volatile("" : "+v"(qb), "+v"(trb));   // keep the per-read XORs in the loop (no hoisted address table)
-        constexpr int QK_AHEAD = CSA_ATTN64_QK_AHEAD;
+        constexpr int QK_AHEAD = ATT64_QK_AHEAD;
         bf16x8_t ka[KS];
         f32x16_t sacc;
 #pragma unroll
@@ -512,7 +485,7 @@ __device__ __forceinline__ void attn64_body(
             return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                    (CSA_LDS i16x4_t*)const_cast<CSA_LDS char*>(Pb + off)));
         };
-        constexpr int PV_AHEAD = CSA_ATTN64_PV_AHEAD;
+        constexpr int PV_AHEAD = ATT64_PV_AHEAD;
         u32x2_t vr[DT][4];
         auto load_d = [&](int d) {
             const uint32_t e = trb ^ (64u * d), o = trb ^ (64u * d + 32u);
@@ -635,14 +608,14 @@ __device__ __forceinline__ void attn64_body(
     __shared__ __attribute__((aligned(1024))) uint16_t bufC[2 * TILE * HD];   \
     __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];
 
-template <int MODE, bool BIG>
+template <int MODE>
 __global__ __launch_bounds__(TPB, 1) void k_attn64(
     const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
     int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse)
 {
     CSA_ATT64_LDS
-    attn64_body<MODE, BIG>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
+    attn64_body<MODE>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
                            part_o, part_ml, out, lse);
 }
 
@@ -716,22 +689,17 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // workgroup per CU): about one workgroup per CU, but at least ATT_MIN_TILES
 // tiles per split (each split writes 64 heads x 512 fp32 partials, so thin
 // splits cost more in partials than they save), tile counts a multiple of 3.
-#ifndef CSA_ATT_MIN_TILES
-#define CSA_ATT_MIN_TILES 6
-#endif
-#ifndef CSA_ATT_TARGET_WG
-#define CSA_ATT_TARGET_WG 256
-#endif
+constexpr int ATT_MIN_TILES = 6, ATT_TARGET_WG = 256;
 static bool use64(int D, int H) { return D == 512 && H % 32 == 0; }
 
 static void choose_split(int BT, int H, int D, int max_rows, int* nsplit, int* rps) {
     if (max_rows <= 0) { *nsplit = 1; *rps = 128; return; }
     if (use64(D, H)) {
         const int HP = (H + 63) / 64;
-        const int ns = std::max(1, CSA_ATT_TARGET_WG / (BT * HP));
+        const int ns = std::max(1, ATT_TARGET_WG / (BT * HP));
         const int unit = ATT_TILES * TILE;
         int r = (max_rows + ns - 1) / ns;
-        r = std::max(r, CSA_ATT_MIN_TILES * TILE);
+        r = std::max(r, ATT_MIN_TILES * TILE);
         r = (r + unit - 1) / unit * unit;
         *rps = r;
         *nsplit = (max_rows + r - 1) / r;
@@ -756,21 +724,13 @@ static int attn_rows(int mode, int H, int D, int n, int W) {
 
 // k_attn128 (128 heads per workgroup, one workgroup per CU): the rows per split are the same for every
 // workgroup of a launch (a multiple of 4 tiles), chosen so that the launch's tiles spread over about
-// CSA_A128_TARGET_WG workgroups, and at least CSA_A128_MIN_TILES tiles per split.
-#ifndef CSA_ATT128
-#define CSA_ATT128 1
-#endif
-#ifndef CSA_A128_TARGET_WG
-#define CSA_A128_TARGET_WG 256
-#endif
-#ifndef CSA_A128_MIN_TILES
-#define CSA_A128_MIN_TILES 4
-#endif
-static bool use128(int D, int H) { return CSA_ATT128 && D == 512 && H % 128 == 0; }
+// A128_TARGET_WG workgroups, and at least A128_MIN_TILES tiles per split.
+constexpr int A128_TARGET_WG = 256, A128_MIN_TILES = 4;
+static bool use128(int D, int H) { return D == 512 && H % 128 == 0; }
 static int a128_tiles(int rows) { return (rows + TILE - 1) / TILE; }
 static int a128_rps(long long total_tiles) {
-    long long tpw = (total_tiles + CSA_A128_TARGET_WG - 1) / CSA_A128_TARGET_WG;
-    tpw = std::max<long long>(tpw, CSA_A128_MIN_TILES);
+    long long tpw = (total_tiles + A128_TARGET_WG - 1) / A128_TARGET_WG;
+    tpw = std::max<long long>(tpw, A128_MIN_TILES);
     long long r = (tpw * TILE + ATT128_UNIT - 1) / ATT128_UNIT * ATT128_UNIT;
     return (int)std::min<long long>(r, ATT128_MAX_RPS);
 }
@@ -840,20 +800,17 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
             return attn128_launch(j, st, tag);
         }
     }
-    if (use64(D, H)) {
+    // the buffer-load kernels need every array within reach of 32-bit byte offsets; a larger one (a cache
+    // of more than 4 GiB per sequence) runs the generic kernel, which addresses rows with 64-bit pointers
+    if (use64(D, H) && !big32) {
         const int nunits = BT * ns, HP = (H + 63) / 64;
         const int nblk = (nunits + 7) / 8 * 8 * HP;
-        // byte offsets of whole arrays must fit 32 bits for the buffer-load variant
-        const bool big = (size_t)a.N * D * 2 > 0xffffffffull || (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
-#define CSA_ATTN64(M, BIG_)                                                                                  \
-    CSA_LAUNCH(tag, (k_attn64<M, BIG_>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, \
-               nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse)
-        if (a.mode == 0) {
-            if (big) CSA_ATTN64(0, true); else CSA_ATTN64(0, false);
-        } else {
-            if (big) CSA_ATTN64(1, true); else CSA_ATTN64(1, false);
-        }
-#undef CSA_ATTN64
+        if (a.mode == 0)
+            CSA_LAUNCH(tag, k_attn64<0>, dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2,
+                       nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
+        else
+            CSA_LAUNCH(tag, k_attn64<1>, dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2,
+                       nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse, R.sink);

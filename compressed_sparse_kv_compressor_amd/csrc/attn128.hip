@@ -32,12 +32,8 @@ constexpr int A_TPB = 256;
 constexpr int NBUF = 4;                  // tile buffers (a split's tile count is a multiple of this)
 constexpr int ROWB = 1024;               // bytes of one 512-wide bf16 row
 
-#ifndef CSA_A128_QK_AHEAD
-#define CSA_A128_QK_AHEAD 4              // K-operand LDS reads in flight ahead of the QK MFMAs
-#endif
-#ifndef CSA_A128_PV_AHEAD
-#define CSA_A128_PV_AHEAD 2              // d-tiles of V reads in flight ahead of the PV MFMAs
-#endif
+constexpr int A128_QK_AHEAD = 4;         // K-operand LDS reads in flight ahead of the QK MFMAs
+constexpr int A128_PV_AHEAD = 2;         // d-tiles of V reads in flight ahead of the PV MFMAs
 
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
@@ -167,7 +163,7 @@ __device__ __forceinline__ void attn128_body(
         const CSA_LDS char* Qb = (const CSA_LDS char*)Qbuf;
         uint32_t qb = qk_off, trb = tr_off;
         asm volatile("" : "+v"(qb), "+v"(trb));   // keep the per-read XORs in the loop
-        constexpr int QK_AHEAD = CSA_A128_QK_AHEAD;
+        constexpr int QK_AHEAD = A128_QK_AHEAD;
         bf16x8_t ka[KS];
         f32x16_t sacc;
 #pragma unroll
@@ -222,7 +218,7 @@ __device__ __forceinline__ void attn128_body(
             return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                    (CSA_LDS i16x4_t*)const_cast<CSA_LDS char*>(Pb + off)));
         };
-        constexpr int PV_AHEAD = CSA_A128_PV_AHEAD;
+        constexpr int PV_AHEAD = A128_PV_AHEAD;
         u32x2_t vr[DT][4];
         auto load_d = [&](int d) {
             const uint32_t e = trb ^ (64u * d), o = trb ^ (64u * d + 32u);

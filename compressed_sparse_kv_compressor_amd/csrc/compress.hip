@@ -432,10 +432,7 @@ __global__ __launch_bounds__(GTPB) void k_gemm(ARows a, const uint16_t* __restri
 // ---------------------------------------------------------------------------
 constexpr int G2_T = 256, G2_KS = 32, G2_NB = 4, G2_ROWB = G2_KS * 2;     // tile, K step, buffers, row bytes
 constexpr int G2_BUF = 2 * G2_T * G2_ROWB;                                 // A rows then B rows: 32 KiB
-#ifndef CSA_G2_NW
-#define CSA_G2_NW 8
-#endif
-constexpr int G2_NW = CSA_G2_NW;                                           // waves per workgroup (4 or 8)
+constexpr int G2_NW = 8;                                                   // waves per workgroup (4 or 8)
 constexpr int G2_WNB = 16 / G2_NW;                                         // 32-column blocks per wave (4 or 2)
 constexpr int G2_WNW = G2_T / (32 * G2_WNB);                               // waves across N (2 or 4)
 constexpr int G2_DMA = G2_T * G2_ROWB / 1024 / G2_NW;                      // 1 KiB loads per wave per operand

@@ -144,10 +144,7 @@ __global__ __launch_bounds__(TPB) void k_score(
     constexpr int EPL = DI / 4;               // key elements per lane
     constexpr int KB = DT == 0 ? EPL * 2 : EPL;   // key bytes per lane
     constexpr int NV = KB / 16;               // 16-byte loads per lane per tile
-#ifndef CSA_SCORE_BATCH_BYTES
-#define CSA_SCORE_BATCH_BYTES 128
-#endif
-    constexpr int U = CSA_SCORE_BATCH_BYTES / KB;   // tiles per load batch (bytes per lane in flight)
+    constexpr int U = 128 / KB;                // tiles per load batch (bytes per lane in flight)
     constexpr int HP = HI < 4 ? 4 : HI;       // padded heads per query row
     constexpr int G = 16 / HP;                // query rows per column group
     constexpr int LPR = HP / 4;               // lanes (of one key) holding one row's heads
@@ -225,12 +222,12 @@ __global__ __launch_bounds__(TPB) void k_score(
         const int lrow = tr - g * G;
 
         // key loads are software-pipelined: batch i+1 is in flight while batch i computes
-        // (rows past the end reread the last row: branch-free loads keep the wait counts exact, so the
-        //  next batch stays in flight; those keys are never written)
+        // (rows past the last visible entry reread it: branch-free loads keep the wait counts exact, so
+        //  the next batch stays in flight; those keys are never written)
         auto load_batch = [&](int tt0, u32x4_t (&dst)[U][NV]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int krow = min(key0 + ((tt0 + u) * 4 + wave) * 16 + col, Nc - 1);
+                const int krow = min(key0 + ((tt0 + u) * 4 + wave) * 16 + col, nvmax - 1);
                 const char* kp = (const char*)k_idx + ((size_t)b * Nc + krow) * DI * ES + (size_t)grp * 16;
 #pragma unroll
                 for (int i = 0; i < NV; ++i) dst[u][i] = *(const u32x4_t*)(kp + i * 64);
@@ -413,7 +410,7 @@ __global__ __launch_bounds__(STPB) void k_select(
     uint2* __restrict__ band_g, unsigned long long* __restrict__ bkey_g, uint8_t* __restrict__ flag_g,
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int topk,
-    int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out, float* __restrict__ score_out)
 {
     constexpr int ES = DT == 0 ? 2 : 1;
     __shared__ uint32_t lh[BINS2];
@@ -428,8 +425,11 @@ __global__ __launch_bounds__(STPB) void k_select(
     const int lane = lane_id(), wave = tid >> 6;
     const int nv = n_visible(pos0 + t, L, m, Nc);
     int32_t* out = idx_out + (size_t)r * topk;
-    if (nv <= topk) {                                 // every visible entry is selected
-        for (int i = tid; i < topk; i += STPB) out[i] = i < nv ? i : -1;
+    if (nv <= topk) {                                 // every visible entry is selected (no score is formed)
+        for (int i = tid; i < topk; i += STPB) {
+            out[i] = i < nv ? i : -1;
+            if (score_out) score_out[(size_t)r * topk + i] = __builtin_nanf("");
+        }
         if (cnt_out && tid == 0) cnt_out[r] = nv;
         return;
     }
@@ -568,8 +568,13 @@ __global__ __launch_bounds__(STPB) void k_select(
     for (uint32_t e = e0; e < e1; ++e) mine += fget(e) == 1;
     uint32_t tot2;
     uint32_t o = block_scan(mine, scratch, &tot2);
+    float* sout = score_out ? score_out + (size_t)r * topk : nullptr;
     for (uint32_t e = e0; e < e1; ++e)
-        if (fget(e) == 1 && o < (uint32_t)topk) out[o++] = (int32_t)cand(e).x;
+        if (fget(e) == 1 && o < (uint32_t)topk) {
+            const uint2 c = cand(e);
+            if (sout) sout[o] = __uint_as_float(c.y);          // the approximate score it was ranked by
+            out[o++] = (int32_t)c.x;
+        }
     if (cnt_out && tid == 0) cnt_out[r] = topk;
 }
 
@@ -594,7 +599,7 @@ static size_t decode_index_ws_bytes(int B, int Tq, int Nc) {
 template <int DT, int DI, int HI>
 static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx, int B, int Tq, int Nc,
                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
-                        void* ws, hipStream_t st) {
+                        float* score_out, void* ws, hipStream_t st) {
     const size_t R = (size_t)B * Tq;
     const int NcP = (Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
     char* p = (char*)ws;
@@ -612,18 +617,14 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
     }
     // keys per scoring workgroup (4 waves x tiles of 16): the largest of 4096/2048/1024 that still
     // gives >= 512 workgroups (two per CU), so the grid runs in one round without a tail
-#ifndef CSA_SCORE_KPW
     int kpw = 4096;
     while (kpw > 1024 && (size_t)((Nc + kpw - 1) / kpw) * B < 512) kpw >>= 1;
-#else
-    const int kpw = CSA_SCORE_KPW;
-#endif
     CSA_LAUNCH("k_score", (k_score<DT, DI, HI>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
                q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist);
     CSA_LAUNCH("k_collect", k_collect, dim3(NcP / CCHUNK, (unsigned)R), dim3(STPB), 0, st, S, hist, list, ctab, Tq,
                Nc, NcP, L, m, pos0, topk);
     CSA_LAUNCH("k_select", (k_select<DT, DI, HI>), dim3((unsigned)R), dim3(STPB), 0, st, hist, list, ctab, band,
-               bkey, flags, q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out);
+               bkey, flags, q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out, score_out);
     return 0;
 }
 
@@ -634,13 +635,14 @@ size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int
 
 int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
                       int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
-                      int32_t* idx_out, int32_t* cnt_out, void* ws, hipStream_t st) {
+                      int32_t* idx_out, int32_t* cnt_out, float* score_out, void* ws, hipStream_t st) {
     if (prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk))
-        return prefill_index_launch(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk, idx_out, cnt_out, ws, st);
+        return prefill_index_launch(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk, idx_out, cnt_out, score_out,
+                                    ws, st);
 #define CSA_IDX_CASE(DT, DI, HI_)                                                              \
     if (dtype == DT && dI == DI && HI == HI_)                                                  \
         return launch_index<DT, DI, HI_>(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk,     \
-                                         idx_out, cnt_out, ws, st);
+                                         idx_out, cnt_out, score_out, ws, st);
 #define CSA_IDX_HI(DT, DI) CSA_IDX_CASE(DT, DI, 1) CSA_IDX_CASE(DT, DI, 2) CSA_IDX_CASE(DT, DI, 4) \
                            CSA_IDX_CASE(DT, DI, 8) CSA_IDX_CASE(DT, DI, 16)
     CSA_IDX_HI(0, 64) CSA_IDX_HI(0, 128) CSA_IDX_HI(1, 64) CSA_IDX_HI(1, 128)

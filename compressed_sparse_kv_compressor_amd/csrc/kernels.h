@@ -11,13 +11,13 @@ namespace csa_host {
 size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk);
 int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
                       int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
-                      int32_t* idx_out, int32_t* cnt_out, void* ws, hipStream_t st);
+                      int32_t* idx_out, int32_t* cnt_out, float* score_out, void* ws, hipStream_t st);
 // many-query (prefill) indexer path: bf16, HI = 8, dI = 128, Tq >= 64, topk <= 1024
 bool prefill_index_applicable(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk);
 size_t prefill_index_ws_bytes(int B, int Tq, int Nc);
 int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_idx, int B, int Tq, int Nc,
-                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out, void* ws,
-                         hipStream_t st);
+                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
+                         float* score_out, void* ws, hipStream_t st);
 int fp8_to_bf16_launch(const void* in, void* out, int n, hipStream_t st);
 int rope_launch(const void* x, void* y, const long long* pos, long long n, int D, int rd, int group, double theta,
                 int inverse, hipStream_t st);

@@ -29,8 +29,10 @@
 // (|d~_h - d_h| <= C_DOT sum_i |q_hi k_i| <= C_DOT N_h by Cauchy-Schwarz, and
 // |d~_h| <= N_h (1 + C_DOT)) gives
 //   |S~ - S| <= sum_h |w_h| N_h [(C_SUM (1 + 2 C_DOT) + C_DOT)(1 + 2^-10)
-//               + 2^-24 (1 + C_DOT)(1 + 2^-21)] + 2^-126 <= Wq Kmax 2^-17 + 2^-126,
-// since the bracket is below 5.8e-6 < 2^-17.  The classification argument is the
+//               + 2^-24 (1 + C_DOT)(1 + 2^-21)] + 2^-126 <= Wq Kmax 2^-16 + 2^-126,
+// since with C_DOT = 2^-17 and C_SUM = 2^-19 the bracket is below 9.7e-6 < 2^-16.  The
+// 32x32x16 MFMA's dot over 128 elements chains 8 instructions of 16 products through the
+// accumulator, which the decode path's order-free model covers.  The classification argument is the
 // decode path's; the list holds every entry with S~ >= thr, so when thr <= tau - 2D
 // it holds every entry that is in or in the band.
 #include "common.h"
@@ -49,25 +51,13 @@ constexpr int P_ROW_B = P_DI * 2;             // bytes per key row (bf16)
 constexpr int P_TK = 64;                      // entries per LDS tile
 constexpr int P_NA = 2;                       // 32-row MFMA blocks per wave (4 queries x 8 heads each)
 constexpr int P_QPW = 4 * P_NA;               // queries per wave
-#ifndef CSA_PF_NW
-#define CSA_PF_NW 4
-#endif
-#ifndef CSA_PF_UNITS
-#define CSA_PF_UNITS 1024
-#endif
-#ifndef CSA_PF_VPM1
-#define CSA_PF_VPM1 8                 // VALU instructions scheduled after each MFMA of a tile's first half
-#endif
-#ifndef CSA_PF_VPM2
-#define CSA_PF_VPM2 5                 // ... and of its second half
-#endif
-#ifndef CSA_PF_NBUF
-#define CSA_PF_NBUF 5
-#endif
-constexpr int P_NBUF = CSA_PF_NBUF;           // LDS tile buffers (loads run P_NBUF - 1 tiles ahead)
+constexpr int P_UNITS = 1024;                 // target workgroups of the contraction
+constexpr int P_VPM1 = 8;                     // VALU instructions scheduled after each MFMA of a tile's first half
+constexpr int P_VPM2 = 5;                     // ... and of its second half
+constexpr int P_NBUF = 5;                     // LDS tile buffers (loads run P_NBUF - 1 tiles ahead)
 static_assert(P_NBUF >= 3 && P_NBUF <= 8, "tile buffers");
 static_assert(P_TK == 64, "the tile pipeline handles two 32-entry sub-tiles per tile");
-constexpr int P_NW = CSA_PF_NW;               // waves per workgroup
+constexpr int P_NW = 4;                       // waves per workgroup
 constexpr int P_QPG = P_QPW * P_NW;           // queries per workgroup
 constexpr int P_TPB = 64 * P_NW;
 constexpr int P_DMA = 16 / P_NW;              // 1 KiB tile loads per wave per tile
@@ -398,15 +388,13 @@ __device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], con
 #pragma unroll
             for (int a = 0; a < P_NA; ++a) acc0[a] = mfma32_bf16(qa[a][s], as_bf16x8(bt[0][s]), acc0[a]);
         finish_prev(tile - 1, tile > 0);
-#ifndef CSA_PF_NO_INTERLEAVE
         // one MFMA, then a share of the VALU work (the 32x32x16 MFMA leaves room for about six VALU
         // instructions beside it)
 #pragma unroll
         for (int i = 0; i < 8 * P_NA; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, CSA_PF_VPM1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, P_VPM1, 0);
         }
-#endif
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 8; ++s)
@@ -417,13 +405,11 @@ __device__ __forceinline__ void pscore_body(uint16_t* const (&bufs)[P_NBUF], con
             block_scores(acc0[a], wv[a], pVA[a], pVB[a]);
             pacc[a] = acc1[a];
         }
-#ifndef CSA_PF_NO_INTERLEAVE
 #pragma unroll
         for (int i = 0; i < 8 * P_NA; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, CSA_PF_VPM2, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, P_VPM2, 1);
         }
-#endif
     };
 
     // ---- the tile pipeline: tile t in buffer t % NB, loads issued NB - 1 tiles ahead ----
@@ -710,7 +696,7 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     const float* __restrict__ wq, const uint32_t* __restrict__ kmax, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, int Tq, int Nc, long long L, int m,
     long long pos0, int topk, int nsplit, int caps, int R, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
-    uint32_t* __restrict__ fail)
+    float* __restrict__ score_out, uint32_t* __restrict__ fail)
 {
     __shared__ uint32_t hist_all[SW_ROWS][1024];
     __shared__ unsigned long long bkey_all[SW_ROWS][SW_BAND];
@@ -727,8 +713,11 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
     const int b = r / Tq, t = r % Tq;
     const int nv = n_visible(pos0 + t, L, m, Nc);
     int32_t* out = idx_out + (size_t)r * topk;
-    if (nv <= topk) {                                 // every visible entry is selected
-        for (int i = lane; i < topk; i += 64) out[i] = i < nv ? i : -1;
+    if (nv <= topk) {                                 // every visible entry is selected (no score is formed)
+        for (int i = lane; i < topk; i += 64) {
+            out[i] = i < nv ? i : -1;
+            if (score_out) score_out[(size_t)r * topk + i] = __builtin_nanf("");
+        }
         if (cnt_out && lane == 0) cnt_out[r] = nv;
         return;
     }
@@ -863,7 +852,7 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
         }
     }
     const float tau = key_f32(base);
-    const double D = (double)wq[r] * (double)__uint_as_float(kmax[b]) * 7.62939453125e-06 * (1.0 + 1.0 / 512) +
+    const double D = (double)wq[r] * (double)__uint_as_float(kmax[b]) * 1.52587890625e-05 * (1.0 + 1.0 / 512) +
                      1.1754943508222875e-38;
     const double lo = (double)tau - 2.0 * D, hi = (double)tau + 2.0 * D;
     if (!((double)thr[r] <= lo)) { give_up(); return; }       // the list might miss band entries
@@ -956,7 +945,14 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
             const bool sel = (cid[k] >> 31) || (((cid[k] >> 30) & 1u) && ((cw >> (lane & 31)) & 1u));
             const unsigned long long ms = __builtin_amdgcn_ballot_w64(sel);
             const uint32_t pos = o + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
-            if (sel && pos < (uint32_t)topk) out[pos] = (int32_t)(cid[k] & 0x3fffffffu);
+            if (sel && pos < (uint32_t)topk) {
+                out[pos] = (int32_t)(cid[k] & 0x3fffffffu);
+                if (score_out) {                      // the approximate score it was ranked by, from the list
+                    const uint32_t so = (uint32_t)__builtin_amdgcn_readlane((int)soff, k);
+                    score_out[(size_t)r * topk + pos] =
+                        __uint_as_float(cand[(size_t)r * nsplit * caps + so + (uint32_t)lane].y);
+                }
+            }
             o += (uint32_t)__popcll(ms);
         }
     }
@@ -1013,7 +1009,8 @@ __device__ __forceinline__ void fb_score_entries(int r, int b, int nv, int s0, i
 // then every entry above tau and the lowest-indexed entries equal to tau, ascending.
 // Thread t owns the contiguous entries [t per, (t + 1) per), per a multiple of 64, read
 // 64 at a time with 16-byte loads (K holds a multiple of 64 keys).
-__device__ __forceinline__ void fb_select_row(const uint32_t* K, int nv, int topk, int32_t* out, uint32_t* h, uint32_t* red) {
+__device__ __forceinline__ void fb_select_row(const uint32_t* K, int nv, int topk, int32_t* out, float* sout, uint32_t* h,
+                                              uint32_t* red) {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int per = ((nv + FB_TPB - 1) / FB_TPB + 63) & ~63;
     const int s0 = min(nv, tid * per), s1 = min(nv, s0 + per);
@@ -1085,7 +1082,10 @@ __device__ __forceinline__ void fb_select_row(const uint32_t* K, int nv, int top
     uint32_t e = eq0;
     for_keys([&](int s, uint32_t x) {
         const bool sel = x > base || (x == base && (e++) < need);
-        if (sel && o < (uint32_t)topk) out[o++] = s;
+        if (sel && o < (uint32_t)topk) {
+            if (sout) sout[o] = key_f32(x);           // the exact score
+            out[o++] = s;
+        }
     });
 }
 
@@ -1105,7 +1105,8 @@ __global__ __launch_bounds__(256) void k_pfb_score(
 
 __global__ __launch_bounds__(FB_TPB) void k_pfb_select(
     const uint32_t* __restrict__ fail, int Tq, int Nc, long long L, int m, long long pos0, int topk,
-    const uint32_t* __restrict__ keys, size_t NcP, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
+    const uint32_t* __restrict__ keys, size_t NcP, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
+    float* __restrict__ score_out)
 {
     __shared__ __align__(16) uint32_t h[1024];
     __shared__ uint32_t red[2 * (FB_TPB / 64)];
@@ -1113,14 +1114,16 @@ __global__ __launch_bounds__(FB_TPB) void k_pfb_select(
     if (fi >= min(fail[0], (uint32_t)FB_SLOTS)) return;
     const int r = (int)fail[1 + fi], t = r % Tq;
     const int nv = n_visible(pos0 + t, L, m, Nc);
-    fb_select_row(keys + (size_t)fi * NcP, nv, topk, idx_out + (size_t)r * topk, h, red);
+    fb_select_row(keys + (size_t)fi * NcP, nv, topk, idx_out + (size_t)r * topk,
+                  score_out ? score_out + (size_t)r * topk : nullptr, h, red);
     if (cnt_out && threadIdx.x == 0) cnt_out[r] = topk;
 }
 
 __global__ __launch_bounds__(FB_TPB) void k_pfallback(
     const uint32_t* __restrict__ fail, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, int Tq, int Nc, long long L, int m, long long pos0, int topk,
-    uint32_t* __restrict__ keys, size_t NcP, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out)
+    uint32_t* __restrict__ keys, size_t NcP, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
+    float* __restrict__ score_out)
 {
     __shared__ __align__(16) uint32_t h[1024];
     __shared__ uint32_t red[2 * (FB_TPB / 64)];
@@ -1133,7 +1136,8 @@ __global__ __launch_bounds__(FB_TPB) void k_pfallback(
         fb_score_entries(r, b, nv, wave, FB_TPB / 64, q_idx, w_idx, k_idx, Nc, K);
         __threadfence_block();
         __syncthreads();
-        fb_select_row(K, nv, topk, idx_out + (size_t)r * topk, h, red);
+        fb_select_row(K, nv, topk, idx_out + (size_t)r * topk, score_out ? score_out + (size_t)r * topk : nullptr,
+                      h, red);
         if (cnt_out && threadIdx.x == 0) cnt_out[r] = topk;
         __syncthreads();                               // K is reused by the next row
     }
@@ -1166,7 +1170,7 @@ static PrefillPlan prefill_plan(int B, int Tq, int Nc) {
     P.nqb = (Tq + P_QPG - 1) / P_QPG;
     auto splits = [&](int nks, int& nsplit, int& span) {
         const int units = B * P.nqb;
-        int ns = (CSA_PF_UNITS + units - 1) / units;
+        int ns = (P_UNITS + units - 1) / units;
         ns = std::max(1, std::min(ns, MAX_SPLIT));
         ns = std::min(ns, std::max(1, (nks + 1023) / 1024));
         span = ((nks + ns - 1) / ns + P_TK - 1) / P_TK * P_TK;
@@ -1199,8 +1203,8 @@ size_t prefill_index_ws_bytes(int B, int Tq, int Nc) {
 }
 
 int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_idx, int B, int Tq, int Nc,
-                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out, void* ws,
-                         hipStream_t st) {
+                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
+                         float* score_out, void* ws, hipStream_t st) {
     const PrefillPlan P = prefill_plan(B, Tq, Nc);
     char* p = (char*)ws;
     uint32_t* kmax = (uint32_t*)p;          p += align256((size_t)B * 4);
@@ -1232,13 +1236,13 @@ int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_id
     CSA_LAUNCH("k_pscore", k_pscore<1>, dim3((unsigned)(B * P.nqb * P.nsplit1)), dim3(P_TPB), 0, st, A);
     CSA_LAUNCH("k_pselect", k_pselect, dim3((unsigned)((P.R + SW_ROWS - 1) / SW_ROWS)), dim3(64 * SW_ROWS), 0, st, cand,
                cnt, thr, wq, kmax, q, w_idx, k, Tq, Nc, L, m, pos0, topk, P.nsplit1, P.caps, (int)P.R, idx_out, cnt_out,
-               fail);
+               score_out, fail);
     CSA_LAUNCH("k_pfb_score", k_pfb_score, dim3(FB_CH), dim3(256), 0, st, fail, q, w_idx, k, Tq, Nc, L, m, pos0, fbk,
                P.NcP);
     CSA_LAUNCH("k_pfb_select", k_pfb_select, dim3(FB_SLOTS), dim3(FB_TPB), 0, st, fail, Tq, Nc, L, m, pos0, topk, fbk,
-               P.NcP, idx_out, cnt_out);
+               P.NcP, idx_out, cnt_out, score_out);
     CSA_LAUNCH("k_pfallback", k_pfallback, dim3(FB_SLOTS), dim3(FB_TPB), 0, st, fail, q, w_idx, k, Tq, Nc, L, m,
-               pos0, topk, fbk, P.NcP, idx_out, cnt_out);
+               pos0, topk, fbk, P.NcP, idx_out, cnt_out, score_out);
     return 0;
 }
 

@@ -198,3 +198,27 @@ def parallel_bits_to_device(seed, name, shape, scale, dtype, device, workers=8, 
             s = starts[ci]
             out[s:s + t.numel()].copy_(t)
     return out.view(*shape)
+
+
+def indexer_inputs_to_device(seed, B, Tq, HI, dI, Nc, dtype, device, planted=0, planted_rho=4.0):
+    """Indexer inputs of the large batched workloads: q_idx and w_idx as in indexer_inputs (host streams,
+    returned as numpy bits and float32), k_idx generated on the device by parallel_bits_to_device.
+    planted > 0: per sequence, `planted` distinct seeded entries get the planted key of indexer_inputs
+    (aligned with the head-weighted sum of the sequence's first query, planted_rho times a typical key
+    norm, plus small noise), written over the generated rows.  Returns (q_bits, w, k_device, planted_idx)."""
+    s = 1.0 / np.sqrt(dI)
+    qf = normal_f32(seed, "q_idx", (B, Tq, HI, dI), s)
+    w = half_normal_f32(seed, "w_idx", (B, Tq, HI), 1.0 / np.sqrt(HI)).astype(np.float32)
+    k = parallel_bits_to_device(seed, "k_idx", (B, Nc, dI), s, dtype, device)
+    planted_idx = None
+    if planted:
+        g = rng(seed, "planted")
+        planted_idx = np.stack([np.sort(g.choice(Nc, size=planted, replace=False)) for _ in range(B)])
+        for b in range(B):
+            u = (w[b, 0][:, None] * qf[b, 0]).sum(0)
+            u = u / np.linalg.norm(u)
+            noise = g.standard_normal((planted, dI)).astype(np.float32) * np.float32(0.05 * s)
+            rows = encode((planted_rho * u)[None, :] + noise, dtype)
+            rows_t = torch.from_numpy(rows.view(np.int16) if dtype == 0 else rows).to(device)
+            k[b, torch.from_numpy(planted_idx[b].astype(np.int64)).to(device)] = rows_t
+    return encode(qf, dtype), w, k, planted_idx

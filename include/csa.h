@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum {
     CSA_OK = 0,
@@ -135,6 +135,13 @@ int csa_hca_compress(const void* hidden, int B, long long L, int Dh,
  *   idx_out [B][Tq][topk] int32: selected entry indices in ascending order,
  *           padded with -1 after cnt entries
  *   cnt_out [B][Tq] int32 or NULL: min(topk, n_visible)
+ *   score_out [B][Tq][topk] fp32 or NULL: for each returned index, the score
+ *           the GPU ranked it by -- the MFMA-path approximate score S~, which
+ *           satisfies |S~ - S| <= the certified bound of that entry (entries
+ *           whose order was settled on exact scores keep their S~ here too),
+ *           or the exact S for rows the exact fallback selected; NaN in the
+ *           padding slots and in rows with at most topk visible entries (those
+ *           are selected whole, without scoring)
  * Supported: dtype in {CSA_BF16, CSA_E4M3}; HI in {1,2,4,8,16}; dI in {64,128};
  * 1 <= topk <= 4096; 1 <= Tq <= 65536; Nc <= 2^24; pos0 >= 0.
  * Workspace: csa_index_topk_ws_bytes with the call's sizes (the many-query path
@@ -144,7 +151,7 @@ int csa_hca_compress(const void* hidden, int B, long long L, int Dh,
 size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype);
 int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype,
                    int B, int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0,
-                   int topk, int32_t* idx_out, int32_t* cnt_out,
+                   int topk, int32_t* idx_out, int32_t* cnt_out, float* score_out,
                    void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(b):
 
 
 def test_version_and_status_strings(b):
-    assert b.lib.csa_abi_version() == 2
+    assert b.lib.csa_abi_version() == 3
     assert b.lib.csa_status_str(CSA_ERR_WORKSPACE) == b"CSA_ERR_WORKSPACE"
     assert b.lib.csa_status_str(99) == b"CSA_ERR_UNKNOWN"
 
@@ -72,13 +72,13 @@ def test_index_topk_validation_codes(b):
     lib = b.lib
     f = lib.csa_index_topk
     good = dict(q=A16, w=A16, k=A16, dt=0, B=1, Tq=1, HI=8, dI=128, Nc=1024, L=4096, m=4, pos0=4095, topk=64,
-                idx=A16, cnt=None, ws=A16, wsb=10 ** 9)
+                idx=A16, cnt=None, score=None, ws=A16, wsb=10 ** 9)
 
     def call(**kw):
         a = dict(good)
         a.update(kw)
         return f(a["q"], a["w"], a["k"], a["dt"], a["B"], a["Tq"], a["HI"], a["dI"], a["Nc"], a["L"], a["m"],
-                 a["pos0"], a["topk"], a["idx"], a["cnt"], a["ws"], a["wsb"], None)
+                 a["pos0"], a["topk"], a["idx"], a["cnt"], a["score"], a["ws"], a["wsb"], None)
 
     assert call(q=None) == CSA_ERR_NULL
     assert call(k=BAD) == CSA_ERR_ALIGN
@@ -92,6 +92,7 @@ def test_index_topk_validation_codes(b):
     assert call(wsb=10) == CSA_ERR_WORKSPACE
     assert b"workspace" in lib.csa_last_error()
     assert call(ws=None) == CSA_ERR_NULL
+    assert call(score=BAD) == CSA_ERR_ALIGN
 
 
 def test_attention_validation_codes(b):
