@@ -40,6 +40,7 @@ def _load():
         "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, Z, P], I),
         "csa_sparse_attn_ws_bytes": ([I, I, I, I, I, I], Z),
         "csa_sparse_attn": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P, Z, P], I),
+        "csa_sparse_attn_noalloc": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P], I),
         "hca_dense_attn_ws_bytes": ([I, I, I, I, I], Z),
         "hca_dense_attn": ([P, P, I, I, I, I, I, LL, I, LL, F, P, P, P, P, Z, P], I),
         "csa_hca_decode_ws_bytes": ([P], Z),
@@ -63,6 +64,7 @@ lib = _load()
 EXPORTED = ("csa_abi_version", "csa_status_str", "csa_last_error", "csa_compress_ws_bytes", "csa_compress",
             "csa_hca_compress_ws_bytes", "csa_hca_compress",
             "csa_index_topk_ws_bytes", "csa_index_topk", "csa_sparse_attn_ws_bytes", "csa_sparse_attn",
+            "csa_sparse_attn_noalloc",
             "hca_dense_attn_ws_bytes", "hca_dense_attn", "csa_hca_decode_ws_bytes", "csa_hca_decode",
             "csa_rope", "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read",
             "csa_prof_only")
@@ -167,6 +169,17 @@ def csa_sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: flo
     _check(lib.csa_sparse_attn(_p(q), _p(kv), _p(idx), _p(kv_raw), B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W,
                                float(scale), _sink(sink, H), _p(out), _p(lse_out), _p(ws),
                                0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def csa_sparse_attn_noalloc(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, out, lse_out=None,
+                            stream=None, sink=None):
+    """csa_sparse_attn with the split partials in the library's static scratch (no workspace, no allocation)."""
+    B, Tq, H, D = q.shape
+    Nc = kv.shape[1] if kv is not None else 0
+    topk = idx.shape[-1] if idx is not None else 0
+    Lr = kv_raw.shape[1] if kv_raw is not None else 0
+    _check(lib.csa_sparse_attn_noalloc(_p(q), _p(kv), _p(idx), _p(kv_raw), B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W,
+                                       float(scale), _sink(sink, H), _p(out), _p(lse_out), _stream(stream)))
 
 
 def hca_dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, out, lse_out=None, ws=None, stream=None,

@@ -76,6 +76,40 @@ void prof_end(void* token, hipStream_t s) {
 using csa_host::fail;
 
 // ---------------------------------------------------------------------------
+// scratch of the no-allocation entry point (csa_sparse_attn_noalloc)
+// ---------------------------------------------------------------------------
+// One file-scope device array per GPU, loaded with the library's code object and held until the process
+// ends.  Host code never passes `scratch` itself to a kernel (in host code the name is a host-side stand-in,
+// not a device address): the device address is looked up once per device with hipGetSymbolAddress, with
+// that device current, and kept below.
+static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+namespace csa_host {
+constexpr int MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[MAX_DEVICES];
+
+// The current device's copy of `scratch` (looked up on the first call on each device).
+static int scratch_ptr(const char* fn, void** out) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CSA_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(CSA_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (r != hipSuccess || !p)
+            return fail(CSA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+                        hipGetErrorString(r));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CSA_OK;
+}
+}  // namespace csa_host
+
+// ---------------------------------------------------------------------------
 // helpers
 // ---------------------------------------------------------------------------
 namespace {
@@ -311,6 +345,28 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
     if (rc) return rc;
     csa_host::AttnRows r{1, kv, Nc, 0, 1, idx, topk, kv_raw, Lr, raw0, W, sink};
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
+                                 "k_attn_sparse");
+}
+
+// As csa_sparse_attn, with the split partials in the library's static scratch instead of a workspace.
+int csa_sparse_attn_noalloc(const void* q, const void* kv, const int32_t* idx, const void* kv_raw, int B, int Tq,
+                            int H, int D, int Nc, int topk, int Lr, long long raw0, long long pos0, int W, float scale,
+                            const float* sink, void* out, float* lse_out, void* stream) {
+    const char* fn = "csa_sparse_attn_noalloc";
+    csa_host::g_err[0] = 0;
+    int rc = validate_sparse(fn, q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse_out);
+    if (rc) return rc;
+    const size_t need = csa_host::attn_ws_bytes(B, Tq, H, D, 1, topk, W);
+    REQ(need <= (size_t)CSA_NOALLOC_SCRATCH_BYTES, CSA_ERR_UNSUPPORTED,
+        "%s: this call needs %zu bytes of scratch, beyond the static %llu (use csa_sparse_attn with a workspace)", fn,
+        need, (unsigned long long)CSA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need) {
+        rc = csa_host::scratch_ptr(fn, &ws);
+        if (rc) return rc;
+    }
+    csa_host::AttnRows r{1, kv, Nc, 0, 1, idx, topk, kv_raw, Lr, raw0, W, sink};
+    return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, need, (hipStream_t)stream,
                                  "k_attn_sparse");
 }
 

@@ -181,6 +181,25 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
                     long long pos0, int W, float scale, const float* sink, void* out, float* lse_out,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* No-allocation variant of csa_sparse_attn, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments and results as csa_sparse_attn
+ * (bitwise: the same kernels and split plan), minus the workspace.  The split
+ * partials live in a static device array of CSA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; its device
+ * address is looked up once per device (the current device; `stream` must
+ * belong to it).  The call allocates nothing.  A call whose partials need more
+ * than CSA_NOALLOC_SCRATCH_BYTES (csa_sparse_attn_ws_bytes of the same sizes)
+ * returns CSA_ERR_UNSUPPORTED and enqueues nothing.  All calls on one GPU share
+ * the one array: calls that overlap in time on one GPU (different streams,
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe (every call rewrites the partials it reads). */
+#define CSA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int csa_sparse_attn_noalloc(const void* q, const void* kv, const int32_t* idx, const void* kv_raw,
+                            int B, int Tq, int H, int D, int Nc, int topk, int Lr, long long raw0,
+                            long long pos0, int W, float scale, const float* sink, void* out, float* lse_out,
+                            void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* A5. HCA attention: dense MQA over every visible compressed entry          */
 /*     ([P1] 1.1; [P2] first section; [P3] item 2)                           */
