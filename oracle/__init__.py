@@ -79,9 +79,9 @@ def _load():
         lib.ora_index_scores.restype = None
         lib.ora_topk.argtypes = [I, I, I, P, P, P, P]
         lib.ora_topk.restype = None
-        lib.ora_sparse_attn.argtypes = [I, I, I, I, I, I, I, LL, LL, I, D, P, P, P, P, P, P, P]
+        lib.ora_sparse_attn.argtypes = [I, I, I, I, I, I, I, LL, LL, I, D, P, P, P, P, P, P, P, P, P]
         lib.ora_sparse_attn.restype = I
-        lib.ora_dense_attn.argtypes = [I, I, I, I, I, LL, I, LL, D, P, P, P, P, P]
+        lib.ora_dense_attn.argtypes = [I, I, I, I, I, LL, I, LL, D, P, P, P, P, P, P]
         lib.ora_dense_attn.restype = None
         lib.ora_rope.argtypes = [I, I, I, I, D, I, P, P, P]
         lib.ora_rope.restype = None
@@ -204,9 +204,10 @@ def _sink(sink, H):
     return s
 
 
-def sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, sink=None):
+def sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, sink=None, v=None, v_raw=None):
     """CSA attention over selected entries + raw window; returns (out, lse) fp64.  sink: optional
-    per-head attention-sink logits [H] (an extra denominator term with no value row)."""
+    per-head attention-sink logits [H] (an extra denominator term with no value row).  v, v_raw: optional
+    separate values of the entries and the raw rows (both or neither; default: each row is its own value)."""
     lib = _load()
     q, pq = _c(q, np.uint16)
     kv, pk = _c(kv, np.uint16)
@@ -221,15 +222,24 @@ def sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, 
     out = np.empty((B, Tq, H, D), np.float64)
     lse = np.empty((B, Tq, H), np.float64)
     sk = _sink(sink, H)
+    if (v is None) != (v_raw is None):
+        raise ValueError("sparse_attn: give both v and v_raw or neither")
+    pv = pvr = None
+    if v is not None:
+        v, pv = _c(v, np.uint16)
+        v_raw, pvr = _c(v_raw, np.uint16)
+        if v.shape != kv.shape or v_raw.shape != kr.shape:
+            raise ValueError("sparse_attn: values must have the keys' shapes")
     rc = lib.ora_sparse_attn(B, Tq, H, D, Nc, topk_, Lr, raw0, pos0, W, float(scale),
-                             pq, pk, pi, pr, _ptr(sk), _ptr(out), _ptr(lse))
+                             pq, pk, pi, pr, pv, pvr, _ptr(sk), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle sparse_attn: index or window outside the given rows")
     return out, lse
 
 
-def dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, sink=None):
-    """HCA attention over all visible compressed entries; returns (out, lse) fp64 (sink as above)."""
+def dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, sink=None, v_h=None):
+    """HCA attention over all visible compressed entries; returns (out, lse) fp64 (sink as above; v_h:
+    optional separate values of the entries)."""
     lib = _load()
     q, pq = _c(q, np.uint16)
     kv, pk = _c(kv_h, np.uint16)
@@ -238,7 +248,12 @@ def dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, sink=None):
     out = np.empty((B, Tq, H, D), np.float64)
     lse = np.empty((B, Tq, H), np.float64)
     sk = _sink(sink, H)
-    lib.ora_dense_attn(B, Tq, H, D, Nh, L, mh, pos0, float(scale), pq, pk, _ptr(sk), _ptr(out), _ptr(lse))
+    pv = None
+    if v_h is not None:
+        v_h, pv = _c(v_h, np.uint16)
+        if v_h.shape != kv.shape:
+            raise ValueError("dense_attn: values must have the keys' shape")
+    lib.ora_dense_attn(B, Tq, H, D, Nh, L, mh, pos0, float(scale), pq, pk, pv, _ptr(sk), _ptr(out), _ptr(lse))
     return out, lse
 
 

@@ -426,8 +426,9 @@ void ora_topk(int rows, int Nc, int k, const float* S, const int* n_vis, int* id
 /* One softmax per head over the rows' logits l_r = scale (q_h . x_r) and, when sink is given, the head's
  * attention-sink logit sink[h] (a term of the denominator with no value row): [P1 section 1.1] gives
  * every query head a learnable sink logit that lets it send its total attention towards 0.
- * out_h = sum_r e^{l_r} x_r / (e^{sink_h} + sum_r e^{l_r}),  lse_h = log(e^{sink_h} + sum_r e^{l_r}). */
-static void ora_attend(const uint16_t* q, int H, int D, const uint16_t** rows, int nr,
+ * out_h = sum_r e^{l_r} y_r / (e^{sink_h} + sum_r e^{l_r}),  lse_h = log(e^{sink_h} + sum_r e^{l_r}),
+ * where y_r = vals[r] when vals is given (separate values) and y_r = x_r otherwise. */
+static void ora_attend(const uint16_t* q, int H, int D, const uint16_t** rows, const uint16_t** vals, int nr,
                        double scale, const double* sink, double* out, double* lse)
 {
     int h, r, d;
@@ -445,9 +446,11 @@ static void ora_attend(const uint16_t* q, int H, int D, const uint16_t** rows, i
         if (mx == -INFINITY) { lse[h] = -INFINITY; continue; }     /* no row and no sink */
         for (r = 0; r < nr; ++r) { l[r] = exp(l[r] - mx); s += l[r]; }
         if (sink) s += exp(sink[h] - mx);
-        for (r = 0; r < nr; ++r)
+        for (r = 0; r < nr; ++r) {
+            const uint16_t* y = vals ? vals[r] : rows[r];
             for (d = 0; d < D; ++d)
-                out[(size_t)h * D + d] += l[r] * ora_bf16_value(rows[r][d]);
+                out[(size_t)h * D + d] += l[r] * ora_bf16_value(y[d]);
+        }
         for (d = 0; d < D; ++d) out[(size_t)h * D + d] /= s;
         lse[h] = mx + log(s);
     }
@@ -462,10 +465,13 @@ static void ora_attend(const uint16_t* q, int H, int D, const uint16_t** rows, i
  * [max(0, p-W+1), p] (the current token included, no de-duplication).
  * q[B][Tq][H][D], kv[B][Nc][D], idx[B][Tq][topk] (-1 = unused),
  * kv_raw[B][Lr][D] holds raw positions raw0..raw0+Lr-1.
+ * v[B][Nc][D] and v_raw[B][Lr][D], when given (both or neither), are separate values of the entries and raw
+ * rows (the variant that keeps keys and values apart; NULL: each row is its own value).
  * out[B][Tq][H][D], lse[B][Tq][H].  Returns -1 on an out-of-range index. */
 int ora_sparse_attn(int B, int Tq, int H, int D, int Nc, int topk, int Lr, long long raw0,
                     long long pos0, int W, double scale,
                     const uint16_t* q, const uint16_t* kv, const int* idx, const uint16_t* kv_raw,
+                    const uint16_t* v, const uint16_t* v_raw,
                     const double* sink, double* out, double* lse)
 {
     int bt, bad = 0;
@@ -474,19 +480,23 @@ int ora_sparse_attn(int B, int Tq, int H, int D, int Nc, int topk, int Lr, long 
         int b = bt / Tq, t = bt % Tq, i, nr = 0;
         long long p = pos0 + t, u, w0 = p - W + 1 < 0 ? 0 : p - W + 1;
         const uint16_t** rows = (const uint16_t**)malloc(sizeof(void*) * (topk + W + 1));
+        const uint16_t** vals = (const uint16_t**)malloc(sizeof(void*) * (topk + W + 1));
         for (i = 0; i < topk; ++i) {
             int j = idx[(size_t)bt * topk + i];
             if (j < 0) continue;
             if (j >= Nc) { bad = 1; continue; }
-            rows[nr++] = kv + ((size_t)b * Nc + j) * D;
+            rows[nr] = kv + ((size_t)b * Nc + j) * D;
+            vals[nr++] = v ? v + ((size_t)b * Nc + j) * D : NULL;
         }
         for (u = w0; W > 0 && u <= p; ++u) {
             if (u < raw0 || u >= raw0 + Lr) { bad = 1; continue; }
-            rows[nr++] = kv_raw + ((size_t)b * Lr + (size_t)(u - raw0)) * D;
+            rows[nr] = kv_raw + ((size_t)b * Lr + (size_t)(u - raw0)) * D;
+            vals[nr++] = v_raw ? v_raw + ((size_t)b * Lr + (size_t)(u - raw0)) * D : NULL;
         }
-        ora_attend(q + (size_t)bt * H * D, H, D, rows, nr, scale, sink,
+        ora_attend(q + (size_t)bt * H * D, H, D, rows, v ? vals : NULL, nr, scale, sink,
                    out + (size_t)bt * H * D, lse + (size_t)bt * H);
         free(rows);
+        free(vals);
     }
     return bad ? -1 : 0;
 }
@@ -494,9 +504,9 @@ int ora_sparse_attn(int B, int Tq, int H, int D, int Nc, int topk, int Lr, long 
 /* A5: HCA attention.  [P1 section 1.1], [P3 item 2]: every m' tokens become
  * one entry and attention is dense over all compressed entries, with no
  * selection.  Reading taken: no sliding window in HCA.  Entries visible to the
- * query at p as defined above.  q[B][Tq][H][D], kv_h[B][Nh][D]. */
+ * query at p as defined above.  q[B][Tq][H][D], kv_h[B][Nh][D]; v_h[B][Nh][D] separate values or NULL. */
 void ora_dense_attn(int B, int Tq, int H, int D, int Nh, long long L, int mh, long long pos0,
-                    double scale, const uint16_t* q, const uint16_t* kv_h, const double* sink,
+                    double scale, const uint16_t* q, const uint16_t* kv_h, const uint16_t* v_h, const double* sink,
                     double* out, double* lse)
 {
     int bt;
@@ -505,11 +515,16 @@ void ora_dense_attn(int B, int Tq, int H, int D, int Nh, long long L, int mh, lo
         int b = bt / Tq, t = bt % Tq, j;
         int nv = ora_n_visible(pos0 + t, L, mh);
         const uint16_t** rows = (const uint16_t**)malloc(sizeof(void*) * (nv > 0 ? nv : 1));
+        const uint16_t** vals = (const uint16_t**)malloc(sizeof(void*) * (nv > 0 ? nv : 1));
         if (nv > Nh) nv = Nh;
-        for (j = 0; j < nv; ++j) rows[j] = kv_h + ((size_t)b * Nh + j) * D;
-        ora_attend(q + (size_t)bt * H * D, H, D, rows, nv, scale, sink,
+        for (j = 0; j < nv; ++j) {
+            rows[j] = kv_h + ((size_t)b * Nh + j) * D;
+            vals[j] = v_h ? v_h + ((size_t)b * Nh + j) * D : NULL;
+        }
+        ora_attend(q + (size_t)bt * H * D, H, D, rows, v_h ? vals : NULL, nv, scale, sink,
                    out + (size_t)bt * H * D, lse + (size_t)bt * H);
         free(rows);
+        free(vals);
     }
 }
 

@@ -589,3 +589,62 @@ def test_rope_group_maps_rows_to_positions():
     assert np.array_equal(a, b)
     with pytest.raises(ValueError):
         oracle.rope(x, pos, group=5)
+
+
+# ---------------------------------------------------------------------------
+# separate keys and values (the variant that keeps them apart)
+# ---------------------------------------------------------------------------
+
+def test_separate_values_match_library_attention():
+    # sparse: selected entries + window, values from their own arrays; the library's SDPA (fp64, CPU) over
+    # the gathered key and value rows gives the same result
+    B, Tq, H, D, Nc, W, Lr = 2, 2, 16, 32, 30, 5, 9
+    q, kv = synth.attn_inputs(40, B, Tq, H, D, Nc, "sk_")
+    _, v = synth.attn_inputs(41, B, Tq, H, D, Nc, "sv_")
+    _, raw = synth.attn_inputs(42, B, Tq, H, D, Lr, "rk_")
+    _, vraw = synth.attn_inputs(43, B, Tq, H, D, Lr, "rv_")
+    idx = np.array([[[1, 4, 9, 22, -1], [0, 7, 8, 29, 3]]] * B, np.int32)
+    raw0, pos0 = 100, 106
+    out, lse = oracle.sparse_attn(q, kv, idx, raw, raw0=raw0, pos0=pos0, W=W, scale=0.7, v=v, v_raw=vraw)
+    for b in range(B):
+        for t in range(Tq):
+            p = pos0 + t
+            sel = [j for j in idx[b, t] if j >= 0]
+            win = list(range(max(0, p - W + 1) - raw0, p - raw0 + 1))
+            K = np.concatenate([_bf16_f64(kv[b, sel]), _bf16_f64(raw[b, win])])
+            V = np.concatenate([_bf16_f64(v[b, sel]), _bf16_f64(vraw[b, win])])
+            Q = torch.from_numpy(_bf16_f64(q[b, t]))[:, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                Q, torch.from_numpy(K)[None].expand(H, -1, -1), torch.from_numpy(V)[None].expand(H, -1, -1), scale=0.7)
+            np.testing.assert_allclose(out[b, t], ref[:, 0].numpy(), rtol=1e-10, atol=1e-13)
+            lg = 0.7 * _bf16_f64(q[b, t]) @ K.T
+            np.testing.assert_allclose(lse[b, t], np.log(np.exp(lg).sum(1)), rtol=1e-12)
+    # dense: every visible entry with its own value
+    out_d, _ = oracle.dense_attn(q, kv, L=Nc * 4, mh=4, pos0=Nc * 4 - Tq, scale=0.7, v_h=v)
+    for b in range(B):
+        K, V = _bf16_f64(kv[b]), _bf16_f64(v[b])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(_bf16_f64(q[b, -1]))[:, None, :], torch.from_numpy(K)[None].expand(H, -1, -1),
+            torch.from_numpy(V)[None].expand(H, -1, -1), scale=0.7)
+        np.testing.assert_allclose(out_d[b, -1], ref[:, 0].numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_separate_values_single_row_and_linearity():
+    B, Tq, H, D = 1, 1, 16, 32
+    q, kv = synth.attn_inputs(44, B, Tq, H, D, 6, "lk_")
+    _, v1 = synth.attn_inputs(45, B, Tq, H, D, 6, "lv1_")
+    _, v2 = synth.attn_inputs(46, B, Tq, H, D, 6, "lv2_")
+    # one visible entry: the output is that entry's value, not its key
+    out, _ = oracle.dense_attn(q, kv[:, :1], L=4, mh=4, pos0=3, scale=0.3, v_h=v1[:, :1])
+    np.testing.assert_array_equal(out[0, 0], np.broadcast_to(_bf16_f64(v1[0, 0]), (H, D)))
+    # the output is linear in the values: out(v1) + out(v2) = out over value rows v1 + v2
+    a, _ = oracle.dense_attn(q, kv, L=24, mh=4, pos0=23, scale=0.3, v_h=v1)
+    c, _ = oracle.dense_attn(q, kv, L=24, mh=4, pos0=23, scale=0.3, v_h=v2)
+    s = _bf16_f64(v1) + _bf16_f64(v2)
+    w = np.exp(0.3 * _bf16_f64(q[0, 0]) @ _bf16_f64(kv[0]).T)
+    w /= w.sum(1, keepdims=True)
+    np.testing.assert_allclose(a[0, 0] + c[0, 0], w @ s[0], rtol=1e-12, atol=1e-15)
+    # values equal to the keys reproduce the shared-row result exactly
+    same, _ = oracle.dense_attn(q, kv, L=24, mh=4, pos0=23, scale=0.3, v_h=kv)
+    base, _ = oracle.dense_attn(q, kv, L=24, mh=4, pos0=23, scale=0.3)
+    np.testing.assert_array_equal(same, base)
