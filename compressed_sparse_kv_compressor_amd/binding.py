@@ -38,6 +38,10 @@ def _load():
         "csa_hca_compress": ([P, I, LL, I, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, I, P, P, Z, P], I),
         "csa_index_topk_ws_bytes": ([I, I, I, I, I, I, I], Z),
         "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, Z, P], I),
+        "csa_index_topk_ex_ws_bytes": ([I, I, I, I, I, I, I, P], Z),
+        "csa_index_topk_ex": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, P, Z, P], I),
+        "csa_sparse_attn_ex": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P, P, Z, P], I),
+        "hca_dense_attn_ex": ([P, P, P, I, I, I, I, I, LL, I, LL, F, P, P, P, P, P, Z, P], I),
         "csa_sparse_attn_ws_bytes": ([I, I, I, I, I, I], Z),
         "csa_sparse_attn": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P, Z, P], I),
         "csa_sparse_attn_noalloc": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P], I),
@@ -64,10 +68,35 @@ lib = _load()
 EXPORTED = ("csa_abi_version", "csa_status_str", "csa_last_error", "csa_compress_ws_bytes", "csa_compress",
             "csa_hca_compress_ws_bytes", "csa_hca_compress",
             "csa_index_topk_ws_bytes", "csa_index_topk", "csa_sparse_attn_ws_bytes", "csa_sparse_attn",
-            "csa_sparse_attn_noalloc",
+            "csa_sparse_attn_noalloc", "csa_index_topk_ex_ws_bytes", "csa_index_topk_ex", "csa_sparse_attn_ex",
+            "hca_dense_attn_ex",
             "hca_dense_attn_ws_bytes", "hca_dense_attn", "csa_hca_decode_ws_bytes", "csa_hca_decode",
             "csa_rope", "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read",
             "csa_prof_only")
+
+
+class CacheLayout(ctypes.Structure):
+    """Mirror of csa_cache_layout_t (variable-length batch and/or paged caches)."""
+    _fields_ = [("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int),
+                ("num_blocks", ctypes.c_int), ("block_tokens", ctypes.c_int)]
+
+
+def make_layout(seq_lens=None, block_table=None, num_blocks: int = 0, block_tokens: int = 0) -> CacheLayout:
+    """seq_lens: int64 device tensor [B] or None; block_table: int32 device tensor [B][max_blocks] or None."""
+    if seq_lens is not None and (seq_lens.dtype != torch.int64 or not seq_lens.is_contiguous()):
+        raise ValueError("seq_lens must be a contiguous int64 tensor")
+    if block_table is not None and (block_table.dtype != torch.int32 or block_table.dim() != 2
+                                    or not block_table.is_contiguous()):
+        raise ValueError("block_table must be a contiguous int32 [B][max_blocks] tensor")
+    lay = CacheLayout(seq_lens=_p(seq_lens), block_table=_p(block_table),
+                      max_blocks=0 if block_table is None else block_table.shape[1], num_blocks=num_blocks,
+                      block_tokens=block_tokens)
+    lay._keep = (seq_lens, block_table)
+    return lay
+
+
+def _lay(layout):
+    return None if layout is None else ctypes.byref(layout)
 
 
 class DecodeArgs(ctypes.Structure):
@@ -83,6 +112,7 @@ class DecodeArgs(ctypes.Structure):
         ("csa_sink", ctypes.c_void_p),
         ("hca_q", ctypes.c_void_p), ("kv_h", ctypes.c_void_p), ("mh", ctypes.c_int),
         ("hca_out", ctypes.c_void_p), ("hca_lse", ctypes.c_void_p), ("hca_sink", ctypes.c_void_p),
+        ("layout", ctypes.POINTER(CacheLayout)),
     ]
 
 
@@ -139,15 +169,26 @@ def csa_hca_compress(hidden, w_kv, w_ik, w_gate, b_slot, m: int, W: int, kv_out,
 
 
 def csa_index_topk(q_idx, w_idx, k_idx, dtype: int, L: int, m: int, pos0: int, topk: int, idx_out, cnt_out=None,
-                   ws=None, stream=None, score_out=None):
+                   ws=None, stream=None, score_out=None, layout=None, Nc=None):
+    """layout (make_layout): variable-length batch and/or paged keys (k_idx is then the pool and Nc = ceil(L/m)
+    unless given)."""
     B, Tq, HI, dI = q_idx.shape
-    Nc = k_idx.shape[1]
-    need = lib.csa_index_topk_ws_bytes(B, Tq, HI, dI, Nc, topk, dtype)
+    if Nc is None:
+        Nc = k_idx.shape[1] if (layout is None or not layout.block_table) else -(-L // m)
+    if layout is None:
+        need = lib.csa_index_topk_ws_bytes(B, Tq, HI, dI, Nc, topk, dtype)
+    else:
+        need = lib.csa_index_topk_ex_ws_bytes(B, Tq, HI, dI, Nc, topk, dtype, _lay(layout))
     if ws is None:
         ws = workspace(need, q_idx.device)
-    _check(lib.csa_index_topk(_p(q_idx), _p(w_idx), _p(k_idx), dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,
-                              _p(idx_out), _p(cnt_out), _p(score_out), _p(ws), 0 if ws is None else ws.numel(),
-                              _stream(stream)))
+    if layout is None:
+        _check(lib.csa_index_topk(_p(q_idx), _p(w_idx), _p(k_idx), dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,
+                                  _p(idx_out), _p(cnt_out), _p(score_out), _p(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream)))
+    else:
+        _check(lib.csa_index_topk_ex(_p(q_idx), _p(w_idx), _p(k_idx), dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,
+                                     _p(idx_out), _p(cnt_out), _p(score_out), _lay(layout), _p(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def _sink(sink, H: int):
@@ -158,17 +199,25 @@ def _sink(sink, H: int):
 
 
 def csa_sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, out, lse_out=None, ws=None,
-                    stream=None, sink=None):
+                    stream=None, sink=None, v=None, v_raw=None, layout=None, m: int = 1, Nc=None):
+    """v, v_raw: separate values (or None); layout (make_layout): variable-length batch and/or paged entries
+    (kv and v are then pools of ratio m; Nc = the entries per sequence the idx refer to)."""
     B, Tq, H, D = q.shape
-    Nc = kv.shape[1] if kv is not None else 0
+    if Nc is None:
+        Nc = kv.shape[1] if kv is not None else 0
     topk = idx.shape[-1] if idx is not None else 0
     Lr = kv_raw.shape[1] if kv_raw is not None else 0
     need = lib.csa_sparse_attn_ws_bytes(B, Tq, H, D, topk, W)
     if ws is None:
         ws = workspace(need, q.device)
-    _check(lib.csa_sparse_attn(_p(q), _p(kv), _p(idx), _p(kv_raw), B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W,
-                               float(scale), _sink(sink, H), _p(out), _p(lse_out), _p(ws),
-                               0 if ws is None else ws.numel(), _stream(stream)))
+    if layout is None and v is None and v_raw is None:
+        _check(lib.csa_sparse_attn(_p(q), _p(kv), _p(idx), _p(kv_raw), B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W,
+                                   float(scale), _sink(sink, H), _p(out), _p(lse_out), _p(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream)))
+    else:
+        _check(lib.csa_sparse_attn_ex(_p(q), _p(kv), _p(v), _p(idx), _p(kv_raw), _p(v_raw), B, Tq, H, D, Nc, m, topk,
+                                      Lr, raw0, pos0, W, float(scale), _sink(sink, H), _lay(layout), _p(out),
+                                      _p(lse_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def csa_sparse_attn_noalloc(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, out, lse_out=None,
@@ -183,29 +232,37 @@ def csa_sparse_attn_noalloc(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, sc
 
 
 def hca_dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, out, lse_out=None, ws=None, stream=None,
-                   sink=None):
+                   sink=None, v_h=None, layout=None):
+    """v_h: separate values (or None); layout (make_layout): variable-length batch (L = capacity) and/or a
+    paged pool kv_h of ratio mh."""
     B, Tq, H, D = q.shape
-    Nh = kv_h.shape[1]
+    Nh = -(-L // mh) if (layout is not None and layout.block_table) else kv_h.shape[1]
     need = lib.hca_dense_attn_ws_bytes(B, Tq, H, D, Nh)
     if ws is None:
         ws = workspace(need, q.device)
-    _check(lib.hca_dense_attn(_p(q), _p(kv_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale), _sink(sink, H), _p(out),
-                              _p(lse_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    if layout is None and v_h is None:
+        _check(lib.hca_dense_attn(_p(q), _p(kv_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale), _sink(sink, H),
+                                  _p(out), _p(lse_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    else:
+        _check(lib.hca_dense_attn_ex(_p(q), _p(kv_h), _p(v_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale),
+                                     _sink(sink, H), _lay(layout), _p(out), _p(lse_out), _p(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def make_decode_args(*, L, scale, csa_q, q_idx, w_idx, k_idx, kv, kv_raw, idx_dtype, m, topk, W, csa_out,
                      hca_q, kv_h, mh, hca_out, csa_lse=None, hca_lse=None, idx_out=None, csa_sink=None,
-                     hca_sink=None) -> DecodeArgs:
+                     hca_sink=None, layout=None) -> DecodeArgs:
     B, H, D = csa_q.shape[0], csa_q.shape[-2], csa_q.shape[-1]
     HI, dI = q_idx.shape[-2], q_idx.shape[-1]
     args = DecodeArgs(B=B, L=L, H=H, D=D, scale=float(scale), csa_q=_p(csa_q), q_idx=_p(q_idx), w_idx=_p(w_idx),
                       k_idx=_p(k_idx), kv=_p(kv), kv_raw=_p(kv_raw), idx_dtype=idx_dtype, HI=HI, dI=dI, m=m,
                       topk=topk, W=W, csa_out=_p(csa_out), csa_lse=_p(csa_lse), idx_out=_p(idx_out),
                       csa_sink=_sink(csa_sink, H), hca_q=_p(hca_q), kv_h=_p(kv_h), mh=mh, hca_out=_p(hca_out),
-                      hca_lse=_p(hca_lse), hca_sink=_sink(hca_sink, hca_q.shape[-2]))
+                      hca_lse=_p(hca_lse), hca_sink=_sink(hca_sink, hca_q.shape[-2]),
+                      layout=None if layout is None else ctypes.pointer(layout))
     # the struct holds bare device addresses: keep every tensor they point into alive as long as the struct
     args._keep = (csa_q, q_idx, w_idx, k_idx, kv, kv_raw, csa_out, csa_lse, idx_out, csa_sink, hca_q, kv_h, hca_out,
-                  hca_lse, hca_sink)
+                  hca_lse, hca_sink, layout)
     return args
 
 

@@ -160,6 +160,36 @@ int validate_index(const char* fn, const void* q_idx, const float* w_idx, const 
     return CSA_OK;
 }
 
+// Checks an optional batch / cache layout for caches of ratios r1 (N1 entries per sequence) and, if r2 > 0,
+// r2 (N2 entries), and converts it to the launchers' form.
+int read_layout(const char* fn, const csa_cache_layout_t* lay, int r1, int N1, int r2, int N2,
+                csa_host::CacheLayout* out) {
+    *out = csa_host::CacheLayout{nullptr, nullptr, 0, 0, 0};
+    if (!lay) return CSA_OK;
+    if (lay->seq_lens)
+        REQ(((uintptr_t)lay->seq_lens & 7u) == 0, CSA_ERR_ALIGN, "%s: seq_lens is not 8-byte aligned", fn);
+    if (lay->block_table) {
+        REQ(((uintptr_t)lay->block_table & 3u) == 0, CSA_ERR_ALIGN, "%s: block_table is not 4-byte aligned", fn);
+        REQ(lay->max_blocks >= 1 && lay->num_blocks >= 1 && lay->block_tokens >= 1, CSA_ERR_SHAPE,
+            "%s: max_blocks, num_blocks and block_tokens must be >= 1", fn);
+        const int rs[2] = {r1, r2}, ns[2] = {N1, N2};
+        for (int i = 0; i < 2; ++i) {
+            if (rs[i] <= 0) continue;
+            const int epb = lay->block_tokens / rs[i];
+            REQ(lay->block_tokens % rs[i] == 0 && epb >= 1 && (epb & (epb - 1)) == 0, CSA_ERR_UNSUPPORTED,
+                "%s: block_tokens=%d must be a multiple of the ratio %d with a power-of-two quotient", fn,
+                lay->block_tokens, rs[i]);
+            REQ((long long)lay->max_blocks * epb >= ns[i], CSA_ERR_SHAPE,
+                "%s: %d table columns of %d entries cover fewer than the %d entries of the cache", fn,
+                lay->max_blocks, epb, ns[i]);
+            REQ((long long)lay->num_blocks * epb < (1LL << 31), CSA_ERR_UNSUPPORTED, "%s: pool too large", fn);
+        }
+    }
+    *out = csa_host::CacheLayout{lay->seq_lens, lay->block_table, lay->max_blocks, lay->num_blocks,
+                                 lay->block_tokens};
+    return CSA_OK;
+}
+
 int validate_attn_common(const char* fn, const void* q, int B, int Tq, int H, int D, float scale, const void* out,
                          const float* lse) {
     REQ_PTR(q);
@@ -174,7 +204,7 @@ int validate_attn_common(const char* fn, const void* q, int B, int Tq, int H, in
 
 int validate_sparse(const char* fn, const void* q, const void* kv, const int32_t* idx, const void* kv_raw, int B,
                     int Tq, int H, int D, int Nc, int topk, int Lr, long long raw0, long long pos0, int W,
-                    float scale, const void* out, const float* lse) {
+                    float scale, const void* out, const float* lse, bool varlen = false) {
     int rc = validate_attn_common(fn, q, B, Tq, H, D, scale, out, lse);
     if (rc) return rc;
     REQ(topk >= 0 && W >= 0 && pos0 >= 0 && Nc >= 0, CSA_ERR_SHAPE, "%s: topk, W, pos0, Nc must be >= 0", fn);
@@ -185,7 +215,11 @@ int validate_sparse(const char* fn, const void* q, const void* kv, const int32_t
         REQ_PTR(idx);
         REQ(Nc >= 1, CSA_ERR_SHAPE, "%s: Nc must be >= 1 when topk > 0", fn);
     }
-    if (W > 0) {
+    if (W > 0 && varlen) {           // every sequence's raw rows are its last Lr tokens
+        REQ_PTR(kv_raw);
+        REQ((long long)Lr >= (long long)Tq + W - 1, CSA_ERR_SHAPE,
+            "%s: Lr=%d raw rows per sequence cannot hold the windows of %d queries (W=%d)", fn, Lr, Tq, W);
+    } else if (W > 0) {
         REQ_PTR(kv_raw);
         REQ(Lr >= 1, CSA_ERR_SHAPE, "%s: Lr must be >= 1 when W > 0", fn);
         const long long first = pos0 - W + 1 < 0 ? 0 : pos0 - W + 1;
@@ -310,23 +344,48 @@ int csa_hca_compress(const void* hidden, int B, long long L, int Dh, const void*
                                          ws, (hipStream_t)stream);
 }
 
+static bool plain_layout(const csa_cache_layout_t* lay) { return !lay || (!lay->seq_lens && !lay->block_table); }
+
 size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype) {
     if (B < 1 || Tq < 1 || Nc < 1 || HI < 1 || dI < 1 || topk < 1) return 0;
     return csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk);
 }
 
-int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq, int HI, int dI,
-                   int Nc, long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
-                   float* score_out, void* ws, size_t ws_bytes, void* stream) {
-    const char* fn = "csa_index_topk";
+size_t csa_index_topk_ex_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype,
+                                  const csa_cache_layout_t* layout) {
+    if (B < 1 || Tq < 1 || Nc < 1 || HI < 1 || dI < 1 || topk < 1) return 0;
+    return csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk, plain_layout(layout));
+}
+
+static int index_topk_impl(const char* fn, const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B,
+                           int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
+                           int32_t* idx_out, int32_t* cnt_out, float* score_out, const csa_cache_layout_t* layout,
+                           void* ws, size_t ws_bytes, void* stream) {
     csa_host::g_err[0] = 0;
     int rc = validate_index(fn, q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out, cnt_out);
     if (rc) return rc;
     OPT_PTR(score_out);
-    rc = check_ws(fn, ws, ws_bytes, csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk));
+    csa_host::CacheLayout lay;
+    rc = read_layout(fn, layout, m, Nc, 0, 0, &lay);
+    if (rc) return rc;
+    rc = check_ws(fn, ws, ws_bytes, csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk, plain_layout(layout)));
     if (rc) return rc;
     return csa_host::index_topk_launch(q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out,
-                                       cnt_out, score_out, ws, (hipStream_t)stream);
+                                       cnt_out, score_out, lay, ws, (hipStream_t)stream);
+}
+
+int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq, int HI, int dI,
+                   int Nc, long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
+                   float* score_out, void* ws, size_t ws_bytes, void* stream) {
+    return index_topk_impl("csa_index_topk", q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out,
+                           cnt_out, score_out, nullptr, ws, ws_bytes, stream);
+}
+
+int csa_index_topk_ex(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq, int HI,
+                      int dI, int Nc, long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
+                      float* score_out, const csa_cache_layout_t* layout, void* ws, size_t ws_bytes, void* stream) {
+    return index_topk_impl("csa_index_topk_ex", q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,
+                           idx_out, cnt_out, score_out, layout, ws, ws_bytes, stream);
 }
 
 size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W) {
@@ -334,18 +393,46 @@ size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W) {
     return csa_host::attn_ws_bytes(B, Tq, H, D, 1, topk, W);
 }
 
-int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const void* kv_raw, int B, int Tq, int H, int D,
-                    int Nc, int topk, int Lr, long long raw0, long long pos0, int W, float scale, const float* sink,
-                    void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
-    const char* fn = "csa_sparse_attn";
+static int sparse_impl(const char* fn, const void* q, const void* kv, const void* v, const int32_t* idx,
+                       const void* kv_raw, const void* v_raw, int B, int Tq, int H, int D, int Nc, int m, int topk,
+                       int Lr, long long raw0, long long pos0, int W, float scale, const float* sink,
+                       const csa_cache_layout_t* layout, void* out, float* lse_out, void* ws, size_t ws_bytes,
+                       void* stream) {
     csa_host::g_err[0] = 0;
-    int rc = validate_sparse(fn, q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse_out);
+    const bool varlen = layout && layout->seq_lens;
+    int rc = validate_sparse(fn, q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse_out,
+                             varlen);
+    if (rc) return rc;
+    OPT_PTR(v);
+    OPT_PTR(v_raw);
+    csa_host::CacheLayout lay;
+    REQ(m >= 1, CSA_ERR_SHAPE, "%s: m must be >= 1", fn);
+    rc = read_layout(fn, layout, m, Nc, 0, 0, &lay);
     if (rc) return rc;
     rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, 1, topk, W));
     if (rc) return rc;
     csa_host::AttnRows r{1, kv, Nc, 0, 1, idx, topk, kv_raw, Lr, raw0, W, sink};
+    r.seq_lens = lay.seq_lens;
+    r.v = v;
+    r.v_raw = W > 0 ? v_raw : nullptr;
+    r.pm = csa_host::page_map(lay, m);
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
                                  "k_attn_sparse");
+}
+
+int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const void* kv_raw, int B, int Tq, int H, int D,
+                    int Nc, int topk, int Lr, long long raw0, long long pos0, int W, float scale, const float* sink,
+                    void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+    return sparse_impl("csa_sparse_attn", q, kv, nullptr, idx, kv_raw, nullptr, B, Tq, H, D, Nc, 1, topk, Lr, raw0, pos0,
+                       W, scale, sink, nullptr, out, lse_out, ws, ws_bytes, stream);
+}
+
+int csa_sparse_attn_ex(const void* q, const void* kv, const void* v, const int32_t* idx, const void* kv_raw,
+                       const void* v_raw, int B, int Tq, int H, int D, int Nc, int m, int topk, int Lr, long long raw0,
+                       long long pos0, int W, float scale, const float* sink, const csa_cache_layout_t* layout,
+                       void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+    return sparse_impl("csa_sparse_attn_ex", q, kv, v, idx, kv_raw, v_raw, B, Tq, H, D, Nc, m, topk, Lr, raw0, pos0, W,
+                       scale, sink, layout, out, lse_out, ws, ws_bytes, stream);
 }
 
 // As csa_sparse_attn, with the split partials in the library's static scratch instead of a workspace.
@@ -375,18 +462,40 @@ size_t hca_dense_attn_ws_bytes(int B, int Tq, int H, int D, int Nh) {
     return csa_host::attn_ws_bytes(B, Tq, H, D, 0, Nh, 0);
 }
 
-int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D, int Nh, long long L, int mh,
-                   long long pos0, float scale, const float* sink, void* out, float* lse_out, void* ws,
-                   size_t ws_bytes, void* stream) {
-    const char* fn = "hca_dense_attn";
+static int dense_impl(const char* fn, const void* q, const void* kv_h, const void* v_h, int B, int Tq, int H, int D,
+                      int Nh, long long L, int mh, long long pos0, float scale, const float* sink,
+                      const csa_cache_layout_t* layout, void* out, float* lse_out, void* ws, size_t ws_bytes,
+                      void* stream) {
     csa_host::g_err[0] = 0;
     int rc = validate_dense(fn, q, kv_h, B, Tq, H, D, Nh, L, mh, pos0, scale, out, lse_out);
+    if (rc) return rc;
+    OPT_PTR(v_h);
+    csa_host::CacheLayout lay;
+    rc = read_layout(fn, layout, mh, Nh, 0, 0, &lay);
     if (rc) return rc;
     rc = check_ws(fn, ws, ws_bytes, csa_host::attn_ws_bytes(B, Tq, H, D, 0, Nh, 0));
     if (rc) return rc;
     csa_host::AttnRows r{0, kv_h, Nh, L, mh, nullptr, 0, nullptr, 0, 0, 0, sink};
+    r.seq_lens = lay.seq_lens;
+    r.v = v_h;
+    r.pm = csa_host::page_map(lay, mh);
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
                                  "k_attn_dense");
+}
+
+int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D, int Nh, long long L, int mh,
+                   long long pos0, float scale, const float* sink, void* out, float* lse_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+    return dense_impl("hca_dense_attn", q, kv_h, nullptr, B, Tq, H, D, Nh, L, mh, pos0, scale, sink, nullptr, out,
+                      lse_out, ws, ws_bytes, stream);
+}
+
+int hca_dense_attn_ex(const void* q, const void* kv_h, const void* v_h, int B, int Tq, int H, int D, int Nh,
+                      long long L, int mh, long long pos0, float scale, const float* sink,
+                      const csa_cache_layout_t* layout, void* out, float* lse_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+    return dense_impl("hca_dense_attn_ex", q, kv_h, v_h, B, Tq, H, D, Nh, L, mh, pos0, scale, sink, layout, out,
+                      lse_out, ws, ws_bytes, stream);
 }
 
 // Fused decode: workspace = [idx (if not caller-owned)] [index_topk ws] [attention ws (max of both layers)]
@@ -396,7 +505,8 @@ size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a) {
     if (!a || a->B < 1 || a->L < 1 || a->m < 1 || a->mh < 1 || a->topk < 1) return 0;
     const int Nc = (int)((a->L + a->m - 1) / a->m), Nh = (int)((a->L + a->mh - 1) / a->mh);
     size_t s = a->idx_out ? 0 : align256((size_t)a->B * a->topk * 4);
-    s += align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk));
+    s += align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk,
+                                                plain_layout(a->layout)));
     s += align256(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 1, a->topk, a->W));
     s += csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 0, Nh, 0);
     return s;
@@ -415,6 +525,9 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     rc = validate_sparse(fn, a->csa_q, a->kv, (const int32_t*)16, a->kv_raw, a->B, 1, a->H, a->D, Nc, a->topk, a->W,
                          a->L - a->W, p, a->W, a->scale, a->csa_out, a->csa_lse);
     if (rc) return rc;
+    csa_host::CacheLayout lay;
+    rc = read_layout(fn, a->layout, a->m, Nc, a->mh, Nh, &lay);
+    if (rc) return rc;
     rc = validate_dense(fn, a->hca_q, a->kv_h, a->B, 1, a->H, a->D, Nh, a->L, a->mh, p, a->scale, a->hca_out,
                         a->hca_lse);
     if (rc) return rc;
@@ -427,14 +540,18 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
         idx = (int32_t*)w;
         w += align256((size_t)a->B * a->topk * 4);
     }
-    const size_t iws = align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk));
+    const size_t iws = align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk,
+                                                              plain_layout(a->layout)));
     rc = csa_host::index_topk_launch(a->q_idx, a->w_idx, a->k_idx, a->idx_dtype, a->B, 1, a->HI, a->dI, Nc, a->L, a->m,
-                                     p, a->topk, idx, nullptr, nullptr, w, st);
+                                     p, a->topk, idx, nullptr, nullptr, lay, w, st);
     if (rc) return rc;
     w += iws;
     const size_t aws = ws_bytes - (size_t)(w - (char*)ws);
     csa_host::AttnRows rs{1, a->kv, Nc, 0, 1, idx, a->topk, a->kv_raw, a->W, a->L - a->W, a->W, a->csa_sink};
     csa_host::AttnRows rd{0, a->kv_h, Nh, a->L, a->mh, nullptr, 0, nullptr, 0, 0, 0, a->hca_sink};
+    rs.seq_lens = rd.seq_lens = lay.seq_lens;
+    rs.pm = csa_host::page_map(lay, a->m);
+    rd.pm = csa_host::page_map(lay, a->mh);
     // the CSA layer's attention, then the HCA layer's (layer order: a real next layer's query depends on the
     // previous layer's output, so the two are never overlapped)
     const size_t sws = align256(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 1, a->topk, a->W));

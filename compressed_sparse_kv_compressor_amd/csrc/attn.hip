@@ -32,19 +32,23 @@ using namespace csa;
 using namespace csa_attn;
 
 constexpr int TPB = 256;
-// Number of rows of query (b, t) and pointer to row r (nullptr = masked row).
+// Number of rows of query (b, t) and pointer to row r's key (value = false) or value (value = true) data
+// (nullptr = masked row).  Entries go through the page map; keys and values are one row unless separate
+// value arrays are given.
 struct RowSet {
     int n;
     int b, bt;
-    long long w0;
-    __device__ const uint16_t* row(const Rows& R, int r, int D) const {
-        if (R.mode == 0) return R.kv + ((size_t)b * R.N + r) * D;
+    long long w0, raw0;
+    __device__ const uint16_t* row(const Rows& R, int r, int D, bool value) const {
+        const uint16_t* ent = value && R.v ? R.v : R.kv;
+        if (R.mode == 0) return ent + entry_row(R.pm, b, R.N, r) * D;
         if (r < R.topk) {
             const int j = R.idx[(size_t)bt * R.topk + r];
-            return j >= 0 ? R.kv + ((size_t)b * R.N + j) * D : nullptr;
+            return j >= 0 ? ent + entry_row(R.pm, b, R.N, j) * D : nullptr;
         }
         const long long u = w0 + (r - R.topk);
-        return R.kv_raw + ((size_t)b * R.Lr + (size_t)(u - R.raw0)) * D;
+        const uint16_t* raw = value && R.v_raw ? R.v_raw : R.kv_raw;
+        return raw + ((size_t)b * R.Lr + (size_t)(u - raw0)) * D;
     }
 };
 
@@ -52,9 +56,10 @@ __device__ __forceinline__ RowSet make_rowset(const Rows& R, int bt, int Tq, lon
     RowSet s;
     s.bt = bt;
     s.b = bt / Tq;
-    const long long p = pos0 + bt % Tq;
+    int nd;
+    const long long p = row_geo(R, s.b, bt % Tq, Tq, pos0, s.raw0, nd);
     if (R.mode == 0) {
-        s.n = dense_visible(p, R.L, R.ratio, R.N);
+        s.n = nd;
         s.w0 = 0;
     } else {
         s.w0 = p - R.W + 1 < 0 ? 0 : p - R.W + 1;
@@ -63,7 +68,7 @@ __device__ __forceinline__ RowSet make_rowset(const Rows& R, int bt, int Tq, lon
     return s;
 }
 
-template <int D>
+template <int D, bool SEPV>
 __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q, Rows R, int Tq, int H,
                                                   long long pos0, float scale_log2, int nsplit, int rps,
                                                   float* __restrict__ part_o, float2* __restrict__ part_ml,
@@ -74,7 +79,9 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
     constexpr int DT = D / 16;
     constexpr int CHUNKS = TILE * D / 8;      // 16-byte chunks per tile
     __shared__ __attribute__((aligned(16))) uint16_t tile[TILE * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t vtile_[SEPV ? TILE * RS : 8];   // separate values
     __shared__ float bias[TILE];
+    uint16_t* vtile = SEPV ? vtile_ : tile;
 
     const int split = blockIdx.x, hg = blockIdx.y, bt = blockIdx.z;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -103,10 +110,16 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
         for (int c = threadIdx.x; c < CHUNKS; c += TPB) {
             const int rr = c / (D / 8), cc = c % (D / 8);
             const int r = rb + rr;
-            const uint16_t* src = r < r_end ? rs.row(R, r, D) : nullptr;
+            const uint16_t* src = r < r_end ? rs.row(R, r, D, false) : nullptr;
             u32x4_t v = u32x4_t{0, 0, 0, 0};
             if (src) v = *(const u32x4_t*)(src + cc * 8);
             *(u32x4_t*)(tile + rr * RS + cc * 8) = v;
+            if constexpr (SEPV) {
+                const uint16_t* vsrc = src ? rs.row(R, r, D, true) : nullptr;
+                u32x4_t vv = u32x4_t{0, 0, 0, 0};
+                if (vsrc) vv = *(const u32x4_t*)(vsrc + cc * 8);
+                *(u32x4_t*)(vtile + rr * RS + cc * 8) = vv;
+            }
             if (cc == 0) bias[rr] = src ? 0.0f : -INFINITY;
         }
         __syncthreads();
@@ -159,9 +172,9 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
             for (int d = 0; d < DT; ++d) {
                 acc[d] *= alpha;
                 const CSA_LDS i16x4_t* p0 = (const CSA_LDS i16x4_t*)(
-                    (CSA_LDS uint16_t*)tile + rsel * RS + d * 16 + csel);
+                    (CSA_LDS uint16_t*)vtile + rsel * RS + d * 16 + csel);
                 const CSA_LDS i16x4_t* p1 = (const CSA_LDS i16x4_t*)(
-                    (CSA_LDS uint16_t*)tile + (16 + rsel) * RS + d * 16 + csel);
+                    (CSA_LDS uint16_t*)vtile + (16 + rsel) * RS + d * 16 + csel);
                 const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<CSA_LDS i16x4_t*>(p0));
                 const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<CSA_LDS i16x4_t*>(p1));
                 u32x4_t aw;
@@ -250,14 +263,16 @@ __device__ __forceinline__ void attn64_body(
     const int h = hbase + hl;
 
     const int b = bt / Tq;
-    const long long p = pos0 + bt % Tq;
+    long long raw0;
+    int ndense;
+    const long long p = row_geo(R, b, bt % Tq, Tq, pos0, raw0, ndense);
     // MODE 1 row space: [0, topk) selected entries, [topk, topk32) masked padding (so that no tile
     // mixes the two sources), [topk32, topk32 + window) raw window rows.
     const int topk32 = MODE == 1 ? (R.topk + TILE - 1) / TILE * TILE : 0;
     int nrows;
     long long w0 = 0;
     if (MODE == 0) {
-        nrows = dense_visible(p, R.L, R.ratio, R.N);
+        nrows = ndense;
     } else {
         w0 = p - R.W + 1 < 0 ? 0 : p - R.W + 1;
         nrows = topk32 + (R.W > 0 ? (int)(p - w0 + 1) : 0);
@@ -267,7 +282,9 @@ __device__ __forceinline__ void attn64_body(
     // a multiple of ATT_TILES tiles, the same for every wave (barriers inside); an empty split runs none
     const int ntiles = s_begin < nrows ? rps / TILE : 0;
 
-    const uint16_t* kvb = R.kv ? R.kv + (size_t)b * R.N * D : nullptr;
+    // paged entries address the whole pool (the page map gives pool rows); batch-major ones this sequence's
+    const uint16_t* kvb = R.kv ? (R.pm.table ? R.kv : R.kv + (size_t)b * R.N * D) : nullptr;
+    const size_t kv_rows = R.pm.table ? (size_t)R.pm.nblocks << R.pm.eshift : (size_t)R.N;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
 
     bf16x8_t qreg[KS];
@@ -308,7 +325,8 @@ __device__ __forceinline__ void attn64_body(
 #pragma unroll
             for (int i = 0; i < TILE / 2; ++i) {
                 const int r = r0 + 2 * i + rsub;
-                code[i] = (r < s_end && r < R.topk) ? R.idx[(size_t)bt * R.topk + r] : -1;
+                const int j = (r < s_end && r < R.topk) ? R.idx[(size_t)bt * R.topk + r] : -1;
+                code[i] = j >= 0 && R.pm.table ? (int)entry_row(R.pm, b, R.N, j) : j;
             }
         }
     };
@@ -316,10 +334,10 @@ __device__ __forceinline__ void attn64_body(
     // array gets an empty resource: nothing is ever loaded through it.
     const bool has_kv = kvb != nullptr, has_raw = MODE == 1 && rawb != nullptr;
     const __amdgpu_buffer_rsrc_t rs_kv =
-        make_rsrc(has_kv ? kvb + dh * HD : nullptr, has_kv ? (uint32_t)((size_t)R.N * D * 2 - dh * HD * 2) : 0u);
+        make_rsrc(has_kv ? kvb + dh * HD : nullptr, has_kv ? (uint32_t)(kv_rows * D * 2 - dh * HD * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rs_raw =
         make_rsrc(has_raw ? rawb + dh * HD : nullptr, has_raw ? (uint32_t)((size_t)R.Lr * D * 2 - dh * HD * 2) : 0u);
-    const int raw_first = MODE == 1 ? (int)(w0 - R.raw0) : 0;         // raw row of the first window row
+    const int raw_first = MODE == 1 ? (int)(w0 - raw0) : 0;           // raw row of the first window row
     // Issue this wave's part of tile t into `buf`; returns the tile's validity mask (bit = row slot).
     auto issue_tile = [&](uint16_t* buf, int t) -> uint32_t {
         CSA_LDS char* lb = (CSA_LDS char*)buf + dh * HALF_B;
@@ -771,6 +789,10 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     R.raw0 = a.raw0;
     R.W = a.W;
     R.sink = a.sink;
+    R.seq_lens = a.seq_lens;
+    R.pm = a.pm;
+    R.v = (const uint16_t*)a.v;
+    R.v_raw = (const uint16_t*)a.v_raw;
     const int BT = B * Tq;
     const int max_rows = a.mode == 0 ? a.N : attn_rows(1, H, D, a.topk, a.W);
     int ns, rps;
@@ -782,8 +804,14 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         part_ml = (float2*)((char*)ws + align256((size_t)BT * ns * H * D * 4));
     }
     const float sl2 = scale * LOG2E;
-    const bool big32 = (size_t)a.N * D * 2 > 0xffffffffull || (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
-    if (use128(D, H) && !big32) {
+    // The buffer-load kernels (k_attn128, k_attn64) need every array within reach of 32-bit byte offsets (a
+    // cache of more than 4 GiB per sequence, or a page pool of more than 4 GiB, runs the generic kernel, which
+    // addresses rows with 64-bit pointers), keys that are their own values, and, for k_attn64, a dense row
+    // set that is contiguous (paged dense rows run the generic kernel too).
+    const size_t kv_rows = a.pm.table ? (size_t)a.pm.nblocks << a.pm.eshift : (size_t)a.N;
+    const bool big32 = kv_rows * D * 2 > 0xffffffffull || (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
+    const bool sepv = a.v || a.v_raw;
+    if (use128(D, H) && !big32 && !sepv) {
         const int r128 = a.mode == 0 ? a.N : a128_rows(1, a.topk, a.W);
         AttnJob j{};
         j.q = (const uint16_t*)q; j.R = R; j.Tq = Tq; j.H = H; j.pos0 = pos0; j.scale_log2 = sl2;
@@ -800,9 +828,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
             return attn128_launch(j, st, tag);
         }
     }
-    // the buffer-load kernels need every array within reach of 32-bit byte offsets; a larger one (a cache
-    // of more than 4 GiB per sequence) runs the generic kernel, which addresses rows with 64-bit pointers
-    if (use64(D, H) && !big32) {
+    if (use64(D, H) && !big32 && !sepv && !(a.pm.table && a.mode == 0)) {
         const int nunits = BT * ns, HP = (H + 63) / 64;
         const int nblk = (nunits + 7) / 8 * 8 * HP;
         if (a.mode == 0)
@@ -818,14 +844,22 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     }
     dim3 grid(ns, (H + 63) / 64, BT);
     if (D == 512) {
-        CSA_LAUNCH(tag, k_attn<512>, grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns, rps,
-                   part_o, part_ml, (uint16_t*)out, lse);
+        if (sepv)
+            CSA_LAUNCH(tag, (k_attn<512, true>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns,
+                       rps, part_o, part_ml, (uint16_t*)out, lse);
+        else
+            CSA_LAUNCH(tag, (k_attn<512, false>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns,
+                       rps, part_o, part_ml, (uint16_t*)out, lse);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse, R.sink);
     } else if (D == 128) {
-        CSA_LAUNCH(tag, k_attn<128>, grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns, rps,
-                   part_o, part_ml, (uint16_t*)out, lse);
+        if (sepv)
+            CSA_LAUNCH(tag, (k_attn<128, true>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns,
+                       rps, part_o, part_ml, (uint16_t*)out, lse);
+        else
+            CSA_LAUNCH(tag, (k_attn<128, false>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns,
+                       rps, part_o, part_ml, (uint16_t*)out, lse);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<128>, dim3(H, BT), dim3(32), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse, R.sink);

@@ -60,13 +60,15 @@ __device__ __forceinline__ void attn128_body(
     const int h = hq * 128 + w * 32 + hl;
 
     const int b = bt / Tq;
-    const long long p = pos0 + bt % Tq;
+    long long raw0;
+    int ndense;
+    const long long p = row_geo(R, b, bt % Tq, Tq, pos0, raw0, ndense);
     // MODE 1 row space: [0, topk) selected entries, [topk, topk32) masked padding, [topk32, +window) raw rows
     const int topk32 = MODE == 1 ? (R.topk + TILE - 1) / TILE * TILE : 0;
     int nrows;
     long long w0 = 0;
     if (MODE == 0) {
-        nrows = dense_visible(p, R.L, R.ratio, R.N);
+        nrows = ndense;
     } else {
         w0 = p - R.W + 1 < 0 ? 0 : p - R.W + 1;
         nrows = topk32 + (R.W > 0 ? (int)(p - w0 + 1) : 0);
@@ -75,7 +77,7 @@ __device__ __forceinline__ void attn128_body(
     const int s_end = min(nrows, s_begin + rps);
     const int ntiles = s_begin < nrows ? rps / TILE : 0;   // same for every non-empty split
 
-    const int raw_first = MODE == 1 ? (int)(w0 - R.raw0) : 0;      // raw row of the first window row
+    const int raw_first = MODE == 1 ? (int)(w0 - raw0) : 0;        // raw row of the first window row
     // The row of every slot the split will load, staged once in LDS: the entry (dense rows, selected
     // entries) or the raw row (window); -1 for masked slots (unselected padding, rows past the visible
     // ones, and the tiles loaded past the end), which load row 0 and get no weight.
@@ -87,14 +89,17 @@ __device__ __forceinline__ void attn128_body(
             if (MODE == 0) v = r;
             else if (r < R.topk) v = R.idx[(size_t)bt * R.topk + r];
             else if (r >= topk32) v = raw_first + (r - topk32);
+            if (R.pm.table && v >= 0 && (MODE == 0 || r < R.topk)) v = (int)entry_row(R.pm, b, R.N, v);
         }
         rcode[i] = v;
     }
     __syncthreads();
 
-    const uint16_t* kvb = R.kv ? R.kv + (size_t)b * R.N * D : nullptr;
+    // paged entries address the whole pool (the staged rows are pool rows); batch-major ones this sequence's
+    const uint16_t* kvb = R.kv ? (R.pm.table ? R.kv : R.kv + (size_t)b * R.N * D) : nullptr;
+    const size_t kv_rows = R.pm.table ? (size_t)R.pm.nblocks << R.pm.eshift : (size_t)R.N;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
-    const __amdgpu_buffer_rsrc_t rs_kv = make_rsrc(kvb, kvb ? (uint32_t)((size_t)R.N * ROWB) : 0u);
+    const __amdgpu_buffer_rsrc_t rs_kv = make_rsrc(kvb, kvb ? (uint32_t)(kv_rows * ROWB) : 0u);
     const __amdgpu_buffer_rsrc_t rs_raw = make_rsrc(rawb, rawb ? (uint32_t)((size_t)R.Lr * ROWB) : 0u);
 
     bf16x8_t qreg[KS];

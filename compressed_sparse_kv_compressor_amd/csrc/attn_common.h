@@ -27,12 +27,34 @@ struct Rows {
     long long raw0;
     int W;
     const float* sink;        // [H] attention-sink logits (natural log) or null
+    const long long* seq_lens;  // [B] raw tokens per sequence (variable-length batch) or null
+    csa::PageMap pm;          // entries through a block table (pm.table null: batch-major [B][N][D])
+    const uint16_t* v;        // values of the entries when they differ from the keys (kv), or null
+    const uint16_t* v_raw;    // values of the raw rows when they differ from kv_raw, or null
 };
 
 __device__ __forceinline__ int dense_visible(long long p, long long L, int m, int N) {
     if (p >= L - 1) return N;
     long long v = (p + 1) / m;
     return v < N ? (int)v : N;
+}
+
+// Positions of query t of sequence b.  Variable-length batch: sequence b holds Lb = seq_lens[b] raw tokens
+// (clamped to [Tq, L] for the dense rows, whose array holds ceil(L / ratio) entries), its queries are its
+// last Tq tokens and its Lr raw rows its last Lr tokens; otherwise Lb = L, p = pos0 + t, raw rows start at
+// raw0.  Returns p; sets Lb, the raw position of raw row 0, and the dense row count visible to p.
+__device__ __forceinline__ long long row_geo(const Rows& R, int b, int t, int Tq, long long pos0, long long& raw0,
+                                             int& ndense) {
+    long long Lb = R.L, p = pos0 + t;
+    raw0 = R.raw0;
+    if (R.seq_lens) {
+        const long long x = R.seq_lens[b], hi = R.mode == 0 ? R.L : (1LL << 62);
+        Lb = x < Tq ? Tq : (x > hi ? hi : x);
+        p = Lb - Tq + t;
+        raw0 = Lb - R.Lr;
+    }
+    ndense = R.mode == 0 ? dense_visible(p, Lb, R.ratio, (int)((Lb + R.ratio - 1) / R.ratio)) : 0;
+    return p;
 }
 
 // Final normalization of one head.  The rows give (m, l) in the log2 domain (m = -inf, l = 0: no row) and

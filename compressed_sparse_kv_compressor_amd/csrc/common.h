@@ -72,6 +72,26 @@ __host__ __device__ __forceinline__ float key_f32(uint32_t k) {
 }
 
 // ---------------------------------------------------------------------------
+// paged caches
+// ---------------------------------------------------------------------------
+// With a block table, entry s of sequence b lives in physical row
+// (table[b][s >> eshift] << eshift) | (s & (2^eshift - 1)) of a pool of nblocks pages of 2^eshift entries;
+// page ids outside [0, nblocks) are clamped into it (wrong data, never an access out of bounds).  Without a
+// table, entry s lives in row b * N + s of the batch-major array.
+struct PageMap {
+    const int32_t* table;     // [B][max_blocks] or null
+    int max_blocks;
+    int eshift;               // log2(entries per page)
+    int nblocks;              // pages in the pool
+};
+__device__ __forceinline__ size_t entry_row(const PageMap& pm, int b, int N, int s) {
+    if (!pm.table) return (size_t)b * N + s;
+    uint32_t blk = (uint32_t)pm.table[(size_t)b * pm.max_blocks + (s >> pm.eshift)];
+    blk = blk < (uint32_t)pm.nblocks ? blk : (uint32_t)pm.nblocks - 1u;
+    return ((size_t)blk << pm.eshift) | (size_t)(s & ((1 << pm.eshift) - 1));
+}
+
+// ---------------------------------------------------------------------------
 // wave helpers (wave64)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }

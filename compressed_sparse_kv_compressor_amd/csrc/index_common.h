@@ -14,6 +14,17 @@ __device__ __forceinline__ int n_visible(long long p, long long L, int m, int Nc
     return v < Nc ? (int)v : Nc;
 }
 
+// Variable-length batches: with seq_lens, sequence b holds seq_lens[b] raw tokens (clamped to [Tq, L]; L
+// is the capacity that sizes the caches) and its Tq queries are its last Tq tokens; without seq_lens
+// every sequence holds L tokens and query t sits at pos0 + t.  Returns the entries visible to query t.
+__device__ __forceinline__ int row_visible(const long long* seq_lens, int b, int t, int Tq, long long L,
+                                           long long pos0, int m, int Nc) {
+    if (!seq_lens) return n_visible(pos0 + t, L, m, Nc);
+    long long Lb = seq_lens[b];
+    Lb = Lb < Tq ? Tq : (Lb > L ? L : Lb);
+    return n_visible(Lb - Tq + t, Lb, m, (int)((Lb + m - 1) / m));
+}
+
 // Error model of the MFMA path:
 //   |d~_h - d_h| <= E_h = C_DOT * A_h,  A_h = MFMA(|q_h|, |k|) ~ sum_i |q_hi k_i|
 //   |S~ - S| <= sum_h |w_h| ( C_SUM (|d~_h| + E_h) + E_h ) (1 + 2^-10) + 2^-24 |S~| + 2^-126

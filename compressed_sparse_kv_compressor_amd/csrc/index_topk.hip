@@ -134,11 +134,11 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
 // B = 16 keys, both loaded as 1/4 of a row per lane (the same k-slot order),
 // so D[column][key] leaves every lane with HP/4... 4 heads of one key: the
 // head reduction is mostly lane-local (one xor-16 shuffle for HP = 8).
-template <int DT, int DI, int HI>
+template <int DT, int DI, int HI, bool PAGED>
 __global__ __launch_bounds__(TPB) void k_score(
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int keys_per_wg, int topk,
-    float* __restrict__ S, uint32_t* __restrict__ hist)
+    float* __restrict__ S, uint32_t* __restrict__ hist, const long long* __restrict__ seq_lens, PageMap pm)
 {
     constexpr int STEPS = DI / 32;            // bf16 16x16x32 MFMAs per 16-key tile
     constexpr int EPL = DI / 4;               // key elements per lane
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(TPB) void k_score(
             const int hh = (4 * grp + j) % HP;
             w4[j] = (rv && hh < HI) ? w_idx[r * HI + hh] : 0.f;
         }
-        const int nv = rv ? n_visible(pos0 + tr, L, m, Nc) : 0;
+        const int nv = rv ? row_visible(seq_lens, b, tr, Tq, L, pos0, m, Nc) : 0;
         const bool need_sel = rv && nv > topk;
         const bool writer = need_sel && (grp % LPR) == 0;
         int nvmax;                            // keys any row of the group needs scored
@@ -228,7 +228,8 @@ __global__ __launch_bounds__(TPB) void k_score(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int krow = min(key0 + ((tt0 + u) * 4 + wave) * 16 + col, nvmax - 1);
-                const char* kp = (const char*)k_idx + ((size_t)b * Nc + krow) * DI * ES + (size_t)grp * 16;
+                const size_t prow = PAGED ? entry_row(pm, b, Nc, krow) : (size_t)b * Nc + krow;
+                const char* kp = (const char*)k_idx + prow * DI * ES + (size_t)grp * 16;
 #pragma unroll
                 for (int i = 0; i < NV; ++i) dst[u][i] = *(const u32x4_t*)(kp + i * 64);
             }
@@ -338,13 +339,14 @@ constexpr int CAND_LDS = 8192;       // candidates kept in LDS by k_select (more
 // histograms key bits 19..8 of the entries inside bin b1 (second radix level).
 __global__ __launch_bounds__(STPB) void k_collect(const float* __restrict__ S, uint32_t* __restrict__ hist,
                                                   uint2* __restrict__ list, uint2* __restrict__ ctab, int Tq, int Nc,
-                                                  int NcP, long long L, int m, long long pos0, int topk)
+                                                  int NcP, long long L, int m, long long pos0, int topk,
+                                                  const long long* __restrict__ seq_lens)
 {
     constexpr int GPW = CCHUNK / (STPB / 64) / 64;   // groups of 64 entries per wave
     __shared__ uint32_t lh[BINS1];
     __shared__ uint32_t scratch[STPB / 64], res[4], wcount[STPB / 64], wbase[STPB / 64];
     const int r = blockIdx.y, t = r % Tq;
-    const int nv = n_visible(pos0 + t, L, m, Nc);
+    const int nv = row_visible(seq_lens, r / Tq, t, Tq, L, pos0, m, Nc);
     if (nv <= topk) return;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int s_w = blockIdx.x * CCHUNK + wave * (GPW * 64);
@@ -410,7 +412,8 @@ __global__ __launch_bounds__(STPB) void k_select(
     uint2* __restrict__ band_g, unsigned long long* __restrict__ bkey_g, uint8_t* __restrict__ flag_g,
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int topk,
-    int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out, float* __restrict__ score_out)
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out, float* __restrict__ score_out,
+    const long long* __restrict__ seq_lens, PageMap pm)
 {
     constexpr int ES = DT == 0 ? 2 : 1;
     __shared__ uint32_t lh[BINS2];
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(STPB) void k_select(
     __shared__ uint8_t fl[CAND_LDS];                  // their flags
     const int r = blockIdx.x, b = r / Tq, t = r % Tq, tid = threadIdx.x;
     const int lane = lane_id(), wave = tid >> 6;
-    const int nv = n_visible(pos0 + t, L, m, Nc);
+    const int nv = row_visible(seq_lens, b, t, Tq, L, pos0, m, Nc);
     int32_t* out = idx_out + (size_t)r * topk;
     if (nv <= topk) {                                 // every visible entry is selected (no score is formed)
         for (int i = tid; i < topk; i += STPB) {
@@ -517,7 +520,8 @@ __global__ __launch_bounds__(STPB) void k_select(
     if (need > 0 && need < nb) {
         for (uint32_t i = wave; i < nb; i += STPB / 64) {
             const uint2 be = band(i);
-            const float sx = wave_exact_score<DT, DI, HI>(qrow, wrow, (const char*)k_idx + ((size_t)b * Nc + be.x) * DI * ES);
+            const float sx = wave_exact_score<DT, DI, HI>(qrow, wrow,
+                                                          (const char*)k_idx + entry_row(pm, b, Nc, (int)be.x) * DI * ES);
             if (lane == 0) {
                 const unsigned long long ck = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - be.x);
                 if (nb > (uint32_t)BAND_LDS) Kg[i] = ck;       // the radix path reads every key from HBM
@@ -599,7 +603,7 @@ static size_t decode_index_ws_bytes(int B, int Tq, int Nc) {
 template <int DT, int DI, int HI>
 static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx, int B, int Tq, int Nc,
                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
-                        float* score_out, void* ws, hipStream_t st) {
+                        float* score_out, const long long* seq_lens, const PageMap& pm, void* ws, hipStream_t st) {
     const size_t R = (size_t)B * Tq;
     const int NcP = (Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
     char* p = (char*)ws;
@@ -619,30 +623,36 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
     // gives >= 512 workgroups (two per CU), so the grid runs in one round without a tail
     int kpw = 4096;
     while (kpw > 1024 && (size_t)((Nc + kpw - 1) / kpw) * B < 512) kpw >>= 1;
-    CSA_LAUNCH("k_score", (k_score<DT, DI, HI>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
-               q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist);
+    if (pm.table)
+        CSA_LAUNCH("k_score", (k_score<DT, DI, HI, true>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
+                   q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm);
+    else
+        CSA_LAUNCH("k_score", (k_score<DT, DI, HI, false>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
+                   q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm);
     CSA_LAUNCH("k_collect", k_collect, dim3(NcP / CCHUNK, (unsigned)R), dim3(STPB), 0, st, S, hist, list, ctab, Tq,
-               Nc, NcP, L, m, pos0, topk);
+               Nc, NcP, L, m, pos0, topk, seq_lens);
     CSA_LAUNCH("k_select", (k_select<DT, DI, HI>), dim3((unsigned)R), dim3(STPB), 0, st, hist, list, ctab, band,
-               bkey, flags, q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out, score_out);
+               bkey, flags, q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out, score_out, seq_lens, pm);
     return 0;
 }
 
-size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk) {
-    if (prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk)) return prefill_index_ws_bytes(B, Tq, Nc);
+size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk, bool plain) {
+    if (plain && prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk)) return prefill_index_ws_bytes(B, Tq, Nc);
     return decode_index_ws_bytes(B, Tq, Nc);
 }
 
 int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
                       int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
-                      int32_t* idx_out, int32_t* cnt_out, float* score_out, void* ws, hipStream_t st) {
-    if (prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk))
+                      int32_t* idx_out, int32_t* cnt_out, float* score_out, const CacheLayout& lay, void* ws,
+                      hipStream_t st) {
+    const PageMap pm = page_map(lay, m);
+    if (!lay.seq_lens && !lay.table && prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk))
         return prefill_index_launch(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk, idx_out, cnt_out, score_out,
                                     ws, st);
 #define CSA_IDX_CASE(DT, DI, HI_)                                                              \
     if (dtype == DT && dI == DI && HI == HI_)                                                  \
         return launch_index<DT, DI, HI_>(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk,     \
-                                         idx_out, cnt_out, score_out, ws, st);
+                                         idx_out, cnt_out, score_out, lay.seq_lens, pm, ws, st);
 #define CSA_IDX_HI(DT, DI) CSA_IDX_CASE(DT, DI, 1) CSA_IDX_CASE(DT, DI, 2) CSA_IDX_CASE(DT, DI, 4) \
                            CSA_IDX_CASE(DT, DI, 8) CSA_IDX_CASE(DT, DI, 16)
     CSA_IDX_HI(0, 64) CSA_IDX_HI(0, 128) CSA_IDX_HI(1, 64) CSA_IDX_HI(1, 128)

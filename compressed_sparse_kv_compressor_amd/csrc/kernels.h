@@ -5,13 +5,32 @@
 #include <stdint.h>
 #include <algorithm>
 
+#include "common.h"
+
 namespace csa_host {
 
-// workspace of index_topk_launch for these arguments (the many-query path when it applies)
-size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk);
+// Optional layout of a batch and its caches (all null: every sequence holds L tokens, batch-major arrays).
+struct CacheLayout {
+    const long long* seq_lens;   // [B] raw tokens per sequence (variable-length batch) or null
+    const int32_t* table;        // [B][max_blocks] page ids of the paged caches or null
+    int max_blocks;
+    int num_blocks;              // pages in each pool
+    int block_tokens;            // raw tokens per page (entries per page = block_tokens / ratio, a power of two)
+};
+inline int log2_exact(int x) { int e = 0; while ((1 << e) < x) ++e; return e; }
+// The page map of a cache of ratio m under this layout (no table: plain batch-major rows).
+inline csa::PageMap page_map(const CacheLayout& lay, int m) {
+    csa::PageMap pm{lay.table, lay.max_blocks, 0, lay.num_blocks};
+    if (lay.table) pm.eshift = log2_exact(lay.block_tokens / m);
+    return pm;
+}
+// workspace of index_topk_launch for these arguments (plain: no seq_lens and no table, so the many-query
+// path may apply)
+size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk, bool plain = true);
 int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
                       int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
-                      int32_t* idx_out, int32_t* cnt_out, float* score_out, void* ws, hipStream_t st);
+                      int32_t* idx_out, int32_t* cnt_out, float* score_out, const CacheLayout& lay, void* ws,
+                      hipStream_t st);
 // many-query (prefill) indexer path: bf16, HI = 8, dI = 128, Tq >= 64, topk <= 1024
 bool prefill_index_applicable(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk);
 size_t prefill_index_ws_bytes(int B, int Tq, int Nc);
@@ -37,6 +56,10 @@ struct AttnRows {
     long long raw0;
     int W;
     const float* sink;        // [H] per-head attention-sink logits (natural log), or null
+    const long long* seq_lens;  // [B] raw tokens per sequence (variable-length batch) or null
+    csa::PageMap pm;          // entries through a block table (pm.table null: batch-major kv)
+    const void* v;            // values of the entries when separate from kv (same rows), or null
+    const void* v_raw;        // values of the raw rows when separate from kv_raw, or null
 };
 // mode 0: dense over n rows; mode 1: n selected entries + W window rows
 size_t attn_ws_bytes(int B, int Tq, int H, int D, int mode, int n, int W);

@@ -119,6 +119,41 @@ int csa_hca_compress(const void* hidden, int B, long long L, int Dh,
                      void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Batch and cache layouts ([P2] "第二刀：KV cache 被当成系统在管": the      */
+/* compressed entries live in a classical cache managed in blocks)          */
+/* ------------------------------------------------------------------------ */
+/* Optional layout of a batch and of its compressed caches, taken by the *_ex
+ * entry points and by the fused decode.  A NULL pointer or NULL fields give the
+ * plain layout of the entry points without _ex.
+ *  seq_lens     device [B] int64, or NULL.  Variable-length batch: sequence b
+ *               holds seq_lens[b] raw tokens.  The call's L is then the
+ *               capacity (it sizes the caches: ceil(L / ratio) entries per
+ *               sequence), and Tq <= seq_lens[b] <= L is required (values
+ *               outside are clamped into it).  The Tq queries of sequence b are
+ *               its last Tq tokens and its Lr raw rows its last Lr tokens (raw
+ *               row i holds position seq_lens[b] - Lr + i); pos0 and raw0 are
+ *               ignored.
+ *  block_table  device [B][max_blocks] int32, or NULL.  Paged caches: each
+ *               compressed cache is a pool of num_blocks pages, a page holding
+ *               the entries of block_tokens consecutive raw tokens (epb =
+ *               block_tokens / ratio entries, a power of two; block_tokens =
+ *               lcm(m, m') = 128 serves CSA m = 4 and HCA m' = 128 with one
+ *               table).  Entry s of sequence b is row
+ *               block_table[b][s / epb] * epb + s % epb of the pool, whose rows
+ *               have the plain arrays' row layout ([num_blocks * epb][row]).
+ *               Page ids outside [0, num_blocks) are clamped into it (wrong
+ *               data, never an access out of bounds); the pages that hold a
+ *               sequence's visible entries must be valid.  The caller owns the
+ *               table and the pools. */
+typedef struct csa_cache_layout {
+    const long long* seq_lens;
+    const int32_t* block_table;
+    int max_blocks;
+    int num_blocks;
+    int block_tokens;
+} csa_cache_layout_t;
+
+/* ------------------------------------------------------------------------ */
 /* A2 + A3. Lightning-Indexer scores and per-query top-k                     */
 /*          ([P1] 1.1; [P2] first section and "mHC、Muon、FP4")              */
 /* ------------------------------------------------------------------------ */
@@ -154,6 +189,18 @@ int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int
                    int topk, int32_t* idx_out, int32_t* cnt_out, float* score_out,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* csa_index_topk over a variable-length and/or paged batch (layout above):
+ * k_idx is then the pool of indexer-key rows when block_table is given.
+ * Results as csa_index_topk (bit-exact to running each sequence on its own
+ * contiguous cache).  Such calls always take the per-query path, so the
+ * workspace (csa_index_topk_ex_ws_bytes) holds Tq x Nc scores per sequence. */
+size_t csa_index_topk_ex_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype,
+                                  const csa_cache_layout_t* layout);
+int csa_index_topk_ex(const void* q_idx, const float* w_idx, const void* k_idx, int dtype,
+                      int B, int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0,
+                      int topk, int32_t* idx_out, int32_t* cnt_out, float* score_out,
+                      const csa_cache_layout_t* layout, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* A4. CSA core attention: MQA over the selected entries plus a sliding       */
 /*     window of raw local tokens ([P1] 1.1; [P3] item 1)                    */
@@ -180,6 +227,23 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
                     int B, int Tq, int H, int D, int Nc, int topk, int Lr, long long raw0,
                     long long pos0, int W, float scale, const float* sink, void* out, float* lse_out,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* csa_sparse_attn over a variable-length and/or paged batch (layout above;
+ * kv is then the entry pool when block_table is given), and with values that
+ * may differ from the keys ([P1] 1.1 reads MQA with one vector per entry as key
+ * and value; this variant serves models that keep them apart):
+ *   v      [same rows as kv] bf16 or NULL (= kv): the value of entry j
+ *   v_raw  [B][Lr][D] bf16 or NULL (= kv_raw): the value of raw row i
+ *   out_h = sum_r softmax(l)_r v_r with l_r = scale * q_h . k_r.
+ * m is the ratio of the cache kv (it sets the entries per page of a paged
+ * pool).  With seq_lens, every sequence's Lr raw rows are its last Lr tokens,
+ * so Lr >= Tq + W - 1 is required when W > 0.  Workspace:
+ * csa_sparse_attn_ws_bytes. */
+int csa_sparse_attn_ex(const void* q, const void* kv, const void* v, const int32_t* idx, const void* kv_raw,
+                       const void* v_raw, int B, int Tq, int H, int D, int Nc, int m, int topk, int Lr,
+                       long long raw0, long long pos0, int W, float scale, const float* sink,
+                       const csa_cache_layout_t* layout, void* out, float* lse_out,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* No-allocation variant of csa_sparse_attn, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
@@ -214,6 +278,14 @@ int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D,
                    long long L, int mh, long long pos0, float scale, const float* sink,
                    void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
+/* hca_dense_attn over a variable-length and/or paged batch, with optional
+ * separate values v_h (same rows as kv_h, or NULL = kv_h); as csa_sparse_attn_ex.
+ * With seq_lens, L is the capacity (Nh = ceil(L / mh)). */
+int hca_dense_attn_ex(const void* q, const void* kv_h, const void* v_h, int B, int Tq, int H, int D, int Nh,
+                      long long L, int mh, long long pos0, float scale, const float* sink,
+                      const csa_cache_layout_t* layout, void* out, float* lse_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* A6. Fused decode of one interleaved CSA layer followed by one HCA layer   */
 /*     ([P1] 1.1: the two attention kinds alternate across layers)           */
@@ -247,6 +319,11 @@ typedef struct csa_hca_decode_args {
     void* hca_out;         /* [B][H][D] bf16 */
     float* hca_lse;        /* [B][H] fp32 or NULL */
     const float* hca_sink; /* [H] fp32 attention-sink logits of the HCA layer or NULL */
+    /* Batch and cache layout of both layers (see csa_cache_layout_t), or NULL.  With seq_lens, L is the
+     * capacity and each sequence decodes its token at seq_lens[b] - 1 (kv_raw holding its last W raw
+     * tokens); with block_table, k_idx and kv are the CSA pools (ratio m) and kv_h the HCA pool (ratio
+     * mh), all paged by the one table. */
+    const csa_cache_layout_t* layout;
 } csa_hca_decode_args_t;
 
 size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a);

@@ -165,3 +165,36 @@ def test_rope_validation_codes(b):
     assert r(A16, A16, A16, 4, 512, 64, 1, 10000.0, 2, None) == CSA_ERR_SHAPE            # inverse not 0/1
     assert r(A16, A16, None, 4, 512, 64, 1, 10000.0, 0, None) == CSA_ERR_NULL
     assert r(BAD, A16, A16, 4, 512, 64, 1, 10000.0, 0, None) == CSA_ERR_ALIGN
+
+
+def test_layout_validation_codes(b):
+    """The batch / cache layout is checked before any launch."""
+    lib = b.lib
+    f = lib.csa_index_topk_ex
+
+    def idx_call(lay, **kw):
+        a = dict(q=A16, w=A16, k=A16, dt=0, B=1, Tq=1, HI=8, dI=128, Nc=1024, L=4096, m=4, pos0=4095, topk=64)
+        a.update(kw)
+        return f(a["q"], a["w"], a["k"], a["dt"], a["B"], a["Tq"], a["HI"], a["dI"], a["Nc"], a["L"], a["m"],
+                 a["pos0"], a["topk"], A16, None, None, ctypes.byref(lay), A16, 10 ** 9, None)
+
+    ok = b.CacheLayout(seq_lens=A16, block_table=A16, max_blocks=32, num_blocks=40, block_tokens=128)
+    assert idx_call(b.CacheLayout(seq_lens=ctypes.c_void_p(16 * 1000 + 4))) == CSA_ERR_ALIGN
+    bad_tokens = b.CacheLayout(block_table=A16, max_blocks=32, num_blocks=40, block_tokens=100)
+    assert idx_call(bad_tokens) == CSA_ERR_UNSUPPORTED                          # not a multiple of m
+    npow2 = b.CacheLayout(block_table=A16, max_blocks=32, num_blocks=40, block_tokens=12)
+    assert idx_call(npow2) == CSA_ERR_UNSUPPORTED                               # 3 entries per page
+    short = b.CacheLayout(block_table=A16, max_blocks=31, num_blocks=40, block_tokens=128)
+    assert idx_call(short) == CSA_ERR_SHAPE                                     # 31 x 32 < 1024 entries
+    assert idx_call(b.CacheLayout(block_table=A16, max_blocks=32, num_blocks=0, block_tokens=128)) == CSA_ERR_SHAPE
+    assert lib.csa_index_topk_ex_ws_bytes(1, 8192, 8, 128, 65536, 1024, 0, None) < \
+        lib.csa_index_topk_ex_ws_bytes(1, 8192, 8, 128, 65536, 1024, 0, ctypes.byref(ok))   # no many-query path
+    sp = lib.csa_sparse_attn_ex
+    # q, kv, v, idx, kv_raw, v_raw, B, Tq, H, D, Nc, m, topk, Lr, raw0, pos0, W, scale, sink, layout, out, lse, ws...
+    var = b.CacheLayout(seq_lens=A16)
+    assert sp(A16, A16, None, A16, A16, None, 2, 2, 16, 128, 100, 4, 8, 9, 0, 0, 9, 0.1, None, ctypes.byref(var),
+              A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE                   # Lr < Tq + W - 1
+    assert sp(A16, A16, BAD, A16, A16, None, 2, 2, 16, 128, 100, 4, 8, 10, 0, 0, 9, 0.1, None, ctypes.byref(var),
+              A16, None, A16, 10 ** 9, None) == CSA_ERR_ALIGN
+    assert sp(A16, A16, None, A16, A16, None, 2, 2, 16, 128, 100, 0, 8, 10, 0, 0, 9, 0.1, None, ctypes.byref(var),
+              A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE                   # m = 0
