@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--small-steps", type=int, default=200, help="timed calls of the 4K single-sequence leg (0: skip)")
     ap.add_argument("--batched-steps", type=int, default=50,
                     help="timed steps of the 32 x 128K batched CSA decode leg (0: skip)")
+    ap.add_argument("--serving-steps", type=int, default=50,
+                    help="timed steps of the paged, variable-length serving decode leg (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run two plain device copies of MIB MiB (a kernel of known "
                          "traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE by)")
@@ -236,6 +238,9 @@ def main():
     if args.batched_steps > 0:
         out["batched_decode"] = batched_leg(args, dev, cpu=not args.no_cpu_baseline)
         log("batched_decode done")
+    if args.serving_steps > 0:
+        out["serving_decode"] = serving_leg(args, dev, cpu=not args.no_cpu_baseline)
+        log("serving_decode done")
     if args.prefill_steps > 0:
         out["indexer_prefill"] = prefill_leg(args, dev, cpu=not args.no_cpu_baseline)
         log("indexer_prefill done")
@@ -866,6 +871,129 @@ def batched_leg(args, dev, cpu=True):
                                "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
                                "seconds": round(el, 2)}
     del copies, base, iws, aws
+    torch.cuda.empty_cache()
+    return res
+
+
+SERVING_KERNELS = ("k_app_proj", "k_app_state", "k_fill", "k_score", "k_collect", "k_select", "k_attn_sparse",
+                   "k_attn_dense", "k_combine")
+
+
+def serving_leg(args, dev, cpu=True):
+    """The 1M-context decode pair as a serving step: 8 sequences of different lengths (about 0.76M-1M tokens)
+    whose compressed caches live in shuffled pages of 128 raw tokens (CSA m = 4: 32 entries per page, HCA
+    m' = 128: one), and whose window and open blocks live in the per-request state.  A step appends one new
+    token per sequence (hidden 4096: projection, state update, provisional entries, window shift,
+    seq_lens += 1) and runs the CSA + HCA decode pair on the paged, variable-length batch."""
+    import numpy as np
+    import torch
+
+    from compressed_sparse_kv_compressor_amd import binding as b
+    from compressed_sparse_kv_compressor_amd import synth
+    from compressed_sparse_kv_compressor_amd.configs import DECODE_B8_1M as cfg
+
+    B, H, D, HI, dI, m, mh, W, topk, Dh = cfg.B, cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.m, cfg.mh, cfg.W, cfg.topk, 4096
+    L = cfg.L + 4096                                      # capacity: room for the appended tokens
+    bt = 128
+    mb = -(-L // bt)
+    nblk = B * mb
+    g = synth.parallel_bits_to_device
+    table = torch.from_numpy(np.random.default_rng(0).permutation(nblk).astype(np.int32).reshape(B, mb)).to(dev)
+    lens0 = np.linspace(0.75 * cfg.L, cfg.L, B).astype(np.int64) // bt * bt     # multiples of the page size
+    seq = torch.from_numpy(lens0.copy()).to(dev)
+    pools = dict(ik=g(0, "sv_ik", (nblk * (bt // m), dI), dI ** -0.5, cfg.idx_dtype, dev),
+                 kv=g(0, "sv_kv", (nblk * (bt // m), D), D ** -0.5, 0, dev),
+                 kvh=g(0, "sv_kvh", (nblk * (bt // mh), D), D ** -0.5, 0, dev))
+    win = g(0, "sv_win", (B, W, D), D ** -0.5, 0, dev)
+    tod = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    wkv, wik, gate, bslot = (tod(a) for a in synth.compress_weights(0, Dh, D, dI, m, prefix="sv_csa_"))
+    hw = synth.compress_weights(0, Dh, D, 0, mh, prefix="sv_hca_")
+    wkv_h, gate_h, bslot_h = tod(hw[0]), tod(hw[2]), tod(hw[3])
+    hidden = g(0, "sv_hidden", (B, 1, Dh), 1.0, 0, dev)
+    state = torch.zeros(B * b.lib.csa_append_state_bytes(D, dI) // 4, dtype=torch.float32, device=dev)
+    aws = b.workspace(b.lib.csa_decode_append_ws_bytes(B, 1, D, dI), dev)
+    layout = b.make_layout(seq_lens=seq, block_table=table, num_blocks=nblk, block_tokens=bt)
+    q_idx = g(0, "sv_q_idx", (B, 1, HI, dI), dI ** -0.5, cfg.idx_dtype, dev)
+    w_idx = torch.from_numpy(synth.half_normal_f32(0, "sv_w_idx", (B, 1, HI), HI ** -0.5)).to(dev)
+    csa_q, hca_q = g(0, "sv_csa_q", (B, H, D), D ** -0.5, 0, dev), g(0, "sv_hca_q", (B, H, D), D ** -0.5, 0, dev)
+    csa_out = torch.empty((B, H, D), dtype=torch.int16, device=dev)
+    hca_out = torch.empty_like(csa_out)
+    idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    dargs = b.make_decode_args(L=L, scale=cfg.scale, csa_q=csa_q, q_idx=q_idx, w_idx=w_idx, k_idx=pools["ik"],
+                               kv=pools["kv"], kv_raw=win, idx_dtype=cfg.idx_dtype, m=m, topk=topk, W=W,
+                               csa_out=csa_out, hca_q=hca_q, kv_h=pools["kvh"], mh=mh, hca_out=hca_out, idx_out=idx,
+                               layout=layout)
+    dws = b.workspace(b.csa_hca_decode_ws_bytes(dargs), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i=0):
+        b.csa_decode_append(hidden, wkv, wik, gate, bslot, m, wkv_h, gate_h, bslot_h, mh, L, seq, state, pools["kv"],
+                            pools["ik"], pools["kvh"], win, ik_dtype=cfg.idx_dtype, layout=b.make_layout(
+                                block_table=table, num_blocks=nblk, block_tokens=bt), ws=aws, stream=stream)
+        b.csa_hca_decode(dargs, ws=dws, stream=stream)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    n = args.serving_steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    b.prof_reset()
+    b.prof_only(None)
+    b.prof_enable(True)
+    for _ in range(min(n, 20)):
+        step()
+    torch.cuda.synchronize()
+    b.prof_enable(False)
+    kern = {}
+    for name in SERVING_KERNELS:
+        t, k = b.prof_read(name)
+        if k:
+            kern[name] = round(t / k * 1000.0, 2)
+    b.prof_reset()
+    pct = step_percentiles(step, 30, stream)
+    lens = seq.cpu().numpy()
+    res = {"workload": "serving_decode_b8_1m_paged", "B": B, "seq_lens_now": lens.tolist(), "capacity": L,
+           "page_tokens": bt, "pages": nblk, "Dh": Dh, "H": H, "D": D, "topk": topk, "W": W,
+           "idx_dtype": "e4m3" if cfg.idx_dtype else "bf16", "steps": n, "ms_per_step": round(ms, 4),
+           "value": round(B / (ms * 1e-3), 1), "unit": "queries/s", "step_us_percentiles": pct,
+           "kernel_us_breakdown": kern,
+           "note": "append one token per sequence (projection + state + provisional entries + window shift) then "
+                   "the CSA + HCA decode pair over shuffled pages and variable lengths"}
+    if cpu:
+        import oracle
+        t0 = time.perf_counter()
+        Lb = int(lens[0])
+        nc, nh = -(-Lb // m), -(-Lb // mh)
+        tb = table[0].long()
+        rows_c = (tb[:, None] * (bt // m) + torch.arange(bt // m, device=dev)[None]).reshape(-1)[:nc]
+        kb = pools["ik"].index_select(0, rows_c).cpu().numpy()
+        qb = q_idx[0:1].cpu().numpy()
+        want, _, _, _ = oracle.index_topk(qb, w_idx[0:1].cpu().numpy(), kb[None], Lb, m, Lb - 1, topk, cfg.idx_dtype)
+        sel_rows = rows_c.index_select(0, torch.from_numpy(want[0, 0].astype(np.int64)).to(dev))
+        kv_sel = pools["kv"].index_select(0, sel_rows).cpu().numpy().view(np.uint16)[None]
+        u16 = lambda t: t.cpu().numpy().view(np.uint16)
+        o_csa, _ = oracle.sparse_attn(u16(csa_q[0:1]).reshape(1, 1, H, D), kv_sel,
+                                      np.arange(topk, dtype=np.int32).reshape(1, 1, topk), u16(win[0:1]), Lb - W,
+                                      Lb - 1, W, cfg.scale)
+        rows_h = tb[:nh]
+        o_hca, _ = oracle.dense_attn(u16(hca_q[0:1]).reshape(1, 1, H, D), u16(pools["kvh"].index_select(0, rows_h))[None],
+                                     Lb, mh, Lb - 1, cfg.scale)
+
+        def rel(got, want_):
+            gq = (u16(got).astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(-1, D)
+            o = want_.reshape(-1, D)
+            return float((np.abs(gq - o).max(1) / np.abs(o).max(1)).max())
+        res["parity_sample"] = {"sequence": 0, "L": Lb,
+                                "topk_bit_exact": bool(np.array_equal(idx[0].cpu().numpy(), want[0, 0])),
+                                "csa_max_row_rel_err": rel(csa_out[0], o_csa), "hca_max_row_rel_err": rel(hca_out[0], o_hca),
+                                "tolerance": 2e-2, "oracle_s": round(time.perf_counter() - t0, 2)}
+    del pools, win, dws, aws
     torch.cuda.empty_cache()
     return res
 

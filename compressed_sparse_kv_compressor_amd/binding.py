@@ -36,6 +36,9 @@ def _load():
         "csa_compress": ([P, P, P, P, P, I, LL, I, I, I, I, I, I, P, P, P, P, Z, P], I),
         "csa_hca_compress_ws_bytes": ([I, LL, I, I, I, I, I, I], Z),
         "csa_hca_compress": ([P, I, LL, I, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, I, P, P, Z, P], I),
+        "csa_append_state_bytes": ([I, I], Z),
+        "csa_decode_append_ws_bytes": ([I, I, I, I], Z),
+        "csa_decode_append": ([P, I, I, I, P, P, P, P, I, I, I, I, P, P, P, I, LL, P, P, P, P, P, P, I, P, P, Z, P], I),
         "csa_index_topk_ws_bytes": ([I, I, I, I, I, I, I], Z),
         "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, Z, P], I),
         "csa_index_topk_ex_ws_bytes": ([I, I, I, I, I, I, I, P], Z),
@@ -68,7 +71,8 @@ lib = _load()
 EXPORTED = ("csa_abi_version", "csa_status_str", "csa_last_error", "csa_compress_ws_bytes", "csa_compress",
             "csa_hca_compress_ws_bytes", "csa_hca_compress",
             "csa_index_topk_ws_bytes", "csa_index_topk", "csa_sparse_attn_ws_bytes", "csa_sparse_attn",
-            "csa_sparse_attn_noalloc", "csa_index_topk_ex_ws_bytes", "csa_index_topk_ex", "csa_sparse_attn_ex",
+            "csa_sparse_attn_noalloc", "csa_append_state_bytes", "csa_decode_append_ws_bytes", "csa_decode_append",
+            "csa_index_topk_ex_ws_bytes", "csa_index_topk_ex", "csa_sparse_attn_ex",
             "hca_dense_attn_ex",
             "hca_dense_attn_ws_bytes", "hca_dense_attn", "csa_hca_decode_ws_bytes", "csa_hca_decode",
             "csa_rope", "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read",
@@ -166,6 +170,25 @@ def csa_hca_compress(hidden, w_kv, w_ik, w_gate, b_slot, m: int, W: int, kv_out,
     _check(lib.csa_hca_compress(_p(hidden), B, L, Dh, _p(w_kv), _p(w_ik), _p(w_gate), _p(b_slot), D, dI, m, W,
                                 ik_dtype, _p(kv_out), _p(ik_out), _p(win_out), _p(w_kv_h), _p(w_gate_h), _p(b_slot_h),
                                 mh, _p(kv_h_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def csa_decode_append(hidden, w_kv, w_ik, w_gate, b_slot, m: int, w_kv_h, w_gate_h, b_slot_h, mh: int, L: int,
+                      seq_lens, state, kv_out, ik_out, kv_h_out, win, ik_dtype: int = BF16, layout=None, ws=None,
+                      stream=None):
+    """Append hidden[B][T][Dh] to every sequence (see csa.h): projections, running block pools in `state`
+    (bytes: lib.csa_append_state_bytes(D, dI) per sequence), rewritten entries, shifted window, seq_lens += T."""
+    B, T, Dh = hidden.shape
+    D = w_kv.shape[0]
+    dI = w_ik.shape[0] if w_ik is not None else 0
+    W = win.shape[1] if win is not None else 0
+    if seq_lens.dtype != torch.int64 or seq_lens.numel() != B:
+        raise ValueError("seq_lens must be B int64 values")
+    if ws is None:
+        ws = workspace(lib.csa_decode_append_ws_bytes(B, T, D, dI), hidden.device)
+    _check(lib.csa_decode_append(_p(hidden), B, T, Dh, _p(w_kv), _p(w_ik), _p(w_gate), _p(b_slot), D, dI, m, ik_dtype,
+                                 _p(w_kv_h), _p(w_gate_h), _p(b_slot_h), mh, L, _p(seq_lens), _p(state), _p(kv_out),
+                                 _p(ik_out), _p(kv_h_out), _p(win), W, _lay(layout), _p(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def csa_index_topk(q_idx, w_idx, k_idx, dtype: int, L: int, m: int, pos0: int, topk: int, idx_out, cnt_out=None,

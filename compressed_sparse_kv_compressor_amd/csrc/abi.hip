@@ -346,6 +346,61 @@ int csa_hca_compress(const void* hidden, int B, long long L, int Dh, const void*
 
 static bool plain_layout(const csa_cache_layout_t* lay) { return !lay || (!lay->seq_lens && !lay->block_table); }
 
+size_t csa_append_state_bytes(int D, int dI) {
+    if (D < 1 || dI < 0) return 0;
+    return csa_host::append_state_words(D, dI) * 4;
+}
+
+size_t csa_decode_append_ws_bytes(int B, int T, int D, int dI) {
+    if (B < 1 || T < 1 || D < 1 || dI < 0) return 0;
+    return csa_host::append_ws_bytes(B, T, D, dI);
+}
+
+int csa_decode_append(const void* hidden, int B, int T, int Dh, const void* w_kv, const void* w_ik, const float* w_gate,
+                      const float* b_slot, int D, int dI, int m, int ik_dtype, const void* w_kv_h,
+                      const float* w_gate_h, const float* b_slot_h, int mh, long long L, long long* seq_lens,
+                      void* state, void* kv_out, void* ik_out, void* kv_h_out, void* win, int W,
+                      const csa_cache_layout_t* layout, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa_decode_append";
+    csa_host::g_err[0] = 0;
+    REQ_PTR(hidden);
+    REQ_PTR(w_kv);
+    REQ_PTR(w_gate);
+    REQ_PTR(w_kv_h);
+    REQ_PTR(w_gate_h);
+    REQ_PTR(state);
+    REQ_PTR(kv_out);
+    REQ_PTR(kv_h_out);
+    OPT_PTR(b_slot);
+    OPT_PTR(b_slot_h);
+    REQ(seq_lens != nullptr, CSA_ERR_NULL, "%s: seq_lens is NULL", fn);
+    REQ(((uintptr_t)seq_lens & 7u) == 0, CSA_ERR_ALIGN, "%s: seq_lens is not 8-byte aligned", fn);
+    REQ(B >= 1 && T >= 1 && L >= 1 && m >= 1 && mh >= 1 && W >= 0 && dI >= 0, CSA_ERR_SHAPE,
+        "%s: need B, T, L, m, mh >= 1 and W, dI >= 0", fn);
+    REQ(ik_dtype == CSA_BF16 || ik_dtype == CSA_E4M3, CSA_ERR_DTYPE, "%s: ik_dtype %d unknown", fn, ik_dtype);
+    REQ(Dh % 64 == 0 && Dh >= 64 && Dh <= 16384, CSA_ERR_UNSUPPORTED, "%s: Dh=%d (multiple of 64 in [64,16384])", fn, Dh);
+    REQ(D == 64 || D == 128 || D == 256 || D == 512, CSA_ERR_UNSUPPORTED, "%s: D=%d unsupported", fn, D);
+    REQ(dI == 0 || dI == 64 || dI == 128 || dI == 256 || dI == 512, CSA_ERR_UNSUPPORTED, "%s: dI=%d unsupported", fn, dI);
+    REQ(2 * D + dI <= 2048 && m <= 1024 && mh <= 1024 && W <= 1024, CSA_ERR_UNSUPPORTED,
+        "%s: 2 D + dI <= 2048, m, mh, W <= 1024 supported", fn);
+    REQ((long long)B * T <= (1LL << 24) && (L + m - 1) / m <= (1LL << 24), CSA_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+    if (dI) {
+        REQ_PTR(w_ik);
+        REQ_PTR(ik_out);
+    }
+    if (W > 0) REQ_PTR(win);
+    const int Nc = (int)((L + m - 1) / m), Nh = (int)((L + mh - 1) / mh);
+    csa_host::CacheLayout lay;
+    int rc = read_layout(fn, layout, m, Nc, mh, Nh, &lay);
+    if (rc) return rc;
+    lay.seq_lens = nullptr;
+    rc = check_ws(fn, ws, ws_bytes, csa_host::append_ws_bytes(B, T, D, dI));
+    if (rc) return rc;
+    return csa_host::append_launch(hidden, B, T, Dh, w_kv, dI ? w_ik : nullptr, w_gate, b_slot, D, dI, m, ik_dtype,
+                                   w_kv_h, w_gate_h, b_slot_h, mh, L, seq_lens, state, kv_out, dI ? ik_out : nullptr,
+                                   kv_h_out, W > 0 ? win : nullptr, W, lay, ws, (hipStream_t)stream);
+}
+
 size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype) {
     if (B < 1 || Tq < 1 || Nc < 1 || HI < 1 || dI < 1 || topk < 1) return 0;
     return csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk);

@@ -71,6 +71,12 @@ int hca_compress_launch(const void* hidden, const void* w_kv, const void* w_ik, 
                         const float* b_slot, int B, long long L, int Dh, int D, int dI, int m, int W, int ik_dtype,
                         void* kv_out, void* ik_out, void* win_out, const void* w_kv_h, const float* w_gate_h,
                         const float* b_slot_h, int mh, void* kv_h_out, void* ws, hipStream_t st);
+size_t append_state_words(int D, int dI);
+size_t append_ws_bytes(int B, int T, int D, int dI);
+int append_launch(const void* hidden, int B, int T, int Dh, const void* w_kv, const void* w_ik, const float* w_gate,
+                  const float* b_slot, int D, int dI, int m, int ik_dtype, const void* w_kv_h, const float* w_gate_h,
+                  const float* b_slot_h, int mh, long long L, long long* seq_lens, void* state, void* kv, void* ik,
+                  void* kv_h, void* win, int W, const CacheLayout& lay, void* ws, hipStream_t st);
 int compress_launch(const void* hidden, const void* w_kv, const void* w_ik, const float* w_gate,
                     const float* b_slot, int B, long long L, int Dh, int D, int dI, int m, int W,
                     int ik_dtype, void* kv_out, void* ik_out, void* win_out, void* ws, hipStream_t st);

@@ -154,6 +154,49 @@ typedef struct csa_cache_layout {
 } csa_cache_layout_t;
 
 /* ------------------------------------------------------------------------ */
+/* Incremental compression during decode: the per-request state cache       */
+/* ([P2] "第二刀：KV cache 被当成系统在管": compressed entries in a classical */
+/* cache, plus a fixed-size state per request for the window and the tail)  */
+/* ------------------------------------------------------------------------ */
+/* Appends T new tokens to every sequence of a batch whose caches were built by
+ * csa_hca_compress (or by earlier appends).  For each new token at position
+ * p = seq_lens[b] + t, in order: its KV row (w_kv), indexer key (w_ik) and HCA
+ * row (w_kv_h) are projected once, with its gate logits; the running
+ * softmax-gated pools of the open CSA block (p / m) and HCA block (p / mh)
+ * absorb it; the entries of every block it touched are rewritten as the pool
+ * so far, rounded once (so after the call the caches hold exactly what
+ * csa_hca_compress of the whole prefix gives, within fp32 summation order:
+ * complete blocks final, the last entries provisional); the window shifts by
+ * T rows (win[b][i] = the raw KV row of position L_b - W + i); and
+ * seq_lens[b] advances by T on the device (tokens beyond the capacity L are
+ * dropped).  Arguments as csa_hca_compress, plus:
+ *   hidden    [B][T][Dh] bf16: the new tokens
+ *   L         capacity in raw tokens (caches hold ceil(L/m), ceil(L/mh) entries
+ *             per sequence, or their pools through layout->block_table)
+ *   seq_lens  device [B] int64, read and advanced
+ *   state     device [B][csa_append_state_bytes(D, dI)] fp32, caller-owned:
+ *             the open blocks' pools.  It is ignored for a sequence whose
+ *             length is a multiple of both m and mh (both blocks start fresh);
+ *             otherwise it must be the state the previous append left (a
+ *             sequence compressed in bulk should stop at such a multiple, e.g.
+ *             of lcm(m, mh) = 128, and append the rest)
+ *   win       [B][W][D] bf16, caller-owned (the bulk compressor's win_out)
+ *   layout    NULL or a block table for paged caches (its seq_lens field is
+ *             not used; the argument above is)
+ * Supported: D in {64, 128, 256, 512}, dI in {0, 64, 128, 256, 512},
+ * 2 D + dI <= 2048, Dh % 64 == 0, 1 <= m, mh <= 1024, T >= 1, 0 <= W <= 1024.
+ * Workspace: csa_decode_append_ws_bytes (the fp32 projections). */
+size_t csa_append_state_bytes(int D, int dI);
+size_t csa_decode_append_ws_bytes(int B, int T, int D, int dI);
+int csa_decode_append(const void* hidden, int B, int T, int Dh,
+                      const void* w_kv, const void* w_ik, const float* w_gate, const float* b_slot,
+                      int D, int dI, int m, int ik_dtype,
+                      const void* w_kv_h, const float* w_gate_h, const float* b_slot_h, int mh,
+                      long long L, long long* seq_lens, void* state,
+                      void* kv_out, void* ik_out, void* kv_h_out, void* win, int W,
+                      const csa_cache_layout_t* layout, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* A2 + A3. Lightning-Indexer scores and per-query top-k                     */
 /*          ([P1] 1.1; [P2] first section and "mHC、Muon、FP4")              */
 /* ------------------------------------------------------------------------ */
