@@ -85,6 +85,20 @@ def _load():
         lib.ora_dense_attn.restype = None
         lib.ora_rope.argtypes = [I, I, I, I, D, I, P, P, P]
         lib.ora_rope.restype = None
+        lib.ora_kv_fp8_row_bytes.argtypes = [I]
+        lib.ora_kv_fp8_row_bytes.restype = I
+        lib.ora_kv_fp8_encode.argtypes = [I, I, P, P]
+        lib.ora_kv_fp8_encode.restype = None
+        lib.ora_kv_fp8_decode.argtypes = [I, I, P, P]
+        lib.ora_kv_fp8_decode.restype = None
+        lib.ora_mxfp4_encode.argtypes = [I, I, P, P, P]
+        lib.ora_mxfp4_encode.restype = None
+        lib.ora_mxfp4_value.argtypes = [P, P, I]
+        lib.ora_mxfp4_value.restype = D
+        lib.ora_exact_dot_mxfp4.argtypes = [P, P, P, P, I]
+        lib.ora_exact_dot_mxfp4.restype = ctypes.c_float
+        lib.ora_index_scores_mxfp4.argtypes = [I, I, I, I, I, LL, I, LL, P, P, P, P, P, P, P]
+        lib.ora_index_scores_mxfp4.restype = None
         _lib = lib
     return _lib
 
@@ -306,3 +320,92 @@ def compress(hidden, w_kv, w_ik, w_gate, b_slot, m: int, W: int = 0, j0: int = 0
     lib.ora_compress(B, L, Dh, D, dI, m, W, px, pw, pwi, pg, pb, j0, j1,
                      _ptr(kv), _ptr(ik), _ptr(win))
     return kv, ik, win
+
+
+# --- C12: FP8 storage of the non-RoPE KV dimensions ----------------------------------------------------------
+
+def kv_fp8_row_bytes(D: int) -> int:
+    return int(_load().ora_kv_fp8_row_bytes(D))
+
+
+def kv_fp8_encode(x):
+    """bf16 KV rows x[..., D] -> uint8 rows [..., D + 80]: e4m3 codes of the first D - 64 dimensions in groups of
+    64 with a power-of-two scale each, the last 64 (RoPE) dimensions kept as bf16, the scale exponents."""
+    lib = _load()
+    x, px = _c(x, np.uint16)
+    D = x.shape[-1]
+    n = x.size // D
+    y = np.empty(x.shape[:-1] + (D + 80,), np.uint8)
+    lib.ora_kv_fp8_encode(n, D, px, _ptr(y))
+    return y
+
+
+def kv_fp8_decode(y, D: int):
+    """uint8 rows [..., D + 80] -> fp64 values [..., D]."""
+    lib = _load()
+    y, py = _c(y, np.uint8)
+    n = y.size // (D + 80)
+    x = np.empty(y.shape[:-1] + (D,), np.float64)
+    lib.ora_kv_fp8_decode(n, D, py, _ptr(x))
+    return x
+
+
+# --- C13: MXFP4 indexer operands --------------------------------------------------------------------------
+
+def mxfp4_encode(x):
+    """bf16 vectors x[..., n] (n % 32 == 0) -> (codes uint8 [..., n/2], scales uint8 [..., n/32]) in the OCP MX
+    FP4 format (E2M1 elements, one E8M0 scale per 32)."""
+    lib = _load()
+    x, px = _c(x, np.uint16)
+    n = x.shape[-1]
+    rows = x.size // n
+    codes = np.empty(x.shape[:-1] + (n // 2,), np.uint8)
+    scales = np.empty(x.shape[:-1] + (n // 32,), np.uint8)
+    lib.ora_mxfp4_encode(rows, n, px, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mxfp4_values(codes, scales):
+    """Exact values (fp64) of MXFP4 vectors."""
+    lib = _load()
+    codes, pc = _c(codes, np.uint8)
+    scales, ps = _c(scales, np.uint8)
+    n = codes.shape[-1] * 2
+    rows = codes.size // (n // 2)
+    out = np.empty(codes.shape[:-1] + (n,), np.float64)
+    flat = out.reshape(rows, n)
+    for r in range(rows):
+        cr = codes.reshape(rows, n // 2)[r]
+        sr = scales.reshape(rows, n // 32)[r]
+        pcr, psr = _c(cr, np.uint8)[1], _c(sr, np.uint8)[1]
+        for i in range(n):
+            flat[r, i] = lib.ora_mxfp4_value(pcr, psr, i)
+    return out
+
+
+def exact_dot_mxfp4(ac, as_, bc, bs) -> np.float32:
+    lib = _load()
+    ac, pac = _c(ac, np.uint8)
+    as_, pas = _c(as_, np.uint8)
+    bc, pbc = _c(bc, np.uint8)
+    bs, pbs = _c(bs, np.uint8)
+    return np.float32(lib.ora_exact_dot_mxfp4(pac, pas, pbc, pbs, ac.size * 2))
+
+
+def index_topk_mxfp4(qc, qs, w_idx, kc, ks, L: int, m: int, pos0: int, k: int):
+    """Canonical scores over MXFP4 operands (q codes [B][Tq][HI][dI/2], scales [B][Tq][HI][dI/32]; k codes
+    [B][Nc][dI/2], scales [B][Nc][dI/32]) and their top-k: (idx, cnt, S, n_vis)."""
+    lib = _load()
+    qc, pqc = _c(qc, np.uint8)
+    qs, pqs = _c(qs, np.uint8)
+    w, pw = _c(w_idx, np.float32)
+    kc, pkc = _c(kc, np.uint8)
+    ks, pks = _c(ks, np.uint8)
+    B, Tq, HI, half = qc.shape
+    dI = half * 2
+    Nc = kc.shape[1]
+    S = np.empty((B, Tq, Nc), np.float32)
+    nv = np.empty((B, Tq), np.int32)
+    lib.ora_index_scores_mxfp4(B, Tq, HI, dI, Nc, L, m, pos0, pqc, pqs, pw, pkc, pks, _ptr(S), _ptr(nv))
+    idx, cnt = topk(S, nv, k)
+    return idx, cnt, S, nv

@@ -554,3 +554,172 @@ void ora_rope(int n, int D, int rd, int group, double theta, int inverse, const 
         }
     }
 }
+
+/* ---- C12: FP8 storage of the non-RoPE KV dimensions ----------------------------------------------------
+ * [P1 section 1.1, last paragraph]: the KV cache keeps its RoPE dimensions in BF16 and the other dimensions
+ * in FP8.  The pages print no scale scheme.  Reading taken: a D-wide KV row (its first D - 64 dimensions,
+ * then the 64 RoPE dimensions of C11) is stored in D + 80 bytes:
+ *   bytes [0, D-64)        OCP e4m3 codes of x_i / 2^e_g, group g = i / 64 of the non-RoPE dimensions,
+ *   bytes [D-64, D+64)     the 64 RoPE dimensions as they were (bf16),
+ *   bytes [D+64, D+80)     e_g + 127 for each group (one byte each, the unused bytes 0),
+ * where e_g is the smallest integer with max_{i in g} |x_i| <= 448 * 2^e_g (0 for an all-zero group): no code
+ * saturates and the division by 2^e_g is exact, so each code is the e4m3 rounding (to nearest, ties to
+ * even) of its value.  A dimension decodes to e4m3(code) * 2^e_g. */
+int ora_kv_fp8_row_bytes(int D) { return D + 80; }
+
+void ora_kv_fp8_encode(int n, int D, const uint16_t* x, uint8_t* y)
+{
+    const int nope = D - 64, rb = D + 80;
+    for (int r = 0; r < n; ++r) {
+        const uint16_t* xr = x + (size_t)r * D;
+        uint8_t* yr = y + (size_t)r * rb;
+        memset(yr, 0, (size_t)rb);
+        for (int g = 0; g < nope / 64; ++g) {
+            double amax = 0.0;
+            for (int i = 64 * g; i < 64 * g + 64; ++i) {
+                const double a = fabs(ora_bf16_value(xr[i]));
+                if (a > amax) amax = a;
+            }
+            int e = 0;
+            if (amax > 0.0) {
+                e = -200;
+                while (amax > ldexp(448.0, e)) ++e;            /* the smallest e with amax <= 448 * 2^e */
+            }
+            yr[D + 64 + g] = (uint8_t)(e + 127);
+            for (int i = 64 * g; i < 64 * g + 64; ++i)
+                yr[i] = ora_e4m3_round(ldexp(ora_bf16_value(xr[i]), -e));
+        }
+        memcpy(yr + nope, xr + nope, 128);
+    }
+}
+
+void ora_kv_fp8_decode(int n, int D, const uint8_t* y, double* x)
+{
+    const int nope = D - 64, rb = D + 80;
+    for (int r = 0; r < n; ++r) {
+        const uint8_t* yr = y + (size_t)r * rb;
+        double* xr = x + (size_t)r * D;
+        for (int i = 0; i < nope; ++i) xr[i] = ldexp(ora_e4m3_value(yr[i]), (int)yr[D + 64 + i / 64] - 127);
+        for (int i = 0; i < 64; ++i) {
+            uint16_t h;
+            memcpy(&h, yr + nope + 2 * i, 2);
+            xr[nope + i] = ora_bf16_value(h);
+        }
+    }
+}
+
+/* ---- C13: MXFP4 operands of the Lightning Indexer ------------------------------------------------------
+ * [P2 "mHC、Muon、FP4：这些不是论文装饰"]: the indexer's QK path runs in FP4.  The pages print no format.
+ * Reading taken: the OCP Microscaling (MX) FP4 format -- blocks of 32 consecutive elements share a
+ * power-of-two scale 2^X stored as the byte X + 127 (E8M0); each element is an E2M1 code (sign, 2 exponent
+ * bits, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte, element 2i in the low nibble.
+ * Encoding follows the MX specification: X = floor(log2(max |x|)) - 2 (2 = the largest E2M1 exponent),
+ * clamped to [-127, 127] (X = -127 for an all-zero block); each x / 2^X rounds to the nearest E2M1 magnitude,
+ * ties to the even code, saturating at 6.  Scores are the canonical scores of A2 over the decoded values. */
+static const double ora_e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+static uint8_t ora_e2m1_round(double v)
+{
+    const double a = fabs(v);
+    int best = 0;
+    for (int k = 1; k < 8; ++k) {
+        const double dk = fabs(a - ora_e2m1_mag[k]), db = fabs(a - ora_e2m1_mag[best]);
+        if (dk < db || (dk == db && (k & 1) == 0)) best = k;
+    }
+    if (a >= 6.0) best = 7;
+    return (uint8_t)((v < 0.0 && best != 0 ? 8 : 0) | best);
+}
+
+void ora_mxfp4_encode(int n, int len, const uint16_t* x, uint8_t* codes, uint8_t* scales)
+{
+    for (int r = 0; r < n; ++r) {
+        const uint16_t* xr = x + (size_t)r * len;
+        uint8_t* cr = codes + (size_t)r * (len / 2);
+        uint8_t* sr = scales + (size_t)r * (len / 32);
+        memset(cr, 0, (size_t)len / 2);
+        for (int blk = 0; blk < len / 32; ++blk) {
+            double amax = 0.0;
+            for (int i = 32 * blk; i < 32 * blk + 32; ++i) {
+                const double a = fabs(ora_bf16_value(xr[i]));
+                if (a > amax) amax = a;
+            }
+            int X = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);                          /* amax in [2^(ex-1), 2^ex) */
+                X = (ex - 1) - 2;
+                if (X < -127) X = -127;
+                if (X > 127) X = 127;
+            }
+            sr[blk] = (uint8_t)(X + 127);
+            for (int i = 32 * blk; i < 32 * blk + 32; ++i) {
+                const uint8_t c = ora_e2m1_round(ldexp(ora_bf16_value(xr[i]), -X));
+                cr[i / 2] |= (uint8_t)(i & 1 ? c << 4 : c);
+            }
+        }
+    }
+}
+
+/* element i of an MXFP4 vector as (-1)^neg M 2^e */
+static void ora_mx_decode(const uint8_t* codes, const uint8_t* scales, int i, int* neg, uint32_t* M, int* e)
+{
+    const uint8_t c = (uint8_t)((codes[i / 2] >> (4 * (i & 1))) & 15);
+    const int k = c & 7, E = k >> 1, mb = k & 1;
+    *neg = c >> 3;
+    if (E == 0) { *M = (uint32_t)mb; *e = -1; }
+    else { *M = 2u + (uint32_t)mb; *e = E - 2; }
+    *e += (int)scales[i / 32] - 127;
+}
+
+double ora_mxfp4_value(const uint8_t* codes, const uint8_t* scales, int i)
+{
+    int neg, e;
+    uint32_t M;
+    ora_mx_decode(codes, scales, i, &neg, &M, &e);
+    return (neg ? -1.0 : 1.0) * ldexp((double)M, e);
+}
+
+/* exact sum_i a_i b_i of two MXFP4 vectors of n elements, rounded once to fp32 */
+float ora_exact_dot_mxfp4(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs, int n)
+{
+    ora_acc acc;
+    memset(&acc, 0, sizeof acc);
+    for (int i = 0; i < n; ++i) {
+        int na, nb, ea, eb;
+        uint32_t Ma, Mb;
+        ora_mx_decode(ac, as, i, &na, &Ma, &ea);
+        ora_mx_decode(bc, bs, i, &nb, &Mb, &eb);
+        ora_acc_add(&acc, na ^ nb, (uint64_t)Ma * Mb, ea + eb);
+    }
+    return ora_acc_to_f32(&acc);
+}
+
+/* Canonical scores (A2) over MXFP4 operands: q codes [B][Tq][HI][dI/2] and scales [B][Tq][HI][dI/32], k codes
+ * [B][Nc][dI/2] and scales [B][Nc][dI/32]; the rest as ora_index_scores. */
+void ora_index_scores_mxfp4(int B, int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0,
+                            const uint8_t* qc, const uint8_t* qs, const float* w_idx, const uint8_t* kc,
+                            const uint8_t* ks, float* S_out, int* n_vis_out)
+{
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < Tq; ++t) {
+            int nv = ora_n_visible(pos0 + t, L, m), j;
+            const size_t r = (size_t)b * Tq + t;
+            const float* w = w_idx + r * HI;
+            float* S = S_out + r * Nc;
+            if (nv > Nc) nv = Nc;
+            n_vis_out[r] = nv;
+            #pragma omp parallel for schedule(static)
+            for (j = 0; j < Nc; ++j) {
+                if (j >= nv) { S[j] = NAN; continue; }
+                float Sx = 0.0f;
+                const size_t kr = (size_t)b * Nc + j;
+                for (int h = 0; h < HI; ++h) {
+                    const size_t qr = r * HI + h;
+                    const float d = ora_exact_dot_mxfp4(qc + qr * (dI / 2), qs + qr * (dI / 32), kc + kr * (dI / 2),
+                                                        ks + kr * (dI / 32), dI);
+                    Sx = fmaf(w[h], d > 0.0f ? d : 0.0f, Sx);
+                }
+                S[j] = Sx;
+            }
+        }
+}

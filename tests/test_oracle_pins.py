@@ -648,3 +648,124 @@ def test_separate_values_single_row_and_linearity():
     same, _ = oracle.dense_attn(q, kv, L=24, mh=4, pos0=23, scale=0.3, v_h=kv)
     base, _ = oracle.dense_attn(q, kv, L=24, mh=4, pos0=23, scale=0.3)
     np.testing.assert_array_equal(same, base)
+
+
+# ---------------------------------------------------------------------------
+# FP8 storage of the non-RoPE KV dimensions (C12) and MXFP4 indexer operands (C13)
+# ---------------------------------------------------------------------------
+
+def _fp8_case(seed, n, D, scale):
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((n, D)) * scale * 2.0 ** g.integers(-6, 7, (n, 1))).astype(np.float32)
+    x[0, :64] = 0.0                                           # an all-zero group
+    x[1, 5] = 448.0 * 2.0 ** -10                              # a group whose maximum sits exactly on 448 * 2^e
+    return synth.to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("D", [128, 512])
+def test_kv_fp8_encode_matches_library_e4m3(D):
+    x = _fp8_case(3, 20, D, 0.05)
+    y = oracle.kv_fp8_encode(x)
+    assert y.shape == (20, D + 80) and oracle.kv_fp8_row_bytes(D) == D + 80
+    xv = _bf16_f64(x)
+    for r in range(x.shape[0]):
+        for g in range((D - 64) // 64):
+            amax = np.abs(xv[r, 64 * g:64 * g + 64]).max()
+            if amax == 0:
+                e = 0
+            else:                                             # smallest e with amax <= 448 * 2^e, in exact rationals
+                e = math.ceil(math.log2(amax / 448.0)) + 1
+                while Fraction(amax) <= Fraction(448) * Fraction(2) ** (e - 1):
+                    e -= 1
+            assert y[r, D + 64 + g] == e + 127
+            ref = torch.from_numpy(np.ldexp(xv[r, 64 * g:64 * g + 64], -e).astype(np.float32))
+            ref = ref.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(y[r, 64 * g:64 * g + 64], ref)
+        assert np.array_equal(y[r, D - 64:D + 64].view(np.uint16), x[r, D - 64:])        # RoPE dims untouched
+        assert (y[r, D + 64 + (D - 64) // 64:] == 0).all()
+    assert (y[0, D + 64] == 127) and (y[0, :64] == 0).all()
+
+
+@pytest.mark.parametrize("D", [128, 512])
+def test_kv_fp8_decode_and_round_trip(D):
+    x = _fp8_case(4, 16, D, 0.05)
+    y = oracle.kv_fp8_encode(x)
+    got = oracle.kv_fp8_decode(y, D)
+    # independent decode through the library's e4m3 type
+    codes = torch.from_numpy(np.ascontiguousarray(y[:, :D - 64])).view(torch.float8_e4m3fn).double().numpy()
+    scale = np.repeat(np.ldexp(1.0, y[:, D + 64:D + 64 + (D - 64) // 64].astype(np.int64) - 127), 64, axis=1)
+    np.testing.assert_array_equal(got[:, :D - 64], codes * scale)
+    xv = _bf16_f64(x)
+    np.testing.assert_array_equal(got[:, D - 64:], xv[:, D - 64:])
+    err = np.abs(got[:, :D - 64] - xv[:, :D - 64])
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(xv[:, :D - 64]), 2.0 ** -10 * scale))
+    # values already on the grid come back exactly
+    np.testing.assert_array_equal(oracle.kv_fp8_decode(oracle.kv_fp8_encode(synth.to_bf16_bits(got.astype(np.float32))),
+                                                       D), got)
+
+
+def _mx_reference(xv):
+    """The MX FP4 encoding from its specification, in plain numpy (independent of the oracle's C)."""
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    n = xv.shape[-1]
+    codes = np.zeros(xv.shape[:-1] + (n // 2,), np.uint8)
+    scales = np.zeros(xv.shape[:-1] + (n // 32,), np.uint8)
+    for idx in np.ndindex(xv.shape[:-1]):
+        for blk in range(n // 32):
+            v = xv[idx][32 * blk:32 * blk + 32]
+            amax = np.abs(v).max()
+            X = -127 if amax == 0 else int(np.clip(np.frexp(amax)[1] - 1 - 2, -127, 127))
+            scales[idx][blk] = X + 127
+            for i, t in enumerate(np.ldexp(v, -X)):
+                a = min(abs(t), 6.0)
+                d = np.abs(mags - a)
+                cand = np.flatnonzero(d == d.min())
+                k = int(cand[0]) if len(cand) == 1 else int(cand[cand % 2 == 0][0])
+                c = k | (8 if (t < 0 and k) else 0)
+                j = 32 * blk + i
+                codes[idx][j // 2] |= c << (4 * (j & 1))
+    return codes, scales
+
+
+def test_mxfp4_encode_matches_specification():
+    g = np.random.default_rng(5)
+    x = (g.standard_normal((6, 128)) * 2.0 ** g.integers(-20, 20, (6, 1))).astype(np.float32)
+    x[0, :32] = 0.0
+    # ties of E2M1 at scale 2^0 (amax 6): 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 2.5 -> 2, 5 -> 4, 3.5 -> 4
+    x[1, 32:64] = 0.0
+    x[1, 32:39] = [6.0, 0.25, 0.75, 1.25, 2.5, 5.0, -3.5]
+    xb = synth.to_bf16_bits(x)
+    codes, scales = oracle.mxfp4_encode(xb)
+    rc, rs = _mx_reference(_bf16_f64(xb))
+    assert np.array_equal(scales, rs) and np.array_equal(codes, rc)
+    vals = oracle.mxfp4_values(codes, scales)
+    np.testing.assert_array_equal(vals[1, 32:39], [6.0, 0.0, 1.0, 1.0, 2.0, 4.0, -4.0])
+    assert scales[0, 0] == 0 and (vals[0, :32] == 0).all()
+
+
+def test_mxfp4_exact_dot_vs_fraction_and_bf16_path():
+    g = np.random.default_rng(6)
+    for _ in range(20):
+        a = synth.to_bf16_bits((g.standard_normal(128) * 2.0 ** g.integers(-30, 30, 128)).astype(np.float32))
+        b_ = synth.to_bf16_bits((g.standard_normal(128) * 0.1).astype(np.float32))
+        ac, as_ = oracle.mxfp4_encode(a)
+        bc, bs = oracle.mxfp4_encode(b_)
+        av, bv = oracle.mxfp4_values(ac, as_), oracle.mxfp4_values(bc, bs)
+        want = frac_to_f32(sum((Fraction(float(p)) * Fraction(float(q)) for p, q in zip(av, bv)), Fraction(0)))
+        assert oracle.exact_dot_mxfp4(ac, as_, bc, bs) == np.float32(want)
+
+
+def test_mxfp4_scores_equal_bf16_scores_of_the_decoded_values():
+    # every MXFP4 value of a quantized bf16 vector is a bf16 value, so the canonical MXFP4 scores and selection
+    # must equal the bf16 path's on the decoded values
+    B, Tq, HI, dI, Nc, m, k = 1, 2, 8, 128, 300, 4, 40
+    q, w, kk, _ = synth.indexer_inputs(7, B, Tq, HI, dI, Nc, 0)
+    qc, qs = oracle.mxfp4_encode(q)
+    kc, ks = oracle.mxfp4_encode(kk)
+    L = Nc * m
+    idx, cnt, S, nv = oracle.index_topk_mxfp4(qc, qs, w, kc, ks, L, m, L - Tq, k)
+    qb = synth.to_bf16_bits(oracle.mxfp4_values(qc, qs).astype(np.float32))
+    kb = synth.to_bf16_bits(oracle.mxfp4_values(kc, ks).astype(np.float32))
+    assert np.array_equal(_bf16_f64(qb), oracle.mxfp4_values(qc, qs))
+    idx2, cnt2, S2, _ = oracle.index_topk(qb, w, kb, L, m, L - Tq, k)
+    assert np.array_equal(S, S2, equal_nan=True) and np.array_equal(idx, idx2) and np.array_equal(cnt, cnt2)
