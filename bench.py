@@ -19,7 +19,10 @@ The other workloads run as sub-lines of the same JSON object: "small_decode"
 microseconds), "batched_decode" (32 x 131,072 tokens, CSA layer with 64 heads,
 bf16 indexer, planted keys: queries/s and GB/s with its own roofline) and
 "compress_stack" (4 x 64K tokens of hidden 4096 compressed into both caches,
-then a 4-layer alternating decode stack).
+then a 4-layer alternating decode stack), "serving_decode" (the same 8 x 1M
+decode as a serving step over paged, variable-length caches with one token
+appended per sequence) and "lowp_decode" (the 8 x 1M decode over MXFP4
+indexer operands and FP8 KV entry rows).
 
 The metric's second part, indexer prefill TFLOP/s, is measured in the same run
 and reported under "indexer_prefill" (workload prefill_8k_on_256k: 8192 new
@@ -97,6 +100,8 @@ def main():
                     help="timed steps of the 32 x 128K batched CSA decode leg (0: skip)")
     ap.add_argument("--serving-steps", type=int, default=50,
                     help="timed steps of the paged, variable-length serving decode leg (0: skip)")
+    ap.add_argument("--lowp-steps", type=int, default=50,
+                    help="timed steps of the MXFP4-indexer / FP8-KV decode leg (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run two plain device copies of MIB MiB (a kernel of known "
                          "traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE by)")
@@ -241,6 +246,9 @@ def main():
     if args.serving_steps > 0:
         out["serving_decode"] = serving_leg(args, dev, cpu=not args.no_cpu_baseline)
         log("serving_decode done")
+    if args.lowp_steps > 0:
+        out["lowp_decode"] = lowp_leg(args, dev, cpu=not args.no_cpu_baseline)
+        log("lowp_decode done")
     if args.prefill_steps > 0:
         out["indexer_prefill"] = prefill_leg(args, dev, cpu=not args.no_cpu_baseline)
         log("indexer_prefill done")
@@ -994,6 +1002,129 @@ def serving_leg(args, dev, cpu=True):
                                 "csa_max_row_rel_err": rel(csa_out[0], o_csa), "hca_max_row_rel_err": rel(hca_out[0], o_hca),
                                 "tolerance": 2e-2, "oracle_s": round(time.perf_counter() - t0, 2)}
     del pools, win, dws, aws
+    torch.cuda.empty_cache()
+    return res
+
+
+def lowp_leg(args, dev, cpu=True):
+    """The 1M-context decode pair over the low-precision cache formats: MXFP4 indexer operands (E2M1 codes with
+    one E8M0 scale per 32: 68 bytes per key instead of 128) and FP8 KV entry rows (e4m3 non-RoPE dimensions in
+    groups of 64 with power-of-two scales, bf16 RoPE dimensions: D + 80 = 592 bytes instead of 1024) for both
+    the CSA and the HCA caches; the raw window stays bf16.  A step is csa_index_topk (MXFP4) + csa_sparse_attn
+    (FP8 entries) + hca_dense_attn (FP8 entries) over the 8 x 1M batch; the operands are encoded from bf16 by
+    the library's encoders before the timed region."""
+    import numpy as np
+    import torch
+
+    from compressed_sparse_kv_compressor_amd import binding as b
+    from compressed_sparse_kv_compressor_amd import synth
+    from compressed_sparse_kv_compressor_amd.configs import DECODE_B8_1M as cfg
+
+    B, H, D, L, HI, dI = cfg.B, cfg.H, cfg.D, cfg.L, cfg.HI, cfg.dI
+    Nc, Nh, W, topk, m, mh = cfg.Nc, cfg.Nh, cfg.W, cfg.topk, cfg.m, cfg.mh
+    g = synth.parallel_bits_to_device
+    copies = []
+    for c in range(args.copies):
+        qb = g(c, "lp_q_idx", (B, 1, HI, dI), dI ** -0.5, 0, dev)
+        kb = g(c, "lp_k_idx", (B, Nc, dI), dI ** -0.5, 0, dev)
+        qc, qs = b.csa_mxfp4_encode(qb)
+        kc, ks = b.csa_mxfp4_encode(kb)
+        kv = b.csa_kv_fp8_encode(g(c, "lp_kv", (B, Nc, D), D ** -0.5, 0, dev))
+        kvh = b.csa_kv_fp8_encode(g(c, "lp_kvh", (B, Nh, D), D ** -0.5, 0, dev))
+        torch.cuda.synchronize()
+        copies.append(dict(qb=qb if c == 0 else None, kb=kb if c == 0 else None, qc=qc, qs=qs, kc=kc, ks=ks, kv=kv,
+                           kvh=kvh, w=torch.from_numpy(synth.half_normal_f32(c, "lp_w_idx", (B, 1, HI),
+                                                                             HI ** -0.5)).to(dev),
+                           raw=g(c, "lp_raw", (B, W, D), D ** -0.5, 0, dev),
+                           csa_q=g(c, "lp_csa_q", (B, 1, H, D), D ** -0.5, 0, dev),
+                           hca_q=g(c, "lp_hca_q", (B, 1, H, D), D ** -0.5, 0, dev)))
+        if c:
+            del qb, kb
+    idx = torch.empty((B, 1, topk), dtype=torch.int32, device=dev)
+    csa_out = torch.empty((B, 1, H, D), dtype=torch.int16, device=dev)
+    hca_out = torch.empty_like(csa_out)
+    iws = b.workspace(b.lib.csa_index_topk_ex_ws_bytes(B, 1, HI, dI, Nc, topk, b.MXFP4, b._lay(None)), dev)
+    sws = b.workspace(b.lib.csa_sparse_attn_ws_bytes(B, 1, H, D, topk, W), dev)
+    dws = b.workspace(b.lib.hca_dense_attn_ws_bytes(B, 1, H, D, Nh), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i=0):
+        c = copies[i % len(copies)]
+        b.csa_index_topk(c["qc"], c["w"], c["kc"], b.MXFP4, L, m, L - 1, topk, idx, q_scale=c["qs"],
+                         k_scale=c["ks"], ws=iws, stream=stream)
+        b.csa_sparse_attn(c["csa_q"], c["kv"], idx, c["raw"], L - W, L - 1, W, cfg.scale, csa_out, ws=sws,
+                          stream=stream, kv_format=b.KV_FP8)
+        b.hca_dense_attn(c["hca_q"], c["kvh"], L, mh, L - 1, cfg.scale, hca_out, ws=dws, stream=stream,
+                         kv_format=b.KV_FP8)
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    n = args.lowp_steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    b.prof_reset()
+    b.prof_only(None)
+    b.prof_enable(True)
+    for i in range(min(n, 30)):
+        step(i)
+    torch.cuda.synchronize()
+    b.prof_enable(False)
+    kern = {}
+    for name in KERNELS:
+        t, k = b.prof_read(name)
+        if k:
+            kern[name] = round(t / k * 1000.0, 2)
+    b.prof_reset()
+    key_b = dI // 2 + dI // 32
+    score_bytes = B * Nc * key_b + B * HI * key_b + B * HI * 4
+    step_bytes = (score_bytes + B * topk * (D + 80) + B * W * D * 2 + 2 * B * H * D * 2 + B * Nh * (D + 80)
+                  + 2 * B * H * D * 2)
+    res = {"workload": "decode_b8_1m_mxfp4_fp8kv", "B": B, "L": L, "H": H, "D": D, "topk": topk, "W": W,
+           "idx_format": "mxfp4 (e2m1 + e8m0 per 32)", "kv_format": "fp8 rows (e4m3 x 448 dims + bf16 rope 64)",
+           "steps": n, "ms_per_step": round(ms, 4), "value": round(B / (ms * 1e-3), 1), "unit": "queries/s",
+           "step_algorithmic_bytes": step_bytes, "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+           "kernel_us_breakdown": kern}
+    if "k_score" in kern:
+        a = score_bytes / (kern["k_score"] * 1e-6) / 1e9
+        res["k_score_roofline"] = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                   "frac": round(a / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": score_bytes}
+    if cpu:
+        import oracle
+        t0 = time.perf_counter()
+        c = copies[(min(n, 30) - 1) % len(copies)]            # the copy the last profiled step used
+        u8 = lambda t: t.cpu().numpy()
+        u16 = lambda t: t.cpu().numpy().view(np.uint16)
+        want, _, _, _ = oracle.index_topk_mxfp4(u8(c["qc"][0:1]), u8(c["qs"][0:1]), u8(c["w"][0:1]),
+                                                u8(c["kc"][0:1]), u8(c["ks"][0:1]), L, m, L - 1, topk)
+        sel = u8(c["kv"][0].index_select(0, torch.from_numpy(want[0, 0].astype(np.int64)).to(dev)))
+        dec = synth.to_bf16_bits(oracle.kv_fp8_decode(sel, D).astype(np.float32))[None]
+        o_csa, _ = oracle.sparse_attn(u16(c["csa_q"][0:1]), dec, np.arange(topk, dtype=np.int32).reshape(1, 1, topk),
+                                      u16(c["raw"][0:1]), L - W, L - 1, W, cfg.scale)
+        dech = synth.to_bf16_bits(oracle.kv_fp8_decode(u8(c["kvh"][0]), D).astype(np.float32))[None]
+        o_hca, _ = oracle.dense_attn(u16(c["hca_q"][0:1]), dech, L, mh, L - 1, cfg.scale)
+
+        def rel(got, want_):
+            gq = (u16(got).astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(-1, D)
+            o = want_.reshape(-1, D)
+            return float((np.abs(gq - o).max(1) / np.abs(o).max(1)).max())
+        samp = {"sequence": 0, "topk_bit_exact": bool(np.array_equal(idx[0, 0].cpu().numpy(), want[0, 0])),
+                "csa_max_row_rel_err": rel(csa_out[0], o_csa), "hca_max_row_rel_err": rel(hca_out[0], o_hca),
+                "tolerance": 2e-2}
+        c0 = copies[0]
+        exact, _, _, _ = oracle.index_topk(u16(c0["qb"][0:1]), u8(c0["w"][0:1]), u16(c0["kb"][0:1]), L, m, L - 1,
+                                           topk)
+        got0, _, _, _ = oracle.index_topk_mxfp4(u8(c0["qc"][0:1]), u8(c0["qs"][0:1]), u8(c0["w"][0:1]),
+                                                u8(c0["kc"][0:1]), u8(c0["ks"][0:1]), L, m, L - 1, topk)
+        samp["mxfp4_recall_of_bf16_topk"] = round(len(set(got0[0, 0]) & set(exact[0, 0])) / topk, 4)
+        samp["oracle_s"] = round(time.perf_counter() - t0, 2)
+        res["parity_sample"] = samp
+    del copies, iws, sws, dws
     torch.cuda.empty_cache()
     return res
 

@@ -17,6 +17,9 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 BF16 = 0
 E4M3 = 1
+MXFP4 = 2
+KV_BF16 = 0
+KV_FP8 = 1
 
 
 class CsaError(RuntimeError):
@@ -42,9 +45,11 @@ def _load():
         "csa_index_topk_ws_bytes": ([I, I, I, I, I, I, I], Z),
         "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, Z, P], I),
         "csa_index_topk_ex_ws_bytes": ([I, I, I, I, I, I, I, P], Z),
-        "csa_index_topk_ex": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, P, Z, P], I),
-        "csa_sparse_attn_ex": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P, P, Z, P], I),
-        "hca_dense_attn_ex": ([P, P, P, I, I, I, I, I, LL, I, LL, F, P, P, P, P, P, Z, P], I),
+        "csa_index_topk_ex": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, P, P, P, Z, P], I),
+        "csa_sparse_attn_ex": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, LL, LL, I, F, P, P, I, P, P, P, Z, P], I),
+        "hca_dense_attn_ex": ([P, P, P, I, I, I, I, I, LL, I, LL, F, P, P, I, P, P, P, Z, P], I),
+        "csa_kv_fp8_encode": ([P, LL, I, P, P], I),
+        "csa_mxfp4_encode": ([P, LL, I, P, P, P], I),
         "csa_sparse_attn_ws_bytes": ([I, I, I, I, I, I], Z),
         "csa_sparse_attn": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P, Z, P], I),
         "csa_sparse_attn_noalloc": ([P, P, P, P, I, I, I, I, I, I, I, LL, LL, I, F, P, P, P, P], I),
@@ -73,7 +78,7 @@ EXPORTED = ("csa_abi_version", "csa_status_str", "csa_last_error", "csa_compress
             "csa_index_topk_ws_bytes", "csa_index_topk", "csa_sparse_attn_ws_bytes", "csa_sparse_attn",
             "csa_sparse_attn_noalloc", "csa_append_state_bytes", "csa_decode_append_ws_bytes", "csa_decode_append",
             "csa_index_topk_ex_ws_bytes", "csa_index_topk_ex", "csa_sparse_attn_ex",
-            "hca_dense_attn_ex",
+            "hca_dense_attn_ex", "csa_kv_fp8_encode", "csa_mxfp4_encode",
             "hca_dense_attn_ws_bytes", "hca_dense_attn", "csa_hca_decode_ws_bytes", "csa_hca_decode",
             "csa_rope", "csa_debug_fp8_to_bf16", "csa_prof_enable", "csa_prof_reset", "csa_prof_read",
             "csa_prof_only")
@@ -117,6 +122,7 @@ class DecodeArgs(ctypes.Structure):
         ("hca_q", ctypes.c_void_p), ("kv_h", ctypes.c_void_p), ("mh", ctypes.c_int),
         ("hca_out", ctypes.c_void_p), ("hca_lse", ctypes.c_void_p), ("hca_sink", ctypes.c_void_p),
         ("layout", ctypes.POINTER(CacheLayout)),
+        ("q_idx_scale", ctypes.c_void_p), ("k_idx_scale", ctypes.c_void_p),
     ]
 
 
@@ -192,26 +198,30 @@ def csa_decode_append(hidden, w_kv, w_ik, w_gate, b_slot, m: int, w_kv_h, w_gate
 
 
 def csa_index_topk(q_idx, w_idx, k_idx, dtype: int, L: int, m: int, pos0: int, topk: int, idx_out, cnt_out=None,
-                   ws=None, stream=None, score_out=None, layout=None, Nc=None):
+                   ws=None, stream=None, score_out=None, layout=None, Nc=None, q_scale=None, k_scale=None):
     """layout (make_layout): variable-length batch and/or paged keys (k_idx is then the pool and Nc = ceil(L/m)
-    unless given)."""
+    unless given).  dtype MXFP4: q_idx / k_idx are the E2M1 codes (last dim dI/2) and q_scale / k_scale their
+    E8M0 scales (last dim dI/32)."""
     B, Tq, HI, dI = q_idx.shape
+    if dtype == MXFP4:
+        dI *= 2
     if Nc is None:
         Nc = k_idx.shape[1] if (layout is None or not layout.block_table) else -(-L // m)
-    if layout is None:
+    ex = layout is not None or dtype == MXFP4
+    if not ex:
         need = lib.csa_index_topk_ws_bytes(B, Tq, HI, dI, Nc, topk, dtype)
     else:
         need = lib.csa_index_topk_ex_ws_bytes(B, Tq, HI, dI, Nc, topk, dtype, _lay(layout))
     if ws is None:
         ws = workspace(need, q_idx.device)
-    if layout is None:
+    if not ex:
         _check(lib.csa_index_topk(_p(q_idx), _p(w_idx), _p(k_idx), dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,
                                   _p(idx_out), _p(cnt_out), _p(score_out), _p(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream)))
     else:
         _check(lib.csa_index_topk_ex(_p(q_idx), _p(w_idx), _p(k_idx), dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,
-                                     _p(idx_out), _p(cnt_out), _p(score_out), _lay(layout), _p(ws),
-                                     0 if ws is None else ws.numel(), _stream(stream)))
+                                     _p(idx_out), _p(cnt_out), _p(score_out), _lay(layout), _p(q_scale), _p(k_scale),
+                                     _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def _sink(sink, H: int):
@@ -222,9 +232,10 @@ def _sink(sink, H: int):
 
 
 def csa_sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, out, lse_out=None, ws=None,
-                    stream=None, sink=None, v=None, v_raw=None, layout=None, m: int = 1, Nc=None):
+                    stream=None, sink=None, v=None, v_raw=None, layout=None, m: int = 1, Nc=None, kv_format=KV_BF16):
     """v, v_raw: separate values (or None); layout (make_layout): variable-length batch and/or paged entries
-    (kv and v are then pools of ratio m; Nc = the entries per sequence the idx refer to)."""
+    (kv and v are then pools of ratio m; Nc = the entries per sequence the idx refer to); kv_format KV_FP8: kv
+    (and v) rows in the FP8 format (csa_kv_fp8_encode)."""
     B, Tq, H, D = q.shape
     if Nc is None:
         Nc = kv.shape[1] if kv is not None else 0
@@ -233,13 +244,13 @@ def csa_sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: flo
     need = lib.csa_sparse_attn_ws_bytes(B, Tq, H, D, topk, W)
     if ws is None:
         ws = workspace(need, q.device)
-    if layout is None and v is None and v_raw is None:
+    if layout is None and v is None and v_raw is None and kv_format == KV_BF16:
         _check(lib.csa_sparse_attn(_p(q), _p(kv), _p(idx), _p(kv_raw), B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W,
                                    float(scale), _sink(sink, H), _p(out), _p(lse_out), _p(ws),
                                    0 if ws is None else ws.numel(), _stream(stream)))
     else:
         _check(lib.csa_sparse_attn_ex(_p(q), _p(kv), _p(v), _p(idx), _p(kv_raw), _p(v_raw), B, Tq, H, D, Nc, m, topk,
-                                      Lr, raw0, pos0, W, float(scale), _sink(sink, H), _lay(layout), _p(out),
+                                      Lr, raw0, pos0, W, float(scale), _sink(sink, H), _lay(layout), kv_format, _p(out),
                                       _p(lse_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
@@ -255,37 +266,38 @@ def csa_sparse_attn_noalloc(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, sc
 
 
 def hca_dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, out, lse_out=None, ws=None, stream=None,
-                   sink=None, v_h=None, layout=None):
+                   sink=None, v_h=None, layout=None, kv_format=KV_BF16):
     """v_h: separate values (or None); layout (make_layout): variable-length batch (L = capacity) and/or a
-    paged pool kv_h of ratio mh."""
+    paged pool kv_h of ratio mh; kv_format KV_FP8: FP8 entry rows."""
     B, Tq, H, D = q.shape
     Nh = -(-L // mh) if (layout is not None and layout.block_table) else kv_h.shape[1]
     need = lib.hca_dense_attn_ws_bytes(B, Tq, H, D, Nh)
     if ws is None:
         ws = workspace(need, q.device)
-    if layout is None and v_h is None:
+    if layout is None and v_h is None and kv_format == KV_BF16:
         _check(lib.hca_dense_attn(_p(q), _p(kv_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale), _sink(sink, H),
                                   _p(out), _p(lse_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     else:
         _check(lib.hca_dense_attn_ex(_p(q), _p(kv_h), _p(v_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale),
-                                     _sink(sink, H), _lay(layout), _p(out), _p(lse_out), _p(ws),
+                                     _sink(sink, H), _lay(layout), kv_format, _p(out), _p(lse_out), _p(ws),
                                      0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def make_decode_args(*, L, scale, csa_q, q_idx, w_idx, k_idx, kv, kv_raw, idx_dtype, m, topk, W, csa_out,
                      hca_q, kv_h, mh, hca_out, csa_lse=None, hca_lse=None, idx_out=None, csa_sink=None,
-                     hca_sink=None, layout=None) -> DecodeArgs:
+                     hca_sink=None, layout=None, q_idx_scale=None, k_idx_scale=None) -> DecodeArgs:
     B, H, D = csa_q.shape[0], csa_q.shape[-2], csa_q.shape[-1]
-    HI, dI = q_idx.shape[-2], q_idx.shape[-1]
+    HI, dI = q_idx.shape[-2], q_idx.shape[-1] * (2 if idx_dtype == MXFP4 else 1)
     args = DecodeArgs(B=B, L=L, H=H, D=D, scale=float(scale), csa_q=_p(csa_q), q_idx=_p(q_idx), w_idx=_p(w_idx),
                       k_idx=_p(k_idx), kv=_p(kv), kv_raw=_p(kv_raw), idx_dtype=idx_dtype, HI=HI, dI=dI, m=m,
                       topk=topk, W=W, csa_out=_p(csa_out), csa_lse=_p(csa_lse), idx_out=_p(idx_out),
                       csa_sink=_sink(csa_sink, H), hca_q=_p(hca_q), kv_h=_p(kv_h), mh=mh, hca_out=_p(hca_out),
                       hca_lse=_p(hca_lse), hca_sink=_sink(hca_sink, hca_q.shape[-2]),
-                      layout=None if layout is None else ctypes.pointer(layout))
+                      layout=None if layout is None else ctypes.pointer(layout), q_idx_scale=_p(q_idx_scale),
+                      k_idx_scale=_p(k_idx_scale))
     # the struct holds bare device addresses: keep every tensor they point into alive as long as the struct
     args._keep = (csa_q, q_idx, w_idx, k_idx, kv, kv_raw, csa_out, csa_lse, idx_out, csa_sink, hca_q, kv_h, hca_out,
-                  hca_lse, hca_sink, layout)
+                  hca_lse, hca_sink, layout, q_idx_scale, k_idx_scale)
     return args
 
 
@@ -311,6 +323,26 @@ def csa_rope(x, pos, out=None, rd: int = 64, theta: float = 10000.0, inverse: bo
     _check(lib.csa_rope(_p(x), _p(out), _p(pos), n, D, rd, n // pos.numel(), float(theta), 1 if inverse else 0,
                         _stream(stream)))
     return out
+
+
+def csa_kv_fp8_encode(x, out=None, stream=None):
+    """bf16 KV rows x[..., D] (int16 bits) -> uint8 FP8 rows [..., D + 80]."""
+    D = x.shape[-1]
+    if out is None:
+        out = torch.empty(x.shape[:-1] + (D + 80,), dtype=torch.uint8, device=x.device)
+    _check(lib.csa_kv_fp8_encode(_p(x), x.numel() // D, D, _p(out), _stream(stream)))
+    return out
+
+
+def csa_mxfp4_encode(x, codes=None, scales=None, stream=None):
+    """bf16 vectors x[..., n] (int16 bits) -> (codes uint8 [..., n/2], scales uint8 [..., n/32]) in MXFP4."""
+    n = x.shape[-1]
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (n // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (n // 32,), dtype=torch.uint8, device=x.device)
+    _check(lib.csa_mxfp4_encode(_p(x), x.numel() // n, n, _p(codes), _p(scales), _stream(stream)))
+    return codes, scales
 
 
 def csa_debug_fp8_to_bf16(inp, out, stream=None):

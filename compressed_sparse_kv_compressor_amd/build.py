@@ -12,7 +12,7 @@ OUT = os.path.join(HERE, "libcsa.so")
 OBJ = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["abi.hip", "index_topk.hip", "prefill_index.hip", "attn.hip", "attn128.hip", "compress.hip", "rope.hip",
-           "append.hip"]
+           "append.hip", "lowp.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # keep the compiler from emitting packed-fp32 VALU ops
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

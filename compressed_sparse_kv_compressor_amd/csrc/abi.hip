@@ -147,7 +147,8 @@ int validate_index(const char* fn, const void* q_idx, const float* w_idx, const 
     REQ_PTR(k_idx);
     REQ_PTR(idx_out);
     OPT_PTR(cnt_out);
-    REQ(dtype == CSA_BF16 || dtype == CSA_E4M3, CSA_ERR_DTYPE, "%s: dtype %d unknown", fn, dtype);
+    REQ(dtype == CSA_BF16 || dtype == CSA_E4M3 || dtype == CSA_MXFP4, CSA_ERR_DTYPE, "%s: dtype %d unknown", fn,
+        dtype);
     REQ(B >= 1 && Tq >= 1 && L >= 1 && m >= 1 && pos0 >= 0, CSA_ERR_SHAPE,
         "%s: need B, Tq, L, m >= 1 and pos0 >= 0 (B=%d Tq=%d L=%lld m=%d pos0=%lld)", fn, B, Tq, L, m, pos0);
     REQ((long long)Nc == (L + m - 1) / m, CSA_ERR_SHAPE, "%s: Nc=%d but ceil(L/m)=%lld", fn, Nc, (L + m - 1) / m);
@@ -409,16 +410,20 @@ size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, 
 size_t csa_index_topk_ex_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype,
                                   const csa_cache_layout_t* layout) {
     if (B < 1 || Tq < 1 || Nc < 1 || HI < 1 || dI < 1 || topk < 1) return 0;
-    return csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk, plain_layout(layout));
+    return csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk, plain_layout(layout) && dtype != CSA_MXFP4);
 }
 
 static int index_topk_impl(const char* fn, const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B,
                            int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
                            int32_t* idx_out, int32_t* cnt_out, float* score_out, const csa_cache_layout_t* layout,
-                           void* ws, size_t ws_bytes, void* stream) {
+                           const uint8_t* q_scale, const uint8_t* k_scale, void* ws, size_t ws_bytes, void* stream) {
     csa_host::g_err[0] = 0;
     int rc = validate_index(fn, q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out, cnt_out);
     if (rc) return rc;
+    if (dtype == CSA_MXFP4) {
+        REQ(q_scale && k_scale, CSA_ERR_NULL, "%s: MXFP4 operands need q_scale and k_scale", fn);
+        REQ(dI == 128, CSA_ERR_UNSUPPORTED, "%s: MXFP4 indexer rows of dI = 128 supported (got %d)", fn, dI);
+    }
     OPT_PTR(score_out);
     csa_host::CacheLayout lay;
     rc = read_layout(fn, layout, m, Nc, 0, 0, &lay);
@@ -426,21 +431,25 @@ static int index_topk_impl(const char* fn, const void* q_idx, const float* w_idx
     rc = check_ws(fn, ws, ws_bytes, csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk, plain_layout(layout)));
     if (rc) return rc;
     return csa_host::index_topk_launch(q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out,
-                                       cnt_out, score_out, lay, ws, (hipStream_t)stream);
+                                       cnt_out, score_out, lay, q_scale, k_scale, ws, (hipStream_t)stream);
 }
 
 int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq, int HI, int dI,
                    int Nc, long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
                    float* score_out, void* ws, size_t ws_bytes, void* stream) {
+    if (dtype == CSA_MXFP4)
+        return fail(CSA_ERR_DTYPE, "csa_index_topk: MXFP4 operands carry scales: call csa_index_topk_ex");
     return index_topk_impl("csa_index_topk", q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk, idx_out,
-                           cnt_out, score_out, nullptr, ws, ws_bytes, stream);
+                           cnt_out, score_out, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 int csa_index_topk_ex(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq, int HI,
                       int dI, int Nc, long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
-                      float* score_out, const csa_cache_layout_t* layout, void* ws, size_t ws_bytes, void* stream) {
+                      float* score_out, const csa_cache_layout_t* layout, const void* q_scale, const void* k_scale,
+                      void* ws, size_t ws_bytes, void* stream) {
     return index_topk_impl("csa_index_topk_ex", q_idx, w_idx, k_idx, dtype, B, Tq, HI, dI, Nc, L, m, pos0, topk,
-                           idx_out, cnt_out, score_out, layout, ws, ws_bytes, stream);
+                           idx_out, cnt_out, score_out, layout, (const uint8_t*)q_scale, (const uint8_t*)k_scale, ws,
+                           ws_bytes, stream);
 }
 
 size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W) {
@@ -451,8 +460,8 @@ size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W) {
 static int sparse_impl(const char* fn, const void* q, const void* kv, const void* v, const int32_t* idx,
                        const void* kv_raw, const void* v_raw, int B, int Tq, int H, int D, int Nc, int m, int topk,
                        int Lr, long long raw0, long long pos0, int W, float scale, const float* sink,
-                       const csa_cache_layout_t* layout, void* out, float* lse_out, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out, void* ws,
+                       size_t ws_bytes, void* stream) {
     csa_host::g_err[0] = 0;
     const bool varlen = layout && layout->seq_lens;
     int rc = validate_sparse(fn, q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse_out,
@@ -471,6 +480,8 @@ static int sparse_impl(const char* fn, const void* q, const void* kv, const void
     r.v = v;
     r.v_raw = W > 0 ? v_raw : nullptr;
     r.pm = csa_host::page_map(lay, m);
+    REQ(kv_format == CSA_KV_BF16 || kv_format == CSA_KV_FP8, CSA_ERR_DTYPE, "%s: kv_format %d unknown", fn, kv_format);
+    r.kv_fp8 = kv_format == CSA_KV_FP8;
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
                                  "k_attn_sparse");
 }
@@ -479,15 +490,15 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
                     int Nc, int topk, int Lr, long long raw0, long long pos0, int W, float scale, const float* sink,
                     void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
     return sparse_impl("csa_sparse_attn", q, kv, nullptr, idx, kv_raw, nullptr, B, Tq, H, D, Nc, 1, topk, Lr, raw0, pos0,
-                       W, scale, sink, nullptr, out, lse_out, ws, ws_bytes, stream);
+                       W, scale, sink, nullptr, CSA_KV_BF16, out, lse_out, ws, ws_bytes, stream);
 }
 
 int csa_sparse_attn_ex(const void* q, const void* kv, const void* v, const int32_t* idx, const void* kv_raw,
                        const void* v_raw, int B, int Tq, int H, int D, int Nc, int m, int topk, int Lr, long long raw0,
                        long long pos0, int W, float scale, const float* sink, const csa_cache_layout_t* layout,
-                       void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+                       int kv_format, void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
     return sparse_impl("csa_sparse_attn_ex", q, kv, v, idx, kv_raw, v_raw, B, Tq, H, D, Nc, m, topk, Lr, raw0, pos0, W,
-                       scale, sink, layout, out, lse_out, ws, ws_bytes, stream);
+                       scale, sink, layout, kv_format, out, lse_out, ws, ws_bytes, stream);
 }
 
 // As csa_sparse_attn, with the split partials in the library's static scratch instead of a workspace.
@@ -519,8 +530,8 @@ size_t hca_dense_attn_ws_bytes(int B, int Tq, int H, int D, int Nh) {
 
 static int dense_impl(const char* fn, const void* q, const void* kv_h, const void* v_h, int B, int Tq, int H, int D,
                       int Nh, long long L, int mh, long long pos0, float scale, const float* sink,
-                      const csa_cache_layout_t* layout, void* out, float* lse_out, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out, void* ws,
+                      size_t ws_bytes, void* stream) {
     csa_host::g_err[0] = 0;
     int rc = validate_dense(fn, q, kv_h, B, Tq, H, D, Nh, L, mh, pos0, scale, out, lse_out);
     if (rc) return rc;
@@ -534,6 +545,8 @@ static int dense_impl(const char* fn, const void* q, const void* kv_h, const voi
     r.seq_lens = lay.seq_lens;
     r.v = v_h;
     r.pm = csa_host::page_map(lay, mh);
+    REQ(kv_format == CSA_KV_BF16 || kv_format == CSA_KV_FP8, CSA_ERR_DTYPE, "%s: kv_format %d unknown", fn, kv_format);
+    r.kv_fp8 = kv_format == CSA_KV_FP8;
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
                                  "k_attn_dense");
 }
@@ -541,16 +554,16 @@ static int dense_impl(const char* fn, const void* q, const void* kv_h, const voi
 int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D, int Nh, long long L, int mh,
                    long long pos0, float scale, const float* sink, void* out, float* lse_out, void* ws,
                    size_t ws_bytes, void* stream) {
-    return dense_impl("hca_dense_attn", q, kv_h, nullptr, B, Tq, H, D, Nh, L, mh, pos0, scale, sink, nullptr, out,
-                      lse_out, ws, ws_bytes, stream);
+    return dense_impl("hca_dense_attn", q, kv_h, nullptr, B, Tq, H, D, Nh, L, mh, pos0, scale, sink, nullptr,
+                      CSA_KV_BF16, out, lse_out, ws, ws_bytes, stream);
 }
 
 int hca_dense_attn_ex(const void* q, const void* kv_h, const void* v_h, int B, int Tq, int H, int D, int Nh,
                       long long L, int mh, long long pos0, float scale, const float* sink,
-                      const csa_cache_layout_t* layout, void* out, float* lse_out, void* ws, size_t ws_bytes,
-                      void* stream) {
-    return dense_impl("hca_dense_attn_ex", q, kv_h, v_h, B, Tq, H, D, Nh, L, mh, pos0, scale, sink, layout, out,
-                      lse_out, ws, ws_bytes, stream);
+                      const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+    return dense_impl("hca_dense_attn_ex", q, kv_h, v_h, B, Tq, H, D, Nh, L, mh, pos0, scale, sink, layout, kv_format,
+                      out, lse_out, ws, ws_bytes, stream);
 }
 
 // Fused decode: workspace = [idx (if not caller-owned)] [index_topk ws] [attention ws (max of both layers)]
@@ -561,7 +574,7 @@ size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a) {
     const int Nc = (int)((a->L + a->m - 1) / a->m), Nh = (int)((a->L + a->mh - 1) / a->mh);
     size_t s = a->idx_out ? 0 : align256((size_t)a->B * a->topk * 4);
     s += align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk,
-                                                plain_layout(a->layout)));
+                                                plain_layout(a->layout) && a->idx_dtype != CSA_MXFP4));
     s += align256(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 1, a->topk, a->W));
     s += csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 0, Nh, 0);
     return s;
@@ -577,6 +590,10 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     int rc = validate_index(fn, a->q_idx, a->w_idx, a->k_idx, a->idx_dtype, a->B, 1, a->HI, a->dI, Nc, a->L, a->m, p,
                             a->topk, a->idx_out ? a->idx_out : (const int32_t*)16, nullptr);
     if (rc) return rc;
+    if (a->idx_dtype == CSA_MXFP4) {
+        REQ(a->q_idx_scale && a->k_idx_scale, CSA_ERR_NULL, "%s: MXFP4 indexer operands need their scales", fn);
+        REQ(a->dI == 128, CSA_ERR_UNSUPPORTED, "%s: MXFP4 indexer rows of dI = 128 supported", fn);
+    }
     rc = validate_sparse(fn, a->csa_q, a->kv, (const int32_t*)16, a->kv_raw, a->B, 1, a->H, a->D, Nc, a->topk, a->W,
                          a->L - a->W, p, a->W, a->scale, a->csa_out, a->csa_lse);
     if (rc) return rc;
@@ -596,9 +613,10 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
         w += align256((size_t)a->B * a->topk * 4);
     }
     const size_t iws = align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk,
-                                                              plain_layout(a->layout)));
+                                                              plain_layout(a->layout) && a->idx_dtype != CSA_MXFP4));
     rc = csa_host::index_topk_launch(a->q_idx, a->w_idx, a->k_idx, a->idx_dtype, a->B, 1, a->HI, a->dI, Nc, a->L, a->m,
-                                     p, a->topk, idx, nullptr, nullptr, lay, w, st);
+                                     p, a->topk, idx, nullptr, nullptr, lay, (const uint8_t*)a->q_idx_scale,
+                                     (const uint8_t*)a->k_idx_scale, w, st);
     if (rc) return rc;
     w += iws;
     const size_t aws = ws_bytes - (size_t)(w - (char*)ws);
@@ -633,6 +651,30 @@ int csa_rope(const void* x, void* y, const long long* pos, long long n, int D, i
     REQ(pos != nullptr, CSA_ERR_NULL, "%s: pos is NULL", fn);
     REQ(((uintptr_t)pos & 7u) == 0, CSA_ERR_ALIGN, "%s: pos is not 8-byte aligned", fn);
     return csa_host::rope_launch(x, y, pos, n, D, rd, group, theta, inverse, (hipStream_t)stream);
+}
+
+// FP8 KV rows and MXFP4 indexer operands (see include/csa.h).
+int csa_kv_fp8_encode(const void* x, long long n, int D, void* y, void* stream) {
+    const char* fn = "csa_kv_fp8_encode";
+    csa_host::g_err[0] = 0;
+    REQ(n >= 0, CSA_ERR_SHAPE, "%s: n must be >= 0", fn);
+    REQ(D == 128 || D == 512, CSA_ERR_UNSUPPORTED, "%s: D=%d (supported 128, 512)", fn, D);
+    if (n == 0) return CSA_OK;
+    REQ_PTR(x);
+    REQ_PTR(y);
+    return csa_host::kv_fp8_launch(x, n, D, y, (hipStream_t)stream);
+}
+
+int csa_mxfp4_encode(const void* x, long long n, int len, void* codes, void* scales, void* stream) {
+    const char* fn = "csa_mxfp4_encode";
+    csa_host::g_err[0] = 0;
+    REQ(n >= 0 && len >= 32 && len % 32 == 0 && len <= 4096, CSA_ERR_SHAPE,
+        "%s: need n >= 0 and len a multiple of 32 in [32, 4096]", fn);
+    if (n == 0) return CSA_OK;
+    REQ_PTR(x);
+    REQ_PTR(codes);
+    REQ(scales != nullptr, CSA_ERR_NULL, "%s: scales is NULL", fn);
+    return csa_host::mxfp4_launch(x, n, len, codes, scales, (hipStream_t)stream);
 }
 
 // Diagnostic: fp8 (OCP e4m3) -> bf16 conversion exactly as the indexer kernel does it.

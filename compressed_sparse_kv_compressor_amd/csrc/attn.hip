@@ -32,25 +32,47 @@ using namespace csa;
 using namespace csa_attn;
 
 constexpr int TPB = 256;
-// Number of rows of query (b, t) and pointer to row r's key (value = false) or value (value = true) data
-// (nullptr = masked row).  Entries go through the page map; keys and values are one row unless separate
+// Number of rows of query (b, t) and the byte address of row r's key (value = false) or value (value = true)
+// data (nullptr = masked row); `ent` is set for compressed entries (which may be FP8 rows), cleared for raw
+// window rows (always bf16).  Entries go through the page map; keys and values are one row unless separate
 // value arrays are given.
 struct RowSet {
     int n;
     int b, bt;
     long long w0, raw0;
-    __device__ const uint16_t* row(const Rows& R, int r, int D, bool value) const {
-        const uint16_t* ent = value && R.v ? R.v : R.kv;
-        if (R.mode == 0) return ent + entry_row(R.pm, b, R.N, r) * D;
+    __device__ const char* row(const Rows& R, int r, int D, bool value, bool& ent) const {
+        const size_t eb = R.kv_fp8 ? (size_t)D + 80 : (size_t)D * 2;
+        const char* base = (const char*)(value && R.v ? R.v : R.kv);
+        ent = true;
+        if (R.mode == 0) return base + entry_row(R.pm, b, R.N, r) * eb;
         if (r < R.topk) {
             const int j = R.idx[(size_t)bt * R.topk + r];
-            return j >= 0 ? ent + entry_row(R.pm, b, R.N, j) * D : nullptr;
+            return j >= 0 ? base + entry_row(R.pm, b, R.N, j) * eb : nullptr;
         }
+        ent = false;
         const long long u = w0 + (r - R.topk);
         const uint16_t* raw = value && R.v_raw ? R.v_raw : R.kv_raw;
-        return raw + ((size_t)b * R.Lr + (size_t)(u - raw0)) * D;
+        return (const char*)(raw + ((size_t)b * R.Lr + (size_t)(u - raw0)) * D);
     }
 };
+
+// 16-byte chunk cc (dimensions 8 cc .. 8 cc + 7) of a row as bf16: from a bf16 row, or from an FP8 row (codes of
+// the non-RoPE dimensions times their group's power-of-two scale, exact in bf16; the RoPE dimensions stored
+// as bf16 after the codes).
+template <int D>
+__device__ __forceinline__ u32x4_t row_chunk(const char* p, int cc, bool fp8) {
+    if (!fp8) return *(const u32x4_t*)(p + cc * 16);
+    constexpr int NOPE = D - 64;
+    if (cc >= NOPE / 8) return *(const u32x4_t*)(p + NOPE + (cc - NOPE / 8) * 16);
+    const uint2 w = *(const uint2*)(p + cc * 8);
+    const uint32_t s = (uint32_t)(uint8_t)p[D + 64 + (cc * 8) / 64];
+    const float scale = __uint_as_float((s < 1u ? 1u : s) << 23);       // 2^(s - 127)
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+#define CSA_FP8_PAIR(X, HI) __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(X, scale, HI))
+    return u32x4_t{CSA_FP8_PAIR(w.x, false), CSA_FP8_PAIR(w.x, true), CSA_FP8_PAIR(w.y, false),
+                   CSA_FP8_PAIR(w.y, true)};
+#undef CSA_FP8_PAIR
+}
 
 __device__ __forceinline__ RowSet make_rowset(const Rows& R, int bt, int Tq, long long pos0) {
     RowSet s;
@@ -68,7 +90,7 @@ __device__ __forceinline__ RowSet make_rowset(const Rows& R, int bt, int Tq, lon
     return s;
 }
 
-template <int D, bool SEPV>
+template <int D, bool SEPV, bool FP8>
 __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q, Rows R, int Tq, int H,
                                                   long long pos0, float scale_log2, int nsplit, int rps,
                                                   float* __restrict__ part_o, float2* __restrict__ part_ml,
@@ -110,14 +132,15 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
         for (int c = threadIdx.x; c < CHUNKS; c += TPB) {
             const int rr = c / (D / 8), cc = c % (D / 8);
             const int r = rb + rr;
-            const uint16_t* src = r < r_end ? rs.row(R, r, D, false) : nullptr;
+            bool ent = false;
+            const char* src = r < r_end ? rs.row(R, r, D, false, ent) : nullptr;
             u32x4_t v = u32x4_t{0, 0, 0, 0};
-            if (src) v = *(const u32x4_t*)(src + cc * 8);
+            if (src) v = row_chunk<D>(src, cc, FP8 && ent);
             *(u32x4_t*)(tile + rr * RS + cc * 8) = v;
             if constexpr (SEPV) {
-                const uint16_t* vsrc = src ? rs.row(R, r, D, true) : nullptr;
+                const char* vsrc = src ? rs.row(R, r, D, true, ent) : nullptr;
                 u32x4_t vv = u32x4_t{0, 0, 0, 0};
-                if (vsrc) vv = *(const u32x4_t*)(vsrc + cc * 8);
+                if (vsrc) vv = row_chunk<D>(vsrc, cc, FP8 && ent);
                 *(u32x4_t*)(vtile + rr * RS + cc * 8) = vv;
             }
             if (cc == 0) bias[rr] = src ? 0.0f : -INFINITY;
@@ -793,6 +816,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     R.pm = a.pm;
     R.v = (const uint16_t*)a.v;
     R.v_raw = (const uint16_t*)a.v_raw;
+    R.kv_fp8 = a.kv_fp8;
     const int BT = B * Tq;
     const int max_rows = a.mode == 0 ? a.N : attn_rows(1, H, D, a.topk, a.W);
     int ns, rps;
@@ -811,7 +835,8 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     const size_t kv_rows = a.pm.table ? (size_t)a.pm.nblocks << a.pm.eshift : (size_t)a.N;
     const bool big32 = kv_rows * D * 2 > 0xffffffffull || (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
     const bool sepv = a.v || a.v_raw;
-    if (use128(D, H) && !big32 && !sepv) {
+    const bool fp8 = a.kv_fp8 != 0;                  // FP8 entry rows: the generic kernel widens them on load
+    if (use128(D, H) && !big32 && !sepv && !fp8) {
         const int r128 = a.mode == 0 ? a.N : a128_rows(1, a.topk, a.W);
         AttnJob j{};
         j.q = (const uint16_t*)q; j.R = R; j.Tq = Tq; j.H = H; j.pos0 = pos0; j.scale_log2 = sl2;
@@ -828,7 +853,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
             return attn128_launch(j, st, tag);
         }
     }
-    if (use64(D, H) && !big32 && !sepv && !(a.pm.table && a.mode == 0)) {
+    if (use64(D, H) && !big32 && !sepv && !fp8 && !(a.pm.table && a.mode == 0)) {
         const int nunits = BT * ns, HP = (H + 63) / 64;
         const int nblk = (nunits + 7) / 8 * 8 * HP;
         if (a.mode == 0)
@@ -843,29 +868,29 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         return 0;
     }
     dim3 grid(ns, (H + 63) / 64, BT);
+#define CSA_GENERIC(D_, S_, F_)                                                                            \
+    CSA_LAUNCH(tag, (k_attn<D_, S_, F_>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns, rps, \
+               part_o, part_ml, (uint16_t*)out, lse)
     if (D == 512) {
-        if (sepv)
-            CSA_LAUNCH(tag, (k_attn<512, true>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns,
-                       rps, part_o, part_ml, (uint16_t*)out, lse);
-        else
-            CSA_LAUNCH(tag, (k_attn<512, false>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns,
-                       rps, part_o, part_ml, (uint16_t*)out, lse);
+        if (sepv && fp8) CSA_GENERIC(512, true, true);
+        else if (sepv) CSA_GENERIC(512, true, false);
+        else if (fp8) CSA_GENERIC(512, false, true);
+        else CSA_GENERIC(512, false, false);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse, R.sink);
     } else if (D == 128) {
-        if (sepv)
-            CSA_LAUNCH(tag, (k_attn<128, true>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns,
-                       rps, part_o, part_ml, (uint16_t*)out, lse);
-        else
-            CSA_LAUNCH(tag, (k_attn<128, false>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns,
-                       rps, part_o, part_ml, (uint16_t*)out, lse);
+        if (sepv && fp8) CSA_GENERIC(128, true, true);
+        else if (sepv) CSA_GENERIC(128, true, false);
+        else if (fp8) CSA_GENERIC(128, false, true);
+        else CSA_GENERIC(128, false, false);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<128>, dim3(H, BT), dim3(32), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse, R.sink);
     } else {
         return fail(6, "attention: D = %d unsupported", D);
     }
+#undef CSA_GENERIC
     return 0;
 }
 

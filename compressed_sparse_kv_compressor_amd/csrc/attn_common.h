@@ -31,6 +31,7 @@ struct Rows {
     csa::PageMap pm;          // entries through a block table (pm.table null: batch-major [B][N][D])
     const uint16_t* v;        // values of the entries when they differ from the keys (kv), or null
     const uint16_t* v_raw;    // values of the raw rows when they differ from kv_raw, or null
+    int kv_fp8;               // entry rows (kv, v) in the FP8 format (D + 80 bytes: e4m3 groups + bf16 RoPE dims)
 };
 
 __device__ __forceinline__ int dense_visible(long long p, long long L, int m, int N) {

@@ -126,6 +126,19 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
                    e4m3x2_to_bf16x2<false>(x1), e4m3x2_to_bf16x2<true>(x1)};
 }
 
+// MXFP4: the E8M0 scale byte as the float 2^(s - 127), and eight E2M1 codes (one dword, element 2i in the low
+// nibble of byte i) times that scale as bf16 -- exact: every such value is a bf16 value for the scales the
+// encoder produces (2^-127 .. 2^125).
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+    return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+}
+__device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t x, float scale) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+#define CSA_FP4_PAIR(B) __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, B))
+    return u32x4_t{CSA_FP4_PAIR(0), CSA_FP4_PAIR(1), CSA_FP4_PAIR(2), CSA_FP4_PAIR(3)};
+#undef CSA_FP4_PAIR
+}
+
 
 // ---------------------------------------------------------------------------
 // k_score
@@ -138,17 +151,19 @@ template <int DT, int DI, int HI, bool PAGED>
 __global__ __launch_bounds__(TPB) void k_score(
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int keys_per_wg, int topk,
-    float* __restrict__ S, uint32_t* __restrict__ hist, const long long* __restrict__ seq_lens, PageMap pm)
+    float* __restrict__ S, uint32_t* __restrict__ hist, const long long* __restrict__ seq_lens, PageMap pm,
+    const uint8_t* __restrict__ q_scale, const uint8_t* __restrict__ k_scale)
 {
     constexpr int STEPS = DI / 32;            // bf16 16x16x32 MFMAs per 16-key tile
     constexpr int EPL = DI / 4;               // key elements per lane
-    constexpr int KB = DT == 0 ? EPL * 2 : EPL;   // key bytes per lane
+    constexpr int KB = DT == 0 ? EPL * 2 : (DT == 1 ? EPL : EPL / 2);   // key bytes per lane
     constexpr int NV = KB / 16;               // 16-byte loads per lane per tile
     constexpr int U = 128 / KB;                // tiles per load batch (bytes per lane in flight)
     constexpr int HP = HI < 4 ? 4 : HI;       // padded heads per query row
     constexpr int G = 16 / HP;                // query rows per column group
     constexpr int LPR = HP / 4;               // lanes (of one key) holding one row's heads
-    constexpr int ES = DT == 0 ? 2 : 1;
+    constexpr int RB = DT == 0 ? DI * 2 : (DT == 1 ? DI : DI / 2);     // bytes per key / query-head row
+    static_assert(DT != 2 || DI == 128, "MXFP4 rows: one 32-element scale block per lane group");
 
     __shared__ uint32_t lh[2][BINS1];         // histograms of up to 2 rows of a group
     __shared__ uint32_t ldmax[2];
@@ -174,14 +189,23 @@ __global__ __launch_bounds__(TPB) void k_score(
         u32x4_t qf8a[2];                      // |q| as raw e4m3 bytes (DT == 1)
         // Element order of the contraction (shared by Q and K): lane group grp takes the 16-byte chunks
         // at bytes 64 i + 16 grp of a row, so that one load instruction reads 64 contiguous bytes of
-        // each of its 16 key rows.  bf16: k-step s = chunk s; e4m3: k-step s = half (s & 1) of chunk s / 2.
+        // each of its 16 key rows.  bf16: k-step s = chunk s; e4m3: k-step s = half (s & 1) of chunk s / 2;
+        // MXFP4: the lane group's one chunk holds elements 32 grp .. 32 grp + 31 (one scale block), and
+        // k-step s takes its dword s.
         if (av) {
             const size_t r = (size_t)b * Tq + ta;
-            const char* qp = (const char*)q_idx + (r * HI + ha) * DI * ES + (size_t)grp * 16;
+            const char* qp = (const char*)q_idx + (r * HI + ha) * RB + (size_t)grp * 16;
+            float qsc = 1.f;
+            u32x4_t qw = u32x4_t{0, 0, 0, 0};
+            if (DT == 2) {
+                qsc = e8m0_scale(q_scale[(r * HI + ha) * (DI / 32) + grp]);
+                qw = *(const u32x4_t*)qp;
+            }
 #pragma unroll
             for (int s = 0; s < STEPS; ++s) {
                 u32x4_t v;
                 if (DT == 0) v = *(const u32x4_t*)(qp + s * 64);
+                else if (DT == 2) v = fp4x8_to_bf16x8(qw[s], qsc);
                 else {
                     const char* c = qp + (s >> 1) * 64 + (s & 1) * 8;
                     v = e4m3x8_to_bf16x8(*(const uint32_t*)c, *(const uint32_t*)(c + 4));
@@ -224,17 +248,18 @@ __global__ __launch_bounds__(TPB) void k_score(
         // key loads are software-pipelined: batch i+1 is in flight while batch i computes
         // (rows past the last visible entry reread it: branch-free loads keep the wait counts exact, so
         //  the next batch stays in flight; those keys are never written)
-        auto load_batch = [&](int tt0, u32x4_t (&dst)[U][NV]) {
+        auto load_batch = [&](int tt0, u32x4_t (&dst)[U][NV], uint32_t (&dsc)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int krow = min(key0 + ((tt0 + u) * 4 + wave) * 16 + col, nvmax - 1);
                 const size_t prow = PAGED ? entry_row(pm, b, Nc, krow) : (size_t)b * Nc + krow;
-                const char* kp = (const char*)k_idx + prow * DI * ES + (size_t)grp * 16;
+                const char* kp = (const char*)k_idx + prow * RB + (size_t)grp * 16;
 #pragma unroll
                 for (int i = 0; i < NV; ++i) dst[u][i] = *(const u32x4_t*)(kp + i * 64);
+                if (DT == 2) dsc[u] = k_scale[prow * (DI / 32) + grp];
             }
         };
-        auto compute_batch = [&](int tt0, const u32x4_t (&cur)[U][NV]) {
+        auto compute_batch = [&](int tt0, const u32x4_t (&cur)[U][NV], const uint32_t (&csc)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                     // (tiles past the visible keys are computed and dropped: no branch between the
@@ -245,9 +270,10 @@ __global__ __launch_bounds__(TPB) void k_score(
                     for (int s = 0; s < STEPS; ++s) {
                         u32x4_t v;
                         if (DT == 0) v = cur[u][s];
+                        else if (DT == 2) v = fp4x8_to_bf16x8(cur[u][0][s], e8m0_scale(csc[u]));
                         else v = e4m3x8_to_bf16x8(cur[u][s / 2][(s & 1) * 2], cur[u][s / 2][(s & 1) * 2 + 1]);
                         acc = mfma16_bf16(qb[s], as_bf16x8(v), acc);
-                        if (DT == 0) aacc = mfma16_bf16(qa[s], as_bf16x8(v & 0x7fff7fffu), aacc);
+                        if (DT != 1) aacc = mfma16_bf16(qa[s], as_bf16x8(v & 0x7fff7fffu), aacc);
                     }
                     if (DT == 1) {
                         // |q|.|k| bound: one e4m3 MFMA (K = 128) on the raw bytes with the sign bits cleared
@@ -289,16 +315,17 @@ __global__ __launch_bounds__(TPB) void k_score(
         // counts stay exact: the next batch stays in flight while this one computes.
         __builtin_amdgcn_s_waitcnt(0);        // the per-row loads above have landed
         u32x4_t ka[U][NV], kb[U][NV];
+        uint32_t sa[U], sb[U];                // MXFP4 scale bytes of the batch's key rows (DT == 2)
         if (key0 + wave * 16 < nvmax) {
-            load_batch(0, ka);
+            load_batch(0, ka, sa);
             for (int tt0 = 0; tt0 < tiles; tt0 += 2 * U) {
                 const bool more1 = tt0 + U < tiles && key0 + ((tt0 + U) * 4 + wave) * 16 < nvmax;
-                load_batch(more1 ? tt0 + U : tt0, kb);
-                compute_batch(tt0, ka);
+                load_batch(more1 ? tt0 + U : tt0, kb, sb);
+                compute_batch(tt0, ka, sa);
                 if (!more1) break;
                 const bool more2 = tt0 + 2 * U < tiles && key0 + ((tt0 + 2 * U) * 4 + wave) * 16 < nvmax;
-                load_batch(more2 ? tt0 + 2 * U : tt0 + U, ka);
-                compute_batch(tt0 + U, kb);
+                load_batch(more2 ? tt0 + 2 * U : tt0 + U, ka, sa);
+                compute_batch(tt0 + U, kb, sb);
                 if (!more2) break;
             }
         }
@@ -413,9 +440,13 @@ __global__ __launch_bounds__(STPB) void k_select(
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int topk,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out, float* __restrict__ score_out,
-    const long long* __restrict__ seq_lens, PageMap pm)
+    const long long* __restrict__ seq_lens, PageMap pm, const uint8_t* __restrict__ q_scale,
+    const uint8_t* __restrict__ k_scale)
 {
-    constexpr int ES = DT == 0 ? 2 : 1;
+    constexpr int RB = DT == 0 ? DI * 2 : (DT == 1 ? DI : DI / 2);     // bytes per key / query-head row
+    // MXFP4 (DT == 2): the band is rescored on exact bf16 copies of the query row and of each band key
+    __shared__ __attribute__((aligned(16))) uint16_t mxq[DT == 2 ? HI * DI : 2];
+    __shared__ __attribute__((aligned(16))) uint16_t mxk[DT == 2 ? STPB / 64 * DI : 2];
     __shared__ uint32_t lh[BINS2];
     __shared__ uint32_t scratch[STPB / 64], res[4], nband;
     __shared__ uint32_t cpre[STPB + 1], cbase[STPB];
@@ -515,13 +546,41 @@ __global__ __launch_bounds__(STPB) void k_select(
     // 3. exact rescoring of the band (one wave per entry); composite keys (exact score key,
     //    inverted index): larger composite = earlier in the order
     unsigned long long* Kg = bkey_g + (size_t)r * NcP;
-    const char* qrow = (const char*)q_idx + (size_t)r * HI * DI * ES;
+    const char* qrow = (const char*)q_idx + (size_t)r * HI * RB;
     const float* wrow = w_idx + (size_t)r * HI;
     if (need > 0 && need < nb) {
+        if constexpr (DT == 2) {                      // widen the query's HI rows (two elements per thread)
+            for (int e = tid; e < HI * DI / 2; e += STPB) {
+                const int hh = (2 * e) / DI, i = (2 * e) % DI;
+                const float sc = e8m0_scale(q_scale[((size_t)r * HI + hh) * (DI / 32) + i / 32]);
+                typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+                const uint32_t w = (uint32_t)(uint8_t)qrow[(size_t)hh * RB + i / 2];
+                *(uint32_t*)&mxq[hh * DI + i] =
+                    __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+            }
+            __syncthreads();
+        }
         for (uint32_t i = wave; i < nb; i += STPB / 64) {
             const uint2 be = band(i);
-            const float sx = wave_exact_score<DT, DI, HI>(qrow, wrow,
-                                                          (const char*)k_idx + entry_row(pm, b, Nc, (int)be.x) * DI * ES);
+            const size_t krow = entry_row(pm, b, Nc, (int)be.x);
+            float sx;
+            if constexpr (DT == 2) {
+                uint16_t* kw = mxk + wave * DI;
+                for (int e = lane; e < DI / 2; e += 64) {
+                    const float sc = e8m0_scale(k_scale[krow * (DI / 32) + (2 * e) / 32]);
+                    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+                    const uint32_t w = (uint32_t)((const uint8_t*)k_idx)[krow * RB + e];
+                    *(uint32_t*)&kw[2 * e] =
+                        __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                sx = wave_exact_score<0, DI, HI>(mxq, wrow, kw);
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();   // the next band entry overwrites kw
+            } else {
+                sx = wave_exact_score<DT, DI, HI>(qrow, wrow, (const char*)k_idx + krow * RB);
+            }
             if (lane == 0) {
                 const unsigned long long ck = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - be.x);
                 if (nb > (uint32_t)BAND_LDS) Kg[i] = ck;       // the radix path reads every key from HBM
@@ -603,7 +662,8 @@ static size_t decode_index_ws_bytes(int B, int Tq, int Nc) {
 template <int DT, int DI, int HI>
 static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx, int B, int Tq, int Nc,
                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
-                        float* score_out, const long long* seq_lens, const PageMap& pm, void* ws, hipStream_t st) {
+                        float* score_out, const long long* seq_lens, const PageMap& pm, const uint8_t* q_scale,
+                        const uint8_t* k_scale, void* ws, hipStream_t st) {
     const size_t R = (size_t)B * Tq;
     const int NcP = (Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
     char* p = (char*)ws;
@@ -625,14 +685,15 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
     while (kpw > 1024 && (size_t)((Nc + kpw - 1) / kpw) * B < 512) kpw >>= 1;
     if (pm.table)
         CSA_LAUNCH("k_score", (k_score<DT, DI, HI, true>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
-                   q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm);
+                   q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm, q_scale, k_scale);
     else
         CSA_LAUNCH("k_score", (k_score<DT, DI, HI, false>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
-                   q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm);
+                   q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm, q_scale, k_scale);
     CSA_LAUNCH("k_collect", k_collect, dim3(NcP / CCHUNK, (unsigned)R), dim3(STPB), 0, st, S, hist, list, ctab, Tq,
                Nc, NcP, L, m, pos0, topk, seq_lens);
     CSA_LAUNCH("k_select", (k_select<DT, DI, HI>), dim3((unsigned)R), dim3(STPB), 0, st, hist, list, ctab, band,
-               bkey, flags, q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out, score_out, seq_lens, pm);
+               bkey, flags, q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out, score_out, seq_lens, pm,
+               q_scale, k_scale);
     return 0;
 }
 
@@ -643,8 +704,8 @@ size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int
 
 int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
                       int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
-                      int32_t* idx_out, int32_t* cnt_out, float* score_out, const CacheLayout& lay, void* ws,
-                      hipStream_t st) {
+                      int32_t* idx_out, int32_t* cnt_out, float* score_out, const CacheLayout& lay,
+                      const uint8_t* q_scale, const uint8_t* k_scale, void* ws, hipStream_t st) {
     const PageMap pm = page_map(lay, m);
     if (!lay.seq_lens && !lay.table && prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk))
         return prefill_index_launch(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk, idx_out, cnt_out, score_out,
@@ -652,10 +713,10 @@ int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, 
 #define CSA_IDX_CASE(DT, DI, HI_)                                                              \
     if (dtype == DT && dI == DI && HI == HI_)                                                  \
         return launch_index<DT, DI, HI_>(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk,     \
-                                         idx_out, cnt_out, score_out, lay.seq_lens, pm, ws, st);
+                                         idx_out, cnt_out, score_out, lay.seq_lens, pm, q_scale, k_scale, ws, st);
 #define CSA_IDX_HI(DT, DI) CSA_IDX_CASE(DT, DI, 1) CSA_IDX_CASE(DT, DI, 2) CSA_IDX_CASE(DT, DI, 4) \
                            CSA_IDX_CASE(DT, DI, 8) CSA_IDX_CASE(DT, DI, 16)
-    CSA_IDX_HI(0, 64) CSA_IDX_HI(0, 128) CSA_IDX_HI(1, 64) CSA_IDX_HI(1, 128)
+    CSA_IDX_HI(0, 64) CSA_IDX_HI(0, 128) CSA_IDX_HI(1, 64) CSA_IDX_HI(1, 128) CSA_IDX_HI(2, 128)
 #undef CSA_IDX_HI
 #undef CSA_IDX_CASE
     return fail(6, "index_topk: unsupported (dtype %d, dI %d, HI %d)", dtype, dI, HI);

@@ -29,8 +29,10 @@ inline csa::PageMap page_map(const CacheLayout& lay, int m) {
 size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk, bool plain = true);
 int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
                       int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
-                      int32_t* idx_out, int32_t* cnt_out, float* score_out, const CacheLayout& lay, void* ws,
-                      hipStream_t st);
+                      int32_t* idx_out, int32_t* cnt_out, float* score_out, const CacheLayout& lay,
+                      const uint8_t* q_scale, const uint8_t* k_scale, void* ws, hipStream_t st);
+int kv_fp8_launch(const void* x, long long n, int D, void* y, hipStream_t st);
+int mxfp4_launch(const void* x, long long n, int len, void* codes, void* scales, hipStream_t st);
 // many-query (prefill) indexer path: bf16, HI = 8, dI = 128, Tq >= 64, topk <= 1024
 bool prefill_index_applicable(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk);
 size_t prefill_index_ws_bytes(int B, int Tq, int Nc);
@@ -60,6 +62,7 @@ struct AttnRows {
     csa::PageMap pm;          // entries through a block table (pm.table null: batch-major kv)
     const void* v;            // values of the entries when separate from kv (same rows), or null
     const void* v_raw;        // values of the raw rows when separate from kv_raw, or null
+    int kv_fp8;               // entry rows in the FP8 format (D + 80 bytes per row), raw rows bf16
 };
 // mode 0: dense over n rows; mode 1: n selected entries + W window rows
 size_t attn_ws_bytes(int B, int Tq, int H, int D, int mode, int n, int W);

@@ -65,7 +65,9 @@ typedef enum {
     CSA_ERR_HIP = 7          /* a HIP runtime call or launch failed */
 } csa_status_t;
 
-typedef enum { CSA_BF16 = 0, CSA_E4M3 = 1 } csa_dtype_t;
+typedef enum { CSA_BF16 = 0, CSA_E4M3 = 1, CSA_MXFP4 = 2 } csa_dtype_t;
+/* Storage format of compressed KV entry rows (the *_ex attention entry points). */
+typedef enum { CSA_KV_BF16 = 0, CSA_KV_FP8 = 1 } csa_kv_format_t;
 
 /* Library identity and error reporting. */
 int csa_abi_version(void);                 /* returns CSA_ABI_VERSION */
@@ -237,12 +239,20 @@ int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int
  * Results as csa_index_topk (bit-exact to running each sequence on its own
  * contiguous cache).  Such calls always take the per-query path, so the
  * workspace (csa_index_topk_ex_ws_bytes) holds Tq x Nc scores per sequence. */
+/* dtype CSA_MXFP4 ([P2] "mHC、Muon、FP4": the indexer's QK path in FP4; see
+ * csa_mxfp4_encode for the format): q_idx is then the E2M1 codes
+ * [B][Tq][HI][dI/2] and q_scale their E8M0 scales [B][Tq][HI][dI/32], k_idx the
+ * codes [B][Nc][dI/2] (or their pool) and k_scale [B][Nc][dI/32] (or their pool,
+ * rows alongside k_idx); dI = 128.  The canonical score is taken over the
+ * decoded values, so the selection is bit-exact to the oracle's over the same
+ * MXFP4 operands.  q_scale and k_scale are NULL for the other dtypes. */
 size_t csa_index_topk_ex_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype,
                                   const csa_cache_layout_t* layout);
 int csa_index_topk_ex(const void* q_idx, const float* w_idx, const void* k_idx, int dtype,
                       int B, int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0,
                       int topk, int32_t* idx_out, int32_t* cnt_out, float* score_out,
-                      const csa_cache_layout_t* layout, void* ws, size_t ws_bytes, void* stream);
+                      const csa_cache_layout_t* layout, const void* q_scale, const void* k_scale,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* A4. CSA core attention: MQA over the selected entries plus a sliding       */
@@ -279,13 +289,15 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
  *   v_raw  [B][Lr][D] bf16 or NULL (= kv_raw): the value of raw row i
  *   out_h = sum_r softmax(l)_r v_r with l_r = scale * q_h . k_r.
  * m is the ratio of the cache kv (it sets the entries per page of a paged
- * pool).  With seq_lens, every sequence's Lr raw rows are its last Lr tokens,
+ * pool).  kv_format CSA_KV_FP8: kv (and v) rows are FP8 rows of D + 80 bytes
+ * (csa_kv_fp8_encode; the raw rows stay bf16), attended as their exact bf16
+ * decoding.  With seq_lens, every sequence's Lr raw rows are its last Lr tokens,
  * so Lr >= Tq + W - 1 is required when W > 0.  Workspace:
  * csa_sparse_attn_ws_bytes. */
 int csa_sparse_attn_ex(const void* q, const void* kv, const void* v, const int32_t* idx, const void* kv_raw,
                        const void* v_raw, int B, int Tq, int H, int D, int Nc, int m, int topk, int Lr,
                        long long raw0, long long pos0, int W, float scale, const float* sink,
-                       const csa_cache_layout_t* layout, void* out, float* lse_out,
+                       const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out,
                        void* ws, size_t ws_bytes, void* stream);
 
 /* No-allocation variant of csa_sparse_attn, for callers that cannot allocate
@@ -322,12 +334,33 @@ int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D,
                    void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /* hca_dense_attn over a variable-length and/or paged batch, with optional
- * separate values v_h (same rows as kv_h, or NULL = kv_h); as csa_sparse_attn_ex.
- * With seq_lens, L is the capacity (Nh = ceil(L / mh)). */
+ * separate values v_h (same rows as kv_h, or NULL = kv_h) and FP8 entry rows;
+ * as csa_sparse_attn_ex.  With seq_lens, L is the capacity (Nh = ceil(L / mh)). */
 int hca_dense_attn_ex(const void* q, const void* kv_h, const void* v_h, int B, int Tq, int H, int D, int Nh,
                       long long L, int mh, long long pos0, float scale, const float* sink,
-                      const csa_cache_layout_t* layout, void* out, float* lse_out,
+                      const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Low-precision cache formats ([P1] 1.1, last paragraph: RoPE dimensions in */
+/* BF16, the others in FP8; [P2] "mHC、Muon、FP4": the indexer QK in FP4)    */
+/* ------------------------------------------------------------------------ */
+/* FP8 KV rows.  x [n][D] bf16 (D in {128, 512}; its last 64 dimensions are the
+ * RoPE dimensions) -> y [n][D + 80] bytes: e4m3 codes of dimensions 0..D-65 in
+ * groups of 64, each group divided by its smallest power-of-two scale 2^e with
+ * max |x| <= 448 * 2^e (0 for an all-zero group; exact division, rounding to
+ * nearest even, no saturation), then the 64 RoPE dimensions as bf16, then one
+ * byte e + 127 per group (16 bytes, unused ones 0).  A dimension decodes to
+ * e4m3(code) * 2^e, exact in bf16 for e >= -126.  Bit-exact. */
+int csa_kv_fp8_encode(const void* x, long long n, int D, void* y, void* stream);
+/* MXFP4 (the OCP Microscaling FP4 format).  x [n][len] bf16 (len % 32 == 0,
+ * len <= 4096) -> codes [n][len/2] (E2M1: sign, 2 exponent bits, 1 mantissa bit;
+ * element 2i in the low nibble of byte i) and scales [n][len/32] (E8M0: the
+ * byte X + 127 for the scale 2^X of each 32 elements, X = floor(log2 max|x|)
+ * - 2 clamped to [-127, 127], -127 for an all-zero block); each element is
+ * x / 2^X rounded to the nearest E2M1 value, ties to the even code, saturating
+ * at 6.  Bit-exact.  Pointers 16-byte aligned except scales (any). */
+int csa_mxfp4_encode(const void* x, long long n, int len, void* codes, void* scales, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* A6. Fused decode of one interleaved CSA layer followed by one HCA layer   */
@@ -367,6 +400,9 @@ typedef struct csa_hca_decode_args {
      * tokens); with block_table, k_idx and kv are the CSA pools (ratio m) and kv_h the HCA pool (ratio
      * mh), all paged by the one table. */
     const csa_cache_layout_t* layout;
+    /* With idx_dtype CSA_MXFP4: the E8M0 scales of q_idx [B][HI][dI/32] and of k_idx (rows alongside it). */
+    const void* q_idx_scale;
+    const void* k_idx_scale;
 } csa_hca_decode_args_t;
 
 size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a);

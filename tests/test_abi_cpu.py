@@ -176,7 +176,7 @@ def test_layout_validation_codes(b):
         a = dict(q=A16, w=A16, k=A16, dt=0, B=1, Tq=1, HI=8, dI=128, Nc=1024, L=4096, m=4, pos0=4095, topk=64)
         a.update(kw)
         return f(a["q"], a["w"], a["k"], a["dt"], a["B"], a["Tq"], a["HI"], a["dI"], a["Nc"], a["L"], a["m"],
-                 a["pos0"], a["topk"], A16, None, None, ctypes.byref(lay), A16, 10 ** 9, None)
+                 a["pos0"], a["topk"], A16, None, None, ctypes.byref(lay), None, None, A16, 10 ** 9, None)
 
     ok = b.CacheLayout(seq_lens=A16, block_table=A16, max_blocks=32, num_blocks=40, block_tokens=128)
     assert idx_call(b.CacheLayout(seq_lens=ctypes.c_void_p(16 * 1000 + 4))) == CSA_ERR_ALIGN
@@ -190,11 +190,11 @@ def test_layout_validation_codes(b):
     assert lib.csa_index_topk_ex_ws_bytes(1, 8192, 8, 128, 65536, 1024, 0, None) < \
         lib.csa_index_topk_ex_ws_bytes(1, 8192, 8, 128, 65536, 1024, 0, ctypes.byref(ok))   # no many-query path
     sp = lib.csa_sparse_attn_ex
-    # q, kv, v, idx, kv_raw, v_raw, B, Tq, H, D, Nc, m, topk, Lr, raw0, pos0, W, scale, sink, layout, out, lse, ws...
+    # q, kv, v, idx, kv_raw, v_raw, B, Tq, H, D, Nc, m, topk, Lr, raw0, pos0, W, scale, sink, layout, fmt, out, ...
     var = b.CacheLayout(seq_lens=A16)
-    assert sp(A16, A16, None, A16, A16, None, 2, 2, 16, 128, 100, 4, 8, 9, 0, 0, 9, 0.1, None, ctypes.byref(var),
+    assert sp(A16, A16, None, A16, A16, None, 2, 2, 16, 128, 100, 4, 8, 9, 0, 0, 9, 0.1, None, ctypes.byref(var), 0,
               A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE                   # Lr < Tq + W - 1
-    assert sp(A16, A16, BAD, A16, A16, None, 2, 2, 16, 128, 100, 4, 8, 10, 0, 0, 9, 0.1, None, ctypes.byref(var),
+    assert sp(A16, A16, BAD, A16, A16, None, 2, 2, 16, 128, 100, 4, 8, 10, 0, 0, 9, 0.1, None, ctypes.byref(var), 0,
               A16, None, A16, 10 ** 9, None) == CSA_ERR_ALIGN
-    assert sp(A16, A16, None, A16, A16, None, 2, 2, 16, 128, 100, 0, 8, 10, 0, 0, 9, 0.1, None, ctypes.byref(var),
+    assert sp(A16, A16, None, A16, A16, None, 2, 2, 16, 128, 100, 0, 8, 10, 0, 0, 9, 0.1, None, ctypes.byref(var), 0,
               A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE                   # m = 0
