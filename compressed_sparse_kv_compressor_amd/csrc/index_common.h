@@ -57,6 +57,69 @@ __device__ __forceinline__ float raw_to_f32(const char* p, int i) {
     return x.neg ? -v : v;
 }
 
+// Reduction over groups of G consecutive lanes (G a power of two): DPP lane moves within 16 lanes (two quad
+// permutations, then the half-row and row mirrors, each of which pairs the two halves of the group so far)
+// and shuffles beyond.
+template <int G, typename Op>
+__device__ __forceinline__ uint32_t grp_reduce(uint32_t v, Op op) {
+    if (G >= 2) v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+    if (G >= 4) v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+    if (G >= 8) v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half mirror
+    if (G >= 16) v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false)); // mirror
+    if (G >= 32) v = op(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+    if (G >= 64) v = op(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+    return v;
+}
+template <int G>
+__device__ __forceinline__ double grp_sum_f64(double s) {
+    auto mv = [](double x, int ctl) -> double {
+        const unsigned long long u = __double_as_longlong(x);
+        int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+        if (ctl == 16 || ctl == 32) { lo = __shfl_xor(lo, ctl, 64); hi = __shfl_xor(hi, ctl, 64); }
+        else {
+            switch (ctl) {
+            case 0xB1: lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
+                       hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false); break;
+            case 0x4E: lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
+                       hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false); break;
+            case 0x141: lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, false);
+                        hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, false); break;
+            default: lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, false);
+                     hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, false); break;
+            }
+        }
+        return __longlong_as_double(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+    };
+    if (G >= 2) s += mv(s, 0xB1);
+    if (G >= 4) s += mv(s, 0x4E);
+    if (G >= 8) s += mv(s, 0x141);
+    if (G >= 16) s += mv(s, 0x140);
+    if (G >= 32) s += mv(s, 16);
+    if (G >= 64) s += mv(s, 32);
+    return s;
+}
+
+// The EPL elements of a lane as exact fp32 values (e4m3: the hardware conversion, a pair at a time, when the
+// lane's bytes are whole dwords).
+template <int DT, int EPL>
+__device__ __forceinline__ void load_exact_f32(const char* p, float (&x)[EPL]) {
+    if constexpr (DT == 0) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) x[i] = __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+    } else if constexpr (EPL % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < EPL / 4; ++j) {
+            const uint32_t w = ((const uint32_t*)p)[j];
+            const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+            const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+            x[4 * j] = lo[0]; x[4 * j + 1] = lo[1]; x[4 * j + 2] = hi[0]; x[4 * j + 3] = hi[1];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) x[i] = raw_to_f32<DT>(p, i);
+    }
+}
+
 template <int DT, int DI, int HI>
 __device__ float wave_exact_score(const void* qrow, const float* wrow, const void* krow) {
     using namespace csa_exact;
@@ -67,39 +130,35 @@ __device__ float wave_exact_score(const void* qrow, const float* wrow, const voi
     const char* qp = (const char*)qrow + ((size_t)h * DI + sub * EPL) * ES;
     const char* kp = (const char*)krow + (size_t)sub * EPL * ES;
     {
+        float xq[EPL], xk[EPL];
+        load_exact_f32<DT, EPL>(qp, xq);
+        load_exact_f32<DT, EPL>(kp, xk);
         double s = 0.0;
-        int emin = 1000, emax = -1000, bad = 0;
+        // leading-bit exponents of the nonzero products through their magnitudes' bit patterns (monotone)
+        uint32_t mx = 0u, mn = 0xffffffffu, bad = 0u;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            const float x = raw_to_f32<DT>(qp, i), y = raw_to_f32<DT>(kp, i);
-            const float pr = x * y;
-            const int e = (int)((__float_as_uint(pr) >> 23) & 0xffu);
-            if (x != 0.0f && y != 0.0f) {
-                bad |= e == 0 || e == 255;            // zero/subnormal product (maybe inexact) or overflow
-                emin = min(emin, e);
-                emax = max(emax, e);
-            }
+            const float pr = xq[i] * xk[i];
+            const uint32_t ab = __float_as_uint(pr) & 0x7fffffffu;
+            const bool nz = xq[i] != 0.0f && xk[i] != 0.0f;
+            // zero/subnormal product of nonzero factors (maybe inexact), or overflow
+            bad |= (uint32_t)(nz && (ab < 0x00800000u || ab >= 0x7f800000u));
+            mx = nz ? max(mx, ab) : mx;
+            mn = nz ? min(mn, ab) : mn;
             s += (double)pr;
         }
-#pragma unroll
-        for (int o = 1; o < LPH; o <<= 1) {
-            emin = min(emin, __shfl_xor(emin, o, 64));
-            emax = max(emax, __shfl_xor(emax, o, 64));
-            bad |= __shfl_xor(bad, o, 64);
-        }
-        const bool fast = !bad && emax - emin <= 45 - MB;     // uniform within a head's lanes
+        mx = grp_reduce<LPH>(mx, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+        mn = grp_reduce<LPH>(mn, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+        bad = grp_reduce<LPH>(bad, [](uint32_t a, uint32_t b) { return a | b; });
+        const bool fast = !bad && (mn > mx || (int)(mx >> 23) - (int)(mn >> 23) <= 45 - MB);
         if (__builtin_amdgcn_ballot_w64(!fast) == 0ull) {      // every head fast (the common case)
-#pragma unroll
-            for (int o = 1; o < LPH; o <<= 1) {
-                const unsigned long long u = __double_as_longlong(s);
-                const int lo = __shfl_xor((int)(uint32_t)u, o, 64), hi = __shfl_xor((int)(uint32_t)(u >> 32), o, 64);
-                s += __longlong_as_double(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
-            }
+            s = grp_sum_f64<LPH>(s);
             const float d = (float)s;
             const float rr = d > 0.0f ? d : 0.0f;
             float Sx = 0.0f;
+#pragma unroll
             for (int hh = 0; hh < HI; ++hh) {
-                const float rh = __shfl(rr, hh * LPH, 64);
+                const float rh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rr), hh * LPH));
                 Sx = __builtin_fmaf(wrow[hh], rh, Sx);
             }
             return Sx;

@@ -8,7 +8,7 @@
 // none): S = fma-chain_h w_h * ReLU(RN32(exact q_h . k_s)).
 //
 // GPU pipeline (all on the caller's stream, no host synchronisation):
-//   k_fill     zero the per-row histogram, error maximum and candidate count
+//   k_fill     zero the per-row histogram and error maximum
 //   k_score    the HBM-bound pass: v_mfma_f32_16x16x32_bf16 approximate scores
 //              S~ (e4m3 keys are widened to bf16 exactly in registers), a
 //              rigorous per-entry error bound from a second MFMA on |q|, |k|,
@@ -16,14 +16,14 @@
 //              largest bound Dmax
 //   k_collect  every entry that can still reach the top-k (S~ >= lower edge of
 //              the bin holding the k-th largest, minus 2 Dmax) -> a per-row
-//              candidate list of (index, S~)
-//   k_select   one workgroup per row: exact k-th largest S~ (tau) from the two
-//              histogram levels plus an 8-bit third level over the candidates;
-//              S~ > tau + 2 Dmax is certainly selected, S~ < tau - 2 Dmax
-//              certainly not; the band in between is rescored exactly
-//              (wave-cooperative exact dot products) and its remaining slots go
-//              by (exact S desc, index asc); the candidates are kept in index
-//              order, so one prefix scan writes the k indices ascending.
+//              candidate list of (index, S~), one region per workgroup
+//   k_select   one workgroup per row: exact k-th largest S~ (tau) from the
+//              level-1 bin plus a 12-bit and an 8-bit level over the
+//              candidates; S~ > tau + 2 Dmax is certainly selected,
+//              S~ < tau - 2 Dmax certainly not; the band in between is rescored
+//              exactly (wave-cooperative exact dot products) and its remaining
+//              slots go by (exact S desc, index asc); the candidates are kept in
+//              index order, so one prefix scan writes the k indices ascending.
 // Why the classification is safe.  Let every entry satisfy |S~_s - S_s| <= D
 // (D = Dmax of the row) and let tau be the k-th largest S~ (so fewer than k
 // entries have S~ > tau and at least k have S~ >= tau).
@@ -46,10 +46,10 @@ namespace {
 using namespace csa;
 
 constexpr int BINS1 = 4096;                  // histogram of key bits 31..20
-constexpr int BINS2 = 4096;                  // histogram of key bits 19..8 inside the threshold bin
-constexpr int HW_DMAX = BINS1 + BINS2, HW_CNT = BINS1 + BINS2 + 1;   // row max error bound; candidate count
-constexpr int HW_B1 = BINS1 + BINS2 + 2, HW_A1 = BINS1 + BINS2 + 3;    // level-1 bin of tau; count above it
-constexpr int HIST_WORDS = BINS1 + BINS2 + 8;
+constexpr int BINS2 = 4096;                  // (k_select, in LDS) key bits 19..8 inside the threshold bin
+constexpr int HW_DMAX = BINS1;               // per row: the largest error bound
+constexpr int HW_B1 = BINS1 + 2, HW_A1 = BINS1 + 3;    // level-1 bin of tau; count above it
+constexpr int HIST_WORDS = BINS1 + 8;
 constexpr int TPB = 256;
 
 
@@ -347,31 +347,29 @@ __global__ __launch_bounds__(TPB) void k_score(
 // candidate lists, then the per-row selection
 // ---------------------------------------------------------------------------
 // Each k_collect workgroup filters CCHUNK entries of one row against the row's
-// threshold (lower edge of the bin holding the k-th largest S~, minus 2 Dmax),
-// appends (index, S~) pairs to the row's candidate list and builds the second
-// radix level; k_select then selects each row with one workgroup and emits the
+// threshold (lower edge of the bin holding the k-th largest S~, minus 2 Dmax) and
+// writes its (index, S~) candidates in index order to its own region of the
+// row's list; k_select then selects each row with one workgroup and emits the
 // chosen indices in ascending order without sorting.
 constexpr int STPB = 1024;
 constexpr int CCHUNK = STPB * 16;    // entries per workgroup (16 waves x 16 groups of 64)
 constexpr int BAND_LDS = 1024;       // band entries ranked in LDS (larger bands: 64-bit radix in HBM)
 constexpr int CAND_LDS = 8192;       // candidates kept in LDS by k_select (more: read from HBM each pass)
-
-
-
-
+constexpr int PF_MAX = 64;           // key rows near tau that k_select fetches into LDS ahead of the band
+constexpr int SEL_TPB = 512;         // k_select threads (256 VGPRs each: the exact rescoring does not spill)
 
 // k_collect: each workgroup filters CCHUNK entries of one row against the row's threshold (lower edge of
-// the bin b1 holding the k-th largest S~, minus 2 Dmax), appends (index, S~) pairs to the row's candidate
-// list in ascending index order (one contiguous run per workgroup, recorded in the chunk table), and
-// histograms key bits 19..8 of the entries inside bin b1 (second radix level).
+// the bin b1 holding the k-th largest S~, minus 2 Dmax) and writes its candidates (index, S~) in ascending
+// index order at the start of its chunk's region of the row's list (chunk c at c * CCHUNK), with their count
+// in the chunk table.  Workgroup 0 of the row publishes b1 and the count above it.
 __global__ __launch_bounds__(STPB) void k_collect(const float* __restrict__ S, uint32_t* __restrict__ hist,
-                                                  uint2* __restrict__ list, uint2* __restrict__ ctab, int Tq, int Nc,
-                                                  int NcP, long long L, int m, long long pos0, int topk,
+                                                  uint2* __restrict__ list, uint32_t* __restrict__ ctab, int Tq,
+                                                  int Nc, int NcP, long long L, int m, long long pos0, int topk,
                                                   const long long* __restrict__ seq_lens)
 {
     constexpr int GPW = CCHUNK / (STPB / 64) / 64;   // groups of 64 entries per wave
     __shared__ uint32_t lh[BINS1];
-    __shared__ uint32_t scratch[STPB / 64], res[4], wcount[STPB / 64], wbase[STPB / 64];
+    __shared__ uint32_t scratch[STPB / 64], res[4], wcount[STPB / 64];
     const int r = blockIdx.y, t = r % Tq;
     const int nv = row_visible(seq_lens, r / Tq, t, Tq, L, pos0, m, Nc);
     if (nv <= topk) return;
@@ -387,37 +385,29 @@ __global__ __launch_bounds__(STPB) void k_collect(const float* __restrict__ S, u
     }
     uint32_t* H = hist + (size_t)r * HIST_WORDS;
     for (int i = threadIdx.x; i < BINS1; i += STPB) lh[i] = H[i];
+    const float dmax = __uint_as_float(H[HW_DMAX]);
     __syncthreads();
     find_bin_wide(lh, (uint32_t)topk, res, scratch);
     const uint32_t b1 = res[0];
     if (blockIdx.x == 0 && threadIdx.x == 0) { H[HW_B1] = b1; H[HW_A1] = res[1]; }   // for k_select
-    const double thr = (double)key_f32(b1 << 20) - 2.0 * (double)__uint_as_float(H[HW_DMAX]);
-    for (int i = threadIdx.x; i < BINS2; i += STPB) lh[i] = 0;
-    __syncthreads();
+    const double thr = (double)key_f32(b1 << 20) - 2.0 * (double)dmax;
     unsigned long long mask[GPW];
     uint32_t cnt = 0;
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
         const int sidx = s_w + gi * 64 + lane;
-        const bool c = sidx < nv && (double)v[gi] >= thr;
-        if (c) {
-            const uint32_t key = f32_key(v[gi]);
-            if ((key >> 20) == b1) atomicAdd(&lh[(key >> 8) & (BINS2 - 1)], 1u);
-        }
-        mask[gi] = __ballot(c);
+        mask[gi] = __ballot(sidx < nv && (double)v[gi] >= thr);
         cnt += __popcll(mask[gi]);
     }
     if (lane == 0) wcount[wave] = cnt;
     __syncthreads();
+    uint32_t pos = blockIdx.x * CCHUNK;
+    for (int w = 0; w < wave; ++w) pos += wcount[w];
     if (threadIdx.x == 0) {
         uint32_t tot = 0;
         for (int w = 0; w < STPB / 64; ++w) tot += wcount[w];
-        uint32_t base = tot ? atomicAdd(&H[HW_CNT], tot) : 0;
-        ctab[(size_t)r * (NcP / CCHUNK) + blockIdx.x] = make_uint2(base, tot);
-        for (int w = 0; w < STPB / 64; ++w) { wbase[w] = base; base += wcount[w]; }
+        ctab[(size_t)r * gridDim.x + blockIdx.x] = tot;
     }
-    __syncthreads();
-    uint32_t pos = wbase[wave];
     uint2* Lr = list + (size_t)r * NcP;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
@@ -427,15 +417,16 @@ __global__ __launch_bounds__(STPB) void k_collect(const float* __restrict__ S, u
             Lr[pos + __popcll(mask[gi] & below)] = make_uint2((uint32_t)sidx, __float_as_uint(v[gi]));
         pos += __popcll(mask[gi]);
     }
-    for (int i = threadIdx.x; i < BINS2; i += STPB)
-        if (lh[i]) atomicAdd(&H[BINS1 + i], lh[i]);
 }
 
-// k_select: one 1024-thread workgroup per row (see the header for the argument).  Candidates are addressed
-// in ascending index order through the chunk table ("sorted position" e).
+// k_select: one 512-thread workgroup per row (see the header for the argument).  Candidates are addressed
+// in ascending index order through the chunk counts ("sorted position" e).  The query row and its head
+// weights are staged in LDS at the start, and the key rows of the candidates that can fall in the band
+// are fetched into LDS as soon as tau is known to 12 + 12 bits, so that their loads overlap the rest of
+// the search and the classification.
 template <int DT, int DI, int HI>
-__global__ __launch_bounds__(STPB) void k_select(
-    const uint32_t* __restrict__ hist, const uint2* __restrict__ list, const uint2* __restrict__ ctab,
+__global__ __launch_bounds__(SEL_TPB) void k_select(
+    const uint32_t* __restrict__ hist, const uint2* __restrict__ list, const uint32_t* __restrict__ ctab,
     uint2* __restrict__ band_g, unsigned long long* __restrict__ bkey_g, uint8_t* __restrict__ flag_g,
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int topk,
@@ -444,12 +435,18 @@ __global__ __launch_bounds__(STPB) void k_select(
     const uint8_t* __restrict__ k_scale)
 {
     constexpr int RB = DT == 0 ? DI * 2 : (DT == 1 ? DI : DI / 2);     // bytes per key / query-head row
-    // MXFP4 (DT == 2): the band is rescored on exact bf16 copies of the query row and of each band key
-    __shared__ __attribute__((aligned(16))) uint16_t mxq[DT == 2 ? HI * DI : 2];
-    __shared__ __attribute__((aligned(16))) uint16_t mxk[DT == 2 ? STPB / 64 * DI : 2];
+    constexpr int SB = DT == 2 ? DI / 32 : 0;                          // MXFP4 scale bytes per row
+    // the query's HI rows (MXFP4: widened to exact bf16), its head weights, and the prefetched key rows
+    // (raw bytes, MXFP4 scales after them); MXFP4 band keys are widened per wave into mxk
+    __shared__ __attribute__((aligned(16))) uint8_t qs[DT == 2 ? HI * DI * 2 : HI * RB];
+    __shared__ float ws[HI];
+    __shared__ __attribute__((aligned(16))) uint8_t pk[PF_MAX][RB + SB];
+    __shared__ __attribute__((aligned(16))) uint16_t mxk[DT == 2 ? SEL_TPB / 64 * DI : 2];
+    __shared__ uint32_t pfe[PF_MAX], npf, ovf;
+    __shared__ uint8_t pslot[CAND_LDS];               // prefetch slot of each candidate (0xff: none)
     __shared__ uint32_t lh[BINS2];
-    __shared__ uint32_t scratch[STPB / 64], res[4], nband;
-    __shared__ uint32_t cpre[STPB + 1], cbase[STPB];
+    __shared__ uint32_t scratch[SEL_TPB / 64], res[4], nband;
+    __shared__ uint32_t cpre[2 * SEL_TPB + 1];
     __shared__ unsigned long long bkey[BAND_LDS];
     __shared__ uint32_t bpos[BAND_LDS];
     __shared__ uint2 bl[BAND_LDS];                    // band entries (index, position); more go to HBM
@@ -460,7 +457,7 @@ __global__ __launch_bounds__(STPB) void k_select(
     const int nv = row_visible(seq_lens, b, t, Tq, L, pos0, m, Nc);
     int32_t* out = idx_out + (size_t)r * topk;
     if (nv <= topk) {                                 // every visible entry is selected (no score is formed)
-        for (int i = tid; i < topk; i += STPB) {
+        for (int i = tid; i < topk; i += SEL_TPB) {
             out[i] = i < nv ? i : -1;
             if (score_out) score_out[(size_t)r * topk + i] = __builtin_nanf("");
         }
@@ -468,62 +465,150 @@ __global__ __launch_bounds__(STPB) void k_select(
         return;
     }
     const uint32_t* H = hist + (size_t)r * HIST_WORDS;
-    const float dmax = __uint_as_float(H[HW_DMAX]);
     const uint2* Lr = list + (size_t)r * NcP;
     uint8_t* F = flag_g + (size_t)r * NcP;
-    // chunk table -> prefix of counts in chunk (= index) order
+    const char* qrow = (const char*)q_idx + (size_t)r * HI * RB;
     const int NCH = NcP / CCHUNK;                     // <= 1024
+    // chunk counts first (the loads below stay in flight behind them)
+    const uint32_t c0 = 2 * tid < NCH ? ctab[(size_t)r * NCH + 2 * tid] : 0u;
+    const uint32_t c1 = 2 * tid + 1 < NCH ? ctab[(size_t)r * NCH + 2 * tid + 1] : 0u;
+    const uint32_t b1 = H[HW_B1], a1 = H[HW_A1];
+    const float dmax = __uint_as_float(H[HW_DMAX]);
+    // the query row and weights: loaded into registers now, written to LDS after the first barrier (a store
+    // right behind its load would hold its wave, and with it the barrier, for a memory round trip)
+    constexpr int QW = DT == 2 ? HI * RB / 4 : HI * RB / 16;   // code dwords (MXFP4) or 16-byte chunks
+    static_assert(QW <= SEL_TPB, "one staging word per thread");
+    u32x4_t qv = u32x4_t{0u, 0u, 0u, 0u};
+    uint32_t qd = 0u, qsb = 0u;
+    float wv = 0.f;
+    if (tid < QW) {
+        if constexpr (DT == 2) {
+            qd = ((const uint32_t*)qrow)[tid];
+            qsb = q_scale[((size_t)r * HI + (8 * tid) / DI) * (DI / 32) + ((8 * tid) % DI) / 32];
+        } else {
+            qv = ((const u32x4_t*)qrow)[tid];
+        }
+    }
+    if (tid < HI) wv = w_idx[(size_t)r * HI + tid];
+    // The first entries of every chunk's region are read before the counts are known (the regions start at
+    // fixed offsets), so the candidates cost no second dependent round trip: chunk c's first `spec` entries
+    // go to thread registers, spec = 2^ls <= 256 with NCH spec <= CAND_LDS / 2 (the reads cost time in
+    // proportion to their bytes: a chunk holding more than spec candidates costs one more round trip).
+    int ls = 8;
+    while (ls > 0 && (NCH << ls) > CAND_LDS / 2) --ls;
+    const uint32_t nspec = (uint32_t)NCH << ls;
+    constexpr int SPR = CAND_LDS / 2 / SEL_TPB;      // speculative entries per thread
+    uint2 sv[SPR];
+#pragma unroll
+    for (int u = 0; u < SPR; ++u) {
+        const uint32_t i = tid + u * SEL_TPB;
+        sv[u] = i < nspec ? Lr[(size_t)(i >> ls) * CCHUNK + (i & ((1u << ls) - 1))] : make_uint2(0u, 0u);
+    }
     uint32_t total;
-    {
-        const uint2 c = tid < NCH ? ctab[(size_t)r * NCH + tid] : make_uint2(0u, 0u);
-        const uint32_t pre = block_scan(c.y, scratch, &total);
-        if (tid < NCH) { cpre[tid] = pre; cbase[tid] = c.x; }
+    {   // thread tid owns chunks 2 tid and 2 tid + 1
+        if (tid == 0) { npf = 0; ovf = 0; }
+        const uint32_t pre = block_scan(c0 + c1, scratch, &total);
+        if (2 * tid < NCH) cpre[2 * tid] = pre;
+        if (2 * tid + 1 < NCH) cpre[2 * tid + 1] = pre + c0;
         if (tid == 0) cpre[NCH] = total;
+        if (max(c0, c1) > (1u << ls)) ovf = 1;       // a chunk holds more than its speculative part
         __syncthreads();
     }
+    if (tid < QW) {                                   // (read only after later barriers)
+        if constexpr (DT == 2)                        // eight elements of one 32-element block, widened exactly
+            *(u32x4_t*)&qs[(8 * tid) * 2] = fp4x8_to_bf16x8(qd, e8m0_scale(qsb));
+        else
+            ((u32x4_t*)qs)[tid] = qv;
+    }
+    if (tid < HI) ws[tid] = wv;
     const uint32_t n = total;
-    auto cand_g = [&](uint32_t e) -> uint2 {          // e-th candidate in index order, from HBM
-        int lo_c = 0, hi_c = NCH - 1;                 // largest c with cpre[c] <= e: a non-empty chunk holding e
+    auto chunk_of = [&](uint32_t e) -> int {          // largest c with cpre[c] <= e: a non-empty chunk holding e
+        int lo_c = 0, hi_c = NCH - 1;
         while (lo_c < hi_c) {
             const int mid = (lo_c + hi_c + 1) >> 1;
             if (cpre[mid] <= e) lo_c = mid; else hi_c = mid - 1;
         }
-        return Lr[cbase[lo_c] + (e - cpre[lo_c])];
+        return lo_c;
+    };
+    auto cand_g = [&](uint32_t e) -> uint2 {          // e-th candidate in index order, from HBM
+        const int c = chunk_of(e);
+        return Lr[(uint32_t)c * CCHUNK + (e - cpre[c])];
     };
     const bool inl = n <= (uint32_t)CAND_LDS;        // candidates and flags live in LDS (uniform)
     auto cand = [&](uint32_t e) -> uint2 { return inl ? cl[e] : cand_g(e); };
     auto fget = [&](uint32_t e) -> uint8_t { return inl ? fl[e] : F[e]; };
     auto fset = [&](uint32_t e, uint8_t f) { if (inl) fl[e] = f; else F[e] = f; };
 
-    // 1. tau: the bin b1 (level 1, found by k_collect), then b2 (level 2, built by k_collect), then the
-    //    last 8 bits.  The candidates are read once into LDS in the same pass as the level-2 histogram.
-    const uint32_t b1 = H[HW_B1], a1 = H[HW_A1];
-    for (int i = tid; i < BINS2; i += STPB) lh[i] = H[BINS1 + i];
-    if (inl)
-        for (uint32_t e = tid; e < n; e += STPB) cl[e] = cand_g(e);
+    // 1. tau to 24 bits: the bin b1 (level 1, found by k_collect), then key bits 19..8 (level 2) over the
+    //    candidates (every entry at or above b1 is one), built in the pass that puts them in LDS.
+    for (int i = tid; i < BINS2; i += SEL_TPB) lh[i] = 0;
     __syncthreads();
-    find_bin_wide(lh, (uint32_t)topk - a1, res, scratch);
-    const uint32_t b2 = res[0], a2 = res[1];
-    __syncthreads();
-    const uint32_t pfx = (b1 << 12) | b2;
-    for (int i = tid; i < 256; i += STPB) lh[i] = 0;
-    __syncthreads();
-    for (uint32_t e = tid; e < n; e += STPB) {
-        const uint32_t key = f32_key(__uint_as_float(cand(e).y));
-        if ((key >> 8) == pfx) atomicAdd(&lh[key & 255u], 1u);
+    auto level2 = [&](uint32_t y) {
+        const uint32_t key = f32_key(__uint_as_float(y));
+        if ((key >> 20) == b1) atomicAdd(&lh[(key >> 8) & (BINS2 - 1)], 1u);
+    };
+    if (inl) {
+        for (uint32_t e = tid; e < n; e += SEL_TPB) pslot[e] = 0xff;
+#pragma unroll
+        for (int u = 0; u < SPR; ++u) {
+            const uint32_t i = tid + u * SEL_TPB, c = i >> ls, j = i & ((1u << ls) - 1);
+            if (i < nspec && j < cpre[c + 1] - cpre[c]) { cl[cpre[c] + j] = sv[u]; level2(sv[u].y); }
+        }
+        if (ovf)                                      // the rest of the chunks that hold more
+            for (uint32_t e = tid; e < n; e += SEL_TPB) {
+                const int c = chunk_of(e);
+                const uint32_t j = e - cpre[c];
+                if (j >= (1u << ls)) {
+                    const uint2 v = Lr[(uint32_t)c * CCHUNK + j];
+                    cl[e] = v;
+                    level2(v.y);
+                }
+            }
+    } else {
+        for (uint32_t e = tid; e < n; e += SEL_TPB) level2(cand_g(e).y);
     }
     __syncthreads();
-    if (wave == 0) wave_find_bin256(lh, (uint32_t)topk - a1 - a2, 0u, res);
+    find_bin_wide(lh, (uint32_t)topk - a1, res, scratch);
+    const uint32_t pfx = (b1 << 12) | res[0];
+    // The k-th largest S~ lies in the level-2 bin [tlo, thi] and fewer than k entries lie above it, so the
+    // classification of the header holds with tau replaced by tlo on the "out" side and by thi on the "in"
+    // side: S~ < tlo - 2 Dmax is certainly out, S~ > thi + 2 Dmax certainly in.
+    const double lo = (double)key_f32(pfx << 8) - 2.0 * (double)dmax;
+    const double hi = (double)key_f32((pfx << 8) | 255u) + 2.0 * (double)dmax;
+    // fetch the band's key rows into LDS now: their loads overlap the classification
+    if (inl) {
+        for (uint32_t e = tid; e < n; e += SEL_TPB) {
+            const double x = (double)__uint_as_float(cl[e].y);
+            if (x >= lo && x <= hi) {
+                const uint32_t slot = atomicAdd(&npf, 1u);
+                if (slot < (uint32_t)PF_MAX) { pfe[slot] = cl[e].x; pslot[e] = (uint8_t)slot; }
+            }
+        }
+    }
     __syncthreads();
-    const float tau = key_f32((pfx << 8) | res[0]);
-    const double lo = (double)tau - 2.0 * (double)dmax, hi = (double)tau + 2.0 * (double)dmax;
+    // (held in registers: a barrier does not wait for loads, so they stay in flight until they are
+    //  written to LDS after the classification)
+    constexpr int CH = (RB + 15) / 16;                // 16-byte chunks per key row
+    constexpr int HU = (PF_MAX * CH + SEL_TPB - 1) / SEL_TPB;
+    const uint32_t np = min(npf, (uint32_t)PF_MAX);
+    u32x4_t hv[HU];
+    uint32_t hsc = 0;
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+        const uint32_t i = tid + u * SEL_TPB;
+        if (i < np * CH) {
+            const size_t krow = entry_row(pm, b, Nc, (int)pfe[i / CH]);
+            hv[u] = *(const u32x4_t*)((const char*)k_idx + krow * RB + 16 * (i % CH));
+        }
+    }
+    if (DT == 2 && tid < np) hsc = *(const uint32_t*)(k_scale + entry_row(pm, b, Nc, (int)pfe[tid]) * SB);
 
     // 2. classify: flag 1 = certainly in, 2 = band (listed with its position), 0 = out
     if (tid == 0) nband = 0;
     __syncthreads();
     uint2* Bg = band_g + (size_t)r * NcP;
     uint32_t my_in = 0;
-    for (uint32_t e = tid; e < n; e += STPB) {
+    for (uint32_t e = tid; e < n; e += SEL_TPB) {
         const uint2 c = cand(e);
         const double v = (double)__uint_as_float(c.y);
         uint8_t f = 0;
@@ -542,44 +627,41 @@ __global__ __launch_bounds__(STPB) void k_select(
     const uint32_t nb = nband;
     const uint32_t need = (uint32_t)topk - n_in;       // 0 <= need <= nb by construction
     auto band = [&](uint32_t i) -> uint2 { return i < (uint32_t)BAND_LDS ? bl[i] : Bg[i]; };
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+        const uint32_t i = tid + u * SEL_TPB;
+        if (i < np * CH) *(u32x4_t*)&pk[i / CH][16 * (i % CH)] = hv[u];
+    }
+    if (DT == 2 && tid < np) *(uint32_t*)&pk[tid][RB] = hsc;
+    __syncthreads();
 
-    // 3. exact rescoring of the band (one wave per entry); composite keys (exact score key,
-    //    inverted index): larger composite = earlier in the order
+    // 3. exact rescoring of the band (one wave per entry; the key row from LDS when it was prefetched);
+    //    composite keys (exact score key, inverted index): larger composite = earlier in the order
     unsigned long long* Kg = bkey_g + (size_t)r * NcP;
-    const char* qrow = (const char*)q_idx + (size_t)r * HI * RB;
-    const float* wrow = w_idx + (size_t)r * HI;
     if (need > 0 && need < nb) {
-        if constexpr (DT == 2) {                      // widen the query's HI rows (two elements per thread)
-            for (int e = tid; e < HI * DI / 2; e += STPB) {
-                const int hh = (2 * e) / DI, i = (2 * e) % DI;
-                const float sc = e8m0_scale(q_scale[((size_t)r * HI + hh) * (DI / 32) + i / 32]);
-                typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-                const uint32_t w = (uint32_t)(uint8_t)qrow[(size_t)hh * RB + i / 2];
-                *(uint32_t*)&mxq[hh * DI + i] =
-                    __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
-            }
-            __syncthreads();
-        }
-        for (uint32_t i = wave; i < nb; i += STPB / 64) {
+        for (uint32_t i = wave; i < nb; i += SEL_TPB / 64) {
             const uint2 be = band(i);
-            const size_t krow = entry_row(pm, b, Nc, (int)be.x);
+            const uint32_t ps = inl ? pslot[be.y] : 0xffu;
+            const size_t krow = ps == 0xffu ? entry_row(pm, b, Nc, (int)be.x) : 0;
             float sx;
             if constexpr (DT == 2) {
                 uint16_t* kw = mxk + wave * DI;
                 for (int e = lane; e < DI / 2; e += 64) {
-                    const float sc = e8m0_scale(k_scale[krow * (DI / 32) + (2 * e) / 32]);
+                    const uint32_t sb = ps == 0xffu ? k_scale[krow * SB + (2 * e) / 32] : pk[ps][RB + (2 * e) / 32];
+                    const float sc = e8m0_scale(sb);
                     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-                    const uint32_t w = (uint32_t)((const uint8_t*)k_idx)[krow * RB + e];
+                    const uint32_t w = ps == 0xffu ? (uint32_t)((const uint8_t*)k_idx)[krow * RB + e] : pk[ps][e];
                     *(uint32_t*)&kw[2 * e] =
                         __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
                 }
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                 __builtin_amdgcn_wave_barrier();
-                sx = wave_exact_score<0, DI, HI>(mxq, wrow, kw);
+                sx = wave_exact_score<0, DI, HI>(qs, ws, kw);
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                 __builtin_amdgcn_wave_barrier();   // the next band entry overwrites kw
             } else {
-                sx = wave_exact_score<DT, DI, HI>(qrow, wrow, (const char*)k_idx + krow * RB);
+                const void* kp = ps == 0xffu ? (const void*)((const char*)k_idx + krow * RB) : (const void*)pk[ps];
+                sx = wave_exact_score<DT, DI, HI>(qs, ws, kp);
             }
             if (lane == 0) {
                 const unsigned long long ck = ((unsigned long long)f32_key(sx) << 32) | (0xffffffffu - be.x);
@@ -592,9 +674,9 @@ __global__ __launch_bounds__(STPB) void k_select(
 
     // 4. the `need` largest composite keys among the band get flag 1
     if (need > 0 && need == nb) {
-        for (uint32_t i = tid; i < nb; i += STPB) fset(band(i).y, 1);
+        for (uint32_t i = tid; i < nb; i += SEL_TPB) fset(band(i).y, 1);
     } else if (need > 0 && nb <= BAND_LDS) {
-        for (uint32_t i = tid; i < nb; i += STPB) {          // rank by counting (keys are distinct)
+        for (uint32_t i = tid; i < nb; i += SEL_TPB) {          // rank by counting (keys are distinct)
             const unsigned long long ki = bkey[i];
             uint32_t rank = 0;
             for (uint32_t j = 0; j < nb; ++j) rank += bkey[j] > ki;
@@ -605,9 +687,9 @@ __global__ __launch_bounds__(STPB) void k_select(
         uint32_t ab = 0;
         for (int pass = 0; pass < 8; ++pass) {
             const int shift = 56 - 8 * pass;
-            for (int i = tid; i < 256; i += STPB) lh[i] = 0;
+            for (int i = tid; i < 256; i += SEL_TPB) lh[i] = 0;
             __syncthreads();
-            for (uint32_t i = tid; i < nb; i += STPB) {
+            for (uint32_t i = tid; i < nb; i += SEL_TPB) {
                 const unsigned long long key = Kg[i];
                 if (pass == 0 || (key >> (shift + 8)) == (kp >> (shift + 8))) atomicAdd(&lh[(key >> shift) & 255u], 1u);
             }
@@ -618,14 +700,14 @@ __global__ __launch_bounds__(STPB) void k_select(
             ab = res[1];
             __syncthreads();
         }
-        for (uint32_t i = tid; i < nb; i += STPB)
+        for (uint32_t i = tid; i < nb; i += SEL_TPB)
             if (Kg[i] >= kp) fset(band(i).y, 1);
     }
     __threadfence_block();
     __syncthreads();
 
     // 5. compaction in index order: thread tid owns positions [tid*per, (tid+1)*per)
-    const uint32_t per = (n + STPB - 1) / STPB;
+    const uint32_t per = (n + SEL_TPB - 1) / SEL_TPB;
     const uint32_t e0 = min(n, tid * per), e1 = min(n, e0 + per);
     uint32_t mine = 0;
     for (uint32_t e = e0; e < e1; ++e) mine += fget(e) == 1;
@@ -650,13 +732,13 @@ namespace csa_host {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// S~ [R][NcP] f32 | hist [R][HIST_WORDS] | list [R][NcP] (index, S~) | chunk table [R][NcP/CCHUNK] |
+// S~ [R][NcP] f32 | hist [R][HIST_WORDS] | list [R][NcP] (index, S~) | chunk counts [R][NcP/CCHUNK] u32 |
 // band [R][NcP] (index, position) | band keys [R][NcP] u64 | flags [R][NcP] u8
 static size_t decode_index_ws_bytes(int B, int Tq, int Nc) {
     const size_t R = (size_t)B * Tq;
     const size_t NcP = ((size_t)Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
     return align256(R * NcP * 4) + align256(R * HIST_WORDS * 4) + align256(R * NcP * 8) +
-           align256(R * (NcP / CCHUNK) * 8) + align256(R * NcP * 8) + align256(R * NcP * 8) + align256(R * NcP);
+           align256(R * (NcP / CCHUNK) * 4) + align256(R * NcP * 8) + align256(R * NcP * 8) + align256(R * NcP);
 }
 
 template <int DT, int DI, int HI>
@@ -670,7 +752,7 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
     float* S = (float*)p;                       p += align256(R * (size_t)NcP * 4);
     uint32_t* hist = (uint32_t*)p;              p += align256(R * HIST_WORDS * 4);
     uint2* list = (uint2*)p;                    p += align256(R * (size_t)NcP * 8);
-    uint2* ctab = (uint2*)p;                    p += align256(R * (size_t)(NcP / CCHUNK) * 8);
+    uint32_t* ctab = (uint32_t*)p;              p += align256(R * (size_t)(NcP / CCHUNK) * 4);
     uint2* band = (uint2*)p;                    p += align256(R * (size_t)NcP * 8);
     unsigned long long* bkey = (unsigned long long*)p; p += align256(R * (size_t)NcP * 8);
     uint8_t* flags = (uint8_t*)p;
@@ -691,7 +773,7 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
                    q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm, q_scale, k_scale);
     CSA_LAUNCH("k_collect", k_collect, dim3(NcP / CCHUNK, (unsigned)R), dim3(STPB), 0, st, S, hist, list, ctab, Tq,
                Nc, NcP, L, m, pos0, topk, seq_lens);
-    CSA_LAUNCH("k_select", (k_select<DT, DI, HI>), dim3((unsigned)R), dim3(STPB), 0, st, hist, list, ctab, band,
+    CSA_LAUNCH("k_select", (k_select<DT, DI, HI>), dim3((unsigned)R), dim3(SEL_TPB), 0, st, hist, list, ctab, band,
                bkey, flags, q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, topk, idx_out, cnt_out, score_out, seq_lens, pm,
                q_scale, k_scale);
     return 0;
