@@ -51,6 +51,7 @@ constexpr int HW_DMAX = BINS1;               // per row: the largest error bound
 constexpr int HW_B1 = BINS1 + 2, HW_A1 = BINS1 + 3;    // level-1 bin of tau; count above it
 constexpr int HIST_WORDS = BINS1 + 8;
 constexpr int TPB = 256;
+constexpr int KPW_MAX = 4096;               // keys per scoring workgroup, at most
 
 
 // Given a histogram in LDS (nb bins, nb % TPB == 0) find the bin b holding the
@@ -167,6 +168,9 @@ __global__ __launch_bounds__(TPB) void k_score(
 
     __shared__ uint32_t lh[2][BINS1];         // histograms of up to 2 rows of a group
     __shared__ uint32_t ldmax[2];
+    // the same rows' scores, written out in 16-byte stores after the key sweep (scattered 4-byte stores
+    // between the key loads cost the stream ~9% of its rate)
+    __shared__ __attribute__((aligned(16))) float lsc[2][KPW_MAX];
 
     const int b = blockIdx.y;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -301,7 +305,8 @@ __global__ __launch_bounds__(TPB) void k_score(
                     const int s = kbase + col;
                     if (writer && s < nv) {
                         const float sc = x + 0.0f;                        // canonical +0
-                        S[r * NcP + s] = sc;
+                        if (lrow < nlds) lsc[lrow][s - key0] = sc;
+                        else S[r * NcP + s] = sc;
                         const uint32_t key = f32_key(sc);
                         if (lrow < nlds) atomicAdd(&lh[lrow][key >> 20], 1u);
                         else atomicAdd(&hist[r * HIST_WORDS + (key >> 20)], 1u);
@@ -334,6 +339,13 @@ __global__ __launch_bounds__(TPB) void k_score(
             else atomicMax(&hist[r * HIST_WORDS + HW_DMAX], __float_as_uint(dmax_loc));
         }
         __syncthreads();
+        for (int lr = 0; lr < nlds; ++lr) {
+            const int nvr = row_visible(seq_lens, b, g * G + lr, Tq, L, pos0, m, Nc);
+            const int nk = nvr > topk ? min(keys_per_wg, nvr - key0) : 0;     // (key0 and NcP are multiples of 4)
+            float* Sr = S + ((size_t)b * Tq + g * G + lr) * NcP + key0;
+            for (int i = threadIdx.x; i < nk / 4; i += TPB) ((f32x4_t*)Sr)[i] = ((const f32x4_t*)lsc[lr])[i];
+            for (int i = (nk / 4) * 4 + threadIdx.x; i < nk; i += TPB) Sr[i] = lsc[lr][i];
+        }
         for (int lr = 0; lr < nlds; ++lr) {
             const size_t rr = (size_t)b * Tq + g * G + lr;
             for (int i = threadIdx.x; i < BINS1; i += TPB)
@@ -763,7 +775,7 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
     }
     // keys per scoring workgroup (4 waves x tiles of 16): the largest of 4096/2048/1024 that still
     // gives >= 512 workgroups (two per CU), so the grid runs in one round without a tail
-    int kpw = 4096;
+    int kpw = KPW_MAX;
     while (kpw > 1024 && (size_t)((Nc + kpw - 1) / kpw) * B < 512) kpw >>= 1;
     if (pm.table)
         CSA_LAUNCH("k_score", (k_score<DT, DI, HI, true>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
