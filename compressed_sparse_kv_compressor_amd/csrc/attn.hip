@@ -258,10 +258,12 @@ constexpr int ATT_TILES = 3;      // tile buffers; a split's tile count is a mul
 
 // MODE 0: dense prefix (row r = entry r); MODE 1: selected entries then window rows.  Every array must
 // be within reach of 32-bit byte offsets: tiles are moved by buffer loads only, which keeps the LDS wait
-// counting exact in the main loop (larger arrays run the generic kernel).
+// counting exact in the main loop (larger arrays run the generic kernel).  PAGED: the selected entries go
+// through the page map (a compile-time switch: the page-map code in the tile loop cost the batch-major
+// kernel half its rate).
 typedef float SxArr[4][4][64][4];         // score exchange [wave][j/4][lane][j%4] (one parity)
 
-template <int MODE>
+template <int MODE, bool PAGED>
 __device__ __forceinline__ void attn64_body(
     int bid, uint16_t* bufA, uint16_t* bufB, uint16_t* bufC, SxArr* sx,
     const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
@@ -306,8 +308,8 @@ __device__ __forceinline__ void attn64_body(
     const int ntiles = s_begin < nrows ? rps / TILE : 0;
 
     // paged entries address the whole pool (the page map gives pool rows); batch-major ones this sequence's
-    const uint16_t* kvb = R.kv ? (R.pm.table ? R.kv : R.kv + (size_t)b * R.N * D) : nullptr;
-    const size_t kv_rows = R.pm.table ? (size_t)R.pm.nblocks << R.pm.eshift : (size_t)R.N;
+    const uint16_t* kvb = R.kv ? (PAGED ? R.kv : R.kv + (size_t)b * R.N * D) : nullptr;
+    const size_t kv_rows = PAGED ? (size_t)R.pm.nblocks << R.pm.eshift : (size_t)R.N;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
 
     bf16x8_t qreg[KS];
@@ -349,7 +351,7 @@ __device__ __forceinline__ void attn64_body(
             for (int i = 0; i < TILE / 2; ++i) {
                 const int r = r0 + 2 * i + rsub;
                 const int j = (r < s_end && r < R.topk) ? R.idx[(size_t)bt * R.topk + r] : -1;
-                code[i] = j >= 0 && R.pm.table ? (int)entry_row(R.pm, b, R.N, j) : j;
+                code[i] = PAGED && j >= 0 ? (int)entry_row(R.pm, b, R.N, j) : j;
             }
         }
     };
@@ -649,14 +651,14 @@ __device__ __forceinline__ void attn64_body(
     __shared__ __attribute__((aligned(1024))) uint16_t bufC[2 * TILE * HD];   \
     __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];
 
-template <int MODE>
+template <int MODE, bool PAGED>
 __global__ __launch_bounds__(TPB, 1) void k_attn64(
     const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
     int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse)
 {
     CSA_ATT64_LDS
-    attn64_body<MODE>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
+    attn64_body<MODE, PAGED>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
                            part_o, part_ml, out, lse);
 }
 
@@ -857,11 +859,14 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         const int nunits = BT * ns, HP = (H + 63) / 64;
         const int nblk = (nunits + 7) / 8 * 8 * HP;
         if (a.mode == 0)
-            CSA_LAUNCH(tag, k_attn64<0>, dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2,
-                       nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
+            CSA_LAUNCH(tag, (k_attn64<0, false>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0,
+                       sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
+        else if (a.pm.table)
+            CSA_LAUNCH(tag, (k_attn64<1, true>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0,
+                       sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
         else
-            CSA_LAUNCH(tag, k_attn64<1>, dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2,
-                       nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
+            CSA_LAUNCH(tag, (k_attn64<1, false>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0,
+                       sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse, R.sink);
