@@ -40,6 +40,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 // R.mode 0: dense prefix (row r = entry r); 1: selected entries, masked padding up to a whole tile,
 // then the raw window rows.  The mode is a uniform run-time value (one body serves both jobs of a
 // fused launch).
+template <bool PAGED>
 __device__ __forceinline__ void attn128_body(
     int bid, uint16_t* buf0, uint16_t* buf1, uint16_t* buf2, uint16_t* buf3, int* rcode,
     const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
@@ -89,15 +90,15 @@ __device__ __forceinline__ void attn128_body(
             if (MODE == 0) v = r;
             else if (r < R.topk) v = R.idx[(size_t)bt * R.topk + r];
             else if (r >= topk32) v = raw_first + (r - topk32);
-            if (R.pm.table && v >= 0 && (MODE == 0 || r < R.topk)) v = (int)entry_row(R.pm, b, R.N, v);
+            if (PAGED && v >= 0 && (MODE == 0 || r < R.topk)) v = (int)entry_row(R.pm, b, R.N, v);
         }
         rcode[i] = v;
     }
     __syncthreads();
 
     // paged entries address the whole pool (the staged rows are pool rows); batch-major ones this sequence's
-    const uint16_t* kvb = R.kv ? (R.pm.table ? R.kv : R.kv + (size_t)b * R.N * D) : nullptr;
-    const size_t kv_rows = R.pm.table ? (size_t)R.pm.nblocks << R.pm.eshift : (size_t)R.N;
+    const uint16_t* kvb = R.kv ? (PAGED ? R.kv : R.kv + (size_t)b * R.N * D) : nullptr;
+    const size_t kv_rows = PAGED ? (size_t)R.pm.nblocks << R.pm.eshift : (size_t)R.N;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
     const __amdgpu_buffer_rsrc_t rs_kv = make_rsrc(kvb, kvb ? (uint32_t)(kv_rows * ROWB) : 0u);
     const __amdgpu_buffer_rsrc_t rs_raw = make_rsrc(rawb, rawb ? (uint32_t)((size_t)R.Lr * ROWB) : 0u);
@@ -415,12 +416,13 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
 // Two job slots: workgroups [0, nblk_s) run job s, the rest job d; one job is launched with every workgroup
 // below nblk_s.  (With the parameters selected per workgroup like this the compiler allocates the body's
 // registers without spills; with the job's fields passed straight in it spilled ~100 VGPRs.)
+template <bool PAGED>
 __global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, int nblk_s)
 {
     CSA_A128_LDS
     const bool first = (int)blockIdx.x < nblk_s;
     const AttnJob& j = first ? js : jd;
-    attn128_body(first ? blockIdx.x : blockIdx.x - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
+    attn128_body<PAGED>(first ? blockIdx.x : blockIdx.x - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
                  j.pos0, j.scale_log2, j.nunits, j.nsplit, j.rps, j.part_o, j.part_ml, j.out, j.lse);
 }
 #undef CSA_A128_LDS
@@ -439,7 +441,9 @@ namespace csa_host {
 int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag) {
     const int HQ = j.H / 128, BT = j.nunits / j.nsplit;
     const int nblk = j.nunits * HQ;
-    CSA_LAUNCH(tag, k_attn128, dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
+    // (paged entries: a compile-time switch, so that the batch-major kernel carries no page-map code)
+    if (j.R.pm.table) CSA_LAUNCH(tag, k_attn128<true>, dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
+    else CSA_LAUNCH(tag, k_attn128<false>, dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
     if (j.nsplit > 1) CSA_LAUNCH("k_combine", k_combine128, dim3(32, HQ, BT), dim3(256), 0, st, j);
     return 0;
 }
