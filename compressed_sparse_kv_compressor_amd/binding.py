@@ -46,8 +46,8 @@ def _load():
         "csa_index_topk": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, Z, P], I),
         "csa_index_topk_ex_ws_bytes": ([I, I, I, I, I, I, I, P], Z),
         "csa_index_topk_ex": ([P, P, P, I, I, I, I, I, I, LL, I, LL, I, P, P, P, P, P, P, P, Z, P], I),
-        "csa_sparse_attn_ex": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, LL, LL, I, F, P, P, I, P, P, P, Z, P], I),
-        "hca_dense_attn_ex": ([P, P, P, I, I, I, I, I, LL, I, LL, F, P, P, I, P, P, P, Z, P], I),
+        "csa_sparse_attn_ex": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, LL, LL, I, F, P, P, I, P, P, P, P, Z, P], I),
+        "hca_dense_attn_ex": ([P, P, P, I, I, I, I, I, LL, I, LL, F, P, P, I, P, P, P, P, Z, P], I),
         "csa_kv_fp8_encode": ([P, LL, I, P, P], I),
         "csa_mxfp4_encode": ([P, LL, I, P, P, P], I),
         "csa_sparse_attn_ws_bytes": ([I, I, I, I, I, I], Z),
@@ -108,6 +108,16 @@ def _lay(layout):
     return None if layout is None else ctypes.byref(layout)
 
 
+class RopeSpec(ctypes.Structure):
+    """Mirror of csa_rope_t: the fused rotary embedding of an attention call (rd = 64)."""
+    _fields_ = [("rd", ctypes.c_int), ("theta", ctypes.c_double)]
+
+
+def _rope(rope):
+    """None, or (rd, theta) -> a csa_rope_t the call can point at."""
+    return None if rope is None else RopeSpec(rd=int(rope[0]), theta=float(rope[1]))
+
+
 class DecodeArgs(ctypes.Structure):
     """Mirror of csa_hca_decode_args_t."""
     _fields_ = [
@@ -123,6 +133,7 @@ class DecodeArgs(ctypes.Structure):
         ("hca_out", ctypes.c_void_p), ("hca_lse", ctypes.c_void_p), ("hca_sink", ctypes.c_void_p),
         ("layout", ctypes.POINTER(CacheLayout)),
         ("q_idx_scale", ctypes.c_void_p), ("k_idx_scale", ctypes.c_void_p),
+        ("csa_rope", ctypes.POINTER(RopeSpec)), ("hca_rope", ctypes.POINTER(RopeSpec)),
     ]
 
 
@@ -232,10 +243,11 @@ def _sink(sink, H: int):
 
 
 def csa_sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, out, lse_out=None, ws=None,
-                    stream=None, sink=None, v=None, v_raw=None, layout=None, m: int = 1, Nc=None, kv_format=KV_BF16):
+                    stream=None, sink=None, v=None, v_raw=None, layout=None, m: int = 1, Nc=None, kv_format=KV_BF16,
+                    rope=None):
     """v, v_raw: separate values (or None); layout (make_layout): variable-length batch and/or paged entries
     (kv and v are then pools of ratio m; Nc = the entries per sequence the idx refer to); kv_format KV_FP8: kv
-    (and v) rows in the FP8 format (csa_kv_fp8_encode)."""
+    (and v) rows in the FP8 format (csa_kv_fp8_encode); rope = (rd, theta): the fused rotary embedding."""
     B, Tq, H, D = q.shape
     if Nc is None:
         Nc = kv.shape[1] if kv is not None else 0
@@ -244,14 +256,15 @@ def csa_sparse_attn(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: flo
     need = lib.csa_sparse_attn_ws_bytes(B, Tq, H, D, topk, W)
     if ws is None:
         ws = workspace(need, q.device)
-    if layout is None and v is None and v_raw is None and kv_format == KV_BF16:
+    if layout is None and v is None and v_raw is None and kv_format == KV_BF16 and rope is None:
         _check(lib.csa_sparse_attn(_p(q), _p(kv), _p(idx), _p(kv_raw), B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W,
                                    float(scale), _sink(sink, H), _p(out), _p(lse_out), _p(ws),
                                    0 if ws is None else ws.numel(), _stream(stream)))
     else:
         _check(lib.csa_sparse_attn_ex(_p(q), _p(kv), _p(v), _p(idx), _p(kv_raw), _p(v_raw), B, Tq, H, D, Nc, m, topk,
-                                      Lr, raw0, pos0, W, float(scale), _sink(sink, H), _lay(layout), kv_format, _p(out),
-                                      _p(lse_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+                                      Lr, raw0, pos0, W, float(scale), _sink(sink, H), _lay(layout), kv_format,
+                                      _lay(_rope(rope)), _p(out), _p(lse_out), _p(ws), 0 if ws is None else ws.numel(),
+                                      _stream(stream)))
 
 
 def csa_sparse_attn_noalloc(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, scale: float, out, lse_out=None,
@@ -266,26 +279,28 @@ def csa_sparse_attn_noalloc(q, kv, idx, kv_raw, raw0: int, pos0: int, W: int, sc
 
 
 def hca_dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, out, lse_out=None, ws=None, stream=None,
-                   sink=None, v_h=None, layout=None, kv_format=KV_BF16):
+                   sink=None, v_h=None, layout=None, kv_format=KV_BF16, rope=None):
     """v_h: separate values (or None); layout (make_layout): variable-length batch (L = capacity) and/or a
-    paged pool kv_h of ratio mh; kv_format KV_FP8: FP8 entry rows."""
+    paged pool kv_h of ratio mh; kv_format KV_FP8: FP8 entry rows; rope = (rd, theta): the fused rotary
+    embedding."""
     B, Tq, H, D = q.shape
     Nh = -(-L // mh) if (layout is not None and layout.block_table) else kv_h.shape[1]
     need = lib.hca_dense_attn_ws_bytes(B, Tq, H, D, Nh)
     if ws is None:
         ws = workspace(need, q.device)
-    if layout is None and v_h is None and kv_format == KV_BF16:
+    if layout is None and v_h is None and kv_format == KV_BF16 and rope is None:
         _check(lib.hca_dense_attn(_p(q), _p(kv_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale), _sink(sink, H),
                                   _p(out), _p(lse_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     else:
         _check(lib.hca_dense_attn_ex(_p(q), _p(kv_h), _p(v_h), B, Tq, H, D, Nh, L, mh, pos0, float(scale),
-                                     _sink(sink, H), _lay(layout), kv_format, _p(out), _p(lse_out), _p(ws),
-                                     0 if ws is None else ws.numel(), _stream(stream)))
+                                     _sink(sink, H), _lay(layout), kv_format, _lay(_rope(rope)), _p(out),
+                                     _p(lse_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def make_decode_args(*, L, scale, csa_q, q_idx, w_idx, k_idx, kv, kv_raw, idx_dtype, m, topk, W, csa_out,
                      hca_q, kv_h, mh, hca_out, csa_lse=None, hca_lse=None, idx_out=None, csa_sink=None,
-                     hca_sink=None, layout=None, q_idx_scale=None, k_idx_scale=None) -> DecodeArgs:
+                     hca_sink=None, layout=None, q_idx_scale=None, k_idx_scale=None, csa_rope=None,
+                     hca_rope=None) -> DecodeArgs:
     B, H, D = csa_q.shape[0], csa_q.shape[-2], csa_q.shape[-1]
     HI, dI = q_idx.shape[-2], q_idx.shape[-1] * (2 if idx_dtype == MXFP4 else 1)
     args = DecodeArgs(B=B, L=L, H=H, D=D, scale=float(scale), csa_q=_p(csa_q), q_idx=_p(q_idx), w_idx=_p(w_idx),
@@ -295,9 +310,14 @@ def make_decode_args(*, L, scale, csa_q, q_idx, w_idx, k_idx, kv, kv_raw, idx_dt
                       hca_lse=_p(hca_lse), hca_sink=_sink(hca_sink, hca_q.shape[-2]),
                       layout=None if layout is None else ctypes.pointer(layout), q_idx_scale=_p(q_idx_scale),
                       k_idx_scale=_p(k_idx_scale))
+    crope, hrope = _rope(csa_rope), _rope(hca_rope)
+    if crope is not None:
+        args.csa_rope = ctypes.pointer(crope)
+    if hrope is not None:
+        args.hca_rope = ctypes.pointer(hrope)
     # the struct holds bare device addresses: keep every tensor they point into alive as long as the struct
     args._keep = (csa_q, q_idx, w_idx, k_idx, kv, kv_raw, csa_out, csa_lse, idx_out, csa_sink, hca_q, kv_h, hca_out,
-                  hca_lse, hca_sink, layout, q_idx_scale, k_idx_scale)
+                  hca_lse, hca_sink, layout, q_idx_scale, k_idx_scale, crope, hrope)
     return args
 
 

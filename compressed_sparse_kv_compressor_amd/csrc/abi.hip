@@ -457,11 +457,24 @@ size_t csa_sparse_attn_ws_bytes(int B, int Tq, int H, int D, int topk, int W) {
     return csa_host::attn_ws_bytes(B, Tq, H, D, 1, topk, W);
 }
 
+// The fused rotary embedding (csa_rope_t) of an attention call: NULL = none.
+static int read_rope(const char* fn, const csa_rope_t* rope, int D, csa_host::AttnRows& r) {
+    r.rope_rd = 0;
+    r.rope_theta = 0.0;
+    if (!rope) return CSA_OK;
+    REQ(rope->rd == 64 && D >= 64, CSA_ERR_UNSUPPORTED, "%s: the fused rotary embedding covers rd = 64 (got %d)", fn,
+        rope->rd);
+    REQ(std::isfinite(rope->theta) && rope->theta > 1.0, CSA_ERR_SHAPE, "%s: rope theta must be finite and > 1", fn);
+    r.rope_rd = rope->rd;
+    r.rope_theta = rope->theta;
+    return CSA_OK;
+}
+
 static int sparse_impl(const char* fn, const void* q, const void* kv, const void* v, const int32_t* idx,
                        const void* kv_raw, const void* v_raw, int B, int Tq, int H, int D, int Nc, int m, int topk,
                        int Lr, long long raw0, long long pos0, int W, float scale, const float* sink,
-                       const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       const csa_cache_layout_t* layout, int kv_format, const csa_rope_t* rope, void* out,
+                       float* lse_out, void* ws, size_t ws_bytes, void* stream) {
     csa_host::g_err[0] = 0;
     const bool varlen = layout && layout->seq_lens;
     int rc = validate_sparse(fn, q, kv, idx, kv_raw, B, Tq, H, D, Nc, topk, Lr, raw0, pos0, W, scale, out, lse_out,
@@ -482,6 +495,8 @@ static int sparse_impl(const char* fn, const void* q, const void* kv, const void
     r.pm = csa_host::page_map(lay, m);
     REQ(kv_format == CSA_KV_BF16 || kv_format == CSA_KV_FP8, CSA_ERR_DTYPE, "%s: kv_format %d unknown", fn, kv_format);
     r.kv_fp8 = kv_format == CSA_KV_FP8;
+    rc = read_rope(fn, rope, D, r);
+    if (rc) return rc;
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
                                  "k_attn_sparse");
 }
@@ -490,15 +505,16 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
                     int Nc, int topk, int Lr, long long raw0, long long pos0, int W, float scale, const float* sink,
                     void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
     return sparse_impl("csa_sparse_attn", q, kv, nullptr, idx, kv_raw, nullptr, B, Tq, H, D, Nc, 1, topk, Lr, raw0, pos0,
-                       W, scale, sink, nullptr, CSA_KV_BF16, out, lse_out, ws, ws_bytes, stream);
+                       W, scale, sink, nullptr, CSA_KV_BF16, nullptr, out, lse_out, ws, ws_bytes, stream);
 }
 
 int csa_sparse_attn_ex(const void* q, const void* kv, const void* v, const int32_t* idx, const void* kv_raw,
                        const void* v_raw, int B, int Tq, int H, int D, int Nc, int m, int topk, int Lr, long long raw0,
                        long long pos0, int W, float scale, const float* sink, const csa_cache_layout_t* layout,
-                       int kv_format, void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+                       int kv_format, const csa_rope_t* rope, void* out, float* lse_out, void* ws, size_t ws_bytes,
+                       void* stream) {
     return sparse_impl("csa_sparse_attn_ex", q, kv, v, idx, kv_raw, v_raw, B, Tq, H, D, Nc, m, topk, Lr, raw0, pos0, W,
-                       scale, sink, layout, kv_format, out, lse_out, ws, ws_bytes, stream);
+                       scale, sink, layout, kv_format, rope, out, lse_out, ws, ws_bytes, stream);
 }
 
 // As csa_sparse_attn, with the split partials in the library's static scratch instead of a workspace.
@@ -530,8 +546,8 @@ size_t hca_dense_attn_ws_bytes(int B, int Tq, int H, int D, int Nh) {
 
 static int dense_impl(const char* fn, const void* q, const void* kv_h, const void* v_h, int B, int Tq, int H, int D,
                       int Nh, long long L, int mh, long long pos0, float scale, const float* sink,
-                      const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      const csa_cache_layout_t* layout, int kv_format, const csa_rope_t* rope, void* out,
+                      float* lse_out, void* ws, size_t ws_bytes, void* stream) {
     csa_host::g_err[0] = 0;
     int rc = validate_dense(fn, q, kv_h, B, Tq, H, D, Nh, L, mh, pos0, scale, out, lse_out);
     if (rc) return rc;
@@ -547,6 +563,8 @@ static int dense_impl(const char* fn, const void* q, const void* kv_h, const voi
     r.pm = csa_host::page_map(lay, mh);
     REQ(kv_format == CSA_KV_BF16 || kv_format == CSA_KV_FP8, CSA_ERR_DTYPE, "%s: kv_format %d unknown", fn, kv_format);
     r.kv_fp8 = kv_format == CSA_KV_FP8;
+    rc = read_rope(fn, rope, D, r);
+    if (rc) return rc;
     return csa_host::attn_launch(q, r, B, Tq, H, D, pos0, scale, out, lse_out, ws, ws_bytes, (hipStream_t)stream,
                                  "k_attn_dense");
 }
@@ -555,15 +573,15 @@ int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D,
                    long long pos0, float scale, const float* sink, void* out, float* lse_out, void* ws,
                    size_t ws_bytes, void* stream) {
     return dense_impl("hca_dense_attn", q, kv_h, nullptr, B, Tq, H, D, Nh, L, mh, pos0, scale, sink, nullptr,
-                      CSA_KV_BF16, out, lse_out, ws, ws_bytes, stream);
+                      CSA_KV_BF16, nullptr, out, lse_out, ws, ws_bytes, stream);
 }
 
 int hca_dense_attn_ex(const void* q, const void* kv_h, const void* v_h, int B, int Tq, int H, int D, int Nh,
                       long long L, int mh, long long pos0, float scale, const float* sink,
-                      const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      const csa_cache_layout_t* layout, int kv_format, const csa_rope_t* rope, void* out,
+                      float* lse_out, void* ws, size_t ws_bytes, void* stream) {
     return dense_impl("hca_dense_attn_ex", q, kv_h, v_h, B, Tq, H, D, Nh, L, mh, pos0, scale, sink, layout, kv_format,
-                      out, lse_out, ws, ws_bytes, stream);
+                      rope, out, lse_out, ws, ws_bytes, stream);
 }
 
 // Fused decode: workspace = [idx (if not caller-owned)] [index_topk ws] [attention ws (max of both layers)]
@@ -625,6 +643,10 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     rs.seq_lens = rd.seq_lens = lay.seq_lens;
     rs.pm = csa_host::page_map(lay, a->m);
     rd.pm = csa_host::page_map(lay, a->mh);
+    rc = read_rope(fn, a->csa_rope, a->D, rs);
+    if (rc) return rc;
+    rc = read_rope(fn, a->hca_rope, a->D, rd);
+    if (rc) return rc;
     // the CSA layer's attention, then the HCA layer's (layer order: a real next layer's query depends on the
     // previous layer's output, so the two are never overlapped)
     const size_t sws = align256(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 1, a->topk, a->W));

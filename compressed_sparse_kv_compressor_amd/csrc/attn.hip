@@ -39,7 +39,7 @@ constexpr int TPB = 256;
 struct RowSet {
     int n;
     int b, bt;
-    long long w0, raw0;
+    long long w0, raw0, p;
     __device__ const char* row(const Rows& R, int r, int D, bool value, bool& ent) const {
         const size_t eb = R.kv_fp8 ? (size_t)D + 80 : (size_t)D * 2;
         const char* base = (const char*)(value && R.v ? R.v : R.kv);
@@ -80,6 +80,7 @@ __device__ __forceinline__ RowSet make_rowset(const Rows& R, int bt, int Tq, lon
     s.b = bt / Tq;
     int nd;
     const long long p = row_geo(R, s.b, bt % Tq, Tq, pos0, s.raw0, nd);
+    s.p = p;
     if (R.mode == 0) {
         s.n = nd;
         s.w0 = 0;
@@ -90,7 +91,7 @@ __device__ __forceinline__ RowSet make_rowset(const Rows& R, int bt, int Tq, lon
     return s;
 }
 
-template <int D, bool SEPV, bool FP8>
+template <int D, bool SEPV, bool FP8, bool ROPE>
 __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q, Rows R, int Tq, int H,
                                                   long long pos0, float scale_log2, int nsplit, int rps,
                                                   float* __restrict__ part_o, float2* __restrict__ part_ml,
@@ -121,6 +122,11 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
         const uint16_t* qp = q + ((size_t)bt * H + h) * D + 8 * grp;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) qreg[s] = as_bf16x8(*(const u32x4_t*)(qp + 32 * s));
+        if constexpr (ROPE) {                   // fused rotary embedding of the last 64 dims, at +p
+#pragma unroll
+            for (int s = KSTEPS - ROPE_FUSED_RD / 32; s < KSTEPS; ++s)
+                qreg[s] = as_bf16x8(rope8(__builtin_bit_cast(u32x4_t, qreg[s]), 32 * s + 8 * grp, D, R, (double)rs.p));
+        }
     }
     f32x4_t acc[DT];
 #pragma unroll
@@ -215,6 +221,13 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
     if (nsplit == 1) {
         float lse_v;
         const float inv = sink_norm(m_run, l_run, sink_log2(R.sink, h), lse_v);
+        if constexpr (ROPE) {                   // the output's last 64 dims turn back by -p
+#pragma unroll
+            for (int d = DT - ROPE_FUSED_RD / 16; d < DT; ++d) {
+                CSA_ROPE_PAIR(acc[d], 0, 1, d * 16 + 4 * grp, D, R, -(double)rs.p)
+                CSA_ROPE_PAIR(acc[d], 2, 3, d * 16 + 4 * grp + 2, D, R, -(double)rs.p)
+            }
+        }
         uint16_t* op = out + ((size_t)bt * H + h) * D + 4 * grp;
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
@@ -263,7 +276,7 @@ constexpr int ATT_TILES = 3;      // tile buffers; a split's tile count is a mul
 // kernel half its rate).
 typedef float SxArr[4][4][64][4];         // score exchange [wave][j/4][lane][j%4] (one parity)
 
-template <int MODE, bool PAGED>
+template <int MODE, bool PAGED, bool ROPE>
 __device__ __forceinline__ void attn64_body(
     int bid, uint16_t* bufA, uint16_t* bufB, uint16_t* bufC, SxArr* sx,
     const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
@@ -317,6 +330,11 @@ __device__ __forceinline__ void attn64_body(
         const uint16_t* qp = q + ((size_t)bt * H + (hv ? h : 0)) * D + dh * HD + 8 * g;
 #pragma unroll
         for (int s = 0; s < KS; ++s) qreg[s] = hv ? as_bf16x8(*(const u32x4_t*)(qp + 16 * s)) : as_bf16x8(u32x4_t{0, 0, 0, 0});
+        if (ROPE && dh == 1) {                  // fused rotary embedding of the last 64 dims, at +p
+#pragma unroll
+            for (int s = KS - ROPE_FUSED_RD / 16; s < KS; ++s)
+                qreg[s] = as_bf16x8(rope8(__builtin_bit_cast(u32x4_t, qreg[s]), HD + 16 * s + 8 * g, D, R, (double)p));
+        }
     }
     const bf16x8_t qmask = as_bf16x8(u32x4_t{g == 0 && dh == 0 ? BF16_NEG_2P100 : 0u, 0u, 0u, 0u});
     f32x16_t acc[DT];
@@ -618,6 +636,15 @@ __device__ __forceinline__ void attn64_body(
     if (nsplit == 1) {
         float lse_v;
         const float inv = sink_norm(m_run, l_run, sink_log2(R.sink, h), lse_v);
+        if (ROPE && dh == 1) {                  // the output's last 64 dims turn back by -p
+#pragma unroll
+            for (int d = DT - ROPE_FUSED_RD / 32; d < DT; ++d)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    CSA_ROPE_PAIR(acc[d], 4 * q4, 4 * q4 + 1, HD + d * 32 + 8 * q4 + 4 * g, D, R, -(double)p)
+                    CSA_ROPE_PAIR(acc[d], 4 * q4 + 2, 4 * q4 + 3, HD + d * 32 + 8 * q4 + 4 * g + 2, D, R, -(double)p)
+                }
+        }
         uint16_t* op = out + ((size_t)bt * H + h) * D + dh * HD + 4 * g;
 #pragma unroll
         for (int d = 0; d < DT; ++d)
@@ -651,14 +678,14 @@ __device__ __forceinline__ void attn64_body(
     __shared__ __attribute__((aligned(1024))) uint16_t bufC[2 * TILE * HD];   \
     __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];
 
-template <int MODE, bool PAGED>
+template <int MODE, bool PAGED, bool ROPE>
 __global__ __launch_bounds__(TPB, 1) void k_attn64(
     const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
     int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse)
 {
     CSA_ATT64_LDS
-    attn64_body<MODE, PAGED>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
+    attn64_body<MODE, PAGED, ROPE>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
                            part_o, part_ml, out, lse);
 }
 
@@ -670,7 +697,8 @@ __global__ __launch_bounds__(TPB, 1) void k_attn64(
 template <int D>
 __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
                                              int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
-                                             const float* __restrict__ sink, int h, int bt)
+                                             const float* __restrict__ sink, int h, int bt, const Rows& R, int Tq,
+                                             long long pos0)
 {
     const int d = threadIdx.x * 4;
     const size_t s0 = (size_t)bt * nsplit * H + h;     // slot of split 0; split s at s0 + s H
@@ -706,6 +734,13 @@ __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, c
     }
     float lse_v;
     const float inv = sink_norm(M, l, sink_log2(sink, h), lse_v);
+    if (R.rope_rd && d + 4 > D - ROPE_FUSED_RD) {      // the output's last 64 dims turn back by -p
+        long long raw0;
+        int nd;
+        const double sp = -(double)row_geo(R, bt / Tq, bt % Tq, Tq, pos0, raw0, nd);
+        CSA_ROPE_PAIR(o, 0, 1, d, D, R, sp)
+        CSA_ROPE_PAIR(o, 2, 3, d + 2, D, R, sp)
+    }
     uint2 v;
     v.x = (uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16);
     v.y = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
@@ -716,9 +751,9 @@ __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, c
 template <int D>
 __global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
                                                    int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                   const float* __restrict__ sink)
+                                                   const float* __restrict__ sink, Rows R, int Tq, long long pos0)
 {
-    combine_body<D>(part_o, part_ml, H, nsplit, out, lse, sink, blockIdx.x, blockIdx.y);
+    combine_body<D>(part_o, part_ml, H, nsplit, out, lse, sink, blockIdx.x, blockIdx.y, R, Tq, pos0);
 }
 
 }  // namespace
@@ -819,6 +854,8 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     R.v = (const uint16_t*)a.v;
     R.v_raw = (const uint16_t*)a.v_raw;
     R.kv_fp8 = a.kv_fp8;
+    R.rope_rd = a.rope_rd;
+    R.rope_l2t = a.rope_rd ? log2(a.rope_theta) : 0.0;
     const int BT = B * Tq;
     const int max_rows = a.mode == 0 ? a.N : attn_rows(1, H, D, a.topk, a.W);
     int ns, rps;
@@ -846,8 +883,9 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         j.nsplit = a128_nsplit(r128, j.rps);
         j.nunits = BT * j.nsplit;
         j.out = (uint16_t*)out; j.lse = lse;
-        // k_attn128 applies an attention sink in its merge only: a sink with a single split runs k_attn64
-        if (!(R.sink && j.nsplit == 1)) {
+        // k_attn128 applies an attention sink and the output's rotation in its merge only: a sink or a rotation
+        // with a single split runs k_attn64
+        if (!((R.sink || R.rope_rd) && j.nsplit == 1)) {
             if (j.nsplit > 1) {
                 j.part_o = (float*)ws;
                 j.part_ml = (float2*)((char*)ws + align256((size_t)BT * j.nsplit * H * D * 4));
@@ -858,24 +896,29 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     if (use64(D, H) && !big32 && !sepv && !fp8 && !(a.pm.table && a.mode == 0)) {
         const int nunits = BT * ns, HP = (H + 63) / 64;
         const int nblk = (nunits + 7) / 8 * 8 * HP;
-        if (a.mode == 0)
-            CSA_LAUNCH(tag, (k_attn64<0, false>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0,
-                       sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
-        else if (a.pm.table)
-            CSA_LAUNCH(tag, (k_attn64<1, true>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0,
-                       sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
-        else
-            CSA_LAUNCH(tag, (k_attn64<1, false>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0,
-                       sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse);
+#define CSA_ATT64(MODE_, PAGED_, ROPE_)                                                                      \
+    CSA_LAUNCH(tag, (k_attn64<MODE_, PAGED_, ROPE_>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, \
+               sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse)
+        const bool rope = R.rope_rd != 0;
+        if (a.mode == 0) { if (rope) CSA_ATT64(0, false, true); else CSA_ATT64(0, false, false); }
+        else if (a.pm.table) { if (rope) CSA_ATT64(1, true, true); else CSA_ATT64(1, true, false); }
+        else { if (rope) CSA_ATT64(1, false, true); else CSA_ATT64(1, false, false); }
+#undef CSA_ATT64
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
-                       (uint16_t*)out, lse, R.sink);
+                       (uint16_t*)out, lse, R.sink, R, Tq, pos0);
         return 0;
     }
     dim3 grid(ns, (H + 63) / 64, BT);
 #define CSA_GENERIC(D_, S_, F_)                                                                            \
-    CSA_LAUNCH(tag, (k_attn<D_, S_, F_>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, sl2, ns, rps, \
-               part_o, part_ml, (uint16_t*)out, lse)
+    do {                                                                                                     \
+        if (R.rope_rd)                                                                                       \
+            CSA_LAUNCH(tag, (k_attn<D_, S_, F_, true>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, \
+                       sl2, ns, rps, part_o, part_ml, (uint16_t*)out, lse);                                  \
+        else                                                                                                 \
+            CSA_LAUNCH(tag, (k_attn<D_, S_, F_, false>), grid, dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, \
+                       sl2, ns, rps, part_o, part_ml, (uint16_t*)out, lse);                                  \
+    } while (0)
     if (D == 512) {
         if (sepv && fp8) CSA_GENERIC(512, true, true);
         else if (sepv) CSA_GENERIC(512, true, false);
@@ -883,7 +926,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         else CSA_GENERIC(512, false, false);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
-                       (uint16_t*)out, lse, R.sink);
+                       (uint16_t*)out, lse, R.sink, R, Tq, pos0);
     } else if (D == 128) {
         if (sepv && fp8) CSA_GENERIC(128, true, true);
         else if (sepv) CSA_GENERIC(128, true, false);
@@ -891,7 +934,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         else CSA_GENERIC(128, false, false);
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<128>, dim3(H, BT), dim3(32), 0, st, part_o, part_ml, H, ns,
-                       (uint16_t*)out, lse, R.sink);
+                       (uint16_t*)out, lse, R.sink, R, Tq, pos0);
     } else {
         return fail(6, "attention: D = %d unsupported", D);
     }

@@ -40,7 +40,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 // R.mode 0: dense prefix (row r = entry r); 1: selected entries, masked padding up to a whole tile,
 // then the raw window rows.  The mode is a uniform run-time value (one body serves both jobs of a
 // fused launch).
-template <bool PAGED>
+template <bool PAGED, bool ROPE>
 __device__ __forceinline__ void attn128_body(
     int bid, uint16_t* buf0, uint16_t* buf1, uint16_t* buf2, uint16_t* buf3, int* rcode,
     const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
@@ -108,6 +108,11 @@ __device__ __forceinline__ void attn128_body(
         const uint16_t* qp = q + ((size_t)bt * H + h) * D + 8 * g;
 #pragma unroll
         for (int s = 0; s < KS; ++s) qreg[s] = as_bf16x8(*(const u32x4_t*)(qp + 16 * s));
+        if constexpr (ROPE) {                   // fused rotary embedding of the last 64 dims, at +p
+#pragma unroll
+            for (int s = KS - ROPE_FUSED_RD / 16; s < KS; ++s)
+                qreg[s] = as_bf16x8(rope8(__builtin_bit_cast(u32x4_t, qreg[s]), 16 * s + 8 * g, D, R, (double)p));
+        }
     }
     const bf16x8_t qmask = as_bf16x8(u32x4_t{g == 0 ? BF16_NEG_2P100 : 0u, 0u, 0u, 0u});
     f32x16_t acc[DT];
@@ -295,8 +300,8 @@ __device__ __forceinline__ void attn128_body(
     }
     // lane holds O^T[d*32 + 8 (j/4) + 4 g + j%4][h]
     if (nsplit == 1) {
-        // (a launch with an attention sink and a single split runs k_attn64 instead; the sink of a split
-        // launch is applied by the merge)
+        // (a launch with an attention sink or the fused rotary embedding and a single split runs k_attn64
+        // instead; the sink and the output's rotation of a split launch are applied by the merge)
         const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
         uint16_t* op = out + ((size_t)bt * H + h) * D + 4 * g;
 #pragma unroll
@@ -352,7 +357,7 @@ __device__ __forceinline__ __attribute__((ext_vector_type(2))) _Float16 as_f16x2
 __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ part, const float2* __restrict__ part_ml,
                                                 int H, int nsplit, uint16_t* __restrict__ out,
                                                 float* __restrict__ lse, const float* __restrict__ sink, int bt,
-                                                int hq, int tid)
+                                                int hq, int tid, const Rows& R, int Tq, long long pos0)
 {
     const int HQ = H >> 7;
     const int w = tid >> 11, c = (tid >> 6) & 31, lane = tid & 63;
@@ -398,7 +403,15 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
     float lse_v;
     const float inv = sink_norm(M, l, sink_log2(sink, h), lse_v);
     // o[jj] is O^T[d][h] at d = 32 (c / 2) + 8 ((8 (c % 2) + jj) / 4) + 4 g + jj % 4: two runs of 4
-    uint16_t* op = out + ((size_t)bt * H + h) * 512 + 32 * (c >> 1) + 16 * (c & 1) + 4 * g;
+    const int d0 = 32 * (c >> 1) + 16 * (c & 1) + 4 * g;
+    if (R.rope_rd && d0 + 12 > 512 - ROPE_FUSED_RD) {     // the output's last 64 dims turn back by -p
+        long long raw0;
+        int nd;
+        const double sp = -(double)row_geo(R, bt / Tq, bt % Tq, Tq, pos0, raw0, nd);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) CSA_ROPE_PAIR(o, 2 * (k & 1) + 4 * (k >> 1), 2 * (k & 1) + 4 * (k >> 1) + 1, d0 + 2 * (k & 1) + 8 * (k >> 1), 512, R, sp)
+    }
+    uint16_t* op = out + ((size_t)bt * H + h) * 512 + d0;
     *(uint2*)op = make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
     *(uint2*)(op + 8) = make_uint2(pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv));
     if (lse && c == 0 && g == 0) lse[(size_t)bt * H + h] = lse_v;
@@ -416,13 +429,13 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
 // Two job slots: workgroups [0, nblk_s) run job s, the rest job d; one job is launched with every workgroup
 // below nblk_s.  (With the parameters selected per workgroup like this the compiler allocates the body's
 // registers without spills; with the job's fields passed straight in it spilled ~100 VGPRs.)
-template <bool PAGED>
+template <bool PAGED, bool ROPE>
 __global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, int nblk_s)
 {
     CSA_A128_LDS
     const bool first = (int)blockIdx.x < nblk_s;
     const AttnJob& j = first ? js : jd;
-    attn128_body<PAGED>(first ? blockIdx.x : blockIdx.x - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
+    attn128_body<PAGED, ROPE>(first ? blockIdx.x : blockIdx.x - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
                  j.pos0, j.scale_log2, j.nunits, j.nsplit, j.rps, j.part_o, j.part_ml, j.out, j.lse);
 }
 #undef CSA_A128_LDS
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, in
 __global__ __launch_bounds__(256) void k_combine128(AttnJob j)
 {
     combine128_body((const uint16_t*)j.part_o, j.part_ml, j.H, j.nsplit, j.out, j.lse, j.R.sink, blockIdx.z,
-                    blockIdx.y, blockIdx.x * 256 + threadIdx.x);
+                    blockIdx.y, blockIdx.x * 256 + threadIdx.x, j.R, j.Tq, j.pos0);
 }
 
 }  // namespace
@@ -441,9 +454,13 @@ namespace csa_host {
 int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag) {
     const int HQ = j.H / 128, BT = j.nunits / j.nsplit;
     const int nblk = j.nunits * HQ;
-    // (paged entries: a compile-time switch, so that the batch-major kernel carries no page-map code)
-    if (j.R.pm.table) CSA_LAUNCH(tag, k_attn128<true>, dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
-    else CSA_LAUNCH(tag, k_attn128<false>, dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
+    // (paged entries and the fused rotary embedding: compile-time switches, so that the plain kernel carries
+    // neither the page-map nor the rotation code, whose registers it cannot spare)
+    const bool paged = j.R.pm.table != nullptr, rope = j.R.rope_rd != 0;
+    if (paged && rope) CSA_LAUNCH(tag, (k_attn128<true, true>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
+    else if (paged) CSA_LAUNCH(tag, (k_attn128<true, false>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
+    else if (rope) CSA_LAUNCH(tag, (k_attn128<false, true>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
+    else CSA_LAUNCH(tag, (k_attn128<false, false>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
     if (j.nsplit > 1) CSA_LAUNCH("k_combine", k_combine128, dim3(32, HQ, BT), dim3(256), 0, st, j);
     return 0;
 }

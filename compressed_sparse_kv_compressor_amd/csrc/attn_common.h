@@ -32,7 +32,40 @@ struct Rows {
     const uint16_t* v;        // values of the entries when they differ from the keys (kv), or null
     const uint16_t* v_raw;    // values of the raw rows when they differ from kv_raw, or null
     int kv_fp8;               // entry rows (kv, v) in the FP8 format (D + 80 bytes: e4m3 groups + bf16 RoPE dims)
+    int rope_rd;              // fused rotary embedding of the last rope_rd dims (0: none; a multiple of 8)
+    double rope_l2t;          // log2 of its base theta
 };
+
+constexpr int ROPE_FUSED_RD = 64;         // the fused rotation covers the last 64 dims (the pages' RoPE width)
+// Fused partial rotary embedding: the query's last rd dimensions turn by +p before the scores (rounded to
+// bf16 as the MFMA operand, as the separate rotary kernel rounds them) and the output's by -p after the
+// softmax (in fp32, before its single bf16 rounding).  Pairs (2i, 2i+1) of a row's dims.
+// Eight consecutive bf16 dims d0 .. d0 + 7 (d0 a multiple of 8) of a row of width D, turned by angle sign * p.
+__device__ __forceinline__ u32x4_t rope8(u32x4_t v, int d0, int D, const Rows& R, double sp) {
+    if (R.rope_rd == 0 || d0 < D - R.rope_rd) return v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float c, s;
+        csa::rope_cs(sp, (d0 - (D - R.rope_rd)) / 2 + k, R.rope_rd, R.rope_l2t, c, s);
+        const float u = csa::bf16_to_f32((uint16_t)(v[k] & 0xffffu)), t = csa::bf16_to_f32((uint16_t)(v[k] >> 16));
+        v[k] = (uint32_t)csa::f32_to_bf16(u * c - t * s) | ((uint32_t)csa::f32_to_bf16(u * s + t * c) << 16);
+    }
+    return v;
+}
+// One fp32 pair (x at even dim d, y at d + 1) turned by angle sign * p; CSA_ROPE_PAIR updates two elements
+// of a vector value in place.
+__device__ __forceinline__ float2 rope2(float x, float y, int d, int D, const Rows& R, double sp) {
+    if (R.rope_rd == 0 || d < D - R.rope_rd) return make_float2(x, y);
+    float c, s;
+    csa::rope_cs(sp, (d - (D - R.rope_rd)) / 2, R.rope_rd, R.rope_l2t, c, s);
+    return make_float2(x * c - y * s, x * s + y * c);
+}
+#define CSA_ROPE_PAIR(V, I, J, DIM, DD, RR, SP)                  \
+    {                                                          \
+        const float2 rp_ = rope2((V)[I], (V)[J], DIM, DD, RR, SP); \
+        (V)[I] = rp_.x;                                        \
+        (V)[J] = rp_.y;                                        \
+    }
 
 __device__ __forceinline__ int dense_visible(long long p, long long L, int m, int N) {
     if (p >= L - 1) return N;

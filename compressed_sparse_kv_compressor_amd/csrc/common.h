@@ -106,6 +106,18 @@ __device__ __forceinline__ f32x16_t mfma32_bf16(const bf16x8_t& a, const bf16x8_
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Rotary embedding angle of pair j (of rd rotated dimensions) at position p: cos and sin of
+// p * theta^(-2j/rd), the angle formed in fp64 (positions reach 2^20 and more) and reduced modulo 2 pi with a
+// two-term (Cody-Waite) constant, then an fp32 sincos of the reduced angle.  log2_theta = log2(theta).
+constexpr double ROPE_TWO_PI_HI = 6.283185307179586;          // 2 pi rounded to double
+constexpr double ROPE_TWO_PI_LO = 2.4492935982947064e-16;     // 2 pi - ROPE_TWO_PI_HI
+constexpr double ROPE_INV_TWO_PI = 0.15915494309189535;
+__device__ __forceinline__ void rope_cs(double p, int j, int rd, double log2_theta, float& c, float& s) {
+    const double a = p * exp2(-2.0 * j / rd * log2_theta);
+    const double q = rint(a * ROPE_INV_TWO_PI);
+    sincosf((float)fma(-q, ROPE_TWO_PI_LO, fma(-q, ROPE_TWO_PI_HI, a)), &s, &c);
+}
+
 }  // namespace csa
 
 // ---------------------------------------------------------------------------

@@ -63,6 +63,8 @@ struct AttnRows {
     const void* v;            // values of the entries when separate from kv (same rows), or null
     const void* v_raw;        // values of the raw rows when separate from kv_raw, or null
     int kv_fp8;               // entry rows in the FP8 format (D + 80 bytes per row), raw rows bf16
+    int rope_rd;              // fused rotary embedding of the last rope_rd dims (0: none)
+    double rope_theta;
 };
 // mode 0: dense over n rows; mode 1: n selected entries + W window rows
 size_t attn_ws_bytes(int B, int Tq, int H, int D, int mode, int n, int W);

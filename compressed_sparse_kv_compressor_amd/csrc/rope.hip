@@ -69,10 +69,8 @@ __global__ __launch_bounds__(RT) void k_rope512(const uint16_t* x, uint16_t* y, 
         const long long r = i >> 6;
         uint4 v = *(const uint4*)(x + r * 512 + 8 * lane);
         const double p = (double)pos[r / group];
-        const double a = (inverse ? -p : p) * exp2(-2.0 * (lane < rd / 2 ? lane : 0) / rd * log2_theta);
-        const double q = rint(a * INV_TWO_PI);
         float sn, cs;
-        sincosf((float)fma(-q, TWO_PI_LO, fma(-q, TWO_PI_HI, a)), &sn, &cs);
+        rope_cs(inverse ? -p : p, lane < rd / 2 ? lane : 0, rd, log2_theta, cs, sn);
         const int src = lane >= first ? 4 * (lane - first) : 0;
         float sk[4], ck[4];
 #pragma unroll

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef enum {
     CSA_OK = 0,
@@ -281,6 +281,22 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
                     long long pos0, int W, float scale, const float* sink, void* out, float* lse_out,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* Partial rotary position embedding fused into the attention ([P1] 1.1: RoPE
+ * acts on the last 64 dimensions of the queries and keys, and the core
+ * attention's output takes the inverse rotation at the query's position).
+ * With a non-NULL csa_rope_t the attention computes
+ *   out = R(-p) . attn(R(p) q)
+ * for the query at absolute position p (pos0 + t, or its sequence's position
+ * with seq_lens), R(a) turning pair j = (D-rd+2j, D-rd+2j+1) by the angle
+ * a * theta^(-2j/rd) (as csa_rope; the keys are rotated by the caller when it
+ * stores them).  The rotated query is rounded to bf16 like csa_rope's output;
+ * the output is rotated in fp32 before its one bf16 rounding.  Supported:
+ * rd = 64 (the pages' RoPE width), theta finite and > 1. */
+typedef struct csa_rope {
+    int rd;          /* rotated dimensions at the end of each row: 64 */
+    double theta;    /* frequency base (10000 in the usual reading) */
+} csa_rope_t;
+
 /* csa_sparse_attn over a variable-length and/or paged batch (layout above;
  * kv is then the entry pool when block_table is given), and with values that
  * may differ from the keys ([P1] 1.1 reads MQA with one vector per entry as key
@@ -292,13 +308,13 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, const voi
  * pool).  kv_format CSA_KV_FP8: kv (and v) rows are FP8 rows of D + 80 bytes
  * (csa_kv_fp8_encode; the raw rows stay bf16), attended as their exact bf16
  * decoding.  With seq_lens, every sequence's Lr raw rows are its last Lr tokens,
- * so Lr >= Tq + W - 1 is required when W > 0.  Workspace:
- * csa_sparse_attn_ws_bytes. */
+ * so Lr >= Tq + W - 1 is required when W > 0.  rope: the fused rotary
+ * embedding above, or NULL (none).  Workspace: csa_sparse_attn_ws_bytes. */
 int csa_sparse_attn_ex(const void* q, const void* kv, const void* v, const int32_t* idx, const void* kv_raw,
                        const void* v_raw, int B, int Tq, int H, int D, int Nc, int m, int topk, int Lr,
                        long long raw0, long long pos0, int W, float scale, const float* sink,
-                       const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out,
-                       void* ws, size_t ws_bytes, void* stream);
+                       const csa_cache_layout_t* layout, int kv_format, const csa_rope_t* rope, void* out,
+                       float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /* No-allocation variant of csa_sparse_attn, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
@@ -334,12 +350,13 @@ int hca_dense_attn(const void* q, const void* kv_h, int B, int Tq, int H, int D,
                    void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /* hca_dense_attn over a variable-length and/or paged batch, with optional
- * separate values v_h (same rows as kv_h, or NULL = kv_h) and FP8 entry rows;
- * as csa_sparse_attn_ex.  With seq_lens, L is the capacity (Nh = ceil(L / mh)). */
+ * separate values v_h (same rows as kv_h, or NULL = kv_h), FP8 entry rows and
+ * the fused rotary embedding; as csa_sparse_attn_ex.  With seq_lens, L is the
+ * capacity (Nh = ceil(L / mh)). */
 int hca_dense_attn_ex(const void* q, const void* kv_h, const void* v_h, int B, int Tq, int H, int D, int Nh,
                       long long L, int mh, long long pos0, float scale, const float* sink,
-                      const csa_cache_layout_t* layout, int kv_format, void* out, float* lse_out,
-                      void* ws, size_t ws_bytes, void* stream);
+                      const csa_cache_layout_t* layout, int kv_format, const csa_rope_t* rope, void* out,
+                      float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Low-precision cache formats ([P1] 1.1, last paragraph: RoPE dimensions in */
@@ -403,6 +420,10 @@ typedef struct csa_hca_decode_args {
     /* With idx_dtype CSA_MXFP4: the E8M0 scales of q_idx [B][HI][dI/32] and of k_idx (rows alongside it). */
     const void* q_idx_scale;
     const void* k_idx_scale;
+    /* The fused rotary embedding of each layer's attention (csa_rope_t above) or NULL: each query at its
+     * decode position. */
+    const csa_rope_t* csa_rope;
+    const csa_rope_t* hca_rope;
 } csa_hca_decode_args_t;
 
 size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a);

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(b):
 
 
 def test_version_and_status_strings(b):
-    assert b.lib.csa_abi_version() == 3
+    assert b.lib.csa_abi_version() == 4
     assert b.lib.csa_status_str(CSA_ERR_WORKSPACE) == b"CSA_ERR_WORKSPACE"
     assert b.lib.csa_status_str(99) == b"CSA_ERR_UNKNOWN"
 
@@ -190,11 +190,16 @@ def test_layout_validation_codes(b):
     assert lib.csa_index_topk_ex_ws_bytes(1, 8192, 8, 128, 65536, 1024, 0, None) < \
         lib.csa_index_topk_ex_ws_bytes(1, 8192, 8, 128, 65536, 1024, 0, ctypes.byref(ok))   # no many-query path
     sp = lib.csa_sparse_attn_ex
-    # q, kv, v, idx, kv_raw, v_raw, B, Tq, H, D, Nc, m, topk, Lr, raw0, pos0, W, scale, sink, layout, fmt, out, ...
+    # q, kv, v, idx, kv_raw, v_raw, B, Tq, H, D, Nc, m, topk, Lr, raw0, pos0, W, scale, sink, layout, fmt, rope, out, ...
     var = b.CacheLayout(seq_lens=A16)
     assert sp(A16, A16, None, A16, A16, None, 2, 2, 16, 128, 100, 4, 8, 9, 0, 0, 9, 0.1, None, ctypes.byref(var), 0,
-              A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE                   # Lr < Tq + W - 1
+              None, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE                   # Lr < Tq + W - 1
     assert sp(A16, A16, BAD, A16, A16, None, 2, 2, 16, 128, 100, 4, 8, 10, 0, 0, 9, 0.1, None, ctypes.byref(var), 0,
-              A16, None, A16, 10 ** 9, None) == CSA_ERR_ALIGN
+              None, A16, None, A16, 10 ** 9, None) == CSA_ERR_ALIGN
     assert sp(A16, A16, None, A16, A16, None, 2, 2, 16, 128, 100, 0, 8, 10, 0, 0, 9, 0.1, None, ctypes.byref(var), 0,
-              A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE                   # m = 0
+              None, A16, None, A16, 10 ** 9, None) == CSA_ERR_SHAPE                   # m = 0
+    # the fused rotary embedding: rd must be 64, theta finite and > 1
+    for rope, code in (((32, 1e4), CSA_ERR_UNSUPPORTED), ((64, 1.0), CSA_ERR_SHAPE), ((64, float("inf")), CSA_ERR_SHAPE)):
+        rp = b.RopeSpec(rd=rope[0], theta=rope[1])
+        assert sp(A16, A16, None, A16, A16, None, 2, 2, 16, 128, 100, 4, 8, 10, 0, 0, 9, 0.1, None, None, 0,
+                  ctypes.byref(rp), A16, None, A16, 10 ** 9, None) == code
