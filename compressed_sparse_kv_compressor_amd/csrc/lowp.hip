@@ -25,26 +25,50 @@ __device__ __forceinline__ int fp8_group_exp(float a) {
     return (double)a <= ldexp(448.0, k - 9) ? k - 9 : k - 8;   // 448 * 2^(k-9) = 0.875 * 2^k
 }
 
-// One wave per row: lane j holds dimension 64 g + j of every group g.
+// One lane per 16-byte chunk of a row (8 dims: D / 8 lanes per row, so a wave holds one row at D = 512 and
+// four at D = 128, and every load and store is a vector access); the 8 lanes of a 64-dim group find its
+// maximum by xor shuffles.  Lanes of one group always belong to one row, so a row past the end leaves whole
+// groups idle.
 __global__ __launch_bounds__(256) void k_kv_fp8(const uint16_t* __restrict__ x, long long n, int D,
                                                 uint8_t* __restrict__ y)
 {
-    const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lpr = D / 8;
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long r = t / lpr;
+    const int c = (int)(t - r * lpr), G = (D - 64) / 64;
     if (r >= n) return;
-    const int lane = threadIdx.x & 63, G = (D - 64) / 64, RB = D + 80;
-    const uint16_t* xr = x + r * D;
-    uint8_t* yr = y + r * RB;
-    for (int g = 0; g < G; ++g) {
-        const float v = bf16_to_f32(xr[64 * g + lane]);
-        float a = fabsf(v);
+    const u32x4_t v = *(const u32x4_t*)(x + r * D + 8 * c);
+    uint8_t* yr = y + r * (D + 80);
+    if (c < 8 * G) {                                 // an e4m3 chunk of group c / 8
+        float f[8];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+        for (int k = 0; k < 4; ++k) {
+            f[2 * k] = bf16_to_f32((uint16_t)(v[k] & 0xffffu));
+            f[2 * k + 1] = bf16_to_f32((uint16_t)(v[k] >> 16));
+        }
+        float a = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
         const int e = a > 0.f ? fp8_group_exp(a) : 0;
-        yr[64 * g + lane] = f32_to_e4m3((float)ldexp((double)v, -e));   // exact scaling, |.| <= 448
-        if (lane == 0) yr[D + 64 + g] = (uint8_t)(e + 127);
+        // exact scaling (a bf16 value times a power of two; what underflows fp32 lies far below e4m3's
+        // smallest half-step and codes to a signed zero either way), |.| <= 448, then the hardware's
+        // round-to-nearest-even conversion, two values at a time
+        uint32_t w[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f[4 * k], -e), ldexpf(f[4 * k + 1], -e), 0, false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f[4 * k + 2], -e), ldexpf(f[4 * k + 3], -e), pk, true);
+            w[k] = (uint32_t)pk;
+        }
+        *(uint2*)(yr + 8 * c) = make_uint2(w[0], w[1]);
+        if ((c & 7) == 0) yr[D + 64 + c / 8] = (uint8_t)(e + 127);
+    } else {                                         // a RoPE chunk, kept as bf16
+        *(u32x4_t*)(yr + (D - 64) + 16 * (c - 8 * G)) = v;
+        if (c == 8 * G)
+            for (int g = G; g < 16; ++g) yr[D + 64 + g] = 0;   // unused scale bytes
     }
-    if (lane < 8) *(u32x4_t*)(yr + (D - 64) + 16 * lane) = *(const u32x4_t*)(xr + (D - 64) + 8 * lane);
-    if (lane >= G && lane < 16) yr[D + 64 + lane] = 0;
 }
 
 // E2M1 code of v (|v| < 8 after scaling): the count of midpoints below |v|, a tie going up only to an even code
@@ -54,33 +78,39 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
     return (v < 0.f && k ? 8u : 0u) | k;
 }
 
-// One wave per row of len elements (len % 32 == 0, len <= 4096): lane l owns the element pairs 2l + 128 i.
+// One lane per 16-byte chunk (8 elements) of a row of len elements (len % 32 == 0): the 4 lanes of a 32-element
+// block find its maximum by xor shuffles, and each lane writes its 8 codes as one dword.
 __global__ __launch_bounds__(256) void k_mxfp4(const uint16_t* __restrict__ x, long long n, int len,
                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lpr = len / 8;
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long r = t / lpr;
+    const int c = (int)(t - r * lpr);
     if (r >= n) return;
-    const int lane = threadIdx.x & 63;
-    const uint16_t* xr = x + r * len;
-    for (int base = 0; base < len; base += 128) {
-        const int i = base + 2 * lane;                 // the block of i is (i / 32): 16 lanes per block
-        const bool act = i < len;
-        const float v0 = act ? bf16_to_f32(xr[i]) : 0.f, v1 = act ? bf16_to_f32(xr[i + 1]) : 0.f;
-        float a = fmaxf(fabsf(v0), fabsf(v1));
+    const u32x4_t v = *(const u32x4_t*)(x + r * len + 8 * c);
+    float f[8];
 #pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-        int X = -127;
-        if (a > 0.f) {
-            int k;
-            (void)frexp((double)a, &k);
-            X = min(127, max(-127, k - 1 - 2));
-        }
-        const uint32_t c = e2m1_code((float)ldexp((double)v0, -X)) | (e2m1_code((float)ldexp((double)v1, -X)) << 4);
-        if (act) {
-            codes[r * (len / 2) + i / 2] = (uint8_t)c;
-            if ((lane & 15) == 0) scales[r * (len / 32) + i / 32] = (uint8_t)(X + 127);
-        }
+    for (int k = 0; k < 4; ++k) {
+        f[2 * k] = bf16_to_f32((uint16_t)(v[k] & 0xffffu));
+        f[2 * k + 1] = bf16_to_f32((uint16_t)(v[k] >> 16));
     }
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));
+    a = fmaxf(a, __shfl_xor(a, 2, 64));
+    int X = -127;
+    if (a > 0.f) {
+        int k;
+        (void)frexp((double)a, &k);
+        X = min(127, max(-127, k - 1 - 2));
+    }
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w |= e2m1_code(ldexpf(f[k], -X)) << (4 * k);     // exact scaling
+    *(uint32_t*)(codes + r * (len / 2) + 4 * c) = w;
+    if ((c & 3) == 0) scales[r * (len / 32) + c / 4] = (uint8_t)(X + 127);
 }
 
 }  // namespace
@@ -88,14 +118,16 @@ __global__ __launch_bounds__(256) void k_mxfp4(const uint16_t* __restrict__ x, l
 namespace csa_host {
 
 int kv_fp8_launch(const void* x, long long n, int D, void* y, hipStream_t st) {
-    CSA_LAUNCH("k_kv_fp8", k_kv_fp8, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, (const uint16_t*)x, n, D,
-               (uint8_t*)y);
+    const long long threads = n * (D / 8);
+    CSA_LAUNCH("k_kv_fp8", k_kv_fp8, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, (const uint16_t*)x, n,
+               D, (uint8_t*)y);
     return 0;
 }
 
 int mxfp4_launch(const void* x, long long n, int len, void* codes, void* scales, hipStream_t st) {
-    CSA_LAUNCH("k_mxfp4", k_mxfp4, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, (const uint16_t*)x, n, len,
-               (uint8_t*)codes, (uint8_t*)scales);
+    const long long threads = n * (len / 8);
+    CSA_LAUNCH("k_mxfp4", k_mxfp4, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, (const uint16_t*)x, n,
+               len, (uint8_t*)codes, (uint8_t*)scales);
     return 0;
 }
 
