@@ -872,10 +872,11 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     // addresses rows with 64-bit pointers), keys that are their own values, and, for k_attn64, a dense row
     // set that is contiguous (paged dense rows run the generic kernel too).
     const size_t kv_rows = a.pm.table ? (size_t)a.pm.nblocks << a.pm.eshift : (size_t)a.N;
-    const bool big32 = kv_rows * D * 2 > 0xffffffffull || (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
+    const bool fp8 = a.kv_fp8 != 0;                  // FP8 entry rows: k_attn128 and the generic kernel widen them
+    const bool big32 = kv_rows * (fp8 ? D + 80 : D * 2) > 0xffffffffull ||
+                       (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
     const bool sepv = a.v || a.v_raw;
-    const bool fp8 = a.kv_fp8 != 0;                  // FP8 entry rows: the generic kernel widens them on load
-    if (use128(D, H) && !big32 && !sepv && !fp8) {
+    if (use128(D, H) && !big32 && !sepv) {
         const int r128 = a.mode == 0 ? a.N : a128_rows(1, a.topk, a.W);
         AttnJob j{};
         j.q = (const uint16_t*)q; j.R = R; j.Tq = Tq; j.H = H; j.pos0 = pos0; j.scale_log2 = sl2;
@@ -884,7 +885,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         j.nunits = BT * j.nsplit;
         j.out = (uint16_t*)out; j.lse = lse;
         // k_attn128 applies an attention sink and the output's rotation in its merge only: a sink or a rotation
-        // with a single split runs k_attn64
+        // with a single split runs k_attn64 (the generic kernel for FP8 rows)
         if (!((R.sink || R.rope_rd) && j.nsplit == 1)) {
             if (j.nsplit > 1) {
                 j.part_o = (float*)ws;

@@ -18,7 +18,11 @@
 //     ds_read_b64_tr_b16), then one barrier that recycles tile t's buffer;
 //   * every workgroup of a launch runs the same number of steps (rows past the split are masked and
 //     the loads past the last tile reread a valid row), so the loop has no data-dependent branch and
-//     the load counters stay exact.
+//     the load counters stay exact;
+//   * FP8 entry rows (592 bytes: e4m3 codes of the 448 non-RoPE dims, the 64 RoPE dims in bf16, one
+//     power-of-two scale per 64-dim group) land unswizzled in the top 592 bytes of their row slot, and
+//     the wave that loaded a row widens it in place to the bf16 layout above (every decoded value is a
+//     bf16 value, so the MFMA loops are those of bf16 rows) before the barrier that publishes the tile.
 #include "common.h"
 #include "kernels.h"
 #include "attn_common.h"
@@ -31,6 +35,8 @@ using namespace csa_attn;
 constexpr int A_TPB = 256;
 constexpr int NBUF = 4;                  // tile buffers (a split's tile count is a multiple of this)
 constexpr int ROWB = 1024;               // bytes of one 512-wide bf16 row
+constexpr int FROWB = 512 + 80;          // bytes of one FP8 row (448 codes, 64 bf16 RoPE dims, 16 scale bytes)
+constexpr int FOFF = ROWB - FROWB;       // where an FP8 row lands in its slot (chunk 27)
 
 constexpr int A128_QK_AHEAD = 4;         // K-operand LDS reads in flight ahead of the QK MFMAs
 constexpr int A128_PV_AHEAD = 2;         // d-tiles of V reads in flight ahead of the PV MFMAs
@@ -40,7 +46,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 // R.mode 0: dense prefix (row r = entry r); 1: selected entries, masked padding up to a whole tile,
 // then the raw window rows.  The mode is a uniform run-time value (one body serves both jobs of a
 // fused launch).
-template <bool PAGED, bool ROPE>
+template <bool PAGED, bool ROPE, bool FP8>
 __device__ __forceinline__ void attn128_body(
     int bid, uint16_t* buf0, uint16_t* buf1, uint16_t* buf2, uint16_t* buf3, int* rcode,
     const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
@@ -97,10 +103,11 @@ __device__ __forceinline__ void attn128_body(
     __syncthreads();
 
     // paged entries address the whole pool (the staged rows are pool rows); batch-major ones this sequence's
-    const uint16_t* kvb = R.kv ? (PAGED ? R.kv : R.kv + (size_t)b * R.N * D) : nullptr;
+    constexpr int EROWB = FP8 ? FROWB : ROWB;  // bytes of an entry row (raw window rows are always bf16)
+    const char* kvb = R.kv ? (PAGED ? (const char*)R.kv : (const char*)R.kv + (size_t)b * R.N * EROWB) : nullptr;
     const size_t kv_rows = PAGED ? (size_t)R.pm.nblocks << R.pm.eshift : (size_t)R.N;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
-    const __amdgpu_buffer_rsrc_t rs_kv = make_rsrc(kvb, kvb ? (uint32_t)(kv_rows * ROWB) : 0u);
+    const __amdgpu_buffer_rsrc_t rs_kv = make_rsrc(kvb, kvb ? (uint32_t)(kv_rows * EROWB) : 0u);
     const __amdgpu_buffer_rsrc_t rs_raw = make_rsrc(rawb, rawb ? (uint32_t)((size_t)R.Lr * ROWB) : 0u);
 
     bf16x8_t qreg[KS];
@@ -129,6 +136,8 @@ __device__ __forceinline__ void attn128_body(
     // rows reads the raw array.  One group of 8 loads serves every kind of tile, so the compiler's
     // tracking of loads into LDS stays exact (a read waits only for the loads of its own buffer).
     const uint32_t lane16 = 16u * (uint32_t)lane;
+    // (FP8 tiles: lane l >= 27 fetches chunk l - 27 of the 592-byte row into chunk l of the slot; the lanes
+    // below repeat chunks of the same row into slot bytes that the widening overwrites)
     auto issue = [&](uint16_t* bufp, int t) {
         CSA_LDS char* lb = (CSA_LDS char*)bufp + w * 8 * ROWB;
         const bool from_raw = MODE == 1 && s_begin + t * TILE >= topk32 && R.W > 0;
@@ -137,13 +146,74 @@ __device__ __forceinline__ void attn128_body(
         const u32x4_t c0 = *(const CSA_LDS u32x4_t*)cp, c1 = *(const CSA_LDS u32x4_t*)(cp + 4);
         uint32_t l16 = lane16;
         asm volatile("" : "+v"(l16));             // per-issue lane offsets (nothing held across the loop)
+        if constexpr (FP8) {
+            // both kinds of rows land unswizzled (the widening puts every chunk in its place)
+            const uint32_t voff = from_raw ? l16 : (lane >= FOFF / 16 ? l16 - FOFF : l16);
+            const uint32_t rowb = from_raw ? ROWB : FROWB;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int c = (int)__builtin_amdgcn_readfirstlane(k < 4 ? c0[k] : c1[k - 4]);
-            const uint32_t row = (uint32_t)(c >= 0 ? c : 0);
-            const uint32_t voff = l16 ^ (16u * (uint32_t)swz_chunk(8 * w + k));   // w, k uniform
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (CSA_LDS void*)(lb + ROWB * k), 16, (int)voff,
-                                                     (int)(row * ROWB), 0, 0);
+            for (int k = 0; k < 8; ++k) {
+                const int c = (int)__builtin_amdgcn_readfirstlane(k < 4 ? c0[k] : c1[k - 4]);
+                const uint32_t row = (uint32_t)(c >= 0 ? c : 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (CSA_LDS void*)(lb + ROWB * k), 16, (int)voff,
+                                                         (int)(row * rowb), 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int c = (int)__builtin_amdgcn_readfirstlane(k < 4 ? c0[k] : c1[k - 4]);
+                const uint32_t row = (uint32_t)(c >= 0 ? c : 0);
+                const uint32_t voff = l16 ^ (16u * (uint32_t)swz_chunk(8 * w + k));   // w, k uniform
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (CSA_LDS void*)(lb + ROWB * k), 16, (int)voff,
+                                                         (int)(row * ROWB), 0, 0);
+            }
+        }
+    };
+    // FP8 tiles: each wave widens the 8 rows it loaded, once its own loads of the tile have landed.  Lane l
+    // writes logical chunk l (dims 8l .. 8l+7) of the bf16 row at its swizzled place: from 8 codes times
+    // the group's scale (l < 56) or from the stored bf16 RoPE dims.  A row's write takes its data from every
+    // read of that row, so it is issued after them, and LDS executes one wave's instructions in order: the
+    // in-place widening never overwrites bytes still to be read.  (Raw tiles land unswizzled too, and the
+    // same pass moves each chunk to its place.)
+    auto widen = [&](uint16_t* bufp, int t) {
+        if constexpr (FP8) {
+            CSA_LDS char* lb = (CSA_LDS char*)bufp + w * 8 * ROWB;
+            if (MODE == 1 && s_begin + t * TILE >= topk32 && R.W > 0) {       // raw rows: swizzle in place
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    CSA_LDS char* rb = lb + ROWB * k;
+                    const u32x4_t o = *(const CSA_LDS u32x4_t*)(rb + 16 * lane);
+                    *(CSA_LDS u32x4_t*)(rb + 16 * (lane ^ swz_chunk(8 * w + k))) = o;
+                }
+                return;
+            }
+            const bool nope = lane < 56;
+            const uint32_t a0 = nope ? FOFF + 8 * lane : FOFF + 448 + 16 * (lane - 56);
+            const uint32_t sa = FOFF + 576 + (nope ? lane >> 3 : 0);
+            const uint32_t keep = nope ? 0u : ~0u;    // RoPE lanes keep the stored bf16 (a select, no branch)
+            typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {             // two groups of 4 rows: all reads, then the writes
+                u32x2_t x0[4], x1[4];
+                uint32_t sb[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const CSA_LDS char* rb = lb + ROWB * (4 * h + k);
+                    x0[k] = *(const CSA_LDS u32x2_t*)(rb + a0);
+                    x1[k] = *(const CSA_LDS u32x2_t*)(rb + a0 + 8);
+                    sb[k] = *(const CSA_LDS uint8_t*)(rb + sa);
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float scale = __uint_as_float((sb[k] < 1u ? 1u : sb[k]) << 23);      // 2^(s - 127)
+#define CSA_W8(X, HI) __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(X, scale, HI))
+                    const u32x4_t o = {(CSA_W8(x0[k][0], false) & ~keep) | (x0[k][0] & keep),
+                                       (CSA_W8(x0[k][0], true) & ~keep) | (x0[k][1] & keep),
+                                       (CSA_W8(x0[k][1], false) & ~keep) | (x1[k][0] & keep),
+                                       (CSA_W8(x0[k][1], true) & ~keep) | (x1[k][1] & keep)};
+#undef CSA_W8
+                    *(CSA_LDS u32x4_t*)(lb + ROWB * (4 * h + k) + 16 * (lane ^ swz_chunk(8 * w + 4 * h + k))) = o;
+                }
+            }
         }
     };
     // the lane's row (slot hl) of tile t is a valid row
@@ -263,7 +333,14 @@ __device__ __forceinline__ void attn128_body(
         issue(buf1, 1);
         issue(buf2, 2);
         issue(buf3, 3);
-        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");     // tiles 0 and 1 landed
+        if constexpr (FP8) {
+            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");               // this wave's rows of tiles 0, 1
+            widen(buf0, 0);
+            widen(buf1, 1);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");     // tiles 0 and 1 landed
+        }
         const CSA_LDS char* Qb = (const CSA_LDS char*)buf0;
         f32x16_t s0;
 #pragma unroll
@@ -277,17 +354,23 @@ __device__ __forceinline__ void attn128_body(
         for (int i = 0; i < 16; ++i) x[i] = s0[i] * scale_log2;
     }
     for (int t = 0; t < ntiles; t += NBUF) {
-#define CSA_A128_STEP(PB, QB, K)                                                                     \
+#define CSA_A128_STEP(PB, QB, NB, K)                                                                 \
         {                                                                                            \
             const f32x16_t sn = step(PB, QB, row_ok(t + K + 1));                                     \
-            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");  /* tile t+K+2 landed */   \
+            if constexpr (FP8) {                                                                     \
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");     /* this wave's rows of t+K+2 */   \
+                widen(NB, t + K + 2);                                                                \
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                      \
+            } else {                                                                                 \
+                asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");  /* tile t+K+2 landed */ \
+            }                                                                                        \
             issue(PB, t + K + 4);                                                                    \
             _Pragma("unroll") for (int i = 0; i < 16; ++i) x[i] = sn[i] * scale_log2;              \
         }
-        CSA_A128_STEP(buf0, buf1, 0)
-        CSA_A128_STEP(buf1, buf2, 1)
-        CSA_A128_STEP(buf2, buf3, 2)
-        CSA_A128_STEP(buf3, buf0, 3)
+        CSA_A128_STEP(buf0, buf1, buf2, 0)
+        CSA_A128_STEP(buf1, buf2, buf3, 1)
+        CSA_A128_STEP(buf2, buf3, buf0, 2)
+        CSA_A128_STEP(buf3, buf0, buf1, 3)
 #undef CSA_A128_STEP
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the dummy loads past the last tile
@@ -429,13 +512,13 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
 // Two job slots: workgroups [0, nblk_s) run job s, the rest job d; one job is launched with every workgroup
 // below nblk_s.  (With the parameters selected per workgroup like this the compiler allocates the body's
 // registers without spills; with the job's fields passed straight in it spilled ~100 VGPRs.)
-template <bool PAGED, bool ROPE>
+template <bool PAGED, bool ROPE, bool FP8>
 __global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, int nblk_s)
 {
     CSA_A128_LDS
     const bool first = (int)blockIdx.x < nblk_s;
     const AttnJob& j = first ? js : jd;
-    attn128_body<PAGED, ROPE>(first ? blockIdx.x : blockIdx.x - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
+    attn128_body<PAGED, ROPE, FP8>(first ? blockIdx.x : blockIdx.x - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
                  j.pos0, j.scale_log2, j.nunits, j.nsplit, j.rps, j.part_o, j.part_ml, j.out, j.lse);
 }
 #undef CSA_A128_LDS
@@ -454,13 +537,22 @@ namespace csa_host {
 int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag) {
     const int HQ = j.H / 128, BT = j.nunits / j.nsplit;
     const int nblk = j.nunits * HQ;
-    // (paged entries and the fused rotary embedding: compile-time switches, so that the plain kernel carries
-    // neither the page-map nor the rotation code, whose registers it cannot spare)
-    const bool paged = j.R.pm.table != nullptr, rope = j.R.rope_rd != 0;
-    if (paged && rope) CSA_LAUNCH(tag, (k_attn128<true, true>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
-    else if (paged) CSA_LAUNCH(tag, (k_attn128<true, false>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
-    else if (rope) CSA_LAUNCH(tag, (k_attn128<false, true>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
-    else CSA_LAUNCH(tag, (k_attn128<false, false>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);
+    // (paged entries, the fused rotary embedding and FP8 entry rows: compile-time switches, so that the plain
+    // kernel carries none of their code, whose registers it cannot spare)
+    const bool paged = j.R.pm.table != nullptr, rope = j.R.rope_rd != 0, fp8 = j.R.kv_fp8 != 0;
+#define CSA_A128(P_, R_, F_) CSA_LAUNCH(tag, (k_attn128<P_, R_, F_>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk)
+    if (fp8) {
+        if (paged && rope) CSA_A128(true, true, true);
+        else if (paged) CSA_A128(true, false, true);
+        else if (rope) CSA_A128(false, true, true);
+        else CSA_A128(false, false, true);
+    } else {
+        if (paged && rope) CSA_A128(true, true, false);
+        else if (paged) CSA_A128(true, false, false);
+        else if (rope) CSA_A128(false, true, false);
+        else CSA_A128(false, false, false);
+    }
+#undef CSA_A128
     if (j.nsplit > 1) CSA_LAUNCH("k_combine", k_combine128, dim3(32, HQ, BT), dim3(256), 0, st, j);
     return 0;
 }

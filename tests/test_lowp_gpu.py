@@ -115,6 +115,74 @@ def test_fp8_attention_matches_decoded_rows(b, H, D):
         rows_close(outd[bb].cpu().numpy().view(np.uint16), o[0], f"dense over FP8 rows, sequence {bb}")
 
 
+def pool_rows(arr, table, epb):
+    """Batch-major rows [B][N][...] -> a page pool of epb entries per page, page table[b][k] for block k."""
+    B, nb = table.shape
+    out = np.zeros((B * nb * epb,) + arr.shape[2:], arr.dtype)
+    for bb in range(B):
+        for k in range(nb):
+            out[table[bb, k] * epb:(table[bb, k] + 1) * epb] = arr[bb, k * epb:(k + 1) * epb]
+    return out
+
+
+# 128-head launches that split the rows (so the merge applies a sink and the output's rotation): FP8 entry rows go
+# through the same kernel as bf16 rows, widened in LDS to exactly their decoding, so the two outputs (and lse)
+# are equal bit for bit.  Cases: decode and multi-query sparse (selected tiles + raw window tiles), 256 heads,
+# dense with variable lengths, paged pools, a sink and the fused rotation.
+@pytest.mark.parametrize("kind,B,Tq,H,N,topk,W,paged,rope,sink", [
+    ("sparse", 2, 1, 128, 4096, 1024, 128, False, False, False),
+    ("sparse", 2, 3, 256, 3072, 384, 96, True, True, True),
+    ("sparse", 1, 2, 128, 2000, 200, 0, False, True, False),
+    ("dense", 2, 1, 128, 8192, 0, 0, False, False, False),
+    ("dense", 2, 2, 128, 3072, 0, 0, True, True, True),
+])
+def test_fp8_attn128_equals_bf16_over_decoded_rows(b, kind, B, Tq, H, N, topk, W, paged, rope, sink):
+    D, m = 512, 4
+    seed = 300 + N + H + Tq
+    q, _ = synth.attn_inputs(seed, B, Tq, H, D, 1, "f8k_")
+    kv = kv_rows(seed + 1, B * N, D, spread=3).reshape(B, N, D)
+    y = b.csa_kv_fp8_encode(dev(kv)).cpu().numpy().reshape(B, N, D + 80)
+    dec = decoded_bits(y.reshape(-1, D + 80), D).reshape(B, N, D)
+    sk = dev(np.random.default_rng(seed).standard_normal(H).astype(np.float32)) if sink else None
+    rp = (64, 10000.0) if rope else None
+    lay = None
+    ry, rd = y, dec
+    if kind == "sparse":
+        ratio = m
+        L = N * m
+    else:
+        ratio = 4
+        L = N * ratio
+    lens = np.array([L - 517 * bb for bb in range(B)], np.int64)
+    if paged:
+        epb = 128 // ratio
+        nb = -(-N // epb)
+        assert nb * epb == N
+        table = np.random.default_rng(seed + 2).permutation(B * nb).astype(np.int32).reshape(B, nb)
+        ry, rd = pool_rows(y, table, epb), pool_rows(dec, table, epb)
+        lay = b.make_layout(seq_lens=dev(lens), block_table=dev(table), num_blocks=B * nb, block_tokens=128)
+    else:
+        lay = b.make_layout(seq_lens=dev(lens))
+    outs = []
+    for fmt, rows in ((b.KV_FP8, ry), (b.KV_BF16, rd)):
+        out = torch.empty((B, Tq, H, D), dtype=torch.int16, device=DEV)
+        lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+        if kind == "sparse":
+            g = np.random.default_rng(seed + 3)
+            idx = np.stack([np.stack([np.sort(g.choice(N - 200, topk, replace=False)) for _ in range(Tq)])
+                            for _ in range(B)]).astype(np.int32)
+            _, raw = synth.attn_inputs(seed + 4, B, 1, H, D, L, "f8kr_")
+            b.csa_sparse_attn(dev(q), dev(rows), dev(idx), dev(raw), 0, L - Tq, W, D ** -0.5, out, lse, sink=sk,
+                              layout=lay, m=m, Nc=N, kv_format=fmt, rope=rp)
+        else:
+            b.hca_dense_attn(dev(q), dev(rows), L, ratio, L - Tq, D ** -0.5, out, lse, sink=sk, layout=lay,
+                             kv_format=fmt, rope=rp)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
 def mx_inputs(seed, B, Tq, HI, dI, Nc, planted=0):
     q, w, k, pl = synth.indexer_inputs(seed, B, Tq, HI, dI, Nc, 0, planted=planted)
     qc, qs = oracle.mxfp4_encode(q)
