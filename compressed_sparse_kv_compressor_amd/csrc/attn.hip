@@ -262,6 +262,12 @@ __global__ __launch_bounds__(TPB, 2) void k_attn(const uint16_t* __restrict__ q,
 // Tiles are unpadded and XOR-swizzled per 16-byte chunk (conflict-free row
 // reads and transposed reads).  1D grid, XCD-aware: the head-pair workgroups
 // that read the same rows land on the same XCD (workgroup i runs on XCD i mod 8).
+// FP8 entry rows (592 bytes: e4m3 codes of dims 0..447, bf16 RoPE dims 448..511,
+// one power-of-two scale per 64-dim group): each d-half slot (512 bytes) takes the
+// bytes its half needs at its top (half 0: codes 0..255 + scales; half 1: codes
+// 256..447, the RoPE dims, the scales) and the wave that loaded it widens it in
+// place to the bf16 layout above before the tile's barrier; raw window rows stay
+// bf16.
 // ---------------------------------------------------------------------------
 constexpr int HD = 256;   // d-half handled by one wave
 
@@ -276,7 +282,7 @@ constexpr int ATT_TILES = 3;      // tile buffers; a split's tile count is a mul
 // kernel half its rate).
 typedef float SxArr[4][4][64][4];         // score exchange [wave][j/4][lane][j%4] (one parity)
 
-template <int MODE, bool PAGED, bool ROPE>
+template <int MODE, bool PAGED, bool ROPE, bool FP8>
 __device__ __forceinline__ void attn64_body(
     int bid, uint16_t* bufA, uint16_t* bufB, uint16_t* bufC, SxArr* sx,
     const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
@@ -321,7 +327,8 @@ __device__ __forceinline__ void attn64_body(
     const int ntiles = s_begin < nrows ? rps / TILE : 0;
 
     // paged entries address the whole pool (the page map gives pool rows); batch-major ones this sequence's
-    const uint16_t* kvb = R.kv ? (PAGED ? R.kv : R.kv + (size_t)b * R.N * D) : nullptr;
+    constexpr int FROWB = D + 80;             // bytes of an FP8 row
+    const uint16_t* kvb = R.kv ? (PAGED ? R.kv : (const uint16_t*)((const char*)R.kv + (size_t)b * R.N * (FP8 ? FROWB : D * 2))) : nullptr;
     const size_t kv_rows = PAGED ? (size_t)R.pm.nblocks << R.pm.eshift : (size_t)R.N;
     const uint16_t* rawb = MODE == 1 && R.kv_raw ? R.kv_raw + (size_t)b * R.Lr * D : nullptr;
 
@@ -376,8 +383,14 @@ __device__ __forceinline__ void attn64_body(
     // Buffer resources over this d-half of the batch's rows (raw buffer, byte offsets).  An absent
     // array gets an empty resource: nothing is ever loaded through it.
     const bool has_kv = kvb != nullptr, has_raw = MODE == 1 && rawb != nullptr;
-    const __amdgpu_buffer_rsrc_t rs_kv =
+    const __amdgpu_buffer_rsrc_t rs_kv = FP8 ?
+        make_rsrc(kvb, has_kv ? (uint32_t)(kv_rows * FROWB) : 0u) :
         make_rsrc(has_kv ? kvb + dh * HD : nullptr, has_kv ? (uint32_t)(kv_rows * D * 2 - dh * HD * 2) : 0u);
+    // FP8 rows: slot chunk pch of the lane's half takes row chunk f8src (half 0: chunks 15..30 <- codes 0..15,
+    // 31 <- the scales; half 1: chunks 11..31 <- row chunks 16..36; the chunks below repeat row chunks that the
+    // widening overwrites)
+    const uint32_t f8src = dh == 0 ? (pch == 31 ? 36u : (pch >= 15 ? (uint32_t)pch - 15u : (uint32_t)pch))
+                                   : (pch >= 11 ? (uint32_t)pch + 5u : (uint32_t)pch + 16u);
     const __amdgpu_buffer_rsrc_t rs_raw =
         make_rsrc(has_raw ? rawb + dh * HD : nullptr, has_raw ? (uint32_t)((size_t)R.Lr * D * 2 - dh * HD * 2) : 0u);
     const int raw_first = MODE == 1 ? (int)(w0 - raw0) : 0;           // raw row of the first window row
@@ -390,7 +403,13 @@ __device__ __forceinline__ void attn64_body(
         };
         const int nval = max(0, min(TILE, s_end - r0));
         if constexpr (MODE == 0) {
-            if (r0 + TILE <= R.N) {                     // all 32 row slots lie inside the array
+            if (FP8) {                                  // (slots past the array reread row 0)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int i = i0 + k, r = r0 + 2 * i + rsub;
+                    bdma(rs_kv, (uint32_t)(r < R.N ? r : 0) * FROWB + 16u * f8src, 0u, i);
+                }
+            } else if (r0 + TILE <= R.N) {              // all 32 row slots lie inside the array
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int i = i0 + k;
@@ -419,7 +438,8 @@ __device__ __forceinline__ void attn64_body(
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int i = i0 + k;
-                    bdma(rs_kv, roff[i] * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
+                    if constexpr (FP8) bdma(rs_kv, roff[i] * FROWB + 16u * f8src, 0u, i);
+                    else bdma(rs_kv, roff[i] * (D * 2) + (lane_chunk ^ (16u * kappa(i))), 0u, i);
                 }
             } else {                                    // raw window rows (masked slots read the first one)
                 const int u0 = raw_first + (r0 - topk32);                   // raw row of slot 0
@@ -443,6 +463,49 @@ __device__ __forceinline__ void attn64_body(
         }
     };
 
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+    // FP8 tiles: the wave widens the 16 half rows it loaded (rows 16 hgl .. + 15 of its d-half), once its
+    // own loads of the tile have landed.  Lane (rsub, pch) writes logical chunk pch of its half row at the
+    // swizzled place, from 8 codes times the group's scale or (half 1, pch >= 24) the stored RoPE dims.  A
+    // row's write takes its data from every read of that row, so it is issued after them, and LDS executes
+    // one wave's instructions in order: the in-place widening never overwrites bytes still to be read.
+    auto widen = [&](uint16_t* buf, int t) {
+        if constexpr (FP8) {
+            if (t >= ntiles || (MODE == 1 && s_begin + t * TILE >= topk32)) return;   // raw rows are bf16
+            CSA_LDS char* lb = (CSA_LDS char*)buf + dh * HALF_B;
+            const bool nope = dh == 0 || pch < 24;
+            const uint32_t a0 = dh == 0 ? 240u + 8u * pch : (nope ? 176u + 8u * pch : 16u * (pch - 1));
+            const uint32_t sa = dh == 0 ? 496u + (pch >> 3) : 500u + (nope ? (uint32_t)(pch >> 3) : 0u);
+            const uint32_t keep = nope ? 0u : ~0u;
+            typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {          // two groups of 4 row pairs: all reads, then the writes
+                u32x2_t x0[4], x1[4];
+                uint32_t sb[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int row = 2 * (i0 + 4 * h2 + k) + rsub;
+                    const CSA_LDS char* rb = lb + 512 * row;
+                    x0[k] = *(const CSA_LDS u32x2_t*)(rb + a0);
+                    x1[k] = *(const CSA_LDS u32x2_t*)(rb + a0 + 8);
+                    sb[k] = *(const CSA_LDS uint8_t*)(rb + sa);
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int row = 2 * (i0 + 4 * h2 + k) + rsub;
+                    const float scale = __uint_as_float((sb[k] < 1u ? 1u : sb[k]) << 23);      // 2^(s - 127)
+#define CSA_W8(X, HI) __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(X, scale, HI))
+                    const u32x4_t o = {(CSA_W8(x0[k][0], false) & ~keep) | (x0[k][0] & keep),
+                                       (CSA_W8(x0[k][0], true) & ~keep) | (x0[k][1] & keep),
+                                       (CSA_W8(x0[k][1], false) & ~keep) | (x1[k][0] & keep),
+                                       (CSA_W8(x0[k][1], true) & ~keep) | (x1[k][1] & keep)};
+#undef CSA_W8
+                    *(CSA_LDS u32x4_t*)(lb + 512 * row + 16 * (pch ^ swz_chunk(row))) = o;
+                }
+            }
+        }
+    };
+
     // ---- LDS reads ----
     // Byte offsets of this lane's reads inside a tile buffer.  With the half 512-byte aligned the
     // swizzled address of k-step s is (qk_off ^ 32 s), and that of the transposed read of rows 8k.. and
@@ -450,7 +513,6 @@ __device__ __forceinline__ void attn64_body(
     const uint32_t qk_off = dh * HALF_B + hl * 512 + 16 * (g ^ swz_chunk(hl));
     const uint32_t tr_off = dh * HALF_B + tr_row * 512 +
                             16 * ((2 * (b16 & 1) + ((j16 >> 1) & 1)) ^ swz_chunk(tr_row)) + 8 * (j16 & 1);
-    typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
     // max / sum over the two lane halves (the two 16-row groups of a head's column)
     auto xhalf_max = [](float v) -> float {
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -591,12 +653,14 @@ __device__ __forceinline__ void attn64_body(
         vm0 = issue_tile(bufA, 0);
         fetch_codes(1);
         __builtin_amdgcn_s_waitcnt(0);         // own loads of tile 0, codes of tile 1
+        widen(bufA, 0);
         vm1 = issue_tile(bufB, 1);
         fetch_codes(2);
-        __syncthreads();                       // tile 0 complete for all waves
+        exchange_barrier();                    // tile 0 complete for all waves
         const f32x16_t s0 = qk_only(bufA, vm0);
         write_scores(s0, 0);
         __builtin_amdgcn_s_waitcnt(0);         // own loads of tile 1, codes of tile 2
+        widen(bufB, 1);
         exchange_barrier();
         vm2 = issue_tile(bufC, 2);
         fetch_codes(3);
@@ -604,12 +668,13 @@ __device__ __forceinline__ void attn64_body(
     }
     for (int t = 0; t < ntiles; t += ATT_TILES) {
         // step t (P = A, QK = B), step t+1 (P = B, QK = C), step t+2 (P = C, QK = A)
-#define CSA_ATT_STEP(PB, QB, VMN, DMA_BUF, VM_OUT, K)                                             \
+#define CSA_ATT_STEP(PB, QB, WB, VMN, DMA_BUF, VM_OUT, K)                                         \
         {                                                                                         \
             const int par = (t + K + 1) & 1;   /* exchange parity of tile t+K+1 */                  \
             const f32x16_t sn = step(PB, QB, VMN);                                                \
             write_scores(sn, par);                                                                \
             __builtin_amdgcn_s_waitcnt(0);     /* own loads of tile t+K+2, codes of tile t+K+3 */  \
+            widen(WB, t + K + 2);                                                                 \
             exchange_barrier();                                                                   \
             if (t + K + 3 < ntiles) {                                                             \
                 VM_OUT = issue_tile(DMA_BUF, t + K + 3);                                          \
@@ -619,9 +684,9 @@ __device__ __forceinline__ void attn64_body(
             }                                                                                     \
             read_scores(sn, par);                                                                 \
         }
-        CSA_ATT_STEP(bufA, bufB, vm1, bufA, vm0, 0)
-        CSA_ATT_STEP(bufB, bufC, vm2, bufB, vm1, 1)
-        CSA_ATT_STEP(bufC, bufA, vm0, bufC, vm2, 2)
+        CSA_ATT_STEP(bufA, bufB, bufC, vm1, bufA, vm0, 0)
+        CSA_ATT_STEP(bufB, bufC, bufA, vm2, bufB, vm1, 1)
+        CSA_ATT_STEP(bufC, bufA, bufB, vm0, bufC, vm2, 2)
 #undef CSA_ATT_STEP
     }
 
@@ -678,14 +743,14 @@ __device__ __forceinline__ void attn64_body(
     __shared__ __attribute__((aligned(1024))) uint16_t bufC[2 * TILE * HD];   \
     __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];
 
-template <int MODE, bool PAGED, bool ROPE>
+template <int MODE, bool PAGED, bool ROPE, bool FP8>
 __global__ __launch_bounds__(TPB, 1) void k_attn64(
     const uint16_t* __restrict__ q, Rows R, int Tq, int H, long long pos0, float scale_log2, int nunits, int nsplit,
     int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse)
 {
     CSA_ATT64_LDS
-    attn64_body<MODE, PAGED, ROPE>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
+    attn64_body<MODE, PAGED, ROPE, FP8>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
                            part_o, part_ml, out, lse);
 }
 
@@ -872,7 +937,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     // addresses rows with 64-bit pointers), keys that are their own values, and, for k_attn64, a dense row
     // set that is contiguous (paged dense rows run the generic kernel too).
     const size_t kv_rows = a.pm.table ? (size_t)a.pm.nblocks << a.pm.eshift : (size_t)a.N;
-    const bool fp8 = a.kv_fp8 != 0;                  // FP8 entry rows: k_attn128 and the generic kernel widen them
+    const bool fp8 = a.kv_fp8 != 0;                  // FP8 entry rows: every kernel widens them to bf16 in LDS
     const bool big32 = kv_rows * (fp8 ? D + 80 : D * 2) > 0xffffffffull ||
                        (a.mode == 1 && (size_t)a.Lr * D * 2 > 0xffffffffull);
     const bool sepv = a.v || a.v_raw;
@@ -885,7 +950,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         j.nunits = BT * j.nsplit;
         j.out = (uint16_t*)out; j.lse = lse;
         // k_attn128 applies an attention sink and the output's rotation in its merge only: a sink or a rotation
-        // with a single split runs k_attn64 (the generic kernel for FP8 rows)
+        // with a single split runs k_attn64
         if (!((R.sink || R.rope_rd) && j.nsplit == 1)) {
             if (j.nsplit > 1) {
                 j.part_o = (float*)ws;
@@ -894,16 +959,19 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
             return attn128_launch(j, st, tag);
         }
     }
-    if (use64(D, H) && !big32 && !sepv && !fp8 && !(a.pm.table && a.mode == 0)) {
+    if (use64(D, H) && !big32 && !sepv && !(a.pm.table && a.mode == 0)) {
         const int nunits = BT * ns, HP = (H + 63) / 64;
         const int nblk = (nunits + 7) / 8 * 8 * HP;
-#define CSA_ATT64(MODE_, PAGED_, ROPE_)                                                                      \
-    CSA_LAUNCH(tag, (k_attn64<MODE_, PAGED_, ROPE_>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, pos0, \
-               sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse)
+#define CSA_ATT64(MODE_, PAGED_, ROPE_, FP8_)                                                                \
+    CSA_LAUNCH(tag, (k_attn64<MODE_, PAGED_, ROPE_, FP8_>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, \
+               pos0, sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse)
+#define CSA_ATT64_F(MODE_, PAGED_, ROPE_) \
+    do { if (fp8) CSA_ATT64(MODE_, PAGED_, ROPE_, true); else CSA_ATT64(MODE_, PAGED_, ROPE_, false); } while (0)
         const bool rope = R.rope_rd != 0;
-        if (a.mode == 0) { if (rope) CSA_ATT64(0, false, true); else CSA_ATT64(0, false, false); }
-        else if (a.pm.table) { if (rope) CSA_ATT64(1, true, true); else CSA_ATT64(1, true, false); }
-        else { if (rope) CSA_ATT64(1, false, true); else CSA_ATT64(1, false, false); }
+        if (a.mode == 0) { if (rope) CSA_ATT64_F(0, false, true); else CSA_ATT64_F(0, false, false); }
+        else if (a.pm.table) { if (rope) CSA_ATT64_F(1, true, true); else CSA_ATT64_F(1, true, false); }
+        else { if (rope) CSA_ATT64_F(1, false, true); else CSA_ATT64_F(1, false, false); }
+#undef CSA_ATT64_F
 #undef CSA_ATT64
         if (ns > 1)
             CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,

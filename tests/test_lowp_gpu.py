@@ -125,16 +125,24 @@ def pool_rows(arr, table, epb):
     return out
 
 
-# 128-head launches that split the rows (so the merge applies a sink and the output's rotation): FP8 entry rows go
-# through the same kernel as bf16 rows, widened in LDS to exactly their decoding, so the two outputs (and lse)
-# are equal bit for bit.  Cases: decode and multi-query sparse (selected tiles + raw window tiles), 256 heads,
-# dense with variable lengths, paged pools, a sink and the fused rotation.
+# FP8 entry rows go through the same kernel as bf16 rows, widened in LDS to exactly their decoding, so the two
+# outputs (and lse) are equal bit for bit.  128 and 256 heads (launches that split the rows, so the merge applies a
+# sink and the output's rotation): decode and multi-query sparse (selected tiles + raw window tiles), dense with
+# variable lengths, paged pools, a sink and the fused rotation.  64 and 96 heads (the 64-head kernel; 96 leaves
+# a half head pair): sparse batch-major and paged, dense, one split per query (rotation and sink in the
+# epilogue) and several.
 @pytest.mark.parametrize("kind,B,Tq,H,N,topk,W,paged,rope,sink", [
     ("sparse", 2, 1, 128, 4096, 1024, 128, False, False, False),
     ("sparse", 2, 3, 256, 3072, 384, 96, True, True, True),
     ("sparse", 1, 2, 128, 2000, 200, 0, False, True, False),
     ("dense", 2, 1, 128, 8192, 0, 0, False, False, False),
     ("dense", 2, 2, 128, 3072, 0, 0, True, True, True),
+    ("sparse", 2, 1, 64, 4096, 512, 128, False, False, False),
+    ("sparse", 2, 2, 64, 3072, 1024, 100, True, True, True),
+    ("sparse", 1, 160, 64, 3000, 256, 128, False, True, True),
+    ("sparse", 2, 3, 96, 3072, 320, 64, True, False, True),
+    ("dense", 2, 1, 64, 8192, 0, 0, False, True, False),
+    ("dense", 1, 3, 96, 3001, 0, 0, False, False, True),
 ])
 def test_fp8_attn128_equals_bf16_over_decoded_rows(b, kind, B, Tq, H, N, topk, W, paged, rope, sink):
     D, m = 512, 4
