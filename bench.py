@@ -1010,9 +1010,9 @@ def lowp_leg(args, dev, cpu=True):
     """The 1M-context decode pair over the low-precision cache formats: MXFP4 indexer operands (E2M1 codes with
     one E8M0 scale per 32: 68 bytes per key instead of 128) and FP8 KV entry rows (e4m3 non-RoPE dimensions in
     groups of 64 with power-of-two scales, bf16 RoPE dimensions: D + 80 = 592 bytes instead of 1024) for both
-    the CSA and the HCA caches; the raw window stays bf16.  A step is csa_index_topk (MXFP4) + csa_sparse_attn
-    (FP8 entries) + hca_dense_attn (FP8 entries) over the 8 x 1M batch; the operands are encoded from bf16 by
-    the library's encoders before the timed region."""
+    the CSA and the HCA caches; the raw window stays bf16.  A step is one fused decode pair (csa_hca_decode with
+    idx_dtype MXFP4 and kv_format FP8) over the 8 x 1M batch; the operands are encoded from bf16 by the
+    library's encoders before the timed region."""
     import numpy as np
     import torch
 
@@ -1040,22 +1040,19 @@ def lowp_leg(args, dev, cpu=True):
                            hca_q=g(c, "lp_hca_q", (B, 1, H, D), D ** -0.5, 0, dev)))
         if c:
             del qb, kb
-    idx = torch.empty((B, 1, topk), dtype=torch.int32, device=dev)
-    csa_out = torch.empty((B, 1, H, D), dtype=torch.int16, device=dev)
+    idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    csa_out = torch.empty((B, H, D), dtype=torch.int16, device=dev)
     hca_out = torch.empty_like(csa_out)
-    iws = b.workspace(b.lib.csa_index_topk_ex_ws_bytes(B, 1, HI, dI, Nc, topk, b.MXFP4, b._lay(None)), dev)
-    sws = b.workspace(b.lib.csa_sparse_attn_ws_bytes(B, 1, H, D, topk, W), dev)
-    dws = b.workspace(b.lib.hca_dense_attn_ws_bytes(B, 1, H, D, Nh), dev)
+    dargs = [b.make_decode_args(L=L, scale=cfg.scale, csa_q=c["csa_q"].view(B, H, D), q_idx=c["qc"], w_idx=c["w"],
+                                k_idx=c["kc"], kv=c["kv"], kv_raw=c["raw"], idx_dtype=b.MXFP4, m=m, topk=topk, W=W,
+                                csa_out=csa_out, hca_q=c["hca_q"].view(B, H, D), kv_h=c["kvh"], mh=mh,
+                                hca_out=hca_out, idx_out=idx, q_idx_scale=c["qs"], k_idx_scale=c["ks"],
+                                kv_format=b.KV_FP8) for c in copies]
+    ws = b.workspace(b.csa_hca_decode_ws_bytes(dargs[0]), dev)
     stream = torch.cuda.current_stream()
 
     def step(i=0):
-        c = copies[i % len(copies)]
-        b.csa_index_topk(c["qc"], c["w"], c["kc"], b.MXFP4, L, m, L - 1, topk, idx, q_scale=c["qs"],
-                         k_scale=c["ks"], ws=iws, stream=stream)
-        b.csa_sparse_attn(c["csa_q"], c["kv"], idx, c["raw"], L - W, L - 1, W, cfg.scale, csa_out, ws=sws,
-                          stream=stream, kv_format=b.KV_FP8)
-        b.hca_dense_attn(c["hca_q"], c["kvh"], L, mh, L - 1, cfg.scale, hca_out, ws=dws, stream=stream,
-                         kv_format=b.KV_FP8)
+        b.csa_hca_decode(dargs[i % len(dargs)], ws=ws, stream=stream)
 
     for i in range(5):
         step(i)
@@ -1113,7 +1110,7 @@ def lowp_leg(args, dev, cpu=True):
             gq = (u16(got).astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(-1, D)
             o = want_.reshape(-1, D)
             return float((np.abs(gq - o).max(1) / np.abs(o).max(1)).max())
-        samp = {"sequence": 0, "topk_bit_exact": bool(np.array_equal(idx[0, 0].cpu().numpy(), want[0, 0])),
+        samp = {"sequence": 0, "topk_bit_exact": bool(np.array_equal(idx[0].cpu().numpy(), want[0, 0])),
                 "csa_max_row_rel_err": rel(csa_out[0], o_csa), "hca_max_row_rel_err": rel(hca_out[0], o_hca),
                 "tolerance": 2e-2}
         c0 = copies[0]
@@ -1124,7 +1121,7 @@ def lowp_leg(args, dev, cpu=True):
         samp["mxfp4_recall_of_bf16_topk"] = round(len(set(got0[0, 0]) & set(exact[0, 0])) / topk, 4)
         samp["oracle_s"] = round(time.perf_counter() - t0, 2)
         res["parity_sample"] = samp
-    del copies, iws, sws, dws
+    del copies, dargs, ws
     torch.cuda.empty_cache()
     return res
 

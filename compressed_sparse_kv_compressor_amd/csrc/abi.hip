@@ -621,6 +621,19 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     rc = validate_dense(fn, a->hca_q, a->kv_h, a->B, 1, a->H, a->D, Nh, a->L, a->mh, p, a->scale, a->hca_out,
                         a->hca_lse);
     if (rc) return rc;
+    // every argument is checked before the first launch: an error leaves the outputs untouched
+    csa_host::AttnRows rs{1, a->kv, Nc, 0, 1, nullptr, a->topk, a->kv_raw, a->W, a->L - a->W, a->W, a->csa_sink};
+    csa_host::AttnRows rd{0, a->kv_h, Nh, a->L, a->mh, nullptr, 0, nullptr, 0, 0, 0, a->hca_sink};
+    rs.seq_lens = rd.seq_lens = lay.seq_lens;
+    rs.pm = csa_host::page_map(lay, a->m);
+    rd.pm = csa_host::page_map(lay, a->mh);
+    rc = read_rope(fn, a->csa_rope, a->D, rs);
+    if (rc) return rc;
+    rc = read_rope(fn, a->hca_rope, a->D, rd);
+    if (rc) return rc;
+    REQ(a->kv_format == CSA_KV_BF16 || a->kv_format == CSA_KV_FP8, CSA_ERR_DTYPE, "%s: kv_format %d unknown", fn,
+        a->kv_format);
+    rs.kv_fp8 = rd.kv_fp8 = a->kv_format == CSA_KV_FP8;
     rc = check_ws(fn, ws, ws_bytes, csa_hca_decode_ws_bytes(a));
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
@@ -630,6 +643,7 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
         idx = (int32_t*)w;
         w += align256((size_t)a->B * a->topk * 4);
     }
+    rs.idx = idx;
     const size_t iws = align256(csa_host::index_topk_ws_bytes(a->idx_dtype, a->HI, a->dI, a->B, 1, Nc, a->topk,
                                                               plain_layout(a->layout) && a->idx_dtype != CSA_MXFP4));
     rc = csa_host::index_topk_launch(a->q_idx, a->w_idx, a->k_idx, a->idx_dtype, a->B, 1, a->HI, a->dI, Nc, a->L, a->m,
@@ -638,15 +652,6 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     if (rc) return rc;
     w += iws;
     const size_t aws = ws_bytes - (size_t)(w - (char*)ws);
-    csa_host::AttnRows rs{1, a->kv, Nc, 0, 1, idx, a->topk, a->kv_raw, a->W, a->L - a->W, a->W, a->csa_sink};
-    csa_host::AttnRows rd{0, a->kv_h, Nh, a->L, a->mh, nullptr, 0, nullptr, 0, 0, 0, a->hca_sink};
-    rs.seq_lens = rd.seq_lens = lay.seq_lens;
-    rs.pm = csa_host::page_map(lay, a->m);
-    rd.pm = csa_host::page_map(lay, a->mh);
-    rc = read_rope(fn, a->csa_rope, a->D, rs);
-    if (rc) return rc;
-    rc = read_rope(fn, a->hca_rope, a->D, rd);
-    if (rc) return rc;
     // the CSA layer's attention, then the HCA layer's (layer order: a real next layer's query depends on the
     // previous layer's output, so the two are never overlapped)
     const size_t sws = align256(csa_host::attn_ws_bytes(a->B, 1, a->H, a->D, 1, a->topk, a->W));

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 typedef enum {
     CSA_OK = 0,
@@ -424,6 +424,9 @@ typedef struct csa_hca_decode_args {
      * decode position. */
     const csa_rope_t* csa_rope;
     const csa_rope_t* hca_rope;
+    /* CSA_KV_BF16 (0), or CSA_KV_FP8: the entry rows of both layers (kv, kv_h) in the FP8 format of
+     * csa_kv_fp8_encode, D + 80 bytes per row (the raw window rows kv_raw stay bf16). */
+    int kv_format;
 } csa_hca_decode_args_t;
 
 size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a);

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(b):
 
 
 def test_version_and_status_strings(b):
-    assert b.lib.csa_abi_version() == 4
+    assert b.lib.csa_abi_version() == 5
     assert b.lib.csa_status_str(CSA_ERR_WORKSPACE) == b"CSA_ERR_WORKSPACE"
     assert b.lib.csa_status_str(99) == b"CSA_ERR_UNKNOWN"
 
@@ -129,6 +129,9 @@ def test_compress_and_decode_validation_codes(b):
     assert lib.csa_hca_decode(ctypes.byref(args), A16, 10 ** 9, None) == CSA_ERR_NULL
     assert lib.csa_hca_decode(None, A16, 10 ** 9, None) == CSA_ERR_NULL
     args.kv_h = A16
+    args.kv_format = 7                     # checked before any launch
+    assert lib.csa_hca_decode(ctypes.byref(args), A16, 10 ** 9, None) == CSA_ERR_DTYPE
+    args.kv_format = 0
     assert lib.csa_hca_decode(ctypes.byref(args), A16, 16, None) == CSA_ERR_WORKSPACE
     assert lib.csa_hca_decode_ws_bytes(ctypes.byref(args)) > 16
 

@@ -191,6 +191,46 @@ def test_fp8_attn128_equals_bf16_over_decoded_rows(b, kind, B, Tq, H, N, topk, W
     assert np.array_equal(outs[0][1], outs[1][1])
 
 
+def test_fused_decode_fp8_rows_equal_decoded_bf16(b):
+    # the fused decode pair with FP8 entry rows in both layers (kv_format on the decode struct) equals, bit for
+    # bit, the same call over the decoded bf16 rows; paged pools, variable lengths, a sink and the rotation
+    B, H, D, HI, dI, m, mh, topk, W = 2, 128, 512, 8, 128, 4, 128, 512, 128
+    L = 128 * 96
+    Nc, Nh = L // m, L // mh
+    q_idx, w_idx, k_idx, _ = synth.indexer_inputs(81, B, 1, HI, dI, Nc, 0)
+    csa_q, _ = synth.attn_inputs(82, B, 1, H, D, 1, "f8dq_")
+    hca_q, _ = synth.attn_inputs(83, B, 1, H, D, 1, "f8dh_")
+    _, raw = synth.attn_inputs(84, B, 1, H, D, W, "f8dr_")
+    kv = kv_rows(85, B * Nc, D, spread=2).reshape(B, Nc, D)
+    kvh = kv_rows(86, B * Nh, D, spread=2).reshape(B, Nh, D)
+    y = b.csa_kv_fp8_encode(dev(kv)).cpu().numpy().reshape(B, Nc, D + 80)
+    yh = b.csa_kv_fp8_encode(dev(kvh)).cpu().numpy().reshape(B, Nh, D + 80)
+    dec = decoded_bits(y.reshape(-1, D + 80), D).reshape(B, Nc, D)
+    dech = decoded_bits(yh.reshape(-1, D + 80), D).reshape(B, Nh, D)
+    lens = np.array([L, L - 1000], np.int64)
+    mb = L // 128
+    table = np.random.default_rng(87).permutation(B * mb).astype(np.int32).reshape(B, mb)
+    lay = b.make_layout(seq_lens=dev(lens), block_table=dev(table), num_blocks=B * mb, block_tokens=128)
+    sinks = [dev(np.random.default_rng(88 + i).standard_normal(H).astype(np.float32)) for i in range(2)]
+    res = []
+    for fmt, rc, rh in ((b.KV_FP8, y, yh), (b.KV_BF16, dec, dech)):
+        csa_out = torch.empty((B, H, D), dtype=torch.int16, device=DEV)
+        hca_out = torch.empty_like(csa_out)
+        idx = torch.empty((B, topk), dtype=torch.int32, device=DEV)
+        lse = torch.empty((B, H), dtype=torch.float32, device=DEV)
+        args = b.make_decode_args(L=L, scale=D ** -0.5, csa_q=dev(csa_q).view(B, H, D), q_idx=dev(q_idx),
+                                  w_idx=dev(w_idx), k_idx=dev(pool_rows(k_idx, table, 32)), kv=dev(pool_rows(rc, table, 32)),
+                                  kv_raw=dev(raw), idx_dtype=0, m=m, topk=topk, W=W, csa_out=csa_out,
+                                  hca_q=dev(hca_q).view(B, H, D), kv_h=dev(pool_rows(rh, table, 1)), mh=mh,
+                                  hca_out=hca_out, idx_out=idx, hca_lse=lse, layout=lay, csa_sink=sinks[0],
+                                  hca_sink=sinks[1], csa_rope=(64, 10000.0), hca_rope=(64, 10000.0), kv_format=fmt)
+        b.csa_hca_decode(args, device=torch.device(DEV))
+        torch.cuda.synchronize()
+        res.append([t.cpu().numpy() for t in (idx, csa_out, hca_out, lse)])
+    for got, want in zip(res[0], res[1]):
+        assert np.array_equal(got, want)
+
+
 def mx_inputs(seed, B, Tq, HI, dI, Nc, planted=0):
     q, w, k, pl = synth.indexer_inputs(seed, B, Tq, HI, dI, Nc, 0, planted=planted)
     qc, qs = oracle.mxfp4_encode(q)
