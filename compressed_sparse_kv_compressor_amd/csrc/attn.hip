@@ -866,7 +866,7 @@ static int attn_rows(int mode, int H, int D, int n, int W) {
 }
 
 // k_attn128 (128 heads per workgroup, one workgroup per CU): the rows per split are the same for every
-// workgroup of a launch (a multiple of 4 tiles), chosen so that the launch's tiles spread over about
+// workgroup of a launch (whole tiles), chosen so that the launch's tiles spread over about
 // A128_TARGET_WG workgroups, and at least A128_MIN_TILES tiles per split.
 constexpr int A128_TARGET_WG = 256, A128_MIN_TILES = 4;
 static bool use128(int D, int H) { return D == 512 && H % 128 == 0; }

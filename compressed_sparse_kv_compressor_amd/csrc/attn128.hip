@@ -18,7 +18,8 @@
 //     ds_read_b64_tr_b16), then one barrier that recycles tile t's buffer;
 //   * every workgroup of a launch runs the same number of steps (rows past the split are masked and
 //     the loads past the last tile reread a valid row), so the loop has no data-dependent branch and
-//     the load counters stay exact;
+//     the load counters stay exact (a split whose tile count is not a multiple of four leaves the
+//     unrolled group early, uniformly, and the final wait drains the loads in flight);
 //   * FP8 entry rows (592 bytes: e4m3 codes of the 448 non-RoPE dims, the 64 RoPE dims in bf16, one
 //     power-of-two scale per 64-dim group) land unswizzled in the top 592 bytes of their row slot, and
 //     the wave that loaded a row widens it in place to the bf16 layout above (every decoded value is a
@@ -46,7 +47,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 // R.mode 0: dense prefix (row r = entry r); 1: selected entries, masked padding up to a whole tile,
 // then the raw window rows.  The mode is a uniform run-time value (one body serves both jobs of a
 // fused launch).
-template <bool PAGED, bool ROPE, bool FP8>
+template <bool PAGED, bool ROPE, bool FP8, bool PART>
 __device__ __forceinline__ void attn128_body(
     int bid, uint16_t* buf0, uint16_t* buf1, uint16_t* buf2, uint16_t* buf3, int* rcode,
     const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
@@ -367,10 +368,12 @@ __device__ __forceinline__ void attn128_body(
             issue(PB, t + K + 4);                                                                    \
             _Pragma("unroll") for (int i = 0; i < 16; ++i) x[i] = sn[i] * scale_log2;              \
         }
+        // (PART: a split of ntiles % 4 != 0 tiles, whose last group ends early, uniformly; a compile-time
+        //  switch, since the guards cost the other launches their register allocation)
         CSA_A128_STEP(buf0, buf1, buf2, 0)
-        CSA_A128_STEP(buf1, buf2, buf3, 1)
-        CSA_A128_STEP(buf2, buf3, buf0, 2)
-        CSA_A128_STEP(buf3, buf0, buf1, 3)
+        if (!PART || t + 1 < ntiles) CSA_A128_STEP(buf1, buf2, buf3, 1)
+        if (!PART || t + 2 < ntiles) CSA_A128_STEP(buf2, buf3, buf0, 2)
+        if (!PART || t + 3 < ntiles) CSA_A128_STEP(buf3, buf0, buf1, 3)
 #undef CSA_A128_STEP
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the dummy loads past the last tile
@@ -512,13 +515,13 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
 // Two job slots: workgroups [0, nblk_s) run job s, the rest job d; one job is launched with every workgroup
 // below nblk_s.  (With the parameters selected per workgroup like this the compiler allocates the body's
 // registers without spills; with the job's fields passed straight in it spilled ~100 VGPRs.)
-template <bool PAGED, bool ROPE, bool FP8>
+template <bool PAGED, bool ROPE, bool FP8, bool PART>
 __global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, int nblk_s)
 {
     CSA_A128_LDS
     const bool first = (int)blockIdx.x < nblk_s;
     const AttnJob& j = first ? js : jd;
-    attn128_body<PAGED, ROPE, FP8>(first ? blockIdx.x : blockIdx.x - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
+    attn128_body<PAGED, ROPE, FP8, PART>(first ? blockIdx.x : blockIdx.x - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
                  j.pos0, j.scale_log2, j.nunits, j.nsplit, j.rps, j.part_o, j.part_ml, j.out, j.lse);
 }
 #undef CSA_A128_LDS
@@ -540,7 +543,12 @@ int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag) 
     // (paged entries, the fused rotary embedding and FP8 entry rows: compile-time switches, so that the plain
     // kernel carries none of their code, whose registers it cannot spare)
     const bool paged = j.R.pm.table != nullptr, rope = j.R.rope_rd != 0, fp8 = j.R.kv_fp8 != 0;
-#define CSA_A128(P_, R_, F_) CSA_LAUNCH(tag, (k_attn128<P_, R_, F_>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk)
+    const bool part = (j.rps / TILE) % NBUF != 0;
+#define CSA_A128(P_, R_, F_)                                                                                 \
+    do {                                                                                                     \
+        if (part) CSA_LAUNCH(tag, (k_attn128<P_, R_, F_, true>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);  \
+        else CSA_LAUNCH(tag, (k_attn128<P_, R_, F_, false>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);      \
+    } while (0)
     if (fp8) {
         if (paged && rope) CSA_A128(true, true, true);
         else if (paged) CSA_A128(true, false, true);

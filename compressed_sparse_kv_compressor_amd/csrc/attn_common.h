@@ -146,7 +146,7 @@ struct AttnJob {
 namespace csa_host {
 // k_attn128 (attn128.hip): D = 512, H % 128 == 0, every array within reach of 32-bit byte offsets.
 // Rows per split must be a multiple of ATT128_UNIT and at most ATT128_MAX_RPS.
-constexpr int ATT128_UNIT = 128, ATT128_MAX_RPS = 2048;
+constexpr int ATT128_UNIT = 32, ATT128_MAX_RPS = 2048;
 // Launches the attention and, for a job with more than one split, the merge of the split partials
 // (part_o then holds fp16 partials, half the bytes of the fp32 ones of k_attn64; part_ml as there).
 int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag);
