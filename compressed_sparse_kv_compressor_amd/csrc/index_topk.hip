@@ -173,8 +173,10 @@ __global__ __launch_bounds__(TPB) void k_score(
     __shared__ __attribute__((aligned(16))) float lsc[2][KPW_MAX];
     // paged keys: the pool page of every page the workgroup's key range touches, read once here, so that a
     // key load waits on no table load (a table load between two key batches made the wait for it wait for
-    // the batch in flight as well)
-    __shared__ uint32_t lpg[PAGED ? KPW_MAX : 1];
+    // the batch in flight as well).  Sized for pages of >= 2 entries, which keeps two workgroups per CU;
+    // pages of one entry read the table per key.
+    constexpr int PG_CAP = KPW_MAX / 2 + 1;
+    __shared__ uint32_t lpg[PAGED ? PG_CAP : 1];
 
     const int b = blockIdx.y;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -183,8 +185,9 @@ __global__ __launch_bounds__(TPB) void k_score(
     const int NG = (Tq + G - 1) / G;
     const int tiles = keys_per_wg / 64;       // 16-key tiles per wave
     const int pg0 = PAGED ? key0 >> pm.eshift : 0;
-    if constexpr (PAGED) {
-        const int np = ((key0 + keys_per_wg - 1) >> pm.eshift) - pg0 + 1;     // <= keys_per_wg
+    const bool pg_lds = PAGED && pm.eshift > 0;        // (uniform)
+    if (pg_lds) {
+        const int np = ((key0 + keys_per_wg - 1) >> pm.eshift) - pg0 + 1;     // <= keys_per_wg / 2 + 1
         for (int i = threadIdx.x; i < np; i += TPB) {
             const int pi = pg0 + i;
             uint32_t blk = pi < pm.max_blocks ? (uint32_t)pm.table[(size_t)b * pm.max_blocks + pi] : 0u;
@@ -270,9 +273,10 @@ __global__ __launch_bounds__(TPB) void k_score(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int krow = min(key0 + ((tt0 + u) * 4 + wave) * 16 + col, nvmax - 1);
-                const size_t prow = PAGED ? ((size_t)lpg[(krow >> pm.eshift) - pg0] << pm.eshift) |
-                                                (size_t)(krow & ((1 << pm.eshift) - 1))
-                                          : (size_t)b * Nc + krow;
+                const size_t prow = !PAGED ? (size_t)b * Nc + krow
+                                  : pg_lds ? ((size_t)lpg[(krow >> pm.eshift) - pg0] << pm.eshift) |
+                                                 (size_t)(krow & ((1 << pm.eshift) - 1))
+                                           : entry_row(pm, b, Nc, krow);
                 const char* kp = (const char*)k_idx + prow * RB + (size_t)grp * 16;
 #pragma unroll
                 for (int i = 0; i < NV; ++i) dst[u][i] = *(const u32x4_t*)(kp + i * 64);

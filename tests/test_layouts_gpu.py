@@ -62,8 +62,8 @@ def paged(arr, epb, seed, spare=3):
 
 @pytest.mark.parametrize("dtype", [0, 1])
 @pytest.mark.parametrize("Tq", [1, 3])
-@pytest.mark.parametrize("paged_keys", [False, True])
-def test_index_topk_varlen(b, dtype, Tq, paged_keys):
+@pytest.mark.parametrize("block_tokens", [0, 128, 4])     # batch-major; pages of 32 entries; of one entry
+def test_index_topk_varlen(b, dtype, Tq, block_tokens):
     B, HI, dI, m, topk = 4, 8, 128, 4, 256
     L = 4 * 3000
     lens = np.array([L, 7001, 900, 5555], np.int64)
@@ -71,9 +71,9 @@ def test_index_topk_varlen(b, dtype, Tq, paged_keys):
     q, w, k, _ = synth.indexer_inputs(50 + dtype + Tq, B, Tq, HI, dI, Nc, dtype)
     layout_args = dict(seq_lens=dev(lens))
     kin = k
-    if paged_keys:
-        kin, table, nblk = paged(k, 128 // m, 7)
-        layout_args.update(block_table=dev(table), num_blocks=nblk, block_tokens=128)
+    if block_tokens:
+        kin, table, nblk = paged(k, block_tokens // m, 7)
+        layout_args.update(block_table=dev(table), num_blocks=nblk, block_tokens=block_tokens)
     lay = b.make_layout(**layout_args)
     idx = torch.empty((B, Tq, topk), dtype=torch.int32, device=DEV)
     cnt = torch.empty((B, Tq), dtype=torch.int32, device=DEV)
