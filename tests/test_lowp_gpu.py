@@ -143,6 +143,8 @@ def pool_rows(arr, table, epb):
     ("sparse", 2, 3, 96, 3072, 320, 64, True, False, True),
     ("dense", 2, 1, 64, 8192, 0, 0, False, True, False),
     ("dense", 1, 3, 96, 3001, 0, 0, False, False, True),
+    ("dense", 2, 1, 128, 19200, 0, 0, False, True, True),      # splits of 5 tiles (early-ending variant)
+    ("sparse", 16, 1, 128, 2304, 2048, 128, True, False, False),  # splits of 5 tiles, paged
 ])
 def test_fp8_attn128_equals_bf16_over_decoded_rows(b, kind, B, Tq, H, N, topk, W, paged, rope, sink):
     D, m = 512, 4

@@ -338,6 +338,7 @@ SPARSE_CASES = [
     (1, 1, 128, 512, 100, 0, 17, 1.0),         # window only
     (2, 1, 256, 512, 3000, 300, 0, 1.0),       # two head quads, no window
     (1, 1, 128, 512, 70000, 2048, 128, 1.0),   # one query: many splits of the selected rows
+    (32, 1, 128, 512, 4096, 2048, 128, 1.0),   # splits of 9 tiles (not a multiple of 4: the early-ending variant)
 ]
 
 
@@ -384,6 +385,8 @@ DENSE_CASES = [
     (1, 5, 128, 512, 4 * 33, 4, 4.0),          # causal visibility per query (mostly masked tiles)
     (1, 1, 128, 512, 128 * 20000 + 9, 128, 1.0),   # long prefix: many splits, ragged last one
     (3, 2, 256, 512, 4 * 500, 4, 1.0),         # two head quads, two queries
+    (2, 1, 128, 512, 128 * 19200, 128, 1.0),   # splits of 5 tiles (the early-ending variant)
+    (1, 3, 128, 512, 4 * 14000 + 3, 4, 1.0),   # splits of 6 tiles, causal visibility per query
 ]
 
 
