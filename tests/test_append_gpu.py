@@ -201,3 +201,34 @@ def test_append_drops_tokens_beyond_capacity(b):
     got = bf16_f64(kv.cpu().numpy().view(np.uint16))
     rows_close(got[0, 8:], okv[0, 8:], "entries of the appended tokens")
     rows_close(bf16_f64(win.cpu().numpy().view(np.uint16))[0, -8:], ow[0, -8:], "window rows of the appended tokens")
+
+
+def test_append_odd_hidden_and_row_blocks(b):
+    # from empty sequences: hidden 192 (six 32-wide steps over four K quarters: uneven quarters), 15 then 18 new
+    # token rows (a partial 16-row block, then two blocks), both caches and the window vs the oracle's prefix
+    B, Dh, D, dI, m, mh, W, L = 3, 192, 128, 64, 4, 8, 8, 64
+    X, wkv, wik, gate, bslot = synth.compress_inputs(140, B, L, Dh, D, dI, m)
+    wkv_h, _, gate_h, bslot_h = synth.compress_weights(141, Dh, D, 0, mh, prefix="oh_")
+    kv = torch.zeros((B, L // m, D), dtype=torch.int16, device=DEV)
+    ik = torch.zeros((B, L // m, dI), dtype=torch.int16, device=DEV)
+    kvh = torch.zeros((B, L // mh, D), dtype=torch.int16, device=DEV)
+    win = torch.zeros((B, W, D), dtype=torch.int16, device=DEV)
+    seq = torch.zeros(B, dtype=torch.int64, device=DEV)
+    state = torch.zeros(B * b.lib.csa_append_state_bytes(D, dI) // 4, dtype=torch.float32, device=DEV)
+    n = 0
+    for T in (5, 6):
+        b.csa_decode_append(dev(X[:, n:n + T]), dev(wkv), dev(wik), dev(gate), dev(bslot), m, dev(wkv_h), dev(gate_h),
+                            dev(bslot_h), mh, L, seq, state, kv, ik, kvh, win)
+        torch.cuda.synchronize()
+        n += T
+        assert seq.cpu().tolist() == [n] * B
+        nc, nh = -(-n // m), -(-n // mh)
+        for bb in range(B):
+            okv, oik, ow = oracle.compress(X[bb:bb + 1, :n], wkv, wik, gate, bslot, m, W=W)
+            okh, _, _ = oracle.compress(X[bb:bb + 1, :n], wkv_h, None, gate_h, bslot_h, mh)
+            what = f"after {n} tokens, sequence {bb}"
+            rows_close(bf16_f64(kv[bb, :nc].cpu().numpy().view(np.uint16)), okv[0], "kv " + what)
+            rows_close(bf16_f64(ik[bb, :nc].cpu().numpy().view(np.uint16)), oik[0], "ik " + what)
+            rows_close(bf16_f64(kvh[bb, :nh].cpu().numpy().view(np.uint16)), okh[0], "kv_h " + what)
+            rows_close(bf16_f64(win[bb].cpu().numpy().view(np.uint16))[W - min(n, W):], ow[0][W - min(n, W):],
+                       "window " + what)
