@@ -295,9 +295,13 @@ __device__ __forceinline__ void attn64_body(
     constexpr int HALF_B = TILE * HD * 2;     // bytes of one d-half of a tile (16 KiB)
 
     const int HP = (H + 63) / 64;
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int hp = slot % HP, unit = (slot / HP) * 8 + xcd;
-    if (unit >= nunits) return;                // padding workgroups (uniform exit)
+    // XCD-aware order: workgroup i runs on XCD i mod 8, and XCD x takes the contiguous range [x per, (x + 1) per)
+    // of the (unit, head pair) blocks, so the head pairs of a unit (the same rows) and the splits of a query
+    // (whose partials the merge reads) share an XCD and its L2
+    const int per = (nunits * HP + 7) / 8;
+    const int vb = (bid & 7) * per + (bid >> 3);
+    if (vb >= nunits * HP) return;             // padding workgroups (uniform exit)
+    const int hp = vb % HP, unit = vb / HP;
     const int bt = unit / nsplit, split = unit % nsplit;
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // w: wave-uniform
     const int hgl = w & 1, dh = w >> 1;        // head group within the pair, d half
@@ -813,12 +817,21 @@ __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, c
     if (lse && threadIdx.x == 0) lse[(size_t)bt * H + h] = lse_v;
 }
 
-template <int D>
+// grid (H, BT), or with XMAP a 1-D grid of jobs (query, head) laid out by XCD (see XcdJobs)
+template <int D, bool XMAP>
 __global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
                                                    int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                   const float* __restrict__ sink, Rows R, int Tq, long long pos0)
+                                                   const float* __restrict__ sink, Rows R, int Tq, long long pos0,
+                                                   XcdJobs xj)
 {
-    combine_body<D>(part_o, part_ml, H, nsplit, out, lse, sink, blockIdx.x, blockIdx.y, R, Tq, pos0);
+    int h = blockIdx.x, bt = blockIdx.y;
+    if constexpr (XMAP) {
+        const int x = (int)(blockIdx.x & 7u), J = xj.lo[x] + (int)(blockIdx.x >> 3);
+        if (J >= xj.lo[x + 1]) return;
+        h = J % H;
+        bt = J / H;
+    }
+    combine_body<D>(part_o, part_ml, H, nsplit, out, lse, sink, h, bt, R, Tq, pos0);
 }
 
 }  // namespace
@@ -962,7 +975,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
     }
     if (use64(D, H) && !big32 && !sepv && !(a.pm.table && a.mode == 0)) {
         const int nunits = BT * ns, HP = (H + 63) / 64;
-        const int nblk = (nunits + 7) / 8 * 8 * HP;
+        const int per = (nunits * HP + 7) / 8, nblk = 8 * per;
 #define CSA_ATT64(MODE_, PAGED_, ROPE_, FP8_)                                                                \
     CSA_LAUNCH(tag, (k_attn64<MODE_, PAGED_, ROPE_, FP8_>), dim3(nblk), dim3(TPB), 0, st, (const uint16_t*)q, R, Tq, H, \
                pos0, sl2, nunits, ns, rps, part_o, part_ml, (uint16_t*)out, lse)
@@ -974,9 +987,14 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         else { if (rope) CSA_ATT64_F(1, false, true); else CSA_ATT64_F(1, false, false); }
 #undef CSA_ATT64_F
 #undef CSA_ATT64
-        if (ns > 1)
-            CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
-                       (uint16_t*)out, lse, R.sink, R, Tq, pos0);
+        if (ns > 1) {
+            // a query's head h: the XCD of its middle split's block of head pair h / 64
+            int most;
+            const XcdJobs xj = xcd_jobs(BT * H, 1, [&](int g) {
+                return ((g / H * ns + ns / 2) * HP + g % H / 64) / per; }, &most);
+            CSA_LAUNCH("k_combine", (k_combine<512, true>), dim3(8 * most), dim3(128), 0, st, part_o, part_ml, H, ns,
+                       (uint16_t*)out, lse, R.sink, R, Tq, pos0, xj);
+        }
         return 0;
     }
     dim3 grid(ns, (H + 63) / 64, BT);
@@ -995,16 +1013,16 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         else if (fp8) CSA_GENERIC(512, false, true);
         else CSA_GENERIC(512, false, false);
         if (ns > 1)
-            CSA_LAUNCH("k_combine", k_combine<512>, dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
-                       (uint16_t*)out, lse, R.sink, R, Tq, pos0);
+            CSA_LAUNCH("k_combine", (k_combine<512, false>), dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
+                       (uint16_t*)out, lse, R.sink, R, Tq, pos0, XcdJobs{});
     } else if (D == 128) {
         if (sepv && fp8) CSA_GENERIC(128, true, true);
         else if (sepv) CSA_GENERIC(128, true, false);
         else if (fp8) CSA_GENERIC(128, false, true);
         else CSA_GENERIC(128, false, false);
         if (ns > 1)
-            CSA_LAUNCH("k_combine", k_combine<128>, dim3(H, BT), dim3(32), 0, st, part_o, part_ml, H, ns,
-                       (uint16_t*)out, lse, R.sink, R, Tq, pos0);
+            CSA_LAUNCH("k_combine", (k_combine<128, false>), dim3(H, BT), dim3(32), 0, st, part_o, part_ml, H, ns,
+                       (uint16_t*)out, lse, R.sink, R, Tq, pos0, XcdJobs{});
     } else {
         return fail(6, "attention: D = %d unsupported", D);
     }

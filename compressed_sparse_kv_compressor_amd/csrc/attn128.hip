@@ -533,7 +533,6 @@ __global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, in
 // Merge jobs (query, head quad, chunk c of 32), in that order, each 256 threads x 32 covering the 8192 chunk
 // positions of one query and head quad.  Workgroup i runs on XCD i mod 8 and takes job lo[x] + i / 8 of the jobs
 // [lo[x], lo[x + 1]) whose query's partials were written on XCD x (the attention's map above).
-struct XcdJobs { int lo[9]; };
 __global__ __launch_bounds__(256) void k_combine128(AttnJob j, XcdJobs xj)
 {
     const int x = (int)(blockIdx.x & 7u), J = xj.lo[x] + (int)(blockIdx.x >> 3);
@@ -574,15 +573,9 @@ int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag) 
 #undef CSA_A128
     if (j.nsplit > 1) {
         // the XCD holding most of a (query, head quad)'s splits: that of its middle split's block
-        XcdJobs xj;
-        int x = 0, most = 0;
-        xj.lo[0] = 0;
-        for (int bh = 0; bh < BT * HQ; ++bh) {
-            const int home = ((bh / HQ * j.nsplit + j.nsplit / 2) * HQ + bh % HQ) / per;
-            while (x < home) xj.lo[++x] = bh * 32;
-        }
-        while (x < 8) xj.lo[++x] = BT * HQ * 32;
-        for (int k = 0; k < 8; ++k) most = std::max(most, xj.lo[k + 1] - xj.lo[k]);
+        int most;
+        const XcdJobs xj = xcd_jobs(BT * HQ, 32, [&](int bh) {
+            return ((bh / HQ * j.nsplit + j.nsplit / 2) * HQ + bh % HQ) / per; }, &most);
         CSA_LAUNCH("k_combine", k_combine128, dim3(8 * most), dim3(256), 0, st, j, xj);
     }
     return 0;

@@ -141,6 +141,26 @@ struct AttnJob {
     float* lse;
 };
 
+// Merge jobs laid out by XCD: workgroup i runs on XCD i mod 8 and takes job lo[x] + i / 8 of the jobs
+// [lo[x], lo[x + 1]) whose query's split partials were written on XCD x (jobs in query-major order, so the
+// ranges are contiguous).  xcd_jobs builds the table from G groups of jpg jobs and the home XCD of each group
+// (non-decreasing in the group).
+struct XcdJobs { int lo[9]; };
+template <class Home>
+inline XcdJobs xcd_jobs(int G, int jpg, Home home, int* most) {
+    XcdJobs xj;
+    int x = 0;
+    xj.lo[0] = 0;
+    for (int g = 0; g < G; ++g) {
+        const int h = home(g);
+        while (x < h && x < 8) xj.lo[++x] = g * jpg;
+    }
+    while (x < 8) xj.lo[++x] = G * jpg;
+    *most = 0;
+    for (int k = 0; k < 8; ++k) *most = xj.lo[k + 1] - xj.lo[k] > *most ? xj.lo[k + 1] - xj.lo[k] : *most;
+    return xj;
+}
+
 }  // namespace csa_attn
 
 namespace csa_host {
