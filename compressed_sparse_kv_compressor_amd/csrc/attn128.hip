@@ -515,31 +515,22 @@ __device__ __forceinline__ void combine128_body(const uint16_t* __restrict__ par
 // Two job slots: workgroups [0, nblk_s) run job s, the rest job d; one job is launched with every workgroup
 // below nblk_s.  (With the parameters selected per workgroup like this the compiler allocates the body's
 // registers without spills; with the job's fields passed straight in it spilled ~100 VGPRs.)
-// XCD-aware order: workgroup i runs on XCD i mod 8, and XCD x takes the contiguous range [x per, (x + 1) per)
-// of the launch's blocks (nblk of them, query-major), so the splits of one query share an XCD and its L2,
-// where the merge (launched with the same map) finds their partials.
 template <bool PAGED, bool ROPE, bool FP8, bool PART>
-__global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, int nblk_s, int per)
+__global__ __launch_bounds__(A_TPB, 1) void k_attn128(AttnJob js, AttnJob jd, int nblk_s)
 {
     CSA_A128_LDS
-    const int vb = (int)(blockIdx.x & 7u) * per + (int)(blockIdx.x >> 3);
-    const bool first = vb < nblk_s;
+    const bool first = (int)blockIdx.x < nblk_s;
     const AttnJob& j = first ? js : jd;
-    attn128_body<PAGED, ROPE, FP8, PART>(first ? vb : vb - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
+    attn128_body<PAGED, ROPE, FP8, PART>(first ? blockIdx.x : blockIdx.x - nblk_s, buf0, buf1, buf2, buf3, rcode, j.q, j.R, j.Tq, j.H,
                  j.pos0, j.scale_log2, j.nunits, j.nsplit, j.rps, j.part_o, j.part_ml, j.out, j.lse);
 }
 #undef CSA_A128_LDS
 
-// Merge jobs (query, head quad, chunk c of 32), in that order, each 256 threads x 32 covering the 8192 chunk
-// positions of one query and head quad.  Workgroup i runs on XCD i mod 8 and takes job lo[x] + i / 8 of the jobs
-// [lo[x], lo[x + 1]) whose query's partials were written on XCD x (the attention's map above).
-__global__ __launch_bounds__(256) void k_combine128(AttnJob j, XcdJobs xj)
+// grid (32, HQ, BT): 256 threads x 32 cover the 8192 chunk positions of one query and head quad
+__global__ __launch_bounds__(256) void k_combine128(AttnJob j)
 {
-    const int x = (int)(blockIdx.x & 7u), J = xj.lo[x] + (int)(blockIdx.x >> 3);
-    if (J >= xj.lo[x + 1]) return;
-    const int HQ = j.H >> 7;
-    combine128_body((const uint16_t*)j.part_o, j.part_ml, j.H, j.nsplit, j.out, j.lse, j.R.sink, J / (32 * HQ),
-                    (J >> 5) % HQ, (J & 31) * 256 + threadIdx.x, j.R, j.Tq, j.pos0);
+    combine128_body((const uint16_t*)j.part_o, j.part_ml, j.H, j.nsplit, j.out, j.lse, j.R.sink, blockIdx.z,
+                    blockIdx.y, blockIdx.x * 256 + threadIdx.x, j.R, j.Tq, j.pos0);
 }
 
 }  // namespace
@@ -553,11 +544,10 @@ int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag) 
     // kernel carries none of their code, whose registers it cannot spare)
     const bool paged = j.R.pm.table != nullptr, rope = j.R.rope_rd != 0, fp8 = j.R.kv_fp8 != 0;
     const bool part = (j.rps / TILE) % NBUF != 0;
-    const int per = (nblk + 7) / 8;
-#define CSA_A128(P_, R_, F_)                                                                                    \
-    do {                                                                                                        \
-        if (part) CSA_LAUNCH(tag, (k_attn128<P_, R_, F_, true>), dim3(8 * per), dim3(A_TPB), 0, st, j, j, nblk, per); \
-        else CSA_LAUNCH(tag, (k_attn128<P_, R_, F_, false>), dim3(8 * per), dim3(A_TPB), 0, st, j, j, nblk, per);     \
+#define CSA_A128(P_, R_, F_)                                                                                 \
+    do {                                                                                                     \
+        if (part) CSA_LAUNCH(tag, (k_attn128<P_, R_, F_, true>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);  \
+        else CSA_LAUNCH(tag, (k_attn128<P_, R_, F_, false>), dim3(nblk), dim3(A_TPB), 0, st, j, j, nblk);      \
     } while (0)
     if (fp8) {
         if (paged && rope) CSA_A128(true, true, true);
@@ -571,13 +561,7 @@ int attn128_launch(const csa_attn::AttnJob& j, hipStream_t st, const char* tag) 
         else CSA_A128(false, false, false);
     }
 #undef CSA_A128
-    if (j.nsplit > 1) {
-        // the XCD holding most of a (query, head quad)'s splits: that of its middle split's block
-        int most;
-        const XcdJobs xj = xcd_jobs(BT * HQ, 32, [&](int bh) {
-            return ((bh / HQ * j.nsplit + j.nsplit / 2) * HQ + bh % HQ) / per; }, &most);
-        CSA_LAUNCH("k_combine", k_combine128, dim3(8 * most), dim3(256), 0, st, j, xj);
-    }
+    if (j.nsplit > 1) CSA_LAUNCH("k_combine", k_combine128, dim3(32, HQ, BT), dim3(256), 0, st, j);
     return 0;
 }
 
