@@ -141,6 +141,36 @@ __device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t x, float scale) {
 }
 
 
+// LDS accesses of the ring sweep in k_score, in asm: the compiler cannot tell the ring (written by loads to
+// LDS) from the other LDS arrays, so it would hold every LDS access of the sweep until all loads in flight had
+// landed, draining the ring at each tile.  A read block waits for its own results.
+__device__ __forceinline__ uint32_t lds_addr(const CSA_LDS void* p) { return (uint32_t)(size_t)p; }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(size_t)(const CSA_LDS void*)p; }
+template <int N>
+__device__ __forceinline__ void lds_read_b128(u32x4_t (&v)[N], uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+    static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 reads");
+    if constexpr (N == 1)
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v[0]) : "v"(a0) : "memory");
+    else if constexpr (N == 2)
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1]) : "v"(a0), "v"(a1) : "memory");
+    else
+        asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(a0), "v"(a1), "v"(a2), "v"(a3) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_read_b32(uint32_t a) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+    return v;
+}
+__device__ __forceinline__ void lds_write_b32(uint32_t a, uint32_t v) {
+    asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_add_u32(uint32_t a, uint32_t v) {
+    asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // k_score
 // ---------------------------------------------------------------------------
@@ -148,7 +178,7 @@ __device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t x, float scale) {
 // B = 16 keys, both loaded as 1/4 of a row per lane (the same k-slot order),
 // so D[column][key] leaves every lane with HP/4... 4 heads of one key: the
 // head reduction is mostly lane-local (one xor-16 shuffle for HP = 8).
-template <int DT, int DI, int HI, bool PAGED>
+template <int DT, int DI, int HI, bool PAGED, bool RING>
 __global__ __launch_bounds__(TPB) void k_score(
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int keys_per_wg, int topk,
@@ -165,12 +195,22 @@ __global__ __launch_bounds__(TPB) void k_score(
     constexpr int LPR = HP / 4;               // lanes (of one key) holding one row's heads
     constexpr int RB = DT == 0 ? DI * 2 : (DT == 1 ? DI : DI / 2);     // bytes per key / query-head row
     static_assert(DT != 2 || DI == 128, "MXFP4 rows: one 32-element scale block per lane group");
+    // RING: the keys stream through a per-wave ring of NS 16-key tiles in LDS, filled by loads to LDS in
+    // which each 64-lane instruction moves 1 KiB of contiguous rows (the register loads below read 16 rows
+    // x 64 bytes per instruction); only for groups whose rows all keep their histogram in LDS (NL = 1),
+    // so that the sweep issues no other vector-memory instruction and the load counts stay exact.
+    static_assert(!RING || (DT != 2 && G >= 1), "ring sweep: bf16 / e4m3 keys");
+    constexpr int NL = RING ? 1 : 2;          // rows of a group with LDS histograms
+    constexpr int TILEB = 16 * RB;            // bytes of one 16-key tile
+    constexpr int NS = RING ? (32768 / 4) / TILEB : 1;   // ring slots per wave (32 KiB per workgroup)
+    static_assert(!RING || (NS >= 2 && TILEB % 1024 == 0), "ring: >= 2 slots of whole 1 KiB loads");
 
-    __shared__ uint32_t lh[2][BINS1];         // histograms of up to 2 rows of a group
-    __shared__ uint32_t ldmax[2];
+    __shared__ uint32_t lh[NL][BINS1];        // histograms of up to NL rows of a group
+    __shared__ uint32_t ldmax[NL];
     // the same rows' scores, written out in 16-byte stores after the key sweep (scattered 4-byte stores
     // between the key loads cost the stream ~9% of its rate)
-    __shared__ __attribute__((aligned(16))) float lsc[2][KPW_MAX];
+    __shared__ __attribute__((aligned(16))) float lsc[NL][KPW_MAX];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[RING ? 4 * NS * TILEB : 16];
     // paged keys: the pool page of every page the workgroup's key range touches, read once here, so that a
     // key load waits on no table load (a table load between two key batches made the wait for it wait for
     // the batch in flight as well).  Sized for pages of >= 2 entries, which keeps two workgroups per CU;
@@ -179,7 +219,7 @@ __global__ __launch_bounds__(TPB) void k_score(
     __shared__ uint32_t lpg[PAGED ? PG_CAP : 1];
 
     const int b = blockIdx.y;
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int lane = lane_id(), wave = RING ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int key0 = blockIdx.x * keys_per_wg;
     const int NG = (Tq + G - 1) / G;
@@ -198,9 +238,9 @@ __global__ __launch_bounds__(TPB) void k_score(
 
     for (int g = 0; g < NG; ++g) {
         const int nrow = min(G, Tq - g * G);
-        const int nlds = min(nrow, 2);
+        const int nlds = min(nrow, NL);
         for (int i = threadIdx.x; i < nlds * BINS1; i += TPB) (&lh[0][0])[i] = 0;
-        if (threadIdx.x < 2) ldmax[threadIdx.x] = 0;
+        if (threadIdx.x < NL) ldmax[threadIdx.x] = 0;
         __syncthreads();
 
         // A operand: query column `col` = (row ta, head ha)
@@ -283,27 +323,25 @@ __global__ __launch_bounds__(TPB) void k_score(
                 if (DT == 2) dsc[u] = k_scale[prow * (DI / 32) + grp];
             }
         };
-        auto compute_batch = [&](int tt0, const u32x4_t (&cur)[U][NV], const uint32_t (&csc)[U]) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
+        // one 16-key tile: kv = this lane's NV chunks of key kbase + col, sc its MXFP4 scale byte
+        auto compute_tile = [&](int kbase, const u32x4_t (&kv)[NV], uint32_t sc_b) {
                     // (tiles past the visible keys are computed and dropped: no branch between the
                     //  loads and their uses)
-                    const int kbase = key0 + ((tt0 + u) * 4 + wave) * 16;
                     f32x4_t acc = {0, 0, 0, 0}, aacc = {0, 0, 0, 0};
 #pragma unroll
                     for (int s = 0; s < STEPS; ++s) {
                         u32x4_t v;
-                        if (DT == 0) v = cur[u][s];
-                        else if (DT == 2) v = fp4x8_to_bf16x8(cur[u][0][s], e8m0_scale(csc[u]));
-                        else v = e4m3x8_to_bf16x8(cur[u][s / 2][(s & 1) * 2], cur[u][s / 2][(s & 1) * 2 + 1]);
+                        if (DT == 0) v = kv[s];
+                        else if (DT == 2) v = fp4x8_to_bf16x8(kv[0][s], e8m0_scale(sc_b));
+                        else v = e4m3x8_to_bf16x8(kv[s / 2][(s & 1) * 2], kv[s / 2][(s & 1) * 2 + 1]);
                         acc = mfma16_bf16(qb[s], as_bf16x8(v), acc);
                         if (DT != 1) aacc = mfma16_bf16(qa[s], as_bf16x8(v & 0x7fff7fffu), aacc);
                     }
                     if (DT == 1) {
                         // |q|.|k| bound: one e4m3 MFMA (K = 128) on the raw bytes with the sign bits cleared
                         typedef __attribute__((ext_vector_type(8))) int i32x8_t;
-                        const u32x4_t k0 = cur[u][0] & 0x7f7f7f7fu;
-                        const u32x4_t k1 = NV > 1 ? cur[u][NV > 1 ? 1 : 0] & 0x7f7f7f7fu : u32x4_t{0, 0, 0, 0};
+                        const u32x4_t k0 = kv[0] & 0x7f7f7f7fu;
+                        const u32x4_t k1 = NV > 1 ? kv[NV > 1 ? 1 : 0] & 0x7f7f7f7fu : u32x4_t{0, 0, 0, 0};
                         const i32x8_t A8 = {(int)qf8a[0][0], (int)qf8a[0][1], (int)qf8a[0][2], (int)qf8a[0][3],
                                             (int)qf8a[1][0], (int)qf8a[1][1], (int)qf8a[1][2], (int)qf8a[1][3]};
                         const i32x8_t B8 = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
@@ -325,20 +363,80 @@ __global__ __launch_bounds__(TPB) void k_score(
                     const int s = kbase + col;
                     if (writer && s < nv) {
                         const float sc = x + 0.0f;                        // canonical +0
-                        if (lrow < nlds) lsc[lrow][s - key0] = sc;
-                        else S[r * NcP + s] = sc;
                         const uint32_t key = f32_key(sc);
-                        if (lrow < nlds) atomicAdd(&lh[lrow][key >> 20], 1u);
-                        else atomicAdd(&hist[r * HIST_WORDS + (key >> 20)], 1u);
+                        if constexpr (RING) {
+                            lds_write_b32(lds_addr(&lsc[0][s - key0]), __float_as_uint(sc));
+                            lds_add_u32(lds_addr(&lh[0][key >> 20]), 1u);
+                        } else if (lrow < nlds) {
+                            lsc[lrow][s - key0] = sc;
+                            atomicAdd(&lh[lrow][key >> 20], 1u);
+                        } else {
+                            S[r * NcP + s] = sc;
+                            atomicAdd(&hist[r * HIST_WORDS + (key >> 20)], 1u);
+                        }
                         const float ej = e * 1.0009765625f + 1.1754943508222875e-38f;
                         dmax_loc = fmaxf(dmax_loc, ej + fabsf(sc) * 5.9604644775390625e-08f);
                     }
-                }
+        };
+        auto compute_batch = [&](int tt0, const u32x4_t (&cur)[U][NV], const uint32_t (&csc)[U]) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) compute_tile(key0 + ((tt0 + u) * 4 + wave) * 16, cur[u], csc[u]);
         };
         // The loads of the next batch are issued unconditionally (past the end they reread the current
         // batch, an L2 hit), so that no branch separates loads from their uses and the compiler's wait
         // counts stay exact: the next batch stays in flight while this one computes.
         __builtin_amdgcn_s_waitcnt(0);        // the per-row loads above have landed
+        if constexpr (RING) {
+            // Ring sweep.  Load j of a tile moves its rows j RPI .. j RPI + RPI - 1: lane l fetches 16 bytes of
+            // row j RPI + l / CPR into slot bytes 1024 j + 16 l.  Chunk c of tile row kr sits at chunk
+            // c ^ swz(kr) of its slot row, so the 16 lanes of one LDS read phase (16 keys, one chunk) fall on
+            // distinct bank groups.  Tile t goes to slot t mod NS; it is read into registers once its loads have
+            // landed (this wave's loads complete in order: the count of loads still in flight says which), and
+            // the freed slot takes tile t + NS before tile t computes.  Tiles past the wave's last visible
+            // tile reread that tile (an L2 hit), so every step issues the same loads and the counts stay exact.
+            constexpr int CPR = RB / 16;          // 16-byte chunks per key row
+            constexpr int RPI = 1024 / RB;        // key rows per load
+            constexpr int NI = TILEB / 1024;      // loads per tile
+            auto swz = [](int kr) { return (kr / (16 / CPR)) % CPR; };
+            CSA_LDS uint8_t* wr = (CSA_LDS uint8_t*)ring + wave * (NS * TILEB);
+            const int first = key0 + wave * 16;
+            const int ntw = __builtin_amdgcn_readfirstlane(first < nvmax ? min(tiles, (nvmax - first + 63) / 64) : 0);
+            const int lr_i = lane / CPR, lc = lane % CPR;
+            auto issue = [&](int t, int slot) {
+                const int tb = key0 + (min(t, ntw - 1) * 4 + wave) * 16;
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int kr = i * RPI + lr_i;
+                    const int krow = min(tb + kr, nvmax - 1);
+                    size_t prow = (size_t)b * Nc + krow;
+                    if constexpr (PAGED)
+                        prow = ((size_t)lds_read_b32(lds_addr(&lpg[(krow >> pm.eshift) - pg0])) << pm.eshift) |
+                               (size_t)(krow & ((1 << pm.eshift) - 1));
+                    const char* src = (const char*)k_idx + prow * RB + 16 * (lc ^ swz(kr));
+                    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                                     (CSA_LDS void*)(wr + slot * TILEB + i * 1024), 16, 0, 0);
+                }
+            };
+            if (ntw > 0) {
+#pragma unroll
+                for (int j = 0; j < NS; ++j) issue(j, j);
+                for (int t0 = 0; t0 < ntw; t0 += NS) {
+#pragma unroll
+                    for (int j = 0; j < NS; ++j) {
+                        const int t = t0 + j;
+                        if (t >= ntw) break;
+                        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI * (NS - 1)) : "memory");   // tile t landed
+                        const uint32_t sl = lds_addr(wr + j * TILEB + col * RB);
+                        u32x4_t kv[NV];
+                        lds_read_b128<NV>(kv, sl + 16 * ((grp + 0) ^ swz(col)), sl + 16 * ((grp + 4) ^ swz(col)),
+                                          sl + 16 * ((grp + 8) ^ swz(col)), sl + 16 * ((grp + 12) ^ swz(col)));
+                        issue(t + NS, j);
+                        compute_tile(key0 + (t * 4 + wave) * 16, kv, 0u);
+                    }
+                }
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // the reread loads; the asm LDS ops
+            }
+        } else {
         u32x4_t ka[U][NV], kb[U][NV];
         uint32_t sa[U], sb[U];                // MXFP4 scale bytes of the batch's key rows (DT == 2)
         if (key0 + wave * 16 < nvmax) {
@@ -353,6 +451,7 @@ __global__ __launch_bounds__(TPB) void k_score(
                 compute_batch(tt0 + U, kb, sb);
                 if (!more2) break;
             }
+        }
         }
         if (writer) {
             if (lrow < nlds) atomicMax(&ldmax[lrow], __float_as_uint(dmax_loc));
@@ -797,12 +896,26 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
     // gives >= 512 workgroups (two per CU), so the grid runs in one round without a tail
     int kpw = KPW_MAX;
     while (kpw > 1024 && (size_t)((Nc + kpw - 1) / kpw) * B < 512) kpw >>= 1;
-    if (pm.table)
-        CSA_LAUNCH("k_score", (k_score<DT, DI, HI, true>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
-                   q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm, q_scale, k_scale);
-    else
-        CSA_LAUNCH("k_score", (k_score<DT, DI, HI, false>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,
-                   q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm, q_scale, k_scale);
+    // the ring sweep: bf16 / e4m3 keys, one row per group with an LDS histogram (a single query row, or 16
+    // heads per row), and paged keys only with the page table staged in LDS (pages of >= 2 entries)
+    constexpr int HP = HI < 4 ? 4 : HI;
+    const bool ring = DT != 2 && HP >= 8 && (Tq == 1 || HP == 16) && (!pm.table || pm.eshift > 0);
+#define CSA_SCORE(PG, RG)                                                                                        \
+    CSA_LAUNCH("k_score", (k_score<DT, DI, HI, PG, RG>), dim3((Nc + kpw - 1) / kpw, B), dim3(TPB), 0, st,       \
+               q_idx, w_idx, k_idx, Tq, Nc, NcP, L, m, pos0, kpw, topk, S, hist, seq_lens, pm, q_scale, k_scale)
+    bool launched = false;
+    if constexpr (DT != 2 && HP >= 8) {
+        if (ring) {
+            if (pm.table) CSA_SCORE(true, true);
+            else CSA_SCORE(false, true);
+            launched = true;
+        }
+    }
+    if (!launched) {
+        if (pm.table) CSA_SCORE(true, false);
+        else CSA_SCORE(false, false);
+    }
+#undef CSA_SCORE
     CSA_LAUNCH("k_collect", k_collect, dim3(NcP / CCHUNK, (unsigned)R), dim3(STPB), 0, st, S, hist, list, ctab, Tq,
                Nc, NcP, L, m, pos0, topk, seq_lens);
     CSA_LAUNCH("k_select", (k_select<DT, DI, HI>), dim3((unsigned)R), dim3(SEL_TPB), 0, st, hist, list, ctab, band,
