@@ -327,9 +327,57 @@ def prefill_leg(args, dev, cpu=True):
     }
     if cpu:
         res.update(prefill_cpu_leg(pc, q_idx, w_idx, k_idx, idx))
-    del q_idx, k_idx, w_idx, ws
+    del q_idx, k_idx, ws
+    res["e4m3_operands"] = prefill_e4m3_leg(args, dev, pc, w_idx)
+    del w_idx
     torch.cuda.empty_cache()
     res["sparse_attn"] = prefill_attn_leg(args, dev, pc, idx, cpu=cpu)
+    return res
+
+
+def prefill_e4m3_leg(args, dev, pc, w_idx):
+    """The same prefill call with e4m3 queries and keys: widened exactly to bf16 in the workspace
+    (k_pwiden), then the same many-query kernels; ms per call and the widening's share."""
+    import torch
+
+    from compressed_sparse_kv_compressor_amd import binding as b
+    from compressed_sparse_kv_compressor_amd import synth
+
+    Tq, L, m, HI, dI, topk, Nc, pos0 = pc.Tq, pc.L, pc.m, pc.HI, pc.dI, pc.topk, pc.Nc, pc.pos0
+    g = synth.parallel_bits_to_device
+    q8 = g(0, "prefill_q_idx", (1, Tq, HI, dI), dI ** -0.5, 1, dev)
+    k8 = g(0, "prefill_k_idx", (1, Nc, dI), dI ** -0.5, 1, dev)
+    idx = torch.empty((1, Tq, topk), dtype=torch.int32, device=dev)
+    ws = b.workspace(b.lib.csa_index_topk_ws_bytes(1, Tq, HI, dI, Nc, topk, 1), dev)
+    stream = torch.cuda.current_stream()
+    steps = max(1, min(args.prefill_steps, 10))
+
+    def call():
+        b.csa_index_topk(q8, w_idx, k8, 1, L, m, pos0, topk, idx, ws=ws, stream=stream)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    b.prof_reset()
+    b.prof_only("k_pwiden")
+    b.prof_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    b.prof_enable(False)
+    wms, wn = b.prof_read("k_pwiden")
+    b.prof_reset()
+    b.prof_only(None)
+    res = {"dtype": "e4m3 queries and keys", "calls": steps, "ms_per_call": round(el / steps * 1e3, 4),
+           "widen_us_per_call": round(wms / steps * 1000.0, 2) if wn else None,
+           "workspace_bytes": int(ws.numel())}
+    del q8, k8, ws
+    torch.cuda.empty_cache()
     return res
 
 

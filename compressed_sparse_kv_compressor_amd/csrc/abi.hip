@@ -410,7 +410,7 @@ size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, 
 size_t csa_index_topk_ex_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype,
                                   const csa_cache_layout_t* layout) {
     if (B < 1 || Tq < 1 || Nc < 1 || HI < 1 || dI < 1 || topk < 1) return 0;
-    return csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk, plain_layout(layout) && dtype != CSA_MXFP4);
+    return csa_host::index_topk_ws_bytes(dtype, HI, dI, B, Tq, Nc, topk, plain_layout(layout));
 }
 
 static int index_topk_impl(const char* fn, const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B,

@@ -25,6 +25,33 @@ __device__ __forceinline__ int row_visible(const long long* seq_lens, int b, int
     return n_visible(Lb - Tq + t, Lb, m, (int)((Lb + m - 1) / m));
 }
 
+// fp8 (OCP e4m3) pair -> bf16 pair, exact (gfx950 hardware conversion, scale 1).
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t v) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI_WORD);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
+    return u32x4_t{e4m3x2_to_bf16x2<false>(x0), e4m3x2_to_bf16x2<true>(x0),
+                   e4m3x2_to_bf16x2<false>(x1), e4m3x2_to_bf16x2<true>(x1)};
+}
+
+// MXFP4: the E8M0 scale byte as the float 2^(s - 127), and eight E2M1 codes (one dword, element 2i in the low
+// nibble of byte i) times that scale as bf16 -- exact: every such value is a bf16 value for the scales the
+// encoder produces (2^-127 .. 2^125).
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+    return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+}
+__device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t x, float scale) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+#define CSA_FP4_PAIR(B) __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, B))
+    return u32x4_t{CSA_FP4_PAIR(0), CSA_FP4_PAIR(1), CSA_FP4_PAIR(2), CSA_FP4_PAIR(3)};
+#undef CSA_FP4_PAIR
+}
+
+
 // Error model of the MFMA path:
 //   |d~_h - d_h| <= E_h = C_DOT * A_h,  A_h = MFMA(|q_h|, |k|) ~ sum_i |q_hi k_i|
 //   |S~ - S| <= sum_h |w_h| ( C_SUM (|d~_h| + E_h) + E_h ) (1 + 2^-10) + 2^-24 |S~| + 2^-126

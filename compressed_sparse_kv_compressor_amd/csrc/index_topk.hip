@@ -114,31 +114,6 @@ __global__ void k_fill(uint32_t* p, size_t n) {
     for (; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
-// fp8 (OCP e4m3) pair -> bf16 pair, exact (gfx950 hardware conversion, scale 1).
-template <bool HI_WORD>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t v) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-    bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI_WORD);
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
-    return u32x4_t{e4m3x2_to_bf16x2<false>(x0), e4m3x2_to_bf16x2<true>(x0),
-                   e4m3x2_to_bf16x2<false>(x1), e4m3x2_to_bf16x2<true>(x1)};
-}
-
-// MXFP4: the E8M0 scale byte as the float 2^(s - 127), and eight E2M1 codes (one dword, element 2i in the low
-// nibble of byte i) times that scale as bf16 -- exact: every such value is a bf16 value for the scales the
-// encoder produces (2^-127 .. 2^125).
-__device__ __forceinline__ float e8m0_scale(uint32_t s) {
-    return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
-}
-__device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t x, float scale) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-#define CSA_FP4_PAIR(B) __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, B))
-    return u32x4_t{CSA_FP4_PAIR(0), CSA_FP4_PAIR(1), CSA_FP4_PAIR(2), CSA_FP4_PAIR(3)};
-#undef CSA_FP4_PAIR
-}
 
 
 // LDS accesses of the ring sweep in k_score, in asm: the compiler cannot tell the ring (written by loads to
@@ -925,7 +900,8 @@ static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx
 }
 
 size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk, bool plain) {
-    if (plain && prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk)) return prefill_index_ws_bytes(B, Tq, Nc);
+    if (plain && prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk))
+        return prefill_index_ws_bytes(dtype, HI, dI, B, Tq, Nc);
     return decode_index_ws_bytes(B, Tq, Nc);
 }
 
@@ -935,8 +911,8 @@ int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, 
                       const uint8_t* q_scale, const uint8_t* k_scale, void* ws, hipStream_t st) {
     const PageMap pm = page_map(lay, m);
     if (!lay.seq_lens && !lay.table && prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk))
-        return prefill_index_launch(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk, idx_out, cnt_out, score_out,
-                                    ws, st);
+        return prefill_index_launch(q_idx, w_idx, k_idx, dtype, HI, dI, B, Tq, Nc, L, m, pos0, topk, idx_out,
+                                    cnt_out, score_out, q_scale, k_scale, ws, st);
 #define CSA_IDX_CASE(DT, DI, HI_)                                                              \
     if (dtype == DT && dI == DI && HI == HI_)                                                  \
         return launch_index<DT, DI, HI_>(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk,     \

@@ -33,12 +33,14 @@ int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, 
                       const uint8_t* q_scale, const uint8_t* k_scale, void* ws, hipStream_t st);
 int kv_fp8_launch(const void* x, long long n, int D, void* y, hipStream_t st);
 int mxfp4_launch(const void* x, long long n, int len, void* codes, void* scales, hipStream_t st);
-// many-query (prefill) indexer path: bf16, HI = 8, dI = 128, Tq >= 64, topk <= 1024
+// many-query (prefill) indexer path: Tq >= 64, topk <= 1024; bf16 / e4m3 rows of dI = 64 or 128 or MXFP4 rows
+// of 128, HI = 1, 2, 4 or 8 (all but bf16 8 x 128 widened to it in the workspace first)
 bool prefill_index_applicable(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk);
-size_t prefill_index_ws_bytes(int B, int Tq, int Nc);
-int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_idx, int B, int Tq, int Nc,
-                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
-                         float* score_out, void* ws, hipStream_t st);
+size_t prefill_index_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc);
+int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int HI, int dI, int B,
+                         int Tq, int Nc, long long L, int m, long long pos0, int topk, int32_t* idx_out,
+                         int32_t* cnt_out, float* score_out, const uint8_t* q_scale, const uint8_t* k_scale, void* ws,
+                         hipStream_t st);
 int fp8_to_bf16_launch(const void* in, void* out, int n, hipStream_t st);
 int rope_launch(const void* x, void* y, const long long* pos, long long n, int D, int rd, int group, double theta,
                 int inverse, hipStream_t st);

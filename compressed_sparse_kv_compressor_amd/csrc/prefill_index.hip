@@ -25,6 +25,12 @@
 //   k_pfallback rows whose list could be incomplete (fewer than k entries above thr,
 //               thr above tau - 2D, a list or band over its capacity): exact scores
 //               of every visible entry and a 64-bit radix select on (S, index)
+// Other operand formats (e4m3 or MXFP4 rows, HI = 1, 2 or 4 heads, dI = 64) run the same kernels on
+// operands widened once into the workspace by k_pwiden: 8 heads x 128 bf16 dims per row.  Nothing the
+// method computes changes: every e4m3 value and every scaled E2M1 value is a bf16 value, a padded dim
+// is zero in query and key (an exact zero term of every dot and norm), and a padded head has weight +0
+// (each adds fmaf(+0, ReLU(d), S) = S to the fma chain, whose partial sums are never -0), so exact and
+// approximate scores, the bound and the selection are those of the original operands.
 // Row bound.  With N_h = ||q_h|| ||k||, the MFMA error model of the decode path
 // (|d~_h - d_h| <= C_DOT sum_i |q_hi k_i| <= C_DOT N_h by Cauchy-Schwarz, and
 // |d~_h| <= N_h (1 + C_DOT)) gives
@@ -1143,6 +1149,44 @@ __global__ __launch_bounds__(FB_TPB) void k_pfallback(
     }
 }
 
+// k_pwiden: rows of the many-query layout (P_HI heads x P_DI bf16) from rows of hin heads x dI elements
+// in format dtype (0 bf16, 1 e4m3, 2 MXFP4 with one E8M0 scale per 32 elements); output row o is head
+// o % P_HI (or the key row o when hin = 1 and hout = 1) of group o / hout.  One thread per 16-byte
+// output chunk; heads past hin and dims past dI are zero.
+__global__ __launch_bounds__(256) void k_pwiden(const void* __restrict__ src, const uint8_t* __restrict__ scale,
+                                                int dtype, long long nout, int hout, int hin, int dI,
+                                                uint16_t* __restrict__ dst)
+{
+    constexpr int CPR = P_DI / 8;                      // 16-byte chunks per output row
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nout * CPR) return;
+    const long long o = i / CPR;
+    const int c = (int)(i % CPR), h = (int)(o % hout);
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (h < hin && 8 * c < dI) {
+        const long long r = o / hout * hin + h;         // source row
+        if (dtype == 0) {
+            v = *(const u32x4_t*)((const uint16_t*)src + r * dI + 8 * c);
+        } else if (dtype == 1) {
+            const uint2 x = *(const uint2*)((const uint8_t*)src + r * dI + 8 * c);
+            v = e4m3x8_to_bf16x8(x.x, x.y);
+        } else {
+            const uint32_t x = *(const uint32_t*)((const uint8_t*)src + r * (dI / 2) + 4 * c);
+            v = fp4x8_to_bf16x8(x, e8m0_scale(scale[r * (dI / 32) + c / 4]));
+        }
+    }
+    *(u32x4_t*)(dst + o * P_DI + 8 * c) = v;
+}
+
+// head weights of the many-query layout: P_HI per row, +0 past hin
+__global__ __launch_bounds__(256) void k_pwiden_w(const float* __restrict__ w, long long R, int hin, float* __restrict__ dst)
+{
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= R * P_HI) return;
+    const int h = (int)(i % P_HI);
+    dst[i] = h < hin ? w[i / P_HI * hin + h] : 0.0f;
+}
+
 // clears the Kmax accumulators [n] and the fallback row count
 __global__ void k_pzero(uint32_t* p, int n, uint32_t* fail) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1188,25 +1232,53 @@ static PrefillPlan prefill_plan(int B, int Tq, int Nc) {
     return P;
 }
 
+// operands the kernels read as they are (others are widened first)
+static bool prefill_direct(int dtype, int HI, int dI) { return dtype == 0 && HI == P_HI && dI == P_DI; }
+
 bool prefill_index_applicable(int dtype, int HI, int dI, int B, int Tq, int Nc, int topk) {
-    return dtype == 0 && HI == P_HI && dI == P_DI && Tq >= 64 && topk <= 1024 && Nc >= 1 &&
+    const bool fmt = (dtype == 0 || dtype == 1) ? (dI == 64 || dI == P_DI) : (dtype == 2 && dI == P_DI);
+    return fmt && (HI == 1 || HI == 2 || HI == 4 || HI == P_HI) && Tq >= 64 && topk <= 1024 && Nc >= 1 &&
            (size_t)Nc * P_ROW_B < ((size_t)1 << 31) && (size_t)B * Tq <= ((size_t)1 << 24);
+}
+
+// widened operands at the start of the workspace: keys [B][Nc][P_DI] bf16 | queries [R][P_HI][P_DI] bf16 |
+// head weights [R][P_HI] f32
+static size_t prefill_widen_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc) {
+    if (prefill_direct(dtype, HI, dI)) return 0;
+    const size_t R = (size_t)B * Tq;
+    return align256((size_t)B * Nc * P_ROW_B) + align256(R * P_HI * P_ROW_B) + align256(R * P_HI * 4);
 }
 
 // kmax [B] | fail [1 + R] | wq [R] | thr [R] | samp [R][NSP] u16 | cnt [R][nsplit1] | cand [R][nsplit1][caps]
 // | fallback score keys [FB_SLOTS][NcP] u32
-size_t prefill_index_ws_bytes(int B, int Tq, int Nc) {
+size_t prefill_index_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc) {
     const PrefillPlan P = prefill_plan(B, Tq, Nc);
-    return align256((size_t)B * 4) + align256((P.R + 1) * 4) + align256(P.R * 4) + align256(P.R * 4) +
+    return prefill_widen_bytes(dtype, HI, dI, B, Tq, Nc) + align256((size_t)B * 4) + align256((P.R + 1) * 4) + align256(P.R * 4) + align256(P.R * 4) +
            align256(P.R * P.NSP * 2) + align256(P.R * P.nsplit1 * 4) + align256(P.R * P.nsplit1 * P.caps * 8) +
            align256((size_t)FB_SLOTS * P.NcP * 4);
 }
 
-int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_idx, int B, int Tq, int Nc,
-                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
-                         float* score_out, void* ws, hipStream_t st) {
+int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int HI, int dI, int B,
+                         int Tq, int Nc, long long L, int m, long long pos0, int topk, int32_t* idx_out,
+                         int32_t* cnt_out, float* score_out, const uint8_t* q_scale, const uint8_t* k_scale, void* ws,
+                         hipStream_t st) {
     const PrefillPlan P = prefill_plan(B, Tq, Nc);
     char* p = (char*)ws;
+    if (!prefill_direct(dtype, HI, dI)) {
+        uint16_t* kw = (uint16_t*)p;        p += align256((size_t)B * Nc * P_ROW_B);
+        uint16_t* qw = (uint16_t*)p;        p += align256(P.R * P_HI * P_ROW_B);
+        float* ww = (float*)p;              p += align256(P.R * P_HI * 4);
+        const long long nk = (long long)B * Nc, nq = (long long)P.R * P_HI, cpr = P_DI / 8;
+        CSA_LAUNCH("k_pwiden", k_pwiden, dim3((unsigned)((nk * cpr + 255) / 256)), dim3(256), 0, st, k_idx, k_scale,
+                   dtype, nk, 1, 1, dI, kw);
+        CSA_LAUNCH("k_pwiden", k_pwiden, dim3((unsigned)((nq * cpr + 255) / 256)), dim3(256), 0, st, q_idx, q_scale,
+                   dtype, nq, P_HI, HI, dI, qw);
+        CSA_LAUNCH("k_pwiden", k_pwiden_w, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, w_idx,
+                   (long long)P.R, HI, ww);
+        k_idx = kw;
+        q_idx = qw;
+        w_idx = ww;
+    }
     uint32_t* kmax = (uint32_t*)p;          p += align256((size_t)B * 4);
     uint32_t* fail = (uint32_t*)p;          p += align256((P.R + 1) * 4);
     float* wq = (float*)p;                  p += align256(P.R * 4);

@@ -224,10 +224,14 @@ int csa_decode_append(const void* hidden, int B, int T, int Dh,
  *           are selected whole, without scoring)
  * Supported: dtype in {CSA_BF16, CSA_E4M3}; HI in {1,2,4,8,16}; dI in {64,128};
  * 1 <= topk <= 4096; 1 <= Tq <= 65536; Nc <= 2^24; pos0 >= 0.
- * Workspace: csa_index_topk_ws_bytes with the call's sizes (the many-query path
- * used for Tq >= 64 with bf16, HI = 8, dI = 128, topk <= 1024 keeps no score
- * matrix; the per-query path holds Tq x Nc fp32 scores and lists).  Returns 0 on
- * invalid sizes. */
+ * Workspace: csa_index_topk_ws_bytes with the call's sizes (the many-query path,
+ * used for Tq >= 64, topk <= 1024, HI in {1,2,4,8} and bf16 / e4m3 rows of
+ * dI 64 or 128 or MXFP4 rows of 128 on the plain layout, keeps no score matrix:
+ * operands other than bf16 8 x 128 are first widened exactly to that format in
+ * the workspace -- every e4m3 and scaled E2M1 value is a bf16 value, padded
+ * heads carry weight +0 and padded dims are zero, so no score changes; the
+ * per-query path holds Tq x Nc fp32 scores and lists).  Returns 0 on invalid
+ * sizes. */
 size_t csa_index_topk_ws_bytes(int B, int Tq, int HI, int dI, int Nc, int topk, int dtype);
 int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int dtype,
                    int B, int Tq, int HI, int dI, int Nc, long long L, int m, long long pos0,
@@ -238,7 +242,9 @@ int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int
  * k_idx is then the pool of indexer-key rows when block_table is given.
  * Results as csa_index_topk (bit-exact to running each sequence on its own
  * contiguous cache).  Such calls always take the per-query path, so the
- * workspace (csa_index_topk_ex_ws_bytes) holds Tq x Nc scores per sequence. */
+ * workspace (csa_index_topk_ex_ws_bytes) holds Tq x Nc scores per sequence; a
+ * plain layout (NULL, or neither seq_lens nor block_table) routes like
+ * csa_index_topk, MXFP4 operands included. */
 /* dtype CSA_MXFP4 ([P2] "mHC、Muon、FP4": the indexer's QK path in FP4; see
  * csa_mxfp4_encode for the format): q_idx is then the E2M1 codes
  * [B][Tq][HI][dI/2] and q_scale their E8M0 scales [B][Tq][HI][dI/32], k_idx the

@@ -51,8 +51,13 @@ def test_workspace_sizes_are_host_arithmetic(b):
     assert lib.csa_index_topk_ws_bytes(0, 1, 8, 128, 10, 4, 0) == 0
     # chunked prefill, 8192 queries x 65536 entries: the many-query path keeps no score matrix
     assert lib.csa_index_topk_ws_bytes(1, 8192, 8, 128, 65536, 1024, 0) < 8192 * 65536 * 4 // 2
-    # the same queries in e4m3 take the per-query path, which holds the scores
-    assert lib.csa_index_topk_ws_bytes(1, 8192, 8, 128, 65536, 1024, 1) > 8192 * 65536 * 4
+    # the same queries in e4m3, or with 4 heads of 64, are widened to bf16 8 x 128 on that path (two
+    # widened operand copies, still no score matrix); 16 heads take the per-query path, which holds the scores
+    bf16_ws = lib.csa_index_topk_ws_bytes(1, 8192, 8, 128, 65536, 1024, 0)
+    widened = 65536 * 256 + 8192 * 8 * 256 + 8192 * 8 * 4
+    assert bf16_ws < lib.csa_index_topk_ws_bytes(1, 8192, 8, 128, 65536, 1024, 1) <= bf16_ws + widened + 3 * 256
+    assert lib.csa_index_topk_ws_bytes(1, 8192, 4, 64, 65536, 1024, 0) < 8192 * 65536 * 4 // 2
+    assert lib.csa_index_topk_ws_bytes(1, 8192, 16, 128, 65536, 1024, 1) > 8192 * 65536 * 4
     assert lib.csa_sparse_attn_ws_bytes(8, 1, 128, 512, 1024, 128) > 0
     assert lib.hca_dense_attn_ws_bytes(1, 1, 16, 128, 32) == 0          # one split: no partials
     # compression of 4 x 65536 tokens of hidden 4096: the pooled rows, plus split-K partials only for

@@ -179,9 +179,9 @@ def test_index_topk_deterministic(b):
 
 
 # ---------------------------------------------------------------------------
-# A7: the many-query (chunked prefill) indexer path: bf16, HI = 8, dI = 128,
-# Tq >= 64, topk <= 1024 (sampled threshold, MFMA contraction with candidate
-# lists, per-row select, exact fallback)
+# A7: the many-query (chunked prefill) indexer path: Tq >= 64, topk <= 1024
+# (sampled threshold, MFMA contraction with candidate lists, per-row select,
+# exact fallback) on bf16 8 x 128 operands; other formats are widened to them
 # ---------------------------------------------------------------------------
 
 PREFILL_INDEX_CASES = [
@@ -206,6 +206,60 @@ def test_index_topk_many_queries_bit_exact(b, case):
     assert np.array_equal(got_cnt, want_cnt)
     bad = np.nonzero((got_idx != want_idx).any(axis=-1))
     assert len(bad[0]) == 0, f"{len(bad[0])} rows differ, first {bad[0][:5]} {bad[1][:5]}"
+
+
+# Other operand formats on the many-query path: widened exactly to bf16 8 x 128 in the workspace
+# (e4m3 rows, fewer heads with weight +0 in the padding, dI = 64 zero-padded), bit-exact to the oracle
+# over the original operands.  The workspace check confirms the route keeps no score matrix.
+WIDENED_PREFILL_CASES = [
+    # (dtype, HI, dI, B, Tq, L, pos0 or None (= L - Tq), topk)
+    (1, 8, 128, 1, 200, 4 * 3000 + 1, None, 64),    # e4m3 keys and queries, ragged blocks
+    (1, 8, 128, 2, 64, 4 * 2500, None, 100),        # e4m3, two sequences
+    (0, 4, 64, 1, 128, 4 * 4096, None, 64),          # the single-sequence indexer shape (4 x 64)
+    (1, 2, 128, 1, 300, 4 * 3000, 4 * 400, 64),      # e4m3, 2 heads, causal (few samples per row)
+    (0, 1, 64, 1, 96, 4 * 2000, None, 256),          # one head
+    (1, 4, 64, 1, 130, 4 * 9000, None, 1024),        # e4m3 4 x 64 at the largest k, several key splits
+]
+
+
+def widened_ws(b, B, Tq, Nc, topk):
+    """workspace of the many-query path for bf16 8 x 128 operands plus the widened keys, queries and weights"""
+    a = lambda x: (x + 255) // 256 * 256
+    return (b.lib.csa_index_topk_ws_bytes(B, Tq, 8, 128, Nc, topk, 0) + a(B * Nc * 256) + a(B * Tq * 8 * 256)
+            + a(B * Tq * 8 * 4))
+
+
+@pytest.mark.parametrize("case", WIDENED_PREFILL_CASES)
+def test_index_topk_many_queries_widened_bit_exact(b, case):
+    dtype, HI, dI, B, Tq, L, pos0, topk = case
+    m = 4
+    Nc = -(-L // m)
+    pos0 = L - Tq if pos0 is None else pos0
+    assert b.lib.csa_index_topk_ws_bytes(B, Tq, HI, dI, Nc, topk, dtype) == widened_ws(b, B, Tq, Nc, topk)
+    q, w, k, _ = synth.indexer_inputs(500 + Tq + HI, B, Tq, HI, dI, Nc, dtype)
+    want_idx, want_cnt, _, _ = oracle.index_topk(q, w, k, L, m, pos0, topk, dtype)
+    got_idx, got_cnt = run_index(b, q, w, k, L, m, pos0, topk, dtype)
+    assert np.array_equal(got_cnt, want_cnt)
+    bad = np.nonzero((got_idx != want_idx).any(axis=-1))
+    assert len(bad[0]) == 0, f"{len(bad[0])} rows differ, first {bad[0][:5]} {bad[1][:5]}"
+
+
+def test_index_topk_many_queries_mxfp4_bit_exact(b):
+    # MXFP4 codes and scales widened to bf16 (every scaled E2M1 value is a bf16 value)
+    B, Tq, HI, dI, m, topk, Nc = 1, 96, 8, 128, 4, 128, 3000
+    q, w, k, _ = synth.indexer_inputs(31, B, Tq, HI, dI, Nc, 0)
+    qc, qs = oracle.mxfp4_encode(q)
+    kc, ks = oracle.mxfp4_encode(k)
+    L = Nc * m
+    assert b.lib.csa_index_topk_ex_ws_bytes(B, Tq, HI, dI, Nc, topk, b.MXFP4, None) == widened_ws(b, B, Tq, Nc, topk)
+    want, wc, _, _ = oracle.index_topk_mxfp4(qc, qs, w, kc, ks, L, m, L - Tq, topk)
+    idx = torch.empty((B, Tq, topk), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((B, Tq), dtype=torch.int32, device=DEV)
+    b.csa_index_topk(dev(qc), dev(w), dev(kc), b.MXFP4, L, m, L - Tq, topk, idx, cnt, q_scale=dev(qs),
+                     k_scale=dev(ks))
+    torch.cuda.synchronize()
+    assert np.array_equal(cnt.cpu().numpy(), wc)
+    assert np.array_equal(idx.cpu().numpy(), want)
 
 
 def test_index_topk_many_queries_planted(b):
@@ -291,14 +345,16 @@ def test_index_topk_many_queries_rounding_tie(b, fallback):
     assert np.array_equal(got_idx, want_idx)
 
 
-def test_index_topk_many_queries_prefill_size_sampled(b):
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_index_topk_many_queries_prefill_size_sampled(b, dtype):
     # the chunked-prefill workload: 8192 new queries at the end of a 262144-token context
-    # (65536 entries, k = 1024); sampled rows against the oracle, every row for its invariants
+    # (65536 entries, k = 1024); sampled rows against the oracle, every row for its invariants;
+    # e4m3 operands take the same path over their exact bf16 widening
     B, Tq, HI, dI, m, topk = 1, 8192, 8, 128, 4, 1024
     L = 262144
     Nc, pos0 = L // m, L - Tq
-    q, w, k, _ = synth.indexer_inputs(0, B, Tq, HI, dI, Nc, 0)
-    got_idx, got_cnt = run_index(b, q, w, k, L, m, pos0, topk, 0)
+    q, w, k, _ = synth.indexer_inputs(0, B, Tq, HI, dI, Nc, dtype)
+    got_idx, got_cnt = run_index(b, q, w, k, L, m, pos0, topk, dtype)
     assert (got_cnt == topk).all()
     assert (np.diff(got_idx[0], axis=-1) > 0).all()
     nv = (pos0 + np.arange(Tq) + 1) // m
@@ -306,7 +362,7 @@ def test_index_topk_many_queries_prefill_size_sampled(b):
     rows = sorted(set([0, 1, 2, 31, 32, 4095, 4096, 8190, 8191] +
                       list(np.random.default_rng(5).integers(0, Tq, 7))))
     for t in rows:
-        want_idx, _, _, _ = oracle.index_topk(q[:, t:t + 1], w[:, t:t + 1], k, L, m, pos0 + t, topk)
+        want_idx, _, _, _ = oracle.index_topk(q[:, t:t + 1], w[:, t:t + 1], k, L, m, pos0 + t, topk, dtype)
         assert np.array_equal(got_idx[:, t], want_idx[:, 0]), f"row {t}"
 
 
