@@ -49,7 +49,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 DOMINANT = "k_score"
 PREFILL_DOMINANT = "k_pscore"
 PREFILL_KERNELS = ("k_pzero", "k_pnorm", "k_pscore_sample", "k_pthresh", "k_pscore", "k_pselect", "k_pfb_score",
-                   "k_pfb_select", "k_pfallback")
+                   "k_pfb_rows")
 KERNELS = ("k_fill", "k_score", "k_collect", "k_select", "k_attn_sparse", "k_attn_dense", "k_combine")
 
 

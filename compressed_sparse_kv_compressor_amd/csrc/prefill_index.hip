@@ -22,9 +22,10 @@
 //               D (below) entries above tau + 2D are in, those in the band are
 //               rescored exactly and ranked; the chosen indices are written in
 //               ascending order
-//   k_pfallback rows whose list could be incomplete (fewer than k entries above thr,
-//               thr above tau - 2D, a list or band over its capacity): exact scores
-//               of every visible entry and a 64-bit radix select on (S, index)
+//   k_pfb_score, k_pfb_rows  rows whose list could be incomplete (fewer than k
+//               entries above thr, thr above tau - 2D, a list or band over its
+//               capacity): exact scores of every visible entry, then a radix select
+//               on the exact score keys (ties by index)
 // Other operand formats (e4m3 or MXFP4 rows, HI = 1, 2 or 4 heads, dI = 64) run the same kernels on
 // operands widened once into the workspace by k_pwiden: 8 heads x 128 bf16 dims per row.  Nothing the
 // method computes changes: every e4m3 value and every scaled E2M1 value is a bf16 value, a padded dim
@@ -968,9 +969,10 @@ __global__ __launch_bounds__(64 * SW_ROWS) void k_pselect(
 // ---------------------------------------------------------------------------
 // Exact fallback for the rows the certified path gave up on.  The first FB_SLOTS
 // failed rows: k_pfb_score spreads the exact scores of their visible entries over
-// the whole grid (a score key per entry), then k_pfb_select selects each row's
+// the whole grid (a score key per entry), then k_pfb_rows selects each row's
 // top-k from its stored keys with one workgroup.  Rows beyond FB_SLOTS (only when
-// more than FB_SLOTS rows fail) go to k_pfallback, which scores its row itself.
+// more than FB_SLOTS rows fail) are scored and selected by the same workgroups
+// afterwards, one row at a time.
 // ---------------------------------------------------------------------------
 constexpr int FB_CH = 512;                    // workgroups of k_pfb_score (4 waves each)
 constexpr int FB_G = 8;                       // key rows fetched together per wave
@@ -1109,23 +1111,10 @@ __global__ __launch_bounds__(256) void k_pfb_score(
     }
 }
 
-__global__ __launch_bounds__(FB_TPB) void k_pfb_select(
-    const uint32_t* __restrict__ fail, int Tq, int Nc, long long L, int m, long long pos0, int topk,
-    const uint32_t* __restrict__ keys, size_t NcP, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
-    float* __restrict__ score_out)
-{
-    __shared__ __align__(16) uint32_t h[1024];
-    __shared__ uint32_t red[2 * (FB_TPB / 64)];
-    const uint32_t fi = blockIdx.x;
-    if (fi >= min(fail[0], (uint32_t)FB_SLOTS)) return;
-    const int r = (int)fail[1 + fi], t = r % Tq;
-    const int nv = n_visible(pos0 + t, L, m, Nc);
-    fb_select_row(keys + (size_t)fi * NcP, nv, topk, idx_out + (size_t)r * topk,
-                  score_out ? score_out + (size_t)r * topk : nullptr, h, red);
-    if (cnt_out && threadIdx.x == 0) cnt_out[r] = topk;
-}
-
-__global__ __launch_bounds__(FB_TPB) void k_pfallback(
+// One workgroup per fallback slot x: first the top-k of failed row x (x < FB_SLOTS) from the score keys
+// k_pfb_score stored in region x, then (only when more than FB_SLOTS rows failed) rows FB_SLOTS + x,
+// FB_SLOTS + x + gridDim.x, .., each scored by this workgroup itself into the same region and selected.
+__global__ __launch_bounds__(FB_TPB) void k_pfb_rows(
     const uint32_t* __restrict__ fail, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, int Tq, int Nc, long long L, int m, long long pos0, int topk,
     uint32_t* __restrict__ keys, size_t NcP, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
@@ -1134,7 +1123,16 @@ __global__ __launch_bounds__(FB_TPB) void k_pfallback(
     __shared__ __align__(16) uint32_t h[1024];
     __shared__ uint32_t red[2 * (FB_TPB / 64)];
     const uint32_t nf = fail[0];
+    if (blockIdx.x >= nf) return;                      // (uniform) nothing failed for this slot
     uint32_t* K = keys + (size_t)blockIdx.x * NcP;
+    {
+        const int r = (int)fail[1 + blockIdx.x], t = r % Tq;
+        const int nv = n_visible(pos0 + t, L, m, Nc);
+        fb_select_row(K, nv, topk, idx_out + (size_t)r * topk, score_out ? score_out + (size_t)r * topk : nullptr,
+                      h, red);
+        if (cnt_out && threadIdx.x == 0) cnt_out[r] = topk;
+        __syncthreads();                               // K is reused below
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (uint32_t fi = FB_SLOTS + blockIdx.x; fi < nf; fi += gridDim.x) {
         const int r = (int)fail[1 + fi], b = r / Tq, t = r % Tq;
@@ -1311,10 +1309,8 @@ int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_id
                score_out, fail);
     CSA_LAUNCH("k_pfb_score", k_pfb_score, dim3(FB_CH), dim3(256), 0, st, fail, q, w_idx, k, Tq, Nc, L, m, pos0, fbk,
                P.NcP);
-    CSA_LAUNCH("k_pfb_select", k_pfb_select, dim3(FB_SLOTS), dim3(FB_TPB), 0, st, fail, Tq, Nc, L, m, pos0, topk, fbk,
-               P.NcP, idx_out, cnt_out, score_out);
-    CSA_LAUNCH("k_pfallback", k_pfallback, dim3(FB_SLOTS), dim3(FB_TPB), 0, st, fail, q, w_idx, k, Tq, Nc, L, m,
-               pos0, topk, fbk, P.NcP, idx_out, cnt_out, score_out);
+    CSA_LAUNCH("k_pfb_rows", k_pfb_rows, dim3(FB_SLOTS), dim3(FB_TPB), 0, st, fail, q, w_idx, k, Tq, Nc, L, m, pos0,
+               topk, fbk, P.NcP, idx_out, cnt_out, score_out);
     return 0;
 }
 
