@@ -47,6 +47,9 @@ METRIC = "CSA+HCA decode queries/s & HBM GB/s at 1M ctx; indexer prefill TFLOP/s
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 DOMINANT = "k_score"
+# The dominant kernel is bracketed by HIP events on every EVENT_EVERY-th step of a timed region only: an
+# event pair on the launch stream costs the step ~5 us of GPU time, which the whole-job value would carry.
+EVENT_EVERY = 8
 PREFILL_DOMINANT = "k_pscore"
 PREFILL_KERNELS = ("k_pzero", "k_pnorm", "k_pscore_sample", "k_pthresh", "k_pscore", "k_pselect", "k_pfb_score",
                    "k_pfb_rows")
@@ -157,17 +160,20 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: HIP events (on the launch stream) around the dominant kernel only
+    # timed region: HIP events (on the launch stream) around the dominant kernel of every EVENT_EVERY-th step
     b.prof_reset()
     b.prof_only(DOMINANT)
-    b.prof_enable(True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
+        sampled = i % EVENT_EVERY == 0
+        if sampled:
+            b.prof_enable(True)
         step(i)
+        if sampled:
+            b.prof_enable(False)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    b.prof_enable(False)
     ms, n = b.prof_read(DOMINANT)
     score_us = ms / n * 1000.0 if n else None
     ms_step = elapsed / args.steps * 1e3
@@ -218,7 +224,9 @@ def main():
                      "achieved": round(achieved, 1) if achieved else None,
                      "kernel_us": round(score_us, 2) if score_us else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
-                     "traffic": load_traffic(score_bytes), "algorithmic_bytes_per_launch": score_bytes},
+                     "traffic": load_traffic(score_bytes), "algorithmic_bytes_per_launch": score_bytes,
+                     "events": f"HIP events on the launch stream around {n} of the {args.steps} timed steps' "
+                               f"{DOMINANT} launches (every {EVENT_EVERY}th step)"},
         "input_gen_s": round(gen_s, 1),
     }
 
@@ -865,13 +873,16 @@ def batched_leg(args, dev, cpu=True):
     torch.cuda.synchronize()
     b.prof_reset()
     b.prof_only(DOMINANT)
-    b.prof_enable(True)
     t0 = time.perf_counter()
     for i in range(args.batched_steps):
+        sampled = i % EVENT_EVERY == 0
+        if sampled:
+            b.prof_enable(True)
         step(i)
+        if sampled:
+            b.prof_enable(False)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    b.prof_enable(False)
     kms, kn = b.prof_read(DOMINANT)
     b.prof_reset()
     b.prof_only(None)

@@ -86,6 +86,24 @@ __device__ __forceinline__ void attn128_body(
     const int ntiles = s_begin < nrows ? rps / TILE : 0;   // same for every non-empty split
 
     const int raw_first = MODE == 1 ? (int)(w0 - raw0) : 0;        // raw row of the first window row
+    // The query: the wave's 32 head rows (32 KiB, contiguous) land in tile buffer w by loads to LDS, one
+    // 1 KiB row per instruction with the row slots' chunk swizzle, and are read back below in the MFMA
+    // layout.  (Loaded straight into registers, each instruction would touch 32 rows x 32 bytes, so every
+    // 128-byte line would be fetched by four instructions.)  Issued first, so they overlap the row staging.
+    // (the buffer as a 32-bit LDS address, selected in scalar registers.  The FP8-row and rotation
+    // variants, whose widening or rotation leaves no registers to spare, load the query straight into
+    // registers: staged, they spill.)
+    constexpr bool QLDS = !FP8 && !ROPE;
+    const uint32_t qbuf = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(size_t)(CSA_LDS char*)(w == 0 ? buf0 : (w == 1 ? buf1 : (w == 2 ? buf2 : buf3))));
+    if constexpr (QLDS) {
+        const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(q + ((size_t)bt * H + hq * 128 + w * 32) * D, 32u * ROWB);
+        const uint32_t l16q = 16u * (uint32_t)lane;
+#pragma unroll
+        for (int r = 0; r < 32; ++r)           // lane l fetches logical chunk l ^ f(r) into slot position l
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_q, (CSA_LDS void*)(size_t)(qbuf + r * ROWB), 16,
+                                                     (int)(l16q ^ (16u * (uint32_t)swz_chunk(r))), r * ROWB, 0, 0);
+    }
     // The row of every slot the split will load, staged once in LDS: the entry (dense rows, selected
     // entries) or the raw row (window); -1 for masked slots (unselected padding, rows past the visible
     // ones, and the tiles loaded past the end), which load row 0 and get no weight.
@@ -113,14 +131,25 @@ __device__ __forceinline__ void attn128_body(
 
     bf16x8_t qreg[KS];
     {
-        const uint16_t* qp = q + ((size_t)bt * H + h) * D + 8 * g;
+        if constexpr (QLDS) {
+            // k-step s of head hl is logical chunk 2s + g of buffer row hl, stored at (2s + g) ^ f(hl)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");          // this wave's query rows landed
+            // (qbuf is a multiple of 1 KiB, so the XOR of 32 s acts on the row offset alone)
+            const uint32_t qa = qbuf + hl * ROWB + 16 * (g ^ swz_chunk(hl));
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qreg[s] = as_bf16x8(*(const u32x4_t*)(qp + 16 * s));
+            for (int s = 0; s < KS; ++s) qreg[s] = as_bf16x8(*(const CSA_LDS u32x4_t*)(size_t)(qa ^ (32u * s)));
+        } else {
+            const uint16_t* qp = q + ((size_t)bt * H + h) * D + 8 * g;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) qreg[s] = as_bf16x8(*(const u32x4_t*)(qp + 16 * s));
+        }
         if constexpr (ROPE) {                   // fused rotary embedding of the last 64 dims, at +p
 #pragma unroll
             for (int s = KS - ROPE_FUSED_RD / 16; s < KS; ++s)
                 qreg[s] = as_bf16x8(rope8(__builtin_bit_cast(u32x4_t, qreg[s]), 16 * s + 8 * g, D, R, (double)p));
         }
+        // every wave has its query in registers before any tile load reuses the buffers
+        if constexpr (QLDS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     const bf16x8_t qmask = as_bf16x8(u32x4_t{g == 0 ? BF16_NEG_2P100 : 0u, 0u, 0u, 0u});
     f32x16_t acc[DT];
