@@ -134,7 +134,7 @@ class DecodeArgs(ctypes.Structure):
         ("layout", ctypes.POINTER(CacheLayout)),
         ("q_idx_scale", ctypes.c_void_p), ("k_idx_scale", ctypes.c_void_p),
         ("csa_rope", ctypes.POINTER(RopeSpec)), ("hca_rope", ctypes.POINTER(RopeSpec)),
-        ("kv_format", ctypes.c_int),
+        ("kv_format", ctypes.c_int), ("ws_persistent", ctypes.c_int),
     ]
 
 
@@ -301,7 +301,7 @@ def hca_dense_attn(q, kv_h, L: int, mh: int, pos0: int, scale: float, out, lse_o
 def make_decode_args(*, L, scale, csa_q, q_idx, w_idx, k_idx, kv, kv_raw, idx_dtype, m, topk, W, csa_out,
                      hca_q, kv_h, mh, hca_out, csa_lse=None, hca_lse=None, idx_out=None, csa_sink=None,
                      hca_sink=None, layout=None, q_idx_scale=None, k_idx_scale=None, csa_rope=None,
-                     hca_rope=None, kv_format=KV_BF16) -> DecodeArgs:
+                     hca_rope=None, kv_format=KV_BF16, ws_persistent=False) -> DecodeArgs:
     B, H, D = csa_q.shape[0], csa_q.shape[-2], csa_q.shape[-1]
     HI, dI = q_idx.shape[-2], q_idx.shape[-1] * (2 if idx_dtype == MXFP4 else 1)
     args = DecodeArgs(B=B, L=L, H=H, D=D, scale=float(scale), csa_q=_p(csa_q), q_idx=_p(q_idx), w_idx=_p(w_idx),
@@ -310,7 +310,7 @@ def make_decode_args(*, L, scale, csa_q, q_idx, w_idx, k_idx, kv, kv_raw, idx_dt
                       csa_sink=_sink(csa_sink, H), hca_q=_p(hca_q), kv_h=_p(kv_h), mh=mh, hca_out=_p(hca_out),
                       hca_lse=_p(hca_lse), hca_sink=_sink(hca_sink, hca_q.shape[-2]),
                       layout=None if layout is None else ctypes.pointer(layout), q_idx_scale=_p(q_idx_scale),
-                      k_idx_scale=_p(k_idx_scale), kv_format=kv_format)
+                      k_idx_scale=_p(k_idx_scale), kv_format=kv_format, ws_persistent=int(bool(ws_persistent)))
     crope, hrope = _rope(csa_rope), _rope(hca_rope)
     if crope is not None:
         args.csa_rope = ctypes.pointer(crope)
@@ -329,6 +329,8 @@ def csa_hca_decode_ws_bytes(args: DecodeArgs) -> int:
 def csa_hca_decode(args: DecodeArgs, ws=None, stream=None, device=None):
     need = csa_hca_decode_ws_bytes(args)
     if ws is None:
+        if args.ws_persistent:
+            raise ValueError("ws_persistent needs a caller-kept workspace (zero-filled before the first call)")
         ws = workspace(need, device or torch.device("cuda"))
     _check(lib.csa_hca_decode(ctypes.byref(args), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 

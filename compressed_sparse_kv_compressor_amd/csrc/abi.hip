@@ -633,6 +633,8 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
     if (rc) return rc;
     REQ(a->kv_format == CSA_KV_BF16 || a->kv_format == CSA_KV_FP8, CSA_ERR_DTYPE, "%s: kv_format %d unknown", fn,
         a->kv_format);
+    REQ(a->ws_persistent == 0 || a->ws_persistent == 1, CSA_ERR_SHAPE, "%s: ws_persistent must be 0 or 1 (got %d)",
+        fn, a->ws_persistent);
     rs.kv_fp8 = rd.kv_fp8 = a->kv_format == CSA_KV_FP8;
     rc = check_ws(fn, ws, ws_bytes, csa_hca_decode_ws_bytes(a));
     if (rc) return rc;
@@ -648,7 +650,7 @@ int csa_hca_decode(const csa_hca_decode_args_t* a, void* ws, size_t ws_bytes, vo
                                                               plain_layout(a->layout) && a->idx_dtype != CSA_MXFP4));
     rc = csa_host::index_topk_launch(a->q_idx, a->w_idx, a->k_idx, a->idx_dtype, a->B, 1, a->HI, a->dI, Nc, a->L, a->m,
                                      p, a->topk, idx, nullptr, nullptr, lay, (const uint8_t*)a->q_idx_scale,
-                                     (const uint8_t*)a->k_idx_scale, w, st);
+                                     (const uint8_t*)a->k_idx_scale, w, st, a->ws_persistent != 0);
     if (rc) return rc;
     w += iws;
     const size_t aws = ws_bytes - (size_t)(w - (char*)ws);

@@ -532,7 +532,7 @@ __global__ __launch_bounds__(STPB) void k_collect(const float* __restrict__ S, u
 // the search and the classification.
 template <int DT, int DI, int HI>
 __global__ __launch_bounds__(SEL_TPB) void k_select(
-    const uint32_t* __restrict__ hist, const uint2* __restrict__ list, const uint32_t* __restrict__ ctab,
+    uint32_t* __restrict__ hist, const uint2* __restrict__ list, const uint32_t* __restrict__ ctab,
     uint2* __restrict__ band_g, unsigned long long* __restrict__ bkey_g, uint8_t* __restrict__ flag_g,
     const void* __restrict__ q_idx, const float* __restrict__ w_idx, const void* __restrict__ k_idx,
     int Tq, int Nc, int NcP, long long L, int m, long long pos0, int topk,
@@ -827,6 +827,10 @@ __global__ __launch_bounds__(SEL_TPB) void k_select(
             out[o++] = (int32_t)c.x;
         }
     if (cnt_out && tid == 0) cnt_out[r] = topk;
+    // The row's histogram words back to zero (read above, before the barriers in between; k_collect read
+    // the bins in the previous launch), so that a workspace kept across calls needs no clearing launch.
+    uint32_t* Hz = hist + (size_t)r * HIST_WORDS;
+    for (int i = tid; i < HIST_WORDS; i += SEL_TPB) Hz[i] = 0u;
 }
 
 }  // namespace
@@ -838,12 +842,13 @@ namespace csa_host {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// S~ [R][NcP] f32 | hist [R][HIST_WORDS] | list [R][NcP] (index, S~) | chunk counts [R][NcP/CCHUNK] u32 |
-// band [R][NcP] (index, position) | band keys [R][NcP] u64 | flags [R][NcP] u8
+// hist [R][HIST_WORDS] (first, so that its place does not depend on Nc) | S~ [R][NcP] f32 | list [R][NcP]
+// (index, S~) | chunk counts [R][NcP/CCHUNK] u32 | band [R][NcP] (index, position) | band keys [R][NcP] u64 |
+// flags [R][NcP] u8.  k_select leaves every row's histogram words at zero.
 static size_t decode_index_ws_bytes(int B, int Tq, int Nc) {
     const size_t R = (size_t)B * Tq;
     const size_t NcP = ((size_t)Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
-    return align256(R * NcP * 4) + align256(R * HIST_WORDS * 4) + align256(R * NcP * 8) +
+    return align256(R * HIST_WORDS * 4) + align256(R * NcP * 4) + align256(R * NcP * 8) +
            align256(R * (NcP / CCHUNK) * 4) + align256(R * NcP * 8) + align256(R * NcP * 8) + align256(R * NcP);
 }
 
@@ -851,18 +856,18 @@ template <int DT, int DI, int HI>
 static int launch_index(const void* q_idx, const float* w_idx, const void* k_idx, int B, int Tq, int Nc,
                         long long L, int m, long long pos0, int topk, int32_t* idx_out, int32_t* cnt_out,
                         float* score_out, const long long* seq_lens, const PageMap& pm, const uint8_t* q_scale,
-                        const uint8_t* k_scale, void* ws, hipStream_t st) {
+                        const uint8_t* k_scale, void* ws, bool hist_zero, hipStream_t st) {
     const size_t R = (size_t)B * Tq;
     const int NcP = (Nc + CCHUNK - 1) / CCHUNK * CCHUNK;
     char* p = (char*)ws;
-    float* S = (float*)p;                       p += align256(R * (size_t)NcP * 4);
     uint32_t* hist = (uint32_t*)p;              p += align256(R * HIST_WORDS * 4);
+    float* S = (float*)p;                       p += align256(R * (size_t)NcP * 4);
     uint2* list = (uint2*)p;                    p += align256(R * (size_t)NcP * 8);
     uint32_t* ctab = (uint32_t*)p;              p += align256(R * (size_t)(NcP / CCHUNK) * 4);
     uint2* band = (uint2*)p;                    p += align256(R * (size_t)NcP * 8);
     unsigned long long* bkey = (unsigned long long*)p; p += align256(R * (size_t)NcP * 8);
     uint8_t* flags = (uint8_t*)p;
-    {
+    if (!hist_zero) {                           // (a workspace kept across calls is already clear)
         const size_t n = R * HIST_WORDS;
         const int blocks = (int)std::min<size_t>((n + 255) / 256, 2048);
         CSA_LAUNCH("k_fill", k_fill, dim3(blocks), dim3(256), 0, st, hist, n);
@@ -908,7 +913,7 @@ size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int
 int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
                       int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
                       int32_t* idx_out, int32_t* cnt_out, float* score_out, const CacheLayout& lay,
-                      const uint8_t* q_scale, const uint8_t* k_scale, void* ws, hipStream_t st) {
+                      const uint8_t* q_scale, const uint8_t* k_scale, void* ws, hipStream_t st, bool hist_zero) {
     const PageMap pm = page_map(lay, m);
     if (!lay.seq_lens && !lay.table && prefill_index_applicable(dtype, HI, dI, B, Tq, Nc, topk))
         return prefill_index_launch(q_idx, w_idx, k_idx, dtype, HI, dI, B, Tq, Nc, L, m, pos0, topk, idx_out,
@@ -916,7 +921,8 @@ int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, 
 #define CSA_IDX_CASE(DT, DI, HI_)                                                              \
     if (dtype == DT && dI == DI && HI == HI_)                                                  \
         return launch_index<DT, DI, HI_>(q_idx, w_idx, k_idx, B, Tq, Nc, L, m, pos0, topk,     \
-                                         idx_out, cnt_out, score_out, lay.seq_lens, pm, q_scale, k_scale, ws, st);
+                                         idx_out, cnt_out, score_out, lay.seq_lens, pm, q_scale, k_scale, ws, \
+                                         hist_zero, st);
 #define CSA_IDX_HI(DT, DI) CSA_IDX_CASE(DT, DI, 1) CSA_IDX_CASE(DT, DI, 2) CSA_IDX_CASE(DT, DI, 4) \
                            CSA_IDX_CASE(DT, DI, 8) CSA_IDX_CASE(DT, DI, 16)
     CSA_IDX_HI(0, 64) CSA_IDX_HI(0, 128) CSA_IDX_HI(1, 64) CSA_IDX_HI(1, 128) CSA_IDX_HI(2, 128)

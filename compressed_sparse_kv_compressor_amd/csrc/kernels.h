@@ -30,7 +30,8 @@ size_t index_topk_ws_bytes(int dtype, int HI, int dI, int B, int Tq, int Nc, int
 int index_topk_launch(const void* q_idx, const float* w_idx, const void* k_idx, int dtype, int B, int Tq,
                       int HI, int dI, int Nc, long long L, int m, long long pos0, int topk,
                       int32_t* idx_out, int32_t* cnt_out, float* score_out, const CacheLayout& lay,
-                      const uint8_t* q_scale, const uint8_t* k_scale, void* ws, hipStream_t st);
+                      const uint8_t* q_scale, const uint8_t* k_scale, void* ws, hipStream_t st,
+                      bool hist_zero = false);   // hist_zero: the workspace's histogram words already hold zeros
 int kv_fp8_launch(const void* x, long long n, int D, void* y, hipStream_t st);
 int mxfp4_launch(const void* x, long long n, int len, void* codes, void* scales, hipStream_t st);
 // many-query (prefill) indexer path: Tq >= 64, topk <= 1024; bf16 / e4m3 rows of dI = 64 or 128 or MXFP4 rows

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 5
+#define CSA_ABI_VERSION 6
 
 typedef enum {
     CSA_OK = 0,
@@ -433,6 +433,12 @@ typedef struct csa_hca_decode_args {
     /* CSA_KV_BF16 (0), or CSA_KV_FP8: the entry rows of both layers (kv, kv_h) in the FP8 format of
      * csa_kv_fp8_encode, D + 80 bytes per row (the raw window rows kv_raw stay bf16). */
     int kv_format;
+    /* 0, or 1 for a workspace the caller keeps across calls with the same sizes (a serving loop): its first
+     * csa_hca_decode_ws_bytes(a) bytes must hold zeros before the first such call (allocate it zero-filled)
+     * and must not be written by anything else between calls.  Each call then leaves the words the next one
+     * counts on (the per-row score histograms) at zero, and skips clearing them itself.  Calls that overlap
+     * in time on one workspace race, as with any shared workspace. */
+    int ws_persistent;
 } csa_hca_decode_args_t;
 
 size_t csa_hca_decode_ws_bytes(const csa_hca_decode_args_t* a);

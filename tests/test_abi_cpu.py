@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(b):
 
 
 def test_version_and_status_strings(b):
-    assert b.lib.csa_abi_version() == 5
+    assert b.lib.csa_abi_version() == 6
     assert b.lib.csa_status_str(CSA_ERR_WORKSPACE) == b"CSA_ERR_WORKSPACE"
     assert b.lib.csa_status_str(99) == b"CSA_ERR_UNKNOWN"
 
@@ -137,6 +137,9 @@ def test_compress_and_decode_validation_codes(b):
     args.kv_format = 7                     # checked before any launch
     assert lib.csa_hca_decode(ctypes.byref(args), A16, 10 ** 9, None) == CSA_ERR_DTYPE
     args.kv_format = 0
+    args.ws_persistent = 2                 # 0 or 1 only, checked before any launch
+    assert lib.csa_hca_decode(ctypes.byref(args), A16, 10 ** 9, None) == CSA_ERR_SHAPE
+    args.ws_persistent = 0
     assert lib.csa_hca_decode(ctypes.byref(args), A16, 16, None) == CSA_ERR_WORKSPACE
     assert lib.csa_hca_decode_ws_bytes(ctypes.byref(args)) > 16
 

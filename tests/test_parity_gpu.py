@@ -748,6 +748,61 @@ def test_fused_decode_matches_oracle_and_separate_calls(b, L, B, H, D, HI, dI, t
     assert torch.equal(c2, csa_out) and torch.equal(h2, hca_out)
 
 
+@pytest.mark.parametrize("dt,layout", [(1, None), (0, "paged")])
+def test_fused_decode_persistent_workspace(b, dt, layout):
+    # a workspace kept across calls (zero-filled once, ws_persistent = 1): three calls in a row over two
+    # input sets, each bitwise equal to an ordinary call on a fresh workspace, and the histogram words
+    # (the first 8 x 4104 words with a caller-owned idx_out) read back as zero after every call
+    from compressed_sparse_kv_compressor_amd.configs import DecodeCfg
+    B, H, D, topk, L = 8, 128, 512, 1024, 4 * 9000
+    cfg = DecodeCfg("t", B=B, L=L, H=H, D=D, HI=8, dI=128, m=4, mh=128, topk=topk, W=128, idx_dtype=dt)
+    xs = [decode_case(cfg, seed=s) for s in (31, 32)]
+    lay = None
+    if layout == "paged":
+        nb, bt = -(-L // 128), 128
+        perm = np.random.default_rng(3).permutation(B * nb).astype(np.int32).reshape(B, nb)
+        table = torch.from_numpy(perm).to(DEV)
+        lay = b.make_layout(block_table=table, num_blocks=B * nb, block_tokens=bt)
+        for x in xs:
+            for key, ratio in (("k_idx", 4), ("kv", 4), ("kv_h", 128)):
+                a = x[key]
+                epb = bt // ratio
+                rows = a.reshape(B, -1, *a.shape[2:])
+                n = rows.shape[1]
+                pool = np.zeros((B * nb * epb,) + a.shape[2:], a.dtype)
+                for bb in range(B):
+                    for s0 in range(0, n, epb):
+                        pg = perm[bb, s0 // epb]
+                        cnt = min(epb, n - s0)
+                        pool[pg * epb:pg * epb + cnt] = rows[bb, s0:s0 + cnt]
+                x[key] = pool
+    ts = [{k: dev(v) for k, v in x.items()} for x in xs]
+
+    def args_for(t, outs, persistent):
+        return b.make_decode_args(L=L, scale=cfg.scale, csa_q=t["csa_q"].view(B, H, D), q_idx=t["q_idx"],
+                                  w_idx=t["w_idx"], k_idx=t["k_idx"], kv=t["kv"], kv_raw=t["raw"], idx_dtype=dt,
+                                  m=4, topk=topk, W=cfg.W, csa_out=outs[0], hca_q=t["hca_q"].view(B, H, D),
+                                  kv_h=t["kv_h"], mh=128, hca_out=outs[1], idx_out=outs[2], layout=lay,
+                                  ws_persistent=persistent)
+
+    def fresh_outs():
+        return (torch.empty((B, H, D), dtype=torch.int16, device=DEV), torch.empty((B, H, D), dtype=torch.int16,
+                device=DEV), torch.empty((B, topk), dtype=torch.int32, device=DEV))
+
+    outs = fresh_outs()
+    a_p = [args_for(t, outs, True) for t in ts]
+    ws = torch.zeros(b.csa_hca_decode_ws_bytes(a_p[0]), dtype=torch.uint8, device=DEV)
+    hist_bytes = B * 4104 * 4
+    for k in (0, 1, 0):
+        b.csa_hca_decode(a_p[k], ws=ws)
+        ref = fresh_outs()
+        b.csa_hca_decode(args_for(ts[k], ref, False))
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got, want), f"call over input set {k}"
+        assert int(ws[:hist_bytes].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("L,B,H,D,HI,dI,topk,dt", [(4096, 1, 16, 128, 4, 64, 64, 0),
                                                    (4 * 6000, 2, 128, 512, 8, 128, 1024, 1)])
 def test_fused_decode_with_sinks_matches_oracle(b, L, B, H, D, HI, dI, topk, dt):
