@@ -992,8 +992,8 @@ def serving_leg(args, dev, cpu=True):
     dargs = b.make_decode_args(L=L, scale=cfg.scale, csa_q=csa_q, q_idx=q_idx, w_idx=w_idx, k_idx=pools["ik"],
                                kv=pools["kv"], kv_raw=win, idx_dtype=cfg.idx_dtype, m=m, topk=topk, W=W,
                                csa_out=csa_out, hca_q=hca_q, kv_h=pools["kvh"], mh=mh, hca_out=hca_out, idx_out=idx,
-                               layout=layout)
-    dws = b.workspace(b.csa_hca_decode_ws_bytes(dargs), dev)
+                               layout=layout, ws_persistent=True)
+    dws = torch.zeros(b.csa_hca_decode_ws_bytes(dargs), dtype=torch.uint8, device=dev)   # kept across steps
     stream = torch.cuda.current_stream()
 
     def step(i=0):
@@ -1109,8 +1109,8 @@ def lowp_leg(args, dev, cpu=True):
                                 k_idx=c["kc"], kv=c["kv"], kv_raw=c["raw"], idx_dtype=b.MXFP4, m=m, topk=topk, W=W,
                                 csa_out=csa_out, hca_q=c["hca_q"].view(B, H, D), kv_h=c["kvh"], mh=mh,
                                 hca_out=hca_out, idx_out=idx, q_idx_scale=c["qs"], k_idx_scale=c["ks"],
-                                kv_format=b.KV_FP8) for c in copies]
-    ws = b.workspace(b.csa_hca_decode_ws_bytes(dargs[0]), dev)
+                                kv_format=b.KV_FP8, ws_persistent=True) for c in copies]
+    ws = torch.zeros(b.csa_hca_decode_ws_bytes(dargs[0]), dtype=torch.uint8, device=dev)   # kept across steps
     stream = torch.cuda.current_stream()
 
     def step(i=0):
