@@ -1150,39 +1150,41 @@ __global__ __launch_bounds__(FB_TPB) void k_pfb_rows(
 // k_pwiden: rows of the many-query layout (P_HI heads x P_DI bf16) from rows of hin heads x dI elements
 // in format dtype (0 bf16, 1 e4m3, 2 MXFP4 with one E8M0 scale per 32 elements); output row o is head
 // o % P_HI (or the key row o when hin = 1 and hout = 1) of group o / hout.  One thread per 16-byte
-// output chunk; heads past hin and dims past dI are zero.
+// output chunk (grid-stride); heads past hin and dims past dI are zero.
 __global__ __launch_bounds__(256) void k_pwiden(const void* __restrict__ src, const uint8_t* __restrict__ scale,
                                                 int dtype, long long nout, int hout, int hin, int dI,
                                                 uint16_t* __restrict__ dst)
 {
     constexpr int CPR = P_DI / 8;                      // 16-byte chunks per output row
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= nout * CPR) return;
-    const long long o = i / CPR;
-    const int c = (int)(i % CPR), h = (int)(o % hout);
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (h < hin && 8 * c < dI) {
-        const long long r = o / hout * hin + h;         // source row
-        if (dtype == 0) {
-            v = *(const u32x4_t*)((const uint16_t*)src + r * dI + 8 * c);
-        } else if (dtype == 1) {
-            const uint2 x = *(const uint2*)((const uint8_t*)src + r * dI + 8 * c);
-            v = e4m3x8_to_bf16x8(x.x, x.y);
-        } else {
-            const uint32_t x = *(const uint32_t*)((const uint8_t*)src + r * (dI / 2) + 4 * c);
-            v = fp4x8_to_bf16x8(x, e8m0_scale(scale[r * (dI / 32) + c / 4]));
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nout * CPR;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long o = i / CPR;
+        const int c = (int)(i % CPR), h = (int)(o % hout);
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (h < hin && 8 * c < dI) {
+            const long long r = o / hout * hin + h;         // source row
+            if (dtype == 0) {
+                v = *(const u32x4_t*)((const uint16_t*)src + r * dI + 8 * c);
+            } else if (dtype == 1) {
+                const uint2 x = *(const uint2*)((const uint8_t*)src + r * dI + 8 * c);
+                v = e4m3x8_to_bf16x8(x.x, x.y);
+            } else {
+                const uint32_t x = *(const uint32_t*)((const uint8_t*)src + r * (dI / 2) + 4 * c);
+                v = fp4x8_to_bf16x8(x, e8m0_scale(scale[r * (dI / 32) + c / 4]));
+            }
         }
+        *(u32x4_t*)(dst + o * P_DI + 8 * c) = v;
     }
-    *(u32x4_t*)(dst + o * P_DI + 8 * c) = v;
 }
 
 // head weights of the many-query layout: P_HI per row, +0 past hin
 __global__ __launch_bounds__(256) void k_pwiden_w(const float* __restrict__ w, long long R, int hin, float* __restrict__ dst)
 {
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= R * P_HI) return;
-    const int h = (int)(i % P_HI);
-    dst[i] = h < hin ? w[i / P_HI * hin + h] : 0.0f;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < R * P_HI;
+         i += (long long)gridDim.x * blockDim.x) {
+        const int h = (int)(i % P_HI);
+        dst[i] = h < hin ? w[i / P_HI * hin + h] : 0.0f;
+    }
 }
 
 // clears the Kmax accumulators [n] and the fallback row count
@@ -1267,12 +1269,11 @@ int prefill_index_launch(const void* q_idx, const float* w_idx, const void* k_id
         uint16_t* qw = (uint16_t*)p;        p += align256(P.R * P_HI * P_ROW_B);
         float* ww = (float*)p;              p += align256(P.R * P_HI * 4);
         const long long nk = (long long)B * Nc, nq = (long long)P.R * P_HI, cpr = P_DI / 8;
-        CSA_LAUNCH("k_pwiden", k_pwiden, dim3((unsigned)((nk * cpr + 255) / 256)), dim3(256), 0, st, k_idx, k_scale,
-                   dtype, nk, 1, 1, dI, kw);
-        CSA_LAUNCH("k_pwiden", k_pwiden, dim3((unsigned)((nq * cpr + 255) / 256)), dim3(256), 0, st, q_idx, q_scale,
-                   dtype, nq, P_HI, HI, dI, qw);
-        CSA_LAUNCH("k_pwiden", k_pwiden_w, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, w_idx,
-                   (long long)P.R, HI, ww);
+        auto blocks = [](long long n) { return dim3((unsigned)std::min<long long>((n + 255) / 256, 65536)); };
+        CSA_LAUNCH("k_pwiden", k_pwiden, blocks(nk * cpr), dim3(256), 0, st, k_idx, k_scale, dtype, nk, 1, 1, dI, kw);
+        CSA_LAUNCH("k_pwiden", k_pwiden, blocks(nq * cpr), dim3(256), 0, st, q_idx, q_scale, dtype, nq, P_HI, HI, dI,
+                   qw);
+        CSA_LAUNCH("k_pwiden", k_pwiden_w, blocks(nq), dim3(256), 0, st, w_idx, (long long)P.R, HI, ww);
         k_idx = kw;
         q_idx = qw;
         w_idx = ww;
