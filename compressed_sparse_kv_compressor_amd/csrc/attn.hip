@@ -284,7 +284,7 @@ typedef float SxArr[4][4][64][4];         // score exchange [wave][j/4][lane][j%
 
 template <int MODE, bool PAGED, bool ROPE, bool FP8>
 __device__ __forceinline__ void attn64_body(
-    int bid, uint16_t* bufA, uint16_t* bufB, uint16_t* bufC, SxArr* sx,
+    int bid, uint16_t* bufA, uint16_t* bufB, uint16_t* bufC, SxArr* sx, float (*amx)[32],
     const uint16_t* __restrict__ q, const Rows& R, int Tq, int H, long long pos0, float scale_log2, int nunits,
     int nsplit, int rps, float* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse)
@@ -695,6 +695,20 @@ __device__ __forceinline__ void attn64_body(
     }
 
     // ---- output: both d-half waves of a head group hold the same (m, l) ----
+    // Split partials go out as fp16 scaled by one power of two per (split, head), so the two d-half waves of
+    // a head group agree on max |O| through LDS first (before the exit of the waves past H, so that every
+    // wave of the workgroup reaches the barrier; such a wave's partner is past H too).
+    float amax = 0.f;
+    if (nsplit > 1) {                          // uniform
+#pragma unroll
+        for (int d = 0; d < DT; ++d)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(acc[d][j]));
+        amax = xhalf_max(amax);
+        if (g == 0) amx[w][hl] = amax;
+        __syncthreads();
+        amax = fmaxf(amax, amx[w ^ 2][hl]);
+    }
     if (!hv) return;
     const bool empty = !(m_run > EMPTY_M);     // no valid row: garbage-weighted sums under a tiny max
     if (empty) {
@@ -726,16 +740,25 @@ __device__ __forceinline__ void attn64_body(
             }
         if (lse && g == 0 && dh == 0) lse[(size_t)bt * H + h] = lse_v;
     } else {
+        // O 2^-e (fp16, round to nearest even) with 2^e >= max |O| over the head's 512 values, stored with m + e
+        // and l 2^-e: every term of the merge is unchanged, and each value keeps a relative error <= 2^-11 of
+        // the head's largest
+        const int e = empty || !(amax > 0.f) ? 0 : __builtin_amdgcn_frexp_expf(amax);
+        const float sc = empty ? 0.f : __builtin_amdgcn_ldexpf(1.0f, -e);
+        typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+        auto ph = [&](float a, float b2) -> uint32_t {
+            const f16x2_t v = {(_Float16)(a * sc), (_Float16)(b2 * sc)};
+            return __builtin_bit_cast(uint32_t, v);
+        };
         const size_t sl = ((size_t)bt * nsplit + split) * H + h;
-        float* op = part_o + sl * D + dh * HD + 4 * g;
+        uint16_t* op = (uint16_t*)part_o + sl * D + dh * HD + 4 * g;
 #pragma unroll
         for (int d = 0; d < DT; ++d)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4)
-                *(f32x4_t*)(op + d * 32 + 8 * q4) =
-                    empty ? f32x4_t{0.f, 0.f, 0.f, 0.f}
-                          : f32x4_t{acc[d][4 * q4], acc[d][4 * q4 + 1], acc[d][4 * q4 + 2], acc[d][4 * q4 + 3]};
-        if (g == 0 && dh == 0) part_ml[sl] = make_float2(m_run, l_run);
+                *(uint2*)(op + d * 32 + 8 * q4) = make_uint2(ph(acc[d][4 * q4], acc[d][4 * q4 + 1]),
+                                                             ph(acc[d][4 * q4 + 2], acc[d][4 * q4 + 3]));
+        if (g == 0 && dh == 0) part_ml[sl] = make_float2(m_run + (float)e, l_run * sc);
     }
 }
 
@@ -745,7 +768,8 @@ __device__ __forceinline__ void attn64_body(
     __shared__ __attribute__((aligned(1024))) uint16_t bufA[2 * TILE * HD];   \
     __shared__ __attribute__((aligned(1024))) uint16_t bufB[2 * TILE * HD];   \
     __shared__ __attribute__((aligned(1024))) uint16_t bufC[2 * TILE * HD];   \
-    __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];
+    __shared__ __attribute__((aligned(16))) float sx[2][4][4][64][4];       \
+    __shared__ float amx[4][32];
 
 template <int MODE, bool PAGED, bool ROPE, bool FP8>
 __global__ __launch_bounds__(TPB, 1) void k_attn64(
@@ -754,16 +778,29 @@ __global__ __launch_bounds__(TPB, 1) void k_attn64(
     float* __restrict__ lse)
 {
     CSA_ATT64_LDS
-    attn64_body<MODE, PAGED, ROPE, FP8>(blockIdx.x, bufA, bufB, bufC, sx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
+    attn64_body<MODE, PAGED, ROPE, FP8>(blockIdx.x, bufA, bufB, bufC, sx, amx, q, R, Tq, H, pos0, scale_log2, nunits, nsplit, rps,
                            part_o, part_ml, out, lse);
 }
 
 #undef CSA_ATT64_LDS
 
+// four partial values at element offset i: fp16 (converted exactly to fp32) or fp32
+template <bool F16>
+__device__ __forceinline__ f32x4_t part4(const float* p, size_t i) {
+    if constexpr (F16) {
+        typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+        const f16x4_t h = *(const f16x4_t*)((const uint16_t*)p + i);
+        return f32x4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    } else {
+        return *(const f32x4_t*)(p + i);
+    }
+}
+
 // Merge split partials in split order: out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.  Thread tid
 // owns d = 4 tid .. 4 tid + 3 of head h; the split loop is unrolled so that several partial loads are
 // in flight (the order of the sums is fixed, so the result is deterministic).
-template <int D>
+// F16: the partials are fp16 (k_attn64's, scaled as above), else fp32 (k_attn's).
+template <int D, bool F16>
 __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
                                              int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
                                              const float* __restrict__ sink, int h, int bt, const Rows& R, int Tq,
@@ -784,7 +821,7 @@ __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, c
             for (int u = 0; u < 4; ++u) {
                 const size_t slot = s0 + (size_t)(s + u) * H;
                 ml[u] = part_ml[slot];
-                v[u] = *(const f32x4_t*)(part_o + slot * D + d);
+                v[u] = part4<F16>(part_o, slot * D + d);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -798,7 +835,7 @@ __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, c
             const float2 ml = part_ml[slot];
             const float f = exp2f(ml.x - M);
             l += f * ml.y;
-            o += f * *(const f32x4_t*)(part_o + slot * D + d);
+            o += f * part4<F16>(part_o, slot * D + d);
         }
     }
     float lse_v;
@@ -818,7 +855,7 @@ __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, c
 }
 
 // grid (H, BT), or with XMAP a 1-D grid of jobs (query, head) laid out by XCD (see XcdJobs)
-template <int D, bool XMAP>
+template <int D, bool XMAP, bool F16>
 __global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
                                                    int H, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
                                                    const float* __restrict__ sink, Rows R, int Tq, long long pos0,
@@ -831,7 +868,7 @@ __global__ __launch_bounds__(D / 4) void k_combine(const float* __restrict__ par
         h = J % H;
         bt = J / H;
     }
-    combine_body<D>(part_o, part_ml, H, nsplit, out, lse, sink, h, bt, R, Tq, pos0);
+    combine_body<D, F16>(part_o, part_ml, H, nsplit, out, lse, sink, h, bt, R, Tq, pos0);
 }
 
 }  // namespace
@@ -992,7 +1029,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
             int most;
             const XcdJobs xj = xcd_jobs(BT * H, 1, [&](int g) {
                 return ((g / H * ns + ns / 2) * HP + g % H / 64) / per; }, &most);
-            CSA_LAUNCH("k_combine", (k_combine<512, true>), dim3(8 * most), dim3(128), 0, st, part_o, part_ml, H, ns,
+            CSA_LAUNCH("k_combine", (k_combine<512, true, true>), dim3(8 * most), dim3(128), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse, R.sink, R, Tq, pos0, xj);
         }
         return 0;
@@ -1013,7 +1050,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         else if (fp8) CSA_GENERIC(512, false, true);
         else CSA_GENERIC(512, false, false);
         if (ns > 1)
-            CSA_LAUNCH("k_combine", (k_combine<512, false>), dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
+            CSA_LAUNCH("k_combine", (k_combine<512, false, false>), dim3(H, BT), dim3(128), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse, R.sink, R, Tq, pos0, XcdJobs{});
     } else if (D == 128) {
         if (sepv && fp8) CSA_GENERIC(128, true, true);
@@ -1021,7 +1058,7 @@ int attn_launch(const void* q, const AttnRows& a, int B, int Tq, int H, int D, l
         else if (fp8) CSA_GENERIC(128, false, true);
         else CSA_GENERIC(128, false, false);
         if (ns > 1)
-            CSA_LAUNCH("k_combine", (k_combine<128, false>), dim3(H, BT), dim3(32), 0, st, part_o, part_ml, H, ns,
+            CSA_LAUNCH("k_combine", (k_combine<128, false, false>), dim3(H, BT), dim3(32), 0, st, part_o, part_ml, H, ns,
                        (uint16_t*)out, lse, R.sink, R, Tq, pos0, XcdJobs{});
     } else {
         return fail(6, "attention: D = %d unsupported", D);
