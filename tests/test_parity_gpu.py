@@ -748,11 +748,12 @@ def test_fused_decode_matches_oracle_and_separate_calls(b, L, B, H, D, HI, dI, t
     assert torch.equal(c2, csa_out) and torch.equal(h2, hca_out)
 
 
-@pytest.mark.parametrize("dt,layout", [(1, None), (0, "paged")])
-def test_fused_decode_persistent_workspace(b, dt, layout):
+@pytest.mark.parametrize("dt,layout,own_idx", [(1, None, True), (0, "paged", True), (1, None, False)])
+def test_fused_decode_persistent_workspace(b, dt, layout, own_idx):
     # a workspace kept across calls (zero-filled once, ws_persistent = 1): three calls in a row over two
     # input sets, each bitwise equal to an ordinary call on a fresh workspace, and the histogram words
-    # (the first 8 x 4104 words with a caller-owned idx_out) read back as zero after every call
+    # (8 x 4104 words at the start of the index workspace: after the indices when the workspace keeps
+    # them) read back as zero after every call
     from compressed_sparse_kv_compressor_amd.configs import DecodeCfg
     B, H, D, topk, L = 8, 128, 512, 1024, 4 * 9000
     cfg = DecodeCfg("t", B=B, L=L, H=H, D=D, HI=8, dI=128, m=4, mh=128, topk=topk, W=128, idx_dtype=dt)
@@ -782,8 +783,8 @@ def test_fused_decode_persistent_workspace(b, dt, layout):
         return b.make_decode_args(L=L, scale=cfg.scale, csa_q=t["csa_q"].view(B, H, D), q_idx=t["q_idx"],
                                   w_idx=t["w_idx"], k_idx=t["k_idx"], kv=t["kv"], kv_raw=t["raw"], idx_dtype=dt,
                                   m=4, topk=topk, W=cfg.W, csa_out=outs[0], hca_q=t["hca_q"].view(B, H, D),
-                                  kv_h=t["kv_h"], mh=128, hca_out=outs[1], idx_out=outs[2], layout=lay,
-                                  ws_persistent=persistent)
+                                  kv_h=t["kv_h"], mh=128, hca_out=outs[1], idx_out=outs[2] if own_idx else None,
+                                  layout=lay, ws_persistent=persistent)
 
     def fresh_outs():
         return (torch.empty((B, H, D), dtype=torch.int16, device=DEV), torch.empty((B, H, D), dtype=torch.int16,
@@ -792,15 +793,16 @@ def test_fused_decode_persistent_workspace(b, dt, layout):
     outs = fresh_outs()
     a_p = [args_for(t, outs, True) for t in ts]
     ws = torch.zeros(b.csa_hca_decode_ws_bytes(a_p[0]), dtype=torch.uint8, device=DEV)
+    h0 = 0 if own_idx else (B * topk * 4 + 255) // 256 * 256
     hist_bytes = B * 4104 * 4
     for k in (0, 1, 0):
         b.csa_hca_decode(a_p[k], ws=ws)
         ref = fresh_outs()
         b.csa_hca_decode(args_for(ts[k], ref, False))
         torch.cuda.synchronize()
-        for got, want in zip(outs, ref):
+        for got, want in zip(outs[:2] if not own_idx else outs, ref):
             assert torch.equal(got, want), f"call over input set {k}"
-        assert int(ws[:hist_bytes].count_nonzero()) == 0
+        assert int(ws[h0:h0 + hist_bytes].count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("L,B,H,D,HI,dI,topk,dt", [(4096, 1, 16, 128, 4, 64, 64, 0),
