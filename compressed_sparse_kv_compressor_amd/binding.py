@@ -302,6 +302,9 @@ def make_decode_args(*, L, scale, csa_q, q_idx, w_idx, k_idx, kv, kv_raw, idx_dt
                      hca_q, kv_h, mh, hca_out, csa_lse=None, hca_lse=None, idx_out=None, csa_sink=None,
                      hca_sink=None, layout=None, q_idx_scale=None, k_idx_scale=None, csa_rope=None,
                      hca_rope=None, kv_format=KV_BF16, ws_persistent=False) -> DecodeArgs:
+    """The csa_hca_decode_args_t of one decode step.  ws_persistent: the workspace passed to csa_hca_decode is
+    kept across calls with these sizes, zero-filled once before the first (torch.zeros) and written by nothing
+    else in between; each call then leaves it ready for the next."""
     B, H, D = csa_q.shape[0], csa_q.shape[-2], csa_q.shape[-1]
     HI, dI = q_idx.shape[-2], q_idx.shape[-1] * (2 if idx_dtype == MXFP4 else 1)
     args = DecodeArgs(B=B, L=L, H=H, D=D, scale=float(scale), csa_q=_p(csa_q), q_idx=_p(q_idx), w_idx=_p(w_idx),
